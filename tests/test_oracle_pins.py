@@ -1,0 +1,372 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: every expected value comes from
+a closed form, a hand-worked fixture under tests/golden/, an independent
+library routine (numpy float64 / int64 matmul, torch's BF16 rounding), brute
+force in float64, or an invariant the method guarantees.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from conftest import read_golden
+from swiglu_mlp_amd import workloads as W
+
+f32 = np.float32
+
+
+def sylvester_kron(g):
+    """Unnormalised Sylvester matrix built by the Kronecker recursion
+    H_{2n} = [[H_n, H_n], [H_n, -H_n]] (a construction independent of the
+    popcount closed form the oracle uses)."""
+    h = np.array([[1]], dtype=np.int64)
+    h2 = np.array([[1, 1], [1, -1]], dtype=np.int64)
+    while h.shape[0] < g:
+        h = np.kron(h2, h)
+    return h
+
+
+def ulp32(x):
+    return np.spacing(np.abs(np.asarray(x, dtype=np.float32))).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Rotation: H and the FWHT
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("g", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+def test_hadamard_closed_form(orc, g):
+    h = orc.hadamard(g)
+    np.testing.assert_array_equal(h, h.T)                         # symmetric
+    np.testing.assert_allclose(h @ h.T, np.eye(g), atol=1e-12)    # orthogonal
+    np.testing.assert_allclose(np.abs(h), 1 / math.sqrt(g), rtol=1e-15)
+    np.testing.assert_allclose(h * math.sqrt(g), sylvester_kron(g), rtol=1e-15)
+    if g == 2:
+        np.testing.assert_allclose(h, np.array([[1, 1], [1, -1]]) / math.sqrt(2))
+
+
+def test_hadamard_rejects_non_power_of_two(orc):
+    with pytest.raises(ValueError):
+        orc.hadamard(96)
+
+
+@pytest.mark.parametrize("g", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+def test_norm_const_is_rounded_inverse_sqrt(orc, g):
+    from fractions import Fraction
+    c = orc.norm_const(g)
+    # |c - 1/sqrt(g)| <= half an ulp, checked with exact rationals (c^2 g vs 1)
+    lo = Fraction(float(c) - float(ulp32(c)) / 2)
+    hi = Fraction(float(c) + float(ulp32(c)) / 2)
+    assert lo * lo * g <= 1 <= hi * hi * g
+
+
+@pytest.mark.parametrize("g", [2, 8, 64, 128, 256])
+def test_fwht_matches_dense_float64(orc, g):
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((7, 3 * g)).astype(np.float32)
+    u = orc.fwht(x, g)
+    hk = sylvester_kron(g).astype(np.float64)
+    ref = np.concatenate([x[:, j * g:(j + 1) * g].astype(np.float64) @ hk
+                          for j in range(3)], axis=1)
+    err = np.linalg.norm(u - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    assert err.max() < 1e-6
+
+
+@pytest.mark.parametrize("g", [4, 32, 128, 256])
+def test_fwht_exact_on_small_integers(orc, g):
+    """With small integer inputs every FP32 sum is exact, so the transform must
+    equal the integer matrix product bit for bit (catches a wrong sign, a
+    dropped stage or a mis-indexed butterfly)."""
+    rng = np.random.default_rng(2)
+    x = rng.integers(-8, 9, size=(5, 2 * g))
+    u = orc.fwht(x.astype(np.float32), g)
+    hk = sylvester_kron(g)
+    ref = np.concatenate([x[:, j * g:(j + 1) * g] @ hk for j in range(2)], axis=1)
+    np.testing.assert_array_equal(u, ref.astype(np.float32))
+
+
+def test_fwht_stage_order_golden(orc):
+    rows = read_golden("fwht_order_g4.txt")
+    g = int(rows[0][0])
+    x = np.array([float.fromhex(t) for t in rows[1]], dtype=np.float32)
+    want = np.array([float.fromhex(t) for t in rows[2]], dtype=np.float32)
+    np.testing.assert_array_equal(orc.fwht(x, g), want)
+
+
+def test_single_outlier_closed_form(orc):
+    rows = read_golden("single_outlier_g128.txt")
+    g, j, a = int(rows[0][0]), int(rows[1][0]), float(rows[2][0])
+    s_want = float.fromhex(rows[3][0])
+    codes_want = np.array([int(t) for t in rows[4]], dtype=np.int8)
+    x = np.zeros((1, 3 * g), dtype=np.float32)
+    x[0, g + j] = a                       # outlier in the middle group
+    xb = W.to_bf16_bits(x)
+    q, s = orc.act_quant(xb, 0, g)
+    np.testing.assert_array_equal(q[0, g:2 * g], codes_want)
+    assert not q[0, :g].any() and not q[0, 2 * g:].any()
+    assert float(s[0]) == s_want
+    assert abs(float(s[0]) - a / (math.sqrt(g) * 127)) <= float(ulp32(s[0]))
+
+
+# ---------------------------------------------------------------------------
+# Pinned elementary functions (exhaustive where the domain is small)
+# ---------------------------------------------------------------------------
+def all_bf16_finite():
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = (b.astype(np.uint32) << 16).view(np.float32)
+    keep = np.isfinite(f)
+    return b[keep], f[keep]
+
+
+def test_exp_neg_within_2ulp_on_all_bf16_arguments(orc):
+    _, f = all_bf16_finite()
+    t = f[(f >= -80) & (f <= 80)]
+    y = orc.exp_neg(t)
+    ref = np.exp(-t.astype(np.float64))
+    assert (np.abs(y - ref) / ulp32(ref)).max() <= 2.0
+
+
+def test_rcp_exhaustive_on_one_binade(orc):
+    """All 2^23 values of [1, 2): error <= 1 ulp against 1/d in float64."""
+    d = (np.arange(1 << 23, dtype=np.uint32) | np.uint32(127 << 23)).view(np.float32)
+    y = orc.rcp(d)
+    ref = 1.0 / d.astype(np.float64)
+    assert (np.abs(y - ref) / ulp32(ref)).max() <= 1.0
+
+
+def test_rcp_scales_exactly_across_binades(orc):
+    """The seed and Newton steps commute with powers of two, so checking one
+    binade covers [1, 2^116]; confirm on samples of other binades."""
+    rng = np.random.default_rng(3)
+    d = (rng.integers(0, 1 << 23, 4096).astype(np.uint32) | np.uint32(127 << 23)).view(np.float32)
+    y = orc.rcp(d)
+    for e in (1, 7, 40, 80, 116):
+        np.testing.assert_array_equal(orc.rcp(np.ldexp(d, e)), np.ldexp(y, -e))
+
+
+def test_silu_exhaustive_over_bf16(orc):
+    b, f = all_bf16_finite()
+    y = orc.silu_bf16(b)
+    g = f.astype(np.float64)
+    inside = np.abs(g) < 80
+    ref = g[inside] / (1 + np.exp(-g[inside]))
+    err = np.abs(y[inside] - ref) / np.maximum(ulp32(ref), np.spacing(np.float32(0)))
+    assert err.max() <= 4.0
+    big = g >= 80
+    np.testing.assert_array_equal(y[big], f[big])                  # silu(g) = g
+    neg = g <= -80
+    s80 = orc.silu_bf16(np.array([0xC2A0], dtype=np.uint16))[0]     # silu(-80)
+    assert -2e-33 < s80 < 0 and np.all(y[neg] == s80)
+    assert orc.silu_bf16(np.array([0, 0x8000], dtype=np.uint16)).tolist() == [0.0, 0.0]
+
+
+# ---------------------------------------------------------------------------
+# Quantizer
+# ---------------------------------------------------------------------------
+def test_quant_ties_golden(orc):
+    rows = read_golden("quant_ties_g1.txt")
+    g = int(rows[0][0])
+    x = np.array([float.fromhex(t) for t in rows[1]], dtype=np.float32)
+    want = np.array([int(t) for t in rows[2]], dtype=np.int8)
+    s_want = float.fromhex(rows[3][0])
+    q, s = orc.act_quant(W.to_bf16_bits(x[None, :]), 0, g)
+    np.testing.assert_array_equal(q[0], want)
+    assert float(s[0]) == s_want
+
+
+@pytest.mark.parametrize("g", [1, 64, 128, 256])
+def test_quant_invariants(orc, g):
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((64, 4 * 256)).astype(np.float32)
+    x[:, [5, 300, 901]] *= 20
+    xb = W.to_bf16_bits(x)
+    q, s = orc.act_quant(xb, 0, g)
+    u = orc.act_rotate(xb, 0, g).astype(np.float64)
+    amax = np.abs(u).max(axis=1)
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    assert q.min() >= -127
+    # codes round 127 u / amax to the nearest integer (exact maths, within the
+    # rounding of r = 127/amax: |u r - 127 u/amax| < 127 * 2^-23)
+    z = 127 * u / amax[:, None]
+    assert np.abs(z - q).max() <= 0.5 + 127 * 2.0 ** -23
+    # scale = amax(x_rot) / 127 with x_rot = u / sqrt(g)
+    s_ref = amax / math.sqrt(g) / 127
+    assert np.all(np.abs(s - s_ref) <= 1.5 * ulp32(s_ref))
+
+
+def test_quant_all_zero_row(orc):
+    x = np.zeros((3, 256), dtype=np.uint16)
+    x[1, 7] = 0x3F80          # 1.0 in one row only
+    q, s = orc.act_quant(x, 0, 128)
+    assert s[0] == 0 and s[2] == 0 and not q[0].any() and not q[2].any()
+    assert s[1] > 0 and np.abs(q[1]).max() == 127
+
+
+def test_group_one_is_textbook_w8a8(orc):
+    """g = 1: no rotation, so the quantizer is textbook per-token symmetric
+    INT8: round(x / (amax/127)).  Codes agree except where 127 x / amax lies
+    within 1e-5 of a half-integer (the one rounding of r)."""
+    rng = np.random.default_rng(5)
+    x = W.to_bf16_bits(rng.standard_normal((32, 512)).astype(np.float32))
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    q, s = orc.act_quant(x, 0, 1)
+    amax = np.abs(xf).max(axis=1, keepdims=True)
+    z = xf / (amax / 127)
+    ref = np.rint(z)
+    near_tie = np.abs(np.abs(z - np.floor(z)) - 0.5) < 1e-5
+    assert np.all((q == ref) | near_tie)
+    assert near_tie.mean() < 1e-2      # BF16 inputs make exact ties fairly common
+
+
+def test_divisibility_contract(orc):
+    """sglang PR #35994 report: input size must be divisible by the group."""
+    with pytest.raises(ValueError):
+        orc.weight_prep(np.zeros((4, 192), np.float32), 128)
+
+
+# ---------------------------------------------------------------------------
+# GEMM and epilogue
+# ---------------------------------------------------------------------------
+def test_gemm_i32_matches_int64_matmul(orc):
+    rng = np.random.default_rng(6)
+    xq = rng.integers(-127, 128, size=(37, 384), dtype=np.int8)
+    wq = rng.integers(-127, 128, size=(53, 384), dtype=np.int8)
+    ref = xq.astype(np.int64) @ wq.astype(np.int64).T
+    np.testing.assert_array_equal(orc.gemm_i32(xq, wq), ref)
+
+
+def test_gemm_i32_extremes(orc):
+    k = 4096
+    xq = np.full((2, k), -127, np.int8)
+    wq = np.stack([np.full(k, -127, np.int8), np.full(k, 127, np.int8)])
+    np.testing.assert_array_equal(orc.gemm_i32(xq, wq),
+                                  [[127 * 127 * k, -127 * 127 * k]] * 2)
+
+
+def test_bf16_rounding_matches_torch(orc):
+    import torch
+    rng = np.random.default_rng(7)
+    f = np.concatenate([
+        rng.standard_normal(100000).astype(np.float32) * 1e3,
+        # exact ties between two BF16 values, even and odd low bit
+        ((np.arange(256, dtype=np.uint32) << 16) | 0x8000 | (0x3F80 << 16)).view(np.float32),
+    ])
+    want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(orc.f32_to_bf16(f), want)
+
+
+def test_dequant_matches_numpy_float32(orc):
+    import torch
+    rng = np.random.default_rng(8)
+    acc = rng.integers(-(1 << 28), 1 << 28, size=(33, 65), dtype=np.int32)
+    sx = (rng.random(33) * 1e-2).astype(np.float32)
+    sw = (rng.random(65) * 1e-3).astype(np.float32)
+    y32 = (acc.astype(np.float32) * sx[:, None]) * sw[None, :]
+    want = torch.from_numpy(y32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(orc.dequant(acc, sx, sw), want)
+
+
+# ---------------------------------------------------------------------------
+# Method-level pins
+# ---------------------------------------------------------------------------
+def test_rotation_identity_before_quantization(orc):
+    """comfy-kitchen PR #277, "The key observation": x W^T = x_rot W_rot^T."""
+    rng = np.random.default_rng(9)
+    g = 128
+    x = rng.standard_normal((16, 512)).astype(np.float32)
+    w = (0.02 * rng.standard_normal((48, 512))).astype(np.float32)
+    c = orc.norm_const(g)
+    xr = orc.fwht(x, g) * c
+    wr = orc.fwht(w, g) * c
+    y = x.astype(np.float64) @ w.astype(np.float64).T
+    y_rot = xr.astype(np.float64) @ wr.astype(np.float64).T
+    assert np.linalg.norm(y - y_rot) / np.linalg.norm(y) < 1e-5
+
+
+def test_row_norm_invariance(orc):
+    """sglang PR #35994 report, review notes: the rotation keeps each weight
+    row's norm, which the pages use to match rows across checkpoints."""
+    rng = np.random.default_rng(10)
+    g = 128
+    w = (0.02 * rng.standard_normal((64, 1024))).astype(np.float32)
+    wr = orc.fwht(w, g).astype(np.float64) * float(orc.norm_const(g))
+    n0 = np.linalg.norm(w.astype(np.float64), axis=1)
+    assert (np.abs(np.linalg.norm(wr, axis=1) - n0) / n0).max() < 1e-6
+    q, s = orc.weight_prep(w, g)
+    deq = q.astype(np.float64) * s.astype(np.float64)[:, None]
+    assert (np.abs(np.linalg.norm(deq, axis=1) - n0) / n0).max() < 5e-3
+
+
+def test_brute_force_tiny(orc):
+    """Tiny case in float64 with the dense H: codes agree except at near-ties,
+    and the BF16 output agrees to BF16 rounding."""
+    rng = np.random.default_rng(11)
+    g, m, k, n = 8, 6, 32, 10
+    x32 = rng.standard_normal((m, k)).astype(np.float32)
+    x32[:, 3] *= 20
+    xb = W.to_bf16_bits(x32)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    hd = np.kron(np.eye(k // g), sylvester_kron(g) / math.sqrt(g))
+
+    def quant64(v):
+        amax = np.abs(v).max(axis=1, keepdims=True)
+        z = 127 * v / amax
+        return np.rint(z), (amax / 127)[:, 0], z
+
+    qx_ref, sx_ref, zx = quant64(xf @ hd)
+    qw_ref, sw_ref, zw = quant64(w.astype(np.float64) @ hd.T)
+    qx, sx = orc.act_quant(xb, 0, g)
+    qw, sw = orc.weight_prep(w, g)
+
+    def tie(z):
+        return np.abs(np.abs(z - np.floor(z)) - 0.5) < 1e-4
+    assert np.all((qx == qx_ref) | tie(zx)) and np.all((qw == qw_ref) | tie(zw))
+    np.testing.assert_allclose(sx, sx_ref, rtol=3e-7)
+    np.testing.assert_allclose(sw, sw_ref, rtol=3e-7)
+    y = orc.int8_linear(xb, 0, qw, sw, g)
+    y_ref = (qx.astype(np.float64) @ qw.astype(np.float64).T) * sx_ref[:, None] * sw_ref[None, :]
+    yf = (y.astype(np.uint32) << 16).view(np.float32)
+    np.testing.assert_allclose(yf, y_ref, rtol=2 ** -8, atol=1e-30)
+
+
+def test_packed_gate_up_equals_separate_projections(orc):
+    """sglang PR #44196, "Accuracy Tests": the stacked [gate | up] GEMM does
+    the same per-column arithmetic as the two separate projections."""
+    rng = np.random.default_rng(12)
+    g = 128
+    xb = W.to_bf16_bits(rng.standard_normal((20, 256)).astype(np.float32))
+    wg = (0.02 * rng.standard_normal((64, 256))).astype(np.float32)
+    wu = (0.02 * rng.standard_normal((64, 256))).astype(np.float32)
+    qg, sg = orc.weight_prep(wg, g)
+    qu, su = orc.weight_prep(wu, g)
+    qgu, sgu = orc.weight_prep(np.concatenate([wg, wu]), g)
+    y = orc.int8_linear(xb, 0, qgu, sgu, g)
+    np.testing.assert_array_equal(y[:, :64], orc.int8_linear(xb, 0, qg, sg, g))
+    np.testing.assert_array_equal(y[:, 64:], orc.int8_linear(xb, 0, qu, su, g))
+
+
+def test_accuracy_class_tiny_workload(orc):
+    """Relative L2 against the unrotated, unquantized float64 product sits in
+    the ~1% class the pages report (0.885% to 1.46%)."""
+    w = W.WORKLOADS["c1"]
+    d = W.linear_inputs(w)
+    qw, sw = orc.weight_prep(d["w"], w.group)
+    y = orc.int8_linear(d["x"], 0, qw, sw, w.group)
+    e = orc.rel_l2(y, orc.reference_linear_f64(d["x"], 0, d["w"]))
+    assert 0.003 < e < 0.03, e
+
+
+def test_fused_swiglu_not_worse_than_eager(orc):
+    """sglang PR #44196, "Accuracy Tests": keeping silu(gate)*up in FP32 is no
+    worse against the FP32 reference than rounding it to BF16 first."""
+    w = W.WORKLOADS["c2"]
+    d = W.linear_inputs(w, m=128)
+    qw, sw = orc.weight_prep(d["w"], w.group)
+    ref = orc.reference_linear_f64(d["x"], 1, d["w"])
+    fused = orc.int8_linear(d["x"], 1, qw, sw, w.group)
+    eager_a = orc.eager_swiglu_bf16(d["x"])
+    eager = orc.int8_linear(eager_a, 0, qw, sw, w.group)
+    e_f, e_e = orc.rel_l2(fused, ref), orc.rel_l2(eager, ref)
+    assert 0.003 < e_f < 0.03
+    assert e_f <= e_e * 1.02, (e_f, e_e)

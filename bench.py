@@ -1,0 +1,255 @@
+"""Benchmark: effective INT8 TOPS of the ConvRot int8_linear (+ fused SwiGLU)
+hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input, by
+default the SwiGLU MLP block (workload c5: M=4096 tokens, hidden 3072,
+intermediate 12288, group 128): activation quant -> packed [gate | up] INT8
+GEMM -> fused SwiGLU + rotation + quant -> down INT8 GEMM.  The step calls the
+four stage entry points of the C ABI in the order ck_swiglu_mlp uses (a test
+checks the two agree bit for bit) so that each kernel can be bracketed by HIP
+events on the stream it runs on.  Weight preparation happens once, before
+timing, as at model load.  Inputs are resident in HBM before the timed region.
+
+Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
+[--workload c1..c5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective INT8 TOPS of ConvRot int8_linear(+SwiGLU), % of MI355X INT8 peak"
+PEAK_INT8_TOPS = 5000.0        # MI355X dense INT8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of the workload the CPU oracle runs (0: automatic)")
+    return ap.parse_args()
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "quant.hip", "ck_device.hpp"):
+        with open(os.path.join(ROOT, "swiglu_mlp_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, per_launch_units: float):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
+    only if they were taken on the current kernel sources."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha") != kernel_source_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); the sharding design is described in DESIGN.md",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import swiglu_mlp_amd as ck
+    from swiglu_mlp_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = ck.lib()
+    print(f"[bench] workload {wl.name}: {wl.desc}", file=sys.stderr, flush=True)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    g = wl.group
+    if wl.kind == "mlp":
+        d = W.mlp_inputs(wl)
+        m, h, inter = wl.m, wl.k, wl.n
+        x = to_dev(d["x"].view(np.int16)).view(torch.bfloat16)
+        wgu, sgu = ck.ck_weight_prep(to_dev(d["w_gu"]), g)
+        wd, sd = ck.ck_weight_prep(to_dev(d["w_down"]), g)
+        xq = torch.empty((m, h), dtype=torch.int8, device=dev)
+        sx = torch.empty((m,), dtype=torch.float32, device=dev)
+        t1 = torch.empty((m, 2 * inter), dtype=torch.bfloat16, device=dev)
+        hq = torch.empty((m, inter), dtype=torch.int8, device=dev)
+        sh = torch.empty((m,), dtype=torch.float32, device=dev)
+        y = torch.empty((m, h), dtype=torch.bfloat16, device=dev)
+        # (name, callable, algorithmic ops, algorithmic HBM bytes, bound)
+        stages = [
+            ("x_quant", lambda s: L.ck_act_quant(x.data_ptr(), h, m, h, 0, g, xq.data_ptr(),
+                                                 sx.data_ptr(), s),
+             0, m * h * 2 + m * h + m * 4, "hbm"),
+            ("gate_up_gemm", lambda s: L.ck_int8_gemm_bf16(xq.data_ptr(), sx.data_ptr(),
+                                                           wgu.data_ptr(), sgu.data_ptr(),
+                                                           m, 2 * inter, h, t1.data_ptr(), s),
+             2 * m * 2 * inter * h, m * h + 2 * inter * h + m * 2 * inter * 2, "mfma"),
+            ("swiglu_quant", lambda s: L.ck_act_quant(t1.data_ptr(), 2 * inter, m, inter, 1, g,
+                                                      hq.data_ptr(), sh.data_ptr(), s),
+             0, m * inter * 4 + m * inter + m * 4, "hbm"),
+            ("down_gemm", lambda s: L.ck_int8_gemm_bf16(hq.data_ptr(), sh.data_ptr(),
+                                                        wd.data_ptr(), sd.data_ptr(),
+                                                        m, h, inter, y.data_ptr(), s),
+             2 * m * h * inter, m * inter + h * inter + m * h * 2, "mfma"),
+        ]
+    else:
+        d = W.linear_inputs(wl)
+        m, k, n = wl.m, wl.k, wl.n
+        ldx = 2 * k if wl.act == 1 else k
+        x = to_dev(d["x"].view(np.int16)).view(torch.bfloat16)
+        wq, sw = ck.ck_weight_prep(to_dev(d["w"]), g)
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+        sx = torch.empty((m,), dtype=torch.float32, device=dev)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        stages = [
+            ("act_quant", lambda s: L.ck_act_quant(x.data_ptr(), ldx, m, k, wl.act, g,
+                                                   xq.data_ptr(), sx.data_ptr(), s),
+             0, m * ldx * 2 + m * k + m * 4, "hbm"),
+            ("gemm", lambda s: L.ck_int8_gemm_bf16(xq.data_ptr(), sx.data_ptr(), wq.data_ptr(),
+                                                   sw.data_ptr(), m, n, k, y.data_ptr(), s),
+             2 * m * n * k, m * k + n * k + m * n * 2, "mfma"),
+        ]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def run_step(events=None):
+        for j, st in enumerate(stages):
+            if events is not None:
+                events[j][0].record(stream)
+            rc = st[1](sptr)
+            if rc != 0:
+                raise RuntimeError(f"{st[0]} returned {rc}: {L.ck_status_str(rc).decode()}")
+            if events is not None:
+                events[j][1].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in stages] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        run_step(ev[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K
+
+    kern_us = {}
+    for j, st in enumerate(stages):
+        kern_us[st[0]] = 1000.0 * sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(K)) / K
+    value = wl.int8_ops / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: the one with the largest share of the step
+    dom = max(range(len(stages)), key=lambda j: kern_us[stages[j][0]])
+    name, _, ops, nbytes, bound = stages[dom]
+    t_s = kern_us[name] * 1e-6
+    if bound == "mfma":
+        achieved, peak, unit = ops / t_s / 1e12, PEAK_INT8_TOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = nbytes / t_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": load_traffic(name, 1.0),
+                "kernel": name, "avg_us": round(kern_us[name], 2)}
+    stage_roofline = {}
+    for st in stages:
+        ts = kern_us[st[0]] * 1e-6
+        if st[4] == "mfma":
+            stage_roofline[st[0]] = {"us": round(kern_us[st[0]], 2),
+                                     "TOPS": round(st[2] / ts / 1e12, 1),
+                                     "frac_int8_peak": round(st[2] / ts / 1e12 / PEAK_INT8_TOPS, 4)}
+        else:
+            stage_roofline[st[0]] = {"us": round(kern_us[st[0]], 2),
+                                     "GBs": round(st[3] / ts / 1e9, 1),
+                                     "frac_hbm_peak": round(st[3] / ts / 1e9 / PEAK_HBM_GBS, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, d, args.cpu_rows)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.desc}", "m": wl.m, "k": wl.k, "n": wl.n,
+                   "group": g, "int8_ops_per_step": wl.int8_ops, "parallelism": "single-gpu"},
+        "frac_of_int8_peak": round(value / PEAK_INT8_TOPS, 4),
+        "roofline": roofline, "stages": stage_roofline, "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, d, rows):
+    """The CPU oracle, as it stands, on a bounded row sample of the same step."""
+    import numpy as np
+    import oracle
+    g = wl.group
+    threads = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    if wl.kind == "mlp":
+        gq, gs = oracle.weight_prep(d["w_gu"], g)
+        dq, ds = oracle.weight_prep(d["w_down"], g)
+
+        def run(r):
+            oracle.swiglu_mlp(np.ascontiguousarray(d["x"][:r]), gq, gs, dq, ds, g)
+        ops_per_row = 6 * wl.k * wl.n
+    else:
+        wq, sw = oracle.weight_prep(d["w"], g)
+
+        def run(r):
+            oracle.int8_linear(np.ascontiguousarray(d["x"][:r]), wl.act, wq, sw, g)
+        ops_per_row = 2 * wl.k * wl.n
+    if not rows:
+        # calibrate on a few rows, then size the sample to ~15 s of CPU work
+        probe = min(wl.m, 32)
+        t0 = time.perf_counter()
+        run(probe)
+        per_row = (time.perf_counter() - t0) / probe
+        rows = int(min(wl.m, max(probe, 15.0 / max(per_row, 1e-9))))
+    r = rows
+    t0 = time.perf_counter()
+    run(r)
+    dt = time.perf_counter() - t0
+    ops = ops_per_row * r
+    return {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {r} of {wl.m} rows of {wl.name}, whole step "
+                      f"(quant + int GEMM + epilogue), {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * ck.h -- C ABI of the MI355X (gfx950) ConvRot INT8 linear and SwiGLU MLP.
+ *
+ * What the library computes (sources cited by page title and section):
+ *
+ *  - comfy-kitchen PR #277 "Add FP16 tensor-core fallback for int8_linear on
+ *    devices without INT8 tensor cores", section "The key observation": the
+ *    weight is stored pre-rotated, W_rot = W H^T; the activation is rotated
+ *    online, x_rot = x H; the GEMM runs in the rotated basis, so
+ *    y = x W^T = x_rot W_rot^T and no inverse rotation is applied to y.  The
+ *    activation is quantized to INT8 on the same grid as the weight.  Section
+ *    "Measured results": INT8 x INT8 products are accumulated in int32.
+ *  - sglang PR #35994 report "[diffusion] Load serialized Comfy ConvRot INT8
+ *    DiTs", key source excerpts: INT8 weights [out_features, in_features] with
+ *    an F32 per-output-channel scale [out_features, 1] (per_channel=True,
+ *    convrot=True); in_features must be divisible by the rotation group.
+ *  - sglang PR #44196 (comfy_kitchen_swiglu_mlp), section "Motivation": the MLP
+ *    runs as one packed [gate | up] int8_linear and a down projection whose
+ *    quantizer applies the SwiGLU (input_act="swiglu"); section "Accuracy
+ *    Tests": silu(gate) * up is kept in FP32, not rounded to BF16 first.
+ *
+ * H is block-diagonal over contiguous groups of `group` input channels, each
+ * block the normalised Sylvester Hadamard matrix of that size.
+ *
+ * Numerics (identical, bit for bit, to the CPU oracle shipped with the tests):
+ *  - rotation: unnormalised fast Walsh-Hadamard transform per group, strides
+ *    1, 2, 4, ... ascending, FP32; the 1/sqrt(group) factor enters the scale;
+ *  - per row: A = max |u|; scale = fl(fl(A * fl(1/sqrt(group))) / 127);
+ *    codes = round-half-even(u * fl(127 / A)) of the exact product, in
+ *    [-127, 127]; an all-zero row gets scale 0 and zero codes;
+ *  - SwiGLU: a = silu(gate) * up in FP32 with a fixed exp/reciprocal procedure;
+ *  - output: y = bf16_rne(fl(fl(f32(acc) * x_scale[m]) * w_scale[n])).
+ *
+ * Conventions shared by every entry point:
+ *  - All pointers are DEVICE pointers (HBM) except where stated; tensors are
+ *    row-major with a contiguous last dimension.  BF16 values are passed as
+ *    their 16-bit patterns (uint16_t).  W is [out_features, in_features]
+ *    (torch.nn.Linear layout).
+ *  - Ownership: the caller allocates and frees every buffer, including the
+ *    workspace.  The library never allocates, frees or synchronises.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues kernels on that stream and returns; results are visible after the
+ *    caller synchronises the stream.
+ *  - Errors: every argument is checked on the host before anything is
+ *    enqueued; a failed check returns a non-zero ck_status and enqueues
+ *    nothing.  A failed launch returns CK_EHIP.  A fault inside a kernel
+ *    surfaces at the caller's next synchronisation.
+ *  - Shapes: m >= 0 (m == 0 is a no-op that returns CK_OK), n >= 0 (n == 0 is
+ *    a no-op), k >= 1.  group is a power of two in [1, 256] dividing k; k is a
+ *    multiple of 64 and at most CK_MAX_K; n is a multiple of 16.  Pointers are
+ *    16-byte aligned; leading dimensions are multiples of 8 elements.
+ */
+#ifndef CK_H
+#define CK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ck_status {
+    CK_OK = 0,
+    CK_EINVAL = 1,       /* null pointer, unknown act, misaligned pointer      */
+    CK_ESHAPE = 2,       /* negative size, k % group, k % 64, n % 16, ld < k   */
+    CK_EUNSUPPORTED = 3, /* group not a power of two <= 256, k > CK_MAX_K      */
+    CK_EWORKSPACE = 4,   /* workspace too small or null                        */
+    CK_EHIP = 5          /* the HIP runtime reported an error at launch        */
+} ck_status;
+
+typedef enum ck_act {
+    CK_ACT_NONE = 0,     /* a = x                                              */
+    CK_ACT_SWIGLU = 1    /* a = silu(x[:, 0:k]) * x[:, k:2k]  (gate, then up)  */
+} ck_act;
+
+/* Largest in_features: 127 * 127 * k must fit an int32 accumulator and one
+ * activation row (k FP32 values) must fit the quantizer's LDS. */
+#define CK_MAX_K 32768
+
+/* Library version string (static storage). */
+const char *ck_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char *ck_status_str(ck_status s);
+
+/* Weight preparation (done once per weight, at load).
+ * Source: sglang PR #35994 report, key source excerpts (online quantization
+ * with per_channel=True, convrot=True, stochastic_rounding=0, giving an I8
+ * weight and an F32 [out_features, 1] scale); comfy-kitchen PR #277, "The key
+ * observation" (the stored matrix is W H^T).
+ *   w        [n, k] FP32, read
+ *   w_q      [n, k] int8, written: codes of W H^T, row-quantized
+ *   w_scale  [n]    FP32, written: one scale per output row
+ * Errors: CK_EINVAL on null pointers; CK_ESHAPE/CK_EUNSUPPORTED on shapes. */
+ck_status ck_weight_prep(const float *w, int64_t n, int64_t k, int32_t group,
+                         int8_t *w_q, float *w_scale, void *stream);
+
+/* Activation quantizer: optional SwiGLU, rotation, per-token INT8.
+ * Source: comfy-kitchen PR #277, "The key observation" (x_rot = x H, INT8 on
+ * the weight's grid); sglang PR #44196, "Motivation" and "Accuracy Tests"
+ * (input_act="swiglu", silu(gate) * up in FP32).
+ *   x        [m, ldx] BF16, read.  act == CK_ACT_NONE: row r uses x[r, 0:k],
+ *            ldx >= k.  act == CK_ACT_SWIGLU: gate = x[r, 0:k],
+ *            up = x[r, k:2k], ldx >= 2k.
+ *   x_q      [m, k] int8, written (row stride k)
+ *   x_scale  [m]    FP32, written */
+ck_status ck_act_quant(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,
+                       int32_t act, int32_t group, int8_t *x_q, float *x_scale,
+                       void *stream);
+
+/* ConvRot int8_linear: y = dequant(act_quant(x) . w_q^T).
+ * Source: comfy-kitchen PR #277, "The key observation" and "Measured results";
+ * sglang PR #44196, "Motivation" (int8_linear(..., input_act="swiglu")).
+ *   x, ldx, act   as ck_act_quant
+ *   w_q      [n, k] int8 from ck_weight_prep, read
+ *   w_scale  [n]    FP32 from ck_weight_prep, read
+ *   y        [m, n] BF16, written (row stride n)
+ *   workspace  device buffer of at least ck_int8_linear_workspace_size(m, k)
+ *            bytes, 256-byte aligned; clobbered (holds x_q and x_scale). */
+ck_status ck_int8_linear(const uint16_t *x, int64_t ldx, int32_t act,
+                         const int8_t *w_q, const float *w_scale, int64_t m,
+                         int64_t n, int64_t k, int32_t group, uint16_t *y,
+                         void *workspace, size_t workspace_bytes, void *stream);
+size_t ck_int8_linear_workspace_size(int64_t m, int64_t k);
+
+/* The INT8 GEMM with its dequant epilogue alone (the second half of
+ * ck_int8_linear), for callers that hold quantized activations.
+ *   x_q [m, k] int8, x_scale [m] FP32, w_q [n, k] int8, w_scale [n] FP32 read;
+ *   y [m, n] BF16 written. */
+ck_status ck_int8_gemm_bf16(const int8_t *x_q, const float *x_scale,
+                            const int8_t *w_q, const float *w_scale, int64_t m,
+                            int64_t n, int64_t k, uint16_t *y, void *stream);
+
+/* SwiGLU MLP block: y = int8_linear(int8_linear(x, W_gu), W_down, swiglu).
+ * Source: sglang PR #44196, "Motivation" and "Modifications" (one packed
+ * [gate | up] GEMM whose gate rows come first, then the down projection that
+ * applies silu(gate) * up inside its quantizer); "Accuracy Tests" (the stacked
+ * GEMM does the same per-column arithmetic as two separate projections).
+ *   x      [m, h]  BF16, read
+ *   w_gu   [2i, h] int8 + s_gu [2i] FP32: rows 0..i-1 gate, i..2i-1 up
+ *   w_down [h, i]  int8 + s_down [h] FP32
+ *   y      [m, h]  BF16, written
+ *   workspace  at least ck_swiglu_mlp_workspace_size(m, h, i) bytes,
+ *          256-byte aligned; clobbered (x codes/scales, the [m, 2i] BF16
+ *          gate|up output, its codes/scales). */
+ck_status ck_swiglu_mlp(const uint16_t *x, const int8_t *w_gu, const float *s_gu,
+                        const int8_t *w_down, const float *s_down, int64_t m,
+                        int64_t h, int64_t i, int32_t group, uint16_t *y,
+                        void *workspace, size_t workspace_bytes, void *stream);
+size_t ck_swiglu_mlp_workspace_size(int64_t m, int64_t h, int64_t i);
+
+/* ---- test hooks: the same device code with its intermediate exposed ---- */
+
+/* Raw int32 accumulators acc[m, n] = sum_k x_q[m, k] * w_q[n, k] from the
+ * production GEMM kernels (comfy-kitchen PR #277, "Measured results"). */
+ck_status ck_int8_gemm_i32(const int8_t *x_q, const int8_t *w_q, int64_t m,
+                           int64_t n, int64_t k, int32_t *acc, void *stream);
+
+/* FP32 silu of n BF16 gate values, by the quantizer's own device function
+ * (sglang PR #44196, "Accuracy Tests": silu kept in FP32). */
+ck_status ck_silu_f32(const uint16_t *gate, int64_t n, float *out, void *stream);
+
+/* Unnormalised rotated activation u [m, k] FP32 (before quantization), by the
+ * quantizer's own device code (comfy-kitchen PR #277, "The key observation"). */
+ck_status ck_act_rotate_f32(const uint16_t *x, int64_t ldx, int64_t m,
+                            int64_t k, int32_t act, int32_t group, float *u,
+                            void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CK_H */

@@ -1,1 +1,268 @@
-"""MI355X-native ConvRot INT8 linear + fused SwiGLU MLP (binding filled in below)."""
+"""MI355X (gfx950) ConvRot INT8 linear and SwiGLU MLP: Python binding.
+
+This module only marshals arguments: it checks dtypes and shapes, takes device
+pointers and the current HIP stream from torch tensors, and calls the C ABI of
+``libck_convrot.so`` (declared in ``include/ck.h``).  Every step of the path
+runs in that library's HIP kernels; there is no fallback.  If the library is
+missing, importing any entry point raises.
+
+Entry points keep the C names:
+
+* ``ck_weight_prep(w, group)``           -> (w_q int8 [n, k], w_scale f32 [n, 1])
+* ``ck_act_quant(x, act, group, k=None)`` -> (x_q int8 [m, k], x_scale f32 [m, 1])
+* ``ck_int8_linear(x, w_q, w_scale, group, input_act=None)`` -> y bf16 [m, n]
+* ``ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale)``  -> y bf16 [m, n]
+* ``ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group)`` -> y bf16 [m, h]
+* test hooks ``ck_int8_gemm_i32``, ``ck_silu_f32``, ``ck_act_rotate_f32``
+
+Shapes and error behaviour follow sglang PR #35994 report, key source excerpts:
+an INT8 weight is 2-D ``[out_features, in_features]`` with an F32
+``[out_features, 1]`` scale, and in_features must be divisible by the group
+size; violations raise ``ValueError`` before anything is launched.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libck_convrot.so")
+
+CK_ACT_NONE, CK_ACT_SWIGLU = 0, 1
+_STATUS = {0: "CK_OK", 1: "CK_EINVAL", 2: "CK_ESHAPE", 3: "CK_EUNSUPPORTED",
+           4: "CK_EWORKSPACE", 5: "CK_EHIP"}
+
+
+class CKError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libck_convrot.so (after torch, so both use one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        import torch  # noqa: F401  -- loads torch's HIP runtime first
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m swiglu_mlp_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        sig = {
+            "ck_weight_prep": [p, i64, i64, i32, p, p, p],
+            "ck_act_quant": [p, i64, i64, i64, i32, i32, p, p, p],
+            "ck_int8_linear": [p, i64, i32, p, p, i64, i64, i64, i32, p, p, sz, p],
+            "ck_int8_gemm_bf16": [p, p, p, p, i64, i64, i64, p, p],
+            "ck_swiglu_mlp": [p, p, p, p, p, i64, i64, i64, i32, p, p, sz, p],
+            "ck_int8_gemm_i32": [p, p, i64, i64, i64, p, p],
+            "ck_silu_f32": [p, i64, p, p],
+            "ck_act_rotate_f32": [p, i64, i64, i64, i32, i32, p, p],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.ck_int8_linear_workspace_size.argtypes = [i64, i64]
+        L.ck_int8_linear_workspace_size.restype = sz
+        L.ck_swiglu_mlp_workspace_size.argtypes = [i64, i64, i64]
+        L.ck_swiglu_mlp_workspace_size.restype = sz
+        L.ck_status_str.argtypes = [ctypes.c_int]
+        L.ck_status_str.restype = ctypes.c_char_p
+        L.ck_version.argtypes = []
+        L.ck_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise CKError(name, st, lib().ck_status_str(st).decode())
+
+
+def _stream(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t, dtype, ndim, what):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be on a GPU, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{what} needs dtype {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{what} needs a {ndim}D tensor, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+def _scale(s, rows, what):
+    """Accept [rows, 1] (the serialized row-scale layout) or [rows]."""
+    import torch
+    if s.dim() == 2:
+        if tuple(s.shape) != (rows, 1):
+            raise ValueError(f"{what} needs scale shape ({rows}, 1), got {tuple(s.shape)}")
+    else:
+        _need(s, torch.float32, 1, what)
+        if s.shape[0] != rows:
+            raise ValueError(f"{what} needs {rows} scales, got {s.shape[0]}")
+    _need(s, torch.float32, s.dim(), what)
+    return s
+
+
+def _check_group(k, group):
+    if k % group:
+        raise ValueError(f"in_features ({k}) must be divisible by group_size {group}")
+
+
+def _act_code(input_act):
+    if input_act in (None, "none", CK_ACT_NONE):
+        return CK_ACT_NONE
+    if input_act in ("swiglu", CK_ACT_SWIGLU):
+        return CK_ACT_SWIGLU
+    raise ValueError(f"unknown input_act {input_act!r}")
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def ck_weight_prep(w, group: int = 128):
+    import torch
+    _need(w, torch.float32, 2, "weight")
+    n, k = w.shape
+    _check_group(k, group)
+    w_q = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    w_scale = torch.empty((n, 1), dtype=torch.float32, device=w.device)
+    _call("ck_weight_prep", w.data_ptr(), n, k, group, w_q.data_ptr(), w_scale.data_ptr(),
+          _stream(w))
+    return w_q, w_scale
+
+
+def ck_act_quant(x, input_act=None, group: int = 128, k: int | None = None):
+    import torch
+    _need(x, torch.bfloat16, 2, "activation")
+    act = _act_code(input_act)
+    m, ldx = x.shape
+    if k is None:
+        k = ldx // 2 if act == CK_ACT_SWIGLU else ldx
+    _check_group(k, group)
+    x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    x_scale = torch.empty((m, 1), dtype=torch.float32, device=x.device)
+    _call("ck_act_quant", x.data_ptr(), ldx, m, k, act, group, x_q.data_ptr(),
+          x_scale.data_ptr(), _stream(x))
+    return x_q, x_scale
+
+
+def ck_int8_linear(x, w_q, w_scale, group: int = 128, input_act=None, out=None,
+                   workspace=None):
+    import torch
+    _need(x, torch.bfloat16, 2, "activation")
+    _need(w_q, torch.int8, 2, "weight")
+    n, k = w_q.shape
+    _scale(w_scale, n, "weight_scale")
+    act = _act_code(input_act)
+    m, ldx = x.shape
+    need_ld = 2 * k if act == CK_ACT_SWIGLU else k
+    if ldx != need_ld:
+        raise ValueError(f"activation needs {need_ld} columns for in_features {k}, got {ldx}")
+    _check_group(k, group)
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    ws_bytes = lib().ck_int8_linear_workspace_size(m, k)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    _call("ck_int8_linear", x.data_ptr(), ldx, act, w_q.data_ptr(), w_scale.data_ptr(), m, n, k,
+          group, y.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x))
+    return y
+
+
+def ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, out=None):
+    import torch
+    _need(x_q, torch.int8, 2, "activation codes")
+    _need(w_q, torch.int8, 2, "weight")
+    m, k = x_q.shape
+    n = w_q.shape[0]
+    if w_q.shape[1] != k:
+        raise ValueError(f"in_features mismatch: activation {k}, weight {w_q.shape[1]}")
+    _scale(x_scale, m, "activation scale")
+    _scale(w_scale, n, "weight_scale")
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x_q.device)
+    _call("ck_int8_gemm_bf16", x_q.data_ptr(), x_scale.data_ptr(), w_q.data_ptr(),
+          w_scale.data_ptr(), m, n, k, y.data_ptr(), _stream(x_q))
+    return y
+
+
+def ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group: int = 128, out=None, workspace=None):
+    import torch
+    _need(x, torch.bfloat16, 2, "activation")
+    _need(w_gu, torch.int8, 2, "gate_up weight")
+    _need(w_down, torch.int8, 2, "down weight")
+    m, h = x.shape
+    i2, h2 = w_gu.shape
+    if h2 != h or i2 % 2:
+        raise ValueError(f"gate_up weight needs shape (2*intermediate, {h}), got {tuple(w_gu.shape)}")
+    i = i2 // 2
+    if tuple(w_down.shape) != (h, i):
+        raise ValueError(f"down weight needs shape ({h}, {i}), got {tuple(w_down.shape)}")
+    _scale(s_gu, i2, "gate_up weight_scale")
+    _scale(s_down, h, "down weight_scale")
+    _check_group(h, group)
+    _check_group(i, group)
+    y = out if out is not None else torch.empty((m, h), dtype=torch.bfloat16, device=x.device)
+    ws_bytes = lib().ck_swiglu_mlp_workspace_size(m, h, i)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    _call("ck_swiglu_mlp", x.data_ptr(), w_gu.data_ptr(), s_gu.data_ptr(), w_down.data_ptr(),
+          s_down.data_ptr(), m, h, i, group, y.data_ptr(), workspace.data_ptr(),
+          workspace.numel(), _stream(x))
+    return y
+
+
+def ck_int8_gemm_i32(x_q, w_q):
+    import torch
+    _need(x_q, torch.int8, 2, "activation codes")
+    _need(w_q, torch.int8, 2, "weight")
+    m, k = x_q.shape
+    n = w_q.shape[0]
+    if w_q.shape[1] != k:
+        raise ValueError(f"in_features mismatch: activation {k}, weight {w_q.shape[1]}")
+    acc = torch.empty((m, n), dtype=torch.int32, device=x_q.device)
+    _call("ck_int8_gemm_i32", x_q.data_ptr(), w_q.data_ptr(), m, n, k, acc.data_ptr(),
+          _stream(x_q))
+    return acc
+
+
+def ck_silu_f32(gate):
+    import torch
+    if gate.dtype != torch.bfloat16 or gate.device.type != "cuda" or not gate.is_contiguous():
+        raise ValueError("gate must be a contiguous bf16 GPU tensor")
+    out = torch.empty(gate.shape, dtype=torch.float32, device=gate.device)
+    _call("ck_silu_f32", gate.data_ptr(), gate.numel(), out.data_ptr(), _stream(gate))
+    return out
+
+
+def ck_act_rotate_f32(x, input_act=None, group: int = 128, k: int | None = None):
+    import torch
+    _need(x, torch.bfloat16, 2, "activation")
+    act = _act_code(input_act)
+    m, ldx = x.shape
+    if k is None:
+        k = ldx // 2 if act == CK_ACT_SWIGLU else ldx
+    _check_group(k, group)
+    u = torch.empty((m, k), dtype=torch.float32, device=x.device)
+    _call("ck_act_rotate_f32", x.data_ptr(), ldx, m, k, act, group, u.data_ptr(), _stream(x))
+    return u
+
+
+# short aliases
+weight_prep = ck_weight_prep
+act_quant = ck_act_quant
+int8_linear = ck_int8_linear
+int8_gemm_bf16 = ck_int8_gemm_bf16
+swiglu_mlp = ck_swiglu_mlp

@@ -1,0 +1,208 @@
+// api.hip -- the C ABI declared in include/ck.h: host-side argument checks,
+// workspace carving and kernel dispatch.  No function here allocates, frees or
+// synchronises; all checks complete before anything is enqueued.
+#include "ck.h"
+#include "ck_internal.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool pow2_group(int32_t g) { return g >= 1 && g <= 256 && (g & (g - 1)) == 0; }
+
+// Checks shared by every call that takes an in_features dimension.
+ck_status check_k(int64_t k, int32_t group)
+{
+    if (!pow2_group(group)) return CK_EUNSUPPORTED;
+    if (k < 1) return CK_ESHAPE;
+    if (k > CK_MAX_K) return CK_EUNSUPPORTED;
+    if (k % 64 != 0 || k % group != 0) return CK_ESHAPE;
+    return CK_OK;
+}
+
+ck_status check_act(int32_t act, int64_t ldx, int64_t k)
+{
+    if (act != CK_ACT_NONE && act != CK_ACT_SWIGLU) return CK_EINVAL;
+    const int64_t need = act == CK_ACT_SWIGLU ? 2 * k : k;
+    if (ldx < need || ldx % 8 != 0) return CK_ESHAPE;
+    return CK_OK;
+}
+
+ck_status from_hip(hipError_t e) { return e == hipSuccess ? CK_OK : CK_EHIP; }
+
+#define CK_TRY(expr)                     \
+    do {                                 \
+        const ck_status st_ = (expr);    \
+        if (st_ != CK_OK) return st_;    \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* ck_version(void) { return "ck-convrot 0.1 (gfx950)"; }
+
+const char* ck_status_str(ck_status s)
+{
+    switch (s) {
+        case CK_OK: return "ok";
+        case CK_EINVAL: return "invalid argument (null or misaligned pointer, unknown act)";
+        case CK_ESHAPE: return "bad shape (negative size, k % group, k % 64, n % 16, leading dimension)";
+        case CK_EUNSUPPORTED: return "unsupported (group not a power of two <= 256, or k > CK_MAX_K)";
+        case CK_EWORKSPACE: return "workspace missing or too small";
+        case CK_EHIP: return "HIP runtime error at launch";
+    }
+    return "unknown status";
+}
+
+ck_status ck_weight_prep(const float* w, int64_t n, int64_t k, int32_t group, int8_t* w_q,
+                         float* w_scale, void* stream)
+{
+    CK_TRY(check_k(k, group));
+    if (n < 0) return CK_ESHAPE;
+    if (n == 0) return CK_OK;
+    if (!w || !w_q || !w_scale) return CK_EINVAL;
+    if (!aligned16(w) || !aligned16(w_q)) return CK_EINVAL;
+    return from_hip(ck::launch_quant_rows(2, w, k, n, k, group, w_q, w_scale, nullptr,
+                                          (hipStream_t)stream));
+}
+
+ck_status ck_act_quant(const uint16_t* x, int64_t ldx, int64_t m, int64_t k, int32_t act,
+                       int32_t group, int8_t* x_q, float* x_scale, void* stream)
+{
+    CK_TRY(check_k(k, group));
+    CK_TRY(check_act(act, ldx, k));
+    if (m < 0) return CK_ESHAPE;
+    if (m == 0) return CK_OK;
+    if (!x || !x_q || !x_scale) return CK_EINVAL;
+    if (!aligned16(x) || !aligned16(x_q)) return CK_EINVAL;
+    return from_hip(ck::launch_quant_rows(act == CK_ACT_SWIGLU ? 1 : 0, x, ldx, m, k, group, x_q,
+                                          x_scale, nullptr, (hipStream_t)stream));
+}
+
+size_t ck_int8_linear_workspace_size(int64_t m, int64_t k)
+{
+    if (m <= 0 || k <= 0) return 0;
+    return round_up((size_t)m * (size_t)k) + round_up((size_t)m * sizeof(float));
+}
+
+static ck_status check_gemm_args(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                                 const float* w_scale, int64_t m, int64_t n, int64_t k,
+                                 const void* y, bool need_scales)
+{
+    if (k < 1 || k % 64 != 0) return CK_ESHAPE;
+    if (k > CK_MAX_K) return CK_EUNSUPPORTED;
+    if (m < 0 || n < 0 || n % 16 != 0) return CK_ESHAPE;
+    if (m == 0 || n == 0) return CK_OK;
+    if (!x_q || !w_q || !y) return CK_EINVAL;
+    if (need_scales && (!x_scale || !w_scale)) return CK_EINVAL;
+    if (!aligned16(x_q) || !aligned16(w_q) || !aligned16(y)) return CK_EINVAL;
+    if (need_scales && !aligned16(w_scale)) return CK_EINVAL;
+    return CK_OK;
+}
+
+ck_status ck_int8_gemm_bf16(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
+                            const float* w_scale, int64_t m, int64_t n, int64_t k, uint16_t* y,
+                            void* stream)
+{
+    CK_TRY(check_gemm_args(x_q, x_scale, w_q, w_scale, m, n, k, y, true));
+    if (m == 0 || n == 0) return CK_OK;
+    return from_hip(ck::launch_gemm_bf16(x_q, x_scale, w_q, w_scale, m, n, k, y,
+                                         (hipStream_t)stream));
+}
+
+ck_status ck_int8_gemm_i32(const int8_t* x_q, const int8_t* w_q, int64_t m, int64_t n, int64_t k,
+                           int32_t* acc, void* stream)
+{
+    CK_TRY(check_gemm_args(x_q, nullptr, w_q, nullptr, m, n, k, acc, false));
+    if (m == 0 || n == 0) return CK_OK;
+    return from_hip(ck::launch_gemm_i32(x_q, w_q, m, n, k, acc, (hipStream_t)stream));
+}
+
+ck_status ck_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, const int8_t* w_q,
+                         const float* w_scale, int64_t m, int64_t n, int64_t k, int32_t group,
+                         uint16_t* y, void* workspace, size_t workspace_bytes, void* stream)
+{
+    CK_TRY(check_k(k, group));
+    CK_TRY(check_act(act, ldx, k));
+    if (m < 0 || n < 0 || n % 16 != 0) return CK_ESHAPE;
+    if (m == 0 || n == 0) return CK_OK;
+    if (!x || !w_q || !w_scale || !y) return CK_EINVAL;
+    if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_scale) || !aligned16(y)) return CK_EINVAL;
+    const size_t need = ck_int8_linear_workspace_size(m, k);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
+        return CK_EWORKSPACE;
+    int8_t* xq = static_cast<int8_t*>(workspace);
+    float* sx = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up((size_t)m * k));
+    hipStream_t st = (hipStream_t)stream;
+    CK_TRY(from_hip(ck::launch_quant_rows(act == CK_ACT_SWIGLU ? 1 : 0, x, ldx, m, k, group, xq,
+                                          sx, nullptr, st)));
+    return from_hip(ck::launch_gemm_bf16(xq, sx, w_q, w_scale, m, n, k, y, st));
+}
+
+size_t ck_swiglu_mlp_workspace_size(int64_t m, int64_t h, int64_t i)
+{
+    if (m <= 0 || h <= 0 || i <= 0) return 0;
+    const size_t M = (size_t)m, H = (size_t)h, I = (size_t)i;
+    return round_up(M * H) + round_up(M * 4) + round_up(M * 2 * I * 2) + round_up(M * I) +
+           round_up(M * 4);
+}
+
+ck_status ck_swiglu_mlp(const uint16_t* x, const int8_t* w_gu, const float* s_gu,
+                        const int8_t* w_down, const float* s_down, int64_t m, int64_t h, int64_t i,
+                        int32_t group, uint16_t* y, void* workspace, size_t workspace_bytes,
+                        void* stream)
+{
+    CK_TRY(check_k(h, group));   // stage 1 contracts over h
+    CK_TRY(check_k(i, group));   // stage 2 contracts over i
+    if (m < 0 || h % 16 != 0) return CK_ESHAPE;
+    if (m == 0) return CK_OK;
+    if (!x || !w_gu || !s_gu || !w_down || !s_down || !y) return CK_EINVAL;
+    if (!aligned16(x) || !aligned16(w_gu) || !aligned16(s_gu) || !aligned16(w_down) ||
+        !aligned16(s_down) || !aligned16(y))
+        return CK_EINVAL;
+    const size_t need = ck_swiglu_mlp_workspace_size(m, h, i);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
+        return CK_EWORKSPACE;
+    const size_t M = (size_t)m, H = (size_t)h, I = (size_t)i;
+    char* p = static_cast<char*>(workspace);
+    int8_t* xq = reinterpret_cast<int8_t*>(p);          p += round_up(M * H);
+    float* sx = reinterpret_cast<float*>(p);            p += round_up(M * 4);
+    uint16_t* y1 = reinterpret_cast<uint16_t*>(p);      p += round_up(M * 2 * I * 2);
+    int8_t* hq = reinterpret_cast<int8_t*>(p);          p += round_up(M * I);
+    float* sh = reinterpret_cast<float*>(p);
+    hipStream_t st = (hipStream_t)stream;
+    // stage 1: packed [gate | up] projection, BF16 [m, 2i]
+    CK_TRY(from_hip(ck::launch_quant_rows(0, x, h, m, h, group, xq, sx, nullptr, st)));
+    CK_TRY(from_hip(ck::launch_gemm_bf16(xq, sx, w_gu, s_gu, m, 2 * i, h, y1, st)));
+    // stage 2: silu(gate) * up inside the down projection's quantizer
+    CK_TRY(from_hip(ck::launch_quant_rows(1, y1, 2 * i, m, i, group, hq, sh, nullptr, st)));
+    return from_hip(ck::launch_gemm_bf16(hq, sh, w_down, s_down, m, h, i, y, st));
+}
+
+ck_status ck_silu_f32(const uint16_t* gate, int64_t n, float* out, void* stream)
+{
+    if (n < 0) return CK_ESHAPE;
+    if (n == 0) return CK_OK;
+    if (!gate || !out) return CK_EINVAL;
+    return from_hip(ck::launch_silu(gate, n, out, (hipStream_t)stream));
+}
+
+ck_status ck_act_rotate_f32(const uint16_t* x, int64_t ldx, int64_t m, int64_t k, int32_t act,
+                            int32_t group, float* u, void* stream)
+{
+    CK_TRY(check_k(k, group));
+    CK_TRY(check_act(act, ldx, k));
+    if (m < 0) return CK_ESHAPE;
+    if (m == 0) return CK_OK;
+    if (!x || !u) return CK_EINVAL;
+    if (!aligned16(x) || !aligned16(u)) return CK_EINVAL;
+    return from_hip(ck::launch_quant_rows(act == CK_ACT_SWIGLU ? 1 : 0, x, ldx, m, k, group,
+                                          nullptr, nullptr, u, (hipStream_t)stream));
+}
+
+}  // extern "C"

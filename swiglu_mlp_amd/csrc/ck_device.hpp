@@ -1,0 +1,162 @@
+// ck_device.hpp -- device-side building blocks of the ConvRot quantizer for
+// gfx950: BF16 unpacking, the FP32 silu, the blockwise Hadamard butterflies and
+// the INT8 code packing.  Every floating-point step is one IEEE binary32
+// operation in round-to-nearest-even; the translation units that include this
+// file are compiled with -ffp-contract=off, and fused multiply-adds appear only
+// where written as __builtin_fmaf.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ck {
+
+// ---------------------------------------------------------------------------
+// BF16 <-> FP32 (a BF16 value is the high half of an FP32 bit pattern)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even FP32 -> BF16 for finite values.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// FP32 silu.  sglang PR #44196, "Accuracy Tests": the fused quantizer keeps
+// silu(gate) * up in FP32.  The evaluation procedure is fixed so the result is
+// reproducible bit for bit:
+//   gl = max(gamma, -80), gc = min(gl, 80)
+//   e^{-gc}: k = rint(fl(-gc * log2e)); r = fma(k, -ln2_hi, -gc);
+//            r = fma(k, -ln2_lo, r); p = Taylor series of e^r to degree 7
+//            (Horner, fma); e = p * 2^k  (Cody-Waite range reduction)
+//   1/d, d = 1 + e: seed from the bit pattern (magic - bits(d)), then three
+//            Newton steps  t = fma(-d, y, 1); y = fma(y, t, y)
+//   silu = gl * y
+// Constants: log2e = fl(log2 e); ln2_hi = ln 2 rounded to 16 significant bits
+// (so k * ln2_hi is exact for |k| <= 116); ln2_lo = fl(ln 2 - ln2_hi);
+// Taylor coefficients fl(1/n!); the seed constant minimises the seed's maximum
+// relative error (5.05%) over a binade.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float silu_f32(float gamma)
+{
+    constexpr float kNegLog2e = -0x1.715476p+0f;
+    constexpr float kLn2Hi = 0x1.62e4p-1f;
+    constexpr float kLn2Lo = 0x1.7f7d1cp-20f;
+    constexpr uint32_t kRcpMagic = 0x7ef311c2u;
+    const float gl = fmaxf(gamma, -80.0f);
+    const float gc = fminf(gl, 80.0f);
+    const float kf = __builtin_rintf(gc * kNegLog2e);
+    float r = __builtin_fmaf(kf, -kLn2Hi, -gc);
+    r = __builtin_fmaf(kf, -kLn2Lo, r);
+    float p = 0x1.a01a02p-13f;                    // 1/7!
+    p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);    // 1/6!
+    p = __builtin_fmaf(p, r, 0x1.111112p-7f);     // 1/5!
+    p = __builtin_fmaf(p, r, 0x1.555556p-5f);     // 1/4!
+    p = __builtin_fmaf(p, r, 0x1.555556p-3f);     // 1/3!
+    p = __builtin_fmaf(p, r, 0x1p-1f);            // 1/2!
+    p = __builtin_fmaf(p, r, 1.0f);               // 1/1!
+    p = __builtin_fmaf(p, r, 1.0f);               // 1/0!
+    const float e = __builtin_amdgcn_ldexpf(p, (int)kf);
+    const float d = 1.0f + e;
+    float y = __uint_as_float(kRcpMagic - __float_as_uint(d));
+#pragma unroll
+    for (int it = 0; it < 3; ++it) {
+        const float t = __builtin_fmaf(-d, y, 1.0f);
+        y = __builtin_fmaf(y, t, y);
+    }
+    return gl * y;
+}
+
+// ---------------------------------------------------------------------------
+// Blockwise Hadamard rotation.  comfy-kitchen PR #277, "The key observation":
+// the activation is rotated online, x_rot = x H.  The transform is applied
+// unnormalised as a fast Walsh-Hadamard transform with strides 1, 2, 4, ...
+// in ascending order; a butterfly maps (p, q) at (i, i+h) to (p+q, p-q).
+//
+// Register layout: a lane holds 8 consecutive elements of a row (one 16-byte
+// BF16 load), so strides 1, 2 and 4 stay inside the lane; stride 8*d pairs the
+// lane with lane ^ d.  The partner's value comes through ds_swizzle (the LDS
+// crossbar, no VALU slot) and the butterfly is one fma per element:
+//   lower lane: v + partner = fma(v, +1, partner)
+//   upper lane: partner - v = fma(v, -1, partner)
+// both exact equivalents of the IEEE add/subtract.
+// ---------------------------------------------------------------------------
+template <int G>
+__device__ __forceinline__ void fwht_in_lane(float (&v)[8])
+{
+#pragma unroll
+    for (int h = 1; h < 8 && h < G; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if ((i & h) == 0) {
+                const float p = v[i], q = v[i + h];
+                v[i] = p + q;
+                v[i + h] = p - q;
+            }
+        }
+    }
+}
+
+// ds_swizzle in bit-mask mode: lane l reads lane ((l & 0x1f) ^ D) within its
+// group of 32 lanes.
+template <int D>
+__device__ __forceinline__ float swizzle_xor(float v)
+{
+    static_assert(D >= 1 && D <= 16, "swizzle xor distance");
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (D << 10) | 0x1f));
+}
+
+// Cross-lane strides 8 .. G/2.  `lane` is the lane's position in its row team
+// (teams are aligned to the group size).
+template <int G>
+__device__ __forceinline__ void fwht_cross_lane(float (&v)[8], int lane)
+{
+    if constexpr (G >= 16) {
+        const float s = (lane & 1) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, swizzle_xor<1>(v[i]));
+    }
+    if constexpr (G >= 32) {
+        const float s = (lane & 2) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, swizzle_xor<2>(v[i]));
+    }
+    if constexpr (G >= 64) {
+        const float s = (lane & 4) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, swizzle_xor<4>(v[i]));
+    }
+    if constexpr (G >= 128) {
+        const float s = (lane & 8) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, swizzle_xor<8>(v[i]));
+    }
+    if constexpr (G >= 256) {
+        const float s = (lane & 16) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, swizzle_xor<16>(v[i]));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// INT8 codes.  code = round-half-even(u * r) of the exact product: fma(u, r,
+// 1.5 * 2^23) rounds u*r + 1.5*2^23 once to an integer (|u*r| <= 127 + 2^-16,
+// far inside the range where FP32 spacing is 1), and the low byte of its bit
+// pattern is the two's-complement code.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t code_bits(float u, float r)
+{
+    return __float_as_uint(__builtin_fmaf(u, r, 12582912.0f));
+}
+
+// Pack the low bytes of four code words into one dword (v_perm_b32).
+__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x04000c0cu);
+    return lo | hi;
+}
+
+}  // namespace ck

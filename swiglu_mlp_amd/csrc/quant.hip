@@ -1,0 +1,263 @@
+// quant.hip -- fused (SwiGLU) + blockwise Hadamard rotation + per-row INT8
+// quantizer for gfx950, used for activations (per token) and, with FP32 input,
+// for weight preparation (per output row).
+//
+// Sources: comfy-kitchen PR #277, "The key observation" (x_rot = x H online,
+// W_rot = W H^T stored, INT8 on one grid); sglang PR #44196, "Motivation" and
+// "Accuracy Tests" (input_act="swiglu", silu(gate) * up kept in FP32);
+// sglang PR #35994 report, key source excerpts (per-output-channel INT8 weight
+// with an F32 [out, 1] scale).
+//
+// Work decomposition: a row is owned by a team of T lanes (T a power of two,
+// 8 <= T <= 256, T a multiple of group/8).  Lane t of the team holds chunks
+// c = j*T + t (j < CH) of 8 consecutive elements, so each load instruction
+// reads consecutive 16-byte pieces across the team (coalesced) and the 16 lanes
+// of one 128-element group are adjacent (the cross-lane butterflies stay in a
+// swizzle group).  The whole rotated row stays in registers until the row's
+// absmax is known; codes are then written once.  A workgroup holds 256/T rows.
+// The kernel is bound by HBM and by VALU issue; every per-element step is a
+// single VALU op except the SwiGLU's exp/reciprocal.
+#include "ck_device.hpp"
+#include "ck_internal.hpp"
+
+namespace ck {
+
+enum InKind { IN_BF16 = 0, IN_BF16_SWIGLU = 1, IN_F32 = 2 };
+
+template <int KIND, int LOG_G, int CH, bool ROT_OUT>
+__global__ __launch_bounds__(256) void quant_rows_kernel(
+    const void* __restrict__ src, int64_t ld, int m, int k, int log_t, float cg,
+    int8_t* __restrict__ q, float* __restrict__ s, float* __restrict__ u_out)
+{
+    constexpr int G = 1 << LOG_G;
+    const int T = 1 << log_t;
+    const int t = threadIdx.x & (T - 1);
+    const int team = threadIdx.x >> log_t;
+    const int rows_per_wg = blockDim.x >> log_t;
+    int row = blockIdx.x * rows_per_wg + team;
+    const bool row_ok = row < m;
+    if (!row_ok) row = m - 1;               // compute on a valid row, store nothing
+    const int k8 = k >> 3;
+
+    float v[CH][8];
+
+    // ---- load + activation -------------------------------------------------
+    if constexpr (KIND == IN_F32) {
+        const float* rp = static_cast<const float*>(src) + (int64_t)row * ld;
+        float4 raw[CH][2];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = j * T + t;
+            if (c < k8) {
+                raw[j][0] = *reinterpret_cast<const float4*>(rp + c * 8);
+                raw[j][1] = *reinterpret_cast<const float4*>(rp + c * 8 + 4);
+            } else {
+                raw[j][0] = make_float4(0.f, 0.f, 0.f, 0.f);
+                raw[j][1] = raw[j][0];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            v[j][0] = raw[j][0].x; v[j][1] = raw[j][0].y; v[j][2] = raw[j][0].z; v[j][3] = raw[j][0].w;
+            v[j][4] = raw[j][1].x; v[j][5] = raw[j][1].y; v[j][6] = raw[j][1].z; v[j][7] = raw[j][1].w;
+        }
+    } else {
+        const uint16_t* rp = static_cast<const uint16_t*>(src) + (int64_t)row * ld;
+        uint4 rg[CH];
+        uint4 ru[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = j * T + t;
+            if (c < k8) {
+                rg[j] = *reinterpret_cast<const uint4*>(rp + c * 8);
+                if constexpr (KIND == IN_BF16_SWIGLU)
+                    ru[j] = *reinterpret_cast<const uint4*>(rp + k + c * 8);
+            } else {
+                rg[j] = make_uint4(0u, 0u, 0u, 0u);
+                ru[j] = rg[j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const uint32_t w[4] = {rg[j].x, rg[j].y, rg[j].z, rg[j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[j][2 * e] = bf16_lo(w[e]);
+                v[j][2 * e + 1] = bf16_hi(w[e]);
+            }
+            if constexpr (KIND == IN_BF16_SWIGLU) {
+                const uint32_t wu[4] = {ru[j].x, ru[j].y, ru[j].z, ru[j].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[j][2 * e] = silu_f32(v[j][2 * e]) * bf16_lo(wu[e]);
+                    v[j][2 * e + 1] = silu_f32(v[j][2 * e + 1]) * bf16_hi(wu[e]);
+                }
+            }
+        }
+    }
+
+    // ---- rotation (unnormalised blockwise FWHT) + absmax --------------------
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        fwht_in_lane<G>(v[j]);
+        fwht_cross_lane<G>(v[j], t);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
+    }
+
+    if constexpr (ROT_OUT) {
+        float* up = u_out + (int64_t)row * k;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = j * T + t;
+            if (row_ok && c < k8) {
+                *reinterpret_cast<float4*>(up + c * 8) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
+                *reinterpret_cast<float4*>(up + c * 8 + 4) = make_float4(v[j][4], v[j][5], v[j][6], v[j][7]);
+            }
+        }
+        return;
+    }
+
+    // ---- team reduction of the absmax (exact; order does not matter) -------
+    __shared__ float red[4];
+    if (T >= 2) amax = fmaxf(amax, swizzle_xor<1>(amax));
+    if (T >= 4) amax = fmaxf(amax, swizzle_xor<2>(amax));
+    if (T >= 8) amax = fmaxf(amax, swizzle_xor<4>(amax));
+    if (T >= 16) amax = fmaxf(amax, swizzle_xor<8>(amax));
+    if (T >= 32) amax = fmaxf(amax, swizzle_xor<16>(amax));
+    if (T >= 64) amax = fmaxf(amax, __shfl_xor(amax, 32));
+    if (T > 64) {
+        // one team spans T/64 waves of this workgroup
+        const int wave = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) red[wave] = amax;
+        __syncthreads();
+        const int w0 = (team * T) >> 6;
+        for (int w = 0; w < (T >> 6); ++w) amax = fmaxf(amax, red[w0 + w]);
+    }
+
+    // ---- scale and codes ----------------------------------------------------
+    // s = fl(fl(A * c_g) / 127); r = fl(127 / A), or 0 for an all-zero row
+    // (every code is then round(u * 0) = 0 and the scale is 0).
+    const float scale = (amax * cg) / 127.0f;
+    const float r = amax > 0.0f ? 127.0f / amax : 0.0f;
+    int8_t* qp = q + (int64_t)row * k;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const int c = j * T + t;
+        uint32_t b[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) b[i] = code_bits(v[j][i], r);
+        if (row_ok && c < k8)
+            *reinterpret_cast<uint2*>(qp + c * 8) =
+                make_uint2(pack4(b[0], b[1], b[2], b[3]), pack4(b[4], b[5], b[6], b[7]));
+    }
+    if (row_ok && t == 0) s[row] = scale;
+}
+
+__global__ __launch_bounds__(256) void silu_kernel(const uint16_t* __restrict__ g, int64_t n,
+                                                   float* __restrict__ out)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = silu_f32(__uint_as_float((uint32_t)g[i] << 16));
+}
+
+// ---------------------------------------------------------------------------
+// Host side: team shape and template dispatch
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kChOptions[] = {1, 2, 3, 4, 6, 8, 12, 16};
+
+// Choose (log2 T, CH) with T*CH >= k/8, T a power of two in [max(8, G/8), 256].
+// Prefer no idle chunk slots, then T >= 64 (full waves per row), then CH near 6
+// (enough loads in flight per lane without spilling).
+bool choose_team(int k, int g, int* log_t, int* ch)
+{
+    const int k8 = k / 8;
+    const int tmin = g / 8 > 8 ? g / 8 : 8;
+    long best = -1;
+    for (int lt = 3; lt <= 8; ++lt) {
+        const int T = 1 << lt;
+        if (T < tmin) continue;
+        for (int c : kChOptions) {
+            if ((long)T * c < k8) continue;
+            const long waste = (long)T * c - k8;
+            const long score = waste * 1000 + (T < 64 ? 100 : 0) + (c > 6 ? c - 6 : 6 - c);
+            if (best < 0 || score < best) {
+                best = score;
+                *log_t = lt;
+                *ch = c;
+            }
+        }
+    }
+    return best >= 0;
+}
+
+template <int KIND, int LOG_G, bool ROT_OUT>
+hipError_t launch_ch(int ch, dim3 grid, hipStream_t st, const void* src, int64_t ld, int m, int k,
+                     int log_t, float cg, int8_t* q, float* s, float* u)
+{
+    switch (ch) {
+#define CK_CASE(C)                                                                              \
+    case C:                                                                                     \
+        hipLaunchKernelGGL((quant_rows_kernel<KIND, LOG_G, C, ROT_OUT>), grid, dim3(256), 0, st, \
+                           src, ld, m, k, log_t, cg, q, s, u);                                  \
+        break;
+        CK_CASE(1) CK_CASE(2) CK_CASE(3) CK_CASE(4) CK_CASE(6) CK_CASE(8) CK_CASE(12) CK_CASE(16)
+#undef CK_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int KIND, bool ROT_OUT>
+hipError_t launch_g(int log_g, int ch, dim3 grid, hipStream_t st, const void* src, int64_t ld, int m,
+                    int k, int log_t, float cg, int8_t* q, float* s, float* u)
+{
+    switch (log_g) {
+#define CK_G(L) \
+    case L: return launch_ch<KIND, L, ROT_OUT>(ch, grid, st, src, ld, m, k, log_t, cg, q, s, u);
+        CK_G(0) CK_G(1) CK_G(2) CK_G(3) CK_G(4) CK_G(5) CK_G(6) CK_G(7) CK_G(8)
+#undef CK_G
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+// kind: 0 = BF16, 1 = BF16 [gate | up] with SwiGLU, 2 = FP32 (weights).
+hipError_t launch_quant_rows(int kind, const void* src, int64_t ld, int64_t m, int64_t k, int g,
+                             int8_t* q, float* s, float* u_out, hipStream_t st)
+{
+    if (m == 0) return hipSuccess;
+    int log_t = 0, ch = 0;
+    if (!choose_team((int)k, g, &log_t, &ch)) return hipErrorInvalidValue;
+    const int rows_per_wg = 256 >> log_t;
+    const dim3 grid((unsigned)((m + rows_per_wg - 1) / rows_per_wg));
+    int log_g = 0;
+    while ((1 << log_g) < g) ++log_g;
+    const float cg = (float)(1.0 / sqrt((double)g));
+    const bool rot = u_out != nullptr;
+    switch (kind) {
+        case IN_BF16:
+            return rot ? launch_g<IN_BF16, true>(log_g, ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s, u_out)
+                       : launch_g<IN_BF16, false>(log_g, ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s, u_out);
+        case IN_BF16_SWIGLU:
+            return rot ? launch_g<IN_BF16_SWIGLU, true>(log_g, ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s, u_out)
+                       : launch_g<IN_BF16_SWIGLU, false>(log_g, ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s, u_out);
+        case IN_F32:
+            return launch_g<IN_F32, false>(log_g, ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s, u_out);
+        default:
+            return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_silu(const uint16_t* g, int64_t n, float* out, hipStream_t st)
+{
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(silu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g, n, out);
+    return hipGetLastError();
+}
+
+}  // namespace ck

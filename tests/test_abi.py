@@ -1,0 +1,124 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/ck.h declares, and rejects bad arguments on the host (returning the
+documented status, enqueueing nothing) before any device is touched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+import swiglu_mlp_amd as ck
+
+HEADER = os.path.join(ROOT, "include", "ck.h")
+OK, EINVAL, ESHAPE, EUNSUP, EWS = 0, 1, 2, 3, 4
+FAKE = 1 << 20          # an aligned non-null address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ck.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ck_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_path_calls():
+    names = declared_functions()
+    for n in ("ck_weight_prep", "ck_act_quant", "ck_int8_linear", "ck_swiglu_mlp"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version(L):
+    assert L.ck_version().decode().startswith("ck-convrot")
+    for s in range(6):
+        assert L.ck_status_str(s)
+    assert b"unknown" in L.ck_status_str(99)
+
+
+def test_workspace_sizes(L):
+    assert L.ck_int8_linear_workspace_size(0, 256) == 0
+    assert L.ck_int8_linear_workspace_size(3, 256) == 768 + 256
+    ws = L.ck_swiglu_mlp_workspace_size(4096, 3072, 12288)
+    assert ws >= 4096 * 3072 + 4096 * 4 + 4096 * 2 * 12288 * 2 + 4096 * 12288 + 4096 * 4
+    assert ws % 256 == 0
+
+
+@pytest.mark.parametrize("k,group,want", [
+    (256, 128, OK), (192, 128, ESHAPE), (96, 32, ESHAPE), (256, 96, EUNSUP),
+    (256, 512, EUNSUP), (0, 128, ESHAPE), (65536, 128, EUNSUP), (256, 0, EUNSUP),
+])
+def test_weight_prep_shape_checks(L, k, group, want):
+    # n == 0 makes a valid call a no-op, so nothing is launched on success
+    assert L.ck_weight_prep(FAKE, 0, k, group, FAKE, FAKE, None) == want
+
+
+def test_weight_prep_null_and_alignment(L):
+    assert L.ck_weight_prep(None, 4, 256, 128, FAKE, FAKE, None) == EINVAL
+    assert L.ck_weight_prep(FAKE + 4, 4, 256, 128, FAKE, FAKE, None) == EINVAL
+    assert L.ck_weight_prep(FAKE, -1, 256, 128, FAKE, FAKE, None) == ESHAPE
+
+
+def test_act_quant_checks(L):
+    f = L.ck_act_quant
+    assert f(FAKE, 256, 0, 256, 0, 128, FAKE, FAKE, None) == OK          # m == 0: no-op
+    assert f(FAKE, 256, -2, 256, 0, 128, FAKE, FAKE, None) == ESHAPE
+    assert f(FAKE, 256, 4, 256, 1, 128, FAKE, FAKE, None) == ESHAPE      # swiglu needs ld >= 2k
+    assert f(FAKE, 260, 4, 256, 0, 128, FAKE, FAKE, None) == ESHAPE      # ld % 8
+    assert f(FAKE, 256, 4, 256, 7, 128, FAKE, FAKE, None) == EINVAL      # unknown act
+    assert f(None, 256, 4, 256, 0, 128, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE, 256, 4, 256, 0, 128, FAKE, None, None) == EINVAL
+
+
+def test_int8_linear_checks(L):
+    f = L.ck_int8_linear
+    ws = L.ck_int8_linear_workspace_size(4, 256)
+    assert f(FAKE, 256, 0, FAKE, FAKE, 4, 40, 256, 128, FAKE, FAKE, ws, None) == ESHAPE  # n % 16
+    assert f(FAKE, 256, 0, FAKE, FAKE, 4, 32, 256, 128, FAKE, FAKE, ws - 1, None) == EWS
+    assert f(FAKE, 256, 0, FAKE, FAKE, 4, 32, 256, 128, FAKE, None, ws, None) == EWS
+    assert f(FAKE, 256, 0, FAKE, FAKE, 4, 32, 256, 128, FAKE, FAKE + 16, ws, None) == EWS
+    assert f(FAKE, 256, 0, None, FAKE, 4, 32, 256, 128, FAKE, FAKE, ws, None) == EINVAL
+    assert f(FAKE, 256, 0, FAKE, FAKE, 0, 32, 256, 128, FAKE, FAKE, 0, None) == OK
+
+
+def test_swiglu_mlp_checks(L):
+    f = L.ck_swiglu_mlp
+    ws = L.ck_swiglu_mlp_workspace_size(8, 256, 512)
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 256, 500, 128, FAKE, FAKE, ws, None) == ESHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 256, 512, 128, FAKE, FAKE, ws - 256, None) == EWS
+    assert f(FAKE, None, FAKE, FAKE, FAKE, 8, 256, 512, 128, FAKE, FAKE, ws, None) == EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 256, 512, 128, FAKE, FAKE, 0, None) == OK
+
+
+def test_gemm_hook_checks(L):
+    assert L.ck_int8_gemm_i32(FAKE, FAKE, 4, 20, 256, FAKE, None) == ESHAPE
+    assert L.ck_int8_gemm_i32(FAKE, FAKE, 4, 32, 100, FAKE, None) == ESHAPE
+    assert L.ck_int8_gemm_i32(None, FAKE, 4, 32, 256, FAKE, None) == EINVAL
+    assert L.ck_int8_gemm_bf16(FAKE, None, FAKE, FAKE, 4, 32, 256, FAKE, None) == EINVAL
+    assert L.ck_silu_f32(FAKE, -1, FAKE, None) == ESHAPE
+    assert L.ck_act_rotate_f32(FAKE, 256, 4, 256, 0, 100, FAKE, None) == EUNSUP
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    with pytest.raises(ValueError, match="GPU"):
+        ck.ck_weight_prep(torch.zeros(4, 256))
+    with pytest.raises(ValueError):
+        ck.ck_act_quant(torch.zeros(4, 256, dtype=torch.float32))
+
+
+def test_binding_is_not_backed_by_the_oracle():
+    """The product package must not reach the CPU oracle."""
+    import glob
+    for path in glob.glob(os.path.join(ROOT, "swiglu_mlp_amd", "**", "*.py"), recursive=True):
+        src = open(path).read()
+        assert "import oracle" not in src and "from oracle" not in src, path

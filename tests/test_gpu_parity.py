@@ -1,0 +1,269 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars (stated per check below):
+  * INT8 codes, FP32 scales and int32 accumulators: bit-exact.
+  * BF16 outputs: within 1 BF16 ulp or 1e-2 relative per element; the pinned
+    epilogue makes them bit-exact, which is asserted too.
+  * relative L2 against the float64 reference: GPU <= oracle + 1e-4.
+Full-size workloads are compared on sampled rows (every step of the path is
+per row, so the oracle computes those rows end to end from the same inputs).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import swiglu_mlp_amd as ck  # noqa: E402
+from swiglu_mlp_amd import workloads as W  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def bf16_dev(a_u16):
+    return torch.from_numpy(np.ascontiguousarray(a_u16).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def bf16_host(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def assert_bf16_close(got, want, what):
+    """1 BF16 ulp or 1e-2 relative per element; then bit-exact."""
+    g = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    w = (want.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ulp = np.spacing(np.abs(w).astype(np.float32)).astype(np.float64) * 65536.0
+    ok = (np.abs(g - w) <= ulp) | (np.abs(g - w) <= 1e-2 * np.abs(w))
+    assert ok.all(), f"{what}: {np.count_nonzero(~ok)} elements beyond tolerance"
+    mism = np.count_nonzero(got != want)
+    assert mism == 0, f"{what}: {mism} BF16 elements differ (within tolerance, not bit-exact)"
+
+
+def sample_rows(m, count=16, seed=0):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, m // 3, m // 2, m - 2, m - 1]
+    rest = rng.choice(m, size=max(0, count - len(fixed)), replace=False)
+    return np.unique(np.clip(np.concatenate([fixed, rest]), 0, m - 1))
+
+
+_cache = {}
+
+
+def inputs(name):
+    if name not in _cache:
+        w = W.WORKLOADS[name]
+        _cache[name] = W.mlp_inputs(w) if w.kind == "mlp" else W.linear_inputs(w)
+    return _cache[name]
+
+
+def prepped(orc, name, key="w"):
+    ck_key = (name, key)
+    if ck_key not in _cache:
+        _cache[ck_key] = orc.weight_prep(inputs(name)[key], W.WORKLOADS[name].group)
+    return _cache[ck_key]
+
+
+# ---------------------------------------------------------------------------
+def test_silu_exhaustive_bf16(orc):
+    say("silu: all 65536 BF16 patterns")
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = (bits.astype(np.uint32) << 16).view(np.float32)
+    fin = np.isfinite(f)
+    got = host(ck.ck_silu_f32(bf16_dev(bits)))
+    want = orc.silu_bf16(bits)
+    np.testing.assert_array_equal(got[fin].view(np.uint32), want[fin].view(np.uint32))
+
+
+@pytest.mark.parametrize("name,key", [("c1", "w"), ("c2", "w"), ("c3", "w"), ("c4", "w"),
+                                      ("c5", "w_gu"), ("c5", "w_down")])
+def test_weight_prep_bit_exact(orc, name, key):
+    w = inputs(name)[key]
+    say(f"weight_prep {name}.{key} {w.shape}")
+    q, s = ck.ck_weight_prep(dev(w), W.WORKLOADS[name].group)
+    torch.cuda.synchronize()
+    q_o, s_o = prepped(orc, name, key)
+    np.testing.assert_array_equal(host(q), q_o)
+    np.testing.assert_array_equal(host(s)[:, 0].view(np.uint32), s_o.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_act_quant_bit_exact(orc, name):
+    wl = W.WORKLOADS[name]
+    x = inputs(name)["x"]
+    act = 0 if wl.kind == "mlp" else wl.act
+    say(f"act_quant {name} act={act} x{x.shape}")
+    q, s = ck.ck_act_quant(bf16_dev(x), act, wl.group)
+    torch.cuda.synchronize()
+    q_o, s_o = orc.act_quant(x, act, wl.group)
+    np.testing.assert_array_equal(host(s)[:, 0].view(np.uint32), s_o.view(np.uint32))
+    np.testing.assert_array_equal(host(q), q_o)
+
+
+@pytest.mark.parametrize("m,k,act,g", [(37, 384, 1, 128), (64, 1024, 0, 256), (9, 512, 1, 64),
+                                       (5, 256, 0, 1), (3, 32768, 1, 128)])
+def test_act_rotate_bit_exact(orc, m, k, act, g):
+    say(f"act_rotate m={m} k={k} act={act} g={g}")
+    d = W.case(m, k, 16, act, seed=m + k)
+    u = host(ck.ck_act_rotate_f32(bf16_dev(d["x"]), act, g))
+    np.testing.assert_array_equal(u.view(np.uint32), orc.act_rotate(d["x"], act, g).view(np.uint32))
+
+
+GEMM_SHAPES = [  # (m, n, k): every tile shape, both k-step sizes, ragged m and n
+    (1, 16, 64), (64, 128, 256), (77, 144, 192), (300, 272, 1024), (1000, 1040, 640),
+    (600, 1200, 384), (2048, 1024, 3072), (513, 4112, 128),
+]
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
+def test_gemm_i32_bit_exact(orc, m, n, k):
+    say(f"gemm_i32 m={m} n={n} k={k}")
+    rng = np.random.default_rng(m * 7 + n)
+    xq = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    acc = host(ck.ck_int8_gemm_i32(dev(xq), dev(wq)))
+    np.testing.assert_array_equal(acc, orc.gemm_i32(xq, wq))
+
+
+def test_gemm_i32_extreme_codes(orc):
+    say("gemm_i32 extreme codes k=32768")
+    m, n, k = 4, 32, 32768
+    xq = np.full((m, k), -127, np.int8)
+    wq = np.full((n, k), 127, np.int8)
+    wq[::2] = -127
+    acc = host(ck.ck_int8_gemm_i32(dev(xq), dev(wq)))
+    np.testing.assert_array_equal(acc, orc.gemm_i32(xq, wq))
+
+
+LINEAR_CASES = [  # (m, k, n, act, g)
+    (1, 256, 16, 0, 128), (7, 384, 48, 1, 128), (64, 256, 128, 0, 128), (300, 1024, 272, 1, 128),
+    (129, 512, 320, 0, 64), (200, 768, 96, 1, 256), (33, 128, 64, 0, 1), (1000, 640, 1040, 0, 128),
+]
+
+
+@pytest.mark.parametrize("m,k,n,act,g", LINEAR_CASES)
+def test_int8_linear_bit_exact(orc, m, k, n, act, g):
+    say(f"int8_linear m={m} k={k} n={n} act={act} g={g}")
+    d = W.case(m, k, n, act, seed=1000 + m, zero_rows=(m // 2,) if m > 2 else ())
+    wq_o, sw_o = orc.weight_prep(d["w"], g)
+    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    y = bf16_host(ck.ck_int8_linear(bf16_dev(d["x"]), wq, sw, g, act))
+    ref = orc.int8_linear(d["x"], act, wq_o, sw_o, g, return_all=True)
+    np.testing.assert_array_equal(host(wq), wq_o)
+    assert_bf16_close(y, ref["y"], "y")
+    if m > 2:
+        assert not y[m // 2].any()           # an all-zero input row gives a zero output row
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_full_workload_sampled_rows(orc, name):
+    wl = W.WORKLOADS[name]
+    d = inputs(name)
+    say(f"int8_linear full {name}: {wl.desc}")
+    wq, sw = ck.ck_weight_prep(dev(d["w"]), wl.group)
+    x_dev = bf16_dev(d["x"])
+    y = ck.ck_int8_linear(x_dev, wq, sw, wl.group, wl.act)
+    xq_dev, sx_dev = ck.ck_act_quant(x_dev, wl.act, wl.group)
+    acc = ck.ck_int8_gemm_i32(xq_dev, wq)
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.m)
+    y_rows = bf16_host(y)[rows]
+    wq_o, sw_o = prepped(orc, name)
+    ref = orc.int8_linear(d["x"][rows], wl.act, wq_o, sw_o, wl.group, return_all=True)
+    np.testing.assert_array_equal(host(acc)[rows], ref["acc"])
+    assert_bf16_close(y_rows, ref["y"], f"{name} sampled rows")
+    y64 = orc.reference_linear_f64(d["x"][rows], wl.act, d["w"])
+    e_gpu, e_orc = orc.rel_l2(y_rows, y64), orc.rel_l2(ref["y"], y64)
+    say(f"{name}: relL2 gpu={e_gpu:.5f} oracle={e_orc:.5f}")
+    assert e_gpu <= e_orc + 1e-4
+
+
+def test_swiglu_mlp_full_c5_sampled_rows(orc):
+    wl = W.WORKLOADS["c5"]
+    d = inputs("c5")
+    say(f"swiglu_mlp full c5: {wl.desc}")
+    wgu, sgu = ck.ck_weight_prep(dev(d["w_gu"]), wl.group)
+    wd, sd = ck.ck_weight_prep(dev(d["w_down"]), wl.group)
+    y = ck.ck_swiglu_mlp(bf16_dev(d["x"]), wgu, sgu, wd, sd, wl.group)
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.m)
+    y_rows = bf16_host(y)[rows]
+    (gq, gs), (dq, ds) = prepped(orc, "c5", "w_gu"), prepped(orc, "c5", "w_down")
+    ref = orc.swiglu_mlp(d["x"][rows], gq, gs, dq, ds, wl.group)
+    assert_bf16_close(y_rows, ref, "c5 sampled rows")
+    y64 = orc.reference_mlp_f64(d["x"][rows], d["w_gu"], d["w_down"])
+    e_gpu, e_orc = orc.rel_l2(y_rows, y64), orc.rel_l2(ref, y64)
+    say(f"c5: relL2 gpu={e_gpu:.5f} oracle={e_orc:.5f}")
+    assert e_gpu <= e_orc + 1e-4
+
+
+def test_swiglu_mlp_equals_its_stages():
+    """ck_swiglu_mlp is the composition of its stage entry points, bit for bit,
+    and repeated calls give identical bits."""
+    say("swiglu_mlp composition + determinism (m=512, h=1024, i=2048)")
+    m, h, i, g = 512, 1024, 2048, 128
+    rng = np.random.default_rng(21)
+    x = bf16_dev(W.to_bf16_bits(rng.standard_normal((m, h)).astype(np.float32)))
+    wgu, sgu = ck.ck_weight_prep(dev((0.02 * rng.standard_normal((2 * i, h))).astype(np.float32)), g)
+    wd, sd = ck.ck_weight_prep(dev((0.01 * rng.standard_normal((h, i))).astype(np.float32)), g)
+    y1 = ck.ck_swiglu_mlp(x, wgu, sgu, wd, sd, g)
+    y2 = ck.ck_swiglu_mlp(x, wgu, sgu, wd, sd, g)
+    xq, sx = ck.ck_act_quant(x, 0, g)
+    t = ck.ck_int8_gemm_bf16(xq, sx, wgu, sgu)
+    hq, sh = ck.ck_act_quant(t, 1, g)
+    y3 = ck.ck_int8_gemm_bf16(hq, sh, wd, sd)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
+
+
+def test_packed_gate_up_equals_separate():
+    """sglang PR #44196, "Accuracy Tests": packed [gate | up] GEMM columns equal
+    the two separate projections bit for bit."""
+    say("packed gate|up vs separate")
+    rng = np.random.default_rng(22)
+    m, h, i, g = 300, 512, 384, 128
+    x = bf16_dev(W.to_bf16_bits(rng.standard_normal((m, h)).astype(np.float32)))
+    wg = (0.02 * rng.standard_normal((i, h))).astype(np.float32)
+    wu = (0.02 * rng.standard_normal((i, h))).astype(np.float32)
+    q, s = ck.ck_weight_prep(dev(np.concatenate([wg, wu])), g)
+    qg, sg = ck.ck_weight_prep(dev(wg), g)
+    qu, su = ck.ck_weight_prep(dev(wu), g)
+    y = ck.ck_int8_linear(x, q, s, g)
+    yg = ck.ck_int8_linear(x, qg, sg, g)
+    yu = ck.ck_int8_linear(x, qu, su, g)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:, :i].contiguous().view(torch.int16), yg.view(torch.int16))
+    assert torch.equal(y[:, i:].contiguous().view(torch.int16), yu.view(torch.int16))
+
+
+def test_empty_and_degenerate_calls(orc):
+    say("empty and degenerate calls")
+    g = 128
+    x0 = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    wq, sw = ck.ck_weight_prep(torch.zeros((32, 256), dtype=torch.float32, device=DEV), g)
+    torch.cuda.synchronize()
+    assert not wq.any() and not sw.any()                  # all-zero weight rows
+    assert ck.ck_int8_linear(x0, wq, sw, g).shape == (0, 32)
+    xz = torch.zeros((4, 256), dtype=torch.bfloat16, device=DEV)
+    y = ck.ck_int8_linear(xz, wq, sw, g)
+    torch.cuda.synchronize()
+    assert not y.any()

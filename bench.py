@@ -4,11 +4,12 @@ hot path on one MI355X.
 A step is one pass of the whole path over one batch of synthetic input, by
 default the SwiGLU MLP block (workload c5: M=4096 tokens, hidden 3072,
 intermediate 12288, group 128): activation quant -> packed [gate | up] INT8
-GEMM -> fused SwiGLU + rotation + quant -> down INT8 GEMM.  The step calls the
-four stage entry points of the C ABI in the order ck_swiglu_mlp uses (a test
-checks the two agree bit for bit) so that each kernel can be bracketed by HIP
-events on the stream it runs on.  Weight preparation happens once, before
-timing, as at model load.  Inputs are resident in HBM before the timed region.
+GEMM -> fused SwiGLU + rotation + quant -> down INT8 GEMM, with INT8 operands
+in the blocked layout.  The step calls the four stage entry points of the C ABI
+in the order ck_swiglu_mlp uses (a test checks the two agree bit for bit) so
+that each kernel can be bracketed by HIP events on the stream it runs on.
+Weight preparation and the one-time weight relayout happen before timing, as at
+model load.  Inputs are resident in HBM before the timed region.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
 [--workload c1..c5] [--no-cpu-baseline]
@@ -45,7 +46,7 @@ def parse():
 
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("gemm.hip", "quant.hip", "ck_device.hpp"):
+    for f in ("gemm_blk.hip", "quant.hip", "ck_device.hpp"):
         with open(os.path.join(ROOT, "swiglu_mlp_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -89,32 +90,35 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     g = wl.group
+    BLK = ck.CK_LAYOUT_BLOCKED
     if wl.kind == "mlp":
         d = W.mlp_inputs(wl)
         m, h, inter = wl.m, wl.k, wl.n
+        mp = ck.blocked_rows(m)
         x = to_dev(d["x"].view(np.int16)).view(torch.bfloat16)
         wgu, sgu = ck.ck_weight_prep(to_dev(d["w_gu"]), g)
         wd, sd = ck.ck_weight_prep(to_dev(d["w_down"]), g)
-        xq = torch.empty((m, h), dtype=torch.int8, device=dev)
+        wgu, wd = ck.ck_weight_pack(wgu), ck.ck_weight_pack(wd)     # load-time relayout
+        xq = torch.empty((mp, h), dtype=torch.int8, device=dev)
         sx = torch.empty((m,), dtype=torch.float32, device=dev)
         t1 = torch.empty((m, 2 * inter), dtype=torch.bfloat16, device=dev)
-        hq = torch.empty((m, inter), dtype=torch.int8, device=dev)
+        hq = torch.empty((mp, inter), dtype=torch.int8, device=dev)
         sh = torch.empty((m,), dtype=torch.float32, device=dev)
         y = torch.empty((m, h), dtype=torch.bfloat16, device=dev)
         # (name, callable, algorithmic ops, algorithmic HBM bytes, bound)
         stages = [
-            ("x_quant", lambda s: L.ck_act_quant(x.data_ptr(), h, m, h, 0, g, xq.data_ptr(),
+            ("x_quant", lambda s: L.ck_act_quant(x.data_ptr(), h, m, h, 0, g, BLK, xq.data_ptr(),
                                                  sx.data_ptr(), s),
              0, m * h * 2 + m * h + m * 4, "hbm"),
             ("gate_up_gemm", lambda s: L.ck_int8_gemm_bf16(xq.data_ptr(), sx.data_ptr(),
-                                                           wgu.data_ptr(), sgu.data_ptr(),
+                                                           wgu.data_ptr(), sgu.data_ptr(), BLK,
                                                            m, 2 * inter, h, t1.data_ptr(), s),
              2 * m * 2 * inter * h, m * h + 2 * inter * h + m * 2 * inter * 2, "mfma"),
             ("swiglu_quant", lambda s: L.ck_act_quant(t1.data_ptr(), 2 * inter, m, inter, 1, g,
-                                                      hq.data_ptr(), sh.data_ptr(), s),
+                                                      BLK, hq.data_ptr(), sh.data_ptr(), s),
              0, m * inter * 4 + m * inter + m * 4, "hbm"),
             ("down_gemm", lambda s: L.ck_int8_gemm_bf16(hq.data_ptr(), sh.data_ptr(),
-                                                        wd.data_ptr(), sd.data_ptr(),
+                                                        wd.data_ptr(), sd.data_ptr(), BLK,
                                                         m, h, inter, y.data_ptr(), s),
              2 * m * h * inter, m * inter + h * inter + m * h * 2, "mfma"),
         ]
@@ -124,15 +128,16 @@ def main():
         ldx = 2 * k if wl.act == 1 else k
         x = to_dev(d["x"].view(np.int16)).view(torch.bfloat16)
         wq, sw = ck.ck_weight_prep(to_dev(d["w"]), g)
-        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+        wq = ck.ck_weight_pack(wq)
+        xq = torch.empty((ck.blocked_rows(m), k), dtype=torch.int8, device=dev)
         sx = torch.empty((m,), dtype=torch.float32, device=dev)
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         stages = [
-            ("act_quant", lambda s: L.ck_act_quant(x.data_ptr(), ldx, m, k, wl.act, g,
+            ("act_quant", lambda s: L.ck_act_quant(x.data_ptr(), ldx, m, k, wl.act, g, BLK,
                                                    xq.data_ptr(), sx.data_ptr(), s),
              0, m * ldx * 2 + m * k + m * 4, "hbm"),
             ("gemm", lambda s: L.ck_int8_gemm_bf16(xq.data_ptr(), sx.data_ptr(), wq.data_ptr(),
-                                                   sw.data_ptr(), m, n, k, y.data_ptr(), s),
+                                                   sw.data_ptr(), BLK, m, n, k, y.data_ptr(), s),
              2 * m * n * k, m * k + n * k + m * n * 2, "mfma"),
         ]
     torch.cuda.synchronize()

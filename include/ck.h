@@ -49,6 +49,19 @@
  *    a no-op), k >= 1.  group is a power of two in [1, 256] dividing k; k is a
  *    multiple of 64 and at most CK_MAX_K; n is a multiple of 16.  Pointers are
  *    16-byte aligned; leading dimensions are multiples of 8 elements.
+ *  - INT8 operand layouts (`layout` arguments), for an int8 matrix A [R, K]:
+ *      CK_LAYOUT_ROWS     row-major, A[r][k] at byte r * K + k (R * K bytes).
+ *      CK_LAYOUT_BLOCKED  rows padded to R_pad = ck_blocked_rows(R) (a multiple
+ *                         of 256); 1 KB blocks, block (r / 32, k / 32) at byte
+ *                         ((r / 32) * (K / 32) + k / 32) * 1024, and inside a
+ *                         block A[r][k] at ((k % 32) / 16) * 512 + (r % 32) * 16
+ *                         + k % 16.  R_pad * K bytes; padding rows are never
+ *                         read into valid outputs.  A block is one 32-row x
+ *                         32-byte MFMA operand fragment in lane order, so the
+ *                         GEMM streams whole kilobytes from HBM into LDS and
+ *                         reads LDS without bank conflicts.
+ *    The blocked layout is the fast path; the row-major one is the serialized
+ *    checkpoint format (sglang PR #35994 report, key source excerpts).
  */
 #ifndef CK_H
 #define CK_H
@@ -74,9 +87,18 @@ typedef enum ck_act {
     CK_ACT_SWIGLU = 1    /* a = silu(x[:, 0:k]) * x[:, k:2k]  (gate, then up)  */
 } ck_act;
 
+typedef enum ck_layout {
+    CK_LAYOUT_ROWS = 0,    /* row-major int8 [R, K]                             */
+    CK_LAYOUT_BLOCKED = 1  /* 1 KB fragment blocks, rows padded to 256          */
+} ck_layout;
+
 /* Largest in_features: 127 * 127 * k must fit an int32 accumulator and one
  * activation row (k FP32 values) must fit the quantizer's LDS. */
 #define CK_MAX_K 32768
+
+/* Largest element count of one int8 operand or output buffer addressed with
+ * 32-bit offsets by the GEMM kernels. */
+#define CK_MAX_ELEMS 0x7fffffffLL
 
 /* Library version string (static storage). */
 const char *ck_version(void);
@@ -96,6 +118,21 @@ const char *ck_status_str(ck_status s);
 ck_status ck_weight_prep(const float *w, int64_t n, int64_t k, int32_t group,
                          int8_t *w_q, float *w_scale, void *stream);
 
+/* Padded row count and byte size of an int8 [rows, k] matrix in the blocked
+ * layout (0 for rows <= 0 or k <= 0). */
+int64_t ck_blocked_rows(int64_t rows);
+size_t ck_blocked_size(int64_t rows, int64_t k);
+
+/* One-time relayout of prepared weights into the blocked layout.
+ * Source: comfy-kitchen PR #248 "Performance improvements for qwen 3.x
+ * (Part 2)", "Description" (weights are relaid out once so the GEMM reads them
+ * linearly); the input is the serialized I8 [out_features, in_features] weight
+ * of sglang PR #35994 report, key source excerpts.
+ *   w_q      [n, k] int8 row-major, read
+ *   w_blk    ck_blocked_size(n, k) bytes, written (padding rows zeroed) */
+ck_status ck_weight_pack(const int8_t *w_q, int64_t n, int64_t k, int8_t *w_blk,
+                         void *stream);
+
 /* Activation quantizer: optional SwiGLU, rotation, per-token INT8.
  * Source: comfy-kitchen PR #277, "The key observation" (x_rot = x H, INT8 on
  * the weight's grid); sglang PR #44196, "Motivation" and "Accuracy Tests"
@@ -103,34 +140,40 @@ ck_status ck_weight_prep(const float *w, int64_t n, int64_t k, int32_t group,
  *   x        [m, ldx] BF16, read.  act == CK_ACT_NONE: row r uses x[r, 0:k],
  *            ldx >= k.  act == CK_ACT_SWIGLU: gate = x[r, 0:k],
  *            up = x[r, k:2k], ldx >= 2k.
- *   x_q      [m, k] int8, written (row stride k)
+ *   x_q      int8 codes, written, in `layout` (below)
  *   x_scale  [m]    FP32, written */
 ck_status ck_act_quant(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,
-                       int32_t act, int32_t group, int8_t *x_q, float *x_scale,
-                       void *stream);
+                       int32_t act, int32_t group, int32_t layout, int8_t *x_q,
+                       float *x_scale, void *stream);
+/*   layout   CK_LAYOUT_ROWS: x_q is [m, k] (m * k bytes); CK_LAYOUT_BLOCKED:
+ *            x_q is ck_blocked_size(m, k) bytes (padding rows not written). */
 
 /* ConvRot int8_linear: y = dequant(act_quant(x) . w_q^T).
  * Source: comfy-kitchen PR #277, "The key observation" and "Measured results";
  * sglang PR #44196, "Motivation" (int8_linear(..., input_act="swiglu")).
  *   x, ldx, act   as ck_act_quant
- *   w_q      [n, k] int8 from ck_weight_prep, read
+ *   w_q      int8 weight codes from ck_weight_prep (CK_LAYOUT_ROWS) or
+ *            ck_weight_pack (CK_LAYOUT_BLOCKED), read
  *   w_scale  [n]    FP32 from ck_weight_prep, read
+ *   layout   layout of w_q; the activation codes use the same one
  *   y        [m, n] BF16, written (row stride n)
  *   workspace  device buffer of at least ck_int8_linear_workspace_size(m, k)
  *            bytes, 256-byte aligned; clobbered (holds x_q and x_scale). */
 ck_status ck_int8_linear(const uint16_t *x, int64_t ldx, int32_t act,
-                         const int8_t *w_q, const float *w_scale, int64_t m,
-                         int64_t n, int64_t k, int32_t group, uint16_t *y,
-                         void *workspace, size_t workspace_bytes, void *stream);
+                         const int8_t *w_q, const float *w_scale, int32_t layout,
+                         int64_t m, int64_t n, int64_t k, int32_t group,
+                         uint16_t *y, void *workspace, size_t workspace_bytes,
+                         void *stream);
 size_t ck_int8_linear_workspace_size(int64_t m, int64_t k);
 
 /* The INT8 GEMM with its dequant epilogue alone (the second half of
  * ck_int8_linear), for callers that hold quantized activations.
- *   x_q [m, k] int8, x_scale [m] FP32, w_q [n, k] int8, w_scale [n] FP32 read;
- *   y [m, n] BF16 written. */
+ *   x_q, w_q int8 codes in `layout` (both), x_scale [m], w_scale [n] FP32,
+ *   read; y [m, n] BF16 written. */
 ck_status ck_int8_gemm_bf16(const int8_t *x_q, const float *x_scale,
-                            const int8_t *w_q, const float *w_scale, int64_t m,
-                            int64_t n, int64_t k, uint16_t *y, void *stream);
+                            const int8_t *w_q, const float *w_scale,
+                            int32_t layout, int64_t m, int64_t n, int64_t k,
+                            uint16_t *y, void *stream);
 
 /* SwiGLU MLP block: y = int8_linear(int8_linear(x, W_gu), W_down, swiglu).
  * Source: sglang PR #44196, "Motivation" and "Modifications" (one packed
@@ -140,13 +183,14 @@ ck_status ck_int8_gemm_bf16(const int8_t *x_q, const float *x_scale,
  *   x      [m, h]  BF16, read
  *   w_gu   [2i, h] int8 + s_gu [2i] FP32: rows 0..i-1 gate, i..2i-1 up
  *   w_down [h, i]  int8 + s_down [h] FP32
+ *   layout layout of both weights (and of the internal activation codes)
  *   y      [m, h]  BF16, written
  *   workspace  at least ck_swiglu_mlp_workspace_size(m, h, i) bytes,
  *          256-byte aligned; clobbered (x codes/scales, the [m, 2i] BF16
  *          gate|up output, its codes/scales). */
 ck_status ck_swiglu_mlp(const uint16_t *x, const int8_t *w_gu, const float *s_gu,
-                        const int8_t *w_down, const float *s_down, int64_t m,
-                        int64_t h, int64_t i, int32_t group, uint16_t *y,
+                        const int8_t *w_down, const float *s_down, int32_t layout,
+                        int64_t m, int64_t h, int64_t i, int32_t group, uint16_t *y,
                         void *workspace, size_t workspace_bytes, void *stream);
 size_t ck_swiglu_mlp_workspace_size(int64_t m, int64_t h, int64_t i);
 
@@ -154,8 +198,9 @@ size_t ck_swiglu_mlp_workspace_size(int64_t m, int64_t h, int64_t i);
 
 /* Raw int32 accumulators acc[m, n] = sum_k x_q[m, k] * w_q[n, k] from the
  * production GEMM kernels (comfy-kitchen PR #277, "Measured results"). */
-ck_status ck_int8_gemm_i32(const int8_t *x_q, const int8_t *w_q, int64_t m,
-                           int64_t n, int64_t k, int32_t *acc, void *stream);
+ck_status ck_int8_gemm_i32(const int8_t *x_q, const int8_t *w_q, int32_t layout,
+                           int64_t m, int64_t n, int64_t k, int32_t *acc,
+                           void *stream);
 
 /* FP32 silu of n BF16 gate values, by the quantizer's own device function
  * (sglang PR #44196, "Accuracy Tests": silu kept in FP32). */

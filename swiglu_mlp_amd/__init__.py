@@ -9,11 +9,16 @@ missing, importing any entry point raises.
 Entry points keep the C names:
 
 * ``ck_weight_prep(w, group)``           -> (w_q int8 [n, k], w_scale f32 [n, 1])
-* ``ck_act_quant(x, act, group, k=None)`` -> (x_q int8 [m, k], x_scale f32 [m, 1])
-* ``ck_int8_linear(x, w_q, w_scale, group, input_act=None)`` -> y bf16 [m, n]
-* ``ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale)``  -> y bf16 [m, n]
-* ``ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group)`` -> y bf16 [m, h]
+* ``ck_weight_pack(w_q)``                 -> w_q in the blocked layout [n_pad, k]
+* ``ck_act_quant(x, act, group, k=None, layout=...)`` -> (x_q, x_scale f32 [m, 1])
+* ``ck_int8_linear(x, w_q, w_scale, group, input_act=None, layout=...)`` -> y bf16
+* ``ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, layout=...)``  -> y bf16 [m, n]
+* ``ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group, layout=...)`` -> y bf16
 * test hooks ``ck_int8_gemm_i32``, ``ck_silu_f32``, ``ck_act_rotate_f32``
+
+``layout`` is ``"rows"`` (row-major int8, the serialized checkpoint format) or
+``"blocked"`` (the GEMM-native layout of include/ck.h, rows padded to 256).
+With blocked operands the logical row counts come from the scale vectors.
 
 Shapes and error behaviour follow sglang PR #35994 report, key source excerpts:
 an INT8 weight is 2-D ``[out_features, in_features]`` with an F32
@@ -29,6 +34,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libck_convrot.so")
 
 CK_ACT_NONE, CK_ACT_SWIGLU = 0, 1
+CK_LAYOUT_ROWS, CK_LAYOUT_BLOCKED = 0, 1
 _STATUS = {0: "CK_OK", 1: "CK_EINVAL", 2: "CK_ESHAPE", 3: "CK_EUNSUPPORTED",
            4: "CK_EWORKSPACE", 5: "CK_EHIP"}
 
@@ -54,11 +60,12 @@ def lib() -> ctypes.CDLL:
         p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
         sig = {
             "ck_weight_prep": [p, i64, i64, i32, p, p, p],
-            "ck_act_quant": [p, i64, i64, i64, i32, i32, p, p, p],
-            "ck_int8_linear": [p, i64, i32, p, p, i64, i64, i64, i32, p, p, sz, p],
-            "ck_int8_gemm_bf16": [p, p, p, p, i64, i64, i64, p, p],
-            "ck_swiglu_mlp": [p, p, p, p, p, i64, i64, i64, i32, p, p, sz, p],
-            "ck_int8_gemm_i32": [p, p, i64, i64, i64, p, p],
+            "ck_weight_pack": [p, i64, i64, p, p],
+            "ck_act_quant": [p, i64, i64, i64, i32, i32, i32, p, p, p],
+            "ck_int8_linear": [p, i64, i32, p, p, i32, i64, i64, i64, i32, p, p, sz, p],
+            "ck_int8_gemm_bf16": [p, p, p, p, i32, i64, i64, i64, p, p],
+            "ck_swiglu_mlp": [p, p, p, p, p, i32, i64, i64, i64, i32, p, p, sz, p],
+            "ck_int8_gemm_i32": [p, p, i32, i64, i64, i64, p, p],
             "ck_silu_f32": [p, i64, p, p],
             "ck_act_rotate_f32": [p, i64, i64, i64, i32, i32, p, p],
         }
@@ -70,6 +77,10 @@ def lib() -> ctypes.CDLL:
         L.ck_int8_linear_workspace_size.restype = sz
         L.ck_swiglu_mlp_workspace_size.argtypes = [i64, i64, i64]
         L.ck_swiglu_mlp_workspace_size.restype = sz
+        L.ck_blocked_rows.argtypes = [i64]
+        L.ck_blocked_rows.restype = i64
+        L.ck_blocked_size.argtypes = [i64, i64]
+        L.ck_blocked_size.restype = sz
         L.ck_status_str.argtypes = [ctypes.c_int]
         L.ck_status_str.restype = ctypes.c_char_p
         L.ck_version.argtypes = []
@@ -122,6 +133,27 @@ def _check_group(k, group):
         raise ValueError(f"in_features ({k}) must be divisible by group_size {group}")
 
 
+def _layout_code(layout):
+    if layout in ("rows", CK_LAYOUT_ROWS):
+        return CK_LAYOUT_ROWS
+    if layout in ("blocked", CK_LAYOUT_BLOCKED):
+        return CK_LAYOUT_BLOCKED
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def blocked_rows(rows: int) -> int:
+    return int(lib().ck_blocked_rows(rows))
+
+
+def _operand_rows(t, rows, layout, what):
+    """Check an int8 operand buffer holds `rows` logical rows in `layout`."""
+    need = rows if layout == CK_LAYOUT_ROWS else blocked_rows(rows)
+    if t.shape[0] != need:
+        raise ValueError(f"{what} needs {need} rows for {rows} logical rows in "
+                         f"{'row-major' if layout == CK_LAYOUT_ROWS else 'blocked'} layout, "
+                         f"got {t.shape[0]}")
+
+
 def _act_code(input_act):
     if input_act in (None, "none", CK_ACT_NONE):
         return CK_ACT_NONE
@@ -145,27 +177,42 @@ def ck_weight_prep(w, group: int = 128):
     return w_q, w_scale
 
 
-def ck_act_quant(x, input_act=None, group: int = 128, k: int | None = None):
+def ck_weight_pack(w_q):
+    """Relayout row-major int8 weight codes [n, k] into the blocked layout."""
+    import torch
+    _need(w_q, torch.int8, 2, "weight")
+    n, k = w_q.shape
+    out = torch.empty((blocked_rows(n), k), dtype=torch.int8, device=w_q.device)
+    _call("ck_weight_pack", w_q.data_ptr(), n, k, out.data_ptr(), _stream(w_q))
+    return out
+
+
+def ck_act_quant(x, input_act=None, group: int = 128, k: int | None = None, layout="rows"):
     import torch
     _need(x, torch.bfloat16, 2, "activation")
     act = _act_code(input_act)
+    lay = _layout_code(layout)
     m, ldx = x.shape
     if k is None:
         k = ldx // 2 if act == CK_ACT_SWIGLU else ldx
     _check_group(k, group)
-    x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    rows = m if lay == CK_LAYOUT_ROWS else blocked_rows(m)
+    x_q = torch.empty((rows, k), dtype=torch.int8, device=x.device)
     x_scale = torch.empty((m, 1), dtype=torch.float32, device=x.device)
-    _call("ck_act_quant", x.data_ptr(), ldx, m, k, act, group, x_q.data_ptr(),
+    _call("ck_act_quant", x.data_ptr(), ldx, m, k, act, group, lay, x_q.data_ptr(),
           x_scale.data_ptr(), _stream(x))
     return x_q, x_scale
 
 
 def ck_int8_linear(x, w_q, w_scale, group: int = 128, input_act=None, out=None,
-                   workspace=None):
+                   workspace=None, layout="rows"):
     import torch
     _need(x, torch.bfloat16, 2, "activation")
     _need(w_q, torch.int8, 2, "weight")
-    n, k = w_q.shape
+    lay = _layout_code(layout)
+    k = w_q.shape[1]
+    n = w_scale.shape[0]
+    _operand_rows(w_q, n, lay, "weight")
     _scale(w_scale, n, "weight_scale")
     act = _act_code(input_act)
     m, ldx = x.shape
@@ -177,39 +224,46 @@ def ck_int8_linear(x, w_q, w_scale, group: int = 128, input_act=None, out=None,
     ws_bytes = lib().ck_int8_linear_workspace_size(m, k)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
-    _call("ck_int8_linear", x.data_ptr(), ldx, act, w_q.data_ptr(), w_scale.data_ptr(), m, n, k,
-          group, y.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x))
+    _call("ck_int8_linear", x.data_ptr(), ldx, act, w_q.data_ptr(), w_scale.data_ptr(), lay, m, n,
+          k, group, y.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x))
     return y
 
 
-def ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, out=None):
+def ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, out=None, layout="rows"):
     import torch
     _need(x_q, torch.int8, 2, "activation codes")
     _need(w_q, torch.int8, 2, "weight")
-    m, k = x_q.shape
-    n = w_q.shape[0]
+    lay = _layout_code(layout)
+    k = x_q.shape[1]
+    m, n = x_scale.shape[0], w_scale.shape[0]
     if w_q.shape[1] != k:
         raise ValueError(f"in_features mismatch: activation {k}, weight {w_q.shape[1]}")
+    _operand_rows(x_q, m, lay, "activation codes")
+    _operand_rows(w_q, n, lay, "weight")
     _scale(x_scale, m, "activation scale")
     _scale(w_scale, n, "weight_scale")
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x_q.device)
     _call("ck_int8_gemm_bf16", x_q.data_ptr(), x_scale.data_ptr(), w_q.data_ptr(),
-          w_scale.data_ptr(), m, n, k, y.data_ptr(), _stream(x_q))
+          w_scale.data_ptr(), lay, m, n, k, y.data_ptr(), _stream(x_q))
     return y
 
 
-def ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group: int = 128, out=None, workspace=None):
+def ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group: int = 128, out=None, workspace=None,
+                  layout="rows"):
     import torch
     _need(x, torch.bfloat16, 2, "activation")
     _need(w_gu, torch.int8, 2, "gate_up weight")
     _need(w_down, torch.int8, 2, "down weight")
+    lay = _layout_code(layout)
     m, h = x.shape
-    i2, h2 = w_gu.shape
-    if h2 != h or i2 % 2:
+    i2 = s_gu.shape[0]
+    if w_gu.shape[1] != h or i2 % 2:
         raise ValueError(f"gate_up weight needs shape (2*intermediate, {h}), got {tuple(w_gu.shape)}")
     i = i2 // 2
-    if tuple(w_down.shape) != (h, i):
+    _operand_rows(w_gu, i2, lay, "gate_up weight")
+    if w_down.shape[1] != i or s_down.shape[0] != h:
         raise ValueError(f"down weight needs shape ({h}, {i}), got {tuple(w_down.shape)}")
+    _operand_rows(w_down, h, lay, "down weight")
     _scale(s_gu, i2, "gate_up weight_scale")
     _scale(s_down, h, "down weight_scale")
     _check_group(h, group)
@@ -219,21 +273,26 @@ def ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group: int = 128, out=None, wor
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     _call("ck_swiglu_mlp", x.data_ptr(), w_gu.data_ptr(), s_gu.data_ptr(), w_down.data_ptr(),
-          s_down.data_ptr(), m, h, i, group, y.data_ptr(), workspace.data_ptr(),
+          s_down.data_ptr(), lay, m, h, i, group, y.data_ptr(), workspace.data_ptr(),
           workspace.numel(), _stream(x))
     return y
 
 
-def ck_int8_gemm_i32(x_q, w_q):
+def ck_int8_gemm_i32(x_q, w_q, layout="rows", m: int | None = None, n: int | None = None):
+    """Raw int32 accumulators; with blocked operands pass the logical m and n."""
     import torch
     _need(x_q, torch.int8, 2, "activation codes")
     _need(w_q, torch.int8, 2, "weight")
-    m, k = x_q.shape
-    n = w_q.shape[0]
+    lay = _layout_code(layout)
+    k = x_q.shape[1]
+    m = x_q.shape[0] if m is None else m
+    n = w_q.shape[0] if n is None else n
     if w_q.shape[1] != k:
         raise ValueError(f"in_features mismatch: activation {k}, weight {w_q.shape[1]}")
+    _operand_rows(x_q, m, lay, "activation codes")
+    _operand_rows(w_q, n, lay, "weight")
     acc = torch.empty((m, n), dtype=torch.int32, device=x_q.device)
-    _call("ck_int8_gemm_i32", x_q.data_ptr(), w_q.data_ptr(), m, n, k, acc.data_ptr(),
+    _call("ck_int8_gemm_i32", x_q.data_ptr(), w_q.data_ptr(), lay, m, n, k, acc.data_ptr(),
           _stream(x_q))
     return acc
 
@@ -262,6 +321,7 @@ def ck_act_rotate_f32(x, input_act=None, group: int = 128, k: int | None = None)
 
 # short aliases
 weight_prep = ck_weight_prep
+weight_pack = ck_weight_pack
 act_quant = ck_act_quant
 int8_linear = ck_int8_linear
 int8_gemm_bf16 = ck_int8_gemm_bf16

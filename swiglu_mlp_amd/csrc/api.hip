@@ -34,6 +34,22 @@ ck_status check_act(int32_t act, int64_t ldx, int64_t k)
 
 ck_status from_hip(hipError_t e) { return e == hipSuccess ? CK_OK : CK_EHIP; }
 
+int64_t pad_rows(int64_t r) { return (r + 255) / 256 * 256; }
+
+ck_status check_layout(int32_t layout)
+{
+    return (layout == CK_LAYOUT_ROWS || layout == CK_LAYOUT_BLOCKED) ? CK_OK : CK_EINVAL;
+}
+
+// Every int8 operand and output of the GEMM kernels is addressed with 32-bit
+// byte offsets (buffer resources).
+ck_status check_gemm_extent(int64_t m, int64_t n, int64_t k)
+{
+    if (pad_rows(m) * k > CK_MAX_ELEMS || pad_rows(n) * k > CK_MAX_ELEMS || m * n * 4 > CK_MAX_ELEMS)
+        return CK_EUNSUPPORTED;
+    return CK_OK;
+}
+
 #define CK_TRY(expr)                     \
     do {                                 \
         const ck_status st_ = (expr);    \
@@ -67,36 +83,60 @@ ck_status ck_weight_prep(const float* w, int64_t n, int64_t k, int32_t group, in
     if (n == 0) return CK_OK;
     if (!w || !w_q || !w_scale) return CK_EINVAL;
     if (!aligned16(w) || !aligned16(w_q)) return CK_EINVAL;
-    return from_hip(ck::launch_quant_rows(2, w, k, n, k, group, w_q, w_scale, nullptr,
+    return from_hip(ck::launch_quant_rows(2, w, k, n, k, group, w_q, w_scale, nullptr, false,
                                           (hipStream_t)stream));
 }
 
+int64_t ck_blocked_rows(int64_t rows) { return rows <= 0 ? 0 : pad_rows(rows); }
+
+size_t ck_blocked_size(int64_t rows, int64_t k)
+{
+    if (rows <= 0 || k <= 0) return 0;
+    return (size_t)pad_rows(rows) * (size_t)k;
+}
+
+ck_status ck_weight_pack(const int8_t* w_q, int64_t n, int64_t k, int8_t* w_blk, void* stream)
+{
+    if (n < 0 || k < 1 || k % 64 != 0) return CK_ESHAPE;
+    if (k > CK_MAX_K || pad_rows(n) * k > CK_MAX_ELEMS) return CK_EUNSUPPORTED;
+    if (n == 0) return CK_OK;
+    if (!w_q || !w_blk) return CK_EINVAL;
+    if (!aligned16(w_q) || !aligned16(w_blk)) return CK_EINVAL;
+    return from_hip(ck::launch_pack_blocked(w_q, n, k, w_blk, (hipStream_t)stream));
+}
+
 ck_status ck_act_quant(const uint16_t* x, int64_t ldx, int64_t m, int64_t k, int32_t act,
-                       int32_t group, int8_t* x_q, float* x_scale, void* stream)
+                       int32_t group, int32_t layout, int8_t* x_q, float* x_scale, void* stream)
 {
     CK_TRY(check_k(k, group));
     CK_TRY(check_act(act, ldx, k));
+    CK_TRY(check_layout(layout));
     if (m < 0) return CK_ESHAPE;
+    if (layout == CK_LAYOUT_BLOCKED && pad_rows(m) * k > CK_MAX_ELEMS) return CK_EUNSUPPORTED;
     if (m == 0) return CK_OK;
     if (!x || !x_q || !x_scale) return CK_EINVAL;
     if (!aligned16(x) || !aligned16(x_q)) return CK_EINVAL;
     return from_hip(ck::launch_quant_rows(act == CK_ACT_SWIGLU ? 1 : 0, x, ldx, m, k, group, x_q,
-                                          x_scale, nullptr, (hipStream_t)stream));
+                                          x_scale, nullptr, layout == CK_LAYOUT_BLOCKED,
+                                          (hipStream_t)stream));
 }
 
+// Sized for either layout (the blocked codes are the larger).
 size_t ck_int8_linear_workspace_size(int64_t m, int64_t k)
 {
     if (m <= 0 || k <= 0) return 0;
-    return round_up((size_t)m * (size_t)k) + round_up((size_t)m * sizeof(float));
+    return round_up((size_t)pad_rows(m) * (size_t)k) + round_up((size_t)m * sizeof(float));
 }
 
 static ck_status check_gemm_args(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
-                                 const float* w_scale, int64_t m, int64_t n, int64_t k,
-                                 const void* y, bool need_scales)
+                                 const float* w_scale, int32_t layout, int64_t m, int64_t n,
+                                 int64_t k, const void* y, bool need_scales)
 {
+    CK_TRY(check_layout(layout));
     if (k < 1 || k % 64 != 0) return CK_ESHAPE;
     if (k > CK_MAX_K) return CK_EUNSUPPORTED;
     if (m < 0 || n < 0 || n % 16 != 0) return CK_ESHAPE;
+    CK_TRY(check_gemm_extent(m, n, k));
     if (m == 0 || n == 0) return CK_OK;
     if (!x_q || !w_q || !y) return CK_EINVAL;
     if (need_scales && (!x_scale || !w_scale)) return CK_EINVAL;
@@ -106,60 +146,71 @@ static ck_status check_gemm_args(const int8_t* x_q, const float* x_scale, const 
 }
 
 ck_status ck_int8_gemm_bf16(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
-                            const float* w_scale, int64_t m, int64_t n, int64_t k, uint16_t* y,
-                            void* stream)
+                            const float* w_scale, int32_t layout, int64_t m, int64_t n, int64_t k,
+                            uint16_t* y, void* stream)
 {
-    CK_TRY(check_gemm_args(x_q, x_scale, w_q, w_scale, m, n, k, y, true));
+    CK_TRY(check_gemm_args(x_q, x_scale, w_q, w_scale, layout, m, n, k, y, true));
     if (m == 0 || n == 0) return CK_OK;
     return from_hip(ck::launch_gemm_bf16(x_q, x_scale, w_q, w_scale, m, n, k, y,
-                                         (hipStream_t)stream));
+                                         layout == CK_LAYOUT_BLOCKED, (hipStream_t)stream));
 }
 
-ck_status ck_int8_gemm_i32(const int8_t* x_q, const int8_t* w_q, int64_t m, int64_t n, int64_t k,
-                           int32_t* acc, void* stream)
+ck_status ck_int8_gemm_i32(const int8_t* x_q, const int8_t* w_q, int32_t layout, int64_t m,
+                           int64_t n, int64_t k, int32_t* acc, void* stream)
 {
-    CK_TRY(check_gemm_args(x_q, nullptr, w_q, nullptr, m, n, k, acc, false));
+    CK_TRY(check_gemm_args(x_q, nullptr, w_q, nullptr, layout, m, n, k, acc, false));
     if (m == 0 || n == 0) return CK_OK;
-    return from_hip(ck::launch_gemm_i32(x_q, w_q, m, n, k, acc, (hipStream_t)stream));
+    return from_hip(ck::launch_gemm_i32(x_q, w_q, m, n, k, acc, layout == CK_LAYOUT_BLOCKED,
+                                        (hipStream_t)stream));
 }
 
 ck_status ck_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, const int8_t* w_q,
-                         const float* w_scale, int64_t m, int64_t n, int64_t k, int32_t group,
-                         uint16_t* y, void* workspace, size_t workspace_bytes, void* stream)
+                         const float* w_scale, int32_t layout, int64_t m, int64_t n, int64_t k,
+                         int32_t group, uint16_t* y, void* workspace, size_t workspace_bytes,
+                         void* stream)
 {
     CK_TRY(check_k(k, group));
     CK_TRY(check_act(act, ldx, k));
+    CK_TRY(check_layout(layout));
     if (m < 0 || n < 0 || n % 16 != 0) return CK_ESHAPE;
+    CK_TRY(check_gemm_extent(m, n, k));
     if (m == 0 || n == 0) return CK_OK;
     if (!x || !w_q || !w_scale || !y) return CK_EINVAL;
     if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_scale) || !aligned16(y)) return CK_EINVAL;
     const size_t need = ck_int8_linear_workspace_size(m, k);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
         return CK_EWORKSPACE;
+    const bool blocked = layout == CK_LAYOUT_BLOCKED;
     int8_t* xq = static_cast<int8_t*>(workspace);
-    float* sx = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up((size_t)m * k));
+    float* sx = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         round_up((size_t)pad_rows(m) * (size_t)k));
     hipStream_t st = (hipStream_t)stream;
     CK_TRY(from_hip(ck::launch_quant_rows(act == CK_ACT_SWIGLU ? 1 : 0, x, ldx, m, k, group, xq,
-                                          sx, nullptr, st)));
-    return from_hip(ck::launch_gemm_bf16(xq, sx, w_q, w_scale, m, n, k, y, st));
+                                          sx, nullptr, blocked, st)));
+    return from_hip(ck::launch_gemm_bf16(xq, sx, w_q, w_scale, m, n, k, y, blocked, st));
 }
 
+// Sized for either layout: x codes, x scales, the [m, 2i] BF16 gate|up
+// output, its codes and scales.
 size_t ck_swiglu_mlp_workspace_size(int64_t m, int64_t h, int64_t i)
 {
     if (m <= 0 || h <= 0 || i <= 0) return 0;
-    const size_t M = (size_t)m, H = (size_t)h, I = (size_t)i;
-    return round_up(M * H) + round_up(M * 4) + round_up(M * 2 * I * 2) + round_up(M * I) +
+    const size_t M = (size_t)m, MP = (size_t)pad_rows(m), H = (size_t)h, I = (size_t)i;
+    return round_up(MP * H) + round_up(M * 4) + round_up(M * 2 * I * 2) + round_up(MP * I) +
            round_up(M * 4);
 }
 
 ck_status ck_swiglu_mlp(const uint16_t* x, const int8_t* w_gu, const float* s_gu,
-                        const int8_t* w_down, const float* s_down, int64_t m, int64_t h, int64_t i,
-                        int32_t group, uint16_t* y, void* workspace, size_t workspace_bytes,
-                        void* stream)
+                        const int8_t* w_down, const float* s_down, int32_t layout, int64_t m,
+                        int64_t h, int64_t i, int32_t group, uint16_t* y, void* workspace,
+                        size_t workspace_bytes, void* stream)
 {
     CK_TRY(check_k(h, group));   // stage 1 contracts over h
     CK_TRY(check_k(i, group));   // stage 2 contracts over i
+    CK_TRY(check_layout(layout));
     if (m < 0 || h % 16 != 0) return CK_ESHAPE;
+    CK_TRY(check_gemm_extent(m, 2 * i, h));
+    CK_TRY(check_gemm_extent(m, h, i));
     if (m == 0) return CK_OK;
     if (!x || !w_gu || !s_gu || !w_down || !s_down || !y) return CK_EINVAL;
     if (!aligned16(x) || !aligned16(w_gu) || !aligned16(s_gu) || !aligned16(w_down) ||
@@ -168,20 +219,21 @@ ck_status ck_swiglu_mlp(const uint16_t* x, const int8_t* w_gu, const float* s_gu
     const size_t need = ck_swiglu_mlp_workspace_size(m, h, i);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
         return CK_EWORKSPACE;
-    const size_t M = (size_t)m, H = (size_t)h, I = (size_t)i;
+    const size_t M = (size_t)m, MP = (size_t)pad_rows(m), H = (size_t)h, I = (size_t)i;
+    const bool blocked = layout == CK_LAYOUT_BLOCKED;
     char* p = static_cast<char*>(workspace);
-    int8_t* xq = reinterpret_cast<int8_t*>(p);          p += round_up(M * H);
+    int8_t* xq = reinterpret_cast<int8_t*>(p);          p += round_up(MP * H);
     float* sx = reinterpret_cast<float*>(p);            p += round_up(M * 4);
     uint16_t* y1 = reinterpret_cast<uint16_t*>(p);      p += round_up(M * 2 * I * 2);
-    int8_t* hq = reinterpret_cast<int8_t*>(p);          p += round_up(M * I);
+    int8_t* hq = reinterpret_cast<int8_t*>(p);          p += round_up(MP * I);
     float* sh = reinterpret_cast<float*>(p);
     hipStream_t st = (hipStream_t)stream;
     // stage 1: packed [gate | up] projection, BF16 [m, 2i]
-    CK_TRY(from_hip(ck::launch_quant_rows(0, x, h, m, h, group, xq, sx, nullptr, st)));
-    CK_TRY(from_hip(ck::launch_gemm_bf16(xq, sx, w_gu, s_gu, m, 2 * i, h, y1, st)));
+    CK_TRY(from_hip(ck::launch_quant_rows(0, x, h, m, h, group, xq, sx, nullptr, blocked, st)));
+    CK_TRY(from_hip(ck::launch_gemm_bf16(xq, sx, w_gu, s_gu, m, 2 * i, h, y1, blocked, st)));
     // stage 2: silu(gate) * up inside the down projection's quantizer
-    CK_TRY(from_hip(ck::launch_quant_rows(1, y1, 2 * i, m, i, group, hq, sh, nullptr, st)));
-    return from_hip(ck::launch_gemm_bf16(hq, sh, w_down, s_down, m, h, i, y, st));
+    CK_TRY(from_hip(ck::launch_quant_rows(1, y1, 2 * i, m, i, group, hq, sh, nullptr, blocked, st)));
+    return from_hip(ck::launch_gemm_bf16(hq, sh, w_down, s_down, m, h, i, y, blocked, st));
 }
 
 ck_status ck_silu_f32(const uint16_t* gate, int64_t n, float* out, void* stream)
@@ -202,7 +254,7 @@ ck_status ck_act_rotate_f32(const uint16_t* x, int64_t ldx, int64_t m, int64_t k
     if (!x || !u) return CK_EINVAL;
     if (!aligned16(x) || !aligned16(u)) return CK_EINVAL;
     return from_hip(ck::launch_quant_rows(act == CK_ACT_SWIGLU ? 1 : 0, x, ldx, m, k, group,
-                                          nullptr, nullptr, u, (hipStream_t)stream));
+                                          nullptr, nullptr, u, false, (hipStream_t)stream));
 }
 
 }  // extern "C"

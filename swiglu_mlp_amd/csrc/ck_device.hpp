@@ -23,6 +23,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two FP32 values -> packed BF16 pair (lo = a, hi = b), round-to-nearest-even:
+// one v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // ---------------------------------------------------------------------------
 // FP32 silu.  sglang PR #44196, "Accuracy Tests": the fused quantizer keeps
 // silu(gate) * up in FP32.  The evaluation procedure is fixed so the result is

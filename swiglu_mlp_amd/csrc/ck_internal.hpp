@@ -11,18 +11,37 @@ namespace ck {
 // kind: 0 = BF16 x[r, 0:k]; 1 = BF16 [gate | up] with SwiGLU; 2 = FP32 rows.
 // u_out != nullptr selects the diagnostic variant that writes the unnormalised
 // rotated FP32 rows instead of codes and scales.
+// blocked: write the codes in the blocked layout (rows padded to 256, see
+// include/ck.h) instead of row-major.
 hipError_t launch_quant_rows(int kind, const void* src, int64_t ld, int64_t m, int64_t k, int g,
-                             int8_t* q, float* s, float* u_out, hipStream_t st);
+                             int8_t* q, float* s, float* u_out, bool blocked, hipStream_t st);
+
+// Row-major [n, k] int8 -> blocked layout, padding rows zero-filled.
+hipError_t launch_pack_blocked(const int8_t* w, int64_t n, int64_t k, int8_t* out, hipStream_t st);
 
 // FP32 silu of n BF16 values (the quantizer's device function).
 hipError_t launch_silu(const uint16_t* g, int64_t n, float* out, hipStream_t st);
 
-// y[m, n] = bf16(fl(fl(f32(x_q . w_q^T) * sx[m]) * sw[n])).
+// y[m, n] = bf16(fl(fl(f32(x_q . w_q^T) * sx[m]) * sw[n])); both operands in
+// the row-major or the blocked layout.
 hipError_t launch_gemm_bf16(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                            int64_t m, int64_t n, int64_t k, uint16_t* y, hipStream_t st);
+                            int64_t m, int64_t n, int64_t k, uint16_t* y, bool blocked, hipStream_t st);
 
 // acc[m, n] = x_q . w_q^T in int32.
 hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
-                           int32_t* acc, hipStream_t st);
+                           int32_t* acc, bool blocked, hipStream_t st);
+
+// Blocked-layout GEMM (gemm_blk.hip).
+hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                           int64_t m, int64_t n, int64_t k, void* out, bool out_i32, int num_cu,
+                           hipStream_t st);
+
+int num_cus();
+
+// Persistent large-tile GEMM (256 x bn tiles, bn = 256 or 192), one workgroup
+// per CU; writes BF16 y (with scales) or int32 acc (out_i32).
+hipError_t launch_gemm_big(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                           int64_t m, int64_t n, int64_t k, void* out, bool out_i32, int bn,
+                           int num_cu, hipStream_t st);
 
 }  // namespace ck

@@ -197,24 +197,47 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_i8_kernel(
 // ---------------------------------------------------------------------------
 namespace {
 
+// Candidate shapes: the two persistent large-tile kernels (gemm_big.hip) and
+// the three generic tiles above.  `eff` is the relative per-CU MFMA
+// efficiency of the shape; the choice minimises rounds * tile area / eff,
+// where a round is one tile per CU.
 struct TileCfg {
-    int bm, bn, nthreads;
-    double eff;   // relative per-CU efficiency of the shape (larger tiles reuse more)
+    int bm, bn;
+    bool big;
+    double eff;
 };
 constexpr TileCfg kCfgs[] = {
-    {256, 256, 256, 1.00},
-    {128, 128, 256, 0.70},
-    {64, 128, 256, 0.40},
+    {256, 256, true, 1.00},
+    {256, 192, true, 0.97},
+    {128, 128, false, 0.60},
+    {64, 128, false, 0.35},
 };
-constexpr int kNumCU = 256;
 
-int pick_cfg(int64_t m, int64_t n)
+}  // namespace
+
+int num_cus()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+namespace {
+
+int pick_cfg(int64_t m, int64_t n, int ncu)
 {
     int best = 0;
     double best_t = 0;
-    for (int c = 0; c < 3; ++c) {
+    for (int c = 0; c < 4; ++c) {
         const int64_t tiles = ((m + kCfgs[c].bm - 1) / kCfgs[c].bm) * ((n + kCfgs[c].bn - 1) / kCfgs[c].bn);
-        const int64_t rounds = (tiles + kNumCU - 1) / kNumCU;
+        const int64_t rounds = (tiles + ncu - 1) / ncu;
         const double t = (double)rounds * kCfgs[c].bm * kCfgs[c].bn / kCfgs[c].eff;
         if (c == 0 || t < best_t) {
             best = c;
@@ -241,15 +264,16 @@ template <bool I32>
 hipError_t launch_gemm_t(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                          int64_t m, int64_t n, int64_t k, void* out, hipStream_t st)
 {
-    const int cfg = pick_cfg(m, n);
+    const int ncu = num_cus();
+    const int cfg = pick_cfg(m, n, ncu);
+    if (kCfgs[cfg].big)
+        return launch_gemm_big(xq, sx, wq, sw, m, n, k, out, I32, kCfgs[cfg].bn, ncu, st);
     const bool bk128 = (k % 128) == 0;
     const int M = (int)m, N = (int)n, K = (int)k;
-    switch (cfg * 2 + (bk128 ? 1 : 0)) {
-        case 0: return launch_one<256, 256, 64, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st);
-        case 1: return launch_one<256, 256, 128, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st);
-        case 2: return launch_one<128, 128, 64, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st);
-        case 3: return launch_one<128, 128, 128, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st);
-        case 4: return launch_one<64, 128, 64, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st);
+    switch ((cfg - 2) * 2 + (bk128 ? 1 : 0)) {
+        case 0: return launch_one<128, 128, 64, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st);
+        case 1: return launch_one<128, 128, 128, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st);
+        case 2: return launch_one<64, 128, 64, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st);
         default: return launch_one<64, 128, 128, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st);
     }
 }
@@ -257,16 +281,18 @@ hipError_t launch_gemm_t(const int8_t* xq, const float* sx, const int8_t* wq, co
 }  // namespace
 
 hipError_t launch_gemm_bf16(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                            int64_t m, int64_t n, int64_t k, uint16_t* y, hipStream_t st)
+                            int64_t m, int64_t n, int64_t k, uint16_t* y, bool blocked, hipStream_t st)
 {
     if (m == 0 || n == 0) return hipSuccess;
+    if (blocked) return launch_gemm_blk(xq, sx, wq, sw, m, n, k, y, false, num_cus(), st);
     return launch_gemm_t<false>(xq, sx, wq, sw, m, n, k, y, st);
 }
 
 hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
-                           int32_t* acc, hipStream_t st)
+                           int32_t* acc, bool blocked, hipStream_t st)
 {
     if (m == 0 || n == 0) return hipSuccess;
+    if (blocked) return launch_gemm_blk(xq, nullptr, wq, nullptr, m, n, k, acc, true, num_cus(), st);
     return launch_gemm_t<true>(xq, nullptr, wq, nullptr, m, n, k, acc, st);
 }
 

@@ -1,0 +1,372 @@
+// gemm_blk.hip -- INT8 GEMM for gfx950 on operands stored in the blocked
+// layout (include/ck.h, CK_LAYOUT_BLOCKED), with the ConvRot dequant
+// epilogue y = bf16(fl(fl(f32(acc) * sx[m]) * sw[n])).
+//
+// Sources: comfy-kitchen PR #277, "The key observation" (the GEMM runs in the
+// rotated basis, y = x_rot W_rot^T) and "Measured results" (int32
+// accumulation); sglang PR #35994 report, key source excerpts (F32
+// per-output-row weight scale); comfy-kitchen PR #248 "Performance
+// improvements for qwen 3.x (Part 2)", "Description" (weights relaid out once
+// so the GEMM reads them linearly).
+//
+// Why the blocked layout: on MI355X the L2 -> LDS stream rate depends on how
+// many cache lines one load instruction touches.  Measured with
+// buffer_load_dwordx4 ... lds over all 256 CUs: 1 KB contiguous per
+// instruction streams at ~27 TB/s, 8 rows x 128 B at ~15 TB/s, 16 rows x 64 B
+// at ~12.7 TB/s.  A 256 x 256 tile needs ~66 GB/s per CU (~17 TB/s) at full
+// MFMA rate.  In the blocked layout each 1 KB block is one 32-row x 32-byte
+// MFMA operand fragment in lane order, so
+//   * one load instruction moves one contiguous KB into LDS, and
+//   * every ds_read_b128 of a fragment reads 1 KB linearly (no bank conflicts).
+//
+// Kernel structure (one wave per SIMD, 4 waves in a 2 x 2 grid):
+//   * Workgroup tile BM x BN (m x n), wave sub-tile BM/2 x BN/2 built from
+//     32 x 32 fragments of v_mfma_i32_32x32x32_i8 with accumulators in AGPRs.
+//     The MFMA computes D[n][m] = sum_k W[n][k] X[m][k] (W is the A operand),
+//     so a lane ends with 4 consecutive n of one output row m.
+//   * K advances 64 bytes per stage (two 32-byte k-slices).  Stages live in a
+//     ring of 4 LDS buffers; loads run 3 stages ahead.  Each stage is split in
+//     two halves around one barrier: the first half multiplies k-slice 0,
+//     reads k-slice 1's fragments and issues the loads of stage s+3; the second
+//     multiplies k-slice 1 and reads the next stage's k-slice-0 fragments, so
+//     MFMAs never wait on LDS.  sched_group_barrier interleaves the LDS reads and
+//     the loads between MFMAs.
+//   * Workgroups are persistent; the stage sequence runs across a workgroup's
+//     tiles so the next tile's loads overlap the current tile's epilogue.  In
+//     each round the workgroups of one XCD take consecutive tiles of a grouped
+//     order, so they share operand panels in that XCD's L2.
+#include "ck_device.hpp"
+#include "ck_internal.hpp"
+
+#include <type_traits>
+
+namespace ck {
+namespace blk {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt encodings (gfx9: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8])
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// s_barrier without a memory fence (a fenced __syncthreads would also wait for
+// the loads still in flight for later stages); the empty asm statements stop
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void workgroup_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int BM_, int BN_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_;
+    static constexpr int NBUF = 4, P = 3;          // LDS ring, stages in flight
+    static constexpr int FM = BM / 64;             // fragments per wave along m
+    static constexpr int FN = BN / 64;             // fragments per wave along n
+    static constexpr int A_BLK = (BN / 32) * 2;    // W blocks per stage
+    static constexpr int B_BLK = (BM / 32) * 2;    // X blocks per stage
+    static constexpr int BLK = A_BLK + B_BLK;
+    static constexpr int L = BLK / 4;              // block loads per lane per stage
+    static constexpr int STAGE = BLK * 1024;
+    static_assert(BLK % 4 == 0, "blocks must split evenly over 4 waves");
+};
+
+__device__ __forceinline__ void tile_coords(int j, int tiles_m, int tiles_n, int group_m, int& tm,
+                                            int& tn)
+{
+    const int width = group_m * tiles_n;
+    const int grp = j / width;
+    const int first_m = grp * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    tm = first_m + (j % width) % gm;
+    tn = (j % width) / gm;
+}
+
+template <int BM, int BN, bool OUT_I32>
+__global__ __launch_bounds__(256) void gemm_blk_kernel(
+    const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
+    const float* __restrict__ sw, int M, int N, int K, int m_rows, int n_rows, void* __restrict__ out,
+    int tiles_m, int tiles_n, int group_m)
+{
+    // The body uses AMDGPU-only types (buffer resources); the host pass only
+    // needs this function's launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = Cfg<BM, BN>;
+    __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = gridDim.x;
+    const int b = blockIdx.x;
+    const int tiles = tiles_m * tiles_n;
+    const int KT = K / 64;          // stages per tile
+    const int KB = K / 32;          // k-slices (blocks) per 32-row block
+    const int my_tiles = (tiles - b + G - 1) / G;
+    const int total = my_tiles * KT;
+    if (total == 0) return;
+
+    // Within a full round the workgroups of one XCD (b % 8) take consecutive
+    // tiles; the last, partial round keeps the plain order.  Branch-free, so
+    // the load-issue code stays in one scheduling region with the MFMAs.
+    const bool xcd_order = (G & 7) == 0;
+    const int b_xcd = (b & 7) * (G >> 3) + (b >> 3);
+    auto tile_of = [&](int q) {
+        const bool full = xcd_order & ((q + 1) * G <= tiles);
+        return q * G + (full ? b_xcd : b);
+    };
+    // Operand buffers span the padded row counts m_rows, n_rows (multiples of
+    // 256), so every block a tile touches is inside the buffer.
+    const __amdgpu_buffer_rsrc_t rs_w =
+        __builtin_amdgcn_make_buffer_rsrc((void*)wq, (short)0, n_rows * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_x =
+        __builtin_amdgcn_make_buffer_rsrc((void*)xq, (short)0, m_rows * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_o =
+        __builtin_amdgcn_make_buffer_rsrc(out, (short)0, M * N * (OUT_I32 ? 4 : 2), 0x00020000);
+
+    // Loads of stage min(s, total - 1) into ring slot `slot` (= s % NBUF).
+    // Past the last stage this reloads the last stage into a slot nobody reads
+    // again, which keeps the loop body free of branches and the wait counts
+    // constant.
+    auto issue = [&](int s, int slot) {
+        const int sc = min(s, total - 1);
+        const int q = sc / KT;
+        const int kt = sc - q * KT;
+        int tm, tn;
+        tile_coords(tile_of(q), tiles_m, tiles_n, group_m, tm, tn);
+        char* dst = smem + slot * C::STAGE;
+#pragma unroll
+        for (int i = 0; i < C::L; ++i) {
+            const int bi = wave + 4 * i;                 // wave-uniform block index
+            const bool is_a = bi < C::A_BLK;
+            const int rel = is_a ? bi : bi - C::A_BLK;
+            const int rb = (is_a ? tn * (BN / 32) : tm * (BM / 32)) + (rel >> 1);
+            const uint32_t boff = (uint32_t)(rb * KB + 2 * kt + (rel & 1)) * 1024u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? rs_w : rs_x, (lds_void_t*)(dst + bi * 1024),
+                                                     16, boff + (uint32_t)lane * 16u, 0, 0, 0);
+        }
+    };
+
+    v16i acc[C::FN][C::FM];
+    const int lr = lane & 31;
+    const int lh = lane >> 5;
+    const int wm0 = (wave & 1) * (BM / 2);
+    const int wn0 = (wave >> 1) * (BN / 2);
+    auto frag_a = [&](int buf, int i, int ks) {
+        const int rb = (wn0 >> 5) + i;
+        return *reinterpret_cast<const v4i*>(smem + buf * C::STAGE + (rb * 2 + ks) * 1024 + lane * 16);
+    };
+    auto frag_b = [&](int buf, int j, int ks) {
+        const int rb = (wm0 >> 5) + j;
+        return *reinterpret_cast<const v4i*>(smem + buf * C::STAGE + (C::A_BLK + rb * 2 + ks) * 1024 +
+                                             lane * 16);
+    };
+
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    static_assert(C::P == 3 && C::NBUF == 4, "prologue and loop unrolling assume P = 3, NBUF = 4");
+    wait_vmcnt<2 * C::L>();
+    workgroup_barrier();
+    v4i fa[C::FN], fb[C::FM];
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i) fa[i] = frag_a(0, i, 0);
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) fb[j] = frag_b(0, j, 0);
+
+    // One stage.  BUF is the stage's ring slot (s % NBUF); unrolling the stage
+    // loop by NBUF makes every LDS offset a constant, which lets the compiler
+    // see that the fragment reads never touch the slots the in-flight loads
+    // write, so it does not drain those loads before each read.
+    auto stage = [&](int s, auto buf_c) {
+        constexpr int buf = decltype(buf_c)::value;
+        constexpr int nbuf = (buf + 1) % C::NBUF;
+        constexpr int lbuf = (buf + C::P) % C::NBUF;
+        v4i ga[C::FN], gb[C::FM];
+        // first half: k-slice 0 MFMAs (zero accumulator input on a tile's first
+        // stage), k-slice 1 fragment reads, loads of stage s + P
+        auto half0 = [&](auto first) {
+#pragma unroll
+            for (int i = 0; i < C::FN; ++i) ga[i] = frag_a(buf, i, 1);
+#pragma unroll
+            for (int j = 0; j < C::FM; ++j) gb[j] = frag_b(buf, j, 1);
+#pragma unroll
+            for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FM; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        fa[i], fb[j], decltype(first)::value ? v16i{} : acc[i][j], 0, 0, 0);
+            issue(s + C::P, lbuf);
+            constexpr int NMF = C::FN * C::FM;
+            constexpr int NDS = C::FN + C::FM;
+#pragma unroll
+            for (int k = 0; k < NMF; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+                if (k < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+                if (k < C::L) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM load
+            }
+        };
+        if (s % KT == 0) half0(std::true_type{});
+        else half0(std::false_type{});
+
+        wait_lgkmcnt0();              // this wave's k-slice 1 fragments are in registers
+        wait_vmcnt<2 * C::L>();       // stage s + 1 has landed (s + 2, s + 3 may be in flight)
+        workgroup_barrier();          // ... for every wave; slot buf is no longer read
+
+        // second half: k-slice 1 MFMAs, next stage's k-slice 0 fragment reads
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i) fa[i] = frag_a(nbuf, i, 0);
+#pragma unroll
+        for (int j = 0; j < C::FM; ++j) fb[j] = frag_b(nbuf, j, 0);
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FM; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ga[i], gb[j], acc[i][j], 0, 0, 0);
+        {
+            constexpr int NMF = C::FN * C::FM;
+            constexpr int NDS = C::FN + C::FM;
+#pragma unroll
+            for (int k = 0; k < NMF; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                if (k < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+            }
+        }
+        if (s % KT == KT - 1) {
+            // ---- epilogue of tile s / KT ----
+            // D fragment (32 x 32): lane l holds column l % 32 (output row m)
+            // and, in registers 4 qd .. 4 qd + 3, rows 8 qd + 4 (l / 32) + 0..3
+            // (four consecutive output columns n).  Stores go through a buffer
+            // resource, so rows past M fall outside it and are dropped.
+            int tm, tn;
+            tile_coords(tile_of(s / KT), tiles_m, tiles_n, group_m, tm, tn);
+            const int m_base = tm * BM + wm0 + lr;
+            const int n_base = tn * BN + wn0 + 4 * lh;
+            float sxm[C::FM];
+#pragma unroll
+            for (int j = 0; j < C::FM; ++j) {
+                sxm[j] = 0.0f;
+                if constexpr (!OUT_I32) sxm[j] = sx[min(m_base + 32 * j, M - 1)];
+            }
+#pragma unroll
+            for (int i = 0; i < C::FN; ++i) {
+                float4 s4[4];
+                bool n_ok[4];
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int n = n_base + 32 * i + 8 * qd;
+                    n_ok[qd] = n < N;
+                    s4[qd] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if constexpr (!OUT_I32) s4[qd] = *reinterpret_cast<const float4*>(sw + min(n, N - 4));
+                }
+#pragma unroll
+                for (int j = 0; j < C::FM; ++j) {
+                    // copy one fragment out of the accumulators here, not all
+                    // of them up front
+                    v16i f = acc[i][j];
+                    asm volatile("" : "+v"(f));
+                    const uint32_t row = (uint32_t)(m_base + 32 * j) * (uint32_t)N;
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd) {
+                        if (!n_ok[qd]) continue;
+                        const uint32_t o = row + (uint32_t)(n_base + 32 * i + 8 * qd);
+                        if constexpr (OUT_I32) {
+                            const v4i d = {f[4 * qd], f[4 * qd + 1], f[4 * qd + 2], f[4 * qd + 3]};
+                            __builtin_amdgcn_raw_buffer_store_b128(d, rs_o, o * 4u, 0, 0);
+                        } else {
+                            const float y0 = ((float)f[4 * qd + 0] * sxm[j]) * s4[qd].x;
+                            const float y1 = ((float)f[4 * qd + 1] * sxm[j]) * s4[qd].y;
+                            const float y2 = ((float)f[4 * qd + 2] * sxm[j]) * s4[qd].z;
+                            const float y3 = ((float)f[4 * qd + 3] * sxm[j]) * s4[qd].w;
+                            const u32x2 d = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+                            __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, o * 2u, 0, 0);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    };
+
+    for (int s0 = 0; s0 < total; s0 += C::NBUF) {
+        stage(s0, std::integral_constant<int, 0>{});
+        if (s0 + 1 < total) stage(s0 + 1, std::integral_constant<int, 1>{});
+        if (s0 + 2 < total) stage(s0 + 2, std::integral_constant<int, 2>{});
+        if (s0 + 3 < total) stage(s0 + 3, std::integral_constant<int, 3>{});
+    }
+    wait_vmcnt<0>();   // no LDS load may land after the workgroup retires
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+template <int BM, int BN, bool I32>
+hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int M, int N,
+                  int K, void* out, int num_cu, hipStream_t st)
+{
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    const int tiles = tiles_m * tiles_n;
+    // LDS per workgroup: 4 stages of (BM + BN) x 64 bytes; 160 KB per CU.
+    const int lds = 4 * (BM + BN) * 64;
+    const int per_cu = (160 * 1024) / lds >= 2 ? 2 : 1;
+    const int slots = num_cu * per_cu;
+    const int grid = tiles < slots ? tiles : slots;
+    const int group_m = tiles_m < 4 ? tiles_m : 4;
+    const int m_rows = (M + 255) / 256 * 256;
+    const int n_rows = (N + 255) / 256 * 256;
+    hipLaunchKernelGGL((gemm_blk_kernel<BM, BN, I32>), dim3(grid), dim3(256), 0, st, xq, sx, wq, sw, M,
+                       N, K, m_rows, n_rows, out, tiles_m, tiles_n, group_m);
+    return hipGetLastError();
+}
+
+}  // namespace blk
+
+// Tile shapes for the blocked-layout GEMM.  `eff` is the relative per-CU MFMA
+// efficiency of the shape; the choice minimises rounds * tile area / eff where
+// a round is one tile per workgroup slot.
+hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                           int64_t m, int64_t n, int64_t k, void* out, bool out_i32, int num_cu,
+                           hipStream_t st)
+{
+    struct Shape {
+        int bm, bn, per_cu;
+        double eff;
+    };
+    static constexpr Shape shapes[] = {
+        {256, 256, 1, 1.00}, {256, 192, 1, 0.97}, {128, 128, 2, 0.55}, {64, 128, 2, 0.30},
+    };
+    int best = 0;
+    double best_t = 0;
+    for (int c = 0; c < 4; ++c) {
+        const int64_t tiles = ((m + shapes[c].bm - 1) / shapes[c].bm) * ((n + shapes[c].bn - 1) / shapes[c].bn);
+        const int64_t slots = (int64_t)num_cu * shapes[c].per_cu;
+        const int64_t rounds = (tiles + slots - 1) / slots;
+        const double t = (double)rounds * shapes[c].bm * shapes[c].bn / shapes[c].per_cu / shapes[c].eff;
+        if (c == 0 || t < best_t) {
+            best = c;
+            best_t = t;
+        }
+    }
+    const int M = (int)m, N = (int)n, K = (int)k;
+#define CK_BLK(BM_, BN_)                                                                          \
+    return out_i32 ? blk::launch<BM_, BN_, true>(xq, sx, wq, sw, M, N, K, out, num_cu, st)        \
+                   : blk::launch<BM_, BN_, false>(xq, sx, wq, sw, M, N, K, out, num_cu, st)
+    switch (best) {
+        case 0: CK_BLK(256, 256);
+        case 1: CK_BLK(256, 192);
+        case 2: CK_BLK(128, 128);
+        default: CK_BLK(64, 128);
+    }
+#undef CK_BLK
+}
+
+}  // namespace ck

@@ -24,7 +24,16 @@ namespace ck {
 
 enum InKind { IN_BF16 = 0, IN_BF16_SWIGLU = 1, IN_F32 = 2 };
 
-template <int KIND, int LOG_G, int CH, bool ROT_OUT>
+// Byte offset of codes (row, 8c .. 8c+7) in the blocked layout: block
+// (row / 32, k / 32) of 1 KB, inside it the 16-byte half (k % 32) / 16, then the
+// row within the block, then k % 16.
+__device__ __forceinline__ int64_t blocked_offset(int row, int c, int kb)
+{
+    return ((int64_t)(row >> 5) * kb + (c >> 2)) * 1024 + ((c >> 1) & 1) * 512 + (row & 31) * 16 +
+           (c & 1) * 8;
+}
+
+template <int KIND, int LOG_G, int CH, bool ROT_OUT, bool BLOCKED>
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const void* __restrict__ src, int64_t ld, int m, int k, int log_t, float cg,
     int8_t* __restrict__ q, float* __restrict__ s, float* __restrict__ u_out)
@@ -148,11 +157,32 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
         uint32_t b[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) b[i] = code_bits(v[j][i], r);
-        if (row_ok && c < k8)
-            *reinterpret_cast<uint2*>(qp + c * 8) =
-                make_uint2(pack4(b[0], b[1], b[2], b[3]), pack4(b[4], b[5], b[6], b[7]));
+        const uint2 codes = make_uint2(pack4(b[0], b[1], b[2], b[3]), pack4(b[4], b[5], b[6], b[7]));
+        if (row_ok && c < k8) {
+            if constexpr (BLOCKED)
+                *reinterpret_cast<uint2*>(q + blocked_offset(row, c, k >> 5)) = codes;
+            else
+                *reinterpret_cast<uint2*>(qp + c * 8) = codes;
+        }
     }
     if (row_ok && t == 0) s[row] = scale;
+}
+
+// Row-major [n, k] int8 -> blocked layout with rows padded to n_rows (zeros).
+// One thread per 16-byte unit of the output, written in order.
+__global__ __launch_bounds__(256) void pack_blocked_kernel(const int8_t* __restrict__ w, int n, int k,
+                                                           int64_t units, int8_t* __restrict__ out)
+{
+    const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= units) return;
+    const int kb = k >> 5;
+    const int64_t block = u >> 6;
+    const int l = (int)(u & 63);
+    const int row = (int)(block / kb) * 32 + (l & 31);
+    const int kbyte = (int)(block % kb) * 32 + (l >> 5) * 16;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < n) v = *reinterpret_cast<const uint4*>(w + (int64_t)row * k + kbyte);
+    *reinterpret_cast<uint4*>(out + u * 16) = v;
 }
 
 __global__ __launch_bounds__(256) void silu_kernel(const uint16_t* __restrict__ g, int64_t n,
@@ -194,14 +224,14 @@ bool choose_team(int k, int g, int* log_t, int* ch)
     return best >= 0;
 }
 
-template <int KIND, int LOG_G, bool ROT_OUT>
+template <int KIND, int LOG_G, bool ROT_OUT, bool BLOCKED>
 hipError_t launch_ch(int ch, dim3 grid, hipStream_t st, const void* src, int64_t ld, int m, int k,
                      int log_t, float cg, int8_t* q, float* s, float* u)
 {
     switch (ch) {
 #define CK_CASE(C)                                                                              \
     case C:                                                                                     \
-        hipLaunchKernelGGL((quant_rows_kernel<KIND, LOG_G, C, ROT_OUT>), grid, dim3(256), 0, st, \
+        hipLaunchKernelGGL((quant_rows_kernel<KIND, LOG_G, C, ROT_OUT, BLOCKED>), grid, dim3(256), 0, st, \
                            src, ld, m, k, log_t, cg, q, s, u);                                  \
         break;
         CK_CASE(1) CK_CASE(2) CK_CASE(3) CK_CASE(4) CK_CASE(6) CK_CASE(8) CK_CASE(12) CK_CASE(16)
@@ -211,13 +241,13 @@ hipError_t launch_ch(int ch, dim3 grid, hipStream_t st, const void* src, int64_t
     return hipGetLastError();
 }
 
-template <int KIND, bool ROT_OUT>
+template <int KIND, bool ROT_OUT, bool BLOCKED>
 hipError_t launch_g(int log_g, int ch, dim3 grid, hipStream_t st, const void* src, int64_t ld, int m,
                     int k, int log_t, float cg, int8_t* q, float* s, float* u)
 {
     switch (log_g) {
 #define CK_G(L) \
-    case L: return launch_ch<KIND, L, ROT_OUT>(ch, grid, st, src, ld, m, k, log_t, cg, q, s, u);
+    case L: return launch_ch<KIND, L, ROT_OUT, BLOCKED>(ch, grid, st, src, ld, m, k, log_t, cg, q, s, u);
         CK_G(0) CK_G(1) CK_G(2) CK_G(3) CK_G(4) CK_G(5) CK_G(6) CK_G(7) CK_G(8)
 #undef CK_G
         default: return hipErrorInvalidValue;
@@ -228,7 +258,7 @@ hipError_t launch_g(int log_g, int ch, dim3 grid, hipStream_t st, const void* sr
 
 // kind: 0 = BF16, 1 = BF16 [gate | up] with SwiGLU, 2 = FP32 (weights).
 hipError_t launch_quant_rows(int kind, const void* src, int64_t ld, int64_t m, int64_t k, int g,
-                             int8_t* q, float* s, float* u_out, hipStream_t st)
+                             int8_t* q, float* s, float* u_out, bool blocked, hipStream_t st)
 {
     if (m == 0) return hipSuccess;
     int log_t = 0, ch = 0;
@@ -238,19 +268,30 @@ hipError_t launch_quant_rows(int kind, const void* src, int64_t ld, int64_t m, i
     int log_g = 0;
     while ((1 << log_g) < g) ++log_g;
     const float cg = (float)(1.0 / sqrt((double)g));
-    const bool rot = u_out != nullptr;
-    switch (kind) {
-        case IN_BF16:
-            return rot ? launch_g<IN_BF16, true>(log_g, ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s, u_out)
-                       : launch_g<IN_BF16, false>(log_g, ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s, u_out);
-        case IN_BF16_SWIGLU:
-            return rot ? launch_g<IN_BF16_SWIGLU, true>(log_g, ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s, u_out)
-                       : launch_g<IN_BF16_SWIGLU, false>(log_g, ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s, u_out);
-        case IN_F32:
-            return launch_g<IN_F32, false>(log_g, ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s, u_out);
-        default:
-            return hipErrorInvalidValue;
+    const int M = (int)m, K = (int)k;
+    if (u_out != nullptr) {
+        if (kind == IN_BF16) return launch_g<IN_BF16, true, false>(log_g, ch, grid, st, src, ld, M, K, log_t, cg, q, s, u_out);
+        if (kind == IN_BF16_SWIGLU) return launch_g<IN_BF16_SWIGLU, true, false>(log_g, ch, grid, st, src, ld, M, K, log_t, cg, q, s, u_out);
+        return hipErrorInvalidValue;
     }
+    switch (kind * 2 + (blocked ? 1 : 0)) {
+        case 0: return launch_g<IN_BF16, false, false>(log_g, ch, grid, st, src, ld, M, K, log_t, cg, q, s, nullptr);
+        case 1: return launch_g<IN_BF16, false, true>(log_g, ch, grid, st, src, ld, M, K, log_t, cg, q, s, nullptr);
+        case 2: return launch_g<IN_BF16_SWIGLU, false, false>(log_g, ch, grid, st, src, ld, M, K, log_t, cg, q, s, nullptr);
+        case 3: return launch_g<IN_BF16_SWIGLU, false, true>(log_g, ch, grid, st, src, ld, M, K, log_t, cg, q, s, nullptr);
+        case 4: return launch_g<IN_F32, false, false>(log_g, ch, grid, st, src, ld, M, K, log_t, cg, q, s, nullptr);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_pack_blocked(const int8_t* w, int64_t n, int64_t k, int8_t* out, hipStream_t st)
+{
+    const int64_t n_rows = (n + 255) / 256 * 256;
+    const int64_t units = n_rows * k / 16;
+    if (units == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_blocked_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, w,
+                       (int)n, (int)k, units, out);
+    return hipGetLastError();
 }
 
 hipError_t launch_silu(const uint16_t* g, int64_t n, float* out, hipStream_t st)

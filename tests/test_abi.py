@@ -47,7 +47,9 @@ def test_status_strings_and_version(L):
 
 def test_workspace_sizes(L):
     assert L.ck_int8_linear_workspace_size(0, 256) == 0
-    assert L.ck_int8_linear_workspace_size(3, 256) == 768 + 256
+    assert L.ck_int8_linear_workspace_size(3, 256) == 256 * 256 + 256   # blocked codes: 256 rows
+    assert L.ck_blocked_rows(1) == 256 and L.ck_blocked_rows(256) == 256 and L.ck_blocked_rows(257) == 512
+    assert L.ck_blocked_size(300, 128) == 512 * 128 and L.ck_blocked_size(0, 128) == 0
     ws = L.ck_swiglu_mlp_workspace_size(4096, 3072, 12288)
     assert ws >= 4096 * 3072 + 4096 * 4 + 4096 * 2 * 12288 * 2 + 4096 * 12288 + 4096 * 4
     assert ws % 256 == 0
@@ -70,40 +72,55 @@ def test_weight_prep_null_and_alignment(L):
 
 def test_act_quant_checks(L):
     f = L.ck_act_quant
-    assert f(FAKE, 256, 0, 256, 0, 128, FAKE, FAKE, None) == OK          # m == 0: no-op
-    assert f(FAKE, 256, -2, 256, 0, 128, FAKE, FAKE, None) == ESHAPE
-    assert f(FAKE, 256, 4, 256, 1, 128, FAKE, FAKE, None) == ESHAPE      # swiglu needs ld >= 2k
-    assert f(FAKE, 260, 4, 256, 0, 128, FAKE, FAKE, None) == ESHAPE      # ld % 8
-    assert f(FAKE, 256, 4, 256, 7, 128, FAKE, FAKE, None) == EINVAL      # unknown act
-    assert f(None, 256, 4, 256, 0, 128, FAKE, FAKE, None) == EINVAL
-    assert f(FAKE, 256, 4, 256, 0, 128, FAKE, None, None) == EINVAL
+    assert f(FAKE, 256, 0, 256, 0, 128, 0, FAKE, FAKE, None) == OK          # m == 0: no-op
+    assert f(FAKE, 256, -2, 256, 0, 128, 0, FAKE, FAKE, None) == ESHAPE
+    assert f(FAKE, 256, 4, 256, 1, 128, 0, FAKE, FAKE, None) == ESHAPE      # swiglu needs ld >= 2k
+    assert f(FAKE, 260, 4, 256, 0, 128, 0, FAKE, FAKE, None) == ESHAPE      # ld % 8
+    assert f(FAKE, 256, 4, 256, 7, 128, 0, FAKE, FAKE, None) == EINVAL      # unknown act
+    assert f(FAKE, 256, 4, 256, 0, 128, 5, FAKE, FAKE, None) == EINVAL      # unknown layout
+    assert f(None, 256, 4, 256, 0, 128, 1, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE, 256, 4, 256, 0, 128, 0, FAKE, None, None) == EINVAL
 
 
-def test_int8_linear_checks(L):
+@pytest.mark.parametrize("layout", [0, 1])
+def test_int8_linear_checks(L, layout):
     f = L.ck_int8_linear
     ws = L.ck_int8_linear_workspace_size(4, 256)
-    assert f(FAKE, 256, 0, FAKE, FAKE, 4, 40, 256, 128, FAKE, FAKE, ws, None) == ESHAPE  # n % 16
-    assert f(FAKE, 256, 0, FAKE, FAKE, 4, 32, 256, 128, FAKE, FAKE, ws - 1, None) == EWS
-    assert f(FAKE, 256, 0, FAKE, FAKE, 4, 32, 256, 128, FAKE, None, ws, None) == EWS
-    assert f(FAKE, 256, 0, FAKE, FAKE, 4, 32, 256, 128, FAKE, FAKE + 16, ws, None) == EWS
-    assert f(FAKE, 256, 0, None, FAKE, 4, 32, 256, 128, FAKE, FAKE, ws, None) == EINVAL
-    assert f(FAKE, 256, 0, FAKE, FAKE, 0, 32, 256, 128, FAKE, FAKE, 0, None) == OK
+    lay = layout
+    assert f(FAKE, 256, 0, FAKE, FAKE, lay, 4, 40, 256, 128, FAKE, FAKE, ws, None) == ESHAPE  # n % 16
+    assert f(FAKE, 256, 0, FAKE, FAKE, lay, 4, 32, 256, 128, FAKE, FAKE, ws - 1, None) == EWS
+    assert f(FAKE, 256, 0, FAKE, FAKE, lay, 4, 32, 256, 128, FAKE, None, ws, None) == EWS
+    assert f(FAKE, 256, 0, FAKE, FAKE, lay, 4, 32, 256, 128, FAKE, FAKE + 16, ws, None) == EWS
+    assert f(FAKE, 256, 0, None, FAKE, lay, 4, 32, 256, 128, FAKE, FAKE, ws, None) == EINVAL
+    assert f(FAKE, 256, 0, FAKE, FAKE, lay, 0, 32, 256, 128, FAKE, FAKE, 0, None) == OK
+    assert f(FAKE, 256, 0, FAKE, FAKE, 9, 4, 32, 256, 128, FAKE, FAKE, ws, None) == EINVAL
+    # operands addressed with 32-bit offsets: refuse what would overflow them
+    assert f(FAKE, 32768, 0, FAKE, FAKE, lay, 70000, 32, 32768, 128, FAKE, FAKE, ws, None) == EUNSUP
 
 
 def test_swiglu_mlp_checks(L):
     f = L.ck_swiglu_mlp
     ws = L.ck_swiglu_mlp_workspace_size(8, 256, 512)
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 256, 500, 128, FAKE, FAKE, ws, None) == ESHAPE
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 256, 512, 128, FAKE, FAKE, ws - 256, None) == EWS
-    assert f(FAKE, None, FAKE, FAKE, FAKE, 8, 256, 512, 128, FAKE, FAKE, ws, None) == EINVAL
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 256, 512, 128, FAKE, FAKE, 0, None) == OK
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 256, 500, 128, FAKE, FAKE, ws, None) == ESHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 256, 512, 128, FAKE, FAKE, ws - 256, None) == EWS
+    assert f(FAKE, None, FAKE, FAKE, FAKE, 1, 8, 256, 512, 128, FAKE, FAKE, ws, None) == EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 256, 512, 128, FAKE, FAKE, ws, None) == EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 256, 512, 128, FAKE, FAKE, 0, None) == OK
+
+
+def test_weight_pack_checks(L):
+    assert L.ck_weight_pack(FAKE, 4, 100, FAKE, None) == ESHAPE
+    assert L.ck_weight_pack(None, 4, 128, FAKE, None) == EINVAL
+    assert L.ck_weight_pack(FAKE, 0, 128, FAKE, None) == OK
+    assert L.ck_weight_pack(FAKE, 4, 65536, FAKE, None) == EUNSUP
 
 
 def test_gemm_hook_checks(L):
-    assert L.ck_int8_gemm_i32(FAKE, FAKE, 4, 20, 256, FAKE, None) == ESHAPE
-    assert L.ck_int8_gemm_i32(FAKE, FAKE, 4, 32, 100, FAKE, None) == ESHAPE
-    assert L.ck_int8_gemm_i32(None, FAKE, 4, 32, 256, FAKE, None) == EINVAL
-    assert L.ck_int8_gemm_bf16(FAKE, None, FAKE, FAKE, 4, 32, 256, FAKE, None) == EINVAL
+    assert L.ck_int8_gemm_i32(FAKE, FAKE, 0, 4, 20, 256, FAKE, None) == ESHAPE
+    assert L.ck_int8_gemm_i32(FAKE, FAKE, 1, 4, 32, 100, FAKE, None) == ESHAPE
+    assert L.ck_int8_gemm_i32(None, FAKE, 0, 4, 32, 256, FAKE, None) == EINVAL
+    assert L.ck_int8_gemm_i32(FAKE, FAKE, 3, 4, 32, 256, FAKE, None) == EINVAL
+    assert L.ck_int8_gemm_bf16(FAKE, None, FAKE, FAKE, 1, 4, 32, 256, FAKE, None) == EINVAL
     assert L.ck_silu_f32(FAKE, -1, FAKE, None) == ESHAPE
     assert L.ck_act_rotate_f32(FAKE, 256, 4, 256, 0, 100, FAKE, None) == EUNSUP
 

@@ -58,6 +58,24 @@ def assert_bf16_close(got, want, what):
     assert mism == 0, f"{what}: {mism} BF16 elements differ (within tolerance, not bit-exact)"
 
 
+def to_blocked(a):
+    """Row-major int8 [R, K] -> the blocked layout of include/ck.h: rows padded
+    to a multiple of 256 with zeros, 1 KB blocks (r/32, k/32) in row-block-major
+    order, inside a block ((k%32)/16, r%32, k%16)."""
+    r, k = a.shape
+    rp = -(-r // 256) * 256
+    p = np.zeros((rp, k), dtype=np.int8)
+    p[:r] = a
+    return np.ascontiguousarray(
+        p.reshape(rp // 32, 32, k // 32, 2, 16).transpose(0, 2, 3, 1, 4)).reshape(rp, k)
+
+
+def from_blocked(b, rows):
+    rp, k = b.shape
+    a = b.reshape(rp // 32, k // 32, 2, 32, 16).transpose(0, 3, 1, 2, 4).reshape(rp, k)
+    return np.ascontiguousarray(a[:rows])
+
+
 def sample_rows(m, count=16, seed=0):
     rng = np.random.default_rng(seed)
     fixed = [0, 1, m // 3, m // 2, m - 2, m - 1]
@@ -130,6 +148,9 @@ def test_act_rotate_bit_exact(orc, m, k, act, g):
 GEMM_SHAPES = [  # (m, n, k): every tile shape, both k-step sizes, ragged m and n
     (1, 16, 64), (64, 128, 256), (77, 144, 192), (300, 272, 1024), (1000, 1040, 640),
     (600, 1200, 384), (2048, 1024, 3072), (513, 4112, 128),
+    # persistent large-tile kernels: 256x256 and 256x192 tiles, ragged m and n,
+    # k % 128 == 64, two rounds of tiles, a partial last round
+    (4000, 4080, 192), (4000, 3056, 320), (4096, 8192, 128), (3968, 5120, 64), (2560, 6144, 256),
 ]
 
 
@@ -156,6 +177,7 @@ def test_gemm_i32_extreme_codes(orc):
 LINEAR_CASES = [  # (m, k, n, act, g)
     (1, 256, 16, 0, 128), (7, 384, 48, 1, 128), (64, 256, 128, 0, 128), (300, 1024, 272, 1, 128),
     (129, 512, 320, 0, 64), (200, 768, 96, 1, 256), (33, 128, 64, 0, 1), (1000, 640, 1040, 0, 128),
+    (4000, 256, 4080, 1, 128), (3968, 384, 5120, 0, 64),
 ]
 
 
@@ -267,3 +289,116 @@ def test_empty_and_degenerate_calls(orc):
     y = ck.ck_int8_linear(xz, wq, sw, g)
     torch.cuda.synchronize()
     assert not y.any()
+
+
+# ---------------------------------------------------------------------------
+# Blocked operand layout (the product path)
+# ---------------------------------------------------------------------------
+def test_blocked_helpers_round_trip():
+    rng = np.random.default_rng(30)
+    a = rng.integers(-127, 128, size=(300, 128), dtype=np.int8)
+    b = to_blocked(a)
+    assert b.shape == (512, 128)
+    np.testing.assert_array_equal(from_blocked(b, 300), a)
+    # spot-check the documented offset formula
+    flat = b.reshape(-1)
+    for r, k in [(0, 0), (31, 17), (33, 95), (299, 127), (64, 32)]:
+        off = ((r // 32) * (128 // 32) + k // 32) * 1024 + ((k % 32) // 16) * 512 + (r % 32) * 16 + k % 16
+        assert flat[off] == a[r, k]
+
+
+@pytest.mark.parametrize("n,k", [(128, 256), (300, 384), (1040, 640), (24576, 3072)])
+def test_weight_pack_layout(orc, n, k):
+    say(f"weight_pack n={n} k={k}")
+    rng = np.random.default_rng(n + k)
+    wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    got = host(ck.ck_weight_pack(dev(wq)))
+    np.testing.assert_array_equal(got, to_blocked(wq))      # padding rows are zero too
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c4"])
+def test_act_quant_blocked(orc, name):
+    wl = W.WORKLOADS[name]
+    x = inputs(name)["x"]
+    say(f"act_quant blocked {name}")
+    q, s = ck.ck_act_quant(bf16_dev(x), wl.act, wl.group, layout="blocked")
+    q_o, s_o = orc.act_quant(x, wl.act, wl.group)
+    np.testing.assert_array_equal(from_blocked(host(q), wl.m), q_o)
+    np.testing.assert_array_equal(host(s)[:, 0].view(np.uint32), s_o.view(np.uint32))
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
+def test_gemm_i32_blocked_bit_exact(orc, m, n, k):
+    say(f"gemm_i32 blocked m={m} n={n} k={k}")
+    rng = np.random.default_rng(m * 11 + n)
+    xq = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    acc = host(ck.ck_int8_gemm_i32(dev(to_blocked(xq)), dev(to_blocked(wq)), "blocked", m=m, n=n))
+    np.testing.assert_array_equal(acc, orc.gemm_i32(xq, wq))
+
+
+@pytest.mark.parametrize("m,k,n,act,g", LINEAR_CASES)
+def test_int8_linear_blocked_bit_exact(orc, m, k, n, act, g):
+    say(f"int8_linear blocked m={m} k={k} n={n} act={act} g={g}")
+    d = W.case(m, k, n, act, seed=1000 + m, zero_rows=(m // 2,) if m > 2 else ())
+    wq_o, sw_o = orc.weight_prep(d["w"], g)
+    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    y = bf16_host(ck.ck_int8_linear(bf16_dev(d["x"]), ck.ck_weight_pack(wq), sw, g, act,
+                                    layout="blocked"))
+    assert_bf16_close(y, orc.int8_linear(d["x"], act, wq_o, sw_o, g), "y")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_full_workload_blocked_sampled_rows(orc, name):
+    wl = W.WORKLOADS[name]
+    d = inputs(name)
+    say(f"int8_linear blocked full {name}: {wl.desc}")
+    wq, sw = ck.ck_weight_prep(dev(d["w"]), wl.group)
+    y = ck.ck_int8_linear(bf16_dev(d["x"]), ck.ck_weight_pack(wq), sw, wl.group, wl.act,
+                          layout="blocked")
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.m, seed=1)
+    wq_o, sw_o = prepped(orc, name)
+    ref = orc.int8_linear(d["x"][rows], wl.act, wq_o, sw_o, wl.group)
+    assert_bf16_close(bf16_host(y)[rows], ref, f"{name} blocked sampled rows")
+
+
+def test_swiglu_mlp_blocked_full_c5_sampled_rows(orc):
+    """The benchmarked path: packed weights, blocked activation codes."""
+    wl = W.WORKLOADS["c5"]
+    d = inputs("c5")
+    say(f"swiglu_mlp blocked full c5: {wl.desc}")
+    wgu, sgu = ck.ck_weight_prep(dev(d["w_gu"]), wl.group)
+    wd, sd = ck.ck_weight_prep(dev(d["w_down"]), wl.group)
+    y = ck.ck_swiglu_mlp(bf16_dev(d["x"]), ck.ck_weight_pack(wgu), sgu, ck.ck_weight_pack(wd), sd,
+                         wl.group, layout="blocked")
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.m, seed=2)
+    (gq, gs), (dq, ds) = prepped(orc, "c5", "w_gu"), prepped(orc, "c5", "w_down")
+    ref = orc.swiglu_mlp(d["x"][rows], gq, gs, dq, ds, wl.group)
+    assert_bf16_close(bf16_host(y)[rows], ref, "c5 blocked sampled rows")
+    y64 = orc.reference_mlp_f64(d["x"][rows], d["w_gu"], d["w_down"])
+    e_gpu, e_orc = orc.rel_l2(bf16_host(y)[rows], y64), orc.rel_l2(ref, y64)
+    say(f"c5 blocked: relL2 gpu={e_gpu:.5f} oracle={e_orc:.5f}")
+    assert e_gpu <= e_orc + 1e-4
+
+
+def test_blocked_stages_equal_swiglu_mlp():
+    """The stage calls bench.py times (blocked layout) compose to ck_swiglu_mlp
+    bit for bit, and agree with the row-major path."""
+    say("blocked stage composition (m=1000, h=1024, i=2048)")
+    m, h, i, g = 1000, 1024, 2048, 128
+    rng = np.random.default_rng(31)
+    x = bf16_dev(W.to_bf16_bits(rng.standard_normal((m, h)).astype(np.float32)))
+    wgu, sgu = ck.ck_weight_prep(dev((0.02 * rng.standard_normal((2 * i, h))).astype(np.float32)), g)
+    wd, sd = ck.ck_weight_prep(dev((0.01 * rng.standard_normal((h, i))).astype(np.float32)), g)
+    pgu, pd = ck.ck_weight_pack(wgu), ck.ck_weight_pack(wd)
+    y_rows = ck.ck_swiglu_mlp(x, wgu, sgu, wd, sd, g)
+    y_blk = ck.ck_swiglu_mlp(x, pgu, sgu, pd, sd, g, layout="blocked")
+    xq, sx = ck.ck_act_quant(x, 0, g, layout="blocked")
+    t1 = ck.ck_int8_gemm_bf16(xq, sx, pgu, sgu, layout="blocked")
+    hq, sh = ck.ck_act_quant(t1, 1, g, layout="blocked")
+    y_st = ck.ck_int8_gemm_bf16(hq, sh, pd, sd, layout="blocked")
+    torch.cuda.synchronize()
+    assert torch.equal(y_blk.view(torch.int16), y_rows.view(torch.int16))
+    assert torch.equal(y_blk.view(torch.int16), y_st.view(torch.int16))

@@ -92,6 +92,30 @@ __device__ __forceinline__ void tile_coords(int j, int tiles_m, int tiles_n, int
     tn = (j % width) / gm;
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes at buffer
+// offset voff + soff land at LDS byte address lds + 16 l.  Written as inline
+// assembly so the compiler does not track this LDS write itself: it would
+// otherwise wait for every such load in flight before any later LDS read,
+// which empties the prefetch ring.  The caller orders the loads and the reads
+// with explicit s_waitcnt vmcnt and barriers.  M0 must be set one instruction
+// before the load uses it.
+__device__ __forceinline__ void lds_dma_b128(v4i rsrc, uint32_t voff, uint32_t soff, uint32_t lds)
+{
+    asm volatile(
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, %2 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+        : "memory", "m0");
+}
+
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)base;
+    return v4i{(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
 template <int BM, int BN, bool OUT_I32>
 __global__ __launch_bounds__(256) void gemm_blk_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
@@ -103,6 +127,14 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = Cfg<BM, BN>;
     __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE];
+    constexpr int AW = C::A_BLK / 4;   // W blocks each wave loads per stage
+    constexpr int XW = C::B_BLK / 4;   // X blocks each wave loads per stage
+    constexpr int NMF = C::FN * C::FM; // MFMAs per wave per k-slice
+    constexpr int NDS = C::FN + C::FM; // fragment reads per wave per k-slice
+    // steps of the two halves of a stage (small tiles have fewer MFMAs than
+    // reads or loads)
+    constexpr int STEPS1 = NMF > NDS ? NMF : NDS;
+    constexpr int STEPS0 = STEPS1 > AW + XW ? STEPS1 : AW + XW;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -117,8 +149,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     if (total == 0) return;
 
     // Within a full round the workgroups of one XCD (b % 8) take consecutive
-    // tiles; the last, partial round keeps the plain order.  Branch-free, so
-    // the load-issue code stays in one scheduling region with the MFMAs.
+    // tiles; the last, partial round keeps the plain order.
     const bool xcd_order = (G & 7) == 0;
     const int b_xcd = (b & 7) * (G >> 3) + (b >> 3);
     auto tile_of = [&](int q) {
@@ -127,33 +158,48 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     };
     // Operand buffers span the padded row counts m_rows, n_rows (multiples of
     // 256), so every block a tile touches is inside the buffer.
-    const __amdgpu_buffer_rsrc_t rs_w =
-        __builtin_amdgcn_make_buffer_rsrc((void*)wq, (short)0, n_rows * K, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs_x =
-        __builtin_amdgcn_make_buffer_rsrc((void*)xq, (short)0, m_rows * K, 0x00020000);
+    const v4i rs_w = make_rsrc(wq, (uint32_t)(n_rows * K));
+    const v4i rs_x = make_rsrc(xq, (uint32_t)(m_rows * K));
     const __amdgpu_buffer_rsrc_t rs_o =
         __builtin_amdgcn_make_buffer_rsrc(out, (short)0, M * N * (OUT_I32 ? 4 : 2), 0x00020000);
+    const uint32_t smem_addr = (uint32_t)(uintptr_t)(lds_void_t*)smem;
+    const uint32_t lane16 = (uint32_t)lane * 16u;
 
-    // Loads of stage min(s, total - 1) into ring slot `slot` (= s % NBUF).
-    // Past the last stage this reloads the last stage into a slot nobody reads
-    // again, which keeps the loop body free of branches and the wait counts
-    // constant.
-    auto issue = [&](int s, int slot) {
-        const int sc = min(s, total - 1);
-        const int q = sc / KT;
-        const int kt = sc - q * KT;
+    // Load cursor: the stage whose loads are issued next (it stops at the last
+    // stage, so the final P issues reload that stage into slots nobody reads
+    // again; this keeps the number of loads per stage, and the wait counts,
+    // constant).  la / lx: byte offset of the cursor tile's first W / X row
+    // block at k = 0.
+    int ls = 0, lq = 0, lkt = 0;
+    uint32_t la = 0, lx = 0;
+    auto set_tile = [&](int q) {
         int tm, tn;
         tile_coords(tile_of(q), tiles_m, tiles_n, group_m, tm, tn);
-        char* dst = smem + slot * C::STAGE;
-#pragma unroll
-        for (int i = 0; i < C::L; ++i) {
-            const int bi = wave + 4 * i;                 // wave-uniform block index
-            const bool is_a = bi < C::A_BLK;
-            const int rel = is_a ? bi : bi - C::A_BLK;
-            const int rb = (is_a ? tn * (BN / 32) : tm * (BM / 32)) + (rel >> 1);
-            const uint32_t boff = (uint32_t)(rb * KB + 2 * kt + (rel & 1)) * 1024u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? rs_w : rs_x, (lds_void_t*)(dst + bi * 1024),
-                                                     16, boff + (uint32_t)lane * 16u, 0, 0, 0);
+        la = (uint32_t)(tn * (BN / 32) * KB) * 1024u;
+        lx = (uint32_t)(tm * (BM / 32) * KB) * 1024u;
+    };
+    auto advance = [&]() {
+        if (ls + 1 < total) {
+            ++ls;
+            if (++lkt == KT) {
+                lkt = 0;
+                set_tile(++lq);
+            }
+        }
+    };
+    // Block a of this wave's share: W block ai = wave * AW + a covers row
+    // block ai / 2, k-slice ai % 2 of the stage (X blocks likewise after the
+    // W blocks in the LDS stage).
+    auto issue_one = [&](int a, uint32_t slot_addr) {
+        const uint32_t kofs = (uint32_t)lkt * 2048u;
+        if (a < AW) {
+            const int ai = wave * AW + a;
+            const uint32_t off = la + kofs + (uint32_t)((ai >> 1) * KB + (ai & 1)) * 1024u;
+            lds_dma_b128(rs_w, lane16, off, slot_addr + (uint32_t)ai * 1024u);
+        } else {
+            const int bj = wave * XW + (a - AW);
+            const uint32_t off = lx + kofs + (uint32_t)((bj >> 1) * KB + (bj & 1)) * 1024u;
+            lds_dma_b128(rs_x, lane16, off, slot_addr + (uint32_t)(C::A_BLK + bj) * 1024u);
         }
     };
 
@@ -162,20 +208,25 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     const int lh = lane >> 5;
     const int wm0 = (wave & 1) * (BM / 2);
     const int wn0 = (wave >> 1) * (BN / 2);
+    // This wave's fragments of a stage: W fragment i, k-slice ks at block
+    // (wn0 / 32 + i) * 2 + ks; X fragment j at block A_BLK + (wm0 / 32 + j) * 2 + ks.
     auto frag_a = [&](int buf, int i, int ks) {
-        const int rb = (wn0 >> 5) + i;
-        return *reinterpret_cast<const v4i*>(smem + buf * C::STAGE + (rb * 2 + ks) * 1024 + lane * 16);
+        const int blk = ((wn0 >> 5) + i) * 2 + ks;
+        return *reinterpret_cast<const v4i*>(smem + buf * C::STAGE + blk * 1024 + lane * 16);
     };
     auto frag_b = [&](int buf, int j, int ks) {
-        const int rb = (wm0 >> 5) + j;
-        return *reinterpret_cast<const v4i*>(smem + buf * C::STAGE + (C::A_BLK + rb * 2 + ks) * 1024 +
-                                             lane * 16);
+        const int blk = C::A_BLK + ((wm0 >> 5) + j) * 2 + ks;
+        return *reinterpret_cast<const v4i*>(smem + buf * C::STAGE + blk * 1024 + lane * 16);
     };
 
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
-    static_assert(C::P == 3 && C::NBUF == 4, "prologue and loop unrolling assume P = 3, NBUF = 4");
+    static_assert(C::P == 3 && C::NBUF == 4, "the prologue assumes P = 3, NBUF = 4");
+    set_tile(0);
+#pragma unroll
+    for (int p = 0; p < C::P; ++p) {
+#pragma unroll
+        for (int a = 0; a < AW + XW; ++a) issue_one(a, smem_addr + (uint32_t)(p * C::STAGE));
+        advance();
+    }
     wait_vmcnt<2 * C::L>();
     workgroup_barrier();
     v4i fa[C::FN], fb[C::FM];
@@ -184,125 +235,101 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
 #pragma unroll
     for (int j = 0; j < C::FM; ++j) fb[j] = frag_b(0, j, 0);
 
-    // One stage.  BUF is the stage's ring slot (s % NBUF); unrolling the stage
-    // loop by NBUF makes every LDS offset a constant, which lets the compiler
-    // see that the fragment reads never touch the slots the in-flight loads
-    // write, so it does not drain those loads before each read.
-    auto stage = [&](int s, auto buf_c) {
-        constexpr int buf = decltype(buf_c)::value;
-        constexpr int nbuf = (buf + 1) % C::NBUF;
-        constexpr int lbuf = (buf + C::P) % C::NBUF;
+    // One stage s (ring slot s % 4).  The instruction order inside each half
+    // is fixed in source order (sched_barrier): MFMA k, then fragment read k,
+    // then load k, so reads and loads issue in the shadow of the MFMAs.
+    auto stage = [&](int s, auto first) {
+        const int buf = s & 3;
+        const int nbuf = (s + 1) & 3;
+        const uint32_t lslot = smem_addr + (uint32_t)(((s + C::P) & 3) * C::STAGE);
         v4i ga[C::FN], gb[C::FM];
-        // first half: k-slice 0 MFMAs (zero accumulator input on a tile's first
-        // stage), k-slice 1 fragment reads, loads of stage s + P
-        auto half0 = [&](auto first) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < C::FN; ++i) ga[i] = frag_a(buf, i, 1);
-#pragma unroll
-            for (int j = 0; j < C::FM; ++j) gb[j] = frag_b(buf, j, 1);
-#pragma unroll
-            for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-                for (int j = 0; j < C::FM; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                        fa[i], fb[j], decltype(first)::value ? v16i{} : acc[i][j], 0, 0, 0);
-            issue(s + C::P, lbuf);
-            constexpr int NMF = C::FN * C::FM;
-            constexpr int NDS = C::FN + C::FM;
-#pragma unroll
-            for (int k = 0; k < NMF; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
-                if (k < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
-                if (k < C::L) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM load
-            }
-        };
-        if (s % KT == 0) half0(std::true_type{});
-        else half0(std::false_type{});
+        for (int k = 0; k < STEPS0; ++k) {
+            const int i = k / C::FM, j = k % C::FM;
+            if (k < NMF)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                    fa[i], fb[j], decltype(first)::value ? v16i{} : acc[i][j], 0, 0, 0);
+            if (k < C::FN) ga[k] = frag_a(buf, k, 1);
+            else if (k < NDS) gb[k - C::FN] = frag_b(buf, k - C::FN, 1);
+            if (k < AW + XW) issue_one(k, lslot);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        advance();
 
         wait_lgkmcnt0();              // this wave's k-slice 1 fragments are in registers
         wait_vmcnt<2 * C::L>();       // stage s + 1 has landed (s + 2, s + 3 may be in flight)
-        workgroup_barrier();          // ... for every wave; slot buf is no longer read
+        workgroup_barrier();          // ... for every wave; slot s % 4 is no longer read
 
-        // second half: k-slice 1 MFMAs, next stage's k-slice 0 fragment reads
 #pragma unroll
-        for (int i = 0; i < C::FN; ++i) fa[i] = frag_a(nbuf, i, 0);
-#pragma unroll
-        for (int j = 0; j < C::FM; ++j) fb[j] = frag_b(nbuf, j, 0);
-#pragma unroll
-        for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-            for (int j = 0; j < C::FM; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ga[i], gb[j], acc[i][j], 0, 0, 0);
-        {
-            constexpr int NMF = C::FN * C::FM;
-            constexpr int NDS = C::FN + C::FM;
-#pragma unroll
-            for (int k = 0; k < NMF; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                if (k < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-            }
+        for (int k = 0; k < STEPS1; ++k) {
+            const int i = k / C::FM, j = k % C::FM;
+            if (k < NMF) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ga[i], gb[j], acc[i][j], 0, 0, 0);
+            if (k < C::FN) fa[k] = frag_a(nbuf, k, 0);
+            else if (k < NDS) fb[k - C::FN] = frag_b(nbuf, k - C::FN, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (s % KT == KT - 1) {
-            // ---- epilogue of tile s / KT ----
-            // D fragment (32 x 32): lane l holds column l % 32 (output row m)
-            // and, in registers 4 qd .. 4 qd + 3, rows 8 qd + 4 (l / 32) + 0..3
-            // (four consecutive output columns n).  Stores go through a buffer
-            // resource, so rows past M fall outside it and are dropped.
-            int tm, tn;
-            tile_coords(tile_of(s / KT), tiles_m, tiles_n, group_m, tm, tn);
-            const int m_base = tm * BM + wm0 + lr;
-            const int n_base = tn * BN + wn0 + 4 * lh;
-            float sxm[C::FM];
+    };
+
+    auto epilogue = [&](int q) {
+        // D fragment (32 x 32): lane l holds column l % 32 (output row m)
+        // and, in registers 4 qd .. 4 qd + 3, rows 8 qd + 4 (l / 32) + 0..3
+        // (four consecutive output columns n).  Stores go through a buffer
+        // resource, so rows past M fall outside it and are dropped.
+        int tm, tn;
+        tile_coords(tile_of(q), tiles_m, tiles_n, group_m, tm, tn);
+        const int m_base = tm * BM + wm0 + lr;
+        const int n_base = tn * BN + wn0 + 4 * lh;
+        float sxm[C::FM];
+#pragma unroll
+        for (int j = 0; j < C::FM; ++j) {
+            sxm[j] = 0.0f;
+            if constexpr (!OUT_I32) sxm[j] = sx[min(m_base + 32 * j, M - 1)];
+        }
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i) {
+            float4 s4[4];
+            bool n_ok[4];
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const int n = n_base + 32 * i + 8 * qd;
+                n_ok[qd] = n < N;
+                s4[qd] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if constexpr (!OUT_I32) s4[qd] = *reinterpret_cast<const float4*>(sw + min(n, N - 4));
+            }
 #pragma unroll
             for (int j = 0; j < C::FM; ++j) {
-                sxm[j] = 0.0f;
-                if constexpr (!OUT_I32) sxm[j] = sx[min(m_base + 32 * j, M - 1)];
-            }
-#pragma unroll
-            for (int i = 0; i < C::FN; ++i) {
-                float4 s4[4];
-                bool n_ok[4];
+                // copy one fragment out of the accumulators here, not all of
+                // them up front
+                v16i f = acc[i][j];
+                asm volatile("" : "+v"(f));
+                const uint32_t row = (uint32_t)(m_base + 32 * j) * (uint32_t)N;
 #pragma unroll
                 for (int qd = 0; qd < 4; ++qd) {
-                    const int n = n_base + 32 * i + 8 * qd;
-                    n_ok[qd] = n < N;
-                    s4[qd] = make_float4(0.f, 0.f, 0.f, 0.f);
-                    if constexpr (!OUT_I32) s4[qd] = *reinterpret_cast<const float4*>(sw + min(n, N - 4));
-                }
-#pragma unroll
-                for (int j = 0; j < C::FM; ++j) {
-                    // copy one fragment out of the accumulators here, not all
-                    // of them up front
-                    v16i f = acc[i][j];
-                    asm volatile("" : "+v"(f));
-                    const uint32_t row = (uint32_t)(m_base + 32 * j) * (uint32_t)N;
-#pragma unroll
-                    for (int qd = 0; qd < 4; ++qd) {
-                        if (!n_ok[qd]) continue;
-                        const uint32_t o = row + (uint32_t)(n_base + 32 * i + 8 * qd);
-                        if constexpr (OUT_I32) {
-                            const v4i d = {f[4 * qd], f[4 * qd + 1], f[4 * qd + 2], f[4 * qd + 3]};
-                            __builtin_amdgcn_raw_buffer_store_b128(d, rs_o, o * 4u, 0, 0);
-                        } else {
-                            const float y0 = ((float)f[4 * qd + 0] * sxm[j]) * s4[qd].x;
-                            const float y1 = ((float)f[4 * qd + 1] * sxm[j]) * s4[qd].y;
-                            const float y2 = ((float)f[4 * qd + 2] * sxm[j]) * s4[qd].z;
-                            const float y3 = ((float)f[4 * qd + 3] * sxm[j]) * s4[qd].w;
-                            const u32x2 d = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-                            __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, o * 2u, 0, 0);
-                        }
+                    if (!n_ok[qd]) continue;
+                    const uint32_t o = row + (uint32_t)(n_base + 32 * i + 8 * qd);
+                    if constexpr (OUT_I32) {
+                        const v4i d = {f[4 * qd], f[4 * qd + 1], f[4 * qd + 2], f[4 * qd + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(d, rs_o, o * 4u, 0, 0);
+                    } else {
+                        const float y0 = ((float)f[4 * qd + 0] * sxm[j]) * s4[qd].x;
+                        const float y1 = ((float)f[4 * qd + 1] * sxm[j]) * s4[qd].y;
+                        const float y2 = ((float)f[4 * qd + 2] * sxm[j]) * s4[qd].z;
+                        const float y3 = ((float)f[4 * qd + 3] * sxm[j]) * s4[qd].w;
+                        const u32x2 d = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+                        __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, o * 2u, 0, 0);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
 
-    for (int s0 = 0; s0 < total; s0 += C::NBUF) {
-        stage(s0, std::integral_constant<int, 0>{});
-        if (s0 + 1 < total) stage(s0 + 1, std::integral_constant<int, 1>{});
-        if (s0 + 2 < total) stage(s0 + 2, std::integral_constant<int, 2>{});
-        if (s0 + 3 < total) stage(s0 + 3, std::integral_constant<int, 3>{});
+    int s = 0;
+    for (int q = 0; q < my_tiles; ++q) {
+        stage(s++, std::true_type{});
+        for (int kt = 1; kt < KT; ++kt) stage(s++, std::false_type{});
+        epilogue(q);
     }
     wait_vmcnt<0>();   // no LDS load may land after the workgroup retires
 #endif  // __HIP_DEVICE_COMPILE__

@@ -45,7 +45,8 @@ ck_status check_layout(int32_t layout)
 // byte offsets (buffer resources).
 ck_status check_gemm_extent(int64_t m, int64_t n, int64_t k)
 {
-    if (pad_rows(m) * k > CK_MAX_ELEMS || pad_rows(n) * k > CK_MAX_ELEMS || m * n * 4 > CK_MAX_ELEMS)
+    if (pad_rows(m) * k > CK_MAX_ELEMS || pad_rows(n) * k > CK_MAX_ELEMS ||
+        pad_rows(m) * n * 4 > CK_MAX_ELEMS)
         return CK_EUNSUPPORTED;
     return CK_OK;
 }

@@ -78,6 +78,7 @@ struct Cfg {
     static constexpr int BLK = A_BLK + B_BLK;
     static constexpr int L = BLK / 4;              // block loads per lane per stage
     static constexpr int STAGE = BLK * 1024;
+    static constexpr int SCALES = 2048;             // one tile's sx and sw in LDS
     static_assert(BLK % 4 == 0, "blocks must split evenly over 4 waves");
 };
 
@@ -126,13 +127,20 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     // needs this function's launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = Cfg<BM, BN>;
-    __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE];
+    // LDS: the 4-slot operand ring, then two scale buffers (tile q uses
+    // buffer q % 2), each 1 KB of row scales sx then 1 KB of column scales sw.
+    __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE + 2 * C::SCALES];
     constexpr int AW = C::A_BLK / 4;   // W blocks each wave loads per stage
     constexpr int XW = C::B_BLK / 4;   // X blocks each wave loads per stage
     constexpr int NMF = C::FN * C::FM; // MFMAs per wave per k-slice
     constexpr int NDS = C::FN + C::FM; // fragment reads per wave per k-slice
     // steps of the two halves of a stage (small tiles have fewer MFMAs than
     // reads or loads)
+    // BF16 stores per wave in one epilogue (two 16-byte stores per fragment).
+    // The int32 variant issues more than the vmcnt field can express and is
+    // waited for in full.
+    constexpr int NST = OUT_I32 ? 0 : 2 * NMF;
+    static_assert(2 * C::L + 1 + NST < 64, "vmcnt range");
     constexpr int STEPS1 = NMF > NDS ? NMF : NDS;
     constexpr int STEPS0 = STEPS1 > AW + XW ? STEPS1 : AW + XW;
 
@@ -160,6 +168,9 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     // 256), so every block a tile touches is inside the buffer.
     const v4i rs_w = make_rsrc(wq, (uint32_t)(n_rows * K));
     const v4i rs_x = make_rsrc(xq, (uint32_t)(m_rows * K));
+    // scale vectors (absent, so every lane out of range, for the int32 variant)
+    const v4i rs_sx = make_rsrc(sx, OUT_I32 ? 0u : (uint32_t)M * 4u);
+    const v4i rs_sw = make_rsrc(sw, OUT_I32 ? 0u : (uint32_t)N * 4u);
     const __amdgpu_buffer_rsrc_t rs_o =
         __builtin_amdgcn_make_buffer_rsrc(out, (short)0, M * N * (OUT_I32 ? 4 : 2), 0x00020000);
     const uint32_t smem_addr = (uint32_t)(uintptr_t)(lds_void_t*)smem;
@@ -238,12 +249,28 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     // One stage s (ring slot s % 4).  The instruction order inside each half
     // is fixed in source order (sched_barrier): MFMA k, then fragment read k,
     // then load k, so reads and loads issue in the shadow of the MFMAs.
-    auto stage = [&](int s, auto first) {
+    // The compiler sees no global loads at all: the tile's scale vectors come
+    // into LDS by the same DMA, one load per wave at the tile's first stage
+    // (even waves sx, odd waves sw), so the epilogue never makes the compiler
+    // wait for the prefetch loads in flight.
+    //
+    // vmcnt bookkeeping at the mid-stage wait of stage s: the loads of stage
+    // s + 1 must have landed.  Issued after them are the loads of s + 2 and
+    // s + 3 (2 L), plus, on a tile's stages kt = 0 and 1, that tile's scale load
+    // (1) and, from the second tile on, the previous epilogue's NST stores.
+    // A smaller wait count than the number issued after is always safe.
+    auto stage = [&](int s, int kt, auto first, bool after_epilogue, int tm, int tn, int q) {
         const int buf = s & 3;
         const int nbuf = (s + 1) & 3;
         const uint32_t lslot = smem_addr + (uint32_t)(((s + C::P) & 3) * C::STAGE);
         v4i ga[C::FN], gb[C::FM];
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (decltype(first)::value) {
+            const bool odd = wave & 1;
+            const uint32_t sdst = smem_addr + (uint32_t)(C::NBUF * C::STAGE + (q & 1) * C::SCALES) +
+                                  (odd ? 1024u : 0u);
+            lds_dma_b128(odd ? rs_sw : rs_sx, lane16, (uint32_t)((odd ? tn * BN : tm * BM) * 4), sdst);
+        }
 #pragma unroll
         for (int k = 0; k < STEPS0; ++k) {
             const int i = k / C::FM, j = k % C::FM;
@@ -258,7 +285,12 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
         advance();
 
         wait_lgkmcnt0();              // this wave's k-slice 1 fragments are in registers
-        wait_vmcnt<2 * C::L>();       // stage s + 1 has landed (s + 2, s + 3 may be in flight)
+        if (kt <= 1) {
+            if (after_epilogue) wait_vmcnt<2 * C::L + 1 + NST>();
+            else wait_vmcnt<2 * C::L + 1>();
+        } else {
+            wait_vmcnt<2 * C::L>();
+        }
         workgroup_barrier();          // ... for every wave; slot s % 4 is no longer read
 
 #pragma unroll
@@ -271,53 +303,73 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
         }
     };
 
-    auto epilogue = [&](int q) {
+    auto epilogue = [&](int q, int tm, int tn) {
         // D fragment (32 x 32): lane l holds column l % 32 (output row m)
         // and, in registers 4 qd .. 4 qd + 3, rows 8 qd + 4 (l / 32) + 0..3
         // (four consecutive output columns n).  Stores go through a buffer
-        // resource, so rows past M fall outside it and are dropped.
-        int tm, tn;
-        tile_coords(tile_of(q), tiles_m, tiles_n, group_m, tm, tn);
+        // resource: rows past M fall outside it, and masked columns are given
+        // an offset past its end, so both are dropped while every lane still
+        // issues the same number of stores.
         const int m_base = tm * BM + wm0 + lr;
         const int n_base = tn * BN + wn0 + 4 * lh;
+        const char* sc = smem + C::NBUF * C::STAGE + (q & 1) * C::SCALES;
         float sxm[C::FM];
 #pragma unroll
         for (int j = 0; j < C::FM; ++j) {
             sxm[j] = 0.0f;
-            if constexpr (!OUT_I32) sxm[j] = sx[min(m_base + 32 * j, M - 1)];
+            if constexpr (!OUT_I32) sxm[j] = *reinterpret_cast<const float*>(sc + (wm0 + lr + 32 * j) * 4);
         }
 #pragma unroll
         for (int i = 0; i < C::FN; ++i) {
             float4 s4[4];
-            bool n_ok[4];
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
-                const int n = n_base + 32 * i + 8 * qd;
-                n_ok[qd] = n < N;
                 s4[qd] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if constexpr (!OUT_I32) s4[qd] = *reinterpret_cast<const float4*>(sw + min(n, N - 4));
+                if constexpr (!OUT_I32)
+                    s4[qd] = *reinterpret_cast<const float4*>(sc + 1024 + (wn0 + 4 * lh + 32 * i + 8 * qd) * 4);
             }
 #pragma unroll
             for (int j = 0; j < C::FM; ++j) {
                 // copy one fragment out of the accumulators here, not all of
-                // them up front
+                // them up front (the empty asm statements pin the copy between
+                // the previous fragment's stores and this fragment's math)
+                asm volatile("" : "+a"(acc[i][j]));
                 v16i f = acc[i][j];
                 asm volatile("" : "+v"(f));
                 const uint32_t row = (uint32_t)(m_base + 32 * j) * (uint32_t)N;
+                if constexpr (OUT_I32) {
 #pragma unroll
-                for (int qd = 0; qd < 4; ++qd) {
-                    if (!n_ok[qd]) continue;
-                    const uint32_t o = row + (uint32_t)(n_base + 32 * i + 8 * qd);
-                    if constexpr (OUT_I32) {
+                    for (int qd = 0; qd < 4; ++qd) {
+                        const int n = n_base + 32 * i + 8 * qd;
+                        const uint32_t ob = n < N ? (row + (uint32_t)n) * 4u : 0x80000000u;
                         const v4i d = {f[4 * qd], f[4 * qd + 1], f[4 * qd + 2], f[4 * qd + 3]};
-                        __builtin_amdgcn_raw_buffer_store_b128(d, rs_o, o * 4u, 0, 0);
-                    } else {
+                        __builtin_amdgcn_raw_buffer_store_b128(d, rs_o, ob, 0, 0);
+                    }
+                } else {
+                    uint32_t w[4][2];
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd) {
                         const float y0 = ((float)f[4 * qd + 0] * sxm[j]) * s4[qd].x;
                         const float y1 = ((float)f[4 * qd + 1] * sxm[j]) * s4[qd].y;
                         const float y2 = ((float)f[4 * qd + 2] * sxm[j]) * s4[qd].z;
                         const float y3 = ((float)f[4 * qd + 3] * sxm[j]) * s4[qd].w;
-                        const u32x2 d = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-                        __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, o * 2u, 0, 0);
+                        w[qd][0] = pack_bf16x2(y0, y1);
+                        w[qd][1] = pack_bf16x2(y2, y3);
+                    }
+                    // Columns 8p + 4 lh + 0..3 (p = qd) -> swap the upper lanes'
+                    // even-p words with the lower lanes' odd-p words, so lane l
+                    // holds 8 consecutive columns 16 h + 8 lh + 0..7 (h = 0, 1)
+                    // and stores them with one 16-byte write each.
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        uint32_t x0 = w[2 * h][0], x1 = w[2 * h][1];
+                        uint32_t y0 = w[2 * h + 1][0], y1 = w[2 * h + 1][1];
+                        const auto r0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+                        const auto r1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+                        const int n = tn * BN + wn0 + 32 * i + 16 * h + 8 * lh;
+                        const uint32_t ob = n < N ? (row + (uint32_t)n) * 2u : 0x80000000u;
+                        const v4i d = {(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]};
+                        __builtin_amdgcn_raw_buffer_store_b128(d, rs_o, ob, 0, 0);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -327,9 +379,16 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
 
     int s = 0;
     for (int q = 0; q < my_tiles; ++q) {
-        stage(s++, std::true_type{});
-        for (int kt = 1; kt < KT; ++kt) stage(s++, std::false_type{});
-        epilogue(q);
+        int tm, tn;
+        tile_coords(tile_of(q), tiles_m, tiles_n, group_m, tm, tn);
+        stage(s++, 0, std::true_type{}, q > 0, tm, tn, q);
+        for (int kt = 1; kt < KT; ++kt) stage(s++, kt, std::false_type{}, q > 0, tm, tn, q);
+        if (KT < 3) {
+            // the scale load is otherwise covered by the waits of stages 2+
+            wait_vmcnt<0>();
+            workgroup_barrier();
+        }
+        epilogue(q, tm, tn);
     }
     wait_vmcnt<0>();   // no LDS load may land after the workgroup retires
 #endif  // __HIP_DEVICE_COMPILE__
@@ -342,8 +401,9 @@ hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const flo
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
-    // LDS per workgroup: 4 stages of (BM + BN) x 64 bytes; 160 KB per CU.
-    const int lds = 4 * (BM + BN) * 64;
+    // LDS per workgroup: 4 stages of (BM + BN) x 64 bytes and two 2 KB scale
+    // buffers; 160 KB per CU.
+    const int lds = 4 * (BM + BN) * 64 + 4096;
     const int per_cu = (160 * 1024) / lds >= 2 ? 2 : 1;
     const int slots = num_cu * per_cu;
     const int grid = tiles < slots ? tiles : slots;

@@ -43,7 +43,20 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
     const int t = threadIdx.x & (T - 1);
     const int team = threadIdx.x >> log_t;
     const int rows_per_wg = blockDim.x >> log_t;
-    int row = blockIdx.x * rows_per_wg + team;
+    int wg = blockIdx.x;
+    if constexpr (BLOCKED) {
+        // In the blocked layout a 128-byte line holds 16 code bytes of each of
+        // 8 consecutive rows.  Workgroups are dispatched to the 8 XCDs round
+        // robin (blockIdx % 8), each with its own L2, so the S workgroups
+        // covering one 8-row set are taken from one XCD: the line then fills
+        // in a single L2 instead of being written back piecewise from
+        // several.  The grid is a multiple of 8 S, which makes this a
+        // permutation of the workgroups.
+        const int S = rows_per_wg >= 8 ? 1 : 8 / rows_per_wg;
+        const int u = wg >> 3;
+        wg = (u / S) * (8 * S) + (wg & 7) * S + (u % S);
+    }
+    int row = wg * rows_per_wg + team;
     const bool row_ok = row < m;
     if (!row_ok) row = m - 1;               // compute on a valid row, store nothing
     const int k8 = k >> 3;
@@ -264,7 +277,13 @@ hipError_t launch_quant_rows(int kind, const void* src, int64_t ld, int64_t m, i
     int log_t = 0, ch = 0;
     if (!choose_team((int)k, g, &log_t, &ch)) return hipErrorInvalidValue;
     const int rows_per_wg = 256 >> log_t;
-    const dim3 grid((unsigned)((m + rows_per_wg - 1) / rows_per_wg));
+    int64_t wgs = (m + rows_per_wg - 1) / rows_per_wg;
+    if (blocked) {
+        // a multiple of 8 S workgroups (see the row mapping in the kernel)
+        const int64_t mult = 8 * (rows_per_wg >= 8 ? 1 : 8 / rows_per_wg);
+        wgs = (wgs + mult - 1) / mult * mult;
+    }
+    const dim3 grid((unsigned)wgs);
     int log_g = 0;
     while ((1 << log_g) < g) ++log_g;
     const float cg = (float)(1.0 / sqrt((double)g));

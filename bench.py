@@ -43,7 +43,53 @@ def parse():
                     help="rows of the workload the CPU oracle runs (0: automatic)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--small-m-sweep", action="store_true",
+                    help="time the few-row GEMM at M = 1..64 instead of the step (one line per case)")
     return ap.parse_args()
+
+
+def small_m_sweep(steps: int, warmup: int):
+    """The few-row path: ck_int8_gemm_bf16 with blocked operands at M in {1, 8, 16, 32, 64}
+    for (N, K) = (4096, 4096) and (4096, 12288).  Bound by HBM: the algorithmic bytes are
+    the weight N*K, the codes M*K, both scale vectors and the BF16 output 2*M*N."""
+    import torch
+    import swiglu_mlp_amd as ck
+    dev = torch.device("cuda:0")
+    L = ck.lib()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    stream = torch.cuda.current_stream(dev)
+    for n, k in ((4096, 4096), (4096, 12288)):
+        w = torch.randint(-127, 128, (n, k), dtype=torch.int8, device=dev, generator=gen)
+        wb = ck.ck_weight_pack(w)
+        sw = torch.rand(n, device=dev, generator=gen) * 1e-3
+        for m in (1, 8, 16, 32, 64):
+            xq = torch.randint(-127, 128, (ck.blocked_rows(m), k), dtype=torch.int8, device=dev,
+                               generator=gen)
+            sx = torch.rand(m, device=dev, generator=gen) * 1e-3
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+            def call():
+                rc = L.ck_int8_gemm_bf16(xq.data_ptr(), sx.data_ptr(), wb.data_ptr(), sw.data_ptr(),
+                                         ck.CK_LAYOUT_BLOCKED, m, n, k, y.data_ptr(),
+                                         stream.cuda_stream)
+                if rc:
+                    raise RuntimeError(L.ck_status_str(rc).decode())
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000.0 / steps
+            nbytes = n * k + m * k + 4 * (m + n) + 2 * m * n
+            print(json.dumps({"small_m": {"m": m, "n": n, "k": k, "us": round(us, 2),
+                                          "GBs": round(nbytes / us / 1e3, 1),
+                                          "frac_hbm_peak": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
+                                          "TOPS": round(2 * m * n * k / us / 1e6, 2)}}), flush=True)
 
 
 def copy_calibration():
@@ -85,6 +131,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.small_m_sweep:
+        small_m_sweep(args.steps, args.warmup)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

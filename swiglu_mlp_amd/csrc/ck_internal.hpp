@@ -36,6 +36,13 @@ hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, 
                            int64_t m, int64_t n, int64_t k, void* out, bool out_i32, int num_cu,
                            hipStream_t st);
 
+// Blocked-layout GEMM for m <= 64 (gemm_small.hip): streams the weights once.
+hipError_t launch_gemm_small(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                             int64_t m, int64_t n, int64_t k, void* out, bool out_i32, hipStream_t st);
+
+// Largest m routed to launch_gemm_small.
+constexpr int64_t kSmallM = 64;
+
 int num_cus();
 
 // Persistent large-tile GEMM (256 x bn tiles, bn = 256 or 192), one workgroup

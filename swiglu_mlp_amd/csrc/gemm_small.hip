@@ -1,0 +1,165 @@
+// gemm_small.hip -- INT8 GEMM + dequant epilogue for few token rows (M <= 64)
+// on operands in the blocked layout (include/ck.h, CK_LAYOUT_BLOCKED).
+//
+// Sources: comfy-kitchen PR #277, "The key observation" (y = x_rot W_rot^T with
+// int32 accumulation); comfy-kitchen PR #248 "Performance improvements for qwen
+// 3.x (Part 2)", "Description" (at small M the layer is bound by streaming the
+// weights, so they are laid out to be read linearly).
+//
+// At M <= 64 the weight matrix (N x K bytes) is read once and the arithmetic is
+// negligible, so the kernel is bound by HBM.  One workgroup owns 16 weight
+// rows and all of K: N / 16 workgroups, each streaming 16 x K contiguous bytes
+// in 256-byte runs (16 rows of a 1 KB block half).  Its 8 waves take
+// interleaved 64-byte k-chunks so the workgroup reads a contiguous front, and
+// each wave keeps two batches of U chunks in flight.  The few activation rows
+// (16 per MFMA fragment) come from L2.  Products use v_mfma_i32_16x16x64_i8
+// with W as the A operand (16 output columns n) and x as B (16 rows m);
+// partial accumulators of the 8 waves are summed through LDS, then one wave
+// per 16-row fragment applies y = bf16(fl(fl(f32(acc) * sx[m]) * sw[n])).
+#include "ck_device.hpp"
+#include "ck_internal.hpp"
+
+namespace ck {
+namespace small {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int WAVES = 8;
+// offset past every buffer's end: a load there returns zeros, a store is dropped
+constexpr uint32_t kOutside = 0x80000000u;
+
+template <int MT>
+struct SmallCfg {
+    static constexpr int U = MT == 1 ? 8 : (MT == 2 ? 4 : 3);   // chunks per batch per wave
+};
+
+template <int MT, bool OUT_I32>
+__global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
+    const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
+    const float* __restrict__ sw, int M, int N, int K, int m_rows, int n_rows, void* __restrict__ out)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int U = SmallCfg<MT>::U;
+    __shared__ v4i red[WAVES][MT][64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nb = blockIdx.x;       // 16-row block of W (output columns 16 nb ..)
+    const int KB = K >> 5;           // 1 KB blocks per 32-row block
+    const int KC = K >> 6;           // 64-byte k-chunks
+
+    const __amdgpu_buffer_rsrc_t rs_w =
+        __builtin_amdgcn_make_buffer_rsrc((void*)wq, (short)0, n_rows * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_x =
+        __builtin_amdgcn_make_buffer_rsrc((void*)xq, (short)0, m_rows * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_o =
+        __builtin_amdgcn_make_buffer_rsrc(out, (short)0, M * N * (OUT_I32 ? 4 : 2), 0x00020000);
+
+    // A 16-row operand fragment of k-chunk j (64 bytes of k): lane l holds row
+    // l % 16 and the 16 k-bytes of quarter c = l / 16, which sit in 1 KB block
+    // 2 j + c / 2, half c % 2, at row offset 16 r (the 16-row half h of the
+    // 32-row block adds 256 bytes).  A and B use the same k assignment, so the
+    // order of k inside the chunk does not matter for the dot products.
+    const int r = lane & 15;
+    const int c = lane >> 4;
+    const uint32_t lane_off = (uint32_t)((c >> 1) * 1024 + (c & 1) * 512 + r * 16);
+    const uint32_t w_base = (uint32_t)((nb >> 1) * KB) * 1024u + (uint32_t)(nb & 1) * 256u + lane_off;
+    uint32_t x_base[MT];
+#pragma unroll
+    for (int f = 0; f < MT; ++f) x_base[f] = (uint32_t)((f >> 1) * KB) * 1024u + (uint32_t)(f & 1) * 256u + lane_off;
+
+    v4i acc[MT];
+#pragma unroll
+    for (int f = 0; f < MT; ++f) acc[f] = v4i{0, 0, 0, 0};
+
+    // batch b covers chunks j = wave + WAVES * (U b + u), u < U; chunks past
+    // the end load zeros (offset outside the buffers) and add nothing
+    auto load = [&](int b, v4i (&w)[U], v4i (&x)[U][MT]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = wave + WAVES * (U * b + u);
+            const bool ok = j < KC;
+            const uint32_t ko = (uint32_t)j * 2048u;
+            w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, ok ? w_base + ko : kOutside, 0, 0);
+#pragma unroll
+            for (int f = 0; f < MT; ++f)
+                x[u][f] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, ok ? x_base[f] + ko : kOutside, 0, 0);
+        }
+    };
+    auto compute = [&](const v4i (&w)[U], const v4i (&x)[U][MT]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int f = 0; f < MT; ++f)
+                acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[u], x[u][f], acc[f], 0, 0, 0);
+    };
+
+    const int batches = (KC + WAVES * U - 1) / (WAVES * U);
+    v4i wa[U], xa[U][MT], wb[U], xb[U][MT];
+    load(0, wa, xa);
+    for (int b = 0; b < batches; b += 2) {
+        if (b + 1 < batches) load(b + 1, wb, xb);
+        compute(wa, xa);
+        if (b + 1 >= batches) break;
+        if (b + 2 < batches) load(b + 2, wa, xa);
+        compute(wb, xb);
+    }
+
+    // ---- sum the waves' partial accumulators ----
+#pragma unroll
+    for (int f = 0; f < MT; ++f) red[wave][f][lane] = acc[f];
+    __syncthreads();
+    if (wave >= MT) return;
+    const int f = wave;
+    v4i t = red[0][f][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) t += red[w][f][lane];
+
+    // ---- epilogue: lane l holds D[n = 4 (l / 16) + i][m = l % 16], i < 4 ----
+    const int m = f * 16 + r;
+    const int n = nb * 16 + 4 * c;
+    const uint32_t row = (uint32_t)m * (uint32_t)N + (uint32_t)n;
+    if constexpr (OUT_I32) {
+        __builtin_amdgcn_raw_buffer_store_b128(t, rs_o, m < M ? row * 4u : kOutside, 0, 0);
+    } else {
+        const float sxm = sx[min(m, M - 1)];
+        const float4 s4 = *reinterpret_cast<const float4*>(sw + n);
+        const float y0 = ((float)t[0] * sxm) * s4.x;
+        const float y1 = ((float)t[1] * sxm) * s4.y;
+        const float y2 = ((float)t[2] * sxm) * s4.z;
+        const float y3 = ((float)t[3] * sxm) * s4.w;
+        const u32x2 d = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+        __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, m < M ? row * 2u : kOutside, 0, 0);
+    }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+template <int MT, bool I32>
+hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int M, int N,
+                  int K, void* out, hipStream_t st)
+{
+    const int m_rows = (M + 255) / 256 * 256;
+    const int n_rows = (N + 255) / 256 * 256;
+    hipLaunchKernelGGL((gemm_small_kernel<MT, I32>), dim3(N / 16), dim3(WAVES * 64), 0, st, xq, sx, wq,
+                       sw, M, N, K, m_rows, n_rows, out);
+    return hipGetLastError();
+}
+
+}  // namespace small
+
+// m <= 64, n % 16 == 0, k % 64 == 0 (checked by the caller).
+hipError_t launch_gemm_small(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                             int64_t m, int64_t n, int64_t k, void* out, bool out_i32, hipStream_t st)
+{
+    const int M = (int)m, N = (int)n, K = (int)k;
+#define CK_SMALL(MT_)                                                                      \
+    return out_i32 ? small::launch<MT_, true>(xq, sx, wq, sw, M, N, K, out, st)            \
+                   : small::launch<MT_, false>(xq, sx, wq, sw, M, N, K, out, st)
+    if (m <= 16) CK_SMALL(1);
+    if (m <= 32) CK_SMALL(2);
+    CK_SMALL(4);
+#undef CK_SMALL
+}
+
+}  // namespace ck

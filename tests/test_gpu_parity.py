@@ -337,6 +337,30 @@ def test_gemm_i32_blocked_bit_exact(orc, m, n, k):
     np.testing.assert_array_equal(acc, orc.gemm_i32(xq, wq))
 
 
+SMALL_M_SHAPES = [  # (m, n, k): the few-row kernel (m <= 64): 1, 2 and 4 row fragments,
+    # k-chunk counts below, at and above one batch of the 8 waves, ragged m
+    (1, 4096, 4096), (2, 48, 1024), (16, 1024, 3072), (17, 2048, 128), (32, 160, 12288),
+    (33, 4096, 4096), (48, 3072, 1536), (64, 4096, 12288), (64, 16, 64),
+]
+
+
+@pytest.mark.parametrize("m,n,k", SMALL_M_SHAPES)
+def test_small_m_gemm_bit_exact(orc, m, n, k):
+    say(f"small-m gemm i32 + bf16 blocked m={m} n={n} k={k}")
+    rng = np.random.default_rng(7 * m + n + k)
+    xq = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    sx = (rng.random(m, dtype=np.float32) * 1e-3).astype(np.float32)
+    sw = (rng.random(n, dtype=np.float32) * 1e-3).astype(np.float32)
+    xb, wb = dev(to_blocked(xq)), dev(to_blocked(wq))
+    acc_o = orc.gemm_i32(xq, wq)
+    acc = host(ck.ck_int8_gemm_i32(xb, wb, "blocked", m=m, n=n))
+    np.testing.assert_array_equal(acc, acc_o)
+    y = bf16_host(ck.ck_int8_gemm_bf16(xb, dev(sx.reshape(m, 1)), wb, dev(sw.reshape(n, 1)),
+                                       layout="blocked"))
+    np.testing.assert_array_equal(y, orc.dequant(acc_o, sx, sw))
+
+
 @pytest.mark.parametrize("m,k,n,act,g", LINEAR_CASES)
 def test_int8_linear_blocked_bit_exact(orc, m, k, n, act, g):
     say(f"int8_linear blocked m={m} k={k} n={n} act={act} g={g}")

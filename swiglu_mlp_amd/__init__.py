@@ -52,41 +52,48 @@ def lib() -> ctypes.CDLL:
     """Load libck_convrot.so (after torch, so both use one HIP runtime)."""
     global _lib
     if _lib is None:
-        import torch  # noqa: F401  -- loads torch's HIP runtime first
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m swiglu_mlp_amd.build` (hipcc, gfx950)")
-        L = ctypes.CDLL(LIB_PATH)
-        p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
-        sig = {
-            "ck_weight_prep": [p, i64, i64, i32, p, p, p],
-            "ck_weight_pack": [p, i64, i64, p, p],
-            "ck_act_quant": [p, i64, i64, i64, i32, i32, i32, p, p, p],
-            "ck_int8_linear": [p, i64, i32, p, p, i32, i64, i64, i64, i32, p, p, sz, p],
-            "ck_int8_gemm_bf16": [p, p, p, p, i32, i64, i64, i64, p, p],
-            "ck_swiglu_mlp": [p, p, p, p, p, i32, i64, i64, i64, i32, p, p, sz, p],
-            "ck_int8_gemm_i32": [p, p, i32, i64, i64, i64, p, p],
-            "ck_silu_f32": [p, i64, p, p],
-            "ck_act_rotate_f32": [p, i64, i64, i64, i32, i32, p, p],
-        }
-        for name, args in sig.items():
-            f = getattr(L, name)
-            f.argtypes = args
-            f.restype = ctypes.c_int
-        L.ck_int8_linear_workspace_size.argtypes = [i64, i64]
-        L.ck_int8_linear_workspace_size.restype = sz
-        L.ck_swiglu_mlp_workspace_size.argtypes = [i64, i64, i64]
-        L.ck_swiglu_mlp_workspace_size.restype = sz
-        L.ck_blocked_rows.argtypes = [i64]
-        L.ck_blocked_rows.restype = i64
-        L.ck_blocked_size.argtypes = [i64, i64]
-        L.ck_blocked_size.restype = sz
-        L.ck_status_str.argtypes = [ctypes.c_int]
-        L.ck_status_str.restype = ctypes.c_char_p
-        L.ck_version.argtypes = []
-        L.ck_version.restype = ctypes.c_char_p
-        _lib = L
+        _lib = bind(LIB_PATH)
     return _lib
+
+
+def bind(path: str) -> ctypes.CDLL:
+    """Load a build of the library at `path` with every entry point's C
+    signature declared.  Without declared argument types ctypes passes Python
+    ints as C int, masking 64-bit pointers and sizes to 32 bits."""
+    import torch  # noqa: F401  -- loads torch's HIP runtime first
+    L = ctypes.CDLL(path)
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "ck_weight_prep": [p, i64, i64, i32, p, p, p],
+        "ck_weight_pack": [p, i64, i64, p, p],
+        "ck_act_quant": [p, i64, i64, i64, i32, i32, i32, p, p, p],
+        "ck_int8_linear": [p, i64, i32, p, p, i32, i64, i64, i64, i32, p, p, sz, p],
+        "ck_int8_gemm_bf16": [p, p, p, p, i32, i64, i64, i64, p, p],
+        "ck_swiglu_mlp": [p, p, p, p, p, i32, i64, i64, i64, i32, p, p, sz, p],
+        "ck_int8_gemm_i32": [p, p, i32, i64, i64, i64, p, p],
+        "ck_silu_f32": [p, i64, p, p],
+        "ck_act_rotate_f32": [p, i64, i64, i64, i32, i32, p, p],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    L.ck_int8_linear_workspace_size.argtypes = [i64, i64]
+    L.ck_int8_linear_workspace_size.restype = sz
+    L.ck_swiglu_mlp_workspace_size.argtypes = [i64, i64, i64]
+    L.ck_swiglu_mlp_workspace_size.restype = sz
+    L.ck_blocked_rows.argtypes = [i64]
+    L.ck_blocked_rows.restype = i64
+    L.ck_blocked_size.argtypes = [i64, i64]
+    L.ck_blocked_size.restype = sz
+    L.ck_status_str.argtypes = [ctypes.c_int]
+    L.ck_status_str.restype = ctypes.c_char_p
+    L.ck_version.argtypes = []
+    L.ck_version.restype = ctypes.c_char_p
+    return L
 
 
 def _call(name: str, *args) -> None:

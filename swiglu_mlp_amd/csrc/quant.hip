@@ -213,8 +213,9 @@ namespace {
 constexpr int kChOptions[] = {1, 2, 3, 4, 6, 8, 12, 16};
 
 // Choose (log2 T, CH) with T*CH >= k/8, T a power of two in [max(8, G/8), 256].
-// Prefer no idle chunk slots, then T >= 64 (full waves per row), then CH near 6
-// (enough loads in flight per lane without spilling).
+// Prefer no idle chunk slots, then the widest team (more lanes in flight per
+// row; measured at k = 3072: T = 128 beats T = 64 and T = 32, and at k = 12288
+// T = 256 beats T = 128), then CH near 6.
 bool choose_team(int k, int g, int* log_t, int* ch)
 {
     const int k8 = k / 8;
@@ -226,7 +227,7 @@ bool choose_team(int k, int g, int* log_t, int* ch)
         for (int c : kChOptions) {
             if ((long)T * c < k8) continue;
             const long waste = (long)T * c - k8;
-            const long score = waste * 1000 + (T < 64 ? 100 : 0) + (c > 6 ? c - 6 : 6 - c);
+            const long score = waste * 1000 + (8 - lt) * 20 + (c > 6 ? c - 6 : 6 - c);
             if (best < 0 || score < best) {
                 best = score;
                 *log_t = lt;

@@ -78,7 +78,7 @@ def small_m_sweep(steps: int, warmup: int):
 
             def call():
                 rc = L.ck_int8_gemm_bf16(xq.data_ptr(), sx.data_ptr(), wb.data_ptr(), sw.data_ptr(),
-                                         ck.CK_LAYOUT_BLOCKED, m, n, k, y.data_ptr(),
+                                         None, None, ck.CK_LAYOUT_BLOCKED, m, n, k, y.data_ptr(),
                                          stream.cuda_stream)
                 if rc:
                     raise RuntimeError(L.ck_status_str(rc).decode())
@@ -187,14 +187,14 @@ def main():
                                                  sx.data_ptr(), s),
              0, m * h * 2 + m * h + m * 4, "hbm"),
             ("gate_up_gemm", lambda s: L.ck_int8_gemm_bf16(xq.data_ptr(), sx.data_ptr(),
-                                                           wgu.data_ptr(), sgu.data_ptr(), BLK,
+                                                           wgu.data_ptr(), sgu.data_ptr(), None, None, BLK,
                                                            m, 2 * inter, h, t1.data_ptr(), s),
              2 * m * 2 * inter * h, m * h + 2 * inter * h + m * 2 * inter * 2, "mfma"),
             ("swiglu_quant", lambda s: L.ck_act_quant(t1.data_ptr(), 2 * inter, m, inter, 1, g,
                                                       BLK, hq.data_ptr(), sh.data_ptr(), s),
              0, m * inter * 4 + m * inter + m * 4, "hbm"),
             ("down_gemm", lambda s: L.ck_int8_gemm_bf16(hq.data_ptr(), sh.data_ptr(),
-                                                        wd.data_ptr(), sd.data_ptr(), BLK,
+                                                        wd.data_ptr(), sd.data_ptr(), None, None, BLK,
                                                         m, h, inter, y.data_ptr(), s),
              2 * m * h * inter, m * inter + h * inter + m * h * 2, "mfma"),
         ]
@@ -213,7 +213,7 @@ def main():
                                                    xq.data_ptr(), sx.data_ptr(), s),
              0, m * ldx * 2 + m * k + m * 4, "hbm"),
             ("gemm", lambda s: L.ck_int8_gemm_bf16(xq.data_ptr(), sx.data_ptr(), wq.data_ptr(),
-                                                   sw.data_ptr(), BLK, m, n, k, y.data_ptr(), s),
+                                                   sw.data_ptr(), None, None, BLK, m, n, k, y.data_ptr(), s),
              2 * m * n * k, m * k + n * k + m * n * 2, "mfma"),
         ]
     torch.cuda.synchronize()

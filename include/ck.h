@@ -148,19 +148,30 @@ ck_status ck_act_quant(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,
 /*   layout   CK_LAYOUT_ROWS: x_q is [m, k] (m * k bytes); CK_LAYOUT_BLOCKED:
  *            x_q is ck_blocked_size(m, k) bytes (padding rows not written). */
 
-/* ConvRot int8_linear: y = dequant(act_quant(x) . w_q^T).
+/* ConvRot int8_linear: y = dequant(act_quant(x) . w_q^T) (+ bias + residual).
  * Source: comfy-kitchen PR #277, "The key observation" and "Measured results";
  * sglang PR #44196, "Motivation" (int8_linear(..., input_act="swiglu")).
+ * Bias and residual: comfy-kitchen PR #277, "Changes" (the INT8 linear is
+ * tested with bias and residual) and PR #248's commit list (residuals fused
+ * into the kernels).
  *   x, ldx, act   as ck_act_quant
  *   w_q      int8 weight codes from ck_weight_prep (CK_LAYOUT_ROWS) or
  *            ck_weight_pack (CK_LAYOUT_BLOCKED), read
  *   w_scale  [n]    FP32 from ck_weight_prep, read
+ *   bias     [n]    FP32, read, 16-byte aligned, or NULL
+ *   residual [m, n] BF16 row-major (row stride n), read, 8-byte aligned, or
+ *            NULL; it may be y itself (each element is read before it is
+ *            written) but must not otherwise overlap y.
+ *            Epilogue order: t = fl(fl(f32(acc) * x_scale[m]) * w_scale[n]);
+ *            t = fl(t + bias[n]); t = fl(t + f32(residual[m, n])); y = bf16(t),
+ *            round-to-nearest-even.
  *   layout   layout of w_q; the activation codes use the same one
  *   y        [m, n] BF16, written (row stride n)
  *   workspace  device buffer of at least ck_int8_linear_workspace_size(m, k)
  *            bytes, 256-byte aligned; clobbered (holds x_q and x_scale). */
 ck_status ck_int8_linear(const uint16_t *x, int64_t ldx, int32_t act,
-                         const int8_t *w_q, const float *w_scale, int32_t layout,
+                         const int8_t *w_q, const float *w_scale, const float *bias,
+                         const uint16_t *residual, int32_t layout,
                          int64_t m, int64_t n, int64_t k, int32_t group,
                          uint16_t *y, void *workspace, size_t workspace_bytes,
                          void *stream);
@@ -169,9 +180,11 @@ size_t ck_int8_linear_workspace_size(int64_t m, int64_t k);
 /* The INT8 GEMM with its dequant epilogue alone (the second half of
  * ck_int8_linear), for callers that hold quantized activations.
  *   x_q, w_q int8 codes in `layout` (both), x_scale [m], w_scale [n] FP32,
- *   read; y [m, n] BF16 written. */
+ *   read; bias, residual as ck_int8_linear (either may be NULL); y [m, n]
+ *   BF16 written. */
 ck_status ck_int8_gemm_bf16(const int8_t *x_q, const float *x_scale,
                             const int8_t *w_q, const float *w_scale,
+                            const float *bias, const uint16_t *residual,
                             int32_t layout, int64_t m, int64_t n, int64_t k,
                             uint16_t *y, void *stream);
 

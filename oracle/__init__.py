@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.orc_gemm_i32.restype = None
         L.orc_dequant_bf16.argtypes = [p, p, p, i64, i64, p]
         L.orc_dequant_bf16.restype = None
+        L.orc_epilogue_bf16.argtypes = [p, p, p, p, p, i64, i64, p]
+        L.orc_epilogue_bf16.restype = None
         L.orc_eager_swiglu_bf16.argtypes = [p, i64, i64, i64, p]
         L.orc_eager_swiglu_bf16.restype = None
         _lib = L
@@ -231,12 +233,32 @@ def dequant(acc, sx, sw) -> np.ndarray:
     return y
 
 
-def int8_linear(x_bf16, act: int, wq, sw, g: int, return_all: bool = False):
+def epilogue(acc, sx, sw, bias=None, residual=None) -> np.ndarray:
+    """Dequant with optional F32 bias [n] and BF16 residual [m, n] (uint16 bits)."""
+    acc = _c(acc, np.int32)
+    sx, sw = _c(sx, np.float32).reshape(-1), _c(sw, np.float32).reshape(-1)
+    m, n = acc.shape
+    b = None if bias is None else _c(bias, np.float32).reshape(-1)
+    r = None if residual is None else _c(residual, np.uint16)
+    assert b is None or b.shape == (n,)
+    assert r is None or r.shape == (m, n)
+    y = np.empty((m, n), dtype=np.uint16)
+    lib().orc_epilogue_bf16(_ptr(acc), _ptr(sx), _ptr(sw), None if b is None else _ptr(b),
+                            None if r is None else _ptr(r), m, n, _ptr(y))
+    return y
+
+
+def int8_linear(x_bf16, act: int, wq, sw, g: int, return_all: bool = False, bias=None,
+                residual=None):
     """ConvRot int8_linear: quantize the (optionally SwiGLU'd) activation in the
-    rotated basis, multiply against W_rot's codes, dequantize to BF16."""
+    rotated basis, multiply against W_rot's codes, dequantize to BF16 (plus the
+    optional bias and residual)."""
     xq, sx = act_quant(x_bf16, act, g, k=np.asarray(wq).shape[1])
     acc = gemm_i32(xq, wq)
-    y = dequant(acc, sx, sw)
+    if bias is None and residual is None:
+        y = dequant(acc, sx, sw)
+    else:
+        y = epilogue(acc, sx, sw, bias, residual)
     if return_all:
         return dict(xq=xq, sx=sx, acc=acc, y=y)
     return y

@@ -303,6 +303,30 @@ void orc_dequant_bf16(const int32_t *acc, const float *sx, const float *sw,
         }
 }
 
+/* Epilogue with the optional bias and residual of a linear layer.
+ * comfy-kitchen PR #277, "Changes": the INT8 linear is tested with bias and
+ * residual; comfy-kitchen PR #248, commit list: input activations and
+ * residuals are fused into the kernels.  The pages do not fix the FP32 order;
+ * the reading taken is one FP32 sum in the epilogue, then one BF16 rounding:
+ *   t = fl(fl(f32(acc) * sx[m]) * sw[n]);  t = fl(t + bias[n]);
+ *   t = fl(t + f32(res[m, n]));  y = bf16(t)
+ * bias is F32 [n] (may be NULL), res is BF16 [m, n] row-major (may be NULL). */
+void orc_epilogue_bf16(const int32_t *acc, const float *sx, const float *sw,
+                       const float *bias, const uint16_t *res, int64_t m, int64_t n,
+                       uint16_t *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            float v = (float)acc[i * n + j];
+            v = v * sx[i];
+            v = v * sw[j];
+            if (bias) v = v + bias[j];
+            if (res) v = v + bf16_to_f32(res[i * n + j]);
+            y[i * n + j] = orc_f32_to_bf16(v);
+        }
+}
+
 /* [SWI] "Motivation": the unfused path writes silu(gate) * up to HBM in BF16
  * (silu rounded to BF16 first, then the product rounded to BF16). */
 void orc_eager_swiglu_bf16(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,

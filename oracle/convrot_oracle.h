@@ -78,6 +78,12 @@ void orc_gemm_i32(const int8_t *xq, const int8_t *wq, int64_t m, int64_t n,
 void orc_dequant_bf16(const int32_t *acc, const float *sx, const float *sw,
                       int64_t m, int64_t n, uint16_t *y);
 
+/* Epilogue with optional F32 bias [n] and BF16 residual [m, n] (either may be
+ * NULL): y = bf16(fl(fl(fl(fl(f32(acc) * sx[m]) * sw[n]) + bias[n]) + res[m, n])). */
+void orc_epilogue_bf16(const int32_t *acc, const float *sx, const float *sw,
+                       const float *bias, const uint16_t *res, int64_t m, int64_t n,
+                       uint16_t *y);
+
 /* Eager (unfused) SwiGLU activation: a = bf16(bf16(silu(gate)) * up),
  * written back as BF16 [m, k]; the path the fused quantizer replaces. */
 void orc_eager_swiglu_bf16(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,

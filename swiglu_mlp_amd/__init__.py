@@ -11,8 +11,8 @@ Entry points keep the C names:
 * ``ck_weight_prep(w, group)``           -> (w_q int8 [n, k], w_scale f32 [n, 1])
 * ``ck_weight_pack(w_q)``                 -> w_q in the blocked layout [n_pad, k]
 * ``ck_act_quant(x, act, group, k=None, layout=...)`` -> (x_q, x_scale f32 [m, 1])
-* ``ck_int8_linear(x, w_q, w_scale, group, input_act=None, layout=...)`` -> y bf16
-* ``ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, layout=...)``  -> y bf16 [m, n]
+* ``ck_int8_linear(x, w_q, w_scale, group, input_act=None, layout=..., bias=None, residual=None)``
+* ``ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, layout=..., bias=None, residual=None)``
 * ``ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group, layout=...)`` -> y bf16
 * test hooks ``ck_int8_gemm_i32``, ``ck_silu_f32``, ``ck_act_rotate_f32``
 
@@ -70,8 +70,8 @@ def bind(path: str) -> ctypes.CDLL:
         "ck_weight_prep": [p, i64, i64, i32, p, p, p],
         "ck_weight_pack": [p, i64, i64, p, p],
         "ck_act_quant": [p, i64, i64, i64, i32, i32, i32, p, p, p],
-        "ck_int8_linear": [p, i64, i32, p, p, i32, i64, i64, i64, i32, p, p, sz, p],
-        "ck_int8_gemm_bf16": [p, p, p, p, i32, i64, i64, i64, p, p],
+        "ck_int8_linear": [p, i64, i32, p, p, p, p, i32, i64, i64, i64, i32, p, p, sz, p],
+        "ck_int8_gemm_bf16": [p, p, p, p, p, p, i32, i64, i64, i64, p, p],
         "ck_swiglu_mlp": [p, p, p, p, p, i32, i64, i64, i64, i32, p, p, sz, p],
         "ck_int8_gemm_i32": [p, p, i32, i64, i64, i64, p, p],
         "ck_silu_f32": [p, i64, p, p],
@@ -211,8 +211,25 @@ def ck_act_quant(x, input_act=None, group: int = 128, k: int | None = None, layo
     return x_q, x_scale
 
 
+def _extra(bias, residual, m, n, dev):
+    """Optional epilogue terms: F32 bias [n] and BF16 residual [m, n]."""
+    import torch
+    bp = rp = None
+    if bias is not None:
+        _need(bias, torch.float32, 1, "bias")
+        if bias.shape[0] != n or bias.device != dev or not bias.is_contiguous():
+            raise ValueError(f"bias needs a contiguous ({n},) float32 tensor on {dev}")
+        bp = bias.data_ptr()
+    if residual is not None:
+        _need(residual, torch.bfloat16, 2, "residual")
+        if tuple(residual.shape) != (m, n) or residual.device != dev or not residual.is_contiguous():
+            raise ValueError(f"residual needs a contiguous ({m}, {n}) bfloat16 tensor on {dev}")
+        rp = residual.data_ptr()
+    return bp, rp
+
+
 def ck_int8_linear(x, w_q, w_scale, group: int = 128, input_act=None, out=None,
-                   workspace=None, layout="rows"):
+                   workspace=None, layout="rows", bias=None, residual=None):
     import torch
     _need(x, torch.bfloat16, 2, "activation")
     _need(w_q, torch.int8, 2, "weight")
@@ -231,12 +248,14 @@ def ck_int8_linear(x, w_q, w_scale, group: int = 128, input_act=None, out=None,
     ws_bytes = lib().ck_int8_linear_workspace_size(m, k)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
-    _call("ck_int8_linear", x.data_ptr(), ldx, act, w_q.data_ptr(), w_scale.data_ptr(), lay, m, n,
-          k, group, y.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x))
+    bp, rp = _extra(bias, residual, m, n, x.device)
+    _call("ck_int8_linear", x.data_ptr(), ldx, act, w_q.data_ptr(), w_scale.data_ptr(), bp, rp,
+          lay, m, n, k, group, y.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x))
     return y
 
 
-def ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, out=None, layout="rows"):
+def ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, out=None, layout="rows", bias=None,
+                      residual=None):
     import torch
     _need(x_q, torch.int8, 2, "activation codes")
     _need(w_q, torch.int8, 2, "weight")
@@ -250,8 +269,9 @@ def ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, out=None, layout="rows"):
     _scale(x_scale, m, "activation scale")
     _scale(w_scale, n, "weight_scale")
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x_q.device)
+    bp, rp = _extra(bias, residual, m, n, x_q.device)
     _call("ck_int8_gemm_bf16", x_q.data_ptr(), x_scale.data_ptr(), w_q.data_ptr(),
-          w_scale.data_ptr(), lay, m, n, k, y.data_ptr(), _stream(x_q))
+          w_scale.data_ptr(), bp, rp, lay, m, n, k, y.data_ptr(), _stream(x_q))
     return y
 
 

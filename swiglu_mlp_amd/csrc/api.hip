@@ -146,14 +146,26 @@ static ck_status check_gemm_args(const int8_t* x_q, const float* x_scale, const 
     return CK_OK;
 }
 
+// Optional epilogue terms: bias is read as float4, the residual as 8-byte
+// groups of 4 BF16 values.
+static ck_status check_extra(const float* bias, const uint16_t* residual)
+{
+    if (bias && !aligned16(bias)) return CK_EINVAL;
+    if (residual && ((uintptr_t)residual % 8) != 0) return CK_EINVAL;
+    return CK_OK;
+}
+
 ck_status ck_int8_gemm_bf16(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
-                            const float* w_scale, int32_t layout, int64_t m, int64_t n, int64_t k,
-                            uint16_t* y, void* stream)
+                            const float* w_scale, const float* bias, const uint16_t* residual,
+                            int32_t layout, int64_t m, int64_t n, int64_t k, uint16_t* y,
+                            void* stream)
 {
     CK_TRY(check_gemm_args(x_q, x_scale, w_q, w_scale, layout, m, n, k, y, true));
     if (m == 0 || n == 0) return CK_OK;
+    CK_TRY(check_extra(bias, residual));
     return from_hip(ck::launch_gemm_bf16(x_q, x_scale, w_q, w_scale, m, n, k, y,
-                                         layout == CK_LAYOUT_BLOCKED, (hipStream_t)stream));
+                                         layout == CK_LAYOUT_BLOCKED, (hipStream_t)stream,
+                                         ck::EpiExtra{bias, residual}));
 }
 
 ck_status ck_int8_gemm_i32(const int8_t* x_q, const int8_t* w_q, int32_t layout, int64_t m,
@@ -166,9 +178,9 @@ ck_status ck_int8_gemm_i32(const int8_t* x_q, const int8_t* w_q, int32_t layout,
 }
 
 ck_status ck_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, const int8_t* w_q,
-                         const float* w_scale, int32_t layout, int64_t m, int64_t n, int64_t k,
-                         int32_t group, uint16_t* y, void* workspace, size_t workspace_bytes,
-                         void* stream)
+                         const float* w_scale, const float* bias, const uint16_t* residual,
+                         int32_t layout, int64_t m, int64_t n, int64_t k, int32_t group, uint16_t* y,
+                         void* workspace, size_t workspace_bytes, void* stream)
 {
     CK_TRY(check_k(k, group));
     CK_TRY(check_act(act, ldx, k));
@@ -178,6 +190,7 @@ ck_status ck_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, const int8
     if (m == 0 || n == 0) return CK_OK;
     if (!x || !w_q || !w_scale || !y) return CK_EINVAL;
     if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_scale) || !aligned16(y)) return CK_EINVAL;
+    CK_TRY(check_extra(bias, residual));
     const size_t need = ck_int8_linear_workspace_size(m, k);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
         return CK_EWORKSPACE;
@@ -188,7 +201,8 @@ ck_status ck_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, const int8
     hipStream_t st = (hipStream_t)stream;
     CK_TRY(from_hip(ck::launch_quant_rows(act == CK_ACT_SWIGLU ? 1 : 0, x, ldx, m, k, group, xq,
                                           sx, nullptr, blocked, st)));
-    return from_hip(ck::launch_gemm_bf16(xq, sx, w_q, w_scale, m, n, k, y, blocked, st));
+    return from_hip(ck::launch_gemm_bf16(xq, sx, w_q, w_scale, m, n, k, y, blocked, st,
+                                         ck::EpiExtra{bias, residual}));
 }
 
 // Sized for either layout: x codes, x scales, the [m, 2i] BF16 gate|up

@@ -23,6 +23,39 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Optional terms of a linear layer's epilogue (either pointer may be null):
+// bias is F32 [N]; res is a BF16 [M, N] row-major residual, which may be the
+// output buffer itself.  comfy-kitchen PR #277, "Changes" (the INT8 linear is
+// tested with bias and residual) and PR #248's commit list (residuals fused
+// into the kernels); the FP32 order is a reading: one FP32 sum, then one BF16
+// rounding, t = fl(fl(t + bias[n]) + f32(res[m, n])).
+struct EpiExtra {
+    const float* bias;
+    const uint16_t* res;
+};
+
+// Adds the optional terms to the four consecutive outputs (m, n .. n + 3).
+// n % 4 == 0; m must be a valid row (callers clamp padding rows, whose stores
+// are dropped).
+__device__ __forceinline__ void epi_extra4(float& y0, float& y1, float& y2, float& y3,
+                                           const EpiExtra& e, int m, int n, int N)
+{
+    if (e.bias) {
+        const float4 b = *reinterpret_cast<const float4*>(e.bias + n);
+        y0 = y0 + b.x;
+        y1 = y1 + b.y;
+        y2 = y2 + b.z;
+        y3 = y3 + b.w;
+    }
+    if (e.res) {
+        const uint2 r = *reinterpret_cast<const uint2*>(e.res + (int64_t)m * N + n);
+        y0 = y0 + bf16_lo(r.x);
+        y1 = y1 + bf16_hi(r.x);
+        y2 = y2 + bf16_lo(r.y);
+        y3 = y3 + bf16_hi(r.y);
+    }
+}
+
 // Two FP32 values -> packed BF16 pair (lo = a, hi = b), round-to-nearest-even:
 // one v_cvt_pk_bf16_f32 on gfx950.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ck_device.hpp"
+
 namespace ck {
 
 // Rotation + per-row INT8 quantization of m rows of k values.
@@ -24,8 +26,10 @@ hipError_t launch_silu(const uint16_t* g, int64_t n, float* out, hipStream_t st)
 
 // y[m, n] = bf16(fl(fl(f32(x_q . w_q^T) * sx[m]) * sw[n])); both operands in
 // the row-major or the blocked layout.
+// `ex` adds an optional bias and residual before the BF16 rounding.
 hipError_t launch_gemm_bf16(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                            int64_t m, int64_t n, int64_t k, uint16_t* y, bool blocked, hipStream_t st);
+                            int64_t m, int64_t n, int64_t k, uint16_t* y, bool blocked, hipStream_t st,
+                            EpiExtra ex = EpiExtra{});
 
 // acc[m, n] = x_q . w_q^T in int32.
 hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
@@ -34,11 +38,12 @@ hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t m, int64_
 // Blocked-layout GEMM (gemm_blk.hip).
 hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                            int64_t m, int64_t n, int64_t k, void* out, bool out_i32, int num_cu,
-                           hipStream_t st);
+                           hipStream_t st, EpiExtra ex = EpiExtra{});
 
 // Blocked-layout GEMM for m <= 64 (gemm_small.hip): streams the weights once.
 hipError_t launch_gemm_small(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                             int64_t m, int64_t n, int64_t k, void* out, bool out_i32, hipStream_t st);
+                             int64_t m, int64_t n, int64_t k, void* out, bool out_i32, hipStream_t st,
+                             EpiExtra ex = EpiExtra{});
 
 // Largest m routed to launch_gemm_small.
 constexpr int64_t kSmallM = 64;
@@ -49,6 +54,6 @@ int num_cus();
 // per CU; writes BF16 y (with scales) or int32 acc (out_i32).
 hipError_t launch_gemm_big(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                            int64_t m, int64_t n, int64_t k, void* out, bool out_i32, int bn,
-                           int num_cu, hipStream_t st);
+                           int num_cu, hipStream_t st, EpiExtra ex = EpiExtra{});
 
 }  // namespace ck

@@ -41,7 +41,7 @@ template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool OUT_I32>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_i8_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
     const float* __restrict__ sw, int M, int N, int K, void* __restrict__ out, int tiles_m,
-    int tiles_n, int group_m)
+    int tiles_n, int group_m, EpiExtra ex)
 {
     constexpr int NT = WAVES_M * WAVES_N * 64;
     constexpr int WM = BM / WAVES_M;     // wave tile, m extent
@@ -178,10 +178,11 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_i8_kernel(
                         make_int4(a0, a1, a2, a3);
                 } else {
                     const float4 s4 = *reinterpret_cast<const float4*>(sw + n);
-                    const float y0 = ((float)a0 * sxm) * s4.x;
-                    const float y1 = ((float)a1 * sxm) * s4.y;
-                    const float y2 = ((float)a2 * sxm) * s4.z;
-                    const float y3 = ((float)a3 * sxm) * s4.w;
+                    float y0 = ((float)a0 * sxm) * s4.x;
+                    float y1 = ((float)a1 * sxm) * s4.y;
+                    float y2 = ((float)a2 * sxm) * s4.z;
+                    float y3 = ((float)a3 * sxm) * s4.w;
+                    epi_extra4(y0, y1, y2, y3, ex, m, n, N);
                     const uint32_t p0 = f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16);
                     const uint32_t p1 = f32_to_bf16_bits(y2) | (f32_to_bf16_bits(y3) << 16);
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (int64_t)m * N + n) =
@@ -249,44 +250,46 @@ int pick_cfg(int64_t m, int64_t n, int ncu)
 
 template <int BM, int BN, int BK, int WM_, int WN_, bool I32>
 hipError_t launch_one(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int M,
-                      int N, int K, void* out, hipStream_t st)
+                      int N, int K, void* out, hipStream_t st, EpiExtra ex)
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int group_m = tiles_m < 8 ? tiles_m : 8;
     hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM_, WN_, I32>), dim3(tiles_m * tiles_n),
                        dim3(WM_ * WN_ * 64), 0, st, xq, sx, wq, sw, M, N, K, out, tiles_m, tiles_n,
-                       group_m);
+                       group_m, ex);
     return hipGetLastError();
 }
 
 template <bool I32>
 hipError_t launch_gemm_t(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                         int64_t m, int64_t n, int64_t k, void* out, hipStream_t st)
+                         int64_t m, int64_t n, int64_t k, void* out, hipStream_t st,
+                         EpiExtra ex = EpiExtra{})
 {
     const int ncu = num_cus();
     const int cfg = pick_cfg(m, n, ncu);
     if (kCfgs[cfg].big)
-        return launch_gemm_big(xq, sx, wq, sw, m, n, k, out, I32, kCfgs[cfg].bn, ncu, st);
+        return launch_gemm_big(xq, sx, wq, sw, m, n, k, out, I32, kCfgs[cfg].bn, ncu, st, ex);
     const bool bk128 = (k % 128) == 0;
     const int M = (int)m, N = (int)n, K = (int)k;
     switch ((cfg - 2) * 2 + (bk128 ? 1 : 0)) {
-        case 0: return launch_one<128, 128, 64, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st);
-        case 1: return launch_one<128, 128, 128, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st);
-        case 2: return launch_one<64, 128, 64, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st);
-        default: return launch_one<64, 128, 128, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st);
+        case 0: return launch_one<128, 128, 64, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st, ex);
+        case 1: return launch_one<128, 128, 128, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st, ex);
+        case 2: return launch_one<64, 128, 64, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st, ex);
+        default: return launch_one<64, 128, 128, 2, 2, I32>(xq, sx, wq, sw, M, N, K, out, st, ex);
     }
 }
 
 }  // namespace
 
 hipError_t launch_gemm_bf16(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                            int64_t m, int64_t n, int64_t k, uint16_t* y, bool blocked, hipStream_t st)
+                            int64_t m, int64_t n, int64_t k, uint16_t* y, bool blocked, hipStream_t st,
+                            EpiExtra ex)
 {
     if (m == 0 || n == 0) return hipSuccess;
-    if (blocked && m <= kSmallM) return launch_gemm_small(xq, sx, wq, sw, m, n, k, y, false, st);
-    if (blocked) return launch_gemm_blk(xq, sx, wq, sw, m, n, k, y, false, num_cus(), st);
-    return launch_gemm_t<false>(xq, sx, wq, sw, m, n, k, y, st);
+    if (blocked && m <= kSmallM) return launch_gemm_small(xq, sx, wq, sw, m, n, k, y, false, st, ex);
+    if (blocked) return launch_gemm_blk(xq, sx, wq, sw, m, n, k, y, false, num_cus(), st, ex);
+    return launch_gemm_t<false>(xq, sx, wq, sw, m, n, k, y, st, ex);
 }
 
 hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,

@@ -91,11 +91,11 @@ __device__ __forceinline__ void tile_coords(int j, int tiles_m, int tiles_n, int
     tn = (j % width) / gm;
 }
 
-template <int BN, bool OUT_I32>
+template <int BN, bool OUT_I32, bool EXTRA>
 __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
     const float* __restrict__ sw, int M, int N, int K, void* __restrict__ out, int tiles_m,
-    int tiles_n, int group_m)
+    int tiles_n, int group_m, EpiExtra ex)
 {
     // The body uses AMDGPU-only types (buffer resources); the host pass only
     // needs this function's launch stub.
@@ -262,10 +262,13 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
                             const v4i d = {f[4 * qd], f[4 * qd + 1], f[4 * qd + 2], f[4 * qd + 3]};
                             __builtin_amdgcn_raw_buffer_store_b128(d, rs_o, o * 4u, 0, 0);
                         } else {
-                            const float y0 = ((float)f[4 * qd + 0] * sxm[j]) * s4[qd].x;
-                            const float y1 = ((float)f[4 * qd + 1] * sxm[j]) * s4[qd].y;
-                            const float y2 = ((float)f[4 * qd + 2] * sxm[j]) * s4[qd].z;
-                            const float y3 = ((float)f[4 * qd + 3] * sxm[j]) * s4[qd].w;
+                            float y0 = ((float)f[4 * qd + 0] * sxm[j]) * s4[qd].x;
+                            float y1 = ((float)f[4 * qd + 1] * sxm[j]) * s4[qd].y;
+                            float y2 = ((float)f[4 * qd + 2] * sxm[j]) * s4[qd].z;
+                            float y3 = ((float)f[4 * qd + 3] * sxm[j]) * s4[qd].w;
+                            if constexpr (EXTRA)
+                                epi_extra4(y0, y1, y2, y3, ex, min(m_base + 32 * j, M - 1),
+                                           n_base + 32 * i + 8 * qd, N);
                             const u32x2 d = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
                             __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, o * 2u, 0, 0);
                         }
@@ -278,17 +281,17 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int BN, bool I32>
+template <int BN, bool I32, bool EXTRA>
 hipError_t launch_big(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int M,
-                      int N, int K, void* out, int num_cu, hipStream_t st)
+                      int N, int K, void* out, int num_cu, hipStream_t st, EpiExtra ex)
 {
     const int tiles_m = (M + 255) / 256;
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
     const int grid = tiles < num_cu ? tiles : num_cu;
     const int group_m = tiles_m < 4 ? tiles_m : 4;
-    hipLaunchKernelGGL((gemm_big_kernel<BN, I32>), dim3(grid), dim3(256), 0, st, xq, sx, wq, sw, M,
-                       N, K, out, tiles_m, tiles_n, group_m);
+    hipLaunchKernelGGL((gemm_big_kernel<BN, I32, EXTRA>), dim3(grid), dim3(256), 0, st, xq, sx, wq, sw, M,
+                       N, K, out, tiles_m, tiles_n, group_m, ex);
     return hipGetLastError();
 }
 
@@ -298,15 +301,18 @@ hipError_t launch_big(const int8_t* xq, const float* sx, const int8_t* wq, const
 // (the caller then uses the generic kernel).
 hipError_t launch_gemm_big(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                            int64_t m, int64_t n, int64_t k, void* out, bool out_i32, int bn,
-                           int num_cu, hipStream_t st)
+                           int num_cu, hipStream_t st, EpiExtra ex)
 {
     const int M = (int)m, N = (int)n, K = (int)k;
+    const bool extra = ex.bias || ex.res;
     if (bn == 256)
-        return out_i32 ? big::launch_big<256, true>(xq, sx, wq, sw, M, N, K, out, num_cu, st)
-                       : big::launch_big<256, false>(xq, sx, wq, sw, M, N, K, out, num_cu, st);
+        return out_i32 ? big::launch_big<256, true, false>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex)
+               : extra ? big::launch_big<256, false, true>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex)
+                       : big::launch_big<256, false, false>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex);
     if (bn == 192)
-        return out_i32 ? big::launch_big<192, true>(xq, sx, wq, sw, M, N, K, out, num_cu, st)
-                       : big::launch_big<192, false>(xq, sx, wq, sw, M, N, K, out, num_cu, st);
+        return out_i32 ? big::launch_big<192, true, false>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex)
+               : extra ? big::launch_big<192, false, true>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex)
+                       : big::launch_big<192, false, false>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex);
     return hipErrorNotSupported;
 }
 

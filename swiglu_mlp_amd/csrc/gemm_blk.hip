@@ -124,11 +124,13 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes)
     return v4i{(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
 
-template <int BM, int BN, bool OUT_I32>
+// EXTRA: the epilogue adds the optional bias / residual (a separate
+// instantiation, so the plain epilogue carries no branches for them).
+template <int BM, int BN, bool OUT_I32, bool EXTRA>
 __global__ __launch_bounds__(256) void gemm_blk_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
     const float* __restrict__ sw, int M, int N, int K, int m_rows, int n_rows, void* __restrict__ out,
-    int tiles_m, int tiles_n, int group_m)
+    int tiles_m, int tiles_n, int group_m, EpiExtra ex)
 {
     // The body uses AMDGPU-only types (buffer resources); the host pass only
     // needs this function's launch stub.
@@ -356,10 +358,13 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
                     uint32_t w[4][2];
 #pragma unroll
                     for (int qd = 0; qd < 4; ++qd) {
-                        const float y0 = ((float)f[4 * qd + 0] * sxm[j]) * s4[qd].x;
-                        const float y1 = ((float)f[4 * qd + 1] * sxm[j]) * s4[qd].y;
-                        const float y2 = ((float)f[4 * qd + 2] * sxm[j]) * s4[qd].z;
-                        const float y3 = ((float)f[4 * qd + 3] * sxm[j]) * s4[qd].w;
+                        float y0 = ((float)f[4 * qd + 0] * sxm[j]) * s4[qd].x;
+                        float y1 = ((float)f[4 * qd + 1] * sxm[j]) * s4[qd].y;
+                        float y2 = ((float)f[4 * qd + 2] * sxm[j]) * s4[qd].z;
+                        float y3 = ((float)f[4 * qd + 3] * sxm[j]) * s4[qd].w;
+                        if constexpr (EXTRA)   // loads straight from global memory
+                            epi_extra4(y0, y1, y2, y3, ex, min(m_base + 32 * j, M - 1),
+                                       min(n_base + 32 * i + 8 * qd, N - 4), N);
                         w[qd][0] = pack_bf16x2(y0, y1);
                         w[qd][1] = pack_bf16x2(y2, y3);
                     }
@@ -401,9 +406,9 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int BM, int BN, bool I32>
+template <int BM, int BN, bool I32, bool EXTRA>
 hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int M, int N,
-                  int K, void* out, int num_cu, hipStream_t st)
+                  int K, void* out, int num_cu, hipStream_t st, EpiExtra ex)
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
@@ -417,8 +422,8 @@ hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const flo
     const int group_m = tiles_m < 4 ? tiles_m : 4;
     const int m_rows = (M + 255) / 256 * 256;
     const int n_rows = (N + 255) / 256 * 256;
-    hipLaunchKernelGGL((gemm_blk_kernel<BM, BN, I32>), dim3(grid), dim3(256), 0, st, xq, sx, wq, sw, M,
-                       N, K, m_rows, n_rows, out, tiles_m, tiles_n, group_m);
+    hipLaunchKernelGGL((gemm_blk_kernel<BM, BN, I32, EXTRA>), dim3(grid), dim3(256), 0, st, xq, sx, wq, sw, M,
+                       N, K, m_rows, n_rows, out, tiles_m, tiles_n, group_m, ex);
     return hipGetLastError();
 }
 
@@ -432,7 +437,7 @@ hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const flo
 // 64 x 128.  Shapes with `on` false are built but not chosen.
 hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                            int64_t m, int64_t n, int64_t k, void* out, bool out_i32, int num_cu,
-                           hipStream_t st)
+                           hipStream_t st, EpiExtra ex)
 {
     struct Shape {
         int bm, bn, per_cu;
@@ -459,8 +464,10 @@ hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, 
     }
     const int M = (int)m, N = (int)n, K = (int)k;
 #define CK_BLK(BM_, BN_)                                                                          \
-    return out_i32 ? blk::launch<BM_, BN_, true>(xq, sx, wq, sw, M, N, K, out, num_cu, st)        \
-                   : blk::launch<BM_, BN_, false>(xq, sx, wq, sw, M, N, K, out, num_cu, st)
+    return out_i32 ? blk::launch<BM_, BN_, true, false>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex) \
+           : (ex.bias || ex.res)                                                                   \
+               ? blk::launch<BM_, BN_, false, true>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex)  \
+               : blk::launch<BM_, BN_, false, false>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex)
     switch (best) {
         case 0: CK_BLK(128, 128);
         case 1: CK_BLK(64, 128);

@@ -37,7 +37,8 @@ struct SmallCfg {
 template <int MT, bool OUT_I32>
 __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
-    const float* __restrict__ sw, int M, int N, int K, int m_rows, int n_rows, void* __restrict__ out)
+    const float* __restrict__ sw, int M, int N, int K, int m_rows, int n_rows, void* __restrict__ out,
+    EpiExtra ex)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int U = SmallCfg<MT>::U;
@@ -125,10 +126,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     } else {
         const float sxm = sx[min(m, M - 1)];
         const float4 s4 = *reinterpret_cast<const float4*>(sw + n);
-        const float y0 = ((float)t[0] * sxm) * s4.x;
-        const float y1 = ((float)t[1] * sxm) * s4.y;
-        const float y2 = ((float)t[2] * sxm) * s4.z;
-        const float y3 = ((float)t[3] * sxm) * s4.w;
+        float y0 = ((float)t[0] * sxm) * s4.x;
+        float y1 = ((float)t[1] * sxm) * s4.y;
+        float y2 = ((float)t[2] * sxm) * s4.z;
+        float y3 = ((float)t[3] * sxm) * s4.w;
+        epi_extra4(y0, y1, y2, y3, ex, min(m, M - 1), n, N);
         const u32x2 d = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
         __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, m < M ? row * 2u : kOutside, 0, 0);
     }
@@ -137,12 +139,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 
 template <int MT, bool I32>
 hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int M, int N,
-                  int K, void* out, hipStream_t st)
+                  int K, void* out, hipStream_t st, EpiExtra ex)
 {
     const int m_rows = (M + 255) / 256 * 256;
     const int n_rows = (N + 255) / 256 * 256;
     hipLaunchKernelGGL((gemm_small_kernel<MT, I32>), dim3(N / 16), dim3(WAVES * 64), 0, st, xq, sx, wq,
-                       sw, M, N, K, m_rows, n_rows, out);
+                       sw, M, N, K, m_rows, n_rows, out, ex);
     return hipGetLastError();
 }
 
@@ -150,12 +152,13 @@ hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const flo
 
 // m <= 64, n % 16 == 0, k % 64 == 0 (checked by the caller).
 hipError_t launch_gemm_small(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                             int64_t m, int64_t n, int64_t k, void* out, bool out_i32, hipStream_t st)
+                             int64_t m, int64_t n, int64_t k, void* out, bool out_i32, hipStream_t st,
+                             EpiExtra ex)
 {
     const int M = (int)m, N = (int)n, K = (int)k;
 #define CK_SMALL(MT_)                                                                      \
-    return out_i32 ? small::launch<MT_, true>(xq, sx, wq, sw, M, N, K, out, st)            \
-                   : small::launch<MT_, false>(xq, sx, wq, sw, M, N, K, out, st)
+    return out_i32 ? small::launch<MT_, true>(xq, sx, wq, sw, M, N, K, out, st, ex)        \
+                   : small::launch<MT_, false>(xq, sx, wq, sw, M, N, K, out, st, ex)
     if (m <= 16) CK_SMALL(1);
     if (m <= 32) CK_SMALL(2);
     CK_SMALL(4);

@@ -94,15 +94,18 @@ def test_int8_linear_checks(L, layout):
     f = L.ck_int8_linear
     ws = L.ck_int8_linear_workspace_size(4, 256)
     lay = layout
-    assert f(FAKE, 256, 0, FAKE, FAKE, lay, 4, 40, 256, 128, FAKE, FAKE, ws, None) == ESHAPE  # n % 16
-    assert f(FAKE, 256, 0, FAKE, FAKE, lay, 4, 32, 256, 128, FAKE, FAKE, ws - 1, None) == EWS
-    assert f(FAKE, 256, 0, FAKE, FAKE, lay, 4, 32, 256, 128, FAKE, None, ws, None) == EWS
-    assert f(FAKE, 256, 0, FAKE, FAKE, lay, 4, 32, 256, 128, FAKE, FAKE + 16, ws, None) == EWS
-    assert f(FAKE, 256, 0, None, FAKE, lay, 4, 32, 256, 128, FAKE, FAKE, ws, None) == EINVAL
-    assert f(FAKE, 256, 0, FAKE, FAKE, lay, 0, 32, 256, 128, FAKE, FAKE, 0, None) == OK
-    assert f(FAKE, 256, 0, FAKE, FAKE, 9, 4, 32, 256, 128, FAKE, FAKE, ws, None) == EINVAL
+    assert f(FAKE, 256, 0, FAKE, FAKE, None, None, lay, 4, 40, 256, 128, FAKE, FAKE, ws, None) == ESHAPE  # n % 16
+    assert f(FAKE, 256, 0, FAKE, FAKE, None, None, lay, 4, 32, 256, 128, FAKE, FAKE, ws - 1, None) == EWS
+    assert f(FAKE, 256, 0, FAKE, FAKE, None, None, lay, 4, 32, 256, 128, FAKE, None, ws, None) == EWS
+    assert f(FAKE, 256, 0, FAKE, FAKE, None, None, lay, 4, 32, 256, 128, FAKE, FAKE + 16, ws, None) == EWS
+    assert f(FAKE, 256, 0, None, FAKE, None, None, lay, 4, 32, 256, 128, FAKE, FAKE, ws, None) == EINVAL
+    assert f(FAKE, 256, 0, FAKE, FAKE, None, None, lay, 0, 32, 256, 128, FAKE, FAKE, 0, None) == OK
+    assert f(FAKE, 256, 0, FAKE, FAKE, None, None, 9, 4, 32, 256, 128, FAKE, FAKE, ws, None) == EINVAL
+    # optional bias (float4 reads) and residual (8-byte reads) must be aligned
+    assert f(FAKE, 256, 0, FAKE, FAKE, FAKE + 4, None, lay, 4, 32, 256, 128, FAKE, FAKE, ws, None) == EINVAL
+    assert f(FAKE, 256, 0, FAKE, FAKE, None, FAKE + 2, lay, 4, 32, 256, 128, FAKE, FAKE, ws, None) == EINVAL
     # operands addressed with 32-bit offsets: refuse what would overflow them
-    assert f(FAKE, 32768, 0, FAKE, FAKE, lay, 70000, 32, 32768, 128, FAKE, FAKE, ws, None) == EUNSUP
+    assert f(FAKE, 32768, 0, FAKE, FAKE, None, None, lay, 70000, 32, 32768, 128, FAKE, FAKE, ws, None) == EUNSUP
 
 
 def test_swiglu_mlp_checks(L):
@@ -127,7 +130,9 @@ def test_gemm_hook_checks(L):
     assert L.ck_int8_gemm_i32(FAKE, FAKE, 1, 4, 32, 100, FAKE, None) == ESHAPE
     assert L.ck_int8_gemm_i32(None, FAKE, 0, 4, 32, 256, FAKE, None) == EINVAL
     assert L.ck_int8_gemm_i32(FAKE, FAKE, 3, 4, 32, 256, FAKE, None) == EINVAL
-    assert L.ck_int8_gemm_bf16(FAKE, None, FAKE, FAKE, 1, 4, 32, 256, FAKE, None) == EINVAL
+    assert L.ck_int8_gemm_bf16(FAKE, None, FAKE, FAKE, None, None, 1, 4, 32, 256, FAKE, None) == EINVAL
+    assert L.ck_int8_gemm_bf16(FAKE, FAKE, FAKE, FAKE, FAKE + 8, None, 1, 4, 32, 256, FAKE, None) == EINVAL
+    assert L.ck_int8_gemm_bf16(FAKE, FAKE, FAKE, FAKE, None, FAKE + 4, 1, 4, 32, 256, FAKE, None) == EINVAL
     assert L.ck_silu_f32(FAKE, -1, FAKE, None) == ESHAPE
     assert L.ck_act_rotate_f32(FAKE, 256, 4, 256, 0, 100, FAKE, None) == EUNSUP
 

@@ -361,6 +361,40 @@ def test_small_m_gemm_bit_exact(orc, m, n, k):
     np.testing.assert_array_equal(y, orc.dequant(acc_o, sx, sw))
 
 
+EXTRA_CASES = [  # (m, k, n, layout): few-row, 128-wide, 256x256 and 256x192 blocked tiles,
+    # ragged m and n, and both row-major kernels
+    (5, 256, 48, "blocked"), (64, 512, 1040, "blocked"), (300, 1024, 272, "blocked"),
+    (2000, 256, 8192, "blocked"), (2000, 256, 6144, "blocked"),
+    (300, 1024, 272, "rows"), (2000, 256, 8192, "rows"),
+]
+
+
+@pytest.mark.parametrize("m,k,n,layout", EXTRA_CASES)
+def test_int8_linear_bias_residual_bit_exact(orc, m, k, n, layout):
+    say(f"int8_linear bias/residual m={m} k={k} n={n} layout={layout}")
+    g = 128
+    d = W.case(m, k, n, 0, seed=2000 + m)
+    rng = np.random.default_rng(m + n)
+    bias = rng.standard_normal(n).astype(np.float32)
+    res = orc.f32_to_bf16(rng.standard_normal((m, n)).astype(np.float32))
+    wq_o, sw_o = orc.weight_prep(d["w"], g)
+    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    if layout == "blocked":
+        wq = ck.ck_weight_pack(wq)
+    x = bf16_dev(d["x"])
+    for b, r in ((bias, None), (None, res), (bias, res)):
+        y = ck.ck_int8_linear(x, wq, sw, g, layout=layout,
+                              bias=None if b is None else dev(b),
+                              residual=None if r is None else bf16_dev(r))
+        want = orc.int8_linear(d["x"], 0, wq_o, sw_o, g, bias=b, residual=r)
+        np.testing.assert_array_equal(bf16_host(y), want)
+    # the residual may be the output buffer itself
+    y = bf16_dev(res)
+    ck.ck_int8_linear(x, wq, sw, g, layout=layout, out=y, bias=dev(bias), residual=y)
+    np.testing.assert_array_equal(bf16_host(y),
+                                  orc.int8_linear(d["x"], 0, wq_o, sw_o, g, bias=bias, residual=res))
+
+
 @pytest.mark.parametrize("m,k,n,act,g", LINEAR_CASES)
 def test_int8_linear_blocked_bit_exact(orc, m, k, n, act, g):
     say(f"int8_linear blocked m={m} k={k} n={n} act={act} g={g}")

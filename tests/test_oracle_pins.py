@@ -371,3 +371,57 @@ def test_fused_swiglu_not_worse_than_eager(orc):
     e_f, e_e = orc.rel_l2(fused, ref), orc.rel_l2(eager, ref)
     assert 0.003 < e_f < 0.03
     assert e_f <= e_e * 1.02, (e_f, e_e)
+
+
+# ---------------------------------------------------------------------------
+# Epilogue with bias and residual (comfy-kitchen PR #277 "Changes"; PR #248
+# commit list).  Reading: one FP32 sum, one BF16 rounding.
+# ---------------------------------------------------------------------------
+def _bf16_bits_of_exact(v):
+    """BF16 bits of float32 values that are exactly representable in BF16."""
+    b = np.asarray(v, dtype=np.float32).view(np.uint32)
+    assert np.all((b & 0xFFFF) == 0)
+    return (b >> 16).astype(np.uint16)
+
+
+def test_epilogue_closed_form_zero_accumulator(orc):
+    # acc = 0: y = bf16(fl(0 + b) + r); integers below 256 are exact in BF16,
+    # so the result is the exact integer sum
+    rng = np.random.default_rng(5)
+    m, n = 7, 32
+    acc = np.zeros((m, n), dtype=np.int32)
+    b = rng.integers(-100, 100, n).astype(np.float32)
+    r = rng.integers(-100, 100, (m, n)).astype(np.float32)
+    y = orc.epilogue(acc, np.ones(m, np.float32), np.ones(n, np.float32), b,
+                     _bf16_bits_of_exact(r))
+    np.testing.assert_array_equal(y, _bf16_bits_of_exact(r + b[None, :]))
+    # residual alone passes through bit for bit
+    y = orc.epilogue(acc, np.ones(m, np.float32), np.ones(n, np.float32), None,
+                     _bf16_bits_of_exact(r))
+    np.testing.assert_array_equal(y, _bf16_bits_of_exact(r))
+
+
+def test_epilogue_without_extras_is_the_dequant(orc):
+    rng = np.random.default_rng(6)
+    acc = rng.integers(-2**24, 2**24, (9, 48)).astype(np.int32)
+    sx = rng.random(9).astype(np.float32)
+    sw = rng.random(48).astype(np.float32)
+    np.testing.assert_array_equal(orc.epilogue(acc, sx, sw), orc.dequant(acc, sx, sw))
+
+
+def test_epilogue_error_bound_vs_float64(orc):
+    rng = np.random.default_rng(7)
+    m, n = 33, 64
+    acc = rng.integers(-2**20, 2**20, (m, n)).astype(np.int32)
+    sx = (rng.random(m) * 1e-3).astype(np.float32)
+    sw = (rng.random(n) * 1e-3).astype(np.float32)
+    b = rng.standard_normal(n).astype(np.float32)
+    r = orc.f32_to_bf16(rng.standard_normal((m, n)).astype(np.float32))
+    y = orc.bf16_to_f32(orc.epilogue(acc, sx, sw, b, r)).astype(np.float64)
+    t1 = acc.astype(np.float64) * sx[:, None] * sw[None, :]
+    ref = t1 + b[None, :] + orc.bf16_to_f32(r).astype(np.float64)
+    # four FP32 roundings (each <= 2^-24 of its operand magnitudes) then one
+    # BF16 rounding (half a BF16 ulp: <= 2^-8 of the result)
+    bound = 2.0 ** -8 * np.abs(ref) + 4 * 2.0 ** -24 * (np.abs(t1) + np.abs(b)[None, :] +
+                                                       np.abs(ref)) + 1e-30
+    assert np.all(np.abs(y - ref) <= bound)

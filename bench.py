@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bias-residual", action="store_true",
+                    help="GEMM epilogues add an F32 bias and (down / single GEMM) a BF16 residual")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of the workload the CPU oracle runs (0: automatic)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -181,22 +183,31 @@ def main():
         hq = torch.empty((mp, inter), dtype=torch.int8, device=dev)
         sh = torch.empty((m,), dtype=torch.float32, device=dev)
         y = torch.empty((m, h), dtype=torch.bfloat16, device=dev)
+        # optional epilogue terms: biases on both GEMMs, the block input as the
+        # down projection's residual (a transformer block's skip connection)
+        ex = args.bias_residual
+        b_gu = torch.randn(2 * inter, device=dev) * 0.1 if ex else None
+        b_d = torch.randn(h, device=dev) * 0.1 if ex else None
+        gu_extra = (b_gu.data_ptr() if ex else None, None)
+        d_extra = (b_d.data_ptr() if ex else None, x.data_ptr() if ex else None)
+        xb = (2 * inter * 4) if ex else 0
+        db = (h * 4 + m * h * 2) if ex else 0
         # (name, callable, algorithmic ops, algorithmic HBM bytes, bound)
         stages = [
             ("x_quant", lambda s: L.ck_act_quant(x.data_ptr(), h, m, h, 0, g, BLK, xq.data_ptr(),
                                                  sx.data_ptr(), s),
              0, m * h * 2 + m * h + m * 4, "hbm"),
             ("gate_up_gemm", lambda s: L.ck_int8_gemm_bf16(xq.data_ptr(), sx.data_ptr(),
-                                                           wgu.data_ptr(), sgu.data_ptr(), None, None, BLK,
+                                                           wgu.data_ptr(), sgu.data_ptr(), *gu_extra, BLK,
                                                            m, 2 * inter, h, t1.data_ptr(), s),
-             2 * m * 2 * inter * h, m * h + 2 * inter * h + m * 2 * inter * 2, "mfma"),
+             2 * m * 2 * inter * h, m * h + 2 * inter * h + m * 2 * inter * 2 + xb, "mfma"),
             ("swiglu_quant", lambda s: L.ck_act_quant(t1.data_ptr(), 2 * inter, m, inter, 1, g,
                                                       BLK, hq.data_ptr(), sh.data_ptr(), s),
              0, m * inter * 4 + m * inter + m * 4, "hbm"),
             ("down_gemm", lambda s: L.ck_int8_gemm_bf16(hq.data_ptr(), sh.data_ptr(),
-                                                        wd.data_ptr(), sd.data_ptr(), None, None, BLK,
+                                                        wd.data_ptr(), sd.data_ptr(), *d_extra, BLK,
                                                         m, h, inter, y.data_ptr(), s),
-             2 * m * h * inter, m * inter + h * inter + m * h * 2, "mfma"),
+             2 * m * h * inter, m * inter + h * inter + m * h * 2 + db, "mfma"),
         ]
     else:
         d = W.linear_inputs(wl)
@@ -208,13 +219,18 @@ def main():
         xq = torch.empty((ck.blocked_rows(m), k), dtype=torch.int8, device=dev)
         sx = torch.empty((m,), dtype=torch.float32, device=dev)
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        ex = args.bias_residual
+        bias = torch.randn(n, device=dev) * 0.1 if ex else None
+        res = (torch.randn((m, n), device=dev) * 0.5).to(torch.bfloat16) if ex else None
+        extra = (bias.data_ptr() if ex else None, res.data_ptr() if ex else None)
+        eb = (n * 4 + m * n * 2) if ex else 0
         stages = [
             ("act_quant", lambda s: L.ck_act_quant(x.data_ptr(), ldx, m, k, wl.act, g, BLK,
                                                    xq.data_ptr(), sx.data_ptr(), s),
              0, m * ldx * 2 + m * k + m * 4, "hbm"),
             ("gemm", lambda s: L.ck_int8_gemm_bf16(xq.data_ptr(), sx.data_ptr(), wq.data_ptr(),
-                                                   sw.data_ptr(), None, None, BLK, m, n, k, y.data_ptr(), s),
-             2 * m * n * k, m * k + n * k + m * n * 2, "mfma"),
+                                                   sw.data_ptr(), *extra, BLK, m, n, k, y.data_ptr(), s),
+             2 * m * n * k, m * k + n * k + m * n * 2 + eb, "mfma"),
         ]
     torch.cuda.synchronize()
 
@@ -311,7 +327,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.desc}", "m": wl.m, "k": wl.k, "n": wl.n,
-                   "group": g, "int8_ops_per_step": wl.int8_ops, "parallelism": "single-gpu"},
+                   "group": g, "int8_ops_per_step": wl.int8_ops, "parallelism": "single-gpu",
+                   "epilogue": "bias+residual" if args.bias_residual else "dequant"},
         "frac_of_int8_peak": round(value / PEAK_INT8_TOPS, 4),
         "roofline": roofline, "stages": stage_roofline, "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),

@@ -85,7 +85,6 @@ struct Cfg {
     static constexpr int BLK = A_BLK + B_BLK;
     static constexpr int L = BLK / 4;              // block loads per lane per stage
     static constexpr int STAGE = BLK * 1024;
-    static constexpr int SCALES = 2048;             // one tile's sx and sw in LDS
     static_assert(BLK % 4 == 0, "blocks must split evenly over 4 waves");
 };
 
@@ -138,7 +137,9 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     using C = Cfg<BM, BN>;
     // LDS: the 4-slot operand ring, then two scale buffers (tile q uses
     // buffer q % 2), each 1 KB of row scales sx then 1 KB of column scales sw.
-    __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE + 2 * C::SCALES];
+    // one tile's sx and sw (and, with EXTRA, its bias) in LDS, 1 KB each
+    constexpr int SCALES = EXTRA ? 3072 : 2048;
+    __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE + 2 * SCALES];
     constexpr int AW = C::A_BLK / 4;   // W blocks each wave loads per stage
     constexpr int XW = C::B_BLK / 4;   // X blocks each wave loads per stage
     constexpr int NMF = C::FN * C::FM; // MFMAs per wave per k-slice
@@ -180,6 +181,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     // scale vectors (absent, so every lane out of range, for the int32 variant)
     const v4i rs_sx = make_rsrc(sx, OUT_I32 ? 0u : (uint32_t)M * 4u);
     const v4i rs_sw = make_rsrc(sw, OUT_I32 ? 0u : (uint32_t)N * 4u);
+    const v4i rs_b = make_rsrc(ex.bias, (EXTRA && ex.bias) ? (uint32_t)N * 4u : 0u);
     const __amdgpu_buffer_rsrc_t rs_o =
         __builtin_amdgcn_make_buffer_rsrc(out, (short)0, M * N * (OUT_I32 ? 4 : 2), 0x00020000);
     const uint32_t smem_addr = (uint32_t)(uintptr_t)(lds_void_t*)smem;
@@ -275,10 +277,22 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
         v4i ga[C::FN], gb[C::FM];
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (decltype(first)::value) {
-            const bool odd = wave & 1;
-            const uint32_t sdst = smem_addr + (uint32_t)(C::NBUF * C::STAGE + (q & 1) * C::SCALES) +
-                                  (odd ? 1024u : 0u);
-            lds_dma_b128(odd ? rs_sw : rs_sx, lane16, (uint32_t)((odd ? tn * BN : tm * BM) * 4), sdst);
+            const uint32_t sbase = smem_addr + (uint32_t)(C::NBUF * C::STAGE + (q & 1) * SCALES);
+            if constexpr (!EXTRA) {
+                const bool odd = wave & 1;
+                lds_dma_b128(odd ? rs_sw : rs_sx, lane16, (uint32_t)((odd ? tn * BN : tm * BM) * 4),
+                             sbase + (odd ? 1024u : 0u));
+            } else {
+                // wave 0: sx, waves 1 and 3: sw, wave 2: the bias (zeros when absent)
+                // (uniform branches: selecting among three resources made the
+                // compiler keep the accumulators in scratch)
+                if (wave == 0)
+                    lds_dma_b128(rs_sx, lane16, (uint32_t)(tm * BM * 4), sbase);
+                else if (wave == 2)
+                    lds_dma_b128(rs_b, lane16, (uint32_t)(tn * BN * 4), sbase + 2048u);
+                else
+                    lds_dma_b128(rs_sw, lane16, (uint32_t)(tn * BN * 4), sbase + 1024u);
+            }
         }
 #pragma unroll
         for (int k = 0; k < STEPS0; ++k) {
@@ -321,7 +335,31 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
         // issues the same number of stores.
         const int m_base = tm * BM + wm0 + lr;
         const int n_base = tn * BN + wn0 + 4 * lh;
-        const char* sc = smem + C::NBUF * C::STAGE + (q & 1) * C::SCALES;
+        const char* sc = smem + C::NBUF * C::STAGE + (q & 1) * SCALES;
+        // EXTRA: all of this lane's residual words, loaded together up front
+        uint2 rall[EXTRA ? C::FN : 1][EXTRA ? C::FM : 1][4];
+        const bool has_b = EXTRA && ex.bias != nullptr;
+        const bool has_r = EXTRA && ex.res != nullptr;
+        if constexpr (EXTRA) {
+#pragma unroll
+            for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd) rall[i][j][qd] = make_uint2(0u, 0u);
+            if (has_r) {
+#pragma unroll
+                for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+                        for (int qd = 0; qd < 4; ++qd) {
+                            const int mm = min(m_base + 32 * j, M - 1);
+                            const int nn = min(n_base + 32 * i + 8 * qd, N - 4);
+                            rall[i][j][qd] = *reinterpret_cast<const uint2*>(ex.res + (int64_t)mm * N + nn);
+                        }
+            }
+        }
         float sxm[C::FM];
 #pragma unroll
         for (int j = 0; j < C::FM; ++j) {
@@ -330,9 +368,11 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
         }
 #pragma unroll
         for (int i = 0; i < C::FN; ++i) {
-            float4 s4[4];
+            float4 s4[4], b4[4];
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
+                if constexpr (EXTRA)
+                    b4[qd] = *reinterpret_cast<const float4*>(sc + 2048 + (wn0 + 4 * lh + 32 * i + 8 * qd) * 4);
                 s4[qd] = make_float4(0.f, 0.f, 0.f, 0.f);
                 if constexpr (!OUT_I32)
                     s4[qd] = *reinterpret_cast<const float4*>(sc + 1024 + (wn0 + 4 * lh + 32 * i + 8 * qd) * 4);
@@ -362,9 +402,19 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
                         float y1 = ((float)f[4 * qd + 1] * sxm[j]) * s4[qd].y;
                         float y2 = ((float)f[4 * qd + 2] * sxm[j]) * s4[qd].z;
                         float y3 = ((float)f[4 * qd + 3] * sxm[j]) * s4[qd].w;
-                        if constexpr (EXTRA)   // loads straight from global memory
-                            epi_extra4(y0, y1, y2, y3, ex, min(m_base + 32 * j, M - 1),
-                                       min(n_base + 32 * i + 8 * qd, N - 4), N);
+                        if constexpr (EXTRA) {
+                            // selects, not branches (an absent term must not
+                            // turn -0 into +0)
+                            y0 = has_b ? y0 + b4[qd].x : y0;
+                            y1 = has_b ? y1 + b4[qd].y : y1;
+                            y2 = has_b ? y2 + b4[qd].z : y2;
+                            y3 = has_b ? y3 + b4[qd].w : y3;
+                            const uint2 r = rall[i][j][qd];
+                            y0 = has_r ? y0 + bf16_lo(r.x) : y0;
+                            y1 = has_r ? y1 + bf16_hi(r.x) : y1;
+                            y2 = has_r ? y2 + bf16_lo(r.y) : y2;
+                            y3 = has_r ? y3 + bf16_hi(r.y) : y3;
+                        }
                         w[qd][0] = pack_bf16x2(y0, y1);
                         w[qd][1] = pack_bf16x2(y2, y3);
                     }
@@ -415,7 +465,7 @@ hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const flo
     const int tiles = tiles_m * tiles_n;
     // LDS per workgroup: 4 stages of (BM + BN) x 64 bytes and two 2 KB scale
     // buffers; 160 KB per CU.
-    const int lds = 4 * (BM + BN) * 64 + 4096;
+    const int lds = 4 * (BM + BN) * 64 + (EXTRA ? 6144 : 4096);
     const int per_cu = (160 * 1024) / lds >= 2 ? 2 : 1;
     const int slots = num_cu * per_cu;
     const int grid = tiles < slots ? tiles : slots;

@@ -460,3 +460,23 @@ def test_blocked_stages_equal_swiglu_mlp():
     torch.cuda.synchronize()
     assert torch.equal(y_blk.view(torch.int16), y_rows.view(torch.int16))
     assert torch.equal(y_blk.view(torch.int16), y_st.view(torch.int16))
+
+
+@pytest.mark.parametrize("g,layout,scalar", [(256, "blocked", False), (128, "rows", False),
+                                             (256, "blocked", True)])
+def test_serialized_layer_bit_exact(orc, g, layout, scalar):
+    """Pre-quantized I8 weights + F32 [out, 1] scales, as a serialized
+    checkpoint holds them (sglang PR #35994 report), used without re-quantizing."""
+    from swiglu_mlp_amd import checkpoint as C
+    say(f"serialized layer g={g} layout={layout} scalar_scale={scalar}")
+    m, k, n = 200, 1024, 528
+    d = W.case(m, k, n, 0, seed=77)
+    wq_o, sw_o = orc.weight_prep(d["w"], g)          # what a serialized file holds
+    if scalar:
+        sw_o = np.full_like(sw_o, sw_o.max())
+        scale = torch.tensor(float(sw_o[0]), dtype=torch.float32)
+    else:
+        scale = dev(sw_o.reshape(n, 1))
+    wq, sw = C.serialized_linear_weights(dev(wq_o), scale, group=g, layout=layout)
+    y = bf16_host(ck.ck_int8_linear(bf16_dev(d["x"]), wq, sw, g, layout=layout))
+    np.testing.assert_array_equal(y, orc.int8_linear(d["x"], 0, wq_o, sw_o, g))

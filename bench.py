@@ -58,9 +58,11 @@ def parse():
 
 
 def small_m_sweep(steps: int, warmup: int):
-    """The few-row path: ck_int8_gemm_bf16 with blocked operands at M in {1, 8, 16, 32, 64}
-    for (N, K) = (4096, 4096) and (4096, 12288).  Bound by HBM: the algorithmic bytes are
-    the weight N*K, the codes M*K, both scale vectors and the BF16 output 2*M*N."""
+    """The few-row path: ck_int8_gemm_bf16 at M in {1, 8, 16, 32, 64} for (N, K) =
+    (4096, 4096) and (4096, 12288), with the weight in the blocked layout (scales
+    apart) and in the decode layout (scales inside each 16-row group).  Bound by
+    HBM: the algorithmic bytes are the weight N*K, the codes M*K, both scale
+    vectors and the BF16 output 2*M*N."""
     import torch
     import swiglu_mlp_amd as ck
     dev = torch.device("cuda:0")
@@ -71,50 +73,53 @@ def small_m_sweep(steps: int, warmup: int):
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     for n, k in ((4096, 4096), (4096, 12288)):
         w = torch.randint(-127, 128, (n, k), dtype=torch.int8, device=dev, generator=gen)
-        wb = ck.ck_weight_pack(w)
         sw = torch.rand(n, device=dev, generator=gen) * 1e-3
+        weights = {"blocked": (ck.ck_weight_pack(w), sw, ck.CK_LAYOUT_BLOCKED),
+                   "decode": (ck.ck_weight_pack_decode(w, sw), None, ck.CK_LAYOUT_DECODE)}
         for m in (1, 8, 16, 32, 64):
             xq = torch.randint(-127, 128, (ck.blocked_rows(m), k), dtype=torch.int8, device=dev,
                                generator=gen)
             sx = torch.rand(m, device=dev, generator=gen) * 1e-3
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-
-            def call():
-                rc = L.ck_int8_gemm_bf16(xq.data_ptr(), sx.data_ptr(), wb.data_ptr(), sw.data_ptr(),
-                                         None, None, ck.CK_LAYOUT_BLOCKED, m, n, k, y.data_ptr(),
-                                         stream.cuda_stream)
-                if rc:
-                    raise RuntimeError(L.ck_status_str(rc).decode())
-            for _ in range(warmup):
-                call()
-            torch.cuda.synchronize()
-            # back to back: the weights may stay in the 256 MB MALL between calls
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(steps):
-                call()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us_warm = e0.elapsed_time(e1) * 1000.0 / steps
-            # flushed: a 512 MB write between calls evicts the MALL, each call
-            # timed alone (the headline: weights come from HBM)
-            reps = max(5, steps // 5)
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(reps)]
-            for a, b in evs:
-                flush.zero_()
-                a.record(stream)
-                call()
-                b.record(stream)
-            torch.cuda.synchronize()
-            us = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2] * 1000.0
-            nbytes = n * k + m * k + 4 * (m + n) + 2 * m * n
-            print(json.dumps({"small_m": {"m": m, "n": n, "k": k, "us": round(us, 2),
-                                          "GBs": round(nbytes / us / 1e3, 1),
-                                          "frac_hbm_peak": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
-                                          "TOPS": round(2 * m * n * k / us / 1e6, 2),
-                                          "us_back_to_back": round(us_warm, 2),
-                                          "timing": "median of flushed single calls"}}), flush=True)
+            for lay_name, (wt, swt, lay) in weights.items():
+                def call():
+                    rc = L.ck_int8_gemm_bf16(xq.data_ptr(), sx.data_ptr(), wt.data_ptr(),
+                                             None if swt is None else swt.data_ptr(), None, None,
+                                             lay, m, n, k, y.data_ptr(), stream.cuda_stream)
+                    if rc:
+                        raise RuntimeError(L.ck_status_str(rc).decode())
+                for _ in range(warmup):
+                    call()
+                torch.cuda.synchronize()
+                # back to back: the weights may stay in the 256 MB MALL between calls
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(steps):
+                    call()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us_warm = e0.elapsed_time(e1) * 1000.0 / steps
+                # flushed: a 512 MB write between calls evicts the MALL, each call
+                # timed alone (the headline: weights come from HBM)
+                reps = max(5, steps // 5)
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(reps)]
+                for a, b in evs:
+                    flush.zero_()
+                    a.record(stream)
+                    call()
+                    b.record(stream)
+                torch.cuda.synchronize()
+                us = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2] * 1000.0
+                nbytes = n * k + m * k + 4 * (m + n) + 2 * m * n
+                print(json.dumps({"small_m": {"layout": lay_name, "m": m, "n": n, "k": k,
+                                              "us": round(us, 2),
+                                              "GBs": round(nbytes / us / 1e3, 1),
+                                              "frac_hbm_peak": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
+                                              "TOPS": round(2 * m * n * k / us / 1e6, 2),
+                                              "us_back_to_back": round(us_warm, 2),
+                                              "timing": "median of flushed single calls"}}),
+                      flush=True)
 
 
 def copy_calibration():

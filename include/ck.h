@@ -89,7 +89,8 @@ typedef enum ck_act {
 
 typedef enum ck_layout {
     CK_LAYOUT_ROWS = 0,    /* row-major int8 [R, K]                             */
-    CK_LAYOUT_BLOCKED = 1  /* 1 KB fragment blocks, rows padded to 256          */
+    CK_LAYOUT_BLOCKED = 1, /* 1 KB fragment blocks, rows padded to 256          */
+    CK_LAYOUT_DECODE = 2   /* weights only, m <= 64: rows and scales interleaved */
 } ck_layout;
 
 /* Largest in_features: 127 * 127 * k must fit an int32 accumulator and one
@@ -122,6 +123,26 @@ ck_status ck_weight_prep(const float *w, int64_t n, int64_t k, int32_t group,
  * layout (0 for rows <= 0 or k <= 0). */
 int64_t ck_blocked_rows(int64_t rows);
 size_t ck_blocked_size(int64_t rows, int64_t k);
+
+/* Decode layout (CK_LAYOUT_DECODE) of a weight [n, k] with its row scales,
+ * for calls with m <= 64 (token-at-a-time decoding).  Source: comfy-kitchen
+ * PR #248 "Performance improvements for qwen 3.x (Part 2)", "Description": at
+ * small M the layer streams its weights, and interleaving the weights with
+ * their scales makes that stream linear.  Each group of 16 rows b is one
+ * contiguous region of 64 + 16 k bytes at byte b * (64 + 16 k): the 16 FP32
+ * row scales of rows 16 b .. 16 b + 15, then k / 64 chunks of 1 KB, chunk c
+ * holding W[16 b + r][64 c + 16 q + e] at byte 64 + 1024 c + 256 q + 16 r + e
+ * (q < 4, r < 16, e < 16): one 16 x 64-byte MFMA operand in lane order.
+ * A call with w_q in this layout ignores w_scale (it may be NULL); its
+ * activation codes use the blocked layout.  m > 64 returns CK_EUNSUPPORTED.
+ * ck_decode_size: bytes of the layout (0 for n <= 0 or k <= 0). */
+size_t ck_decode_size(int64_t n, int64_t k);
+
+/* Row-major codes and scales -> decode layout (done once, at load).
+ *   w_q [n, k] int8 and w_scale [n] FP32 (from ck_weight_prep), read
+ *   w_dec  ck_decode_size(n, k) bytes, written */
+ck_status ck_weight_pack_decode(const int8_t *w_q, const float *w_scale, int64_t n,
+                                int64_t k, void *w_dec, void *stream);
 
 /* One-time relayout of prepared weights into the blocked layout.
  * Source: comfy-kitchen PR #248 "Performance improvements for qwen 3.x

@@ -10,15 +10,20 @@ Entry points keep the C names:
 
 * ``ck_weight_prep(w, group)``           -> (w_q int8 [n, k], w_scale f32 [n, 1])
 * ``ck_weight_pack(w_q)``                 -> w_q in the blocked layout [n_pad, k]
+* ``ck_weight_pack_decode(w_q, w_scale)`` -> codes and scales in the decode layout
 * ``ck_act_quant(x, act, group, k=None, layout=...)`` -> (x_q, x_scale f32 [m, 1])
 * ``ck_int8_linear(x, w_q, w_scale, group, input_act=None, layout=..., bias=None, residual=None)``
 * ``ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, layout=..., bias=None, residual=None)``
 * ``ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group, layout=...)`` -> y bf16
 * test hooks ``ck_int8_gemm_i32``, ``ck_silu_f32``, ``ck_act_rotate_f32``
 
-``layout`` is ``"rows"`` (row-major int8, the serialized checkpoint format) or
-``"blocked"`` (the GEMM-native layout of include/ck.h, rows padded to 256).
-With blocked operands the logical row counts come from the scale vectors.
+``layout`` is ``"rows"`` (row-major int8, the serialized checkpoint format),
+``"blocked"`` (the GEMM-native layout of include/ck.h, rows padded to 256) or
+``"decode"`` (weights only, at most 64 token rows: each 16-row group of the
+weight one linear stream with its row scales in front; activation codes are
+then blocked).  With blocked operands the logical row counts come from the
+scale vectors; a decode weight is a uint8 [n / 16, 64 + 16 k] tensor that
+carries its scales, and its ``w_scale`` argument may be None.
 
 Shapes and error behaviour follow sglang PR #35994 report, key source excerpts:
 an INT8 weight is 2-D ``[out_features, in_features]`` with an F32
@@ -34,7 +39,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libck_convrot.so")
 
 CK_ACT_NONE, CK_ACT_SWIGLU = 0, 1
-CK_LAYOUT_ROWS, CK_LAYOUT_BLOCKED = 0, 1
+CK_LAYOUT_ROWS, CK_LAYOUT_BLOCKED, CK_LAYOUT_DECODE = 0, 1, 2
 _STATUS = {0: "CK_OK", 1: "CK_EINVAL", 2: "CK_ESHAPE", 3: "CK_EUNSUPPORTED",
            4: "CK_EWORKSPACE", 5: "CK_EHIP"}
 
@@ -69,6 +74,7 @@ def bind(path: str) -> ctypes.CDLL:
     sig = {
         "ck_weight_prep": [p, i64, i64, i32, p, p, p],
         "ck_weight_pack": [p, i64, i64, p, p],
+        "ck_weight_pack_decode": [p, p, i64, i64, p, p],
         "ck_act_quant": [p, i64, i64, i64, i32, i32, i32, p, p, p],
         "ck_int8_linear": [p, i64, i32, p, p, p, p, i32, i64, i64, i64, i32, p, p, sz, p],
         "ck_int8_gemm_bf16": [p, p, p, p, p, p, i32, i64, i64, i64, p, p],
@@ -89,6 +95,8 @@ def bind(path: str) -> ctypes.CDLL:
     L.ck_blocked_rows.restype = i64
     L.ck_blocked_size.argtypes = [i64, i64]
     L.ck_blocked_size.restype = sz
+    L.ck_decode_size.argtypes = [i64, i64]
+    L.ck_decode_size.restype = sz
     L.ck_status_str.argtypes = [ctypes.c_int]
     L.ck_status_str.restype = ctypes.c_char_p
     L.ck_version.argtypes = []
@@ -145,11 +153,49 @@ def _layout_code(layout):
         return CK_LAYOUT_ROWS
     if layout in ("blocked", CK_LAYOUT_BLOCKED):
         return CK_LAYOUT_BLOCKED
+    if layout in ("decode", CK_LAYOUT_DECODE):
+        return CK_LAYOUT_DECODE
     raise ValueError(f"unknown layout {layout!r}")
 
 
 def blocked_rows(rows: int) -> int:
     return int(lib().ck_blocked_rows(rows))
+
+
+def _decode_shape(w, what):
+    """(n, k) of a weight in the decode layout: uint8 [n / 16, 64 + 16 k]."""
+    import torch
+    _need(w, torch.uint8, 2, what)
+    if (w.shape[1] - 64) % 1024 or w.shape[1] <= 64:
+        raise ValueError(f"{what}: a decode-layout weight has 64 + 16 k columns with k % 64 == 0, "
+                         f"got {w.shape[1]}")
+    return 16 * w.shape[0], (w.shape[1] - 64) // 16
+
+
+def _weight(w, w_scale, lay, what):
+    """(n, k) of a weight operand in layout `lay`, with its scale checked."""
+    import torch
+    if lay == CK_LAYOUT_DECODE:
+        n, k = _decode_shape(w, what)
+        if w_scale is not None:
+            raise ValueError(f"{what}: the decode layout carries its scales; pass w_scale=None")
+        return n, k
+    _need(w, torch.int8, 2, what)
+    if w_scale is None:
+        raise ValueError(f"{what}: weight scale missing")
+    n = w_scale.shape[0]
+    _operand_rows(w, n, lay, what)
+    _scale(w_scale, n, what + " scale")
+    return n, w.shape[1]
+
+
+def _act_layout(lay):
+    """Layout of the activation codes that go with a weight in layout `lay`."""
+    return CK_LAYOUT_ROWS if lay == CK_LAYOUT_ROWS else CK_LAYOUT_BLOCKED
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
 
 
 def _operand_rows(t, rows, layout, what):
@@ -194,6 +240,22 @@ def ck_weight_pack(w_q):
     return out
 
 
+def ck_weight_pack_decode(w_q, w_scale):
+    """Row-major int8 codes [n, k] and FP32 row scales [n] (or [n, 1]) ->
+    the decode layout, a uint8 tensor [n / 16, 64 + 16 k]."""
+    import torch
+    _need(w_q, torch.int8, 2, "weight")
+    n, k = w_q.shape
+    _scale(w_scale, n, "weight_scale")
+    if n % 16:
+        raise ValueError(f"the decode layout needs out_features % 16 == 0, got {n}")
+    out = torch.empty((n // 16, 64 + 16 * k), dtype=torch.uint8, device=w_q.device)
+    assert out.numel() == lib().ck_decode_size(n, k)
+    _call("ck_weight_pack_decode", w_q.data_ptr(), w_scale.data_ptr(), n, k, out.data_ptr(),
+          _stream(w_q))
+    return out
+
+
 def ck_act_quant(x, input_act=None, group: int = 128, k: int | None = None, layout="rows"):
     import torch
     _need(x, torch.bfloat16, 2, "activation")
@@ -232,12 +294,8 @@ def ck_int8_linear(x, w_q, w_scale, group: int = 128, input_act=None, out=None,
                    workspace=None, layout="rows", bias=None, residual=None):
     import torch
     _need(x, torch.bfloat16, 2, "activation")
-    _need(w_q, torch.int8, 2, "weight")
     lay = _layout_code(layout)
-    k = w_q.shape[1]
-    n = w_scale.shape[0]
-    _operand_rows(w_q, n, lay, "weight")
-    _scale(w_scale, n, "weight_scale")
+    n, k = _weight(w_q, w_scale, lay, "weight")
     act = _act_code(input_act)
     m, ldx = x.shape
     need_ld = 2 * k if act == CK_ACT_SWIGLU else k
@@ -249,7 +307,7 @@ def ck_int8_linear(x, w_q, w_scale, group: int = 128, input_act=None, out=None,
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     bp, rp = _extra(bias, residual, m, n, x.device)
-    _call("ck_int8_linear", x.data_ptr(), ldx, act, w_q.data_ptr(), w_scale.data_ptr(), bp, rp,
+    _call("ck_int8_linear", x.data_ptr(), ldx, act, w_q.data_ptr(), _ptr(w_scale), bp, rp,
           lay, m, n, k, group, y.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x))
     return y
 
@@ -258,20 +316,18 @@ def ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, out=None, layout="rows", bias=
                       residual=None):
     import torch
     _need(x_q, torch.int8, 2, "activation codes")
-    _need(w_q, torch.int8, 2, "weight")
     lay = _layout_code(layout)
     k = x_q.shape[1]
-    m, n = x_scale.shape[0], w_scale.shape[0]
-    if w_q.shape[1] != k:
-        raise ValueError(f"in_features mismatch: activation {k}, weight {w_q.shape[1]}")
-    _operand_rows(x_q, m, lay, "activation codes")
-    _operand_rows(w_q, n, lay, "weight")
+    m = x_scale.shape[0]
+    n, kw = _weight(w_q, w_scale, lay, "weight")
+    if kw != k:
+        raise ValueError(f"in_features mismatch: activation {k}, weight {kw}")
+    _operand_rows(x_q, m, _act_layout(lay), "activation codes")
     _scale(x_scale, m, "activation scale")
-    _scale(w_scale, n, "weight_scale")
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x_q.device)
     bp, rp = _extra(bias, residual, m, n, x_q.device)
     _call("ck_int8_gemm_bf16", x_q.data_ptr(), x_scale.data_ptr(), w_q.data_ptr(),
-          w_scale.data_ptr(), bp, rp, lay, m, n, k, y.data_ptr(), _stream(x_q))
+          _ptr(w_scale), bp, rp, lay, m, n, k, y.data_ptr(), _stream(x_q))
     return y
 
 
@@ -279,28 +335,23 @@ def ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group: int = 128, out=None, wor
                   layout="rows"):
     import torch
     _need(x, torch.bfloat16, 2, "activation")
-    _need(w_gu, torch.int8, 2, "gate_up weight")
-    _need(w_down, torch.int8, 2, "down weight")
     lay = _layout_code(layout)
     m, h = x.shape
-    i2 = s_gu.shape[0]
-    if w_gu.shape[1] != h or i2 % 2:
-        raise ValueError(f"gate_up weight needs shape (2*intermediate, {h}), got {tuple(w_gu.shape)}")
+    i2, kg = _weight(w_gu, s_gu, lay, "gate_up weight")
+    if kg != h or i2 % 2:
+        raise ValueError(f"gate_up weight needs (2*intermediate, {h}), got ({i2}, {kg})")
     i = i2 // 2
-    _operand_rows(w_gu, i2, lay, "gate_up weight")
-    if w_down.shape[1] != i or s_down.shape[0] != h:
-        raise ValueError(f"down weight needs shape ({h}, {i}), got {tuple(w_down.shape)}")
-    _operand_rows(w_down, h, lay, "down weight")
-    _scale(s_gu, i2, "gate_up weight_scale")
-    _scale(s_down, h, "down weight_scale")
+    hd, kd = _weight(w_down, s_down, lay, "down weight")
+    if kd != i or hd != h:
+        raise ValueError(f"down weight needs ({h}, {i}), got ({hd}, {kd})")
     _check_group(h, group)
     _check_group(i, group)
     y = out if out is not None else torch.empty((m, h), dtype=torch.bfloat16, device=x.device)
     ws_bytes = lib().ck_swiglu_mlp_workspace_size(m, h, i)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
-    _call("ck_swiglu_mlp", x.data_ptr(), w_gu.data_ptr(), s_gu.data_ptr(), w_down.data_ptr(),
-          s_down.data_ptr(), lay, m, h, i, group, y.data_ptr(), workspace.data_ptr(),
+    _call("ck_swiglu_mlp", x.data_ptr(), w_gu.data_ptr(), _ptr(s_gu), w_down.data_ptr(),
+          _ptr(s_down), lay, m, h, i, group, y.data_ptr(), workspace.data_ptr(),
           workspace.numel(), _stream(x))
     return y
 
@@ -309,15 +360,19 @@ def ck_int8_gemm_i32(x_q, w_q, layout="rows", m: int | None = None, n: int | Non
     """Raw int32 accumulators; with blocked operands pass the logical m and n."""
     import torch
     _need(x_q, torch.int8, 2, "activation codes")
-    _need(w_q, torch.int8, 2, "weight")
     lay = _layout_code(layout)
     k = x_q.shape[1]
     m = x_q.shape[0] if m is None else m
-    n = w_q.shape[0] if n is None else n
-    if w_q.shape[1] != k:
-        raise ValueError(f"in_features mismatch: activation {k}, weight {w_q.shape[1]}")
-    _operand_rows(x_q, m, lay, "activation codes")
-    _operand_rows(w_q, n, lay, "weight")
+    if lay == CK_LAYOUT_DECODE:
+        n, kw = _decode_shape(w_q, "weight")
+    else:
+        _need(w_q, torch.int8, 2, "weight")
+        n = w_q.shape[0] if n is None else n
+        kw = w_q.shape[1]
+        _operand_rows(w_q, n, lay, "weight")
+    if kw != k:
+        raise ValueError(f"in_features mismatch: activation {k}, weight {kw}")
+    _operand_rows(x_q, m, _act_layout(lay), "activation codes")
     acc = torch.empty((m, n), dtype=torch.int32, device=x_q.device)
     _call("ck_int8_gemm_i32", x_q.data_ptr(), w_q.data_ptr(), lay, m, n, k, acc.data_ptr(),
           _stream(x_q))

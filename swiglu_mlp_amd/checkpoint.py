@@ -93,7 +93,9 @@ def serialized_linear_weights(weight, weight_scale, group: int = 128, layout: st
     """Device tensors of one serialized layer -> (w_q for `layout`, w_scale [n]).
 
     weight: int8 [out, in] (already rotated and quantized); weight_scale: F32
-    [out, 1], [out] or a single value (one scale for all rows)."""
+    [out, 1], [out] or a single value (one scale for all rows).  For
+    layout="decode" the scales go inside the packed weight and the second
+    result is None."""
     import torch
     import swiglu_mlp_amd as ck
     if not isinstance(weight, torch.Tensor) or weight.dtype != torch.int8 or weight.dim() != 2:
@@ -120,6 +122,8 @@ def serialized_linear_weights(weight, weight_scale, group: int = 128, layout: st
     w = weight.contiguous()
     if layout == "blocked":
         w = ck.ck_weight_pack(w)
+    elif layout == "decode":
+        return ck.ck_weight_pack_decode(w, s), None
     elif layout != "rows":
         raise ValueError(f"unknown layout {layout!r}")
     return w, s

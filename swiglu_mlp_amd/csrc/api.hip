@@ -36,17 +36,30 @@ ck_status from_hip(hipError_t e) { return e == hipSuccess ? CK_OK : CK_EHIP; }
 
 int64_t pad_rows(int64_t r) { return (r + 255) / 256 * 256; }
 
+// Layout of activation codes: row-major or blocked.
 ck_status check_layout(int32_t layout)
 {
     return (layout == CK_LAYOUT_ROWS || layout == CK_LAYOUT_BLOCKED) ? CK_OK : CK_EINVAL;
 }
+
+// Layout of a GEMM's weight (the activation codes are then row-major for
+// CK_LAYOUT_ROWS and blocked otherwise).  The decode layout serves m <= 64.
+ck_status check_weight_layout(int32_t layout, int64_t m)
+{
+    if (layout == CK_LAYOUT_ROWS || layout == CK_LAYOUT_BLOCKED) return CK_OK;
+    if (layout != CK_LAYOUT_DECODE) return CK_EINVAL;
+    return m <= 64 ? CK_OK : CK_EUNSUPPORTED;
+}
+
+// Bytes of the decode layout of [n, k] (n % 16 == 0).
+int64_t decode_bytes(int64_t n, int64_t k) { return (n / 16) * (64 + 16 * k); }
 
 // Every int8 operand and output of the GEMM kernels is addressed with 32-bit
 // byte offsets (buffer resources).
 ck_status check_gemm_extent(int64_t m, int64_t n, int64_t k)
 {
     if (pad_rows(m) * k > CK_MAX_ELEMS || pad_rows(n) * k > CK_MAX_ELEMS ||
-        pad_rows(m) * n * 4 > CK_MAX_ELEMS)
+        pad_rows(m) * n * 4 > CK_MAX_ELEMS || decode_bytes(n, k) > CK_MAX_ELEMS)
         return CK_EUNSUPPORTED;
     return CK_OK;
 }
@@ -69,7 +82,7 @@ const char* ck_status_str(ck_status s)
         case CK_OK: return "ok";
         case CK_EINVAL: return "invalid argument (null or misaligned pointer, unknown act)";
         case CK_ESHAPE: return "bad shape (negative size, k % group, k % 64, n % 16, leading dimension)";
-        case CK_EUNSUPPORTED: return "unsupported (group not a power of two <= 256, or k > CK_MAX_K)";
+        case CK_EUNSUPPORTED: return "unsupported (group not a power of two <= 256, k > CK_MAX_K, a buffer past 2^31 bytes, or the decode layout with m > 64)";
         case CK_EWORKSPACE: return "workspace missing or too small";
         case CK_EHIP: return "HIP runtime error at launch";
     }
@@ -106,6 +119,23 @@ ck_status ck_weight_pack(const int8_t* w_q, int64_t n, int64_t k, int8_t* w_blk,
     return from_hip(ck::launch_pack_blocked(w_q, n, k, w_blk, (hipStream_t)stream));
 }
 
+size_t ck_decode_size(int64_t n, int64_t k)
+{
+    if (n <= 0 || k <= 0) return 0;
+    return (size_t)((n + 15) / 16) * (size_t)(64 + 16 * k);
+}
+
+ck_status ck_weight_pack_decode(const int8_t* w_q, const float* w_scale, int64_t n, int64_t k,
+                                void* w_dec, void* stream)
+{
+    if (n < 0 || n % 16 != 0 || k < 1 || k % 64 != 0) return CK_ESHAPE;
+    if (k > CK_MAX_K || decode_bytes(n, k) > CK_MAX_ELEMS) return CK_EUNSUPPORTED;
+    if (n == 0) return CK_OK;
+    if (!w_q || !w_scale || !w_dec) return CK_EINVAL;
+    if (!aligned16(w_q) || !aligned16(w_scale) || !aligned16(w_dec)) return CK_EINVAL;
+    return from_hip(ck::launch_pack_decode(w_q, w_scale, n, k, w_dec, (hipStream_t)stream));
+}
+
 ck_status ck_act_quant(const uint16_t* x, int64_t ldx, int64_t m, int64_t k, int32_t act,
                        int32_t group, int32_t layout, int8_t* x_q, float* x_scale, void* stream)
 {
@@ -133,7 +163,8 @@ static ck_status check_gemm_args(const int8_t* x_q, const float* x_scale, const 
                                  const float* w_scale, int32_t layout, int64_t m, int64_t n,
                                  int64_t k, const void* y, bool need_scales)
 {
-    CK_TRY(check_layout(layout));
+    CK_TRY(check_weight_layout(layout, m));
+    if (layout == CK_LAYOUT_DECODE) w_scale = x_scale;   // the decode layout carries its own
     if (k < 1 || k % 64 != 0) return CK_ESHAPE;
     if (k > CK_MAX_K) return CK_EUNSUPPORTED;
     if (m < 0 || n < 0 || n % 16 != 0) return CK_ESHAPE;
@@ -163,9 +194,8 @@ ck_status ck_int8_gemm_bf16(const int8_t* x_q, const float* x_scale, const int8_
     CK_TRY(check_gemm_args(x_q, x_scale, w_q, w_scale, layout, m, n, k, y, true));
     if (m == 0 || n == 0) return CK_OK;
     CK_TRY(check_extra(bias, residual));
-    return from_hip(ck::launch_gemm_bf16(x_q, x_scale, w_q, w_scale, m, n, k, y,
-                                         layout == CK_LAYOUT_BLOCKED, (hipStream_t)stream,
-                                         ck::EpiExtra{bias, residual}));
+    return from_hip(ck::launch_gemm_bf16(x_q, x_scale, w_q, w_scale, m, n, k, y, layout,
+                                         (hipStream_t)stream, ck::EpiExtra{bias, residual}));
 }
 
 ck_status ck_int8_gemm_i32(const int8_t* x_q, const int8_t* w_q, int32_t layout, int64_t m,
@@ -173,8 +203,7 @@ ck_status ck_int8_gemm_i32(const int8_t* x_q, const int8_t* w_q, int32_t layout,
 {
     CK_TRY(check_gemm_args(x_q, nullptr, w_q, nullptr, layout, m, n, k, acc, false));
     if (m == 0 || n == 0) return CK_OK;
-    return from_hip(ck::launch_gemm_i32(x_q, w_q, m, n, k, acc, layout == CK_LAYOUT_BLOCKED,
-                                        (hipStream_t)stream));
+    return from_hip(ck::launch_gemm_i32(x_q, w_q, m, n, k, acc, layout, (hipStream_t)stream));
 }
 
 ck_status ck_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, const int8_t* w_q,
@@ -184,24 +213,26 @@ ck_status ck_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, const int8
 {
     CK_TRY(check_k(k, group));
     CK_TRY(check_act(act, ldx, k));
-    CK_TRY(check_layout(layout));
+    CK_TRY(check_weight_layout(layout, m));
     if (m < 0 || n < 0 || n % 16 != 0) return CK_ESHAPE;
     CK_TRY(check_gemm_extent(m, n, k));
     if (m == 0 || n == 0) return CK_OK;
-    if (!x || !w_q || !w_scale || !y) return CK_EINVAL;
-    if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_scale) || !aligned16(y)) return CK_EINVAL;
+    const bool dec = layout == CK_LAYOUT_DECODE;   // w_scale unused: the layout carries it
+    if (!x || !w_q || (!w_scale && !dec) || !y) return CK_EINVAL;
+    if (!aligned16(x) || !aligned16(w_q) || (!dec && !aligned16(w_scale)) || !aligned16(y))
+        return CK_EINVAL;
     CK_TRY(check_extra(bias, residual));
     const size_t need = ck_int8_linear_workspace_size(m, k);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
         return CK_EWORKSPACE;
-    const bool blocked = layout == CK_LAYOUT_BLOCKED;
+    const bool blocked = layout != CK_LAYOUT_ROWS;
     int8_t* xq = static_cast<int8_t*>(workspace);
     float* sx = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                          round_up((size_t)pad_rows(m) * (size_t)k));
     hipStream_t st = (hipStream_t)stream;
     CK_TRY(from_hip(ck::launch_quant_rows(act == CK_ACT_SWIGLU ? 1 : 0, x, ldx, m, k, group, xq,
                                           sx, nullptr, blocked, st)));
-    return from_hip(ck::launch_gemm_bf16(xq, sx, w_q, w_scale, m, n, k, y, blocked, st,
+    return from_hip(ck::launch_gemm_bf16(xq, sx, w_q, w_scale, m, n, k, y, layout, st,
                                          ck::EpiExtra{bias, residual}));
 }
 
@@ -222,20 +253,21 @@ ck_status ck_swiglu_mlp(const uint16_t* x, const int8_t* w_gu, const float* s_gu
 {
     CK_TRY(check_k(h, group));   // stage 1 contracts over h
     CK_TRY(check_k(i, group));   // stage 2 contracts over i
-    CK_TRY(check_layout(layout));
+    CK_TRY(check_weight_layout(layout, m));
     if (m < 0 || h % 16 != 0) return CK_ESHAPE;
     CK_TRY(check_gemm_extent(m, 2 * i, h));
     CK_TRY(check_gemm_extent(m, h, i));
     if (m == 0) return CK_OK;
-    if (!x || !w_gu || !s_gu || !w_down || !s_down || !y) return CK_EINVAL;
-    if (!aligned16(x) || !aligned16(w_gu) || !aligned16(s_gu) || !aligned16(w_down) ||
-        !aligned16(s_down) || !aligned16(y))
+    const bool dec = layout == CK_LAYOUT_DECODE;   // scales inside the weights
+    if (!x || !w_gu || !w_down || !y || (!dec && (!s_gu || !s_down))) return CK_EINVAL;
+    if (!aligned16(x) || !aligned16(w_gu) || !aligned16(w_down) || !aligned16(y) ||
+        (!dec && (!aligned16(s_gu) || !aligned16(s_down))))
         return CK_EINVAL;
     const size_t need = ck_swiglu_mlp_workspace_size(m, h, i);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
         return CK_EWORKSPACE;
     const size_t M = (size_t)m, MP = (size_t)pad_rows(m), H = (size_t)h, I = (size_t)i;
-    const bool blocked = layout == CK_LAYOUT_BLOCKED;
+    const bool blocked = layout != CK_LAYOUT_ROWS;
     char* p = static_cast<char*>(workspace);
     int8_t* xq = reinterpret_cast<int8_t*>(p);          p += round_up(MP * H);
     float* sx = reinterpret_cast<float*>(p);            p += round_up(M * 4);
@@ -245,10 +277,10 @@ ck_status ck_swiglu_mlp(const uint16_t* x, const int8_t* w_gu, const float* s_gu
     hipStream_t st = (hipStream_t)stream;
     // stage 1: packed [gate | up] projection, BF16 [m, 2i]
     CK_TRY(from_hip(ck::launch_quant_rows(0, x, h, m, h, group, xq, sx, nullptr, blocked, st)));
-    CK_TRY(from_hip(ck::launch_gemm_bf16(xq, sx, w_gu, s_gu, m, 2 * i, h, y1, blocked, st)));
+    CK_TRY(from_hip(ck::launch_gemm_bf16(xq, sx, w_gu, s_gu, m, 2 * i, h, y1, layout, st)));
     // stage 2: silu(gate) * up inside the down projection's quantizer
     CK_TRY(from_hip(ck::launch_quant_rows(1, y1, 2 * i, m, i, group, hq, sh, nullptr, blocked, st)));
-    return from_hip(ck::launch_gemm_bf16(hq, sh, w_down, s_down, m, h, i, y, blocked, st));
+    return from_hip(ck::launch_gemm_bf16(hq, sh, w_down, s_down, m, h, i, y, layout, st));
 }
 
 ck_status ck_silu_f32(const uint16_t* gate, int64_t n, float* out, void* stream)

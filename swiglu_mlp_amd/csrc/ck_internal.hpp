@@ -27,13 +27,14 @@ hipError_t launch_silu(const uint16_t* g, int64_t n, float* out, hipStream_t st)
 // y[m, n] = bf16(fl(fl(f32(x_q . w_q^T) * sx[m]) * sw[n])); both operands in
 // the row-major or the blocked layout.
 // `ex` adds an optional bias and residual before the BF16 rounding.
+// layout: 0 rows, 1 blocked, 2 decode (W only; the activation codes are blocked).
 hipError_t launch_gemm_bf16(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                            int64_t m, int64_t n, int64_t k, uint16_t* y, bool blocked, hipStream_t st,
+                            int64_t m, int64_t n, int64_t k, uint16_t* y, int layout, hipStream_t st,
                             EpiExtra ex = EpiExtra{});
 
 // acc[m, n] = x_q . w_q^T in int32.
 hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
-                           int32_t* acc, bool blocked, hipStream_t st);
+                           int32_t* acc, int layout, hipStream_t st);
 
 // Blocked-layout GEMM (gemm_blk.hip).
 hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
@@ -41,9 +42,14 @@ hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, 
                            hipStream_t st, EpiExtra ex = EpiExtra{});
 
 // Blocked-layout GEMM for m <= 64 (gemm_small.hip): streams the weights once.
+// decode: W in the decode layout (sw unused).
 hipError_t launch_gemm_small(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                              int64_t m, int64_t n, int64_t k, void* out, bool out_i32, hipStream_t st,
-                             EpiExtra ex = EpiExtra{});
+                             EpiExtra ex = EpiExtra{}, bool decode = false);
+
+// Row-major codes + scales -> decode layout (include/ck.h).
+hipError_t launch_pack_decode(const int8_t* w, const float* sw, int64_t n, int64_t k, void* out,
+                              hipStream_t st);
 
 // Largest m routed to launch_gemm_small.
 constexpr int64_t kSmallM = 64;

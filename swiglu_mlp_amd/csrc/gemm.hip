@@ -283,19 +283,23 @@ hipError_t launch_gemm_t(const int8_t* xq, const float* sx, const int8_t* wq, co
 }  // namespace
 
 hipError_t launch_gemm_bf16(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                            int64_t m, int64_t n, int64_t k, uint16_t* y, bool blocked, hipStream_t st,
+                            int64_t m, int64_t n, int64_t k, uint16_t* y, int layout, hipStream_t st,
                             EpiExtra ex)
 {
     if (m == 0 || n == 0) return hipSuccess;
+    if (layout == 2) return launch_gemm_small(xq, sx, wq, sw, m, n, k, y, false, st, ex, true);
+    const bool blocked = layout == 1;
     if (blocked && m <= kSmallM) return launch_gemm_small(xq, sx, wq, sw, m, n, k, y, false, st, ex);
     if (blocked) return launch_gemm_blk(xq, sx, wq, sw, m, n, k, y, false, num_cus(), st, ex);
     return launch_gemm_t<false>(xq, sx, wq, sw, m, n, k, y, st, ex);
 }
 
 hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
-                           int32_t* acc, bool blocked, hipStream_t st)
+                           int32_t* acc, int layout, hipStream_t st)
 {
     if (m == 0 || n == 0) return hipSuccess;
+    if (layout == 2) return launch_gemm_small(xq, nullptr, wq, nullptr, m, n, k, acc, true, st, EpiExtra{}, true);
+    const bool blocked = layout == 1;
     if (blocked && m <= kSmallM) return launch_gemm_small(xq, nullptr, wq, nullptr, m, n, k, acc, true, st);
     if (blocked) return launch_gemm_blk(xq, nullptr, wq, nullptr, m, n, k, acc, true, num_cus(), st);
     return launch_gemm_t<true>(xq, nullptr, wq, nullptr, m, n, k, acc, st);

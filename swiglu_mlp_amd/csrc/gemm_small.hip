@@ -34,7 +34,9 @@ struct SmallCfg {
     static constexpr int U = MT == 1 ? 8 : (MT == 2 ? 4 : 3);   // chunks per batch per wave
 };
 
-template <int MT, bool OUT_I32>
+// DEC: W in the decode layout (include/ck.h): each 16-row group one linear
+// stream, its row scales in the group's 64-byte header.
+template <int MT, bool OUT_I32, bool DEC>
 __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
     const float* __restrict__ sw, int M, int N, int K, int m_rows, int n_rows, void* __restrict__ out,
@@ -50,8 +52,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const int KB = K >> 5;           // 1 KB blocks per 32-row block
     const int KC = K >> 6;           // 64-byte k-chunks
 
-    const __amdgpu_buffer_rsrc_t rs_w =
-        __builtin_amdgcn_make_buffer_rsrc((void*)wq, (short)0, n_rows * K, 0x00020000);
+    const uint32_t grp_bytes = 64u + 16u * (uint32_t)K;     // DEC: one 16-row group
+    const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)wq, (short)0, DEC ? (int)((uint32_t)(N / 16) * grp_bytes) : n_rows * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_x =
         __builtin_amdgcn_make_buffer_rsrc((void*)xq, (short)0, m_rows * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_o =
@@ -65,7 +68,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const int r = lane & 15;
     const int c = lane >> 4;
     const uint32_t lane_off = (uint32_t)((c >> 1) * 1024 + (c & 1) * 512 + r * 16);
-    const uint32_t w_base = (uint32_t)((nb >> 1) * KB) * 1024u + (uint32_t)(nb & 1) * 256u + lane_off;
+    // DEC: chunk j of group nb is the 1 KB at nb * grp_bytes + 64 + 1024 j,
+    // lane l's 16 bytes at 16 l (quarter l / 16, row l % 16)
+    const uint32_t w_base = DEC ? (uint32_t)nb * grp_bytes + 64u + (uint32_t)lane * 16u
+                                : (uint32_t)((nb >> 1) * KB) * 1024u + (uint32_t)(nb & 1) * 256u + lane_off;
+    const uint32_t w_step = DEC ? 1024u : 2048u;   // bytes per 64-byte k-chunk
     uint32_t x_base[MT];
 #pragma unroll
     for (int f = 0; f < MT; ++f) x_base[f] = (uint32_t)((f >> 1) * KB) * 1024u + (uint32_t)(f & 1) * 256u + lane_off;
@@ -82,7 +89,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
             const int j = wave + WAVES * (U * b + u);
             const bool ok = j < KC;
             const uint32_t ko = (uint32_t)j * 2048u;
-            w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, ok ? w_base + ko : kOutside, 0, 0);
+            w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, ok ? w_base + (uint32_t)j * w_step : kOutside, 0, 0);
 #pragma unroll
             for (int f = 0; f < MT; ++f)
                 x[u][f] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, ok ? x_base[f] + ko : kOutside, 0, 0);
@@ -125,7 +132,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         __builtin_amdgcn_raw_buffer_store_b128(t, rs_o, m < M ? row * 4u : kOutside, 0, 0);
     } else {
         const float sxm = sx[min(m, M - 1)];
-        const float4 s4 = *reinterpret_cast<const float4*>(sw + n);
+        const float4 s4 = DEC ? *reinterpret_cast<const float4*>(wq + (size_t)nb * grp_bytes + 16 * c)
+                              : *reinterpret_cast<const float4*>(sw + n);
         float y0 = ((float)t[0] * sxm) * s4.x;
         float y1 = ((float)t[1] * sxm) * s4.y;
         float y2 = ((float)t[2] * sxm) * s4.z;
@@ -137,13 +145,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int MT, bool I32>
+template <int MT, bool I32, bool DEC>
 hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int M, int N,
                   int K, void* out, hipStream_t st, EpiExtra ex)
 {
     const int m_rows = (M + 255) / 256 * 256;
     const int n_rows = (N + 255) / 256 * 256;
-    hipLaunchKernelGGL((gemm_small_kernel<MT, I32>), dim3(N / 16), dim3(WAVES * 64), 0, st, xq, sx, wq,
+    hipLaunchKernelGGL((gemm_small_kernel<MT, I32, DEC>), dim3(N / 16), dim3(WAVES * 64), 0, st, xq, sx, wq,
                        sw, M, N, K, m_rows, n_rows, out, ex);
     return hipGetLastError();
 }
@@ -153,12 +161,14 @@ hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const flo
 // m <= 64, n % 16 == 0, k % 64 == 0 (checked by the caller).
 hipError_t launch_gemm_small(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                              int64_t m, int64_t n, int64_t k, void* out, bool out_i32, hipStream_t st,
-                             EpiExtra ex)
+                             EpiExtra ex, bool decode)
 {
     const int M = (int)m, N = (int)n, K = (int)k;
-#define CK_SMALL(MT_)                                                                      \
-    return out_i32 ? small::launch<MT_, true>(xq, sx, wq, sw, M, N, K, out, st, ex)        \
-                   : small::launch<MT_, false>(xq, sx, wq, sw, M, N, K, out, st, ex)
+#define CK_SMALL(MT_)                                                                                   \
+    return decode ? (out_i32 ? small::launch<MT_, true, true>(xq, sx, wq, sw, M, N, K, out, st, ex)      \
+                             : small::launch<MT_, false, true>(xq, sx, wq, sw, M, N, K, out, st, ex))    \
+                  : (out_i32 ? small::launch<MT_, true, false>(xq, sx, wq, sw, M, N, K, out, st, ex)     \
+                             : small::launch<MT_, false, false>(xq, sx, wq, sw, M, N, K, out, st, ex))
     if (m <= 16) CK_SMALL(1);
     if (m <= 32) CK_SMALL(2);
     CK_SMALL(4);

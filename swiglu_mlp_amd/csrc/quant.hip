@@ -198,6 +198,30 @@ __global__ __launch_bounds__(256) void pack_blocked_kernel(const int8_t* __restr
     *reinterpret_cast<uint4*>(out + u * 16) = v;
 }
 
+// Row-major codes + row scales -> decode layout (include/ck.h): one thread
+// per 16-byte unit of the output, written in order.  Group b of 16 rows has
+// 4 header units (the 16 scales) then k units: unit 4 + v holds
+// W[16 b + v % 16][64 (v / 64) + 16 ((v / 16) % 4) .. + 16].
+__global__ __launch_bounds__(256) void pack_decode_kernel(const int8_t* __restrict__ w,
+                                                          const float* __restrict__ sw, int k,
+                                                          int64_t units, uint4* __restrict__ out)
+{
+    const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= units) return;
+    const int64_t per = 4 + (int64_t)k;       // units per 16-row group
+    const int64_t b = u / per;
+    const int v = (int)(u - b * per);
+    uint4 o;
+    if (v < 4) {
+        o = *reinterpret_cast<const uint4*>(sw + b * 16 + v * 4);
+    } else {
+        const int t = v - 4;
+        const int r = t & 15, q = (t >> 4) & 3, c = t >> 6;
+        o = *reinterpret_cast<const uint4*>(w + (b * 16 + r) * (int64_t)k + c * 64 + q * 16);
+    }
+    out[u] = o;
+}
+
 __global__ __launch_bounds__(256) void silu_kernel(const uint16_t* __restrict__ g, int64_t n,
                                                    float* __restrict__ out)
 {
@@ -311,6 +335,16 @@ hipError_t launch_pack_blocked(const int8_t* w, int64_t n, int64_t k, int8_t* ou
     if (units == 0) return hipSuccess;
     hipLaunchKernelGGL(pack_blocked_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, w,
                        (int)n, (int)k, units, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_decode(const int8_t* w, const float* sw, int64_t n, int64_t k, void* out,
+                              hipStream_t st)
+{
+    const int64_t units = (n / 16) * (4 + k);
+    if (units == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_decode_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, w, sw,
+                       (int)k, units, static_cast<uint4*>(out));
     return hipGetLastError();
 }
 

@@ -114,8 +114,44 @@ def test_swiglu_mlp_checks(L):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 256, 500, 128, FAKE, FAKE, ws, None) == ESHAPE
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 256, 512, 128, FAKE, FAKE, ws - 256, None) == EWS
     assert f(FAKE, None, FAKE, FAKE, FAKE, 1, 8, 256, 512, 128, FAKE, FAKE, ws, None) == EINVAL
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 256, 512, 128, FAKE, FAKE, ws, None) == EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 256, 512, 128, FAKE, FAKE, ws, None) == EINVAL
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 256, 512, 128, FAKE, FAKE, 0, None) == OK
+    # decode layout: m <= 64 only; the weights carry their scales (NULL accepted)
+    ws65 = L.ck_swiglu_mlp_workspace_size(65, 256, 512)
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 65, 256, 512, 128, FAKE, FAKE, ws65, None) == EUNSUP
+    assert f(FAKE, FAKE, None, FAKE, None, 2, 8, 256, 512, 128, FAKE, FAKE, ws - 256, None) == EWS
+    assert f(FAKE, FAKE, None, FAKE, None, 1, 8, 256, 512, 128, FAKE, FAKE, ws, None) == EINVAL
+
+
+def test_decode_layout_checks(L):
+    """Decode layout (include/ck.h): size, packing and GEMM argument checks.
+    No call here reaches a kernel launch."""
+    assert L.ck_decode_size(32, 256) == 2 * (64 + 16 * 256)
+    assert L.ck_decode_size(0, 256) == 0 and L.ck_decode_size(16, 0) == 0
+    assert L.ck_decode_size(17, 64) == 2 * (64 + 16 * 64)
+    pk = L.ck_weight_pack_decode
+    assert pk(FAKE, FAKE, 20, 256, FAKE, None) == ESHAPE       # n % 16
+    assert pk(FAKE, FAKE, 32, 100, FAKE, None) == ESHAPE       # k % 64
+    assert pk(FAKE, None, 32, 256, FAKE, None) == EINVAL       # scales needed
+    assert pk(FAKE, FAKE + 4, 32, 256, FAKE, None) == EINVAL   # scales read as float4
+    assert pk(FAKE, FAKE, 0, 256, FAKE, None) == OK
+    assert pk(FAKE, FAKE, 32, 65536, FAKE, None) == EUNSUP
+    assert pk(FAKE, FAKE, 16 * 8192, 32768, FAKE, None) == EUNSUP   # > 2^31 bytes
+    assert L.ck_int8_gemm_i32(FAKE, FAKE, 2, 65, 32, 256, FAKE, None) == EUNSUP
+    assert L.ck_int8_gemm_i32(FAKE, FAKE, 2, 4, 20, 256, FAKE, None) == ESHAPE
+    g = L.ck_int8_gemm_bf16
+    assert g(FAKE, FAKE, FAKE, None, None, None, 2, 65, 32, 256, FAKE, None) == EUNSUP
+    assert g(FAKE, None, FAKE, None, None, None, 2, 4, 32, 256, FAKE, None) == EINVAL
+    lin = L.ck_int8_linear
+    ws = L.ck_int8_linear_workspace_size(8, 256)
+    assert lin(FAKE, 256, 0, FAKE, None, None, None, 2, 65, 32, 256, 128, FAKE, FAKE,
+               L.ck_int8_linear_workspace_size(65, 256), None) == EUNSUP
+    assert lin(FAKE, 256, 0, FAKE, None, None, None, 2, 8, 32, 256, 128, FAKE, FAKE,
+               ws - 1, None) == EWS
+    assert lin(FAKE, 256, 0, FAKE, None, None, None, 1, 8, 32, 256, 128, FAKE, FAKE,
+               ws, None) == EINVAL
+    # activation codes are never in the decode layout
+    assert L.ck_act_quant(FAKE, 256, 4, 256, 0, 128, 2, FAKE, FAKE, None) == EINVAL
 
 
 def test_weight_pack_checks(L):

@@ -463,13 +463,13 @@ def test_blocked_stages_equal_swiglu_mlp():
 
 
 @pytest.mark.parametrize("g,layout,scalar", [(256, "blocked", False), (128, "rows", False),
-                                             (256, "blocked", True)])
+                                             (256, "blocked", True), (128, "decode", False)])
 def test_serialized_layer_bit_exact(orc, g, layout, scalar):
     """Pre-quantized I8 weights + F32 [out, 1] scales, as a serialized
     checkpoint holds them (sglang PR #35994 report), used without re-quantizing."""
     from swiglu_mlp_amd import checkpoint as C
     say(f"serialized layer g={g} layout={layout} scalar_scale={scalar}")
-    m, k, n = 200, 1024, 528
+    m, k, n = (64 if layout == "decode" else 200), 1024, 528
     d = W.case(m, k, n, 0, seed=77)
     wq_o, sw_o = orc.weight_prep(d["w"], g)          # what a serialized file holds
     if scalar:
@@ -480,3 +480,99 @@ def test_serialized_layer_bit_exact(orc, g, layout, scalar):
     wq, sw = C.serialized_linear_weights(dev(wq_o), scale, group=g, layout=layout)
     y = bf16_host(ck.ck_int8_linear(bf16_dev(d["x"]), wq, sw, g, layout=layout))
     np.testing.assert_array_equal(y, orc.int8_linear(d["x"], 0, wq_o, sw_o, g))
+
+
+def to_decode(wq, sw):
+    """Row-major int8 [n, k] and FP32 scales [n] -> the decode layout of
+    include/ck.h: per 16-row group b, the 16 scales (64 bytes), then chunk c of
+    1 KB holding W[16 b + r][64 c + 16 q + e] at 256 q + 16 r + e."""
+    n, k = wq.shape
+    g = n // 16
+    body = wq.reshape(g, 16, k // 64, 4, 16).transpose(0, 2, 3, 1, 4).reshape(g, 16 * k)
+    head = np.ascontiguousarray(sw.astype(np.float32).reshape(g, 16)).view(np.uint8)
+    return np.ascontiguousarray(np.concatenate([head, body.view(np.uint8)], axis=1))
+
+
+@pytest.mark.parametrize("n,k", [(16, 64), (48, 1024), (4096, 3072)])
+def test_weight_pack_decode_layout(orc, n, k):
+    say(f"weight_pack_decode n={n} k={k}")
+    rng = np.random.default_rng(n + k)
+    wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    sw = rng.random(n, dtype=np.float32)
+    got = host(ck.ck_weight_pack_decode(dev(wq), dev(sw)))
+    np.testing.assert_array_equal(got, to_decode(wq, sw))
+
+
+DECODE_SHAPES = [  # (m, n, k): 1, 2 and 4 row fragments, ragged m, short and long k
+    (1, 4096, 4096), (2, 48, 1024), (16, 1024, 3072), (17, 2048, 128), (33, 4096, 4096),
+    (64, 4096, 12288), (64, 16, 64),
+]
+
+
+@pytest.mark.parametrize("m,n,k", DECODE_SHAPES)
+def test_decode_gemm_bit_exact(orc, m, n, k):
+    say(f"decode gemm i32 + bf16 m={m} n={n} k={k}")
+    rng = np.random.default_rng(5 * m + n + k)
+    xq = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    sx = (rng.random(m, dtype=np.float32) * 1e-3).astype(np.float32)
+    sw = (rng.random(n, dtype=np.float32) * 1e-3).astype(np.float32)
+    xb, wd = dev(to_blocked(xq)), dev(to_decode(wq, sw))
+    acc_o = orc.gemm_i32(xq, wq)
+    np.testing.assert_array_equal(host(ck.ck_int8_gemm_i32(xb, wd, "decode", m=m)), acc_o)
+    y = bf16_host(ck.ck_int8_gemm_bf16(xb, dev(sx.reshape(m, 1)), wd, None, layout="decode"))
+    np.testing.assert_array_equal(y, orc.dequant(acc_o, sx, sw))
+
+
+DECODE_LINEAR = [  # (m, k, n, act, g)
+    (1, 1024, 4096, 0, 128), (7, 2048, 528, 1, 256), (33, 3072, 1040, 0, 128),
+    (64, 12288, 3072, 1, 128), (64, 256, 16, 1, 64),
+]
+
+
+@pytest.mark.parametrize("m,k,n,act,g", DECODE_LINEAR)
+def test_int8_linear_decode_bit_exact(orc, m, k, n, act, g):
+    say(f"int8_linear decode m={m} k={k} n={n} act={act} g={g}")
+    d = W.case(m, k, n, act, seed=3000 + m, zero_rows=(m // 2,) if m > 2 else ())
+    wq_o, sw_o = orc.weight_prep(d["w"], g)
+    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    wd = ck.ck_weight_pack_decode(wq, sw)
+    x = bf16_dev(d["x"])
+    y = bf16_host(ck.ck_int8_linear(x, wd, None, g, act, layout="decode"))
+    np.testing.assert_array_equal(y, orc.int8_linear(d["x"], act, wq_o, sw_o, g))
+    rng = np.random.default_rng(m + n)
+    bias = rng.standard_normal(n).astype(np.float32)
+    res = orc.f32_to_bf16(rng.standard_normal((m, n)).astype(np.float32))
+    y = ck.ck_int8_linear(x, wd, None, g, act, layout="decode", bias=dev(bias),
+                          residual=bf16_dev(res))
+    np.testing.assert_array_equal(
+        bf16_host(y), orc.int8_linear(d["x"], act, wq_o, sw_o, g, bias=bias, residual=res))
+
+
+@pytest.mark.parametrize("m", [1, 16, 64])
+def test_swiglu_mlp_decode_bit_exact(orc, m):
+    say(f"swiglu_mlp decode m={m} h=1024 i=2816")
+    h, i, g = 1024, 2816, 128
+    rng = np.random.default_rng(40 + m)
+    xb = W.to_bf16_bits(rng.standard_normal((m, h)).astype(np.float32))
+    w_gu = (0.02 * rng.standard_normal((2 * i, h))).astype(np.float32)
+    w_dn = (0.01 * rng.standard_normal((h, i))).astype(np.float32)
+    gq, gs = ck.ck_weight_prep(dev(w_gu), g)
+    dq, ds = ck.ck_weight_prep(dev(w_dn), g)
+    y = ck.ck_swiglu_mlp(bf16_dev(xb), ck.ck_weight_pack_decode(gq, gs), None,
+                         ck.ck_weight_pack_decode(dq, ds), None, g, layout="decode")
+    y_blk = ck.ck_swiglu_mlp(bf16_dev(xb), ck.ck_weight_pack(gq), gs, ck.ck_weight_pack(dq), ds,
+                             g, layout="blocked")
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_blk.view(torch.int16))
+    (gq_o, gs_o), (dq_o, ds_o) = orc.weight_prep(w_gu, g), orc.weight_prep(w_dn, g)
+    np.testing.assert_array_equal(bf16_host(y), orc.swiglu_mlp(xb, gq_o, gs_o, dq_o, ds_o, g))
+
+
+def test_decode_rejects_more_than_64_rows():
+    say("decode layout with m=65 -> CK_EUNSUPPORTED")
+    wq, sw = ck.ck_weight_prep(torch.zeros((32, 256), dtype=torch.float32, device=DEV), 128)
+    wd = ck.ck_weight_pack_decode(wq, sw)
+    x = torch.zeros((65, 256), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ck.CKError, match="CK_EUNSUPPORTED"):
+        ck.ck_int8_linear(x, wd, None, 128, layout="decode")

@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "effective INT8 TOPS of ConvRot int8_linear(+SwiGLU), % of MI355X INT8 peak"
 PEAK_INT8_TOPS = 5000.0        # MI355X dense INT8 MFMA, 5.0 POP/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, 2.5 PFLOP/s (the W8A16 GEMM)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -54,6 +55,9 @@ def parse():
                     help="run only a plain 1 GiB device copy (for scaling HBM counters)")
     ap.add_argument("--small-m-sweep", action="store_true",
                     help="time the few-row GEMM at M = 1..64 instead of the step (one line per case)")
+    ap.add_argument("--w8a16", action="store_true",
+                    help="the W8A16 variant: BF16 rotated activations (no activation quantization) "
+                         "times the INT8 weights on BF16 MFMA")
     return ap.parse_args()
 
 
@@ -214,7 +218,22 @@ def main():
         xb = (2 * inter * 4) if ex else 0
         db = (h * 4 + m * h * 2) if ex else 0
         # (name, callable, algorithmic ops, algorithmic HBM bytes, bound)
+        if args.w8a16:
+            xr = torch.empty((mp, h), dtype=torch.bfloat16, device=dev)
+            hr = torch.empty((mp, inter), dtype=torch.bfloat16, device=dev)
         stages = [
+            ("x_rotate_bf16", lambda s: L.ck_act_rotate_bf16(x.data_ptr(), h, m, h, 0, g, BLK, xr.data_ptr(), s),
+             0, m * h * 4, "hbm"),
+            ("gate_up_w8a16", lambda s: L.ck_w8a16_gemm_bf16(xr.data_ptr(), wgu.data_ptr(), sgu.data_ptr(),
+                                                             *gu_extra, m, 2 * inter, h, t1.data_ptr(), s),
+             2 * m * 2 * inter * h, m * h * 2 + 2 * inter * h + m * 2 * inter * 2 + xb, "mfma_bf16"),
+            ("swiglu_rotate_bf16", lambda s: L.ck_act_rotate_bf16(t1.data_ptr(), 2 * inter, m, inter, 1, g,
+                                                                  BLK, hr.data_ptr(), s),
+             0, m * inter * 6, "hbm"),
+            ("down_w8a16", lambda s: L.ck_w8a16_gemm_bf16(hr.data_ptr(), wd.data_ptr(), sd.data_ptr(),
+                                                          *d_extra, m, h, inter, y.data_ptr(), s),
+             2 * m * h * inter, m * inter * 2 + h * inter + m * h * 2 + db, "mfma_bf16"),
+        ] if args.w8a16 else [
             ("x_quant", lambda s: L.ck_act_quant(x.data_ptr(), h, m, h, 0, g, BLK, xq.data_ptr(),
                                                  sx.data_ptr(), s),
              0, m * h * 2 + m * h + m * 4, "hbm"),
@@ -245,7 +264,16 @@ def main():
         res = (torch.randn((m, n), device=dev) * 0.5).to(torch.bfloat16) if ex else None
         extra = (bias.data_ptr() if ex else None, res.data_ptr() if ex else None)
         eb = (n * 4 + m * n * 2) if ex else 0
+        if args.w8a16:
+            xr = torch.empty((ck.blocked_rows(m), k), dtype=torch.bfloat16, device=dev)
         stages = [
+            ("act_rotate_bf16", lambda s: L.ck_act_rotate_bf16(x.data_ptr(), ldx, m, k, wl.act, g, BLK,
+                                                               xr.data_ptr(), s),
+             0, m * ldx * 2 + m * k * 2, "hbm"),
+            ("w8a16_gemm", lambda s: L.ck_w8a16_gemm_bf16(xr.data_ptr(), wq.data_ptr(), sw.data_ptr(), *extra,
+                                                          m, n, k, y.data_ptr(), s),
+             2 * m * n * k, m * k * 2 + n * k + m * n * 2 + eb, "mfma_bf16"),
+        ] if args.w8a16 else [
             ("act_quant", lambda s: L.ck_act_quant(x.data_ptr(), ldx, m, k, wl.act, g, BLK,
                                                    xq.data_ptr(), sx.data_ptr(), s),
              0, m * ldx * 2 + m * k + m * 4, "hbm"),
@@ -311,7 +339,10 @@ def main():
     name, _, ops, nbytes, bound = stages[dom]
     dom_us = stage_means(ev, K, [dom])[name]
     t_s = dom_us * 1e-6
-    if bound == "mfma":
+    if bound == "mfma_bf16":
+        bound = "mfma"
+        achieved, peak, unit = ops / t_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    elif bound == "mfma":
         achieved, peak, unit = ops / t_s / 1e12, PEAK_INT8_TOPS, "TFLOP/s"
     else:
         achieved, peak, unit = nbytes / t_s / 1e9, PEAK_HBM_GBS, "GB/s"
@@ -334,23 +365,33 @@ def main():
             stage_roofline[st[0]] = {"us": round(kern_us[st[0]], 2),
                                      "TOPS": round(st[2] / ts / 1e12, 1),
                                      "frac_int8_peak": round(st[2] / ts / 1e12 / PEAK_INT8_TOPS, 4)}
+        elif st[4] == "mfma_bf16":
+            stage_roofline[st[0]] = {"us": round(kern_us[st[0]], 2),
+                                     "TFLOPS": round(st[2] / ts / 1e12, 1),
+                                     "frac_bf16_peak": round(st[2] / ts / 1e12 / PEAK_BF16_TFLOPS, 4)}
         else:
             stage_roofline[st[0]] = {"us": round(kern_us[st[0]], 2),
                                      "GBs": round(st[3] / ts / 1e9, 1),
                                      "frac_hbm_peak": round(st[3] / ts / 1e9 / PEAK_HBM_GBS, 4)}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.w8a16:
         cpu = cpu_baseline(wl, d, args.cpu_rows)
 
+    metric, unit, dtype = METRIC, "TOPS", "int8"
+    if args.w8a16:
+        metric = "effective TFLOP/s of the W8A16 ConvRot linear (BF16 activations, INT8 weights)"
+        unit, dtype = "TFLOP/s", "bf16xint8"
     line = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": K,
+        "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.desc}", "m": wl.m, "k": wl.k, "n": wl.n,
                    "group": g, "int8_ops_per_step": wl.int8_ops, "parallelism": "single-gpu",
-                   "epilogue": "bias+residual" if args.bias_residual else "dequant"},
-        "frac_of_int8_peak": round(value / PEAK_INT8_TOPS, 4),
+                   "epilogue": "bias+residual" if args.bias_residual else "dequant",
+                   "activations": "bf16 (W8A16)" if args.w8a16 else "int8"},
+        ("frac_of_bf16_peak" if args.w8a16 else "frac_of_int8_peak"):
+            round(value / (PEAK_BF16_TFLOPS if args.w8a16 else PEAK_INT8_TOPS), 4),
         "roofline": roofline, "stages": stage_roofline, "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }

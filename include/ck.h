@@ -228,6 +228,63 @@ ck_status ck_swiglu_mlp(const uint16_t *x, const int8_t *w_gu, const float *s_gu
                         void *workspace, size_t workspace_bytes, void *stream);
 size_t ck_swiglu_mlp_workspace_size(int64_t m, int64_t h, int64_t i);
 
+/* ---- W8A16: INT8 weights, BF16 activations (no activation quantization) ----
+ * Source: comfy-kitchen PR #277, "Notes for the reviewer": a variant that keeps
+ * the rotated activation in 16-bit floating point instead of quantizing it to
+ * INT8 (a different quantization grid, closer to the float32 result), with
+ * the INT8 weights widened on the fly; "The key observation": the GEMM runs in
+ * the rotated basis, so the widened W_rot is used as it is.  On this target
+ * the activation type is BF16 and the product accumulates in FP32.
+ *
+ * BF16 blocked layout (activations of these calls): rows padded to a multiple
+ * of 256; the 32 values k = 32 j .. 32 j + 31 of the 32-row block r / 32 are
+ * 2 KB at byte ((r / 32) * (k / 32) + j) * 2048, value (r, k) inside at byte
+ * ((k % 16) / 8) * 1024 + ((k % 32) / 16) * 512 + (r % 32) * 16 + (k % 8) * 2:
+ * two 1 KB BF16 MFMA operands that pair with one 1 KB block of the INT8
+ * blocked weight. */
+
+/* Rotated activation in BF16: a (= x, or silu(gate) * up for CK_ACT_SWIGLU,
+ * in FP32), u = the unnormalised blockwise FWHT of a (as ck_act_quant),
+ * x_rot = bf16(fl(u * fl(1 / sqrt(group)))).
+ *   layout  CK_LAYOUT_ROWS: x_rot [m, k] row-major; CK_LAYOUT_BLOCKED: the
+ *           BF16 blocked layout, ck_blocked_size(m, k) * 2 bytes (the padding
+ *           rows are not written)
+ * Errors as ck_act_quant. */
+ck_status ck_act_rotate_bf16(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,
+                             int32_t act, int32_t group, int32_t layout, uint16_t *x_rot,
+                             void *stream);
+
+/* y[m, n] = bf16(fl(acc[m, n] * w_scale[n]) (+ bias[n]) (+ residual[m, n])),
+ * acc = sum_k x_rot[m, k] * w_q[n, k] accumulated in FP32 (order unspecified;
+ * every product is exact in FP32).  x_rot in the BF16 blocked layout, w_q in
+ * CK_LAYOUT_BLOCKED (ck_weight_pack); bias and residual as ck_int8_linear.
+ * k % 64 == 0, n % 16 == 0.  Errors: CK_EINVAL on null or misaligned
+ * pointers; CK_ESHAPE on shapes; CK_EUNSUPPORTED past the 32-bit extents. */
+ck_status ck_w8a16_gemm_bf16(const uint16_t *x_rot, const int8_t *w_q, const float *w_scale,
+                             const float *bias, const uint16_t *residual, int64_t m, int64_t n,
+                             int64_t k, uint16_t *y, void *stream);
+
+/* The W8A16 linear: ck_act_rotate_bf16 (blocked) into the workspace, then
+ * ck_w8a16_gemm_bf16.  Arguments as ck_int8_linear with w_q in
+ * CK_LAYOUT_BLOCKED; workspace of ck_int8_linear_w8a16_workspace_size(m, k)
+ * bytes, 256-byte aligned, clobbered. */
+ck_status ck_int8_linear_w8a16(const uint16_t *x, int64_t ldx, int32_t act, const int8_t *w_q,
+                               const float *w_scale, const float *bias, const uint16_t *residual,
+                               int64_t m, int64_t n, int64_t k, int32_t group, uint16_t *y,
+                               void *workspace, size_t workspace_bytes, void *stream);
+size_t ck_int8_linear_w8a16_workspace_size(int64_t m, int64_t k);
+
+/* The SwiGLU MLP block with W8A16 linears (as ck_swiglu_mlp, with both
+ * rotated activations kept in BF16): rotate x, the packed [gate | up] W8A16
+ * GEMM to BF16, then silu(gate) * up rotated to BF16 and the down W8A16 GEMM.
+ * Weights in CK_LAYOUT_BLOCKED; workspace of
+ * ck_swiglu_mlp_w8a16_workspace_size(m, h, i) bytes, 256-byte aligned. */
+ck_status ck_swiglu_mlp_w8a16(const uint16_t *x, const int8_t *w_gu, const float *s_gu,
+                              const int8_t *w_down, const float *s_down, int64_t m, int64_t h,
+                              int64_t i, int32_t group, uint16_t *y, void *workspace,
+                              size_t workspace_bytes, void *stream);
+size_t ck_swiglu_mlp_w8a16_workspace_size(int64_t m, int64_t h, int64_t i);
+
 /* ---- test hooks: the same device code with its intermediate exposed ---- */
 
 /* Raw int32 accumulators acc[m, n] = sum_k x_q[m, k] * w_q[n, k] from the
@@ -235,6 +292,11 @@ size_t ck_swiglu_mlp_workspace_size(int64_t m, int64_t h, int64_t i);
 ck_status ck_int8_gemm_i32(const int8_t *x_q, const int8_t *w_q, int32_t layout,
                            int64_t m, int64_t n, int64_t k, int32_t *acc,
                            void *stream);
+
+/* Raw FP32 accumulators acc[m, n] of the W8A16 GEMM (operands as
+ * ck_w8a16_gemm_bf16). */
+ck_status ck_w8a16_gemm_f32(const uint16_t *x_rot, const int8_t *w_q, int64_t m, int64_t n,
+                            int64_t k, float *acc, void *stream);
 
 /* FP32 silu of n BF16 gate values, by the quantizer's own device function
  * (sglang PR #44196, "Accuracy Tests": silu kept in FP32). */

@@ -20,6 +20,9 @@ Sources (page title, section):
   * sglang PR #35994 report "[diffusion] Load serialized Comfy ConvRot INT8
     DiTs", key source excerpts (I8 weight + F32 [out, 1] row scale,
     per_channel=True, convrot=True; in_features divisible by the group size).
+  * comfy-kitchen PR #277, "Notes for the reviewer": the variant that keeps
+    the rotated activation in 16-bit floating point (W8A16), with the INT8
+    weight widened on the fly.
 """
 from __future__ import annotations
 
@@ -269,6 +272,63 @@ def swiglu_mlp(x_bf16, wgu_q, sgu, wd_q, sd, g: int, return_all: bool = False):
     int8_linear(..., input_act="swiglu") on its BF16 output."""
     s1 = int8_linear(x_bf16, ACT_NONE, wgu_q, sgu, g, return_all=True)
     s2 = int8_linear(s1["y"], ACT_SWIGLU, wd_q, sd, g, return_all=True)
+    if return_all:
+        return dict(stage1=s1, stage2=s2, y=s2["y"])
+    return s2["y"]
+
+
+# --------------------------------------------------------------------------
+# W8A16: the rotated activation kept in BF16 (comfy-kitchen PR #277, "Notes
+# for the reviewer"; "The key observation": the GEMM stays in the rotated basis)
+# --------------------------------------------------------------------------
+def act_rotate_bf16(x_bf16, act: int, g: int, k: int | None = None) -> np.ndarray:
+    """x_rot = x H with the orthonormal H, rounded to BF16: the unnormalised
+    FWHT u of the (optionally SwiGLU'd) row, then bf16(fl(u * fl(1/sqrt(g))))."""
+    u = act_rotate(x_bf16, act, g, k)
+    return f32_to_bf16(u * norm_const(g))      # float32 * float32: one FP32 rounding
+
+
+def w8a16_acc(x_rot_bf16, wq) -> np.ndarray:
+    """sum_k x_rot[m, k] * q[n, k] in float64 (each product is exact; the sum
+    is exact up to float64 rounding)."""
+    x = bf16_to_f32(_c(x_rot_bf16, np.uint16)).astype(np.float64)
+    return x @ np.asarray(wq, dtype=np.float64).T
+
+
+def w8a16_abs_acc(x_rot_bf16, wq) -> np.ndarray:
+    """sum_k |x_rot[m, k] * q[n, k]|: the scale of the FP32 accumulation error."""
+    x = np.abs(bf16_to_f32(_c(x_rot_bf16, np.uint16)).astype(np.float64))
+    return x @ np.abs(np.asarray(wq, dtype=np.float64)).T
+
+
+def w8a16_epilogue(acc, sw, bias=None, residual=None) -> np.ndarray:
+    """y = bf16(f32(acc * s_w[n]) (+ bias[n]) (+ residual[m, n])), the sums in
+    FP32 in that order, one BF16 rounding at the end."""
+    t = (np.asarray(acc, dtype=np.float64) * _c(sw, np.float64).reshape(1, -1)).astype(np.float32)
+    if bias is not None:
+        t = t + _c(bias, np.float32).reshape(1, -1)
+    if residual is not None:
+        t = t + bf16_to_f32(_c(residual, np.uint16))
+    return f32_to_bf16(t)
+
+
+def w8a16_linear(x_bf16, act: int, wq, sw, g: int, bias=None, residual=None,
+                 return_all: bool = False):
+    """The W8A16 linear: BF16 rotated activation times the INT8 W_rot codes,
+    accumulated exactly, scaled per output row."""
+    x_rot = act_rotate_bf16(x_bf16, act, g, k=np.asarray(wq).shape[1])
+    acc = w8a16_acc(x_rot, wq)
+    y = w8a16_epilogue(acc, sw, bias, residual)
+    if return_all:
+        return dict(x_rot=x_rot, acc=acc, y=y)
+    return y
+
+
+def swiglu_mlp_w8a16(x_bf16, wgu_q, sgu, wd_q, sd, g: int, return_all: bool = False):
+    """The SwiGLU MLP block with W8A16 linears: w8a16_linear of x against the
+    packed [gate | up] codes, then w8a16_linear(..., swiglu) of its BF16 output."""
+    s1 = w8a16_linear(x_bf16, ACT_NONE, wgu_q, sgu, g, return_all=True)
+    s2 = w8a16_linear(s1["y"], ACT_SWIGLU, wd_q, sd, g, return_all=True)
     if return_all:
         return dict(stage1=s1, stage2=s2, y=s2["y"])
     return s2["y"]

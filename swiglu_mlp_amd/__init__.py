@@ -15,7 +15,10 @@ Entry points keep the C names:
 * ``ck_int8_linear(x, w_q, w_scale, group, input_act=None, layout=..., bias=None, residual=None)``
 * ``ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, layout=..., bias=None, residual=None)``
 * ``ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group, layout=...)`` -> y bf16
-* test hooks ``ck_int8_gemm_i32``, ``ck_silu_f32``, ``ck_act_rotate_f32``
+* W8A16 (BF16 activations, INT8 weights in the blocked layout):
+  ``ck_act_rotate_bf16``, ``ck_w8a16_gemm_bf16``, ``ck_int8_linear_w8a16``,
+  ``ck_swiglu_mlp_w8a16``
+* test hooks ``ck_int8_gemm_i32``, ``ck_w8a16_gemm_f32``, ``ck_silu_f32``, ``ck_act_rotate_f32``
 
 ``layout`` is ``"rows"`` (row-major int8, the serialized checkpoint format),
 ``"blocked"`` (the GEMM-native layout of include/ck.h, rows padded to 256) or
@@ -80,6 +83,11 @@ def bind(path: str) -> ctypes.CDLL:
         "ck_int8_gemm_bf16": [p, p, p, p, p, p, i32, i64, i64, i64, p, p],
         "ck_swiglu_mlp": [p, p, p, p, p, i32, i64, i64, i64, i32, p, p, sz, p],
         "ck_int8_gemm_i32": [p, p, i32, i64, i64, i64, p, p],
+        "ck_act_rotate_bf16": [p, i64, i64, i64, i32, i32, i32, p, p],
+        "ck_w8a16_gemm_bf16": [p, p, p, p, p, i64, i64, i64, p, p],
+        "ck_w8a16_gemm_f32": [p, p, i64, i64, i64, p, p],
+        "ck_int8_linear_w8a16": [p, i64, i32, p, p, p, p, i64, i64, i64, i32, p, p, sz, p],
+        "ck_swiglu_mlp_w8a16": [p, p, p, p, p, i64, i64, i64, i32, p, p, sz, p],
         "ck_silu_f32": [p, i64, p, p],
         "ck_act_rotate_f32": [p, i64, i64, i64, i32, i32, p, p],
     }
@@ -89,6 +97,10 @@ def bind(path: str) -> ctypes.CDLL:
         f.restype = ctypes.c_int
     L.ck_int8_linear_workspace_size.argtypes = [i64, i64]
     L.ck_int8_linear_workspace_size.restype = sz
+    L.ck_int8_linear_w8a16_workspace_size.argtypes = [i64, i64]
+    L.ck_int8_linear_w8a16_workspace_size.restype = sz
+    L.ck_swiglu_mlp_w8a16_workspace_size.argtypes = [i64, i64, i64]
+    L.ck_swiglu_mlp_w8a16_workspace_size.restype = sz
     L.ck_swiglu_mlp_workspace_size.argtypes = [i64, i64, i64]
     L.ck_swiglu_mlp_workspace_size.restype = sz
     L.ck_blocked_rows.argtypes = [i64]
@@ -377,6 +389,109 @@ def ck_int8_gemm_i32(x_q, w_q, layout="rows", m: int | None = None, n: int | Non
     _call("ck_int8_gemm_i32", x_q.data_ptr(), w_q.data_ptr(), lay, m, n, k, acc.data_ptr(),
           _stream(x_q))
     return acc
+
+
+def ck_act_rotate_bf16(x, input_act=None, group: int = 128, k: int | None = None, layout="rows"):
+    """Rotated activation in BF16 (no quantization): [m, k] row-major, or the
+    BF16 blocked layout of include/ck.h as a [blocked_rows(m), k] tensor."""
+    import torch
+    _need(x, torch.bfloat16, 2, "activation")
+    act = _act_code(input_act)
+    lay = _layout_code(layout)
+    m, ldx = x.shape
+    if k is None:
+        k = ldx // 2 if act == CK_ACT_SWIGLU else ldx
+    _check_group(k, group)
+    rows = m if lay == CK_LAYOUT_ROWS else blocked_rows(m)
+    xr = torch.empty((rows, k), dtype=torch.bfloat16, device=x.device)
+    _call("ck_act_rotate_bf16", x.data_ptr(), ldx, m, k, act, group, lay, xr.data_ptr(), _stream(x))
+    return xr
+
+
+def _w8a16_operands(x_rot, w_q, m, n):
+    import torch
+    _need(x_rot, torch.bfloat16, 2, "rotated activation")
+    _need(w_q, torch.int8, 2, "weight")
+    k = x_rot.shape[1]
+    if w_q.shape[1] != k:
+        raise ValueError(f"in_features mismatch: activation {k}, weight {w_q.shape[1]}")
+    _operand_rows(x_rot, m, CK_LAYOUT_BLOCKED, "rotated activation")
+    _operand_rows(w_q, n, CK_LAYOUT_BLOCKED, "weight")
+    return k
+
+
+def ck_w8a16_gemm_bf16(x_rot, w_q, w_scale, m: int, out=None, bias=None, residual=None):
+    """y = bf16(acc * w_scale (+ bias) (+ residual)); x_rot in the BF16 blocked
+    layout with m logical rows, w_q blocked."""
+    import torch
+    n = w_scale.shape[0]
+    _scale(w_scale, n, "weight_scale")
+    k = _w8a16_operands(x_rot, w_q, m, n)
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x_rot.device)
+    bp, rp = _extra(bias, residual, m, n, x_rot.device)
+    _call("ck_w8a16_gemm_bf16", x_rot.data_ptr(), w_q.data_ptr(), w_scale.data_ptr(), bp, rp, m, n, k,
+          y.data_ptr(), _stream(x_rot))
+    return y
+
+
+def ck_w8a16_gemm_f32(x_rot, w_q, m: int, n: int):
+    """Raw FP32 accumulators of the W8A16 GEMM."""
+    import torch
+    k = _w8a16_operands(x_rot, w_q, m, n)
+    acc = torch.empty((m, n), dtype=torch.float32, device=x_rot.device)
+    _call("ck_w8a16_gemm_f32", x_rot.data_ptr(), w_q.data_ptr(), m, n, k, acc.data_ptr(),
+          _stream(x_rot))
+    return acc
+
+
+def ck_int8_linear_w8a16(x, w_q, w_scale, group: int = 128, input_act=None, out=None,
+                         workspace=None, bias=None, residual=None):
+    """W8A16 linear: BF16 rotated activation times the blocked INT8 weight."""
+    import torch
+    _need(x, torch.bfloat16, 2, "activation")
+    _need(w_q, torch.int8, 2, "weight")
+    n = w_scale.shape[0]
+    _scale(w_scale, n, "weight_scale")
+    _operand_rows(w_q, n, CK_LAYOUT_BLOCKED, "weight")
+    k = w_q.shape[1]
+    act = _act_code(input_act)
+    m, ldx = x.shape
+    need_ld = 2 * k if act == CK_ACT_SWIGLU else k
+    if ldx != need_ld:
+        raise ValueError(f"activation needs {need_ld} columns for in_features {k}, got {ldx}")
+    _check_group(k, group)
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    ws_bytes = lib().ck_int8_linear_w8a16_workspace_size(m, k)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    bp, rp = _extra(bias, residual, m, n, x.device)
+    _call("ck_int8_linear_w8a16", x.data_ptr(), ldx, act, w_q.data_ptr(), w_scale.data_ptr(), bp, rp,
+          m, n, k, group, y.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x))
+    return y
+
+
+def ck_swiglu_mlp_w8a16(x, w_gu, s_gu, w_down, s_down, group: int = 128, out=None, workspace=None):
+    """The SwiGLU MLP block with W8A16 linears; weights in the blocked layout."""
+    import torch
+    _need(x, torch.bfloat16, 2, "activation")
+    m, h = x.shape
+    i2, kg = _weight(w_gu, s_gu, CK_LAYOUT_BLOCKED, "gate_up weight")
+    if kg != h or i2 % 2:
+        raise ValueError(f"gate_up weight needs (2*intermediate, {h}), got ({i2}, {kg})")
+    i = i2 // 2
+    hd, kd = _weight(w_down, s_down, CK_LAYOUT_BLOCKED, "down weight")
+    if kd != i or hd != h:
+        raise ValueError(f"down weight needs ({h}, {i}), got ({hd}, {kd})")
+    _check_group(h, group)
+    _check_group(i, group)
+    y = out if out is not None else torch.empty((m, h), dtype=torch.bfloat16, device=x.device)
+    ws_bytes = lib().ck_swiglu_mlp_w8a16_workspace_size(m, h, i)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    _call("ck_swiglu_mlp_w8a16", x.data_ptr(), w_gu.data_ptr(), s_gu.data_ptr(), w_down.data_ptr(),
+          s_down.data_ptr(), m, h, i, group, y.data_ptr(), workspace.data_ptr(), workspace.numel(),
+          _stream(x))
+    return y
 
 
 def ck_silu_f32(gate):

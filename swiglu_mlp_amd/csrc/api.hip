@@ -283,6 +283,124 @@ ck_status ck_swiglu_mlp(const uint16_t* x, const int8_t* w_gu, const float* s_gu
     return from_hip(ck::launch_gemm_bf16(hq, sh, w_down, s_down, m, h, i, y, layout, st));
 }
 
+// ---- W8A16 ----------------------------------------------------------------
+
+ck_status ck_act_rotate_bf16(const uint16_t* x, int64_t ldx, int64_t m, int64_t k, int32_t act,
+                             int32_t group, int32_t layout, uint16_t* x_rot, void* stream)
+{
+    CK_TRY(check_k(k, group));
+    CK_TRY(check_act(act, ldx, k));
+    CK_TRY(check_layout(layout));
+    if (m < 0) return CK_ESHAPE;
+    if (pad_rows(m) * k * 2 > CK_MAX_ELEMS) return CK_EUNSUPPORTED;
+    if (m == 0) return CK_OK;
+    if (!x || !x_rot) return CK_EINVAL;
+    if (!aligned16(x) || !aligned16(x_rot)) return CK_EINVAL;
+    return from_hip(ck::launch_rotate_bf16(act == CK_ACT_SWIGLU ? 1 : 0, x, ldx, m, k, group, x_rot,
+                                           layout == CK_LAYOUT_BLOCKED, (hipStream_t)stream));
+}
+
+static ck_status check_w8a16_args(const uint16_t* x_rot, const int8_t* w_q, int64_t m, int64_t n,
+                                  int64_t k, const void* y)
+{
+    if (k < 1 || k % 64 != 0) return CK_ESHAPE;
+    if (k > CK_MAX_K) return CK_EUNSUPPORTED;
+    if (m < 0 || n < 0 || n % 16 != 0) return CK_ESHAPE;
+    CK_TRY(check_gemm_extent(m, n, k));
+    if (pad_rows(m) * k * 2 > CK_MAX_ELEMS) return CK_EUNSUPPORTED;
+    if (m == 0 || n == 0) return CK_OK;
+    if (!x_rot || !w_q || !y) return CK_EINVAL;
+    if (!aligned16(x_rot) || !aligned16(w_q) || !aligned16(y)) return CK_EINVAL;
+    return CK_OK;
+}
+
+ck_status ck_w8a16_gemm_bf16(const uint16_t* x_rot, const int8_t* w_q, const float* w_scale,
+                             const float* bias, const uint16_t* residual, int64_t m, int64_t n,
+                             int64_t k, uint16_t* y, void* stream)
+{
+    CK_TRY(check_w8a16_args(x_rot, w_q, m, n, k, y));
+    if (m == 0 || n == 0) return CK_OK;
+    if (!w_scale || !aligned16(w_scale)) return CK_EINVAL;
+    CK_TRY(check_extra(bias, residual));
+    return from_hip(ck::launch_gemm_w8a16(x_rot, w_q, w_scale, m, n, k, y, false, (hipStream_t)stream,
+                                          ck::EpiExtra{bias, residual}));
+}
+
+ck_status ck_w8a16_gemm_f32(const uint16_t* x_rot, const int8_t* w_q, int64_t m, int64_t n,
+                            int64_t k, float* acc, void* stream)
+{
+    CK_TRY(check_w8a16_args(x_rot, w_q, m, n, k, acc));
+    if (m == 0 || n == 0) return CK_OK;
+    return from_hip(ck::launch_gemm_w8a16(x_rot, w_q, nullptr, m, n, k, acc, true, (hipStream_t)stream));
+}
+
+size_t ck_int8_linear_w8a16_workspace_size(int64_t m, int64_t k)
+{
+    if (m <= 0 || k <= 0) return 0;
+    return round_up((size_t)pad_rows(m) * (size_t)k * 2);
+}
+
+ck_status ck_int8_linear_w8a16(const uint16_t* x, int64_t ldx, int32_t act, const int8_t* w_q,
+                               const float* w_scale, const float* bias, const uint16_t* residual,
+                               int64_t m, int64_t n, int64_t k, int32_t group, uint16_t* y,
+                               void* workspace, size_t workspace_bytes, void* stream)
+{
+    CK_TRY(check_k(k, group));
+    CK_TRY(check_act(act, ldx, k));
+    CK_TRY(check_w8a16_args(reinterpret_cast<const uint16_t*>(x), w_q, m, n, k, y));
+    if (m == 0 || n == 0) return CK_OK;
+    if (!w_scale || !aligned16(w_scale)) return CK_EINVAL;
+    CK_TRY(check_extra(bias, residual));
+    const size_t need = ck_int8_linear_w8a16_workspace_size(m, k);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
+        return CK_EWORKSPACE;
+    uint16_t* xr = static_cast<uint16_t*>(workspace);
+    hipStream_t st = (hipStream_t)stream;
+    CK_TRY(from_hip(ck::launch_rotate_bf16(act == CK_ACT_SWIGLU ? 1 : 0, x, ldx, m, k, group, xr, true, st)));
+    return from_hip(ck::launch_gemm_w8a16(xr, w_q, w_scale, m, n, k, y, false, st,
+                                          ck::EpiExtra{bias, residual}));
+}
+
+// x rotated (BF16 blocked), the [m, 2i] BF16 gate|up output, its SwiGLU'd
+// rotation (BF16 blocked).
+size_t ck_swiglu_mlp_w8a16_workspace_size(int64_t m, int64_t h, int64_t i)
+{
+    if (m <= 0 || h <= 0 || i <= 0) return 0;
+    const size_t M = (size_t)m, MP = (size_t)pad_rows(m), H = (size_t)h, I = (size_t)i;
+    return round_up(MP * H * 2) + round_up(M * 2 * I * 2) + round_up(MP * I * 2);
+}
+
+ck_status ck_swiglu_mlp_w8a16(const uint16_t* x, const int8_t* w_gu, const float* s_gu,
+                              const int8_t* w_down, const float* s_down, int64_t m, int64_t h,
+                              int64_t i, int32_t group, uint16_t* y, void* workspace,
+                              size_t workspace_bytes, void* stream)
+{
+    CK_TRY(check_k(h, group));
+    CK_TRY(check_k(i, group));
+    if (m < 0 || h % 16 != 0) return CK_ESHAPE;
+    CK_TRY(check_gemm_extent(m, 2 * i, h));
+    CK_TRY(check_gemm_extent(m, h, i));
+    if (pad_rows(m) * h * 2 > CK_MAX_ELEMS || pad_rows(m) * i * 2 > CK_MAX_ELEMS) return CK_EUNSUPPORTED;
+    if (m == 0) return CK_OK;
+    if (!x || !w_gu || !w_down || !y || !s_gu || !s_down) return CK_EINVAL;
+    if (!aligned16(x) || !aligned16(w_gu) || !aligned16(w_down) || !aligned16(y) || !aligned16(s_gu) ||
+        !aligned16(s_down))
+        return CK_EINVAL;
+    const size_t need = ck_swiglu_mlp_w8a16_workspace_size(m, h, i);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
+        return CK_EWORKSPACE;
+    const size_t M = (size_t)m, MP = (size_t)pad_rows(m), H = (size_t)h, I = (size_t)i;
+    char* p = static_cast<char*>(workspace);
+    uint16_t* xr = reinterpret_cast<uint16_t*>(p);      p += round_up(MP * H * 2);
+    uint16_t* y1 = reinterpret_cast<uint16_t*>(p);      p += round_up(M * 2 * I * 2);
+    uint16_t* hr = reinterpret_cast<uint16_t*>(p);
+    hipStream_t st = (hipStream_t)stream;
+    CK_TRY(from_hip(ck::launch_rotate_bf16(0, x, h, m, h, group, xr, true, st)));
+    CK_TRY(from_hip(ck::launch_gemm_w8a16(xr, w_gu, s_gu, m, 2 * i, h, y1, false, st)));
+    CK_TRY(from_hip(ck::launch_rotate_bf16(1, y1, 2 * i, m, i, group, hr, true, st)));
+    return from_hip(ck::launch_gemm_w8a16(hr, w_down, s_down, m, h, i, y, false, st));
+}
+
 ck_status ck_silu_f32(const uint16_t* gate, int64_t n, float* out, void* stream)
 {
     if (n < 0) return CK_ESHAPE;

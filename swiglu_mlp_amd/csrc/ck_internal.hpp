@@ -18,6 +18,12 @@ namespace ck {
 hipError_t launch_quant_rows(int kind, const void* src, int64_t ld, int64_t m, int64_t k, int g,
                              int8_t* q, float* s, float* u_out, bool blocked, hipStream_t st);
 
+// Rotation of m rows of k values (kind 0 or 1 as above) to BF16
+// x_rot = bf16(fl(u * fl(1/sqrt(g)))), u the unnormalised blockwise FWHT;
+// written row-major [m, k] or, blocked, in the BF16 blocked layout.
+hipError_t launch_rotate_bf16(int kind, const void* src, int64_t ld, int64_t m, int64_t k, int g,
+                              uint16_t* out, bool blocked, hipStream_t st);
+
 // Row-major [n, k] int8 -> blocked layout, padding rows zero-filled.
 hipError_t launch_pack_blocked(const int8_t* w, int64_t n, int64_t k, int8_t* out, hipStream_t st);
 
@@ -40,6 +46,13 @@ hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t m, int64_
 hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                            int64_t m, int64_t n, int64_t k, void* out, bool out_i32, int num_cu,
                            hipStream_t st, EpiExtra ex = EpiExtra{});
+
+// W8A16 GEMM (gemm_blk.hip): x_rot BF16 in the BF16 blocked layout, W INT8
+// blocked; y = bf16(fl(acc * sw[n])) with FP32 accumulation, or (out_f32) the
+// raw FP32 accumulators.
+hipError_t launch_gemm_w8a16(const uint16_t* x_rot, const int8_t* wq, const float* sw, int64_t m,
+                             int64_t n, int64_t k, void* out, bool out_f32, hipStream_t st,
+                             EpiExtra ex = EpiExtra{});
 
 // Blocked-layout GEMM for m <= 64 (gemm_small.hip): streams the weights once.
 // decode: W in the decode layout (sw unused).

@@ -51,7 +51,10 @@ namespace ck {
 namespace blk {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -74,19 +77,38 @@ __device__ __forceinline__ void workgroup_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <int BM_, int BN_>
+// A16: the X operand is BF16 (2 bytes per k) in the BF16 blocked layout and
+// the INT8 W fragments are widened to BF16 in registers (W8A16); the stage
+// then holds twice the X bytes, and the ring has 3 slots, 2 stages ahead.
+template <int BM_, int BN_, bool A16>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_;
-    static constexpr int NBUF = 4, P = 3;          // LDS ring, stages in flight
+    static constexpr int XS = A16 ? 2 : 1;         // X bytes per k
+    static constexpr int NBUF = A16 ? 3 : 4;       // LDS ring slots
+    static constexpr int P = NBUF - 1;             // stages in flight
     static constexpr int FM = BM / 64;             // fragments per wave along m
     static constexpr int FN = BN / 64;             // fragments per wave along n
     static constexpr int A_BLK = (BN / 32) * 2;    // W blocks per stage
-    static constexpr int B_BLK = (BM / 32) * 2;    // X blocks per stage
+    static constexpr int B_BLK = (BM / 32) * 2 * XS;   // X blocks per stage
     static constexpr int BLK = A_BLK + B_BLK;
     static constexpr int L = BLK / 4;              // block loads per lane per stage
     static constexpr int STAGE = BLK * 1024;
     static_assert(BLK % 4 == 0, "blocks must split evenly over 4 waves");
 };
+
+// 8 INT8 weight codes -> 8 BF16 values (exact: |q| <= 127 has 7 significant
+// bits); one v_cvt_f32_i32 (byte select, sign-extended) per value and one
+// v_cvt_pk_bf16_f32 per pair.
+__device__ __forceinline__ v8bf widen8(int lo, int hi)
+{
+    v8bf r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int w = e < 4 ? lo : hi;
+        r[e] = (__bf16)(float)(int)(signed char)(w >> (8 * (e & 3)));
+    }
+    return r;
+}
 
 __device__ __forceinline__ void tile_coords(int j, int tiles_m, int tiles_n, int group_m, int& tm,
                                             int& tn)
@@ -125,7 +147,10 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes)
 
 // EXTRA: the epilogue adds the optional bias / residual (a separate
 // instantiation, so the plain epilogue carries no branches for them).
-template <int BM, int BN, bool OUT_I32, bool EXTRA>
+// A16 (W8A16): xq points to BF16 values, the accumulators are FP32, the
+// epilogue is y = bf16(fl(acc * sw[n])) (sx unused), and OUT_I32 writes the
+// raw FP32 accumulators.
+template <int BM, int BN, bool OUT_I32, bool EXTRA, bool A16>
 __global__ __launch_bounds__(256) void gemm_blk_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
     const float* __restrict__ sw, int M, int N, int K, int m_rows, int n_rows, void* __restrict__ out,
@@ -134,7 +159,8 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     // The body uses AMDGPU-only types (buffer resources); the host pass only
     // needs this function's launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
-    using C = Cfg<BM, BN>;
+    using C = Cfg<BM, BN, A16>;
+    using AccT = std::conditional_t<A16, v16f, v16i>;
     // LDS: the 4-slot operand ring, then two scale buffers (tile q uses
     // buffer q % 2), each 1 KB of row scales sx then 1 KB of column scales sw.
     // one tile's sx and sw (and, with EXTRA, its bias) in LDS, 1 KB each
@@ -142,15 +168,15 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE + 2 * SCALES];
     constexpr int AW = C::A_BLK / 4;   // W blocks each wave loads per stage
     constexpr int XW = C::B_BLK / 4;   // X blocks each wave loads per stage
-    constexpr int NMF = C::FN * C::FM; // MFMAs per wave per k-slice
-    constexpr int NDS = C::FN + C::FM; // fragment reads per wave per k-slice
+    constexpr int NMF = C::FN * C::FM; // fragment pairs (MFMA steps) per wave per k-slice
+    constexpr int NDS = C::FN + C::FM * C::XS; // fragment reads per wave per k-slice
     // steps of the two halves of a stage (small tiles have fewer MFMAs than
     // reads or loads)
     // BF16 stores per wave in one epilogue (two 16-byte stores per fragment).
     // The int32 variant issues more than the vmcnt field can express and is
     // waited for in full.
     constexpr int NST = OUT_I32 ? 0 : 2 * NMF;
-    static_assert(2 * C::L + 1 + NST < 64, "vmcnt range");
+    static_assert((C::P - 1) * C::L + 1 + NST < 64, "vmcnt range");
     constexpr int STEPS1 = NMF > NDS ? NMF : NDS;
     constexpr int STEPS0 = STEPS1 > AW + XW ? STEPS1 : AW + XW;
 
@@ -161,7 +187,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     const int b = blockIdx.x;
     const int tiles = tiles_m * tiles_n;
     const int KT = K / 64;          // stages per tile
-    const int KB = K / 32;          // k-slices (blocks) per 32-row block
+    const int KB = K / 32;          // k-slices per 32-row block (W: 1 KB, X: XS KB each)
     const int my_tiles = (tiles - b + G - 1) / G;
     const int total = my_tiles * KT;
     if (total == 0) return;
@@ -177,9 +203,10 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     // Operand buffers span the padded row counts m_rows, n_rows (multiples of
     // 256), so every block a tile touches is inside the buffer.
     const v4i rs_w = make_rsrc(wq, (uint32_t)(n_rows * K));
-    const v4i rs_x = make_rsrc(xq, (uint32_t)(m_rows * K));
-    // scale vectors (absent, so every lane out of range, for the int32 variant)
-    const v4i rs_sx = make_rsrc(sx, OUT_I32 ? 0u : (uint32_t)M * 4u);
+    const v4i rs_x = make_rsrc(xq, (uint32_t)(m_rows * K * C::XS));
+    // scale vectors (absent, so every lane out of range, for the int32
+    // variant; no activation scale in W8A16)
+    const v4i rs_sx = make_rsrc(sx, (OUT_I32 || A16) ? 0u : (uint32_t)M * 4u);
     const v4i rs_sw = make_rsrc(sw, OUT_I32 ? 0u : (uint32_t)N * 4u);
     const v4i rs_b = make_rsrc(ex.bias, (EXTRA && ex.bias) ? (uint32_t)N * 4u : 0u);
     const __amdgpu_buffer_rsrc_t rs_o =
@@ -198,7 +225,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
         int tm, tn;
         tile_coords(tile_of(q), tiles_m, tiles_n, group_m, tm, tn);
         la = (uint32_t)(tn * (BN / 32) * KB) * 1024u;
-        lx = (uint32_t)(tm * (BM / 32) * KB) * 1024u;
+        lx = (uint32_t)(tm * (BM / 32) * KB) * (1024u * C::XS);
     };
     auto advance = [&]() {
         if (ls + 1 < total) {
@@ -210,38 +237,53 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
         }
     };
     // Block a of this wave's share: W block ai = wave * AW + a covers row
-    // block ai / 2, k-slice ai % 2 of the stage (X blocks likewise after the
-    // W blocks in the LDS stage).
+    // block ai / 2, k-slice ai % 2 of the stage.  X blocks follow the W blocks
+    // in the LDS stage: X block bj covers row block bj / (2 XS) and the
+    // bj % (2 XS)-th KB of the stage's 2 XS KB of that row block.
     auto issue_one = [&](int a, uint32_t slot_addr) {
-        const uint32_t kofs = (uint32_t)lkt * 2048u;
         if (a < AW) {
             const int ai = wave * AW + a;
-            const uint32_t off = la + kofs + (uint32_t)((ai >> 1) * KB + (ai & 1)) * 1024u;
+            const uint32_t off = la + (uint32_t)lkt * 2048u + (uint32_t)((ai >> 1) * KB + (ai & 1)) * 1024u;
             lds_dma_b128(rs_w, lane16, off, slot_addr + (uint32_t)ai * 1024u);
         } else {
+            constexpr int XR = 2 * C::XS;   // X blocks per row block per stage
             const int bj = wave * XW + (a - AW);
-            const uint32_t off = lx + kofs + (uint32_t)((bj >> 1) * KB + (bj & 1)) * 1024u;
+            const uint32_t off = lx + (uint32_t)lkt * (2048u * C::XS) +
+                                 (uint32_t)((bj / XR) * KB * C::XS + (bj % XR)) * 1024u;
             lds_dma_b128(rs_x, lane16, off, slot_addr + (uint32_t)(C::A_BLK + bj) * 1024u);
         }
     };
 
-    v16i acc[C::FN][C::FM];
+    AccT acc[C::FN][C::FM];
     const int lr = lane & 31;
     const int lh = lane >> 5;
     const int wm0 = (wave & 1) * (BM / 2);
     const int wn0 = (wave >> 1) * (BN / 2);
     // This wave's fragments of a stage: W fragment i, k-slice ks at block
-    // (wn0 / 32 + i) * 2 + ks; X fragment j at block A_BLK + (wm0 / 32 + j) * 2 + ks.
+    // (wn0 / 32 + i) * 2 + ks; X fragment j, k-slice ks, part h (the XS KB of
+    // one k-slice) at block A_BLK + ((wm0 / 32 + j) * 2 + ks) * XS + h.
     auto frag_a = [&](int buf, int i, int ks) {
         const int blk = ((wn0 >> 5) + i) * 2 + ks;
         return *reinterpret_cast<const v4i*>(smem + buf * C::STAGE + blk * 1024 + lane * 16);
     };
-    auto frag_b = [&](int buf, int j, int ks) {
-        const int blk = C::A_BLK + ((wm0 >> 5) + j) * 2 + ks;
+    auto frag_b = [&](int buf, int j, int ks, int h) {
+        const int blk = C::A_BLK + (((wm0 >> 5) + j) * 2 + ks) * C::XS + h;
         return *reinterpret_cast<const v4i*>(smem + buf * C::STAGE + blk * 1024 + lane * 16);
     };
+    // One k-slice of fragment pair (i, j): one INT8 MFMA, or in W8A16 two BF16
+    // MFMAs over the two 8-byte halves of the W fragment (lane k-bytes 0..7,
+    // then 8..15), matched by the two X parts.
+    auto mfma = [&](const v4i& w, const v4i (&x)[C::XS], const AccT& c) -> AccT {
+        if constexpr (A16) {
+            const AccT t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                widen8(w[0], w[1]), __builtin_bit_cast(v8bf, x[0]), c, 0, 0, 0);
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                widen8(w[2], w[3]), __builtin_bit_cast(v8bf, x[C::XS - 1]), t, 0, 0, 0);
+        } else {
+            return __builtin_amdgcn_mfma_i32_32x32x32_i8(w, x[0], c, 0, 0, 0);
+        }
+    };
 
-    static_assert(C::P == 3 && C::NBUF == 4, "the prologue assumes P = 3, NBUF = 4");
     set_tile(0);
 #pragma unroll
     for (int p = 0; p < C::P; ++p) {
@@ -249,13 +291,15 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
         for (int a = 0; a < AW + XW; ++a) issue_one(a, smem_addr + (uint32_t)(p * C::STAGE));
         advance();
     }
-    wait_vmcnt<2 * C::L>();
+    wait_vmcnt<(C::P - 1) * C::L>();
     workgroup_barrier();
-    v4i fa[C::FN], fb[C::FM];
+    v4i fa[C::FN], fb[C::FM][C::XS];
 #pragma unroll
     for (int i = 0; i < C::FN; ++i) fa[i] = frag_a(0, i, 0);
 #pragma unroll
-    for (int j = 0; j < C::FM; ++j) fb[j] = frag_b(0, j, 0);
+    for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+        for (int h = 0; h < C::XS; ++h) fb[j][h] = frag_b(0, j, 0, h);
 
     // One stage s (ring slot s % 4).  The instruction order inside each half
     // is fixed in source order (sched_barrier): MFMA k, then fragment read k,
@@ -270,11 +314,43 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     // s + 3 (2 L), plus, on a tile's stages kt = 0 and 1, that tile's scale load
     // (1) and, from the second tile on, the previous epilogue's NST stores.
     // A smaller wait count than the number issued after is always safe.
+    // W8A16: the W fragments of a k-slice widened to BF16 (two MFMA operands
+    // each); fragment i + 1 is widened in the shadow of fragment i's MFMAs.
+    v8bf cw[A16 ? C::FN : 1][2];
+    auto widen = [&](const v4i (&w)[C::FN], int i) {
+        if constexpr (A16) {
+            cw[i][0] = widen8(w[i][0], w[i][1]);
+            cw[i][1] = widen8(w[i][2], w[i][3]);
+        }
+    };
+    // MFMA step k of a half: fragment pair (i, j) = (k / FM, k % FM).
+    auto mfma_step = [&](int k, const v4i (&w)[C::FN], const v4i (&x)[C::FM][C::XS], bool zero) {
+        const int i = k / C::FM, j = k % C::FM;
+        const AccT c = zero ? AccT{} : acc[i][j];
+        if constexpr (A16) {
+            if (k == 0) widen(w, 0);
+            const AccT t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cw[i][0], __builtin_bit_cast(v8bf, x[j][0]), c,
+                                                                   0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cw[i][1], __builtin_bit_cast(v8bf, x[j][1]), t,
+                                                                0, 0, 0);
+            if (j == 0 && i + 1 < C::FN) widen(w, i + 1);
+        } else {
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w[i], x[j][0], c, 0, 0, 0);
+        }
+    };
+    // Fragment read r of a half: W fragment r < FN, else X fragment
+    // (r - FN) / XS, part (r - FN) % XS.
+    auto read_step = [&](int r, int buf, int ks, v4i (&w)[C::FN], v4i (&x)[C::FM][C::XS]) {
+        if (r < C::FN) w[r] = frag_a(buf, r, ks);
+        else if (r < NDS) x[(r - C::FN) / C::XS][(r - C::FN) % C::XS] =
+            frag_b(buf, (r - C::FN) / C::XS, ks, (r - C::FN) % C::XS);
+    };
+
     auto stage = [&](int s, int kt, auto first, bool after_epilogue, int tm, int tn, int q) {
-        const int buf = s & 3;
-        const int nbuf = (s + 1) & 3;
-        const uint32_t lslot = smem_addr + (uint32_t)(((s + C::P) & 3) * C::STAGE);
-        v4i ga[C::FN], gb[C::FM];
+        const int buf = (int)((unsigned)s % C::NBUF);
+        const int nbuf = (int)((unsigned)(s + 1) % C::NBUF);
+        const uint32_t lslot = smem_addr + (uint32_t)(((unsigned)(s + C::P) % C::NBUF) * C::STAGE);
+        v4i ga[C::FN], gb[C::FM][C::XS];
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (decltype(first)::value) {
             const uint32_t sbase = smem_addr + (uint32_t)(C::NBUF * C::STAGE + (q & 1) * SCALES);
@@ -296,32 +372,26 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
         }
 #pragma unroll
         for (int k = 0; k < STEPS0; ++k) {
-            const int i = k / C::FM, j = k % C::FM;
-            if (k < NMF)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                    fa[i], fb[j], decltype(first)::value ? v16i{} : acc[i][j], 0, 0, 0);
-            if (k < C::FN) ga[k] = frag_a(buf, k, 1);
-            else if (k < NDS) gb[k - C::FN] = frag_b(buf, k - C::FN, 1);
+            if (k < NMF) mfma_step(k, fa, fb, decltype(first)::value);
+            read_step(k, buf, 1, ga, gb);
             if (k < AW + XW) issue_one(k, lslot);
             __builtin_amdgcn_sched_barrier(0);
         }
         advance();
 
         wait_lgkmcnt0();              // this wave's k-slice 1 fragments are in registers
-        if (kt <= 1) {
-            if (after_epilogue) wait_vmcnt<2 * C::L + 1 + NST>();
-            else wait_vmcnt<2 * C::L + 1>();
+        if (kt <= C::P - 2) {
+            if (after_epilogue) wait_vmcnt<(C::P - 1) * C::L + 1 + NST>();
+            else wait_vmcnt<(C::P - 1) * C::L + 1>();
         } else {
-            wait_vmcnt<2 * C::L>();
+            wait_vmcnt<(C::P - 1) * C::L>();
         }
-        workgroup_barrier();          // ... for every wave; slot s % 4 is no longer read
+        workgroup_barrier();          // ... for every wave; slot s % NBUF is no longer read
 
 #pragma unroll
         for (int k = 0; k < STEPS1; ++k) {
-            const int i = k / C::FM, j = k % C::FM;
-            if (k < NMF) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ga[i], gb[j], acc[i][j], 0, 0, 0);
-            if (k < C::FN) fa[k] = frag_a(nbuf, k, 0);
-            else if (k < NDS) fb[k - C::FN] = frag_b(nbuf, k - C::FN, 0);
+            if (k < NMF) mfma_step(k, ga, gb, false);
+            read_step(k, nbuf, 0, fa, fb);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -364,7 +434,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
 #pragma unroll
         for (int j = 0; j < C::FM; ++j) {
             sxm[j] = 0.0f;
-            if constexpr (!OUT_I32) sxm[j] = *reinterpret_cast<const float*>(sc + (wm0 + lr + 32 * j) * 4);
+            if constexpr (!OUT_I32 && !A16) sxm[j] = *reinterpret_cast<const float*>(sc + (wm0 + lr + 32 * j) * 4);
         }
 #pragma unroll
         for (int i = 0; i < C::FN; ++i) {
@@ -383,7 +453,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
                 // them up front (the empty asm statements pin the copy between
                 // the previous fragment's stores and this fragment's math)
                 asm volatile("" : "+a"(acc[i][j]));
-                v16i f = acc[i][j];
+                AccT f = acc[i][j];
                 asm volatile("" : "+v"(f));
                 const uint32_t row = (uint32_t)(m_base + 32 * j) * (uint32_t)N;
                 if constexpr (OUT_I32) {
@@ -391,17 +461,27 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
                     for (int qd = 0; qd < 4; ++qd) {
                         const int n = n_base + 32 * i + 8 * qd;
                         const uint32_t ob = n < N ? (row + (uint32_t)n) * 4u : 0x80000000u;
-                        const v4i d = {f[4 * qd], f[4 * qd + 1], f[4 * qd + 2], f[4 * qd + 3]};
+                        const v4i d = __builtin_bit_cast(
+                            v4i, (std::conditional_t<A16, float4, int4>){f[4 * qd], f[4 * qd + 1], f[4 * qd + 2],
+                                                                         f[4 * qd + 3]});
                         __builtin_amdgcn_raw_buffer_store_b128(d, rs_o, ob, 0, 0);
                     }
                 } else {
                     uint32_t w[4][2];
 #pragma unroll
                     for (int qd = 0; qd < 4; ++qd) {
-                        float y0 = ((float)f[4 * qd + 0] * sxm[j]) * s4[qd].x;
-                        float y1 = ((float)f[4 * qd + 1] * sxm[j]) * s4[qd].y;
-                        float y2 = ((float)f[4 * qd + 2] * sxm[j]) * s4[qd].z;
-                        float y3 = ((float)f[4 * qd + 3] * sxm[j]) * s4[qd].w;
+                        float y0, y1, y2, y3;
+                        if constexpr (A16) {
+                            y0 = f[4 * qd + 0] * s4[qd].x;
+                            y1 = f[4 * qd + 1] * s4[qd].y;
+                            y2 = f[4 * qd + 2] * s4[qd].z;
+                            y3 = f[4 * qd + 3] * s4[qd].w;
+                        } else {
+                            y0 = ((float)f[4 * qd + 0] * sxm[j]) * s4[qd].x;
+                            y1 = ((float)f[4 * qd + 1] * sxm[j]) * s4[qd].y;
+                            y2 = ((float)f[4 * qd + 2] * sxm[j]) * s4[qd].z;
+                            y3 = ((float)f[4 * qd + 3] * sxm[j]) * s4[qd].w;
+                        }
                         if constexpr (EXTRA) {
                             // selects, not branches (an absent term must not
                             // turn -0 into +0)
@@ -445,7 +525,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
         tile_coords(tile_of(q), tiles_m, tiles_n, group_m, tm, tn);
         stage(s++, 0, std::true_type{}, q > 0, tm, tn, q);
         for (int kt = 1; kt < KT; ++kt) stage(s++, kt, std::false_type{}, q > 0, tm, tn, q);
-        if (KT < 3) {
+        if (KT < C::P) {
             // the scale load is otherwise covered by the waits of stages 2+
             wait_vmcnt<0>();
             workgroup_barrier();
@@ -456,24 +536,25 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int BM, int BN, bool I32, bool EXTRA>
-hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int M, int N,
+template <int BM, int BN, bool I32, bool EXTRA, bool A16>
+hipError_t launch(const void* xq, const float* sx, const int8_t* wq, const float* sw, int M, int N,
                   int K, void* out, int num_cu, hipStream_t st, EpiExtra ex)
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
-    // LDS per workgroup: 4 stages of (BM + BN) x 64 bytes and two 2 KB scale
-    // buffers; 160 KB per CU.
-    const int lds = 4 * (BM + BN) * 64 + (EXTRA ? 6144 : 4096);
+    // LDS per workgroup: the stage ring and two scale buffers; 160 KB per CU.
+    using C = Cfg<BM, BN, A16>;
+    const int lds = C::NBUF * C::STAGE + (EXTRA ? 6144 : 4096);
     const int per_cu = (160 * 1024) / lds >= 2 ? 2 : 1;
     const int slots = num_cu * per_cu;
     const int grid = tiles < slots ? tiles : slots;
     const int group_m = tiles_m < 4 ? tiles_m : 4;
     const int m_rows = (M + 255) / 256 * 256;
     const int n_rows = (N + 255) / 256 * 256;
-    hipLaunchKernelGGL((gemm_blk_kernel<BM, BN, I32, EXTRA>), dim3(grid), dim3(256), 0, st, xq, sx, wq, sw, M,
-                       N, K, m_rows, n_rows, out, tiles_m, tiles_n, group_m, ex);
+    hipLaunchKernelGGL((gemm_blk_kernel<BM, BN, I32, EXTRA, A16>), dim3(grid), dim3(256), 0, st,
+                       static_cast<const int8_t*>(xq), sx, wq, sw, M, N, K, m_rows, n_rows, out, tiles_m,
+                       tiles_n, group_m, ex);
     return hipGetLastError();
 }
 
@@ -484,25 +565,21 @@ hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const flo
 // eff, where a round is one tile per workgroup slot and per_cu workgroups
 // share a CU.  The efficiencies are measured (MI355X, random INT8 data):
 // 4096^3 takes 62 us with 256 x 256 tiles, 69 us with 128 x 128, 90 us with
-// 64 x 128.  Shapes with `on` false are built but not chosen.
-hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                           int64_t m, int64_t n, int64_t k, void* out, bool out_i32, int num_cu,
-                           hipStream_t st, EpiExtra ex)
+// 64 x 128.  The W8A16 variant uses the same table.
+namespace {
+
+int choose_shape(int64_t m, int64_t n, int num_cu)
 {
     struct Shape {
         int bm, bn, per_cu;
         double eff;
-        bool on;
     };
     static constexpr Shape shapes[] = {
-        {128, 128, 2, 0.90, true}, {64, 128, 2, 0.70, true}, {256, 256, 1, 1.00, true},
-        {256, 192, 1, 0.97, true},
+        {128, 128, 2, 0.90}, {64, 128, 2, 0.70}, {256, 256, 1, 1.00}, {256, 192, 1, 0.97},
     };
-    constexpr int n_shapes = sizeof(shapes) / sizeof(shapes[0]);
     int best = 0;
     double best_t = 0;
-    for (int c = 0; c < n_shapes; ++c) {
-        if (!shapes[c].on) continue;
+    for (int c = 0; c < 4; ++c) {
         const int64_t tiles = ((m + shapes[c].bm - 1) / shapes[c].bm) * ((n + shapes[c].bn - 1) / shapes[c].bn);
         const int64_t slots = (int64_t)num_cu * shapes[c].per_cu;
         const int64_t rounds = (tiles + slots - 1) / slots;
@@ -512,19 +589,42 @@ hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, 
             best_t = t;
         }
     }
+    return best;
+}
+
+template <bool A16>
+hipError_t launch_shape(const void* xq, const float* sx, const int8_t* wq, const float* sw, int64_t m,
+                        int64_t n, int64_t k, void* out, bool out_raw, int num_cu, hipStream_t st,
+                        EpiExtra ex)
+{
     const int M = (int)m, N = (int)n, K = (int)k;
-#define CK_BLK(BM_, BN_)                                                                          \
-    return out_i32 ? blk::launch<BM_, BN_, true, false>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex) \
-           : (ex.bias || ex.res)                                                                   \
-               ? blk::launch<BM_, BN_, false, true>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex)  \
-               : blk::launch<BM_, BN_, false, false>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex)
-    switch (best) {
+#define CK_BLK(BM_, BN_)                                                                               \
+    return out_raw ? blk::launch<BM_, BN_, true, false, A16>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex) \
+           : (ex.bias || ex.res)                                                                        \
+               ? blk::launch<BM_, BN_, false, true, A16>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex)  \
+               : blk::launch<BM_, BN_, false, false, A16>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex)
+    switch (choose_shape(m, n, num_cu)) {
         case 0: CK_BLK(128, 128);
         case 1: CK_BLK(64, 128);
         case 2: CK_BLK(256, 256);
         default: CK_BLK(256, 192);
     }
 #undef CK_BLK
+}
+
+}  // namespace
+
+hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                           int64_t m, int64_t n, int64_t k, void* out, bool out_i32, int num_cu,
+                           hipStream_t st, EpiExtra ex)
+{
+    return launch_shape<false>(xq, sx, wq, sw, m, n, k, out, out_i32, num_cu, st, ex);
+}
+
+hipError_t launch_gemm_w8a16(const uint16_t* x_rot, const int8_t* wq, const float* sw, int64_t m,
+                             int64_t n, int64_t k, void* out, bool out_f32, hipStream_t st, EpiExtra ex)
+{
+    return launch_shape<true>(x_rot, nullptr, wq, sw, m, n, k, out, out_f32, num_cus(), st, ex);
 }
 
 }  // namespace ck

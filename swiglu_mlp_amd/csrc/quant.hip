@@ -33,10 +33,23 @@ __device__ __forceinline__ int64_t blocked_offset(int row, int c, int kb)
            (c & 1) * 8;
 }
 
-template <int KIND, int LOG_G, int CH, bool ROT_OUT, bool BLOCKED>
+// Byte offset of BF16 values (row, 8c .. 8c+7) in the BF16 blocked layout
+// (include/ck.h): 2 KB per (row / 32, k / 32), inside it the MFMA step
+// (k % 16) / 8, then the half (k % 32) / 16, the row within the block, k % 8.
+__device__ __forceinline__ int64_t blocked_bf16_offset(int row, int c, int kb)
+{
+    return ((int64_t)(row >> 5) * kb + (c >> 2)) * 2048 + (c & 1) * 1024 + ((c >> 1) & 1) * 512 +
+           (row & 31) * 16;
+}
+
+// What the kernel writes: INT8 codes and row scales, the unnormalised rotated
+// row in FP32 (a diagnostic), or the normalised rotated row in BF16.
+enum OutKind { OUT_CODES = 0, OUT_ROT_F32 = 1, OUT_ROT_BF16 = 2 };
+
+template <int KIND, int LOG_G, int CH, int OUT, bool BLOCKED>
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const void* __restrict__ src, int64_t ld, int m, int k, int log_t, float cg,
-    int8_t* __restrict__ q, float* __restrict__ s, float* __restrict__ u_out)
+    int8_t* __restrict__ q, float* __restrict__ s, void* __restrict__ u_out)
 {
     constexpr int G = 1 << LOG_G;
     const int T = 1 << log_t;
@@ -128,8 +141,23 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
     }
 
-    if constexpr (ROT_OUT) {
-        float* up = u_out + (int64_t)row * k;
+    if constexpr (OUT == OUT_ROT_BF16) {
+        // x_rot = bf16(fl(u * c_g)): the rotation with the orthonormal H
+        char* ob = static_cast<char*>(u_out);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = j * T + t;
+            const uint4 w = make_uint4(pack_bf16x2(v[j][0] * cg, v[j][1] * cg), pack_bf16x2(v[j][2] * cg, v[j][3] * cg),
+                                       pack_bf16x2(v[j][4] * cg, v[j][5] * cg), pack_bf16x2(v[j][6] * cg, v[j][7] * cg));
+            if (row_ok && c < k8) {
+                const int64_t off = BLOCKED ? blocked_bf16_offset(row, c, k >> 5) : ((int64_t)row * k + c * 8) * 2;
+                *reinterpret_cast<uint4*>(ob + off) = w;
+            }
+        }
+        return;
+    }
+    if constexpr (OUT == OUT_ROT_F32) {
+        float* up = static_cast<float*>(u_out) + (int64_t)row * k;
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             const int c = j * T + t;
@@ -262,14 +290,14 @@ bool choose_team(int k, int g, int* log_t, int* ch)
     return best >= 0;
 }
 
-template <int KIND, int LOG_G, bool ROT_OUT, bool BLOCKED>
+template <int KIND, int LOG_G, int OUT, bool BLOCKED>
 hipError_t launch_ch(int ch, dim3 grid, hipStream_t st, const void* src, int64_t ld, int m, int k,
-                     int log_t, float cg, int8_t* q, float* s, float* u)
+                     int log_t, float cg, int8_t* q, float* s, void* u)
 {
     switch (ch) {
 #define CK_CASE(C)                                                                              \
     case C:                                                                                     \
-        hipLaunchKernelGGL((quant_rows_kernel<KIND, LOG_G, C, ROT_OUT, BLOCKED>), grid, dim3(256), 0, st, \
+        hipLaunchKernelGGL((quant_rows_kernel<KIND, LOG_G, C, OUT, BLOCKED>), grid, dim3(256), 0, st, \
                            src, ld, m, k, log_t, cg, q, s, u);                                  \
         break;
         CK_CASE(1) CK_CASE(2) CK_CASE(3) CK_CASE(4) CK_CASE(6) CK_CASE(8) CK_CASE(12) CK_CASE(16)
@@ -279,17 +307,46 @@ hipError_t launch_ch(int ch, dim3 grid, hipStream_t st, const void* src, int64_t
     return hipGetLastError();
 }
 
-template <int KIND, bool ROT_OUT, bool BLOCKED>
+template <int KIND, int OUT, bool BLOCKED>
 hipError_t launch_g(int log_g, int ch, dim3 grid, hipStream_t st, const void* src, int64_t ld, int m,
-                    int k, int log_t, float cg, int8_t* q, float* s, float* u)
+                    int k, int log_t, float cg, int8_t* q, float* s, void* u)
 {
     switch (log_g) {
 #define CK_G(L) \
-    case L: return launch_ch<KIND, L, ROT_OUT, BLOCKED>(ch, grid, st, src, ld, m, k, log_t, cg, q, s, u);
+    case L: return launch_ch<KIND, L, OUT, BLOCKED>(ch, grid, st, src, ld, m, k, log_t, cg, q, s, u);
         CK_G(0) CK_G(1) CK_G(2) CK_G(3) CK_G(4) CK_G(5) CK_G(6) CK_G(7) CK_G(8)
 #undef CK_G
         default: return hipErrorInvalidValue;
     }
+}
+
+}  // namespace
+
+namespace {
+
+struct Launch {
+    dim3 grid;
+    int log_t, ch, log_g, m, k;
+    float cg;
+};
+
+bool plan(int64_t m, int64_t k, int g, bool blocked, Launch* p)
+{
+    if (!choose_team((int)k, g, &p->log_t, &p->ch)) return false;
+    const int rows_per_wg = 256 >> p->log_t;
+    int64_t wgs = (m + rows_per_wg - 1) / rows_per_wg;
+    if (blocked) {
+        // a multiple of 8 S workgroups (see the row mapping in the kernel)
+        const int64_t mult = 8 * (rows_per_wg >= 8 ? 1 : 8 / rows_per_wg);
+        wgs = (wgs + mult - 1) / mult * mult;
+    }
+    p->grid = dim3((unsigned)wgs);
+    p->log_g = 0;
+    while ((1 << p->log_g) < g) ++p->log_g;
+    p->cg = (float)(1.0 / sqrt((double)g));
+    p->m = (int)m;
+    p->k = (int)k;
+    return true;
 }
 
 }  // namespace
@@ -299,33 +356,38 @@ hipError_t launch_quant_rows(int kind, const void* src, int64_t ld, int64_t m, i
                              int8_t* q, float* s, float* u_out, bool blocked, hipStream_t st)
 {
     if (m == 0) return hipSuccess;
-    int log_t = 0, ch = 0;
-    if (!choose_team((int)k, g, &log_t, &ch)) return hipErrorInvalidValue;
-    const int rows_per_wg = 256 >> log_t;
-    int64_t wgs = (m + rows_per_wg - 1) / rows_per_wg;
-    if (blocked) {
-        // a multiple of 8 S workgroups (see the row mapping in the kernel)
-        const int64_t mult = 8 * (rows_per_wg >= 8 ? 1 : 8 / rows_per_wg);
-        wgs = (wgs + mult - 1) / mult * mult;
-    }
-    const dim3 grid((unsigned)wgs);
-    int log_g = 0;
-    while ((1 << log_g) < g) ++log_g;
-    const float cg = (float)(1.0 / sqrt((double)g));
-    const int M = (int)m, K = (int)k;
+    Launch p;
+    if (!plan(m, k, g, blocked && u_out == nullptr, &p)) return hipErrorInvalidValue;
+#define CK_ARGS p.log_g, p.ch, p.grid, st, src, ld, p.m, p.k, p.log_t, p.cg
     if (u_out != nullptr) {
-        if (kind == IN_BF16) return launch_g<IN_BF16, true, false>(log_g, ch, grid, st, src, ld, M, K, log_t, cg, q, s, u_out);
-        if (kind == IN_BF16_SWIGLU) return launch_g<IN_BF16_SWIGLU, true, false>(log_g, ch, grid, st, src, ld, M, K, log_t, cg, q, s, u_out);
+        if (kind == IN_BF16) return launch_g<IN_BF16, OUT_ROT_F32, false>(CK_ARGS, q, s, u_out);
+        if (kind == IN_BF16_SWIGLU) return launch_g<IN_BF16_SWIGLU, OUT_ROT_F32, false>(CK_ARGS, q, s, u_out);
         return hipErrorInvalidValue;
     }
     switch (kind * 2 + (blocked ? 1 : 0)) {
-        case 0: return launch_g<IN_BF16, false, false>(log_g, ch, grid, st, src, ld, M, K, log_t, cg, q, s, nullptr);
-        case 1: return launch_g<IN_BF16, false, true>(log_g, ch, grid, st, src, ld, M, K, log_t, cg, q, s, nullptr);
-        case 2: return launch_g<IN_BF16_SWIGLU, false, false>(log_g, ch, grid, st, src, ld, M, K, log_t, cg, q, s, nullptr);
-        case 3: return launch_g<IN_BF16_SWIGLU, false, true>(log_g, ch, grid, st, src, ld, M, K, log_t, cg, q, s, nullptr);
-        case 4: return launch_g<IN_F32, false, false>(log_g, ch, grid, st, src, ld, M, K, log_t, cg, q, s, nullptr);
+        case 0: return launch_g<IN_BF16, OUT_CODES, false>(CK_ARGS, q, s, nullptr);
+        case 1: return launch_g<IN_BF16, OUT_CODES, true>(CK_ARGS, q, s, nullptr);
+        case 2: return launch_g<IN_BF16_SWIGLU, OUT_CODES, false>(CK_ARGS, q, s, nullptr);
+        case 3: return launch_g<IN_BF16_SWIGLU, OUT_CODES, true>(CK_ARGS, q, s, nullptr);
+        case 4: return launch_g<IN_F32, OUT_CODES, false>(CK_ARGS, q, s, nullptr);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_rotate_bf16(int kind, const void* src, int64_t ld, int64_t m, int64_t k, int g,
+                              uint16_t* out, bool blocked, hipStream_t st)
+{
+    if (m == 0) return hipSuccess;
+    Launch p;
+    if (!plan(m, k, g, blocked, &p)) return hipErrorInvalidValue;
+    switch (kind * 2 + (blocked ? 1 : 0)) {
+        case 0: return launch_g<IN_BF16, OUT_ROT_BF16, false>(CK_ARGS, nullptr, nullptr, out);
+        case 1: return launch_g<IN_BF16, OUT_ROT_BF16, true>(CK_ARGS, nullptr, nullptr, out);
+        case 2: return launch_g<IN_BF16_SWIGLU, OUT_ROT_BF16, false>(CK_ARGS, nullptr, nullptr, out);
+        case 3: return launch_g<IN_BF16_SWIGLU, OUT_ROT_BF16, true>(CK_ARGS, nullptr, nullptr, out);
+        default: return hipErrorInvalidValue;
+    }
+#undef CK_ARGS
 }
 
 hipError_t launch_pack_blocked(const int8_t* w, int64_t n, int64_t k, int8_t* out, hipStream_t st)

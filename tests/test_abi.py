@@ -187,3 +187,34 @@ def test_binding_is_not_backed_by_the_oracle():
     for path in glob.glob(os.path.join(ROOT, "swiglu_mlp_amd", "**", "*.py"), recursive=True):
         src = open(path).read()
         assert "import oracle" not in src and "from oracle" not in src, path
+
+
+def test_w8a16_checks(L):
+    """W8A16 entry points: shape, null, alignment and workspace checks on the
+    host; nothing here reaches a launch."""
+    r = L.ck_act_rotate_bf16
+    assert r(FAKE, 256, 0, 256, 0, 128, 1, FAKE, None) == OK                 # m == 0
+    assert r(FAKE, 256, 4, 192, 0, 128, 1, FAKE, None) == ESHAPE            # k % group
+    assert r(FAKE, 256, 4, 256, 0, 128, 2, FAKE, None) == EINVAL            # no decode layout
+    assert r(None, 256, 4, 256, 0, 128, 1, FAKE, None) == EINVAL
+    assert r(FAKE, 32768, 70000, 32768, 0, 128, 1, FAKE, None) == EUNSUP    # > 2^31 bytes
+    g = L.ck_w8a16_gemm_bf16
+    assert g(FAKE, FAKE, FAKE, None, None, 4, 20, 256, FAKE, None) == ESHAPE    # n % 16
+    assert g(FAKE, FAKE, FAKE, None, None, 4, 32, 100, FAKE, None) == ESHAPE    # k % 64
+    assert g(FAKE, FAKE, None, None, None, 4, 32, 256, FAKE, None) == EINVAL    # scale
+    assert g(FAKE, FAKE, FAKE, FAKE + 4, None, 4, 32, 256, FAKE, None) == EINVAL
+    assert g(FAKE, FAKE, FAKE, None, FAKE + 2, 4, 32, 256, FAKE, None) == EINVAL
+    assert g(FAKE, FAKE, FAKE, None, None, 0, 32, 256, FAKE, None) == OK
+    assert L.ck_w8a16_gemm_f32(FAKE, None, 4, 32, 256, FAKE, None) == EINVAL
+    assert L.ck_int8_linear_w8a16_workspace_size(3, 256) == 256 * 256 * 2
+    lin = L.ck_int8_linear_w8a16
+    ws = L.ck_int8_linear_w8a16_workspace_size(8, 256)
+    assert lin(FAKE, 256, 0, FAKE, FAKE, None, None, 8, 32, 256, 128, FAKE, FAKE, ws - 1, None) == EWS
+    assert lin(FAKE, 256, 0, FAKE, None, None, None, 8, 32, 256, 128, FAKE, FAKE, ws, None) == EINVAL
+    assert lin(FAKE, 256, 1, FAKE, FAKE, None, None, 8, 32, 256, 128, FAKE, FAKE, ws, None) == ESHAPE
+    mlp = L.ck_swiglu_mlp_w8a16
+    ws = L.ck_swiglu_mlp_w8a16_workspace_size(8, 256, 512)
+    assert ws >= 256 * 256 * 2 + 8 * 1024 * 2 + 256 * 512 * 2
+    assert mlp(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 256, 512, 128, FAKE, FAKE, ws - 256, None) == EWS
+    assert mlp(FAKE, FAKE, None, FAKE, FAKE, 8, 256, 512, 128, FAKE, FAKE, ws, None) == EINVAL
+    assert mlp(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 256, 500, 128, FAKE, FAKE, ws, None) == ESHAPE

@@ -576,3 +576,204 @@ def test_decode_rejects_more_than_64_rows():
     x = torch.zeros((65, 256), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(ck.CKError, match="CK_EUNSUPPORTED"):
         ck.ck_int8_linear(x, wd, None, 128, layout="decode")
+
+
+# ---------------------------------------------------------------------------
+# W8A16: BF16 rotated activations times INT8 weights (comfy-kitchen PR #277,
+# "Notes for the reviewer")
+# ---------------------------------------------------------------------------
+def to_blocked_bf16(a):
+    """Row-major BF16 bits [R, K] -> the BF16 blocked layout of include/ck.h:
+    rows padded to 256 (zeros), 2 KB per (r / 32, k / 32), inside it
+    ((k % 16) / 8, (k % 32) / 16, r % 32, k % 8)."""
+    r, k = a.shape
+    rp = -(-r // 256) * 256
+    p = np.zeros((rp, k), dtype=np.uint16)
+    p[:r] = a
+    return np.ascontiguousarray(
+        p.reshape(rp // 32, 32, k // 32, 2, 2, 8).transpose(0, 2, 4, 3, 1, 5)).reshape(rp, k)
+
+
+def from_blocked_bf16(b, rows):
+    rp, k = b.shape
+    a = b.reshape(rp // 32, k // 32, 2, 2, 32, 8).transpose(0, 4, 1, 3, 2, 5).reshape(rp, k)
+    return np.ascontiguousarray(a[:rows])
+
+
+def w8a16_bound(orc, x_rot, wq, sw, y_ref, k, bias=None, residual=None):
+    """Elementwise bound of the W8A16 result against the oracle: FP32
+    accumulation in any order errs by at most gamma_k * sum|x q| (every product
+    is exact), scaled by s_w; the epilogue's FP32 roundings add 2^-23 of their
+    operands; the two BF16 roundings differ by at most one BF16 ulp."""
+    u = 2.0 ** -24
+    gamma = k * u / (1 - k * u)
+    s_abs = orc.w8a16_abs_acc(x_rot, wq) * sw.astype(np.float64)[None, :]
+    t = np.abs(orc.w8a16_acc(x_rot, wq) * sw.astype(np.float64)[None, :])
+    if bias is not None:
+        t = t + np.abs(bias.astype(np.float64))[None, :]
+    if residual is not None:
+        t = t + np.abs(orc.bf16_to_f32(residual).astype(np.float64))
+    yr = orc.bf16_to_f32(y_ref).astype(np.float64)
+    ulp = np.spacing(np.maximum(np.abs(yr), 1e-38).astype(np.float32)).astype(np.float64) * 65536.0
+    return ulp + gamma * s_abs + 2 * 2.0 ** -23 * t
+
+
+def assert_w8a16_close(orc, got, want, x_rot, wq, sw, k, what, bias=None, residual=None):
+    g = orc.bf16_to_f32(got).astype(np.float64)
+    w = orc.bf16_to_f32(want).astype(np.float64)
+    bound = w8a16_bound(orc, x_rot, wq, sw, want, k, bias, residual)
+    bad = np.abs(g - w) > bound
+    assert not bad.any(), f"{what}: {np.count_nonzero(bad)} elements beyond the FP32-accumulation bound"
+    say(f"{what}: {np.count_nonzero(got != want)} of {got.size} BF16 elements differ by <= bound; "
+        f"relL2 vs oracle {orc.rel_l2(got, w):.2e}")
+
+
+ROTATE_CASES = [  # (m, k, act, g)
+    (1, 256, 0, 128), (37, 384, 1, 128), (300, 1024, 0, 64), (257, 512, 1, 256), (64, 3072, 1, 128),
+]
+
+
+@pytest.mark.parametrize("m,k,act,g", ROTATE_CASES)
+def test_act_rotate_bf16_bit_exact(orc, m, k, act, g):
+    say(f"act_rotate_bf16 m={m} k={k} act={act} g={g}")
+    d = W.case(m, k, 16, act, seed=500 + m)
+    x = bf16_dev(d["x"])
+    want = orc.act_rotate_bf16(d["x"], act, g, k=k)
+    np.testing.assert_array_equal(bf16_host(ck.ck_act_rotate_bf16(x, act, g, k=k)), want)
+    blk = bf16_host(ck.ck_act_rotate_bf16(x, act, g, k=k, layout="blocked"))
+    np.testing.assert_array_equal(from_blocked_bf16(blk, m), want)
+
+
+W8A16_GEMM_SHAPES = [  # (m, n, k): every tile shape, k-stage counts 1, 2, 3 and more,
+    # ragged m and n, a partial last round of tiles
+    (1, 16, 64), (64, 128, 256), (77, 144, 192), (300, 272, 1024), (1000, 1040, 640),
+    (513, 4112, 128), (4000, 4080, 192), (4000, 3056, 320), (2560, 6144, 256), (2048, 1024, 3072),
+]
+
+
+@pytest.mark.parametrize("m,n,k", W8A16_GEMM_SHAPES)
+def test_w8a16_gemm_exact_on_integer_activations(orc, m, n, k):
+    """Integer activations |x| <= 32 with k <= 4096 keep every partial sum below
+    2^24, so FP32 accumulation in any order is exact: accumulators and BF16
+    outputs must equal the oracle bit for bit."""
+    say(f"w8a16 gemm integer activations m={m} n={n} k={k}")
+    rng = np.random.default_rng(3 * m + n + k)
+    xr = orc.f32_to_bf16(rng.integers(-32, 33, size=(m, k)).astype(np.float32))
+    wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    sw = (rng.random(n, dtype=np.float32) * 1e-3).astype(np.float32)
+    xb, wb = bf16_dev(to_blocked_bf16(xr)), dev(to_blocked(wq))
+    acc_o = orc.w8a16_acc(xr, wq)
+    np.testing.assert_array_equal(host(ck.ck_w8a16_gemm_f32(xb, wb, m, n)).astype(np.float64), acc_o)
+    y = bf16_host(ck.ck_w8a16_gemm_bf16(xb, wb, dev(sw), m))
+    np.testing.assert_array_equal(y, orc.w8a16_epilogue(acc_o, sw))
+    bias = rng.standard_normal(n).astype(np.float32)
+    res = orc.f32_to_bf16(rng.standard_normal((m, n)).astype(np.float32))
+    y = bf16_host(ck.ck_w8a16_gemm_bf16(xb, wb, dev(sw), m, bias=dev(bias), residual=bf16_dev(res)))
+    np.testing.assert_array_equal(y, orc.w8a16_epilogue(acc_o, sw, bias, res))
+
+
+W8A16_LINEAR = [  # (m, k, n, act, g)
+    (1, 256, 16, 0, 128), (7, 384, 48, 1, 128), (300, 1024, 272, 1, 128), (129, 512, 320, 0, 64),
+    (200, 768, 96, 1, 256), (1000, 640, 1040, 0, 128), (4000, 256, 4080, 1, 128),
+]
+
+
+@pytest.mark.parametrize("m,k,n,act,g", W8A16_LINEAR)
+def test_int8_linear_w8a16_within_bound(orc, m, k, n, act, g):
+    say(f"int8_linear_w8a16 m={m} k={k} n={n} act={act} g={g}")
+    d = W.case(m, k, n, act, seed=700 + m, zero_rows=(m // 2,) if m > 2 else ())
+    wq_o, sw_o = orc.weight_prep(d["w"], g)
+    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    x = bf16_dev(d["x"])
+    y = bf16_host(ck.ck_int8_linear_w8a16(x, ck.ck_weight_pack(wq), sw, g, act))
+    ref = orc.w8a16_linear(d["x"], act, wq_o, sw_o, g, return_all=True)
+    assert_w8a16_close(orc, y, ref["y"], ref["x_rot"], wq_o, sw_o, k, "w8a16 y")
+    if m > 2:
+        assert not y[m // 2].any()
+    rng = np.random.default_rng(m + n)
+    bias = rng.standard_normal(n).astype(np.float32)
+    res = orc.f32_to_bf16(rng.standard_normal((m, n)).astype(np.float32))
+    y = bf16_host(ck.ck_int8_linear_w8a16(x, ck.ck_weight_pack(wq), sw, g, act, bias=dev(bias),
+                                          residual=bf16_dev(res)))
+    want = orc.w8a16_epilogue(ref["acc"], sw_o, bias, res)
+    assert_w8a16_close(orc, y, want, ref["x_rot"], wq_o, sw_o, k, "w8a16 y + bias + residual",
+                       bias=bias, residual=res)
+
+
+@pytest.mark.parametrize("name", ["c2", "c4"])
+def test_w8a16_full_workload_sampled_rows(orc, name):
+    wl = W.WORKLOADS[name]
+    d = inputs(name)
+    say(f"int8_linear_w8a16 full {name}: {wl.desc}")
+    wq, sw = ck.ck_weight_prep(dev(d["w"]), wl.group)
+    y = ck.ck_int8_linear_w8a16(bf16_dev(d["x"]), ck.ck_weight_pack(wq), sw, wl.group, wl.act)
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.m, seed=3)
+    wq_o, sw_o = prepped(orc, name)
+    ref = orc.w8a16_linear(d["x"][rows], wl.act, wq_o, sw_o, wl.group, return_all=True)
+    assert_w8a16_close(orc, bf16_host(y)[rows], ref["y"], ref["x_rot"], wq_o, sw_o, wl.k,
+                       f"{name} w8a16 sampled rows")
+    y64 = orc.reference_linear_f64(d["x"][rows], wl.act, d["w"])
+    e16 = orc.rel_l2(bf16_host(y)[rows], y64)
+    e8 = orc.rel_l2(orc.int8_linear(d["x"][rows], wl.act, wq_o, sw_o, wl.group), y64)
+    say(f"{name}: relL2 vs float64  w8a16 gpu={e16:.5f}  int8 oracle={e8:.5f}")
+    assert e16 < e8
+
+
+def _mlp_w8a16_check(orc, xb, rows, w_gu_o, s_gu_o, w_d_o, s_d_o, g, y, y1, what):
+    """Stage 1 against the oracle on the same input; stage 2 against the oracle
+    applied to the GPU's own stage-1 output (stage 1 is exact only up to FP32
+    accumulation order, so its rounding differences must not be compounded)."""
+    h = xb.shape[1]
+    i = w_d_o.shape[1]
+    r1 = orc.w8a16_linear(xb[rows], 0, w_gu_o, s_gu_o, g, return_all=True)
+    assert_w8a16_close(orc, y1[rows], r1["y"], r1["x_rot"], w_gu_o, s_gu_o, h, what + " stage 1")
+    r2 = orc.w8a16_linear(y1[rows], 1, w_d_o, s_d_o, g, return_all=True)
+    assert_w8a16_close(orc, y[rows], r2["y"], r2["x_rot"], w_d_o, s_d_o, i, what + " stage 2")
+
+
+def test_swiglu_mlp_w8a16(orc):
+    m, h, i, g = 300, 1024, 2816, 128
+    say(f"swiglu_mlp_w8a16 m={m} h={h} i={i}")
+    rng = np.random.default_rng(91)
+    xb = W.to_bf16_bits(rng.standard_normal((m, h)).astype(np.float32))
+    w_gu = (0.02 * rng.standard_normal((2 * i, h))).astype(np.float32)
+    w_dn = (0.01 * rng.standard_normal((h, i))).astype(np.float32)
+    gq, gs = ck.ck_weight_prep(dev(w_gu), g)
+    dq, ds = ck.ck_weight_prep(dev(w_dn), g)
+    pgu, pd = ck.ck_weight_pack(gq), ck.ck_weight_pack(dq)
+    x = bf16_dev(xb)
+    y = ck.ck_swiglu_mlp_w8a16(x, pgu, gs, pd, ds, g)
+    # the same stages called one by one compose to the block bit for bit
+    y1 = ck.ck_w8a16_gemm_bf16(ck.ck_act_rotate_bf16(x, 0, g, layout="blocked"), pgu, gs, m)
+    y_st = ck.ck_w8a16_gemm_bf16(ck.ck_act_rotate_bf16(y1, 1, g, layout="blocked"), pd, ds, m)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_st.view(torch.int16))
+    (gq_o, gs_o), (dq_o, ds_o) = orc.weight_prep(w_gu, g), orc.weight_prep(w_dn, g)
+    _mlp_w8a16_check(orc, xb, np.arange(m), gq_o, gs_o, dq_o, ds_o, g, bf16_host(y), bf16_host(y1),
+                     "mlp w8a16")
+    y64 = orc.reference_mlp_f64(xb, w_gu, w_dn)
+    e16 = orc.rel_l2(bf16_host(y), y64)
+    e8 = orc.rel_l2(orc.swiglu_mlp(xb, gq_o, gs_o, dq_o, ds_o, g), y64)
+    say(f"mlp: relL2 vs float64  w8a16 gpu={e16:.5f}  int8 oracle={e8:.5f}")
+    assert e16 < e8
+
+
+def test_swiglu_mlp_w8a16_full_c5_sampled_rows(orc):
+    wl = W.WORKLOADS["c5"]
+    d = inputs("c5")
+    say(f"swiglu_mlp_w8a16 full c5: {wl.desc}")
+    g = wl.group
+    gq, gs = ck.ck_weight_prep(dev(d["w_gu"]), g)
+    dq, ds = ck.ck_weight_prep(dev(d["w_down"]), g)
+    pgu, pd = ck.ck_weight_pack(gq), ck.ck_weight_pack(dq)
+    x = bf16_dev(d["x"])
+    y = ck.ck_swiglu_mlp_w8a16(x, pgu, gs, pd, ds, g)
+    y1 = ck.ck_w8a16_gemm_bf16(ck.ck_act_rotate_bf16(x, 0, g, layout="blocked"), pgu, gs, wl.m)
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.m, seed=4)
+    (gq_o, gs_o), (dq_o, ds_o) = prepped(orc, "c5", "w_gu"), prepped(orc, "c5", "w_down")
+    _mlp_w8a16_check(orc, d["x"], rows, gq_o, gs_o, dq_o, ds_o, g, bf16_host(y), bf16_host(y1),
+                     "c5 w8a16")
+    y64 = orc.reference_mlp_f64(d["x"][rows], d["w_gu"], d["w_down"])
+    say(f"c5 w8a16: relL2 vs float64 {orc.rel_l2(bf16_host(y)[rows], y64):.5f}")

@@ -425,3 +425,95 @@ def test_epilogue_error_bound_vs_float64(orc):
     bound = 2.0 ** -8 * np.abs(ref) + 4 * 2.0 ** -24 * (np.abs(t1) + np.abs(b)[None, :] +
                                                        np.abs(ref)) + 1e-30
     assert np.all(np.abs(y - ref) <= bound)
+
+
+# ---------------------------------------------------------------------------
+# W8A16 (comfy-kitchen PR #277, "Notes for the reviewer": the rotated
+# activation kept in 16-bit floating point, the INT8 weight widened on the fly)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("g", [64, 128, 256])
+def test_rotate_bf16_of_a_hadamard_row(orc, g):
+    """x = row j of the unnormalised Sylvester matrix (entries +-1, exact in
+    BF16) rotates to sqrt(g) e_j: u = g e_j exactly, then fl(g * fl(1/sqrt g))."""
+    h = sylvester_kron(g)
+    k = 2 * g
+    x = np.zeros((3, k), dtype=np.float32)
+    js = [0, g // 2 + 1, g - 1]
+    for r, j in enumerate(js):
+        x[r, g:] = h[j]                      # second group only
+    xb = orc.f32_to_bf16(x)
+    got = orc.bf16_to_f32(orc.act_rotate_bf16(xb, 0, g))
+    want = np.zeros((3, k), dtype=np.float32)
+    peak = f32(f32(g) * f32(1.0 / math.sqrt(g)))
+    for r, j in enumerate(js):
+        want[r, g + j] = orc.bf16_to_f32(orc.f32_to_bf16(np.array([peak], np.float32)))[0]
+    np.testing.assert_array_equal(got, want)
+    assert abs(float(want[0, g]) - math.sqrt(g)) <= 2 ** -8 * math.sqrt(g)
+
+
+def test_rotate_bf16_matches_float64_rotation(orc):
+    """Against an independent dense rotation: x @ blockdiag(H_g) / sqrt(g) in
+    float64 (Kronecker-built H), then within half a BF16 ulp plus the FP32
+    transform's rounding."""
+    g, m, k = 128, 16, 512
+    rng = np.random.default_rng(11)
+    xb = orc.f32_to_bf16(rng.standard_normal((m, k)).astype(np.float32))
+    x = orc.bf16_to_f32(xb).astype(np.float64)
+    hd = sylvester_kron(g).astype(np.float64) / math.sqrt(g)
+    ref = (x.reshape(m, k // g, g) @ hd).reshape(m, k)
+    got = orc.bf16_to_f32(orc.act_rotate_bf16(xb, 0, g)).astype(np.float64)
+    rownorm = np.linalg.norm(x, axis=1, keepdims=True)
+    bound = 2.0 ** -8 * np.abs(ref) + 16 * 2.0 ** -24 * rownorm
+    assert np.all(np.abs(got - ref) <= bound)
+
+
+def test_w8a16_acc_matches_int64_matmul(orc):
+    """Small integer activations (exact in BF16): the accumulator is the
+    integer product, computed by numpy int64 matmul."""
+    rng = np.random.default_rng(12)
+    xi = rng.integers(-64, 65, (7, 192))
+    q = rng.integers(-127, 128, (40, 192)).astype(np.int8)
+    xb = orc.f32_to_bf16(xi.astype(np.float32))
+    np.testing.assert_array_equal(orc.w8a16_acc(xb, q), (xi @ q.astype(np.int64).T).astype(np.float64))
+
+
+def test_w8a16_linear_closed_form_on_hadamard_rows(orc):
+    """x = Sylvester row j of one group, g = 256: x_rot = 16 e_j exactly, so
+    y[n] = bf16(f32(16 q[n, j] s_w[n])): checks the rotation index, the
+    orientation of the product and the per-row scale."""
+    g, k, n = 256, 512, 48
+    rng = np.random.default_rng(13)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    q, sw = orc.weight_prep(w, g)
+    h = sylvester_kron(g)
+    j = 37
+    x = np.zeros((1, k), dtype=np.float32)
+    x[0, :g] = h[j]
+    y = orc.w8a16_linear(orc.f32_to_bf16(x), 0, q, sw, g)
+    want = orc.f32_to_bf16((16.0 * q[:, j].astype(np.float64) * sw.astype(np.float64)).astype(np.float32))
+    np.testing.assert_array_equal(y[0], want)
+
+
+def test_w8a16_more_accurate_than_int8(orc):
+    """Keeping the activation in 16 bits leaves only the weight's INT8 error
+    (~0.75% relative for Gaussian rows: step absmax/127 ~ 3.3 sigma / 127,
+    rms step/sqrt(12)) plus BF16 rounding, below the INT8 path's combined
+    activation and weight error."""
+    w = W.WORKLOADS["c1"]
+    d = W.linear_inputs(w)
+    qw, sw = orc.weight_prep(d["w"], w.group)
+    ref = orc.reference_linear_f64(d["x"], 0, d["w"])
+    e16 = orc.rel_l2(orc.w8a16_linear(d["x"], 0, qw, sw, w.group), ref)
+    e8 = orc.rel_l2(orc.int8_linear(d["x"], 0, qw, sw, w.group), ref)
+    assert 0.002 < e16 < 0.012, e16
+    assert e16 < e8, (e16, e8)
+
+
+def test_w8a16_epilogue_order(orc):
+    """bias then residual in FP32, one BF16 rounding; integers stay exact."""
+    acc = np.array([[3.0, -5.0, 0.0, 200.0]])
+    sw = np.array([2.0, 0.5, 1.0, 0.25], np.float32)
+    b = np.array([1.0, 0.5, -3.0, 0.0], np.float32)
+    r = orc.f32_to_bf16(np.array([[10.0, -1.0, 4.0, -50.0]], np.float32))
+    y = orc.bf16_to_f32(orc.w8a16_epilogue(acc, sw, b, r))
+    np.testing.assert_array_equal(y, np.array([[17.0, -3.0, 1.0, 0.0]], np.float32))

@@ -79,13 +79,14 @@ __device__ __forceinline__ void workgroup_barrier()
 
 // A16: the X operand is BF16 (2 bytes per k) in the BF16 blocked layout and
 // the INT8 W fragments are widened to BF16 in registers (W8A16); the stage
-// then holds twice the X bytes, and the ring has 3 slots, 2 stages ahead.
+// then holds twice the X bytes.
+// The ring has 4 slots (3 stages ahead) when that fits the LDS of the
+// workgroups meant to share a CU (one for tiles of 256 x 192 and larger, two
+// otherwise), else 3 slots (2 stages ahead).
 template <int BM_, int BN_, bool A16>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int XS = A16 ? 2 : 1;         // X bytes per k
-    static constexpr int NBUF = A16 ? 3 : 4;       // LDS ring slots
-    static constexpr int P = NBUF - 1;             // stages in flight
     static constexpr int FM = BM / 64;             // fragments per wave along m
     static constexpr int FN = BN / 64;             // fragments per wave along n
     static constexpr int A_BLK = (BN / 32) * 2;    // W blocks per stage
@@ -93,6 +94,9 @@ struct Cfg {
     static constexpr int BLK = A_BLK + B_BLK;
     static constexpr int L = BLK / 4;              // block loads per lane per stage
     static constexpr int STAGE = BLK * 1024;
+    static constexpr int PER_CU = BM * BN >= 256 * 192 ? 1 : 2;
+    static constexpr int NBUF = PER_CU * (4 * STAGE + 6144) <= 160 * 1024 ? 4 : 3;   // LDS ring slots
+    static constexpr int P = NBUF - 1;             // stages in flight
     static_assert(BLK % 4 == 0, "blocks must split evenly over 4 waves");
 };
 
@@ -565,7 +569,10 @@ hipError_t launch(const void* xq, const float* sx, const int8_t* wq, const float
 // eff, where a round is one tile per workgroup slot and per_cu workgroups
 // share a CU.  The efficiencies are measured (MI355X, random INT8 data):
 // 4096^3 takes 62 us with 256 x 256 tiles, 69 us with 128 x 128, 90 us with
-// 64 x 128.  The W8A16 variant uses the same table.
+// 64 x 128.  128 x 256 and 256 x 128 tiles (two workgroups per CU, 3-slot
+// rings) measured no faster than these (c5 gate_up 295-311 us vs 300 us for
+// 256 x 256; c5 down 152 us vs 128 us for 256 x 192).  The W8A16 variant uses
+// the same table.
 namespace {
 
 int choose_shape(int64_t m, int64_t n, int num_cu)

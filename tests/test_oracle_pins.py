@@ -517,3 +517,25 @@ def test_w8a16_epilogue_order(orc):
     r = orc.f32_to_bf16(np.array([[10.0, -1.0, 4.0, -50.0]], np.float32))
     y = orc.bf16_to_f32(orc.w8a16_epilogue(acc, sw, b, r))
     np.testing.assert_array_equal(y, np.array([[17.0, -3.0, 1.0, 0.0]], np.float32))
+
+
+def test_w8a16_swiglu_input_and_mlp_accuracy(orc):
+    """The fused SwiGLU input of the W8A16 linear and the W8A16 MLP block sit
+    closer to the float64 product than their INT8 counterparts."""
+    w = W.WORKLOADS["c2"]
+    d = W.linear_inputs(w, m=64)
+    qw, sw = orc.weight_prep(d["w"], w.group)
+    ref = orc.reference_linear_f64(d["x"], 1, d["w"])
+    e16 = orc.rel_l2(orc.w8a16_linear(d["x"], 1, qw, sw, w.group), ref)
+    e8 = orc.rel_l2(orc.int8_linear(d["x"], 1, qw, sw, w.group), ref)
+    assert 0.002 < e16 < 0.012 and e16 < e8, (e16, e8)
+    rng = np.random.default_rng(14)
+    m, h, i, g = 32, 256, 512, 128
+    xb = W.to_bf16_bits(rng.standard_normal((m, h)).astype(np.float32))
+    w_gu = (0.05 * rng.standard_normal((2 * i, h))).astype(np.float32)
+    w_dn = (0.05 * rng.standard_normal((h, i))).astype(np.float32)
+    (gq, gs), (dq, ds) = orc.weight_prep(w_gu, g), orc.weight_prep(w_dn, g)
+    y64 = orc.reference_mlp_f64(xb, w_gu, w_dn)
+    e16 = orc.rel_l2(orc.swiglu_mlp_w8a16(xb, gq, gs, dq, ds, g), y64)
+    e8 = orc.rel_l2(orc.swiglu_mlp(xb, gq, gs, dq, ds, g), y64)
+    assert e16 < 0.02 and e16 < e8, (e16, e8)

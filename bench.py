@@ -55,6 +55,9 @@ def parse():
                     help="run only a plain 1 GiB device copy (for scaling HBM counters)")
     ap.add_argument("--small-m-sweep", action="store_true",
                     help="time the few-row GEMM at M = 1..64 instead of the step (one line per case)")
+    ap.add_argument("--decode-mlp", action="store_true",
+                    help="time the c5 MLP block at M = 1..64 tokens with weights in the decode layout "
+                         "(one line per M)")
     ap.add_argument("--w8a16", action="store_true",
                     help="the W8A16 variant: BF16 rotated activations (no activation quantization) "
                          "times the INT8 weights on BF16 MFMA")
@@ -134,6 +137,63 @@ def small_m_sweep(steps: int, warmup: int):
                       flush=True)
 
 
+def decode_mlp(steps: int, warmup: int):
+    """The c5 SwiGLU MLP block (hidden 3072, intermediate 12288, group 128) at
+    decode sizes, M in {1, 8, 16, 64}, through ck_swiglu_mlp with both weights in
+    the decode layout.  Bound by HBM: the weights (2 I H + H I bytes of codes
+    plus their scales) are read once per call."""
+    import torch
+    import swiglu_mlp_amd as ck
+    dev = torch.device("cuda:0")
+    L = ck.lib()
+    h, inter, g = 3072, 12288, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    wgu = torch.randint(-127, 128, (2 * inter, h), dtype=torch.int8, device=dev, generator=gen)
+    wd = torch.randint(-127, 128, (h, inter), dtype=torch.int8, device=dev, generator=gen)
+    dgu = ck.ck_weight_pack_decode(wgu, torch.rand(2 * inter, device=dev, generator=gen) * 1e-3)
+    dd = ck.ck_weight_pack_decode(wd, torch.rand(h, device=dev, generator=gen) * 1e-3)
+    wbytes = dgu.numel() + dd.numel()
+    for m in (1, 8, 16, 64):
+        x = (torch.randn((m, h), device=dev, generator=gen)).to(torch.bfloat16)
+        y = torch.empty((m, h), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(L.ck_swiglu_mlp_workspace_size(m, h, inter), 1), dtype=torch.uint8, device=dev)
+
+        def call():
+            rc = L.ck_swiglu_mlp(x.data_ptr(), dgu.data_ptr(), None, dd.data_ptr(), None, ck.CK_LAYOUT_DECODE,
+                                 m, h, inter, g, y.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream)
+            if rc:
+                raise RuntimeError(L.ck_status_str(rc).decode())
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_b2b = e0.elapsed_time(e1) * 1000.0 / steps
+        reps = max(5, steps // 5)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            flush.view(torch.int32).sum()
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2] * 1000.0
+        print(json.dumps({"decode_mlp": {"m": m, "hidden": h, "intermediate": inter, "us": round(us, 2),
+                                         "weight_MB": round(wbytes / 1e6, 1),
+                                         "GBs_weights": round(wbytes / us / 1e3, 1),
+                                         "frac_hbm_peak": round(wbytes / us / 1e3 / PEAK_HBM_GBS, 4),
+                                         "us_back_to_back": round(us_b2b, 2),
+                                         "timing": "median of single calls after a 512 MB read (4 kernels: "
+                                                   "x quant, gate_up, SwiGLU quant, down)"}}), flush=True)
+
+
 def copy_calibration():
     """A plain elementwise copy of a known size: the reference that scales the
     FETCH_SIZE / WRITE_SIZE counters of the path's kernels to bytes."""
@@ -176,6 +236,9 @@ def main():
         return
     if args.small_m_sweep:
         small_m_sweep(args.steps, args.warmup)
+        return
+    if args.decode_mlp:
+        decode_mlp(args.steps, args.warmup)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

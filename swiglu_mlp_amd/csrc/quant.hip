@@ -46,8 +46,9 @@ __device__ __forceinline__ int64_t blocked_bf16_offset(int row, int c, int kb)
 // row in FP32 (a diagnostic), or the normalised rotated row in BF16.
 enum OutKind { OUT_CODES = 0, OUT_ROT_F32 = 1, OUT_ROT_BF16 = 2 };
 
-template <int KIND, int LOG_G, int CH, int OUT, bool BLOCKED>
-__global__ __launch_bounds__(256) void quant_rows_kernel(
+// BS: threads per workgroup (256, or T for the wide teams of few-row calls).
+template <int KIND, int LOG_G, int CH, int OUT, bool BLOCKED, int BS>
+__global__ __launch_bounds__(BS) void quant_rows_kernel(
     const void* __restrict__ src, int64_t ld, int m, int k, int log_t, float cg,
     int8_t* __restrict__ q, float* __restrict__ s, void* __restrict__ u_out)
 {
@@ -69,6 +70,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
         const int u = wg >> 3;
         wg = (u / S) * (8 * S) + (wg & 7) * S + (u % S);
     }
+    if (wg * rows_per_wg >= m) return;      // a padding workgroup: no rows (uniform exit)
     int row = wg * rows_per_wg + team;
     const bool row_ok = row < m;
     if (!row_ok) row = m - 1;               // compute on a valid row, store nothing
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
     }
 
     // ---- team reduction of the absmax (exact; order does not matter) -------
-    __shared__ float red[4];
+    __shared__ float red[BS / 64];
     if (T >= 2) amax = fmaxf(amax, swizzle_xor<1>(amax));
     if (T >= 4) amax = fmaxf(amax, swizzle_xor<2>(amax));
     if (T >= 8) amax = fmaxf(amax, swizzle_xor<4>(amax));
@@ -268,18 +270,25 @@ constexpr int kChOptions[] = {1, 2, 3, 4, 6, 8, 12, 16};
 // Prefer no idle chunk slots, then the widest team (more lanes in flight per
 // row; measured at k = 3072: T = 128 beats T = 64 and T = 32, and at k = 12288
 // T = 256 beats T = 128), then CH near 6.
-bool choose_team(int k, int g, int* log_t, int* ch)
+// Few rows (fewer than the CUs): the row's latency is the call's, so teams go
+// up to 1024 lanes (one workgroup per row) and the fewest chunks per lane win,
+// then the fewest idle slots.
+constexpr int kFewRows = 256;
+
+bool choose_team(int k, int g, bool few, int* log_t, int* ch)
 {
     const int k8 = k / 8;
     const int tmin = g / 8 > 8 ? g / 8 : 8;
     long best = -1;
-    for (int lt = 3; lt <= 8; ++lt) {
+    for (int lt = 3; lt <= (few ? 10 : 8); ++lt) {
         const int T = 1 << lt;
         if (T < tmin) continue;
         for (int c : kChOptions) {
             if ((long)T * c < k8) continue;
+            if (T > 256 && c > 4) continue;
             const long waste = (long)T * c - k8;
-            const long score = waste * 1000 + (8 - lt) * 20 + (c > 6 ? c - 6 : 6 - c);
+            const long score = few ? (long)c * 100000000L + waste * 16 + lt
+                                   : waste * 1000 + (8 - lt) * 20 + (c > 6 ? c - 6 : 6 - c);
             if (best < 0 || score < best) {
                 best = score;
                 *log_t = lt;
@@ -294,16 +303,30 @@ template <int KIND, int LOG_G, int OUT, bool BLOCKED>
 hipError_t launch_ch(int ch, dim3 grid, hipStream_t st, const void* src, int64_t ld, int m, int k,
                      int log_t, float cg, int8_t* q, float* s, void* u)
 {
-    switch (ch) {
-#define CK_CASE(C)                                                                              \
-    case C:                                                                                     \
-        hipLaunchKernelGGL((quant_rows_kernel<KIND, LOG_G, C, OUT, BLOCKED>), grid, dim3(256), 0, st, \
-                           src, ld, m, k, log_t, cg, q, s, u);                                  \
+    const int bs = log_t > 8 ? 1 << log_t : 256;
+#define CK_CASE(C, BS_)                                                                           \
+    case C:                                                                                       \
+        hipLaunchKernelGGL((quant_rows_kernel<KIND, LOG_G, C, OUT, BLOCKED, BS_>), grid, dim3(BS_), 0, \
+                           st, src, ld, m, k, log_t, cg, q, s, u);                                \
         break;
-        CK_CASE(1) CK_CASE(2) CK_CASE(3) CK_CASE(4) CK_CASE(6) CK_CASE(8) CK_CASE(12) CK_CASE(16)
-#undef CK_CASE
-        default: return hipErrorInvalidValue;
+    if (bs == 256) {
+        switch (ch) {
+            CK_CASE(1, 256) CK_CASE(2, 256) CK_CASE(3, 256) CK_CASE(4, 256) CK_CASE(6, 256)
+            CK_CASE(8, 256) CK_CASE(12, 256) CK_CASE(16, 256)
+            default: return hipErrorInvalidValue;
+        }
+    } else if (bs == 512) {
+        switch (ch) {
+            CK_CASE(1, 512) CK_CASE(2, 512) CK_CASE(3, 512) CK_CASE(4, 512)
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (ch) {
+            CK_CASE(1, 1024) CK_CASE(2, 1024) CK_CASE(3, 1024) CK_CASE(4, 1024)
+            default: return hipErrorInvalidValue;
+        }
     }
+#undef CK_CASE
     return hipGetLastError();
 }
 
@@ -332,8 +355,8 @@ struct Launch {
 
 bool plan(int64_t m, int64_t k, int g, bool blocked, Launch* p)
 {
-    if (!choose_team((int)k, g, &p->log_t, &p->ch)) return false;
-    const int rows_per_wg = 256 >> p->log_t;
+    if (!choose_team((int)k, g, m < kFewRows, &p->log_t, &p->ch)) return false;
+    const int rows_per_wg = p->log_t > 8 ? 1 : 256 >> p->log_t;
     int64_t wgs = (m + rows_per_wg - 1) / rows_per_wg;
     if (blocked) {
         // a multiple of 8 S workgroups (see the row mapping in the kernel)

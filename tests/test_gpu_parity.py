@@ -777,3 +777,24 @@ def test_swiglu_mlp_w8a16_full_c5_sampled_rows(orc):
                      "c5 w8a16")
     y64 = orc.reference_mlp_f64(d["x"][rows], d["w_gu"], d["w_down"])
     say(f"c5 w8a16: relL2 vs float64 {orc.rel_l2(bf16_host(y)[rows], y64):.5f}")
+
+
+@pytest.mark.parametrize("m", [1, 16, 64])
+def test_swiglu_mlp_decode_c5_dims_bit_exact(orc, m):
+    """c5's block dimensions at decode sizes, both weights in the decode layout,
+    in the configuration `bench.py --decode-mlp` times: bit-exact against the
+    oracle on the first m tokens of c5's input."""
+    wl = W.WORKLOADS["c5"]
+    d = inputs("c5")
+    say(f"swiglu_mlp decode c5 dims m={m}")
+    g = wl.group
+    key = ("c5", "decode_weights")
+    if key not in _cache:
+        gq, gs = ck.ck_weight_prep(dev(d["w_gu"]), g)
+        dq, ds = ck.ck_weight_prep(dev(d["w_down"]), g)
+        _cache[key] = (ck.ck_weight_pack_decode(gq, gs), ck.ck_weight_pack_decode(dq, ds))
+    dgu, dd = _cache[key]
+    xb = np.ascontiguousarray(d["x"][:m])
+    y = ck.ck_swiglu_mlp(bf16_dev(xb), dgu, None, dd, None, g, layout="decode")
+    (gq_o, gs_o), (dq_o, ds_o) = prepped(orc, "c5", "w_gu"), prepped(orc, "c5", "w_down")
+    np.testing.assert_array_equal(bf16_host(y), orc.swiglu_mlp(xb, gq_o, gs_o, dq_o, ds_o, g))

@@ -60,6 +60,11 @@ hipError_t launch_gemm_small(const int8_t* xq, const float* sx, const int8_t* wq
                              int64_t m, int64_t n, int64_t k, void* out, bool out_i32, hipStream_t st,
                              EpiExtra ex = EpiExtra{}, bool decode = false);
 
+// W8A16 for m <= 64 (gemm_small.hip): x_rot in the BF16 blocked layout, W blocked.
+hipError_t launch_gemm_small_w8a16(const uint16_t* x_rot, const int8_t* wq, const float* sw, int64_t m,
+                                   int64_t n, int64_t k, void* out, bool out_f32, hipStream_t st,
+                                   EpiExtra ex = EpiExtra{});
+
 // Row-major codes + scales -> decode layout (include/ck.h).
 hipError_t launch_pack_decode(const int8_t* w, const float* sw, int64_t n, int64_t k, void* out,
                               hipStream_t st);

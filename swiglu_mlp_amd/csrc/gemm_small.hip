@@ -16,34 +16,60 @@
 // with W as the A operand (16 output columns n) and x as B (16 rows m);
 // partial accumulators of the 8 waves are summed through LDS, then one wave
 // per 16-row fragment applies y = bf16(fl(fl(f32(acc) * sx[m]) * sw[n])).
+//
+// W8A16 (A16): the activation is the BF16 rotated x in the BF16 blocked layout;
+// each 16-byte INT8 weight piece is widened in registers to two BF16 operands
+// of v_mfma_f32_16x16x32_bf16 (lane k-bytes 0..7, then 8..15), matched by two
+// 16-byte BF16 activation pieces; FP32 accumulators, summed over the waves in a
+// fixed order; y = bf16(fl(acc * sw[n])).
 #include "ck_device.hpp"
 #include "ck_internal.hpp"
+
+#include <type_traits>
 
 namespace ck {
 namespace small {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int WAVES = 8;
 // offset past every buffer's end: a load there returns zeros, a store is dropped
 constexpr uint32_t kOutside = 0x80000000u;
 
-template <int MT>
+template <int MT, bool A16>
 struct SmallCfg {
-    static constexpr int U = MT == 1 ? 8 : (MT == 2 ? 4 : 3);   // chunks per batch per wave
+    // chunks per batch per wave (W8A16 holds twice the activation registers)
+    static constexpr int U = A16 ? (MT == 1 ? 6 : (MT == 2 ? 3 : 2)) : (MT == 1 ? 8 : (MT == 2 ? 4 : 3));
+    static constexpr int XP = A16 ? 2 : 1;   // activation pieces per chunk and fragment
 };
+
+// 8 INT8 weight codes -> 8 BF16 values (exact for |q| <= 127).
+__device__ __forceinline__ v8bf widen8(int lo, int hi)
+{
+    v8bf r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int w = e < 4 ? lo : hi;
+        r[e] = (__bf16)(float)(int)(signed char)(w >> (8 * (e & 3)));
+    }
+    return r;
+}
 
 // DEC: W in the decode layout (include/ck.h): each 16-row group one linear
 // stream, its row scales in the group's 64-byte header.
-template <int MT, bool OUT_I32, bool DEC>
+// A16: xq points to BF16 x_rot (see above); OUT_I32 then writes FP32 sums.
+template <int MT, bool OUT_I32, bool DEC, bool A16>
 __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
     const float* __restrict__ sw, int M, int N, int K, int m_rows, int n_rows, void* __restrict__ out,
     EpiExtra ex)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
-    constexpr int U = SmallCfg<MT>::U;
+    constexpr int U = SmallCfg<MT, A16>::U;
+    constexpr int XP = SmallCfg<MT, A16>::XP;
     __shared__ v4i red[WAVES][MT][64];
 
     const int lane = threadIdx.x & 63;
@@ -56,7 +82,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
         (void*)wq, (short)0, DEC ? (int)((uint32_t)(N / 16) * grp_bytes) : n_rows * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_x =
-        __builtin_amdgcn_make_buffer_rsrc((void*)xq, (short)0, m_rows * K, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)xq, (short)0, m_rows * K * XP, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_o =
         __builtin_amdgcn_make_buffer_rsrc(out, (short)0, M * N * (OUT_I32 ? 4 : 2), 0x00020000);
 
@@ -73,38 +99,67 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const uint32_t w_base = DEC ? (uint32_t)nb * grp_bytes + 64u + (uint32_t)lane * 16u
                                 : (uint32_t)((nb >> 1) * KB) * 1024u + (uint32_t)(nb & 1) * 256u + lane_off;
     const uint32_t w_step = DEC ? 1024u : 2048u;   // bytes per 64-byte k-chunk
+    // activation piece of fragment f (rows 16 f ..), chunk 0: INT8 codes in the
+    // blocked layout, or (A16) BF16 in the BF16 blocked layout, where lane l's
+    // 8 values of chunk j, piece s (k = 64 j + 16 c + 8 s ..) sit in the 2 KB
+    // k-slice 2 j + c / 2 of row block row / 32, at s * 1024 + (c % 2) * 512 + 16 (row % 32)
     uint32_t x_base[MT];
 #pragma unroll
-    for (int f = 0; f < MT; ++f) x_base[f] = (uint32_t)((f >> 1) * KB) * 1024u + (uint32_t)(f & 1) * 256u + lane_off;
+    for (int f = 0; f < MT; ++f) {
+        if constexpr (A16) {
+            const int row = 16 * f + r;
+            x_base[f] = (uint32_t)((row >> 5) * KB + (c >> 1)) * 2048u + (uint32_t)(c & 1) * 512u +
+                        (uint32_t)(row & 31) * 16u;
+        } else {
+            x_base[f] = (uint32_t)((f >> 1) * KB) * 1024u + (uint32_t)(f & 1) * 256u + lane_off;
+        }
+    }
+    const uint32_t x_step = A16 ? 4096u : 2048u;   // activation bytes per 64-k chunk and row block
 
-    v4i acc[MT];
+    using AccT = std::conditional_t<A16, v4f, v4i>;
+    AccT acc[MT];
 #pragma unroll
-    for (int f = 0; f < MT; ++f) acc[f] = v4i{0, 0, 0, 0};
+    for (int f = 0; f < MT; ++f) acc[f] = AccT{0, 0, 0, 0};
 
     // batch b covers chunks j = wave + WAVES * (U b + u), u < U; chunks past
     // the end load zeros (offset outside the buffers) and add nothing
-    auto load = [&](int b, v4i (&w)[U], v4i (&x)[U][MT]) {
+    auto load = [&](int b, v4i (&w)[U], v4i (&x)[U][MT][XP]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = wave + WAVES * (U * b + u);
             const bool ok = j < KC;
-            const uint32_t ko = (uint32_t)j * 2048u;
+            const uint32_t ko = (uint32_t)j * x_step;
             w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, ok ? w_base + (uint32_t)j * w_step : kOutside, 0, 0);
 #pragma unroll
             for (int f = 0; f < MT; ++f)
-                x[u][f] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, ok ? x_base[f] + ko : kOutside, 0, 0);
+#pragma unroll
+                for (int s = 0; s < XP; ++s)
+                    x[u][f][s] = __builtin_amdgcn_raw_buffer_load_b128(
+                        rs_x, ok ? x_base[f] + ko + (uint32_t)s * 1024u : kOutside, 0, 0);
         }
     };
-    auto compute = [&](const v4i (&w)[U], const v4i (&x)[U][MT]) {
+    auto compute = [&](const v4i (&w)[U], const v4i (&x)[U][MT][XP]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u) {
+            if constexpr (A16) {
+                const v8bf w0 = widen8(w[u][0], w[u][1]), w1 = widen8(w[u][2], w[u][3]);
 #pragma unroll
-            for (int f = 0; f < MT; ++f)
-                acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[u], x[u][f], acc[f], 0, 0, 0);
+                for (int f = 0; f < MT; ++f) {
+                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, __builtin_bit_cast(v8bf, x[u][f][0]),
+                                                                     acc[f], 0, 0, 0);
+                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, __builtin_bit_cast(v8bf, x[u][f][XP - 1]),
+                                                                     acc[f], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int f = 0; f < MT; ++f)
+                    acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[u], x[u][f][0], acc[f], 0, 0, 0);
+            }
+        }
     };
 
     const int batches = (KC + WAVES * U - 1) / (WAVES * U);
-    v4i wa[U], xa[U][MT], wb[U], xb[U][MT];
+    v4i wa[U], xa[U][MT][XP], wb[U], xb[U][MT][XP];
     load(0, wa, xa);
     for (int b = 0; b < batches; b += 2) {
         if (b + 1 < batches) load(b + 1, wb, xb);
@@ -114,30 +169,38 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         compute(wb, xb);
     }
 
-    // ---- sum the waves' partial accumulators ----
+    // ---- sum the waves' partial accumulators (in wave order) ----
 #pragma unroll
-    for (int f = 0; f < MT; ++f) red[wave][f][lane] = acc[f];
+    for (int f = 0; f < MT; ++f) red[wave][f][lane] = __builtin_bit_cast(v4i, acc[f]);
     __syncthreads();
     if (wave >= MT) return;
     const int f = wave;
-    v4i t = red[0][f][lane];
+    AccT t = __builtin_bit_cast(AccT, red[0][f][lane]);
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) t += red[w][f][lane];
+    for (int w = 1; w < WAVES; ++w) t += __builtin_bit_cast(AccT, red[w][f][lane]);
 
     // ---- epilogue: lane l holds D[n = 4 (l / 16) + i][m = l % 16], i < 4 ----
     const int m = f * 16 + r;
     const int n = nb * 16 + 4 * c;
     const uint32_t row = (uint32_t)m * (uint32_t)N + (uint32_t)n;
     if constexpr (OUT_I32) {
-        __builtin_amdgcn_raw_buffer_store_b128(t, rs_o, m < M ? row * 4u : kOutside, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, t), rs_o, m < M ? row * 4u : kOutside, 0, 0);
     } else {
-        const float sxm = sx[min(m, M - 1)];
         const float4 s4 = DEC ? *reinterpret_cast<const float4*>(wq + (size_t)nb * grp_bytes + 16 * c)
                               : *reinterpret_cast<const float4*>(sw + n);
-        float y0 = ((float)t[0] * sxm) * s4.x;
-        float y1 = ((float)t[1] * sxm) * s4.y;
-        float y2 = ((float)t[2] * sxm) * s4.z;
-        float y3 = ((float)t[3] * sxm) * s4.w;
+        float y0, y1, y2, y3;
+        if constexpr (A16) {
+            y0 = t[0] * s4.x;
+            y1 = t[1] * s4.y;
+            y2 = t[2] * s4.z;
+            y3 = t[3] * s4.w;
+        } else {
+            const float sxm = sx[min(m, M - 1)];
+            y0 = ((float)t[0] * sxm) * s4.x;
+            y1 = ((float)t[1] * sxm) * s4.y;
+            y2 = ((float)t[2] * sxm) * s4.z;
+            y3 = ((float)t[3] * sxm) * s4.w;
+        }
         epi_extra4(y0, y1, y2, y3, ex, min(m, M - 1), n, N);
         const u32x2 d = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
         __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, m < M ? row * 2u : kOutside, 0, 0);
@@ -145,14 +208,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int MT, bool I32, bool DEC>
+template <int MT, bool I32, bool DEC, bool A16 = false>
 hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int M, int N,
                   int K, void* out, hipStream_t st, EpiExtra ex)
 {
     const int m_rows = (M + 255) / 256 * 256;
     const int n_rows = (N + 255) / 256 * 256;
-    hipLaunchKernelGGL((gemm_small_kernel<MT, I32, DEC>), dim3(N / 16), dim3(WAVES * 64), 0, st, xq, sx, wq,
-                       sw, M, N, K, m_rows, n_rows, out, ex);
+    hipLaunchKernelGGL((gemm_small_kernel<MT, I32, DEC, A16>), dim3(N / 16), dim3(WAVES * 64), 0, st, xq, sx,
+                       wq, sw, M, N, K, m_rows, n_rows, out, ex);
     return hipGetLastError();
 }
 
@@ -169,6 +232,21 @@ hipError_t launch_gemm_small(const int8_t* xq, const float* sx, const int8_t* wq
                              : small::launch<MT_, false, true>(xq, sx, wq, sw, M, N, K, out, st, ex))    \
                   : (out_i32 ? small::launch<MT_, true, false>(xq, sx, wq, sw, M, N, K, out, st, ex)     \
                              : small::launch<MT_, false, false>(xq, sx, wq, sw, M, N, K, out, st, ex))
+    if (m <= 16) CK_SMALL(1);
+    if (m <= 32) CK_SMALL(2);
+    CK_SMALL(4);
+#undef CK_SMALL
+}
+
+// W8A16, m <= 64: x_rot BF16 in the BF16 blocked layout, W blocked.
+hipError_t launch_gemm_small_w8a16(const uint16_t* x_rot, const int8_t* wq, const float* sw, int64_t m,
+                                   int64_t n, int64_t k, void* out, bool out_f32, hipStream_t st, EpiExtra ex)
+{
+    const int M = (int)m, N = (int)n, K = (int)k;
+    const int8_t* xr = reinterpret_cast<const int8_t*>(x_rot);
+#define CK_SMALL(MT_)                                                                                      \
+    return out_f32 ? small::launch<MT_, true, false, true>(xr, nullptr, wq, sw, M, N, K, out, st, ex)       \
+                   : small::launch<MT_, false, false, true>(xr, nullptr, wq, sw, M, N, K, out, st, ex)
     if (m <= 16) CK_SMALL(1);
     if (m <= 32) CK_SMALL(2);
     CK_SMALL(4);

@@ -646,19 +646,23 @@ def test_act_rotate_bf16_bit_exact(orc, m, k, act, g):
 
 W8A16_GEMM_SHAPES = [  # (m, n, k): every tile shape, k-stage counts 1, 2, 3 and more,
     # ragged m and n, a partial last round of tiles
-    (1, 16, 64), (64, 128, 256), (77, 144, 192), (300, 272, 1024), (1000, 1040, 640),
+    (77, 144, 192), (300, 272, 1024), (1000, 1040, 640),
     (513, 4112, 128), (4000, 4080, 192), (4000, 3056, 320), (2560, 6144, 256), (2048, 1024, 3072),
+    # the few-row kernel (m <= 64): 1, 2 and 4 row fragments, short and long k
+    (1, 16, 64), (1, 4096, 4096), (2, 48, 1024), (16, 1024, 3072), (17, 2048, 128), (33, 4096, 4096),
+    (64, 128, 256), (64, 4096, 12288),
 ]
 
 
 @pytest.mark.parametrize("m,n,k", W8A16_GEMM_SHAPES)
 def test_w8a16_gemm_exact_on_integer_activations(orc, m, n, k):
-    """Integer activations |x| <= 32 with k <= 4096 keep every partial sum below
-    2^24, so FP32 accumulation in any order is exact: accumulators and BF16
-    outputs must equal the oracle bit for bit."""
+    """Integer activations with |x| * 127 * k < 2^24 keep every partial sum an
+    integer below 2^24, so FP32 accumulation in any order is exact:
+    accumulators and BF16 outputs must equal the oracle bit for bit."""
     say(f"w8a16 gemm integer activations m={m} n={n} k={k}")
     rng = np.random.default_rng(3 * m + n + k)
-    xr = orc.f32_to_bf16(rng.integers(-32, 33, size=(m, k)).astype(np.float32))
+    xmax = min(32, (1 << 24) // (127 * k) - 1)
+    xr = orc.f32_to_bf16(rng.integers(-xmax, xmax + 1, size=(m, k)).astype(np.float32))
     wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
     sw = (rng.random(n, dtype=np.float32) * 1e-3).astype(np.float32)
     xb, wb = bf16_dev(to_blocked_bf16(xr)), dev(to_blocked(wq))

@@ -161,9 +161,9 @@ def decode_mlp(steps: int, warmup: int):
         y = torch.empty((m, h), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(max(L.ck_swiglu_mlp_workspace_size(m, h, inter), 1), dtype=torch.uint8, device=dev)
 
-        def call():
+        def call(st=stream):
             rc = L.ck_swiglu_mlp(x.data_ptr(), dgu.data_ptr(), None, dd.data_ptr(), None, ck.CK_LAYOUT_DECODE,
-                                 m, h, inter, g, y.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream)
+                                 m, h, inter, g, y.data_ptr(), ws.data_ptr(), ws.numel(), st.cuda_stream)
             if rc:
                 raise RuntimeError(L.ck_status_str(rc).decode())
         for _ in range(warmup):
@@ -185,11 +185,30 @@ def decode_mlp(steps: int, warmup: int):
             b.record(stream)
         torch.cuda.synchronize()
         us = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2] * 1000.0
+        # the same call captured in a HIP graph and replayed back to back
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                call(side)
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream(dev)
+        e0.record(cur)
+        for _ in range(steps):
+            graph.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        us_graph = e0.elapsed_time(e1) * 1000.0 / steps
         print(json.dumps({"decode_mlp": {"m": m, "hidden": h, "intermediate": inter, "us": round(us, 2),
                                          "weight_MB": round(wbytes / 1e6, 1),
                                          "GBs_weights": round(wbytes / us / 1e3, 1),
                                          "frac_hbm_peak": round(wbytes / us / 1e3 / PEAK_HBM_GBS, 4),
                                          "us_back_to_back": round(us_b2b, 2),
+                                         "us_graph_back_to_back": round(us_graph, 2),
                                          "timing": "median of single calls after a 512 MB read (4 kernels: "
                                                    "x quant, gate_up, SwiGLU quant, down)"}}), flush=True)
 

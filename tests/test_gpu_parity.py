@@ -802,3 +802,51 @@ def test_swiglu_mlp_decode_c5_dims_bit_exact(orc, m):
     y = ck.ck_swiglu_mlp(bf16_dev(xb), dgu, None, dd, None, g, layout="decode")
     (gq_o, gs_o), (dq_o, ds_o) = prepped(orc, "c5", "w_gu"), prepped(orc, "c5", "w_down")
     np.testing.assert_array_equal(bf16_host(y), orc.swiglu_mlp(xb, gq_o, gs_o, dq_o, ds_o, g))
+
+
+def test_calls_replay_bit_exact_from_a_hip_graph():
+    """Every entry point only enqueues kernels (no allocation, memset or
+    synchronisation), so a call sequence can be captured into a HIP graph.
+    Each replay, with new inputs copied in eagerly between replays, must match
+    the eager calls bit for bit."""
+    say("graph capture: ck_swiglu_mlp (decode, m=1) + ck_int8_linear (blocked, m=300)")
+    g = 128
+    rng = np.random.default_rng(17)
+    h, i = 1024, 2816
+    gq, gs = ck.ck_weight_prep(dev((0.02 * rng.standard_normal((2 * i, h))).astype(np.float32)), g)
+    dq, ds = ck.ck_weight_prep(dev((0.01 * rng.standard_normal((h, i))).astype(np.float32)), g)
+    dgu, dd = ck.ck_weight_pack_decode(gq, gs), ck.ck_weight_pack_decode(dq, ds)
+    wl, sl = ck.ck_weight_prep(dev((0.02 * rng.standard_normal((528, 768))).astype(np.float32)), g)
+    wlb = ck.ck_weight_pack(wl)
+    x1 = torch.zeros((1, h), dtype=torch.bfloat16, device=DEV)
+    x2 = torch.zeros((300, 768), dtype=torch.bfloat16, device=DEV)
+    y1 = torch.empty((1, h), dtype=torch.bfloat16, device=DEV)
+    y2 = torch.empty((300, 528), dtype=torch.bfloat16, device=DEV)
+    ws1 = torch.empty(ck.lib().ck_swiglu_mlp_workspace_size(1, h, i), dtype=torch.uint8, device=DEV)
+    ws2 = torch.empty(ck.lib().ck_int8_linear_workspace_size(300, 768), dtype=torch.uint8, device=DEV)
+
+    def calls():
+        ck.ck_swiglu_mlp(x1, dgu, None, dd, None, g, out=y1, workspace=ws1, layout="decode")
+        ck.ck_int8_linear(x2, wlb, sl, g, out=y2, workspace=ws2, layout="blocked")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()                                   # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for rep in range(3):
+        a1 = rng.standard_normal((1, h)).astype(np.float32)
+        a2 = rng.standard_normal((300, 768)).astype(np.float32)
+        x1.copy_(torch.from_numpy(a1).to(DEV).to(torch.bfloat16))
+        x2.copy_(torch.from_numpy(a2).to(DEV).to(torch.bfloat16))
+        graph.replay()
+        torch.cuda.synchronize()
+        g1, g2 = y1.clone(), y2.clone()
+        calls()                                   # eager reference on the same inputs
+        torch.cuda.synchronize()
+        assert torch.equal(g1.view(torch.int16), y1.view(torch.int16)), f"replay {rep}: mlp differs"
+        assert torch.equal(g2.view(torch.int16), y2.view(torch.int16)), f"replay {rep}: linear differs"
+        assert g1.abs().sum() > 0 and g2.abs().sum() > 0

@@ -40,6 +40,55 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
+class Event:
+    """A HIP timing event on the runtime torch has loaded, created with
+    hipEventDisableSystemFence: recording it writes a timestamp without the
+    system-scope cache write-back and invalidation a default event performs
+    (measured here: a default event record costs ~6 us of idle GPU between the
+    kernels around it).  Same interface as torch.cuda.Event's timing use."""
+    _hip = None
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            h = ctypes.CDLL("libamdhip64.so.7")        # the copy torch loaded (same soname)
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            for f in (h.hipEventCreateWithFlags, h.hipEventRecord, h.hipEventElapsedTime, h.hipEventDestroy):
+                f.restype = ctypes.c_int
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._h = ctypes.c_void_p()
+        rc = self._lib().hipEventCreateWithFlags(ctypes.byref(self._h), 0x20000000)  # DisableSystemFence
+        if rc:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+
+    def record(self, stream=None):
+        import torch
+        st = stream if stream is not None else torch.cuda.current_stream()
+        rc = self._lib().hipEventRecord(self._h, st.cuda_stream)
+        if rc:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_time(self, end) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self._lib().hipEventElapsedTime(ctypes.byref(ms), self._h, end._h)
+        if rc:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self._h:
+            self._hip.hipEventDestroy(self._h)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,7 +148,7 @@ def small_m_sweep(steps: int, warmup: int):
                     call()
                 torch.cuda.synchronize()
                 # back to back: the weights may stay in the 256 MB MALL between calls
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0, e1 = Event(), Event()
                 e0.record(stream)
                 for _ in range(steps):
                     call()
@@ -114,7 +163,7 @@ def small_m_sweep(steps: int, warmup: int):
                 reps = max(5, steps // 5)
 
                 def flushed(flush_op):
-                    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    evs = [(Event(), Event())
                            for _ in range(reps)]
                     for a, b in evs:
                         flush_op()
@@ -169,7 +218,7 @@ def decode_mlp(steps: int, warmup: int):
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = Event(), Event()
         e0.record(stream)
         for _ in range(steps):
             call()
@@ -177,7 +226,7 @@ def decode_mlp(steps: int, warmup: int):
         torch.cuda.synchronize()
         us_b2b = e0.elapsed_time(e1) * 1000.0 / steps
         reps = max(5, steps // 5)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        evs = [(Event(), Event()) for _ in range(reps)]
         for a, b in evs:
             flush.view(torch.int32).sum()
             a.record(stream)
@@ -389,7 +438,7 @@ def main():
                 events[j][1].record(stream)
 
     def new_events():
-        return [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+        return [[Event(), Event()]
                 for _ in stages]
 
     def stage_means(ev, steps, which):
@@ -413,7 +462,7 @@ def main():
     # dominant kernel (events between every stage would stall the queue)
     K = args.steps
     ev = [new_events() for _ in range(K)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start, end = Event(), Event()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)

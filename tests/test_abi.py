@@ -218,3 +218,20 @@ def test_w8a16_checks(L):
     assert mlp(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 256, 512, 128, FAKE, FAKE, ws - 256, None) == EWS
     assert mlp(FAKE, FAKE, None, FAKE, FAKE, 8, 256, 512, 128, FAKE, FAKE, ws, None) == EINVAL
     assert mlp(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 256, 500, 128, FAKE, FAKE, ws, None) == ESHAPE
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    """include/ck.h is plain C: a C99 program compiled with gcc against it
+    links to the library and gets the documented status codes."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    exe = tmp_path / "abi_check"
+    libdir = os.path.join(ROOT, "swiglu_mlp_amd")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    os.path.join(ROOT, "tests", "abi_check.c"), "-I", os.path.join(ROOT, "include"),
+                    "-L", libdir, "-lck_convrot", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all checks passed" in r.stdout

@@ -850,3 +850,41 @@ def test_calls_replay_bit_exact_from_a_hip_graph():
         assert torch.equal(g1.view(torch.int16), y1.view(torch.int16)), f"replay {rep}: mlp differs"
         assert torch.equal(g2.view(torch.int16), y2.view(torch.int16)), f"replay {rep}: linear differs"
         assert g1.abs().sum() > 0 and g2.abs().sum() > 0
+
+
+def test_concurrent_calls_on_separate_streams():
+    """The library keeps no per-call state of its own (scratch is the caller's
+    workspace), so host threads calling it on separate streams with separate
+    buffers get the results of sequential calls, bit for bit."""
+    import threading
+    say("4 host threads x 5 ck_int8_linear calls on separate streams")
+    g = 128
+    rng = np.random.default_rng(23)
+    wq, sw = ck.ck_weight_prep(dev((0.02 * rng.standard_normal((1040, 1024))).astype(np.float32)), g)
+    wb = ck.ck_weight_pack(wq)
+    xs = [bf16_dev(W.to_bf16_bits(rng.standard_normal((300 + 37 * t, 2048)).astype(np.float32)))
+          for t in range(4)]
+    want = [ck.ck_int8_linear(x, wb, sw, g, "swiglu", layout="blocked") for x in xs]
+    torch.cuda.synchronize()
+    got = [[None] * 5 for _ in range(4)]
+    errors = []
+
+    def worker(t):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for r in range(5):
+                    got[t][r] = ck.ck_int8_linear(xs[t], wb, sw, g, "swiglu", layout="blocked")
+            st.synchronize()
+        except Exception as e:   # surfaced below
+            errors.append(e)
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for t in range(4):
+        for r in range(5):
+            assert torch.equal(got[t][r].view(torch.int16), want[t].view(torch.int16)), (t, r)

@@ -48,7 +48,7 @@ ck_status check_weight_layout(int32_t layout, int64_t m)
 {
     if (layout == CK_LAYOUT_ROWS || layout == CK_LAYOUT_BLOCKED) return CK_OK;
     if (layout != CK_LAYOUT_DECODE) return CK_EINVAL;
-    return m <= 64 ? CK_OK : CK_EUNSUPPORTED;
+    return m <= ck::kDecodeMaxM ? CK_OK : CK_EUNSUPPORTED;
 }
 
 // Bytes of the decode layout of [n, k] (n % 16 == 0).

@@ -69,8 +69,14 @@ hipError_t launch_gemm_small_w8a16(const uint16_t* x_rot, const int8_t* wq, cons
 hipError_t launch_pack_decode(const int8_t* w, const float* sw, int64_t n, int64_t k, void* out,
                               hipStream_t st);
 
-// Largest m routed to launch_gemm_small.
-constexpr int64_t kSmallM = 64;
+// Largest m of a call with weights in the decode layout.
+constexpr int64_t kDecodeMaxM = 64;
+// Largest m the weight-streaming kernel takes (eight 16-row fragments).
+constexpr int64_t kSmallMaxM = 128;
+
+// Blocked-layout GEMMs take the weight-streaming kernel when m <= 32, or when
+// m <= kSmallMaxM and it runs at most one workgroup per CU (n <= 16 * CUs).
+bool use_small_kernel(int64_t m, int64_t n);
 
 int num_cus();
 

@@ -216,6 +216,20 @@ constexpr TileCfg kCfgs[] = {
 
 }  // namespace
 
+// Measured on MI355X: the weight-streaming kernel carries 1 + m / 16 activation
+// fragments per weight fragment through each CU's vector-memory path.  Up to
+// m = 32 that is cheap and it wins or ties everywhere; beyond, it wins while it
+// runs at most one workgroup per CU (n <= 16 * CUs: n = 4096, k = 12288 takes
+// 21 us at m = 65..128 against 32 us on 128 x 128 tiles) and loses when each
+// CU streams several workgroups (n = 24576, k = 3072: 21 us at m = 64 and 34 us
+// at m = 128, against 17 us on tiles).
+bool use_small_kernel(int64_t m, int64_t n)
+{
+    if (m <= 32) return true;
+    if (m > kSmallMaxM) return false;
+    return n / 16 <= num_cus();
+}
+
 int num_cus()
 {
     static int cached[64] = {0};
@@ -289,7 +303,7 @@ hipError_t launch_gemm_bf16(const int8_t* xq, const float* sx, const int8_t* wq,
     if (m == 0 || n == 0) return hipSuccess;
     if (layout == 2) return launch_gemm_small(xq, sx, wq, sw, m, n, k, y, false, st, ex, true);
     const bool blocked = layout == 1;
-    if (blocked && m <= kSmallM) return launch_gemm_small(xq, sx, wq, sw, m, n, k, y, false, st, ex);
+    if (blocked && use_small_kernel(m, n)) return launch_gemm_small(xq, sx, wq, sw, m, n, k, y, false, st, ex);
     if (blocked) return launch_gemm_blk(xq, sx, wq, sw, m, n, k, y, false, num_cus(), st, ex);
     return launch_gemm_t<false>(xq, sx, wq, sw, m, n, k, y, st, ex);
 }
@@ -300,7 +314,7 @@ hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t m, int64_
     if (m == 0 || n == 0) return hipSuccess;
     if (layout == 2) return launch_gemm_small(xq, nullptr, wq, nullptr, m, n, k, acc, true, st, EpiExtra{}, true);
     const bool blocked = layout == 1;
-    if (blocked && m <= kSmallM) return launch_gemm_small(xq, nullptr, wq, nullptr, m, n, k, acc, true, st);
+    if (blocked && use_small_kernel(m, n)) return launch_gemm_small(xq, nullptr, wq, nullptr, m, n, k, acc, true, st);
     if (blocked) return launch_gemm_blk(xq, nullptr, wq, nullptr, m, n, k, acc, true, num_cus(), st);
     return launch_gemm_t<true>(xq, nullptr, wq, nullptr, m, n, k, acc, st);
 }

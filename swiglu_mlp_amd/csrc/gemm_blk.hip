@@ -636,7 +636,7 @@ hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, 
 hipError_t launch_gemm_w8a16(const uint16_t* x_rot, const int8_t* wq, const float* sw, int64_t m,
                              int64_t n, int64_t k, void* out, bool out_f32, hipStream_t st, EpiExtra ex)
 {
-    if (m <= kSmallM) return launch_gemm_small_w8a16(x_rot, wq, sw, m, n, k, out, out_f32, st, ex);
+    if (use_small_kernel(m, n)) return launch_gemm_small_w8a16(x_rot, wq, sw, m, n, k, out, out_f32, st, ex);
     return launch_shape<true>(x_rot, nullptr, wq, sw, m, n, k, out, out_f32, num_cus(), st, ex);
 }
 

@@ -42,7 +42,8 @@ constexpr uint32_t kOutside = 0x80000000u;
 template <int MT, bool A16>
 struct SmallCfg {
     // chunks per batch per wave (W8A16 holds twice the activation registers)
-    static constexpr int U = A16 ? (MT == 1 ? 6 : (MT == 2 ? 3 : 2)) : (MT == 1 ? 8 : (MT == 2 ? 4 : 3));
+    static constexpr int U = A16 ? (MT == 1 ? 6 : (MT == 2 ? 3 : (MT == 4 ? 2 : 1)))
+                                 : (MT == 1 ? 8 : (MT == 2 ? 4 : (MT == 4 ? 3 : 2)));
     static constexpr int XP = A16 ? 2 : 1;   // activation pieces per chunk and fragment
 };
 
@@ -221,7 +222,7 @@ hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const flo
 
 }  // namespace small
 
-// m <= 64, n % 16 == 0, k % 64 == 0 (checked by the caller).
+// m <= kSmallMaxM, n % 16 == 0, k % 64 == 0 (checked by the caller).
 hipError_t launch_gemm_small(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                              int64_t m, int64_t n, int64_t k, void* out, bool out_i32, hipStream_t st,
                              EpiExtra ex, bool decode)
@@ -234,7 +235,8 @@ hipError_t launch_gemm_small(const int8_t* xq, const float* sx, const int8_t* wq
                              : small::launch<MT_, false, false>(xq, sx, wq, sw, M, N, K, out, st, ex))
     if (m <= 16) CK_SMALL(1);
     if (m <= 32) CK_SMALL(2);
-    CK_SMALL(4);
+    if (m <= 64) CK_SMALL(4);
+    CK_SMALL(8);
 #undef CK_SMALL
 }
 
@@ -249,7 +251,8 @@ hipError_t launch_gemm_small_w8a16(const uint16_t* x_rot, const int8_t* wq, cons
                    : small::launch<MT_, false, false, true>(xr, nullptr, wq, sw, M, N, K, out, st, ex)
     if (m <= 16) CK_SMALL(1);
     if (m <= 32) CK_SMALL(2);
-    CK_SMALL(4);
+    if (m <= 64) CK_SMALL(4);
+    CK_SMALL(8);
 #undef CK_SMALL
 }
 

@@ -148,6 +148,8 @@ def test_act_rotate_bit_exact(orc, m, k, act, g):
 GEMM_SHAPES = [  # (m, n, k): every tile shape, both k-step sizes, ragged m and n
     (1, 16, 64), (64, 128, 256), (77, 144, 192), (300, 272, 1024), (1000, 1040, 640),
     (600, 1200, 384), (2048, 1024, 3072), (513, 4112, 128),
+    # few rows on tiles (n > 16 * CUs): 64 x 128 and 128 x 128 tiles at m <= 128
+    (48, 4112, 256), (100, 8192, 128),
     # persistent large-tile kernels: 256x256 and 256x192 tiles, ragged m and n,
     # k % 128 == 64, two rounds of tiles, a partial last round
     (4000, 4080, 192), (4000, 3056, 320), (4096, 8192, 128), (3968, 5120, 64), (2560, 6144, 256),
@@ -337,10 +339,12 @@ def test_gemm_i32_blocked_bit_exact(orc, m, n, k):
     np.testing.assert_array_equal(acc, orc.gemm_i32(xq, wq))
 
 
-SMALL_M_SHAPES = [  # (m, n, k): the few-row kernel (m <= 64): 1, 2 and 4 row fragments,
-    # k-chunk counts below, at and above one batch of the 8 waves, ragged m
+SMALL_M_SHAPES = [  # (m, n, k): the few-row kernel: 1, 2, 4 and 8 row fragments (m up to 128
+    # when n <= 16 * CUs), k-chunk counts below, at and above one batch of the 8 waves,
+    # ragged m
     (1, 4096, 4096), (2, 48, 1024), (16, 1024, 3072), (17, 2048, 128), (32, 160, 12288),
     (33, 4096, 4096), (48, 3072, 1536), (64, 4096, 12288), (64, 16, 64),
+    (65, 4096, 4096), (96, 1040, 3072), (128, 4096, 12288), (100, 16, 64),
 ]
 
 
@@ -363,7 +367,8 @@ def test_small_m_gemm_bit_exact(orc, m, n, k):
 
 EXTRA_CASES = [  # (m, k, n, layout): few-row, 128-wide, 256x256 and 256x192 blocked tiles,
     # ragged m and n, and both row-major kernels
-    (5, 256, 48, "blocked"), (64, 512, 1040, "blocked"), (300, 1024, 272, "blocked"),
+    (5, 256, 48, "blocked"), (64, 512, 1040, "blocked"), (100, 512, 1040, "blocked"),
+    (300, 1024, 272, "blocked"),
     (2000, 256, 8192, "blocked"), (2000, 256, 6144, "blocked"),
     (300, 1024, 272, "rows"), (2000, 256, 8192, "rows"),
 ]
@@ -650,7 +655,9 @@ W8A16_GEMM_SHAPES = [  # (m, n, k): every tile shape, k-stage counts 1, 2, 3 and
     (513, 4112, 128), (4000, 4080, 192), (4000, 3056, 320), (2560, 6144, 256), (2048, 1024, 3072),
     # the few-row kernel (m <= 64): 1, 2 and 4 row fragments, short and long k
     (1, 16, 64), (1, 4096, 4096), (2, 48, 1024), (16, 1024, 3072), (17, 2048, 128), (33, 4096, 4096),
-    (64, 128, 256), (64, 4096, 12288),
+    (64, 128, 256), (64, 4096, 12288), (65, 272, 1024), (128, 4096, 4096),
+    # few rows on tiles (n > 16 * CUs)
+    (48, 4112, 256), (100, 8192, 128),
 ]
 
 

@@ -166,14 +166,21 @@ def test_gemm_i32_bit_exact(orc, m, n, k):
     np.testing.assert_array_equal(acc, orc.gemm_i32(xq, wq))
 
 
-def test_gemm_i32_extreme_codes(orc):
-    say("gemm_i32 extreme codes k=32768")
-    m, n, k = 4, 32, 32768
+@pytest.mark.parametrize("m,n", [(4, 32), (300, 4112)])
+def test_gemm_i32_extreme_codes(orc, m, n):
+    """The largest accumulators CK_MAX_K allows (127 * 127 * 32768 = 5.3e8),
+    through the row-major kernel and both blocked kernels."""
+    say(f"gemm_i32 extreme codes m={m} n={n} k=32768")
+    k = 32768
     xq = np.full((m, k), -127, np.int8)
+    xq[1::3] = 127
     wq = np.full((n, k), 127, np.int8)
     wq[::2] = -127
-    acc = host(ck.ck_int8_gemm_i32(dev(xq), dev(wq)))
-    np.testing.assert_array_equal(acc, orc.gemm_i32(xq, wq))
+    want = orc.gemm_i32(xq, wq)
+    assert np.abs(want).max() == 127 * 127 * k
+    np.testing.assert_array_equal(host(ck.ck_int8_gemm_i32(dev(xq), dev(wq))), want)
+    acc = host(ck.ck_int8_gemm_i32(dev(to_blocked(xq)), dev(to_blocked(wq)), "blocked", m=m, n=n))
+    np.testing.assert_array_equal(acc, want)
 
 
 LINEAR_CASES = [  # (m, k, n, act, g)

@@ -176,9 +176,11 @@ ck_status ck_act_quant(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,
  * tested with bias and residual) and PR #248's commit list (residuals fused
  * into the kernels).
  *   x, ldx, act   as ck_act_quant
- *   w_q      int8 weight codes from ck_weight_prep (CK_LAYOUT_ROWS) or
- *            ck_weight_pack (CK_LAYOUT_BLOCKED), read
- *   w_scale  [n]    FP32 from ck_weight_prep, read
+ *   w_q      int8 weight codes from ck_weight_prep (CK_LAYOUT_ROWS),
+ *            ck_weight_pack (CK_LAYOUT_BLOCKED) or ck_weight_pack_decode
+ *            (CK_LAYOUT_DECODE, m <= 64), read
+ *   w_scale  [n]    FP32 from ck_weight_prep, read (ignored, may be NULL,
+ *            with CK_LAYOUT_DECODE)
  *   bias     [n]    FP32, read, 16-byte aligned, or NULL
  *   residual [m, n] BF16 row-major (row stride n), read, 8-byte aligned, or
  *            NULL; it may be y itself (each element is read before it is
@@ -186,7 +188,8 @@ ck_status ck_act_quant(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,
  *            Epilogue order: t = fl(fl(f32(acc) * x_scale[m]) * w_scale[n]);
  *            t = fl(t + bias[n]); t = fl(t + f32(residual[m, n])); y = bf16(t),
  *            round-to-nearest-even.
- *   layout   layout of w_q; the activation codes use the same one
+ *   layout   layout of w_q; the activation codes use the same one (blocked
+ *            for CK_LAYOUT_DECODE)
  *   y        [m, n] BF16, written (row stride n)
  *   workspace  device buffer of at least ck_int8_linear_workspace_size(m, k)
  *            bytes, 256-byte aligned; clobbered (holds x_q and x_scale). */
@@ -217,7 +220,8 @@ ck_status ck_int8_gemm_bf16(const int8_t *x_q, const float *x_scale,
  *   x      [m, h]  BF16, read
  *   w_gu   [2i, h] int8 + s_gu [2i] FP32: rows 0..i-1 gate, i..2i-1 up
  *   w_down [h, i]  int8 + s_down [h] FP32
- *   layout layout of both weights (and of the internal activation codes)
+ *   layout layout of both weights (and of the internal activation codes;
+ *          with CK_LAYOUT_DECODE, m <= 64, s_gu and s_down may be NULL)
  *   y      [m, h]  BF16, written
  *   workspace  at least ck_swiglu_mlp_workspace_size(m, h, i) bytes,
  *          256-byte aligned; clobbered (x codes/scales, the [m, 2i] BF16

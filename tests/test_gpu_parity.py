@@ -186,7 +186,7 @@ def test_gemm_i32_extreme_codes(orc, m, n):
 LINEAR_CASES = [  # (m, k, n, act, g)
     (1, 256, 16, 0, 128), (7, 384, 48, 1, 128), (64, 256, 128, 0, 128), (300, 1024, 272, 1, 128),
     (129, 512, 320, 0, 64), (200, 768, 96, 1, 256), (33, 128, 64, 0, 1), (1000, 640, 1040, 0, 128),
-    (4000, 256, 4080, 1, 128), (3968, 384, 5120, 0, 64),
+    (4000, 256, 4080, 1, 128), (3968, 384, 5120, 0, 64), (5, 64, 32, 1, 64), (70, 64, 4112, 0, 32),
 ]
 
 
@@ -692,7 +692,7 @@ def test_w8a16_gemm_exact_on_integer_activations(orc, m, n, k):
 
 W8A16_LINEAR = [  # (m, k, n, act, g)
     (1, 256, 16, 0, 128), (7, 384, 48, 1, 128), (300, 1024, 272, 1, 128), (129, 512, 320, 0, 64),
-    (200, 768, 96, 1, 256), (1000, 640, 1040, 0, 128), (4000, 256, 4080, 1, 128),
+    (200, 768, 96, 1, 256), (1000, 640, 1040, 0, 128), (4000, 256, 4080, 1, 128), (5, 64, 32, 1, 64),
 ]
 
 

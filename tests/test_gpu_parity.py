@@ -902,3 +902,42 @@ def test_concurrent_calls_on_separate_streams():
     for t in range(4):
         for r in range(5):
             assert torch.equal(got[t][r].view(torch.int16), want[t].view(torch.int16)), (t, r)
+
+
+def _random_cases(count, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(count):
+        g = int(rng.choice([32, 64, 128, 256]))
+        k = g * int(rng.integers(1, 8)) if g >= 64 else 64 * int(rng.integers(1, 8))
+        n = 16 * int(rng.integers(1, 300))
+        m = int(rng.choice([int(rng.integers(1, 65)), int(rng.integers(65, 700))]))
+        layout = str(rng.choice(["rows", "blocked", "decode"] if m <= 64 else ["rows", "blocked"]))
+        act = int(rng.integers(0, 2))
+        extra = bool(rng.integers(0, 2))
+        cases.append((m, k, n, act, g, layout, extra))
+    return cases
+
+
+@pytest.mark.parametrize("m,k,n,act,g,layout,extra", _random_cases(24, 2024))
+def test_random_shapes_bit_exact(orc, m, k, n, act, g, layout, extra):
+    """Seeded random shapes over every layout, activation, group and epilogue:
+    bit-exact against the oracle."""
+    say(f"random m={m} k={k} n={n} act={act} g={g} layout={layout} extra={extra}")
+    d = W.case(m, k, n, act, seed=m * 7 + n)
+    wq_o, sw_o = orc.weight_prep(d["w"], g)
+    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    if layout == "blocked":
+        wq = ck.ck_weight_pack(wq)
+    elif layout == "decode":
+        wq, sw = ck.ck_weight_pack_decode(wq, sw), None
+    bias = res = None
+    if extra:
+        rng = np.random.default_rng(m + n + k)
+        bias = rng.standard_normal(n).astype(np.float32)
+        res = orc.f32_to_bf16(rng.standard_normal((m, n)).astype(np.float32))
+    y = ck.ck_int8_linear(bf16_dev(d["x"]), wq, sw, g, act, layout=layout,
+                          bias=None if bias is None else dev(bias),
+                          residual=None if res is None else bf16_dev(res))
+    np.testing.assert_array_equal(bf16_host(y), orc.int8_linear(d["x"], act, wq_o, sw_o, g, bias=bias,
+                                                                residual=res))

@@ -20,7 +20,7 @@
 //   * every ds_read_b128 of a fragment reads 1 KB linearly (no bank conflicts).
 //
 // Kernel structure (4 waves in a 2 x 2 grid; one workgroup per CU for the
-// 256-wide tiles, two for the 128-wide ones):
+// 256-wide tiles and the two-slice stages, two for the other 128-wide ones):
 //   * Workgroup tile BM x BN (m x n), wave sub-tile BM/2 x BN/2 built from
 //     32 x 32 fragments of v_mfma_i32_32x32x32_i8 with accumulators in AGPRs.
 //     The MFMA computes D[n][m] = sum_k W[n][k] X[m][k] (W is the A operand),
@@ -29,13 +29,14 @@
 //     the 4 x 4-fragment waves of the 256 x 256 tile are the fastest shape: the
 //     2 x 2-fragment waves of the 128 x 128 tile read as many LDS bytes per
 //     MFMA as the LDS delivers.
-//   * K advances 64 bytes per stage (two 32-byte k-slices).  Stages live in a
-//     ring of 4 LDS buffers; loads run 3 stages ahead.  Each stage is split in
-//     two halves around one barrier: the first half multiplies k-slice 0,
-//     reads k-slice 1's fragments and issues the loads of stage s+3; the second
-//     multiplies k-slice 1 and reads the next stage's k-slice-0 fragments, so
-//     MFMAs never wait on LDS.  The order inside each half is fixed in source
-//     order with sched_barrier.
+//   * K advances 2 KSL 32-byte k-slices per stage (64 bytes, or 128 for the
+//     few-tile GEMMs that use KSL = 2).  Stages live in a ring of (at most) 4
+//     LDS buffers; loads run 3 stages ahead.  Each stage is split in two halves
+//     around one barrier: the first half multiplies the first KSL k-slices,
+//     reads the last KSL k-slices' fragments and issues the loads of stage
+//     s+3; the second multiplies the last KSL k-slices and reads the next
+//     stage's first-half fragments, so MFMAs never wait on LDS.  The order
+//     inside each half is fixed in source order with sched_barrier.
 //   * The loads are LDS DMA (buffer_load_dwordx4 ... lds) issued from inline
 //     assembly, with the waits counted by hand (see lds_dma_b128).
 //   * Workgroups are persistent; the stage sequence runs across a workgroup's
@@ -80,24 +81,33 @@ __device__ __forceinline__ void workgroup_barrier()
 // A16: the X operand is BF16 (2 bytes per k) in the BF16 blocked layout and
 // the INT8 W fragments are widened to BF16 in registers (W8A16); the stage
 // then holds twice the X bytes.
-// The ring has 4 slots (3 stages ahead) when that fits the LDS of the
-// workgroups meant to share a CU (one for tiles of 256 x 192 and larger, two
-// otherwise), else 3 slots (2 stages ahead).
-template <int BM_, int BN_, bool A16>
+// KSL: k-slices (32 bytes of k each) per half stage.  A stage covers 2 KSL
+// k-slices; KSL = 2 halves the stages, and with them the per-stage fixed cost
+// (barrier, waits, read latency), for small tiles that run one workgroup per
+// CU.
+// The ring has as many slots as fit the LDS share of a workgroup (160 KB per
+// CU over the workgroups meant to share it: one for tiles of 256 x 192 and
+// larger and for KSL = 2, two otherwise; 6 KB of it go to scale buffers), at
+// most NMAX; P = NBUF - 1 stages are in flight.
+template <int BM_, int BN_, bool A16, int KSL_ = 1>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_;
+    static constexpr int BM = BM_, BN = BN_, KSL = KSL_;
     static constexpr int XS = A16 ? 2 : 1;         // X bytes per k
     static constexpr int FM = BM / 64;             // fragments per wave along m
     static constexpr int FN = BN / 64;             // fragments per wave along n
-    static constexpr int A_BLK = (BN / 32) * 2;    // W blocks per stage
-    static constexpr int B_BLK = (BM / 32) * 2 * XS;   // X blocks per stage
+    static constexpr int A_BLK = (BN / 32) * 2 * KSL;      // W blocks per stage
+    static constexpr int B_BLK = (BM / 32) * 2 * KSL * XS; // X blocks per stage
     static constexpr int BLK = A_BLK + B_BLK;
     static constexpr int L = BLK / 4;              // block loads per lane per stage
     static constexpr int STAGE = BLK * 1024;
-    static constexpr int PER_CU = BM * BN >= 256 * 192 ? 1 : 2;
-    static constexpr int NBUF = PER_CU * (4 * STAGE + 6144) <= 160 * 1024 ? 4 : 3;   // LDS ring slots
+    static constexpr int PER_CU = (BM * BN >= 256 * 192 || KSL > 1) ? 1 : 2;
+    static constexpr int NMAX = 4;
+    static constexpr int FIT = (160 * 1024 / PER_CU - 6144) / STAGE;
+    static constexpr int NBUF = FIT < NMAX ? FIT : NMAX;   // LDS ring slots
     static constexpr int P = NBUF - 1;             // stages in flight
+    static_assert(NBUF >= 3, "the ring needs at least 3 slots");
     static_assert(BLK % 4 == 0, "blocks must split evenly over 4 waves");
+    static_assert(!A16 || KSL == 1, "W8A16 uses one k-slice per half stage");
 };
 
 // 8 INT8 weight codes -> 8 BF16 values (exact: |q| <= 127 has 7 significant
@@ -154,7 +164,7 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes)
 // A16 (W8A16): xq points to BF16 values, the accumulators are FP32, the
 // epilogue is y = bf16(fl(acc * sw[n])) (sx unused), and OUT_I32 writes the
 // raw FP32 accumulators.
-template <int BM, int BN, bool OUT_I32, bool EXTRA, bool A16>
+template <int BM, int BN, bool OUT_I32, bool EXTRA, bool A16, int KSL>
 __global__ __launch_bounds__(256) void gemm_blk_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
     const float* __restrict__ sw, int M, int N, int K, int m_rows, int n_rows, void* __restrict__ out,
@@ -163,7 +173,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     // The body uses AMDGPU-only types (buffer resources); the host pass only
     // needs this function's launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
-    using C = Cfg<BM, BN, A16>;
+    using C = Cfg<BM, BN, A16, KSL>;
     using AccT = std::conditional_t<A16, v16f, v16i>;
     // LDS: the 4-slot operand ring, then two scale buffers (tile q uses
     // buffer q % 2), each 1 KB of row scales sx then 1 KB of column scales sw.
@@ -174,6 +184,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     constexpr int XW = C::B_BLK / 4;   // X blocks each wave loads per stage
     constexpr int NMF = C::FN * C::FM; // fragment pairs (MFMA steps) per wave per k-slice
     constexpr int NDS = C::FN + C::FM * C::XS; // fragment reads per wave per k-slice
+    constexpr int KS2 = 2 * KSL;       // k-slices per stage
     // steps of the two halves of a stage (small tiles have fewer MFMAs than
     // reads or loads)
     // BF16 stores per wave in one epilogue (two 16-byte stores per fragment).
@@ -181,7 +192,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     // waited for in full.
     constexpr int NST = OUT_I32 ? 0 : 2 * NMF;
     static_assert((C::P - 1) * C::L + 1 + NST < 64, "vmcnt range");
-    constexpr int STEPS1 = NMF > NDS ? NMF : NDS;
+    constexpr int STEPS1 = KSL * (NMF > NDS ? NMF : NDS);
     constexpr int STEPS0 = STEPS1 > AW + XW ? STEPS1 : AW + XW;
 
     const int tid = threadIdx.x;
@@ -190,7 +201,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     const int G = gridDim.x;
     const int b = blockIdx.x;
     const int tiles = tiles_m * tiles_n;
-    const int KT = K / 64;          // stages per tile
+    const int KT = K / (64 * KSL);  // stages per tile
     const int KB = K / 32;          // k-slices per 32-row block (W: 1 KB, X: XS KB each)
     const int my_tiles = (tiles - b + G - 1) / G;
     const int total = my_tiles * KT;
@@ -241,18 +252,19 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
         }
     };
     // Block a of this wave's share: W block ai = wave * AW + a covers row
-    // block ai / 2, k-slice ai % 2 of the stage.  X blocks follow the W blocks
-    // in the LDS stage: X block bj covers row block bj / (2 XS) and the
-    // bj % (2 XS)-th KB of the stage's 2 XS KB of that row block.
+    // block ai / KS2, k-slice ai % KS2 of the stage.  X blocks follow the W
+    // blocks in the LDS stage: X block bj covers row block bj / (KS2 XS) and
+    // the bj % (KS2 XS)-th KB of the stage's KS2 XS KB of that row block.
     auto issue_one = [&](int a, uint32_t slot_addr) {
         if (a < AW) {
             const int ai = wave * AW + a;
-            const uint32_t off = la + (uint32_t)lkt * 2048u + (uint32_t)((ai >> 1) * KB + (ai & 1)) * 1024u;
+            const uint32_t off = la + (uint32_t)lkt * (1024u * KS2) +
+                                 (uint32_t)((ai / (unsigned)KS2) * KB + (ai % (unsigned)KS2)) * 1024u;
             lds_dma_b128(rs_w, lane16, off, slot_addr + (uint32_t)ai * 1024u);
         } else {
-            constexpr int XR = 2 * C::XS;   // X blocks per row block per stage
+            constexpr int XR = KS2 * C::XS;   // X blocks per row block per stage
             const int bj = wave * XW + (a - AW);
-            const uint32_t off = lx + (uint32_t)lkt * (2048u * C::XS) +
+            const uint32_t off = lx + (uint32_t)lkt * (1024u * XR) +
                                  (uint32_t)((bj / XR) * KB * C::XS + (bj % XR)) * 1024u;
             lds_dma_b128(rs_x, lane16, off, slot_addr + (uint32_t)(C::A_BLK + bj) * 1024u);
         }
@@ -264,28 +276,15 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     const int wm0 = (wave & 1) * (BM / 2);
     const int wn0 = (wave >> 1) * (BN / 2);
     // This wave's fragments of a stage: W fragment i, k-slice ks at block
-    // (wn0 / 32 + i) * 2 + ks; X fragment j, k-slice ks, part h (the XS KB of
-    // one k-slice) at block A_BLK + ((wm0 / 32 + j) * 2 + ks) * XS + h.
+    // (wn0 / 32 + i) * KS2 + ks; X fragment j, k-slice ks, part h (the XS KB
+    // of one k-slice) at block A_BLK + ((wm0 / 32 + j) * KS2 + ks) * XS + h.
     auto frag_a = [&](int buf, int i, int ks) {
-        const int blk = ((wn0 >> 5) + i) * 2 + ks;
+        const int blk = ((wn0 >> 5) + i) * KS2 + ks;
         return *reinterpret_cast<const v4i*>(smem + buf * C::STAGE + blk * 1024 + lane * 16);
     };
     auto frag_b = [&](int buf, int j, int ks, int h) {
-        const int blk = C::A_BLK + (((wm0 >> 5) + j) * 2 + ks) * C::XS + h;
+        const int blk = C::A_BLK + (((wm0 >> 5) + j) * KS2 + ks) * C::XS + h;
         return *reinterpret_cast<const v4i*>(smem + buf * C::STAGE + blk * 1024 + lane * 16);
-    };
-    // One k-slice of fragment pair (i, j): one INT8 MFMA, or in W8A16 two BF16
-    // MFMAs over the two 8-byte halves of the W fragment (lane k-bytes 0..7,
-    // then 8..15), matched by the two X parts.
-    auto mfma = [&](const v4i& w, const v4i (&x)[C::XS], const AccT& c) -> AccT {
-        if constexpr (A16) {
-            const AccT t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                widen8(w[0], w[1]), __builtin_bit_cast(v8bf, x[0]), c, 0, 0, 0);
-            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                widen8(w[2], w[3]), __builtin_bit_cast(v8bf, x[C::XS - 1]), t, 0, 0, 0);
-        } else {
-            return __builtin_amdgcn_mfma_i32_32x32x32_i8(w, x[0], c, 0, 0, 0);
-        }
     };
 
     set_tile(0);
@@ -297,13 +296,16 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     }
     wait_vmcnt<(C::P - 1) * C::L>();
     workgroup_barrier();
-    v4i fa[C::FN], fb[C::FM][C::XS];
+    v4i fa[KSL][C::FN], fb[KSL][C::FM][C::XS];
 #pragma unroll
-    for (int i = 0; i < C::FN; ++i) fa[i] = frag_a(0, i, 0);
+    for (int ks = 0; ks < KSL; ++ks) {
 #pragma unroll
-    for (int j = 0; j < C::FM; ++j)
+        for (int i = 0; i < C::FN; ++i) fa[ks][i] = frag_a(0, i, ks);
 #pragma unroll
-        for (int h = 0; h < C::XS; ++h) fb[j][h] = frag_b(0, j, 0, h);
+        for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+            for (int h = 0; h < C::XS; ++h) fb[ks][j][h] = frag_b(0, j, ks, h);
+    }
 
     // One stage s (ring slot s % 4).  The instruction order inside each half
     // is fixed in source order (sched_barrier): MFMA k, then fragment read k,
@@ -327,34 +329,40 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
             cw[i][1] = widen8(w[i][2], w[i][3]);
         }
     };
-    // MFMA step k of a half: fragment pair (i, j) = (k / FM, k % FM).
-    auto mfma_step = [&](int k, const v4i (&w)[C::FN], const v4i (&x)[C::FM][C::XS], bool zero) {
-        const int i = k / C::FM, j = k % C::FM;
-        const AccT c = zero ? AccT{} : acc[i][j];
+    // MFMA step k of a half: k-slice ks = k / NMF of the half, fragment pair
+    // (i, j) = ((k % NMF) / FM, k % FM).  One INT8 MFMA, or in W8A16 two BF16
+    // MFMAs over the two 8-byte halves of the W fragment (lane k-bytes 0..7,
+    // then 8..15), matched by the two X parts.
+    auto mfma_step = [&](int k, const v4i (&w)[KSL][C::FN], const v4i (&x)[KSL][C::FM][C::XS], bool zero) {
+        const int ks = k / NMF, kk = k % NMF;
+        const int i = kk / C::FM, j = kk % C::FM;
+        const AccT c = (zero && ks == 0) ? AccT{} : acc[i][j];
         if constexpr (A16) {
-            if (k == 0) widen(w, 0);
-            const AccT t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cw[i][0], __builtin_bit_cast(v8bf, x[j][0]), c,
-                                                                   0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cw[i][1], __builtin_bit_cast(v8bf, x[j][1]), t,
+            if (kk == 0) widen(w[ks], 0);
+            const AccT t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cw[i][0], __builtin_bit_cast(v8bf, x[ks][j][0]),
+                                                                   c, 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cw[i][1], __builtin_bit_cast(v8bf, x[ks][j][1]), t,
                                                                 0, 0, 0);
-            if (j == 0 && i + 1 < C::FN) widen(w, i + 1);
+            if (j == 0 && i + 1 < C::FN) widen(w[ks], i + 1);
         } else {
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w[i], x[j][0], c, 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w[ks][i], x[ks][j][0], c, 0, 0, 0);
         }
     };
-    // Fragment read r of a half: W fragment r < FN, else X fragment
-    // (r - FN) / XS, part (r - FN) % XS.
-    auto read_step = [&](int r, int buf, int ks, v4i (&w)[C::FN], v4i (&x)[C::FM][C::XS]) {
-        if (r < C::FN) w[r] = frag_a(buf, r, ks);
-        else if (r < NDS) x[(r - C::FN) / C::XS][(r - C::FN) % C::XS] =
-            frag_b(buf, (r - C::FN) / C::XS, ks, (r - C::FN) % C::XS);
+    // Fragment read r of a half: k-slice ks0 + r / NDS; within it W fragment
+    // rr < FN, else X fragment (rr - FN) / XS, part (rr - FN) % XS.
+    auto read_step = [&](int r, int buf, int ks0, v4i (&w)[KSL][C::FN], v4i (&x)[KSL][C::FM][C::XS]) {
+        if (r >= KSL * NDS) return;
+        const int ks = r / NDS, rr = r % NDS;
+        if (rr < C::FN) w[ks][rr] = frag_a(buf, rr, ks0 + ks);
+        else x[ks][(rr - C::FN) / C::XS][(rr - C::FN) % C::XS] =
+            frag_b(buf, (rr - C::FN) / C::XS, ks0 + ks, (rr - C::FN) % C::XS);
     };
 
     auto stage = [&](int s, int kt, auto first, bool after_epilogue, int tm, int tn, int q) {
         const int buf = (int)((unsigned)s % C::NBUF);
         const int nbuf = (int)((unsigned)(s + 1) % C::NBUF);
         const uint32_t lslot = smem_addr + (uint32_t)(((unsigned)(s + C::P) % C::NBUF) * C::STAGE);
-        v4i ga[C::FN], gb[C::FM][C::XS];
+        v4i ga[KSL][C::FN], gb[KSL][C::FM][C::XS];
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (decltype(first)::value) {
             const uint32_t sbase = smem_addr + (uint32_t)(C::NBUF * C::STAGE + (q & 1) * SCALES);
@@ -376,14 +384,14 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
         }
 #pragma unroll
         for (int k = 0; k < STEPS0; ++k) {
-            if (k < NMF) mfma_step(k, fa, fb, decltype(first)::value);
-            read_step(k, buf, 1, ga, gb);
+            if (k < KSL * NMF) mfma_step(k, fa, fb, decltype(first)::value);
+            read_step(k, buf, KSL, ga, gb);
             if (k < AW + XW) issue_one(k, lslot);
             __builtin_amdgcn_sched_barrier(0);
         }
         advance();
 
-        wait_lgkmcnt0();              // this wave's k-slice 1 fragments are in registers
+        wait_lgkmcnt0();              // this wave's second-half fragments are in registers
         if (kt <= C::P - 2) {
             if (after_epilogue) wait_vmcnt<(C::P - 1) * C::L + 1 + NST>();
             else wait_vmcnt<(C::P - 1) * C::L + 1>();
@@ -394,7 +402,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
 
 #pragma unroll
         for (int k = 0; k < STEPS1; ++k) {
-            if (k < NMF) mfma_step(k, ga, gb, false);
+            if (k < KSL * NMF) mfma_step(k, ga, gb, false);
             read_step(k, nbuf, 0, fa, fb);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -545,7 +553,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int BM, int BN, bool I32, bool EXTRA, bool A16>
+template <int BM, int BN, bool I32, bool EXTRA, bool A16, int KSL = 1>
 hipError_t launch(const void* xq, const float* sx, const int8_t* wq, const float* sw, int M, int N,
                   int K, void* out, int num_cu, hipStream_t st, EpiExtra ex)
 {
@@ -553,7 +561,7 @@ hipError_t launch(const void* xq, const float* sx, const int8_t* wq, const float
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
     // LDS per workgroup: the stage ring and two scale buffers; 160 KB per CU.
-    using C = Cfg<BM, BN, A16>;
+    using C = Cfg<BM, BN, A16, KSL>;
     const int lds = C::NBUF * C::STAGE + (EXTRA ? 6144 : 4096);
     const int per_cu = (160 * 1024) / lds >= 2 ? 2 : 1;
     const int slots = num_cu * per_cu;
@@ -561,7 +569,7 @@ hipError_t launch(const void* xq, const float* sx, const int8_t* wq, const float
     const int group_m = tiles_m < 4 ? tiles_m : 4;
     const int m_rows = (M + 255) / 256 * 256;
     const int n_rows = (N + 255) / 256 * 256;
-    hipLaunchKernelGGL((gemm_blk_kernel<BM, BN, I32, EXTRA, A16>), dim3(grid), dim3(256), 0, st,
+    hipLaunchKernelGGL((gemm_blk_kernel<BM, BN, I32, EXTRA, A16, KSL>), dim3(grid), dim3(256), 0, st,
                        static_cast<const int8_t*>(xq), sx, wq, sw, M, N, K, m_rows, n_rows, out, tiles_m,
                        tiles_n, group_m, ex);
     return hipGetLastError();
@@ -604,22 +612,51 @@ int choose_shape(int64_t m, int64_t n, int num_cu)
     return best;
 }
 
+// An INT8 GEMM whose 64 x 128 tiles, or failing that 128 x 128 tiles, number
+// at most one per CU runs as a single round of those tiles with two k-slices
+// per half stage (KSL = 2): its time is then the per-stage fixed cost
+// (barrier, waits, LDS read latency) times the stage count, and KSL = 2 halves
+// the count.  Measured (MI355X, random INT8 codes, warm caches):
+// 2048 x 1024 x 3072 12.3 -> 10.8 us, 1024 x 1024 x 12288 33.5 -> 27.0 us,
+// 256 x 3072 x 12288 32.2 -> 26.1 us (64 x 128 tiles); 1024 x 4096 x 4096,
+// where 512 tiles of 64 x 128 would share CUs two by two, 23.8 us on those,
+// 20.7 us on 128 x 128 tiles with KSL = 2.  Deeper rings (5 or 6 slots) and
+// KSL = 4 measured slower.  Returns the shape index, or -1.
+int two_slice_shape(int64_t m, int64_t n, int64_t k, int num_cu)
+{
+    if (k % 128 != 0) return -1;
+    const int64_t tiles_n = (n + 127) / 128;
+    if (((m + 63) / 64) * tiles_n <= num_cu) return 1;
+    if (((m + 127) / 128) * tiles_n <= num_cu) return 0;
+    return -1;
+}
+
 template <bool A16>
 hipError_t launch_shape(const void* xq, const float* sx, const int8_t* wq, const float* sw, int64_t m,
                         int64_t n, int64_t k, void* out, bool out_raw, int num_cu, hipStream_t st,
                         EpiExtra ex)
 {
     const int M = (int)m, N = (int)n, K = (int)k;
-#define CK_BLK(BM_, BN_)                                                                               \
-    return out_raw ? blk::launch<BM_, BN_, true, false, A16>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex) \
+    const int two = A16 ? -1 : two_slice_shape(m, n, k, num_cu);
+    const bool ksl2 = two >= 0;
+    const int shape = ksl2 ? two : choose_shape(m, n, num_cu);
+#define CK_BLK(BM_, BN_, KSL_)                                                                         \
+    return out_raw                                                                                      \
+               ? blk::launch<BM_, BN_, true, false, A16, KSL_>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex) \
            : (ex.bias || ex.res)                                                                        \
-               ? blk::launch<BM_, BN_, false, true, A16>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex)  \
-               : blk::launch<BM_, BN_, false, false, A16>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex)
-    switch (choose_shape(m, n, num_cu)) {
-        case 0: CK_BLK(128, 128);
-        case 1: CK_BLK(64, 128);
-        case 2: CK_BLK(256, 256);
-        default: CK_BLK(256, 192);
+               ? blk::launch<BM_, BN_, false, true, A16, KSL_>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex) \
+               : blk::launch<BM_, BN_, false, false, A16, KSL_>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex)
+    switch (shape) {
+        case 0:
+            if constexpr (!A16)
+                if (ksl2) CK_BLK(128, 128, 2);
+            CK_BLK(128, 128, 1);
+        case 1:
+            if constexpr (!A16)
+                if (ksl2) CK_BLK(64, 128, 2);
+            CK_BLK(64, 128, 1);
+        case 2: CK_BLK(256, 256, 1);
+        default: CK_BLK(256, 192, 1);
     }
 #undef CK_BLK
 }

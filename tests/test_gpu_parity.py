@@ -150,6 +150,11 @@ GEMM_SHAPES = [  # (m, n, k): every tile shape, both k-step sizes, ragged m and 
     (600, 1200, 384), (2048, 1024, 3072), (513, 4112, 128),
     # few rows on tiles (n > 16 * CUs): 64 x 128 and 128 x 128 tiles at m <= 128
     (48, 4112, 256), (100, 8192, 128),
+    # 64 x 128 and 128 x 128 tiles with one k-slice per half stage: k % 128 == 64
+    # with at most one tile per CU, and more tiles than CUs (several per CU)
+    (300, 272, 192), (600, 1200, 448), (320, 11008, 256), (1500, 4000, 320),
+    # two k-slices per half stage on 128 x 128 tiles (at most one per CU)
+    (1024, 4096, 1024), (700, 5008, 256),
     # persistent large-tile kernels: 256x256 and 256x192 tiles, ragged m and n,
     # k % 128 == 64, two rounds of tiles, a partial last round
     (4000, 4080, 192), (4000, 3056, 320), (4096, 8192, 128), (3968, 5120, 64), (2560, 6144, 256),
@@ -372,10 +377,11 @@ def test_small_m_gemm_bit_exact(orc, m, n, k):
     np.testing.assert_array_equal(y, orc.dequant(acc_o, sx, sw))
 
 
-EXTRA_CASES = [  # (m, k, n, layout): few-row, 128-wide, 256x256 and 256x192 blocked tiles,
-    # ragged m and n, and both row-major kernels
+EXTRA_CASES = [  # (m, k, n, layout): few-row, 128-wide (one and two k-slices per half
+    # stage), 256x256 and 256x192 blocked tiles, ragged m and n, and both row-major kernels
     (5, 256, 48, "blocked"), (64, 512, 1040, "blocked"), (100, 512, 1040, "blocked"),
-    (300, 1024, 272, "blocked"),
+    (300, 1024, 272, "blocked"), (700, 256, 5008, "blocked"), (320, 256, 11008, "blocked"),
+    (1500, 384, 4000, "blocked"),
     (2000, 256, 8192, "blocked"), (2000, 256, 6144, "blocked"),
     (300, 1024, 272, "rows"), (2000, 256, 8192, "rows"),
 ]

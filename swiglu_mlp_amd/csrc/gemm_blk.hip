@@ -107,7 +107,6 @@ struct Cfg {
     static constexpr int P = NBUF - 1;             // stages in flight
     static_assert(NBUF >= 3, "the ring needs at least 3 slots");
     static_assert(BLK % 4 == 0, "blocks must split evenly over 4 waves");
-    static_assert(!A16 || KSL == 1, "W8A16 uses one k-slice per half stage");
 };
 
 // 8 INT8 weight codes -> 8 BF16 values (exact: |q| <= 127 has 7 significant
@@ -612,16 +611,18 @@ int choose_shape(int64_t m, int64_t n, int num_cu)
     return best;
 }
 
-// An INT8 GEMM whose 64 x 128 tiles, or failing that 128 x 128 tiles, number
-// at most one per CU runs as a single round of those tiles with two k-slices
-// per half stage (KSL = 2): its time is then the per-stage fixed cost
-// (barrier, waits, LDS read latency) times the stage count, and KSL = 2 halves
-// the count.  Measured (MI355X, random INT8 codes, warm caches):
+// A GEMM whose 64 x 128 tiles, or failing that 128 x 128 tiles, number at
+// most one per CU runs as a single round of those tiles with two k-slices per
+// half stage (KSL = 2): its time is then the per-stage fixed cost (barrier,
+// waits, LDS read latency) times the stage count, and KSL = 2 halves the
+// count.  Measured (MI355X, random operands, warm caches), INT8:
 // 2048 x 1024 x 3072 12.3 -> 10.8 us, 1024 x 1024 x 12288 33.5 -> 27.0 us,
 // 256 x 3072 x 12288 32.2 -> 26.1 us (64 x 128 tiles); 1024 x 4096 x 4096,
 // where 512 tiles of 64 x 128 would share CUs two by two, 23.8 us on those,
-// 20.7 us on 128 x 128 tiles with KSL = 2.  Deeper rings (5 or 6 slots) and
-// KSL = 4 measured slower.  Returns the shape index, or -1.
+// 20.7 us on 128 x 128 tiles with KSL = 2.  W8A16: 27.4 -> 24.8 us,
+// 89.5 -> 76.5 us, 89.8 -> 76.5 us and 50.4 -> 43.6 us on the same shapes.
+// Deeper rings (5 or 6 slots) and KSL = 4 measured slower.  Returns the shape
+// index, or -1.
 int two_slice_shape(int64_t m, int64_t n, int64_t k, int num_cu)
 {
     if (k % 128 != 0) return -1;
@@ -637,7 +638,7 @@ hipError_t launch_shape(const void* xq, const float* sx, const int8_t* wq, const
                         EpiExtra ex)
 {
     const int M = (int)m, N = (int)n, K = (int)k;
-    const int two = A16 ? -1 : two_slice_shape(m, n, k, num_cu);
+    const int two = two_slice_shape(m, n, k, num_cu);
     const bool ksl2 = two >= 0;
     const int shape = ksl2 ? two : choose_shape(m, n, num_cu);
 #define CK_BLK(BM_, BN_, KSL_)                                                                         \
@@ -648,12 +649,10 @@ hipError_t launch_shape(const void* xq, const float* sx, const int8_t* wq, const
                : blk::launch<BM_, BN_, false, false, A16, KSL_>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex)
     switch (shape) {
         case 0:
-            if constexpr (!A16)
-                if (ksl2) CK_BLK(128, 128, 2);
+            if (ksl2) CK_BLK(128, 128, 2);
             CK_BLK(128, 128, 1);
         case 1:
-            if constexpr (!A16)
-                if (ksl2) CK_BLK(64, 128, 2);
+            if (ksl2) CK_BLK(64, 128, 2);
             CK_BLK(64, 128, 1);
         case 2: CK_BLK(256, 256, 1);
         default: CK_BLK(256, 192, 1);

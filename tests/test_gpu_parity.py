@@ -671,6 +671,10 @@ W8A16_GEMM_SHAPES = [  # (m, n, k): every tile shape, k-stage counts 1, 2, 3 and
     (64, 128, 256), (64, 4096, 12288), (65, 272, 1024), (128, 4096, 4096),
     # few rows on tiles (n > 16 * CUs)
     (48, 4112, 256), (100, 8192, 128),
+    # 64 x 128 and 128 x 128 tiles with one k-slice per half stage (k % 128 == 64, or
+    # more tiles than CUs), and 128 x 128 tiles with two
+    (300, 272, 192), (600, 1200, 448), (320, 11008, 256), (1500, 4000, 320),
+    (1024, 4096, 1024), (700, 5008, 256),
 ]
 
 
@@ -699,6 +703,7 @@ def test_w8a16_gemm_exact_on_integer_activations(orc, m, n, k):
 W8A16_LINEAR = [  # (m, k, n, act, g)
     (1, 256, 16, 0, 128), (7, 384, 48, 1, 128), (300, 1024, 272, 1, 128), (129, 512, 320, 0, 64),
     (200, 768, 96, 1, 256), (1000, 640, 1040, 0, 128), (4000, 256, 4080, 1, 128), (5, 64, 32, 1, 64),
+    (1500, 384, 4000, 0, 128), (700, 256, 5008, 1, 128),
 ]
 
 

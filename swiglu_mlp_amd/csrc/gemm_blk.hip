@@ -174,9 +174,9 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = Cfg<BM, BN, A16, KSL>;
     using AccT = std::conditional_t<A16, v16f, v16i>;
-    // LDS: the 4-slot operand ring, then two scale buffers (tile q uses
-    // buffer q % 2), each 1 KB of row scales sx then 1 KB of column scales sw.
-    // one tile's sx and sw (and, with EXTRA, its bias) in LDS, 1 KB each
+    // LDS: the NBUF-slot operand ring, then two scale buffers (tile q uses
+    // buffer q % 2), each 1 KB of row scales sx, 1 KB of column scales sw
+    // and, with EXTRA, 1 KB of bias.
     constexpr int SCALES = EXTRA ? 3072 : 2048;
     __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE + 2 * SCALES];
     constexpr int AW = C::A_BLK / 4;   // W blocks each wave loads per stage
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
             for (int h = 0; h < C::XS; ++h) fb[ks][j][h] = frag_b(0, j, ks, h);
     }
 
-    // One stage s (ring slot s % 4).  The instruction order inside each half
+    // One stage s (ring slot s % NBUF).  The instruction order inside each half
     // is fixed in source order (sched_barrier): MFMA k, then fragment read k,
     // then load k, so reads and loads issue in the shadow of the MFMAs.
     // The compiler sees no global loads at all: the tile's scale vectors come
@@ -315,9 +315,10 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     // wait for the prefetch loads in flight.
     //
     // vmcnt bookkeeping at the mid-stage wait of stage s: the loads of stage
-    // s + 1 must have landed.  Issued after them are the loads of s + 2 and
-    // s + 3 (2 L), plus, on a tile's stages kt = 0 and 1, that tile's scale load
-    // (1) and, from the second tile on, the previous epilogue's NST stores.
+    // s + 1 must have landed.  Issued after them are the loads of s + 2 ..
+    // s + P ((P - 1) L), plus, on a tile's stages kt <= P - 2, that tile's
+    // scale load (1) and, from the second tile on, the previous epilogue's NST
+    // stores.
     // A smaller wait count than the number issued after is always safe.
     // W8A16: the W fragments of a k-slice widened to BF16 (two MFMA operands
     // each); fragment i + 1 is widened in the shadow of fragment i's MFMAs.

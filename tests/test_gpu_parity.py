@@ -545,6 +545,12 @@ def test_decode_gemm_bit_exact(orc, m, n, k):
 DECODE_LINEAR = [  # (m, k, n, act, g)
     (1, 1024, 4096, 0, 128), (7, 2048, 528, 1, 256), (33, 3072, 1040, 0, 128),
     (64, 12288, 3072, 1, 128), (64, 256, 16, 1, 64),
+    # the quantizer fused into the decode GEMM: x at m <= 2 (k <= 8192), SwiGLU at
+    # m == 1 (k <= 16384), groups 64, 128, 256; 1 to 4 chunks per lane, a row
+    # shorter than the team; then the first shapes past each limit
+    (1, 12288, 3072, 1, 128), (2, 3072, 1040, 0, 64), (1, 8192, 48, 0, 256),
+    (1, 16384, 32, 1, 256), (1, 64, 16, 0, 64), (2, 4096, 528, 0, 128),
+    (3, 256, 32, 0, 128), (2, 512, 16, 1, 128), (1, 8256, 16, 0, 64), (1, 1024, 64, 1, 32),
 ]
 
 
@@ -567,7 +573,7 @@ def test_int8_linear_decode_bit_exact(orc, m, k, n, act, g):
         bf16_host(y), orc.int8_linear(d["x"], act, wq_o, sw_o, g, bias=bias, residual=res))
 
 
-@pytest.mark.parametrize("m", [1, 16, 64])
+@pytest.mark.parametrize("m", [1, 2, 16, 64])
 def test_swiglu_mlp_decode_bit_exact(orc, m):
     say(f"swiglu_mlp decode m={m} h=1024 i=2816")
     h, i, g = 1024, 2816, 128
@@ -585,6 +591,28 @@ def test_swiglu_mlp_decode_bit_exact(orc, m):
     assert torch.equal(y.view(torch.int16), y_blk.view(torch.int16))
     (gq_o, gs_o), (dq_o, ds_o) = orc.weight_prep(w_gu, g), orc.weight_prep(w_dn, g)
     np.testing.assert_array_equal(bf16_host(y), orc.swiglu_mlp(xb, gq_o, gs_o, dq_o, ds_o, g))
+
+
+@pytest.mark.parametrize("m,k,act,g", [(1, 3072, 0, 128), (2, 3072, 0, 128), (2, 8192, 0, 64),
+                                        (1, 12288, 1, 128), (1, 4096, 1, 256)])
+def test_fused_decode_equals_the_stages(m, k, act, g):
+    """ck_int8_linear on decode weights at the fewest rows (one kernel that
+    quantizes the rows itself) equals ck_act_quant followed by the decode GEMM,
+    codes, scales and outputs alike, bit for bit, with bias and residual."""
+    say(f"fused decode vs stages m={m} k={k} act={act} g={g}")
+    n = 1040
+    rng = np.random.default_rng(77 + m + k)
+    d = W.case(m, k, n, act, seed=4000 + m)
+    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    wd = ck.ck_weight_pack_decode(wq, sw)
+    x = bf16_dev(d["x"])
+    bias = dev(rng.standard_normal(n).astype(np.float32))
+    res = bf16_dev(W.to_bf16_bits(rng.standard_normal((m, n)).astype(np.float32)))
+    y = ck.ck_int8_linear(x, wd, None, g, act, layout="decode", bias=bias, residual=res)
+    xq, sx = ck.ck_act_quant(x, act, g, k=k, layout="blocked")
+    y_st = ck.ck_int8_gemm_bf16(xq, sx, wd, None, layout="decode", bias=bias, residual=res)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_st.view(torch.int16))
 
 
 def test_decode_rejects_more_than_64_rows():

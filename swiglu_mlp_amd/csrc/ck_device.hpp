@@ -56,6 +56,26 @@ __device__ __forceinline__ void epi_extra4(float& y0, float& y1, float& y2, floa
     }
 }
 
+// Buffer-resource offset past the end of every buffer the kernels address: a
+// buffer load there returns zeros and a buffer store there is dropped, so
+// lanes with nothing to load or store still issue the same instructions.
+constexpr uint32_t kBufferOutside = 0x80000000u;
+
+// 8 INT8 weight codes (two dwords) -> 8 BF16 values, exact (|q| <= 127 has 7
+// significant bits): one v_cvt_f32_i32 (byte select, sign-extended) per value
+// and one v_cvt_pk_bf16_f32 per pair.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8_t widen8(int lo, int hi)
+{
+    bf16x8_t r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int w = e < 4 ? lo : hi;
+        r[e] = (__bf16)(float)(int)(signed char)(w >> (8 * (e & 3)));
+    }
+    return r;
+}
+
 // Two FP32 values -> packed BF16 pair (lo = a, hi = b), round-to-nearest-even:
 // one v_cvt_pk_bf16_f32 on gfx950.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -109,20 +109,6 @@ struct Cfg {
     static_assert(BLK % 4 == 0, "blocks must split evenly over 4 waves");
 };
 
-// 8 INT8 weight codes -> 8 BF16 values (exact: |q| <= 127 has 7 significant
-// bits); one v_cvt_f32_i32 (byte select, sign-extended) per value and one
-// v_cvt_pk_bf16_f32 per pair.
-__device__ __forceinline__ v8bf widen8(int lo, int hi)
-{
-    v8bf r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int w = e < 4 ? lo : hi;
-        r[e] = (__bf16)(float)(int)(signed char)(w >> (8 * (e & 3)));
-    }
-    return r;
-}
-
 __device__ __forceinline__ void tile_coords(int j, int tiles_m, int tiles_n, int group_m, int& tm,
                                             int& tn)
 {
@@ -477,7 +463,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
 #pragma unroll
                     for (int qd = 0; qd < 4; ++qd) {
                         const int n = n_base + 32 * i + 8 * qd;
-                        const uint32_t ob = n < N ? (row + (uint32_t)n) * 4u : 0x80000000u;
+                        const uint32_t ob = n < N ? (row + (uint32_t)n) * 4u : kBufferOutside;
                         const v4i d = __builtin_bit_cast(
                             v4i, (std::conditional_t<A16, float4, int4>){f[4 * qd], f[4 * qd + 1], f[4 * qd + 2],
                                                                          f[4 * qd + 3]});
@@ -526,7 +512,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
                         const auto r0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
                         const auto r1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
                         const int n = tn * BN + wn0 + 32 * i + 16 * h + 8 * lh;
-                        const uint32_t ob = n < N ? (row + (uint32_t)n) * 2u : 0x80000000u;
+                        const uint32_t ob = n < N ? (row + (uint32_t)n) * 2u : kBufferOutside;
                         const v4i d = {(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]};
                         __builtin_amdgcn_raw_buffer_store_b128(d, rs_o, ob, 0, 0);
                     }

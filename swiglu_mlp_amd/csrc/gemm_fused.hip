@@ -42,8 +42,6 @@ constexpr int WAVES = 8;
 constexpr int NT = WAVES * 64;   // threads per workgroup, all of them one quantizer team
 [[maybe_unused]] constexpr int U = 8;             // 64-byte k-chunks per batch per wave
 [[maybe_unused]] constexpr int PAD = 16;          // bytes after each LDS code row (spreads the 16 rows' banks)
-// offset past every buffer's end: a load there returns zeros, a store is dropped
-[[maybe_unused]] constexpr uint32_t kOutside = 0x80000000u;
 
 // ACT 0: x BF16 [M, ldx], up to 2 rows.  ACT 1: [gate | up] BF16 [M, ldx] with
 // SwiGLU, one row.  CH: 8-element chunks per lane, K <= 8 * NT * CH.
@@ -101,7 +99,7 @@ __global__ __launch_bounds__(NT) void gemm_dec_fused_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = wave + WAVES * (U * b + u);
-            w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, j < KC ? w_base + (uint32_t)j * 1024u : kOutside,
+            w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, j < KC ? w_base + (uint32_t)j * 1024u : kBufferOutside,
                                                          0, 0);
         }
     };
@@ -214,7 +212,7 @@ __global__ __launch_bounds__(NT) void gemm_dec_fused_kernel(
     epi_extra4(y0, y1, y2, y3, ex, xrow, n, N);
     const u32x2 d = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
     const uint32_t row = (uint32_t)m * (uint32_t)N + (uint32_t)n;
-    __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, m < M ? row * 2u : kOutside, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, m < M ? row * 2u : kBufferOutside, 0, 0);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 

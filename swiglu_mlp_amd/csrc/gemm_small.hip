@@ -36,8 +36,6 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int WAVES = 8;
-// offset past every buffer's end: a load there returns zeros, a store is dropped
-constexpr uint32_t kOutside = 0x80000000u;
 
 template <int MT, bool A16>
 struct SmallCfg {
@@ -46,18 +44,6 @@ struct SmallCfg {
                                  : (MT == 1 ? 8 : (MT == 2 ? 4 : (MT == 4 ? 3 : 2)));
     static constexpr int XP = A16 ? 2 : 1;   // activation pieces per chunk and fragment
 };
-
-// 8 INT8 weight codes -> 8 BF16 values (exact for |q| <= 127).
-__device__ __forceinline__ v8bf widen8(int lo, int hi)
-{
-    v8bf r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int w = e < 4 ? lo : hi;
-        r[e] = (__bf16)(float)(int)(signed char)(w >> (8 * (e & 3)));
-    }
-    return r;
-}
 
 // DEC: W in the decode layout (include/ck.h): each 16-row group one linear
 // stream, its row scales in the group's 64-byte header.
@@ -130,13 +116,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
             const int j = wave + WAVES * (U * b + u);
             const bool ok = j < KC;
             const uint32_t ko = (uint32_t)j * x_step;
-            w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, ok ? w_base + (uint32_t)j * w_step : kOutside, 0, 0);
+            w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, ok ? w_base + (uint32_t)j * w_step : kBufferOutside, 0, 0);
 #pragma unroll
             for (int f = 0; f < MT; ++f)
 #pragma unroll
                 for (int s = 0; s < XP; ++s)
                     x[u][f][s] = __builtin_amdgcn_raw_buffer_load_b128(
-                        rs_x, ok ? x_base[f] + ko + (uint32_t)s * 1024u : kOutside, 0, 0);
+                        rs_x, ok ? x_base[f] + ko + (uint32_t)s * 1024u : kBufferOutside, 0, 0);
         }
     };
     auto compute = [&](const v4i (&w)[U], const v4i (&x)[U][MT][XP]) {
@@ -185,7 +171,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const int n = nb * 16 + 4 * c;
     const uint32_t row = (uint32_t)m * (uint32_t)N + (uint32_t)n;
     if constexpr (OUT_I32) {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, t), rs_o, m < M ? row * 4u : kOutside, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, t), rs_o, m < M ? row * 4u : kBufferOutside, 0, 0);
     } else {
         const float4 s4 = DEC ? *reinterpret_cast<const float4*>(wq + (size_t)nb * grp_bytes + 16 * c)
                               : *reinterpret_cast<const float4*>(sw + n);
@@ -204,7 +190,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         }
         epi_extra4(y0, y1, y2, y3, ex, min(m, M - 1), n, N);
         const u32x2 d = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-        __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, m < M ? row * 2u : kOutside, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, m < M ? row * 2u : kBufferOutside, 0, 0);
     }
 #endif  // __HIP_DEVICE_COMPILE__
 }

@@ -29,8 +29,8 @@
 //     the 4 x 4-fragment waves of the 256 x 256 tile are the fastest shape: the
 //     2 x 2-fragment waves of the 128 x 128 tile read as many LDS bytes per
 //     MFMA as the LDS delivers.
-//   * K advances 2 KSL 32-byte k-slices per stage (64 bytes, or 128 for the
-//     few-tile GEMMs that use KSL = 2).  Stages live in a ring of (at most) 4
+//   * K advances 2 KSL 32-byte k-slices per stage (64 bytes, or 128 or 256
+//     for the few-tile GEMMs that use KSL = 2 or 4).  Stages live in a ring of (at most) 4
 //     LDS buffers; loads run 3 stages ahead.  Each stage is split in two halves
 //     around one barrier: the first half multiplies the first KSL k-slices,
 //     reads the last KSL k-slices' fragments and issues the loads of stage
@@ -87,7 +87,7 @@ __device__ __forceinline__ void workgroup_barrier()
 // CU.
 // The ring has as many slots as fit the LDS share of a workgroup (160 KB per
 // CU over the workgroups meant to share it: one for tiles of 256 x 192 and
-// larger and for KSL = 2, two otherwise; 6 KB of it go to scale buffers), at
+// larger and for KSL > 1, two otherwise; 6 KB of it go to scale buffers), at
 // most NMAX; P = NBUF - 1 stages are in flight.
 template <int BM_, int BN_, bool A16, int KSL_ = 1>
 struct Cfg {
@@ -598,25 +598,39 @@ int choose_shape(int64_t m, int64_t n, int num_cu)
     return best;
 }
 
-// A GEMM whose 64 x 128 tiles, or failing that 128 x 128 tiles, number at
-// most one per CU runs as a single round of those tiles with two k-slices per
-// half stage (KSL = 2): its time is then the per-stage fixed cost (barrier,
-// waits, LDS read latency) times the stage count, and KSL = 2 halves the
-// count.  Measured (MI355X, random operands, warm caches), INT8:
-// 2048 x 1024 x 3072 12.3 -> 10.8 us, 1024 x 1024 x 12288 33.5 -> 27.0 us,
-// 256 x 3072 x 12288 32.2 -> 26.1 us (64 x 128 tiles); 1024 x 4096 x 4096,
-// where 512 tiles of 64 x 128 would share CUs two by two, 23.8 us on those,
-// 20.7 us on 128 x 128 tiles with KSL = 2.  W8A16: 27.4 -> 24.8 us,
-// 89.5 -> 76.5 us, 89.8 -> 76.5 us and 50.4 -> 43.6 us on the same shapes.
-// Deeper rings (5 or 6 slots) and KSL = 4 measured slower.  Returns the shape
-// index, or -1.
-int two_slice_shape(int64_t m, int64_t n, int64_t k, int num_cu)
+// Few tiles: a GEMM whose tiles number at most one per CU runs as a single
+// round, and its time is the per-stage fixed cost (barrier, waits, LDS read
+// latency) times the stage count.  Such GEMMs take more k-slices per half
+// stage (KSL), which cuts the count, and the smallest tile that still keeps
+// to one per CU, which spreads the work over more CUs:
+//   * INT8, 64 x 64 tiles at most one per CU: KSL = 4 (k % 256 == 0), else 2;
+//   * else 64 x 128 tiles at most one per CU: KSL = 2;
+//   * else 128 x 128 tiles at most one per CU: KSL = 2.
+// Measured (MI355X, random operands, warm caches), INT8: 2048 x 1024 x 3072
+// 12.3 -> 10.8 us (64 x 128, KSL 2); 1024 x 4096 x 4096, where 512 tiles of
+// 64 x 128 would share CUs two by two, 23.8 us on those, 20.7 us on 128 x 128
+// tiles with KSL = 2; 256 x 3072 x 12288 32.2 us on 64 x 128 tiles, 26.1 us
+// with KSL = 2, 19.4 us on 64 x 64 tiles with KSL = 4 (20.4 with KSL = 2);
+// 1024 x 1024 x 12288 33.5 -> 27.0 -> 20.9 us the same way.  64 x 64 tiles
+// lose once they outnumber the CUs (512 x 3072 x 12288: 35.6 us against
+// 28.4 us on 64 x 128).  W8A16 (64 x 128 and 128 x 128 only): 27.4 -> 24.8
+// us, 89.5 -> 76.5 us, 89.8 -> 76.5 us and 50.4 -> 43.6 us on the first four
+// shapes.  Deeper rings (5 or 6 slots) and KSL = 4 on 64 x 128 measured
+// slower.
+struct FewTiles {
+    int shape;   // index as in choose_shape, 4 for 64 x 64; -1: not a few-tile GEMM
+    int ksl;
+};
+
+FewTiles few_tile_shape(int64_t m, int64_t n, int64_t k, int num_cu, bool a16)
 {
-    if (k % 128 != 0) return -1;
-    const int64_t tiles_n = (n + 127) / 128;
-    if (((m + 63) / 64) * tiles_n <= num_cu) return 1;
-    if (((m + 127) / 128) * tiles_n <= num_cu) return 0;
-    return -1;
+    if (k % 128 != 0) return {-1, 1};
+    const int64_t tm64 = (m + 63) / 64, tm128 = (m + 127) / 128;
+    const int64_t tn64 = (n + 63) / 64, tn128 = (n + 127) / 128;
+    if (!a16 && tm64 * tn64 <= num_cu) return {4, k % 256 == 0 ? 4 : 2};
+    if (tm64 * tn128 <= num_cu) return {1, 2};
+    if (tm128 * tn128 <= num_cu) return {0, 2};
+    return {-1, 1};
 }
 
 template <bool A16>
@@ -625,9 +639,9 @@ hipError_t launch_shape(const void* xq, const float* sx, const int8_t* wq, const
                         EpiExtra ex)
 {
     const int M = (int)m, N = (int)n, K = (int)k;
-    const int two = two_slice_shape(m, n, k, num_cu);
-    const bool ksl2 = two >= 0;
-    const int shape = ksl2 ? two : choose_shape(m, n, num_cu);
+    const FewTiles few = few_tile_shape(m, n, k, num_cu, A16);
+    const int ksl = few.ksl;
+    const int shape = few.shape >= 0 ? few.shape : choose_shape(m, n, num_cu);
 #define CK_BLK(BM_, BN_, KSL_)                                                                         \
     return out_raw                                                                                      \
                ? blk::launch<BM_, BN_, true, false, A16, KSL_>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex) \
@@ -636,11 +650,17 @@ hipError_t launch_shape(const void* xq, const float* sx, const int8_t* wq, const
                : blk::launch<BM_, BN_, false, false, A16, KSL_>(xq, sx, wq, sw, M, N, K, out, num_cu, st, ex)
     switch (shape) {
         case 0:
-            if (ksl2) CK_BLK(128, 128, 2);
+            if (ksl == 2) CK_BLK(128, 128, 2);
             CK_BLK(128, 128, 1);
         case 1:
-            if (ksl2) CK_BLK(64, 128, 2);
+            if (ksl == 2) CK_BLK(64, 128, 2);
             CK_BLK(64, 128, 1);
+        case 4:
+            if constexpr (!A16) {
+                if (ksl == 4) CK_BLK(64, 64, 4);
+                CK_BLK(64, 64, 2);
+            }
+            return hipErrorInvalidValue;   // not reached: W8A16 never takes 64 x 64 tiles
         case 2: CK_BLK(256, 256, 1);
         default: CK_BLK(256, 192, 1);
     }

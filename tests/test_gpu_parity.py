@@ -145,7 +145,10 @@ def test_act_rotate_bit_exact(orc, m, k, act, g):
     np.testing.assert_array_equal(u.view(np.uint32), orc.act_rotate(d["x"], act, g).view(np.uint32))
 
 
-GEMM_SHAPES = [  # (m, n, k): every tile shape, both k-step sizes, ragged m and n
+GEMM_SHAPES = [  # (m, n, k): every tile shape and k-step size, ragged m and n; the few-tile
+    # shapes: 64 x 64 tiles with four k-slices per half stage (300, 272, 1024), (48, 4112, 256)
+    # or two (600, 1200, 384), (100, 8192, 128); 64 x 128 with two (1000, 1040, 640),
+    # (2048, 1024, 3072); 128 x 128 with two (513, 4112, 128)
     (1, 16, 64), (64, 128, 256), (77, 144, 192), (300, 272, 1024), (1000, 1040, 640),
     (600, 1200, 384), (2048, 1024, 3072), (513, 4112, 128),
     # few rows on tiles (n > 16 * CUs): 64 x 128 and 128 x 128 tiles at m <= 128
@@ -377,11 +380,12 @@ def test_small_m_gemm_bit_exact(orc, m, n, k):
     np.testing.assert_array_equal(y, orc.dequant(acc_o, sx, sw))
 
 
-EXTRA_CASES = [  # (m, k, n, layout): few-row, 128-wide (one and two k-slices per half
-    # stage), 256x256 and 256x192 blocked tiles, ragged m and n, and both row-major kernels
+EXTRA_CASES = [  # (m, k, n, layout): few-row, 64x64 (four and two k-slices per half stage),
+    # 64x128 and 128x128 (one and two), 256x256 and 256x192 blocked tiles, ragged m and n,
+    # and both row-major kernels
     (5, 256, 48, "blocked"), (64, 512, 1040, "blocked"), (100, 512, 1040, "blocked"),
     (300, 1024, 272, "blocked"), (700, 256, 5008, "blocked"), (320, 256, 11008, "blocked"),
-    (1500, 384, 4000, "blocked"),
+    (1500, 384, 4000, "blocked"), (600, 384, 1200, "blocked"), (2048, 3072, 1024, "blocked"),
     (2000, 256, 8192, "blocked"), (2000, 256, 6144, "blocked"),
     (300, 1024, 272, "rows"), (2000, 256, 8192, "rows"),
 ]

@@ -603,7 +603,7 @@ int choose_shape(int64_t m, int64_t n, int num_cu)
 // latency) times the stage count.  Such GEMMs take more k-slices per half
 // stage (KSL), which cuts the count, and the smallest tile that still keeps
 // to one per CU, which spreads the work over more CUs:
-//   * INT8, 64 x 64 tiles at most one per CU: KSL = 4 (k % 256 == 0), else 2;
+//   * 64 x 64 tiles at most one per CU: KSL = 4 (k % 256 == 0), else 2;
 //   * else 64 x 128 tiles at most one per CU: KSL = 2;
 //   * else 128 x 128 tiles at most one per CU: KSL = 2.
 // Measured (MI355X, random operands, warm caches), INT8: 2048 x 1024 x 3072
@@ -613,21 +613,22 @@ int choose_shape(int64_t m, int64_t n, int num_cu)
 // with KSL = 2, 19.4 us on 64 x 64 tiles with KSL = 4 (20.4 with KSL = 2);
 // 1024 x 1024 x 12288 33.5 -> 27.0 -> 20.9 us the same way.  64 x 64 tiles
 // lose once they outnumber the CUs (512 x 3072 x 12288: 35.6 us against
-// 28.4 us on 64 x 128).  W8A16 (64 x 128 and 128 x 128 only): 27.4 -> 24.8
-// us, 89.5 -> 76.5 us, 89.8 -> 76.5 us and 50.4 -> 43.6 us on the first four
-// shapes.  Deeper rings (5 or 6 slots) and KSL = 4 on 64 x 128 measured
-// slower.
+// 28.4 us on 64 x 128).  W8A16: 27.4 -> 24.8 us and 50.4 -> 43.6 us on the
+// first two shapes (64 x 128 and 128 x 128, KSL 2), 256 x 3072 x 12288
+// 76.9 -> 48.5 us and 1024 x 1024 x 12288 77.2 -> 48.8 us going from 64 x 128
+// to 64 x 64 tiles.  Deeper rings (5 or 6 slots) and KSL = 4 on 64 x 128
+// measured slower.
 struct FewTiles {
     int shape;   // index as in choose_shape, 4 for 64 x 64; -1: not a few-tile GEMM
     int ksl;
 };
 
-FewTiles few_tile_shape(int64_t m, int64_t n, int64_t k, int num_cu, bool a16)
+FewTiles few_tile_shape(int64_t m, int64_t n, int64_t k, int num_cu)
 {
     if (k % 128 != 0) return {-1, 1};
     const int64_t tm64 = (m + 63) / 64, tm128 = (m + 127) / 128;
     const int64_t tn64 = (n + 63) / 64, tn128 = (n + 127) / 128;
-    if (!a16 && tm64 * tn64 <= num_cu) return {4, k % 256 == 0 ? 4 : 2};
+    if (tm64 * tn64 <= num_cu) return {4, k % 256 == 0 ? 4 : 2};
     if (tm64 * tn128 <= num_cu) return {1, 2};
     if (tm128 * tn128 <= num_cu) return {0, 2};
     return {-1, 1};
@@ -639,7 +640,7 @@ hipError_t launch_shape(const void* xq, const float* sx, const int8_t* wq, const
                         EpiExtra ex)
 {
     const int M = (int)m, N = (int)n, K = (int)k;
-    const FewTiles few = few_tile_shape(m, n, k, num_cu, A16);
+    const FewTiles few = few_tile_shape(m, n, k, num_cu);
     const int ksl = few.ksl;
     const int shape = few.shape >= 0 ? few.shape : choose_shape(m, n, num_cu);
 #define CK_BLK(BM_, BN_, KSL_)                                                                         \
@@ -656,11 +657,8 @@ hipError_t launch_shape(const void* xq, const float* sx, const int8_t* wq, const
             if (ksl == 2) CK_BLK(64, 128, 2);
             CK_BLK(64, 128, 1);
         case 4:
-            if constexpr (!A16) {
-                if (ksl == 4) CK_BLK(64, 64, 4);
-                CK_BLK(64, 64, 2);
-            }
-            return hipErrorInvalidValue;   // not reached: W8A16 never takes 64 x 64 tiles
+            if (ksl == 4) CK_BLK(64, 64, 4);
+            CK_BLK(64, 64, 2);
         case 2: CK_BLK(256, 256, 1);
         default: CK_BLK(256, 192, 1);
     }

@@ -695,7 +695,8 @@ def test_act_rotate_bf16_bit_exact(orc, m, k, act, g):
 
 
 W8A16_GEMM_SHAPES = [  # (m, n, k): every tile shape, k-stage counts 1, 2, 3 and more,
-    # ragged m and n, a partial last round of tiles
+    # ragged m and n, a partial last round of tiles; the few-tile shapes: 64 x 64 with four
+    # k-slices per half stage (300, 272, 1024), (48, 4112, 256) or two (100, 8192, 128)
     (77, 144, 192), (300, 272, 1024), (1000, 1040, 640),
     (513, 4112, 128), (4000, 4080, 192), (4000, 3056, 320), (2560, 6144, 256), (2048, 1024, 3072),
     # the few-row kernel (m <= 64): 1, 2 and 4 row fragments, short and long k

@@ -253,7 +253,7 @@ def decode_mlp(steps: int, warmup: int):
         torch.cuda.synchronize()
         us_graph = e0.elapsed_time(e1) * 1000.0 / steps
         kernels = ["gate_up with the x quantizer inside" if m <= 2 else "x quant", "gate_up"][: 1 if m <= 2 else 2]
-        kernels += ["down with the SwiGLU quantizer inside"] if m == 1 else ["SwiGLU quant", "down"]
+        kernels += ["down with the SwiGLU quantizer inside"] if m <= 2 else ["SwiGLU quant", "down"]
         print(json.dumps({"decode_mlp": {"m": m, "hidden": h, "intermediate": inter, "us": round(us, 2),
                                          "weight_MB": round(wbytes / 1e6, 1),
                                          "GBs_weights": round(wbytes / us / 1e3, 1),

@@ -193,8 +193,8 @@ ck_status ck_act_quant(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,
  *   y        [m, n] BF16, written (row stride n)
  *   workspace  device buffer of at least ck_int8_linear_workspace_size(m, k)
  *            bytes, 256-byte aligned; clobbered (holds x_q and x_scale).
- *            With CK_LAYOUT_DECODE at m <= 2 (act none, k <= 8192) or m == 1
- *            (SwiGLU, k <= 16384), group 64, 128 or 256, the quantizer runs
+ *            With CK_LAYOUT_DECODE at m <= 2 (k <= 8192, or k <= 16384 with
+ *            SwiGLU), group 64, 128 or 256, the quantizer runs
  *            inside the GEMM kernel and the workspace is left untouched (it is
  *            still required); the result is the same bit for bit. */
 ck_status ck_int8_linear(const uint16_t *x, int64_t ldx, int32_t act,

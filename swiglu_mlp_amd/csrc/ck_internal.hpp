@@ -25,8 +25,8 @@ hipError_t launch_rotate_bf16(int kind, const void* src, int64_t ld, int64_t m, 
                               uint16_t* out, bool blocked, hipStream_t st);
 
 // The decode-layout GEMM with the activation quantizer fused in front, for the
-// fewest rows: act 0 (BF16 x [m, ldx], m <= 2, k <= 8192) or 1 (BF16
-// [gate | up] [m, ldx] with SwiGLU, m == 1, k <= 16384), g in {64, 128, 256}.
+// fewest rows (m <= 2): act 0 (BF16 x [m, ldx], k <= 8192) or 1 (BF16
+// [gate | up] [m, ldx] with SwiGLU, k <= 16384), g in {64, 128, 256}.
 // Writes y = bf16(fl(fl(f32(acc) * sx[m]) * sw[n])) (+ ex) with the codes and
 // scales launch_quant_rows would have written.
 bool use_fused_decode(int act, int64_t m, int64_t k, int g);

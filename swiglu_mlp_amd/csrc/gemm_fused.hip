@@ -26,9 +26,10 @@
 // evicts the MALL): at M = 1, 41.0 us with separate quantizers, 35.6 with the
 // x quantizer fused, 29.8 with both; at M = 2, 41.5 -> 37.7 us with the x
 // quantizer fused; at M = 3 and 4 the fused x quantizer is slower back to
-// back (31.7 -> 34.2 us, 31.9 -> 37.4 us).  So the x variant takes up to 2
-// rows and the SwiGLU variant, which repeats silu, the rotation and the
-// absmax of a whole row of i values in each workgroup, one row.
+// back (31.7 -> 34.2 us, 31.9 -> 37.4 us).  The SwiGLU variant repeats
+// silu, the rotation and the absmax of whole rows of i values in each
+// workgroup; at M = 2 it still gains a little (37.5 -> 35.8 us).  So both
+// variants take up to 2 rows.
 #include "ck_device.hpp"
 #include "ck_internal.hpp"
 
@@ -43,11 +44,11 @@ constexpr int NT = WAVES * 64;   // threads per workgroup, all of them one quant
 [[maybe_unused]] constexpr int U = 8;             // 64-byte k-chunks per batch per wave
 [[maybe_unused]] constexpr int PAD = 16;          // bytes after each LDS code row (spreads the 16 rows' banks)
 
-// ACT 0: x BF16 [M, ldx], up to 2 rows.  ACT 1: [gate | up] BF16 [M, ldx] with
-// SwiGLU, one row.  CH: 8-element chunks per lane, K <= 8 * NT * CH.
+// ACT 0: x BF16 [M, ldx]; ACT 1: [gate | up] BF16 [M, ldx] with SwiGLU; up to
+// 2 rows.  CH: 8-element chunks per lane, K <= 8 * NT * CH.
 template <int ACT>
 struct FusedCfg {
-    static constexpr int MAXR = ACT ? 1 : 2;
+    static constexpr int MAXR = 2;
 };
 
 template <int ACT, int LOG_G, int CH>
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(NT) void gemm_dec_fused_kernel(
 
     // ---- the rows' raw BF16 data (issued first: the quantizer waits on it,
     // not on the weight loads issued after it) --------------------------------
-    uint4 rg[MAXR][CH], ru[ACT ? CH : 1];
+    uint4 rg[MAXR][CH], ru[ACT ? MAXR : 1][ACT ? CH : 1];
 #pragma unroll
     for (int m = 0; m < MAXR; ++m) {
         const uint16_t* rp = x + (int64_t)(m < M ? m : 0) * ldx;
@@ -83,7 +84,8 @@ __global__ __launch_bounds__(NT) void gemm_dec_fused_kernel(
             const int c = j * NT + tid;
             const bool ok = m < M && c < k8;
             rg[m][j] = ok ? *reinterpret_cast<const uint4*>(rp + c * 8) : make_uint4(0u, 0u, 0u, 0u);
-            if constexpr (ACT) ru[j] = ok ? *reinterpret_cast<const uint4*>(rp + K + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+            if constexpr (ACT)
+                ru[m][j] = ok ? *reinterpret_cast<const uint4*>(rp + K + c * 8) : make_uint4(0u, 0u, 0u, 0u);
         }
     }
 
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(NT) void gemm_dec_fused_kernel(
                 v[j][2 * e + 1] = bf16_hi(w[e]);
             }
             if constexpr (ACT) {
-                const uint32_t wu[4] = {ru[j].x, ru[j].y, ru[j].z, ru[j].w};
+                const uint32_t wu[4] = {ru[m][j].x, ru[m][j].y, ru[m][j].z, ru[m][j].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     v[j][2 * e] = silu_f32(v[j][2 * e]) * bf16_lo(wu[e]);

@@ -549,12 +549,13 @@ def test_decode_gemm_bit_exact(orc, m, n, k):
 DECODE_LINEAR = [  # (m, k, n, act, g)
     (1, 1024, 4096, 0, 128), (7, 2048, 528, 1, 256), (33, 3072, 1040, 0, 128),
     (64, 12288, 3072, 1, 128), (64, 256, 16, 1, 64),
-    # the quantizer fused into the decode GEMM: x at m <= 2 (k <= 8192), SwiGLU at
-    # m == 1 (k <= 16384), groups 64, 128, 256; 1 to 4 chunks per lane, a row
-    # shorter than the team; then the first shapes past each limit
+    # the quantizer fused into the decode GEMM at m <= 2: x (k <= 8192) and SwiGLU
+    # (k <= 16384), groups 64, 128, 256; 1 to 4 chunks per lane, a row shorter than
+    # the team; then the first shapes past each limit
     (1, 12288, 3072, 1, 128), (2, 3072, 1040, 0, 64), (1, 8192, 48, 0, 256),
-    (1, 16384, 32, 1, 256), (1, 64, 16, 0, 64), (2, 4096, 528, 0, 128),
-    (3, 256, 32, 0, 128), (2, 512, 16, 1, 128), (1, 8256, 16, 0, 64), (1, 1024, 64, 1, 32),
+    (1, 16384, 32, 1, 256), (1, 64, 16, 0, 64), (2, 4096, 528, 0, 128), (2, 512, 16, 1, 128),
+    (2, 12288, 528, 1, 256), (3, 256, 32, 0, 128), (3, 512, 16, 1, 128), (1, 8256, 16, 0, 64),
+    (1, 1024, 64, 1, 32),
 ]
 
 
@@ -598,7 +599,7 @@ def test_swiglu_mlp_decode_bit_exact(orc, m):
 
 
 @pytest.mark.parametrize("m,k,act,g", [(1, 3072, 0, 128), (2, 3072, 0, 128), (2, 8192, 0, 64),
-                                        (1, 12288, 1, 128), (1, 4096, 1, 256)])
+                                        (1, 12288, 1, 128), (1, 4096, 1, 256), (2, 12288, 1, 128)])
 def test_fused_decode_equals_the_stages(m, k, act, g):
     """ck_int8_linear on decode weights at the fewest rows (one kernel that
     quantizes the rows itself) equals ck_act_quant followed by the decode GEMM,

@@ -25,6 +25,8 @@
 #include "ck_device.hpp"
 #include "ck_internal.hpp"
 
+#include <atomic>
+
 namespace ck {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -232,16 +234,17 @@ bool use_small_kernel(int64_t m, int64_t n)
 
 int num_cus()
 {
-    static int cached[64] = {0};
+    // per-device cache; threads may race to fill an entry, all with the same value
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 namespace {

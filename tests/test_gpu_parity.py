@@ -950,13 +950,18 @@ def test_concurrent_calls_on_separate_streams():
 
 
 def _random_cases(count, seed):
+    """Random (m, k, n, act, group, layout, epilogue): m drawn from 1..3 (the
+    fused decode kernel), 1..64 and 65..799; k either a few groups or a multiple
+    of 128 up to 4096 (the few-tile kernels' two and four k-slices)."""
     rng = np.random.default_rng(seed)
     cases = []
     for _ in range(count):
         g = int(rng.choice([32, 64, 128, 256]))
-        k = g * int(rng.integers(1, 8)) if g >= 64 else 64 * int(rng.integers(1, 8))
+        k = int(rng.choice([g * int(rng.integers(1, 9)), 128 * int(rng.integers(1, 33))]))
+        step = max(g, 64)
+        k = max(step, (k + step - 1) // step * step)
         n = 16 * int(rng.integers(1, 300))
-        m = int(rng.choice([int(rng.integers(1, 65)), int(rng.integers(65, 700))]))
+        m = int(rng.choice([int(rng.integers(1, 4)), int(rng.integers(1, 65)), int(rng.integers(65, 800))]))
         layout = str(rng.choice(["rows", "blocked", "decode"] if m <= 64 else ["rows", "blocked"]))
         act = int(rng.integers(0, 2))
         extra = bool(rng.integers(0, 2))
@@ -964,7 +969,7 @@ def _random_cases(count, seed):
     return cases
 
 
-@pytest.mark.parametrize("m,k,n,act,g,layout,extra", _random_cases(24, 2024))
+@pytest.mark.parametrize("m,k,n,act,g,layout,extra", _random_cases(96, 2024))
 def test_random_shapes_bit_exact(orc, m, k, n, act, g, layout, extra):
     """Seeded random shapes over every layout, activation, group and epilogue:
     bit-exact against the oracle."""
@@ -986,3 +991,16 @@ def test_random_shapes_bit_exact(orc, m, k, n, act, g, layout, extra):
                           residual=None if res is None else bf16_dev(res))
     np.testing.assert_array_equal(bf16_host(y), orc.int8_linear(d["x"], act, wq_o, sw_o, g, bias=bias,
                                                                 residual=res))
+
+
+def _random_w8a16_shapes(count, seed):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 800)), 16 * int(rng.integers(1, 300)), 64 * int(rng.integers(1, 64)))
+            for _ in range(count)]
+
+
+@pytest.mark.parametrize("m,n,k", _random_w8a16_shapes(32, 2025))
+def test_random_w8a16_gemm_exact(orc, m, n, k):
+    """Seeded random W8A16 GEMM shapes on integer activations (exact in any
+    summation order): accumulators and outputs bit-exact."""
+    test_w8a16_gemm_exact_on_integer_activations(orc, m, n, k)

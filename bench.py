@@ -186,10 +186,11 @@ def small_m_sweep(steps: int, warmup: int):
                       flush=True)
 
 
-def decode_mlp(steps: int, warmup: int):
+def decode_mlp(steps: int, warmup: int, w8a16: bool = False):
     """The c5 SwiGLU MLP block (hidden 3072, intermediate 12288, group 128) at
     decode sizes, M in {1, 2, 8, 16, 64}, through ck_swiglu_mlp with both weights
-    in the decode layout.  Bound by HBM: the weights (2 I H + H I bytes of codes
+    in the decode layout, or (w8a16) through ck_swiglu_mlp_w8a16 with both in
+    the blocked layout.  Bound by HBM: the weights (2 I H + H I bytes of codes
     plus their scales) are read once per call."""
     import torch
     import swiglu_mlp_amd as ck
@@ -202,17 +203,30 @@ def decode_mlp(steps: int, warmup: int):
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     wgu = torch.randint(-127, 128, (2 * inter, h), dtype=torch.int8, device=dev, generator=gen)
     wd = torch.randint(-127, 128, (h, inter), dtype=torch.int8, device=dev, generator=gen)
-    dgu = ck.ck_weight_pack_decode(wgu, torch.rand(2 * inter, device=dev, generator=gen) * 1e-3)
-    dd = ck.ck_weight_pack_decode(wd, torch.rand(h, device=dev, generator=gen) * 1e-3)
-    wbytes = dgu.numel() + dd.numel()
+    sgu = torch.rand(2 * inter, device=dev, generator=gen) * 1e-3
+    sd = torch.rand(h, device=dev, generator=gen) * 1e-3
+    if w8a16:
+        dgu, dd = ck.ck_weight_pack(wgu), ck.ck_weight_pack(wd)
+        wbytes = wgu.numel() + wd.numel() + 4 * (2 * inter + h)
+    else:
+        dgu, dd = ck.ck_weight_pack_decode(wgu, sgu), ck.ck_weight_pack_decode(wd, sd)
+        wbytes = dgu.numel() + dd.numel()
     for m in (1, 2, 8, 16, 64):
         x = (torch.randn((m, h), device=dev, generator=gen)).to(torch.bfloat16)
         y = torch.empty((m, h), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(max(L.ck_swiglu_mlp_workspace_size(m, h, inter), 1), dtype=torch.uint8, device=dev)
+        wsz = L.ck_swiglu_mlp_w8a16_workspace_size(m, h, inter) if w8a16 else \
+            L.ck_swiglu_mlp_workspace_size(m, h, inter)
+        ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
 
         def call(st=stream):
-            rc = L.ck_swiglu_mlp(x.data_ptr(), dgu.data_ptr(), None, dd.data_ptr(), None, ck.CK_LAYOUT_DECODE,
-                                 m, h, inter, g, y.data_ptr(), ws.data_ptr(), ws.numel(), st.cuda_stream)
+            if w8a16:
+                rc = L.ck_swiglu_mlp_w8a16(x.data_ptr(), dgu.data_ptr(), sgu.data_ptr(), dd.data_ptr(),
+                                           sd.data_ptr(), m, h, inter, g, y.data_ptr(), ws.data_ptr(),
+                                           ws.numel(), st.cuda_stream)
+            else:
+                rc = L.ck_swiglu_mlp(x.data_ptr(), dgu.data_ptr(), None, dd.data_ptr(), None,
+                                     ck.CK_LAYOUT_DECODE, m, h, inter, g, y.data_ptr(), ws.data_ptr(),
+                                     ws.numel(), st.cuda_stream)
             if rc:
                 raise RuntimeError(L.ck_status_str(rc).decode())
         for _ in range(warmup):
@@ -252,9 +266,14 @@ def decode_mlp(steps: int, warmup: int):
         e1.record(cur)
         torch.cuda.synchronize()
         us_graph = e0.elapsed_time(e1) * 1000.0 / steps
-        kernels = ["gate_up with the x quantizer inside" if m <= 2 else "x quant", "gate_up"][: 1 if m <= 2 else 2]
-        kernels += ["down with the SwiGLU quantizer inside"] if m <= 2 else ["SwiGLU quant", "down"]
-        print(json.dumps({"decode_mlp": {"m": m, "hidden": h, "intermediate": inter, "us": round(us, 2),
+        step = "rotation" if w8a16 else "quantizer"
+        kernels = [f"gate_up with the x {step} inside"] if m <= 2 else [f"x {'rotate' if w8a16 else 'quant'}",
+                                                                        "gate_up"]
+        kernels += [f"down with the SwiGLU {step} inside"] if m <= 2 else \
+            [f"SwiGLU {'rotate' if w8a16 else 'quant'}", "down"]
+        print(json.dumps({"decode_mlp": {"m": m, "hidden": h, "intermediate": inter,
+                                         "variant": "W8A16, blocked weights" if w8a16 else "INT8, decode weights",
+                                         "us": round(us, 2),
                                          "weight_MB": round(wbytes / 1e6, 1),
                                          "GBs_weights": round(wbytes / us / 1e3, 1),
                                          "frac_hbm_peak": round(wbytes / us / 1e3 / PEAK_HBM_GBS, 4),
@@ -308,7 +327,7 @@ def main():
         small_m_sweep(args.steps, args.warmup)
         return
     if args.decode_mlp:
-        decode_mlp(args.steps, args.warmup)
+        decode_mlp(args.steps, args.warmup, args.w8a16)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -277,7 +277,9 @@ ck_status ck_w8a16_gemm_bf16(const uint16_t *x_rot, const int8_t *w_q, const flo
 /* The W8A16 linear: ck_act_rotate_bf16 (blocked) into the workspace, then
  * ck_w8a16_gemm_bf16.  Arguments as ck_int8_linear with w_q in
  * CK_LAYOUT_BLOCKED; workspace of ck_int8_linear_w8a16_workspace_size(m, k)
- * bytes, 256-byte aligned, clobbered. */
+ * bytes, 256-byte aligned, clobbered.  At m <= 2 (k <= 8192, or k <= 16384
+ * with CK_ACT_SWIGLU; group 64, 128 or 256) one kernel rotates the rows
+ * itself and the workspace is left untouched; the output is the same bits. */
 ck_status ck_int8_linear_w8a16(const uint16_t *x, int64_t ldx, int32_t act, const int8_t *w_q,
                                const float *w_scale, const float *bias, const uint16_t *residual,
                                int64_t m, int64_t n, int64_t k, int32_t group, uint16_t *y,
@@ -288,7 +290,9 @@ size_t ck_int8_linear_w8a16_workspace_size(int64_t m, int64_t k);
  * rotated activations kept in BF16): rotate x, the packed [gate | up] W8A16
  * GEMM to BF16, then silu(gate) * up rotated to BF16 and the down W8A16 GEMM.
  * Weights in CK_LAYOUT_BLOCKED; workspace of
- * ck_swiglu_mlp_w8a16_workspace_size(m, h, i) bytes, 256-byte aligned. */
+ * ck_swiglu_mlp_w8a16_workspace_size(m, h, i) bytes, 256-byte aligned.  At
+ * the sizes where ck_int8_linear_w8a16 is one kernel, each stage's rotation
+ * runs inside its GEMM and the rotated activations are not written. */
 ck_status ck_swiglu_mlp_w8a16(const uint16_t *x, const int8_t *w_gu, const float *s_gu,
                               const int8_t *w_down, const float *s_down, int64_t m, int64_t h,
                               int64_t i, int32_t group, uint16_t *y, void *workspace,

@@ -366,7 +366,11 @@ ck_status ck_int8_linear_w8a16(const uint16_t* x, int64_t ldx, int32_t act, cons
         return CK_EWORKSPACE;
     uint16_t* xr = static_cast<uint16_t*>(workspace);
     hipStream_t st = (hipStream_t)stream;
-    CK_TRY(from_hip(ck::launch_rotate_bf16(act == CK_ACT_SWIGLU ? 1 : 0, x, ldx, m, k, group, xr, true, st)));
+    const int kind = act == CK_ACT_SWIGLU ? 1 : 0;
+    if (ck::use_fused_decode(kind, m, k, group))   // rotation inside the GEMM: one launch
+        return from_hip(ck::launch_gemm_w8a16_fused(kind, x, ldx, m, k, group, w_q, w_scale, n, y, st,
+                                                    ck::EpiExtra{bias, residual}));
+    CK_TRY(from_hip(ck::launch_rotate_bf16(kind, x, ldx, m, k, group, xr, true, st)));
     return from_hip(ck::launch_gemm_w8a16(xr, w_q, w_scale, m, n, k, y, false, st,
                                           ck::EpiExtra{bias, residual}));
 }
@@ -405,8 +409,15 @@ ck_status ck_swiglu_mlp_w8a16(const uint16_t* x, const int8_t* w_gu, const float
     uint16_t* y1 = reinterpret_cast<uint16_t*>(p);      p += round_up(M * 2 * I * 2);
     uint16_t* hr = reinterpret_cast<uint16_t*>(p);
     hipStream_t st = (hipStream_t)stream;
-    CK_TRY(from_hip(ck::launch_rotate_bf16(0, x, h, m, h, group, xr, true, st)));
-    CK_TRY(from_hip(ck::launch_gemm_w8a16(xr, w_gu, s_gu, m, 2 * i, h, y1, false, st)));
+    // at the fewest rows each stage's rotation runs inside its GEMM
+    if (ck::use_fused_decode(0, m, h, group)) {
+        CK_TRY(from_hip(ck::launch_gemm_w8a16_fused(0, x, h, m, h, group, w_gu, s_gu, 2 * i, y1, st)));
+    } else {
+        CK_TRY(from_hip(ck::launch_rotate_bf16(0, x, h, m, h, group, xr, true, st)));
+        CK_TRY(from_hip(ck::launch_gemm_w8a16(xr, w_gu, s_gu, m, 2 * i, h, y1, false, st)));
+    }
+    if (ck::use_fused_decode(1, m, i, group))
+        return from_hip(ck::launch_gemm_w8a16_fused(1, y1, 2 * i, m, i, group, w_down, s_down, h, y, st));
     CK_TRY(from_hip(ck::launch_rotate_bf16(1, y1, 2 * i, m, i, group, hr, true, st)));
     return from_hip(ck::launch_gemm_w8a16(hr, w_down, s_down, m, h, i, y, false, st));
 }

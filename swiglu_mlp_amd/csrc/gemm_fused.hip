@@ -38,6 +38,7 @@ namespace fused {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int WAVES = 8;
 constexpr int NT = WAVES * 64;   // threads per workgroup, all of them one quantizer team
@@ -218,6 +219,166 @@ __global__ __launch_bounds__(NT) void gemm_dec_fused_kernel(
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// ---- W8A16 ---------------------------------------------------------------
+// The same fusion for the W8A16 linear (comfy-kitchen PR #277, "Notes for the
+// reviewer": the activation rotated but kept in BF16): every workgroup of the
+// few-row W8A16 GEMM (gemm_small.hip; 16 weight rows in the blocked layout)
+// rotates the rows into LDS as BF16, x_rot = bf16(fl(u * c_g)), the rotation
+// kernel's own FP32 steps, then streams its weights against them.  No absmax,
+// so no reduction across the team before the codes are known.  Each wave
+// takes the k-chunks wave + 8 i in increasing order and does the two BF16
+// MFMAs of a chunk in the same order as the few-row kernel, and the waves are
+// summed in the same order, so the output equals the two-launch path's bit for
+// bit.
+constexpr int PADH = 8;   // BF16 values after each LDS row (16 bytes)
+
+template <int ACT, int LOG_G, int CH>
+__global__ __launch_bounds__(NT) void gemm_w8a16_fused_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const int8_t* __restrict__ wq, const float* __restrict__ sw,
+    int M, int N, int K, int n_rows, float cg, void* __restrict__ out, EpiExtra ex)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int G = 1 << LOG_G;
+    constexpr int MAXR = FusedCfg<ACT>::MAXR;
+    constexpr int KMAX = 8 * NT * CH;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[MAXR * (KMAX + PADH)];
+    __shared__ v4f red[WAVES][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nb = blockIdx.x;       // 16-row group of W (output columns 16 nb ..)
+    const int KB = K >> 5;           // 1 KB blocks per 32-row block of W
+    const int KC = K >> 6;           // 64-value k-chunks
+    const int k8 = K >> 3;
+    const int xs_stride = K + PADH;
+
+    uint4 rg[MAXR][CH], ru[ACT ? MAXR : 1][ACT ? CH : 1];
+#pragma unroll
+    for (int m = 0; m < MAXR; ++m) {
+        const uint16_t* rp = x + (int64_t)(m < M ? m : 0) * ldx;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = j * NT + tid;
+            const bool ok = m < M && c < k8;
+            rg[m][j] = ok ? *reinterpret_cast<const uint4*>(rp + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+            if constexpr (ACT)
+                ru[m][j] = ok ? *reinterpret_cast<const uint4*>(rp + K + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+
+    // W in the blocked layout: the 16 bytes of lane l = 16 c + r for chunk j
+    // (row r of the group, k = 64 j + 16 c ..) sit in 1 KB block 2 j + c / 2 of
+    // the 32-row block nb / 2, half c % 2, at row offset 16 r (+ 256 for the
+    // odd 16-row group).
+    const int r16 = lane & 15;
+    const int cq = lane >> 4;
+    const __amdgpu_buffer_rsrc_t rs_w =
+        __builtin_amdgcn_make_buffer_rsrc((void*)wq, (short)0, n_rows * K, 0x00020000);
+    const uint32_t w_base = (uint32_t)((nb >> 1) * KB) * 1024u + (uint32_t)(nb & 1) * 256u +
+                            (uint32_t)((cq >> 1) * 1024 + (cq & 1) * 512 + r16 * 16);
+    auto load_w = [&](int b, v4i (&w)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = wave + WAVES * (U * b + u);
+            w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, j < KC ? w_base + (uint32_t)j * 2048u : kBufferOutside,
+                                                         0, 0);
+        }
+    };
+    const int batches = (KC + WAVES * U - 1) / (WAVES * U);
+    v4i wa[U], wb[U];
+    __builtin_amdgcn_sched_barrier(0);   // keep the row loads ahead of the weight loads
+    load_w(0, wa);
+    if (batches > 1) load_w(1, wb);
+
+    // ---- rotate the rows into LDS (the rotation kernel's steps) ------------
+#pragma unroll
+    for (int m = 0; m < MAXR; ++m) {
+        if (m >= M) break;
+        float v[CH][8];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const uint32_t w[4] = {rg[m][j].x, rg[m][j].y, rg[m][j].z, rg[m][j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[j][2 * e] = bf16_lo(w[e]);
+                v[j][2 * e + 1] = bf16_hi(w[e]);
+            }
+            if constexpr (ACT) {
+                const uint32_t wu[4] = {ru[m][j].x, ru[m][j].y, ru[m][j].z, ru[m][j].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[j][2 * e] = silu_f32(v[j][2 * e]) * bf16_lo(wu[e]);
+                    v[j][2 * e + 1] = silu_f32(v[j][2 * e + 1]) * bf16_hi(wu[e]);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            fwht_in_lane<G>(v[j]);
+            fwht_cross_lane<G>(v[j], tid);
+            const int c = j * NT + tid;
+            const uint4 h = make_uint4(pack_bf16x2(v[j][0] * cg, v[j][1] * cg), pack_bf16x2(v[j][2] * cg, v[j][3] * cg),
+                                       pack_bf16x2(v[j][4] * cg, v[j][5] * cg), pack_bf16x2(v[j][6] * cg, v[j][7] * cg));
+            if (c < k8) *reinterpret_cast<uint4*>(xs + m * xs_stride + c * 8) = h;
+        }
+    }
+    __syncthreads();
+
+    // ---- the weight stream against the LDS rows ----------------------------
+    // lane l's activation pieces of chunk j: row l % 16 (rows past M read row
+    // M - 1; their outputs are not stored), k = 64 j + 16 (l / 16) + 8 s, s < 2
+    const int xrow = r16 < M ? r16 : M - 1;
+    const uint16_t* xl = xs + xrow * xs_stride + cq * 16;
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute = [&](int b, const v4i (&w)[U]) {
+        v4i xv[U][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = wave + WAVES * (U * b + u);
+            const bool ok = j < KC;
+            xv[u][0] = ok ? *reinterpret_cast<const v4i*>(xl + j * 64) : v4i{0, 0, 0, 0};
+            xv[u][1] = ok ? *reinterpret_cast<const v4i*>(xl + j * 64 + 8) : v4i{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bf16x8_t w0 = widen8(w[u][0], w[u][1]), w1 = widen8(w[u][2], w[u][3]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, __builtin_bit_cast(bf16x8_t, xv[u][0]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, __builtin_bit_cast(bf16x8_t, xv[u][1]), acc, 0, 0, 0);
+        }
+    };
+    for (int b = 0; b < batches; b += 2) {
+        compute(b, wa);
+        if (b + 2 < batches) load_w(b + 2, wa);
+        if (b + 1 >= batches) break;
+        compute(b + 1, wb);
+        if (b + 3 < batches) load_w(b + 3, wb);
+    }
+
+    // ---- sum the waves' partial accumulators (in wave order) ----------------
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    v4f t = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) t += red[w][lane];
+
+    // ---- epilogue: lane l holds D[n = 4 (l / 16) + i][m = l % 16], i < 4 ----
+    const int m = r16;
+    const int n = nb * 16 + 4 * cq;
+    const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(out, (short)0, M * N * 2, 0x00020000);
+    const float4 s4 = *reinterpret_cast<const float4*>(sw + n);
+    float y0 = t[0] * s4.x;
+    float y1 = t[1] * s4.y;
+    float y2 = t[2] * s4.z;
+    float y3 = t[3] * s4.w;
+    epi_extra4(y0, y1, y2, y3, ex, xrow, n, N);
+    const u32x2 d = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+    const uint32_t row = (uint32_t)m * (uint32_t)N + (uint32_t)n;
+    __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, m < M ? row * 2u : kBufferOutside, 0, 0);
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
 template <int ACT, int LOG_G, int CH>
 void launch_ch(const uint16_t* x, int64_t ldx, const int8_t* wq, int M, int N, int K, float cg, uint16_t* y,
                hipStream_t st, EpiExtra ex)
@@ -239,6 +400,36 @@ hipError_t launch_g(int ch, const uint16_t* x, int64_t ldx, const int8_t* wq, in
             launch_ch<ACT, LOG_G, 3>(x, ldx, wq, M, N, K, cg, y, st, ex);
         else if (ch == 4)
             launch_ch<ACT, LOG_G, 4>(x, ldx, wq, M, N, K, cg, y, st, ex);
+        else
+            return hipErrorInvalidValue;
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int ACT, int LOG_G, int CH>
+void launch_w8_ch(const uint16_t* x, int64_t ldx, const int8_t* wq, const float* sw, int M, int N, int K,
+                  float cg, uint16_t* y, hipStream_t st, EpiExtra ex)
+{
+    const int n_rows = (N + 255) / 256 * 256;
+    hipLaunchKernelGGL((gemm_w8a16_fused_kernel<ACT, LOG_G, CH>), dim3(N / 16), dim3(NT), 0, st, x, ldx, wq, sw, M,
+                       N, K, n_rows, cg, static_cast<void*>(y), ex);
+}
+
+template <int ACT, int LOG_G>
+hipError_t launch_w8_g(int ch, const uint16_t* x, int64_t ldx, const int8_t* wq, const float* sw, int M, int N,
+                       int K, float cg, uint16_t* y, hipStream_t st, EpiExtra ex)
+{
+    if (ch == 1)
+        launch_w8_ch<ACT, LOG_G, 1>(x, ldx, wq, sw, M, N, K, cg, y, st, ex);
+    else if (ch == 2)
+        launch_w8_ch<ACT, LOG_G, 2>(x, ldx, wq, sw, M, N, K, cg, y, st, ex);
+    else if constexpr (ACT == 1) {
+        if (ch == 3)
+            launch_w8_ch<ACT, LOG_G, 3>(x, ldx, wq, sw, M, N, K, cg, y, st, ex);
+        else if (ch == 4)
+            launch_w8_ch<ACT, LOG_G, 4>(x, ldx, wq, sw, M, N, K, cg, y, st, ex);
         else
             return hipErrorInvalidValue;
     } else {
@@ -272,6 +463,29 @@ hipError_t launch_gemm_dec_fused(int act, const uint16_t* x, int64_t ldx, int64_
     if (g == 64) return fused::launch_g<1, 6>(ch, x, ldx, wq, M, N, K, cg, y, st, ex);
     if (g == 128) return fused::launch_g<1, 7>(ch, x, ldx, wq, M, N, K, cg, y, st, ex);
     return fused::launch_g<1, 8>(ch, x, ldx, wq, M, N, K, cg, y, st, ex);
+}
+
+}  // namespace ck
+
+namespace ck {
+
+hipError_t launch_gemm_w8a16_fused(int act, const uint16_t* x, int64_t ldx, int64_t m, int64_t k, int g,
+                                   const int8_t* wq, const float* sw, int64_t n, uint16_t* y, hipStream_t st,
+                                   EpiExtra ex)
+{
+    if (!use_fused_decode(act, m, k, g)) return hipErrorInvalidValue;
+    const int K = (int)k;
+    const int ch = (K / 8 + fused::NT - 1) / fused::NT;
+    const float cg = (float)(1.0 / sqrt((double)g));
+    const int M = (int)m, N = (int)n;
+    if (act == 0) {
+        if (g == 64) return fused::launch_w8_g<0, 6>(ch, x, ldx, wq, sw, M, N, K, cg, y, st, ex);
+        if (g == 128) return fused::launch_w8_g<0, 7>(ch, x, ldx, wq, sw, M, N, K, cg, y, st, ex);
+        return fused::launch_w8_g<0, 8>(ch, x, ldx, wq, sw, M, N, K, cg, y, st, ex);
+    }
+    if (g == 64) return fused::launch_w8_g<1, 6>(ch, x, ldx, wq, sw, M, N, K, cg, y, st, ex);
+    if (g == 128) return fused::launch_w8_g<1, 7>(ch, x, ldx, wq, sw, M, N, K, cg, y, st, ex);
+    return fused::launch_w8_g<1, 8>(ch, x, ldx, wq, sw, M, N, K, cg, y, st, ex);
 }
 
 }  // namespace ck

@@ -102,6 +102,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         }
     }
     const uint32_t x_step = A16 ? 4096u : 2048u;   // activation bytes per 64-k chunk and row block
+    // rows past M (padding of the last fragment) load zeros without touching
+    // memory: at M < 16 they would be most of the activation reads
+    bool x_ok[MT];
+#pragma unroll
+    for (int f = 0; f < MT; ++f) x_ok[f] = 16 * f + r < M;
 
     using AccT = std::conditional_t<A16, v4f, v4i>;
     AccT acc[MT];
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #pragma unroll
                 for (int s = 0; s < XP; ++s)
                     x[u][f][s] = __builtin_amdgcn_raw_buffer_load_b128(
-                        rs_x, ok ? x_base[f] + ko + (uint32_t)s * 1024u : kBufferOutside, 0, 0);
+                        rs_x, ok && x_ok[f] ? x_base[f] + ko + (uint32_t)s * 1024u : kBufferOutside, 0, 0);
         }
     };
     auto compute = [&](const v4i (&w)[U], const v4i (&x)[U][MT][XP]) {

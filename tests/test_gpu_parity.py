@@ -620,6 +620,29 @@ def test_fused_decode_equals_the_stages(m, k, act, g):
     assert torch.equal(y.view(torch.int16), y_st.view(torch.int16))
 
 
+@pytest.mark.parametrize("m,k,act,g", [(1, 3072, 0, 128), (2, 3072, 0, 128), (2, 8192, 0, 64),
+                                        (1, 12288, 1, 128), (1, 4096, 1, 256), (2, 12288, 1, 128),
+                                        (2, 16384, 1, 64), (1, 64, 0, 64)])
+def test_w8a16_fused_equals_the_stages(m, k, act, g):
+    """ck_int8_linear_w8a16 at the fewest rows (one kernel that rotates the
+    rows itself) equals ck_act_rotate_bf16 followed by the W8A16 GEMM, bit for
+    bit, with bias and residual."""
+    say(f"w8a16 fused vs stages m={m} k={k} act={act} g={g}")
+    n = 1040
+    rng = np.random.default_rng(79 + m + k)
+    d = W.case(m, k, n, act, seed=4100 + m)
+    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    wb = ck.ck_weight_pack(wq)
+    x = bf16_dev(d["x"])
+    bias = dev(rng.standard_normal(n).astype(np.float32))
+    res = bf16_dev(W.to_bf16_bits(rng.standard_normal((m, n)).astype(np.float32)))
+    y = ck.ck_int8_linear_w8a16(x, wb, sw, g, act, bias=bias, residual=res)
+    xr = ck.ck_act_rotate_bf16(x, act, g, k=k, layout="blocked")
+    y_st = ck.ck_w8a16_gemm_bf16(xr, wb, sw, m, bias=bias, residual=res)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_st.view(torch.int16))
+
+
 def test_decode_rejects_more_than_64_rows():
     say("decode layout with m=65 -> CK_EUNSUPPORTED")
     wq, sw = ck.ck_weight_prep(torch.zeros((32, 256), dtype=torch.float32, device=DEV), 128)
@@ -737,7 +760,7 @@ def test_w8a16_gemm_exact_on_integer_activations(orc, m, n, k):
 W8A16_LINEAR = [  # (m, k, n, act, g)
     (1, 256, 16, 0, 128), (7, 384, 48, 1, 128), (300, 1024, 272, 1, 128), (129, 512, 320, 0, 64),
     (200, 768, 96, 1, 256), (1000, 640, 1040, 0, 128), (4000, 256, 4080, 1, 128), (5, 64, 32, 1, 64),
-    (1500, 384, 4000, 0, 128), (700, 256, 5008, 1, 128),
+    (1500, 384, 4000, 0, 128), (700, 256, 5008, 1, 128), (2, 4096, 1040, 1, 256), (2, 3072, 528, 0, 128),
 ]
 
 
@@ -795,8 +818,11 @@ def _mlp_w8a16_check(orc, xb, rows, w_gu_o, s_gu_o, w_d_o, s_d_o, g, y, y1, what
     assert_w8a16_close(orc, y[rows], r2["y"], r2["x_rot"], w_d_o, s_d_o, i, what + " stage 2")
 
 
-def test_swiglu_mlp_w8a16(orc):
-    m, h, i, g = 300, 1024, 2816, 128
+@pytest.mark.parametrize("m", [300, 1, 2, 3])
+def test_swiglu_mlp_w8a16(orc, m):
+    """At m <= 2 each stage is one launch (the rotation inside the GEMM); at
+    m = 3 the rotations are launches of their own."""
+    h, i, g = 1024, 2816, 128
     say(f"swiglu_mlp_w8a16 m={m} h={h} i={i}")
     rng = np.random.default_rng(91)
     xb = W.to_bf16_bits(rng.standard_normal((m, h)).astype(np.float32))

@@ -37,31 +37,36 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int WAVES = 8;
 
-template <int MT, bool A16>
+template <int MT, bool A16, int NG>
 struct SmallCfg {
-    // chunks per batch per wave (W8A16 holds twice the activation registers)
-    static constexpr int U = A16 ? (MT == 1 ? 6 : (MT == 2 ? 3 : (MT == 4 ? 2 : 1)))
-                                 : (MT == 1 ? 8 : (MT == 2 ? 4 : (MT == 4 ? 3 : 2)));
+    // chunks per batch per wave (W8A16 holds twice the activation registers;
+    // two weight groups per workgroup hold twice the weight registers)
+    static constexpr int U1 = A16 ? (MT == 1 ? 6 : (MT == 2 ? 3 : (MT == 4 ? 2 : 1)))
+                                  : (MT == 1 ? 8 : (MT == 2 ? 4 : (MT == 4 ? 3 : 2)));
+    static constexpr int U = NG == 1 ? U1 : (U1 > 4 ? 4 : (U1 > 1 ? U1 - 1 : 1));
     static constexpr int XP = A16 ? 2 : 1;   // activation pieces per chunk and fragment
 };
 
 // DEC: W in the decode layout (include/ck.h): each 16-row group one linear
 // stream, its row scales in the group's 64-byte header.
 // A16: xq points to BF16 x_rot (see above); OUT_I32 then writes FP32 sums.
-template <int MT, bool OUT_I32, bool DEC, bool A16>
+// NG: 16-row weight groups per workgroup (1 or 2).  With 2, each activation
+// fragment loaded serves twice the weight bytes: at 16 or more rows the
+// activation reads, not the weights, fill a CU's vector-memory path.
+template <int MT, bool OUT_I32, bool DEC, bool A16, int NG>
 __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
     const float* __restrict__ sw, int M, int N, int K, int m_rows, int n_rows, void* __restrict__ out,
     EpiExtra ex)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
-    constexpr int U = SmallCfg<MT, A16>::U;
-    constexpr int XP = SmallCfg<MT, A16>::XP;
-    __shared__ v4i red[WAVES][MT][64];
+    constexpr int U = SmallCfg<MT, A16, NG>::U;
+    constexpr int XP = SmallCfg<MT, A16, NG>::XP;
+    __shared__ v4i red[WAVES][NG * MT][64];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nb = blockIdx.x;       // 16-row block of W (output columns 16 nb ..)
+    const int nb0 = blockIdx.x * NG;  // first 16-row group of W (output columns 16 nb0 ..)
     const int KB = K >> 5;           // 1 KB blocks per 32-row block
     const int KC = K >> 6;           // 64-byte k-chunks
 
@@ -83,8 +88,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const uint32_t lane_off = (uint32_t)((c >> 1) * 1024 + (c & 1) * 512 + r * 16);
     // DEC: chunk j of group nb is the 1 KB at nb * grp_bytes + 64 + 1024 j,
     // lane l's 16 bytes at 16 l (quarter l / 16, row l % 16)
-    const uint32_t w_base = DEC ? (uint32_t)nb * grp_bytes + 64u + (uint32_t)lane * 16u
-                                : (uint32_t)((nb >> 1) * KB) * 1024u + (uint32_t)(nb & 1) * 256u + lane_off;
+    uint32_t w_base[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int nb = nb0 + g;
+        w_base[g] = DEC ? (uint32_t)nb * grp_bytes + 64u + (uint32_t)lane * 16u
+                        : (uint32_t)((nb >> 1) * KB) * 1024u + (uint32_t)(nb & 1) * 256u + lane_off;
+    }
     const uint32_t w_step = DEC ? 1024u : 2048u;   // bytes per 64-byte k-chunk
     // activation piece of fragment f (rows 16 f ..), chunk 0: INT8 codes in the
     // blocked layout, or (A16) BF16 in the BF16 blocked layout, where lane l's
@@ -109,19 +119,24 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     for (int f = 0; f < MT; ++f) x_ok[f] = 16 * f + r < M;
 
     using AccT = std::conditional_t<A16, v4f, v4i>;
-    AccT acc[MT];
+    AccT acc[NG][MT];
 #pragma unroll
-    for (int f = 0; f < MT; ++f) acc[f] = AccT{0, 0, 0, 0};
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int f = 0; f < MT; ++f) acc[g][f] = AccT{0, 0, 0, 0};
 
     // batch b covers chunks j = wave + WAVES * (U b + u), u < U; chunks past
     // the end load zeros (offset outside the buffers) and add nothing
-    auto load = [&](int b, v4i (&w)[U], v4i (&x)[U][MT][XP]) {
+    auto load = [&](int b, v4i (&w)[U][NG], v4i (&x)[U][MT][XP]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = wave + WAVES * (U * b + u);
             const bool ok = j < KC;
             const uint32_t ko = (uint32_t)j * x_step;
-            w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, ok ? w_base + (uint32_t)j * w_step : kBufferOutside, 0, 0);
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+                w[u][g] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rs_w, ok ? w_base[g] + (uint32_t)j * w_step : kBufferOutside, 0, 0);
 #pragma unroll
             for (int f = 0; f < MT; ++f)
 #pragma unroll
@@ -130,28 +145,31 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
                         rs_x, ok && x_ok[f] ? x_base[f] + ko + (uint32_t)s * 1024u : kBufferOutside, 0, 0);
         }
     };
-    auto compute = [&](const v4i (&w)[U], const v4i (&x)[U][MT][XP]) {
+    auto compute = [&](const v4i (&w)[U][NG], const v4i (&x)[U][MT][XP]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if constexpr (A16) {
-                const v8bf w0 = widen8(w[u][0], w[u][1]), w1 = widen8(w[u][2], w[u][3]);
 #pragma unroll
-                for (int f = 0; f < MT; ++f) {
-                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, __builtin_bit_cast(v8bf, x[u][f][0]),
-                                                                     acc[f], 0, 0, 0);
-                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, __builtin_bit_cast(v8bf, x[u][f][XP - 1]),
-                                                                     acc[f], 0, 0, 0);
+            for (int g = 0; g < NG; ++g) {
+                if constexpr (A16) {
+                    const v8bf w0 = widen8(w[u][g][0], w[u][g][1]), w1 = widen8(w[u][g][2], w[u][g][3]);
+#pragma unroll
+                    for (int f = 0; f < MT; ++f) {
+                        acc[g][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            w0, __builtin_bit_cast(v8bf, x[u][f][0]), acc[g][f], 0, 0, 0);
+                        acc[g][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            w1, __builtin_bit_cast(v8bf, x[u][f][XP - 1]), acc[g][f], 0, 0, 0);
+                    }
+                } else {
+#pragma unroll
+                    for (int f = 0; f < MT; ++f)
+                        acc[g][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[u][g], x[u][f][0], acc[g][f], 0, 0, 0);
                 }
-            } else {
-#pragma unroll
-                for (int f = 0; f < MT; ++f)
-                    acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[u], x[u][f][0], acc[f], 0, 0, 0);
             }
         }
     };
 
     const int batches = (KC + WAVES * U - 1) / (WAVES * U);
-    v4i wa[U], xa[U][MT][XP], wb[U], xb[U][MT][XP];
+    v4i wa[U][NG], xa[U][MT][XP], wb[U][NG], xb[U][MT][XP];
     load(0, wa, xa);
     for (int b = 0; b < batches; b += 2) {
         if (b + 1 < batches) load(b + 1, wb, xb);
@@ -163,13 +181,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 
     // ---- sum the waves' partial accumulators (in wave order) ----
 #pragma unroll
-    for (int f = 0; f < MT; ++f) red[wave][f][lane] = __builtin_bit_cast(v4i, acc[f]);
-    __syncthreads();
-    if (wave >= MT) return;
-    const int f = wave;
-    AccT t = __builtin_bit_cast(AccT, red[0][f][lane]);
+    for (int g = 0; g < NG; ++g)
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) t += __builtin_bit_cast(AccT, red[w][f][lane]);
+        for (int f = 0; f < MT; ++f) red[wave][g * MT + f][lane] = __builtin_bit_cast(v4i, acc[g][f]);
+    __syncthreads();
+    if (wave >= NG * MT) return;
+    const int f = wave % MT;
+    const int nb = nb0 + wave / MT;
+    AccT t = __builtin_bit_cast(AccT, red[0][wave][lane]);
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) t += __builtin_bit_cast(AccT, red[w][wave][lane]);
 
     // ---- epilogue: lane l holds D[n = 4 (l / 16) + i][m = l % 16], i < 4 ----
     const int m = f * 16 + r;
@@ -200,13 +221,28 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// Two weight groups per workgroup while that still leaves at least two
+// workgroups per CU, and only where the fragments' activation reads are a
+// load: at 16 rows and more (below, the padding rows load nothing).
+bool two_groups(int M, int N, int MT)
+{
+    return MT <= 4 && M >= 16 && N % 32 == 0 && N / 32 >= 2 * num_cus();
+}
+
 template <int MT, bool I32, bool DEC, bool A16 = false>
 hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int M, int N,
                   int K, void* out, hipStream_t st, EpiExtra ex)
 {
     const int m_rows = (M + 255) / 256 * 256;
     const int n_rows = (N + 255) / 256 * 256;
-    hipLaunchKernelGGL((gemm_small_kernel<MT, I32, DEC, A16>), dim3(N / 16), dim3(WAVES * 64), 0, st, xq, sx,
+    if constexpr (MT <= 4) {
+        if (two_groups(M, N, MT)) {
+            hipLaunchKernelGGL((gemm_small_kernel<MT, I32, DEC, A16, 2>), dim3(N / 32), dim3(WAVES * 64), 0, st,
+                               xq, sx, wq, sw, M, N, K, m_rows, n_rows, out, ex);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((gemm_small_kernel<MT, I32, DEC, A16, 1>), dim3(N / 16), dim3(WAVES * 64), 0, st, xq, sx,
                        wq, sw, M, N, K, m_rows, n_rows, out, ex);
     return hipGetLastError();
 }

@@ -193,8 +193,8 @@ ck_status ck_act_quant(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,
  *   y        [m, n] BF16, written (row stride n)
  *   workspace  device buffer of at least ck_int8_linear_workspace_size(m, k)
  *            bytes, 256-byte aligned; clobbered (holds x_q and x_scale).
- *            With CK_LAYOUT_DECODE at m <= 2 (k <= 8192, or k <= 16384 with
- *            SwiGLU), group 64, 128 or 256, the quantizer runs
+ *            With CK_LAYOUT_BLOCKED or CK_LAYOUT_DECODE at m <= 2 (k <= 8192,
+ *            or k <= 16384 with SwiGLU), group 64, 128 or 256, the quantizer runs
  *            inside the GEMM kernel and the workspace is left untouched (it is
  *            still required); the result is the same bit for bit. */
 ck_status ck_int8_linear(const uint16_t *x, int64_t ldx, int32_t act,
@@ -229,9 +229,9 @@ ck_status ck_int8_gemm_bf16(const int8_t *x_q, const float *x_scale,
  *   y      [m, h]  BF16, written
  *   workspace  at least ck_swiglu_mlp_workspace_size(m, h, i) bytes,
  *          256-byte aligned; clobbered (x codes/scales, the [m, 2i] BF16
- *          gate|up output, its codes/scales; with CK_LAYOUT_DECODE at the
- *          fewest rows a stage's quantizer runs inside its GEMM, as in
- *          ck_int8_linear, and its codes are not written). */
+ *          gate|up output, its codes/scales; with CK_LAYOUT_BLOCKED or
+ *          CK_LAYOUT_DECODE at the fewest rows a stage's quantizer runs inside
+ *          its GEMM, as in ck_int8_linear, and its codes are not written). */
 ck_status ck_swiglu_mlp(const uint16_t *x, const int8_t *w_gu, const float *s_gu,
                         const int8_t *w_down, const float *s_down, int32_t layout,
                         int64_t m, int64_t h, int64_t i, int32_t group, uint16_t *y,

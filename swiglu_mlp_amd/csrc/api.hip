@@ -231,8 +231,8 @@ ck_status ck_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, const int8
                                          round_up((size_t)pad_rows(m) * (size_t)k));
     hipStream_t st = (hipStream_t)stream;
     const int kind = act == CK_ACT_SWIGLU ? 1 : 0;
-    if (dec && ck::use_fused_decode(kind, m, k, group))   // quantizer inside the GEMM: one launch
-        return from_hip(ck::launch_gemm_dec_fused(kind, x, ldx, m, k, group, w_q, n, y, st,
+    if (blocked && ck::use_fused_decode(kind, m, k, group))   // quantizer inside the GEMM: one launch
+        return from_hip(ck::launch_gemm_dec_fused(kind, x, ldx, m, k, group, w_q, w_scale, dec, n, y, st,
                                                   ck::EpiExtra{bias, residual}));
     CK_TRY(from_hip(ck::launch_quant_rows(kind, x, ldx, m, k, group, xq, sx, nullptr, blocked, st)));
     return from_hip(ck::launch_gemm_bf16(xq, sx, w_q, w_scale, m, n, k, y, layout, st,
@@ -279,16 +279,16 @@ ck_status ck_swiglu_mlp(const uint16_t* x, const int8_t* w_gu, const float* s_gu
     float* sh = reinterpret_cast<float*>(p);
     hipStream_t st = (hipStream_t)stream;
     // stage 1: packed [gate | up] projection, BF16 [m, 2i]; at the fewest rows
-    // of the decode layout each stage's quantizer runs inside its GEMM
-    if (dec && ck::use_fused_decode(0, m, h, group)) {
-        CK_TRY(from_hip(ck::launch_gemm_dec_fused(0, x, h, m, h, group, w_gu, 2 * i, y1, st)));
+    // (blocked or decode weights) each stage's quantizer runs inside its GEMM
+    if (blocked && ck::use_fused_decode(0, m, h, group)) {
+        CK_TRY(from_hip(ck::launch_gemm_dec_fused(0, x, h, m, h, group, w_gu, s_gu, dec, 2 * i, y1, st)));
     } else {
         CK_TRY(from_hip(ck::launch_quant_rows(0, x, h, m, h, group, xq, sx, nullptr, blocked, st)));
         CK_TRY(from_hip(ck::launch_gemm_bf16(xq, sx, w_gu, s_gu, m, 2 * i, h, y1, layout, st)));
     }
     // stage 2: silu(gate) * up inside the down projection's quantizer
-    if (dec && ck::use_fused_decode(1, m, i, group))
-        return from_hip(ck::launch_gemm_dec_fused(1, y1, 2 * i, m, i, group, w_down, h, y, st));
+    if (blocked && ck::use_fused_decode(1, m, i, group))
+        return from_hip(ck::launch_gemm_dec_fused(1, y1, 2 * i, m, i, group, w_down, s_down, dec, h, y, st));
     CK_TRY(from_hip(ck::launch_quant_rows(1, y1, 2 * i, m, i, group, hq, sh, nullptr, blocked, st)));
     return from_hip(ck::launch_gemm_bf16(hq, sh, w_down, s_down, m, h, i, y, layout, st));
 }

@@ -31,8 +31,8 @@ hipError_t launch_rotate_bf16(int kind, const void* src, int64_t ld, int64_t m, 
 // scales launch_quant_rows would have written.
 bool use_fused_decode(int act, int64_t m, int64_t k, int g);
 hipError_t launch_gemm_dec_fused(int act, const uint16_t* x, int64_t ldx, int64_t m, int64_t k, int g,
-                                 const int8_t* wq, int64_t n, uint16_t* y, hipStream_t st,
-                                 EpiExtra ex = EpiExtra{});
+                                 const int8_t* wq, const float* sw, bool dec, int64_t n, uint16_t* y,
+                                 hipStream_t st, EpiExtra ex = EpiExtra{});
 // The W8A16 linear at the same sizes (use_fused_decode): the BF16 rotation
 // inside the few-row W8A16 GEMM, W in the blocked layout with its row scales sw.
 hipError_t launch_gemm_w8a16_fused(int act, const uint16_t* x, int64_t ldx, int64_t m, int64_t k, int g,

@@ -1,5 +1,5 @@
-// gemm_fused.hip -- the decode-layout INT8 GEMM with the activation quantizer
-// in front of it, in one kernel, for the fewest token rows.
+// gemm_fused.hip -- the few-row INT8 GEMM (decode or blocked weights) with the
+// activation quantizer in front of it, in one kernel, for the fewest token rows.
 //
 // Sources: comfy-kitchen PR #277, "The key observation" (x_rot = x H, per-token
 // INT8, y = x_rot W_rot^T with int32 accumulation); sglang PR #44196,
@@ -52,10 +52,12 @@ struct FusedCfg {
     static constexpr int MAXR = 2;
 };
 
-template <int ACT, int LOG_G, int CH>
+// DEC: W in the decode layout (scales in each group's header); else in the
+// blocked layout with its row scales sw (n_rows: its padded row count).
+template <int ACT, int LOG_G, int CH, bool DEC>
 __global__ __launch_bounds__(NT) void gemm_dec_fused_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, const int8_t* __restrict__ wq, int M, int N, int K,
-    float cg, void* __restrict__ out, EpiExtra ex)
+    const uint16_t* __restrict__ x, int64_t ldx, const int8_t* __restrict__ wq, const float* __restrict__ sw,
+    int M, int N, int K, int n_rows, float cg, void* __restrict__ out, EpiExtra ex)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int G = 1 << LOG_G;
@@ -93,16 +95,23 @@ __global__ __launch_bounds__(NT) void gemm_dec_fused_kernel(
     // ---- the first two batches of this workgroup's weight stream -----------
     // W in the decode layout (include/ck.h): chunk j of group nb is the 1 KB at
     // nb * grp_bytes + 64 + 1024 j; lane l's 16 bytes hold row l % 16, k-bytes
-    // 64 j + 16 (l / 16) .. + 16.  Batch b covers chunks wave + WAVES (U b + u).
+    // 64 j + 16 (l / 16) .. + 16.  In the blocked layout the same 16 bytes sit
+    // in 1 KB block 2 j + c / 2 of the 32-row block nb / 2, half c % 2 (c = l /
+    // 16), at row offset 16 (l % 16), + 256 for the odd 16-row group.  Batch b
+    // covers chunks wave + WAVES (U b + u).
     const uint32_t grp_bytes = 64u + 16u * (uint32_t)K;
     const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)wq, (short)0, (int)((uint32_t)(N / 16) * grp_bytes), 0x00020000);
-    const uint32_t w_base = (uint32_t)nb * grp_bytes + 64u + (uint32_t)lane * 16u;
+        (void*)wq, (short)0, DEC ? (int)((uint32_t)(N / 16) * grp_bytes) : n_rows * K, 0x00020000);
+    const int cq = lane >> 4;
+    const uint32_t w_base = DEC ? (uint32_t)nb * grp_bytes + 64u + (uint32_t)lane * 16u
+                                : (uint32_t)((nb >> 1) * (K >> 5)) * 1024u + (uint32_t)(nb & 1) * 256u +
+                                      (uint32_t)((cq >> 1) * 1024 + (cq & 1) * 512 + (lane & 15) * 16);
+    const uint32_t w_step = DEC ? 1024u : 2048u;
     auto load_w = [&](int b, v4i (&w)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = wave + WAVES * (U * b + u);
-            w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, j < KC ? w_base + (uint32_t)j * 1024u : kBufferOutside,
+            w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, j < KC ? w_base + (uint32_t)j * w_step : kBufferOutside,
                                                          0, 0);
         }
     };
@@ -206,7 +215,8 @@ __global__ __launch_bounds__(NT) void gemm_dec_fused_kernel(
     const int m = r16;
     const int n = nb * 16 + 4 * (lane >> 4);
     const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(out, (short)0, M * N * 2, 0x00020000);
-    const float4 s4 = *reinterpret_cast<const float4*>(wq + (size_t)nb * grp_bytes + 16 * (lane >> 4));
+    const float4 s4 = DEC ? *reinterpret_cast<const float4*>(wq + (size_t)nb * grp_bytes + 16 * (lane >> 4))
+                          : *reinterpret_cast<const float4*>(sw + n);
     const float sxm = sxs[xrow];
     float y0 = ((float)t[0] * sxm) * s4.x;
     float y1 = ((float)t[1] * sxm) * s4.y;
@@ -380,26 +390,31 @@ __global__ __launch_bounds__(NT) void gemm_w8a16_fused_kernel(
 }
 
 template <int ACT, int LOG_G, int CH>
-void launch_ch(const uint16_t* x, int64_t ldx, const int8_t* wq, int M, int N, int K, float cg, uint16_t* y,
-               hipStream_t st, EpiExtra ex)
+void launch_ch(const uint16_t* x, int64_t ldx, const int8_t* wq, const float* sw, bool dec, int M, int N, int K,
+               float cg, uint16_t* y, hipStream_t st, EpiExtra ex)
 {
-    hipLaunchKernelGGL((gemm_dec_fused_kernel<ACT, LOG_G, CH>), dim3(N / 16), dim3(NT), 0, st, x, ldx, wq, M, N, K, cg,
-              static_cast<void*>(y), ex);
+    const int n_rows = (N + 255) / 256 * 256;
+    if (dec)
+        hipLaunchKernelGGL((gemm_dec_fused_kernel<ACT, LOG_G, CH, true>), dim3(N / 16), dim3(NT), 0, st, x, ldx, wq,
+                           sw, M, N, K, n_rows, cg, static_cast<void*>(y), ex);
+    else
+        hipLaunchKernelGGL((gemm_dec_fused_kernel<ACT, LOG_G, CH, false>), dim3(N / 16), dim3(NT), 0, st, x, ldx, wq,
+                           sw, M, N, K, n_rows, cg, static_cast<void*>(y), ex);
 }
 
 template <int ACT, int LOG_G>
-hipError_t launch_g(int ch, const uint16_t* x, int64_t ldx, const int8_t* wq, int M, int N, int K, float cg,
-                    uint16_t* y, hipStream_t st, EpiExtra ex)
+hipError_t launch_g(int ch, const uint16_t* x, int64_t ldx, const int8_t* wq, const float* sw, bool dec, int M,
+                    int N, int K, float cg, uint16_t* y, hipStream_t st, EpiExtra ex)
 {
     if (ch == 1)
-        launch_ch<ACT, LOG_G, 1>(x, ldx, wq, M, N, K, cg, y, st, ex);
+        launch_ch<ACT, LOG_G, 1>(x, ldx, wq, sw, dec, M, N, K, cg, y, st, ex);
     else if (ch == 2)
-        launch_ch<ACT, LOG_G, 2>(x, ldx, wq, M, N, K, cg, y, st, ex);
+        launch_ch<ACT, LOG_G, 2>(x, ldx, wq, sw, dec, M, N, K, cg, y, st, ex);
     else if constexpr (ACT == 1) {
         if (ch == 3)
-            launch_ch<ACT, LOG_G, 3>(x, ldx, wq, M, N, K, cg, y, st, ex);
+            launch_ch<ACT, LOG_G, 3>(x, ldx, wq, sw, dec, M, N, K, cg, y, st, ex);
         else if (ch == 4)
-            launch_ch<ACT, LOG_G, 4>(x, ldx, wq, M, N, K, cg, y, st, ex);
+            launch_ch<ACT, LOG_G, 4>(x, ldx, wq, sw, dec, M, N, K, cg, y, st, ex);
         else
             return hipErrorInvalidValue;
     } else {
@@ -448,7 +463,8 @@ bool use_fused_decode(int act, int64_t m, int64_t k, int g)
 }
 
 hipError_t launch_gemm_dec_fused(int act, const uint16_t* x, int64_t ldx, int64_t m, int64_t k, int g,
-                                 const int8_t* wq, int64_t n, uint16_t* y, hipStream_t st, EpiExtra ex)
+                                 const int8_t* wq, const float* sw, bool dec, int64_t n, uint16_t* y, hipStream_t st,
+                                 EpiExtra ex)
 {
     if (!use_fused_decode(act, m, k, g)) return hipErrorInvalidValue;
     const int K = (int)k;
@@ -456,13 +472,13 @@ hipError_t launch_gemm_dec_fused(int act, const uint16_t* x, int64_t ldx, int64_
     const float cg = (float)(1.0 / sqrt((double)g));
     const int M = (int)m, N = (int)n;
     if (act == 0) {
-        if (g == 64) return fused::launch_g<0, 6>(ch, x, ldx, wq, M, N, K, cg, y, st, ex);
-        if (g == 128) return fused::launch_g<0, 7>(ch, x, ldx, wq, M, N, K, cg, y, st, ex);
-        return fused::launch_g<0, 8>(ch, x, ldx, wq, M, N, K, cg, y, st, ex);
+        if (g == 64) return fused::launch_g<0, 6>(ch, x, ldx, wq, sw, dec, M, N, K, cg, y, st, ex);
+        if (g == 128) return fused::launch_g<0, 7>(ch, x, ldx, wq, sw, dec, M, N, K, cg, y, st, ex);
+        return fused::launch_g<0, 8>(ch, x, ldx, wq, sw, dec, M, N, K, cg, y, st, ex);
     }
-    if (g == 64) return fused::launch_g<1, 6>(ch, x, ldx, wq, M, N, K, cg, y, st, ex);
-    if (g == 128) return fused::launch_g<1, 7>(ch, x, ldx, wq, M, N, K, cg, y, st, ex);
-    return fused::launch_g<1, 8>(ch, x, ldx, wq, M, N, K, cg, y, st, ex);
+    if (g == 64) return fused::launch_g<1, 6>(ch, x, ldx, wq, sw, dec, M, N, K, cg, y, st, ex);
+    if (g == 128) return fused::launch_g<1, 7>(ch, x, ldx, wq, sw, dec, M, N, K, cg, y, st, ex);
+    return fused::launch_g<1, 8>(ch, x, ldx, wq, sw, dec, M, N, K, cg, y, st, ex);
 }
 
 }  // namespace ck

@@ -603,24 +603,29 @@ def test_swiglu_mlp_decode_bit_exact(orc, m):
     np.testing.assert_array_equal(bf16_host(y), orc.swiglu_mlp(xb, gq_o, gs_o, dq_o, ds_o, g))
 
 
+@pytest.mark.parametrize("layout", ["decode", "blocked"])
 @pytest.mark.parametrize("m,k,act,g", [(1, 3072, 0, 128), (2, 3072, 0, 128), (2, 8192, 0, 64),
                                         (1, 12288, 1, 128), (1, 4096, 1, 256), (2, 12288, 1, 128)])
-def test_fused_decode_equals_the_stages(m, k, act, g):
-    """ck_int8_linear on decode weights at the fewest rows (one kernel that
-    quantizes the rows itself) equals ck_act_quant followed by the decode GEMM,
-    codes, scales and outputs alike, bit for bit, with bias and residual."""
-    say(f"fused decode vs stages m={m} k={k} act={act} g={g}")
+def test_fused_decode_equals_the_stages(m, k, act, g, layout):
+    """ck_int8_linear at the fewest rows (one kernel that quantizes the rows
+    itself, decode or blocked weights) equals ck_act_quant followed by the
+    few-row GEMM, codes, scales and outputs alike, bit for bit, with bias and
+    residual."""
+    say(f"fused quantizer vs stages m={m} k={k} act={act} g={g} layout={layout}")
     n = 1040
     rng = np.random.default_rng(77 + m + k)
     d = W.case(m, k, n, act, seed=4000 + m)
     wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
-    wd = ck.ck_weight_pack_decode(wq, sw)
+    if layout == "decode":
+        wl, sl = ck.ck_weight_pack_decode(wq, sw), None
+    else:
+        wl, sl = ck.ck_weight_pack(wq), sw
     x = bf16_dev(d["x"])
     bias = dev(rng.standard_normal(n).astype(np.float32))
     res = bf16_dev(W.to_bf16_bits(rng.standard_normal((m, n)).astype(np.float32)))
-    y = ck.ck_int8_linear(x, wd, None, g, act, layout="decode", bias=bias, residual=res)
+    y = ck.ck_int8_linear(x, wl, sl, g, act, layout=layout, bias=bias, residual=res)
     xq, sx = ck.ck_act_quant(x, act, g, k=k, layout="blocked")
-    y_st = ck.ck_int8_gemm_bf16(xq, sx, wd, None, layout="decode", bias=bias, residual=res)
+    y_st = ck.ck_int8_gemm_bf16(xq, sx, wl, sl, layout=layout, bias=bias, residual=res)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y_st.view(torch.int16))
 

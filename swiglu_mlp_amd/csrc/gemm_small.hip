@@ -8,8 +8,8 @@
 //
 // At M <= 64 the weight matrix (N x K bytes) is read once and the arithmetic is
 // negligible, so the kernel is bound by HBM.  One workgroup owns 16 weight
-// rows and all of K: N / 16 workgroups, each streaming 16 x K contiguous bytes
-// in 256-byte runs (16 rows of a 1 KB block half).  Its 8 waves take
+// rows (or 32, see NG) and all of K: N / 16 workgroups, each streaming 16 x K
+// contiguous bytes in 256-byte runs (16 rows of a 1 KB block half).  Its 8 waves take
 // interleaved 64-byte k-chunks so the workgroup reads a contiguous front, and
 // each wave keeps two batches of U chunks in flight.  The few activation rows
 // (16 per MFMA fragment) come from L2.  Products use v_mfma_i32_16x16x64_i8

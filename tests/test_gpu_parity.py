@@ -564,20 +564,26 @@ DECODE_LINEAR = [  # (m, k, n, act, g)
 ]
 
 
+@pytest.mark.parametrize("layout", ["decode", "blocked"])
 @pytest.mark.parametrize("m,k,n,act,g", DECODE_LINEAR)
-def test_int8_linear_decode_bit_exact(orc, m, k, n, act, g):
-    say(f"int8_linear decode m={m} k={k} n={n} act={act} g={g}")
+def test_int8_linear_decode_bit_exact(orc, m, k, n, act, g, layout):
+    """Few rows on decode or blocked weights, through the fused quantizer at
+    m <= 2 and the separate one past its limits."""
+    say(f"int8_linear few rows m={m} k={k} n={n} act={act} g={g} layout={layout}")
     d = W.case(m, k, n, act, seed=3000 + m, zero_rows=(m // 2,) if m > 2 else ())
     wq_o, sw_o = orc.weight_prep(d["w"], g)
     wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
-    wd = ck.ck_weight_pack_decode(wq, sw)
+    if layout == "decode":
+        wd, sl = ck.ck_weight_pack_decode(wq, sw), None
+    else:
+        wd, sl = ck.ck_weight_pack(wq), sw
     x = bf16_dev(d["x"])
-    y = bf16_host(ck.ck_int8_linear(x, wd, None, g, act, layout="decode"))
+    y = bf16_host(ck.ck_int8_linear(x, wd, sl, g, act, layout=layout))
     np.testing.assert_array_equal(y, orc.int8_linear(d["x"], act, wq_o, sw_o, g))
     rng = np.random.default_rng(m + n)
     bias = rng.standard_normal(n).astype(np.float32)
     res = orc.f32_to_bf16(rng.standard_normal((m, n)).astype(np.float32))
-    y = ck.ck_int8_linear(x, wd, None, g, act, layout="decode", bias=dev(bias),
+    y = ck.ck_int8_linear(x, wd, sl, g, act, layout=layout, bias=dev(bias),
                           residual=bf16_dev(res))
     np.testing.assert_array_equal(
         bf16_host(y), orc.int8_linear(d["x"], act, wq_o, sw_o, g, bias=bias, residual=res))

@@ -52,6 +52,52 @@ struct FusedCfg {
     static constexpr int MAXR = 2;
 };
 
+// The rows' raw BF16 data: lane tid holds chunks c = j * NT + tid (8 values
+// each) of row m < MAXR, zeros past the row or past M; for SwiGLU (ACT 1) also
+// the up half, which starts at column K.
+template <int ACT, int MAXR, int CH>
+__device__ __forceinline__ void load_rows(const uint16_t* __restrict__ x, int64_t ldx, int M, int K, int tid,
+                                          uint4 (&rg)[MAXR][CH], uint4 (&ru)[ACT ? MAXR : 1][ACT ? CH : 1])
+{
+    const int k8 = K >> 3;
+#pragma unroll
+    for (int m = 0; m < MAXR; ++m) {
+        const uint16_t* rp = x + (int64_t)(m < M ? m : 0) * ldx;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = j * NT + tid;
+            const bool ok = m < M && c < k8;
+            rg[m][j] = ok ? *reinterpret_cast<const uint4*>(rp + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+            if constexpr (ACT)
+                ru[m][j] = ok ? *reinterpret_cast<const uint4*>(rp + K + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+}
+
+// Row m's values in FP32, the quantizer's first step: x, or silu(gate) * up.
+template <int ACT, int MAXR, int CH>
+__device__ __forceinline__ void row_values(int m, const uint4 (&rg)[MAXR][CH],
+                                           const uint4 (&ru)[ACT ? MAXR : 1][ACT ? CH : 1], float (&v)[CH][8])
+{
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const uint32_t w[4] = {rg[m][j].x, rg[m][j].y, rg[m][j].z, rg[m][j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[j][2 * e] = bf16_lo(w[e]);
+            v[j][2 * e + 1] = bf16_hi(w[e]);
+        }
+        if constexpr (ACT) {
+            const uint32_t wu[4] = {ru[m][j].x, ru[m][j].y, ru[m][j].z, ru[m][j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[j][2 * e] = silu_f32(v[j][2 * e]) * bf16_lo(wu[e]);
+                v[j][2 * e + 1] = silu_f32(v[j][2 * e + 1]) * bf16_hi(wu[e]);
+            }
+        }
+    }
+}
+
 // DEC: W in the decode layout (scales in each group's header); else in the
 // blocked layout with its row scales sw (n_rows: its padded row count).
 template <int ACT, int LOG_G, int CH, bool DEC>
@@ -79,18 +125,7 @@ __global__ __launch_bounds__(NT) void gemm_dec_fused_kernel(
     // ---- the rows' raw BF16 data (issued first: the quantizer waits on it,
     // not on the weight loads issued after it) --------------------------------
     uint4 rg[MAXR][CH], ru[ACT ? MAXR : 1][ACT ? CH : 1];
-#pragma unroll
-    for (int m = 0; m < MAXR; ++m) {
-        const uint16_t* rp = x + (int64_t)(m < M ? m : 0) * ldx;
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const int c = j * NT + tid;
-            const bool ok = m < M && c < k8;
-            rg[m][j] = ok ? *reinterpret_cast<const uint4*>(rp + c * 8) : make_uint4(0u, 0u, 0u, 0u);
-            if constexpr (ACT)
-                ru[m][j] = ok ? *reinterpret_cast<const uint4*>(rp + K + c * 8) : make_uint4(0u, 0u, 0u, 0u);
-        }
-    }
+    load_rows<ACT, MAXR, CH>(x, ldx, M, K, tid, rg, ru);
 
     // ---- the first two batches of this workgroup's weight stream -----------
     // W in the decode layout (include/ck.h): chunk j of group nb is the 1 KB at
@@ -126,23 +161,7 @@ __global__ __launch_bounds__(NT) void gemm_dec_fused_kernel(
     for (int m = 0; m < MAXR; ++m) {
         if (m >= M) break;
         float v[CH][8];
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const uint32_t w[4] = {rg[m][j].x, rg[m][j].y, rg[m][j].z, rg[m][j].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[j][2 * e] = bf16_lo(w[e]);
-                v[j][2 * e + 1] = bf16_hi(w[e]);
-            }
-            if constexpr (ACT) {
-                const uint32_t wu[4] = {ru[m][j].x, ru[m][j].y, ru[m][j].z, ru[m][j].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[j][2 * e] = silu_f32(v[j][2 * e]) * bf16_lo(wu[e]);
-                    v[j][2 * e + 1] = silu_f32(v[j][2 * e + 1]) * bf16_hi(wu[e]);
-                }
-            }
-        }
+        row_values<ACT, MAXR, CH>(m, rg, ru, v);
         float amax = 0.0f;
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
@@ -264,18 +283,7 @@ __global__ __launch_bounds__(NT) void gemm_w8a16_fused_kernel(
     const int xs_stride = K + PADH;
 
     uint4 rg[MAXR][CH], ru[ACT ? MAXR : 1][ACT ? CH : 1];
-#pragma unroll
-    for (int m = 0; m < MAXR; ++m) {
-        const uint16_t* rp = x + (int64_t)(m < M ? m : 0) * ldx;
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const int c = j * NT + tid;
-            const bool ok = m < M && c < k8;
-            rg[m][j] = ok ? *reinterpret_cast<const uint4*>(rp + c * 8) : make_uint4(0u, 0u, 0u, 0u);
-            if constexpr (ACT)
-                ru[m][j] = ok ? *reinterpret_cast<const uint4*>(rp + K + c * 8) : make_uint4(0u, 0u, 0u, 0u);
-        }
-    }
+    load_rows<ACT, MAXR, CH>(x, ldx, M, K, tid, rg, ru);
 
     // W in the blocked layout: the 16 bytes of lane l = 16 c + r for chunk j
     // (row r of the group, k = 64 j + 16 c ..) sit in 1 KB block 2 j + c / 2 of
@@ -306,23 +314,7 @@ __global__ __launch_bounds__(NT) void gemm_w8a16_fused_kernel(
     for (int m = 0; m < MAXR; ++m) {
         if (m >= M) break;
         float v[CH][8];
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const uint32_t w[4] = {rg[m][j].x, rg[m][j].y, rg[m][j].z, rg[m][j].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[j][2 * e] = bf16_lo(w[e]);
-                v[j][2 * e + 1] = bf16_hi(w[e]);
-            }
-            if constexpr (ACT) {
-                const uint32_t wu[4] = {ru[m][j].x, ru[m][j].y, ru[m][j].z, ru[m][j].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[j][2 * e] = silu_f32(v[j][2 * e]) * bf16_lo(wu[e]);
-                    v[j][2 * e + 1] = silu_f32(v[j][2 * e + 1]) * bf16_hi(wu[e]);
-                }
-            }
-        }
+        row_values<ACT, MAXR, CH>(m, rg, ru, v);
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             fwht_in_lane<G>(v[j]);

@@ -221,12 +221,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// Two weight groups per workgroup while that still leaves at least two
-// workgroups per CU, and only where the fragments' activation reads are a
-// load: at 16 rows and more (below, the padding rows load nothing).
+// Two weight groups per workgroup while that still leaves a workgroup per CU,
+// and only where the fragments' activation reads are a load: at 16 rows and
+// more (below, the padding rows load nothing).  Measured at N = 8192..24576:
+// two groups with one workgroup per CU beat one group with two per CU.
 bool two_groups(int M, int N, int MT)
 {
-    return MT <= 4 && M >= 16 && N % 32 == 0 && N / 32 >= 2 * num_cus();
+    return MT <= 4 && M >= 16 && N % 32 == 0 && N / 32 >= num_cus();
 }
 
 template <int MT, bool I32, bool DEC, bool A16 = false>

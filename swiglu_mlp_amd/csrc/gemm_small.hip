@@ -43,16 +43,16 @@ struct SmallCfg {
     // two weight groups per workgroup hold twice the weight registers)
     static constexpr int U1 = A16 ? (MT == 1 ? 6 : (MT == 2 ? 3 : (MT == 4 ? 2 : 1)))
                                   : (MT == 1 ? 8 : (MT == 2 ? 4 : (MT == 4 ? 3 : 2)));
-    static constexpr int U = NG == 1 ? U1 : (U1 > 4 ? 4 : (U1 > 1 ? U1 - 1 : 1));
+    static constexpr int U = NG == 1 ? U1 : NG == 2 ? (U1 > 4 ? 4 : (U1 > 1 ? U1 - 1 : 1)) : (U1 > 4 ? 2 : 1);
     static constexpr int XP = A16 ? 2 : 1;   // activation pieces per chunk and fragment
 };
 
 // DEC: W in the decode layout (include/ck.h): each 16-row group one linear
 // stream, its row scales in the group's 64-byte header.
 // A16: xq points to BF16 x_rot (see above); OUT_I32 then writes FP32 sums.
-// NG: 16-row weight groups per workgroup (1 or 2).  With 2, each activation
-// fragment loaded serves twice the weight bytes: at 16 or more rows the
-// activation reads, not the weights, fill a CU's vector-memory path.
+// NG: 16-row weight groups per workgroup (1, 2 or 4).  With NG groups, each
+// activation fragment loaded serves NG times the weight bytes: at 16 or more
+// rows the activation reads, not the weights, fill a CU's vector-memory path.
 template <int MT, bool OUT_I32, bool DEC, bool A16, int NG>
 __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
@@ -221,13 +221,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// Two weight groups per workgroup while that still leaves a workgroup per CU,
-// and only where the fragments' activation reads are a load: at 16 rows and
-// more (below, the padding rows load nothing).  Measured at N = 8192..24576:
-// two groups with one workgroup per CU beat one group with two per CU.
-bool two_groups(int M, int N, int MT)
+// Weight groups per workgroup: the most that still leave a workgroup per CU,
+// and more than one only where the fragments' activation reads are a load: at
+// 16 rows and more (below, the padding rows load nothing).  Measured at
+// N = 8192..28672: two groups with one workgroup per CU beat one group with two
+// per CU; four beat two at 17..32 rows, and for W8A16 (twice the activation
+// bytes) at 16; INT8 at 16 rows gains nothing from four.  Not four at MT = 4:
+// its sums would take 128 KB of LDS.
+int groups_per_wg(int M, int N, int MT, bool a16)
 {
-    return MT <= 4 && M >= 16 && N % 32 == 0 && N / 32 >= num_cus();
+    if (MT > 4 || M < 16) return 1;
+    if ((MT == 2 || (MT == 1 && a16)) && N % 64 == 0 && N / 64 >= num_cus()) return 4;
+    if (N % 32 == 0 && N / 32 >= num_cus()) return 2;
+    return 1;
 }
 
 template <int MT, bool I32, bool DEC, bool A16 = false>
@@ -237,7 +243,15 @@ hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const flo
     const int m_rows = (M + 255) / 256 * 256;
     const int n_rows = (N + 255) / 256 * 256;
     if constexpr (MT <= 4) {
-        if (two_groups(M, N, MT)) {
+        const int ng = groups_per_wg(M, N, MT, A16);
+        if constexpr (MT == 2 || (MT == 1 && A16)) {
+            if (ng == 4) {
+                hipLaunchKernelGGL((gemm_small_kernel<MT, I32, DEC, A16, 4>), dim3(N / 64), dim3(WAVES * 64), 0,
+                                   st, xq, sx, wq, sw, M, N, K, m_rows, n_rows, out, ex);
+                return hipGetLastError();
+            }
+        }
+        if (ng == 2) {
             hipLaunchKernelGGL((gemm_small_kernel<MT, I32, DEC, A16, 2>), dim3(N / 32), dim3(WAVES * 64), 0, st,
                                xq, sx, wq, sw, M, N, K, m_rows, n_rows, out, ex);
             return hipGetLastError();

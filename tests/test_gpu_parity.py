@@ -360,10 +360,10 @@ SMALL_M_SHAPES = [  # (m, n, k): the few-row kernel: 1, 2, 4 and 8 row fragments
     (1, 4096, 4096), (2, 48, 1024), (16, 1024, 3072), (17, 2048, 128), (32, 160, 12288),
     (33, 4096, 4096), (48, 3072, 1536), (64, 4096, 12288), (64, 16, 64),
     (65, 4096, 4096), (96, 1040, 3072), (128, 4096, 12288), (100, 16, 64),
-    # two 16-row weight groups per workgroup (m >= 16, n % 32 == 0, n / 32 >= CUs),
-    # and n % 32 != 0 at the same sizes (one group)
+    # two or four 16-row weight groups per workgroup (m >= 16, n % 32 == 0, n / 32 >= CUs;
+    # four: n % 64 == 0, n / 64 >= CUs, 17..32 rows), and n % 32 != 0 (one group)
     (16, 16384, 256), (32, 16416, 320), (31, 24576, 192), (20, 16400, 128), (16, 8192, 192),
-    (25, 12288, 128),
+    (25, 12288, 128), (17, 16384, 128),
 ]
 
 
@@ -534,7 +534,7 @@ DECODE_SHAPES = [  # (m, n, k): 1, 2 and 4 row fragments, ragged m, short and lo
     (64, 4096, 12288), (64, 16, 64),
     # two weight groups per workgroup (1, 2 and 4 row fragments), and n % 32 != 0
     (16, 16384, 256), (23, 16416, 64), (40, 16384, 192), (64, 24576, 128), (50, 16400, 256),
-    (48, 8192, 128), (16, 11008, 256),
+    (48, 8192, 128), (16, 11008, 256), (30, 16384, 192),
 ]
 
 
@@ -752,6 +752,7 @@ W8A16_GEMM_SHAPES = [  # (m, n, k): every tile shape, k-stage counts 1, 2, 3 and
     (1024, 4096, 1024), (700, 5008, 256),
     # few rows, two weight groups per workgroup, and n % 32 != 0
     (16, 16384, 128), (29, 16416, 320), (32, 24576, 64), (18, 16400, 128), (24, 8192, 192),
+    (20, 28672, 128),
 ]
 
 

@@ -62,6 +62,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int U = SmallCfg<MT, A16, NG>::U;
     constexpr int XP = SmallCfg<MT, A16, NG>::XP;
+    static_assert(NG * MT <= WAVES, "one wave per (group, fragment) writes the outputs");
     __shared__ v4i red[WAVES][NG * MT][64];
 
     const int lane = threadIdx.x & 63;

@@ -62,8 +62,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int U = SmallCfg<MT, A16, NG>::U;
     constexpr int XP = SmallCfg<MT, A16, NG>::XP;
-    static_assert(NG * MT <= WAVES, "one wave per (group, fragment) writes the outputs");
-    __shared__ v4i red[WAVES][NG * MT][64];
+    constexpr int NF = NG * MT;                     // output fragments (16 x 16 each)
+    constexpr int PASS = NF < WAVES ? NF : WAVES;   // fragments summed per pass, one per wave
+    __shared__ v4i red[WAVES][PASS][64];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -180,44 +181,53 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
         compute(wb, xb);
     }
 
-    // ---- sum the waves' partial accumulators (in wave order) ----
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-#pragma unroll
-        for (int f = 0; f < MT; ++f) red[wave][g * MT + f][lane] = __builtin_bit_cast(v4i, acc[g][f]);
-    __syncthreads();
-    if (wave >= NG * MT) return;
-    const int f = wave % MT;
-    const int nb = nb0 + wave / MT;
-    AccT t = __builtin_bit_cast(AccT, red[0][wave][lane]);
-#pragma unroll
-    for (int w = 1; w < WAVES; ++w) t += __builtin_bit_cast(AccT, red[w][wave][lane]);
-
-    // ---- epilogue: lane l holds D[n = 4 (l / 16) + i][m = l % 16], i < 4 ----
-    const int m = f * 16 + r;
-    const int n = nb * 16 + 4 * c;
-    const uint32_t row = (uint32_t)m * (uint32_t)N + (uint32_t)n;
-    if constexpr (OUT_I32) {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, t), rs_o, m < M ? row * 4u : kBufferOutside, 0, 0);
-    } else {
-        const float4 s4 = DEC ? *reinterpret_cast<const float4*>(wq + (size_t)nb * grp_bytes + 16 * c)
-                              : *reinterpret_cast<const float4*>(sw + n);
-        float y0, y1, y2, y3;
-        if constexpr (A16) {
-            y0 = t[0] * s4.x;
-            y1 = t[1] * s4.y;
-            y2 = t[2] * s4.z;
-            y3 = t[3] * s4.w;
+    // ---- epilogue: lane l holds D[n = 4 (l / 16) + i][m = l % 16], i < 4, of
+    // fragment f of weight group g ----
+    auto epilogue = [&](int g, int f, AccT t) {
+        const int nb = nb0 + g;
+        const int m = f * 16 + r;
+        const int n = nb * 16 + 4 * c;
+        const uint32_t row = (uint32_t)m * (uint32_t)N + (uint32_t)n;
+        if constexpr (OUT_I32) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, t), rs_o, m < M ? row * 4u : kBufferOutside,
+                                                   0, 0);
         } else {
-            const float sxm = sx[min(m, M - 1)];
-            y0 = ((float)t[0] * sxm) * s4.x;
-            y1 = ((float)t[1] * sxm) * s4.y;
-            y2 = ((float)t[2] * sxm) * s4.z;
-            y3 = ((float)t[3] * sxm) * s4.w;
+            const float4 s4 = DEC ? *reinterpret_cast<const float4*>(wq + (size_t)nb * grp_bytes + 16 * c)
+                                  : *reinterpret_cast<const float4*>(sw + n);
+            float y0, y1, y2, y3;
+            if constexpr (A16) {
+                y0 = t[0] * s4.x;
+                y1 = t[1] * s4.y;
+                y2 = t[2] * s4.z;
+                y3 = t[3] * s4.w;
+            } else {
+                const float sxm = sx[min(m, M - 1)];
+                y0 = ((float)t[0] * sxm) * s4.x;
+                y1 = ((float)t[1] * sxm) * s4.y;
+                y2 = ((float)t[2] * sxm) * s4.z;
+                y3 = ((float)t[3] * sxm) * s4.w;
+            }
+            epi_extra4(y0, y1, y2, y3, ex, min(m, M - 1), n, N);
+            const u32x2 d = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+            __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, m < M ? row * 2u : kBufferOutside, 0, 0);
         }
-        epi_extra4(y0, y1, y2, y3, ex, min(m, M - 1), n, N);
-        const u32x2 d = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-        __builtin_amdgcn_raw_buffer_store_b64(d, rs_o, m < M ? row * 2u : kBufferOutside, 0, 0);
+    };
+
+    // ---- sum the waves' partial accumulators (in wave order), PASS fragments
+    // at a time, wave q taking fragment p0 + q ----
+#pragma unroll
+    for (int p0 = 0; p0 < NF; p0 += PASS) {
+        if (p0 > 0) __syncthreads();   // the previous pass has read its sums
+#pragma unroll
+        for (int q = 0; q < PASS; ++q)
+            red[wave][q][lane] = __builtin_bit_cast(v4i, acc[(p0 + q) / MT][(p0 + q) % MT]);
+        __syncthreads();
+        if (wave < PASS) {
+            AccT t = __builtin_bit_cast(AccT, red[0][wave][lane]);
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w) t += __builtin_bit_cast(AccT, red[w][wave][lane]);
+            epilogue((p0 + wave) / MT, (p0 + wave) % MT, t);
+        }
     }
 #endif  // __HIP_DEVICE_COMPILE__
 }
@@ -227,12 +237,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_kernel(
 // 16 rows and more (below, the padding rows load nothing).  Measured at
 // N = 8192..28672: two groups with one workgroup per CU beat one group with two
 // per CU; four beat two at 17..32 rows, and for W8A16 (twice the activation
-// bytes) at 16; INT8 at 16 rows gains nothing from four.  Not four at MT = 4:
-// its sums would take 128 KB of LDS.
+// bytes) at 16; INT8 at 16 rows gains nothing from four.  (W8A16 at 33..64
+// rows on N this wide runs on tiles.)
 int groups_per_wg(int M, int N, int MT, bool a16)
 {
     if (MT > 4 || M < 16) return 1;
-    if ((MT == 2 || (MT == 1 && a16)) && N % 64 == 0 && N / 64 >= num_cus()) return 4;
+    if ((MT == 2 || (MT == 4 && !a16) || (MT == 1 && a16)) && N % 64 == 0 && N / 64 >= num_cus()) return 4;
     if (N % 32 == 0 && N / 32 >= num_cus()) return 2;
     return 1;
 }
@@ -245,7 +255,7 @@ hipError_t launch(const int8_t* xq, const float* sx, const int8_t* wq, const flo
     const int n_rows = (N + 255) / 256 * 256;
     if constexpr (MT <= 4) {
         const int ng = groups_per_wg(M, N, MT, A16);
-        if constexpr (MT == 2 || (MT == 1 && A16)) {
+        if constexpr (MT == 2 || (MT == 4 && !A16) || (MT == 1 && A16)) {
             if (ng == 4) {
                 hipLaunchKernelGGL((gemm_small_kernel<MT, I32, DEC, A16, 4>), dim3(N / 64), dim3(WAVES * 64), 0,
                                    st, xq, sx, wq, sw, M, N, K, m_rows, n_rows, out, ex);

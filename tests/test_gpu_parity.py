@@ -915,7 +915,8 @@ def test_calls_replay_bit_exact_from_a_hip_graph():
     synchronisation), so a call sequence can be captured into a HIP graph.
     Each replay, with new inputs copied in eagerly between replays, must match
     the eager calls bit for bit."""
-    say("graph capture: ck_swiglu_mlp (decode, m=1) + ck_int8_linear (blocked, m=300)")
+    say("graph capture: ck_swiglu_mlp (decode, m=1; blocked, m=2) + ck_swiglu_mlp_w8a16 (m=1) + "
+        "ck_int8_linear (blocked, m=300)")
     g = 128
     rng = np.random.default_rng(17)
     h, i = 1024, 2816
@@ -930,10 +931,18 @@ def test_calls_replay_bit_exact_from_a_hip_graph():
     y2 = torch.empty((300, 528), dtype=torch.bfloat16, device=DEV)
     ws1 = torch.empty(ck.lib().ck_swiglu_mlp_workspace_size(1, h, i), dtype=torch.uint8, device=DEV)
     ws2 = torch.empty(ck.lib().ck_int8_linear_workspace_size(300, 768), dtype=torch.uint8, device=DEV)
+    bgu, bd = ck.ck_weight_pack(gq), ck.ck_weight_pack(dq)
+    x3 = torch.zeros((2, h), dtype=torch.bfloat16, device=DEV)
+    y3 = torch.empty((2, h), dtype=torch.bfloat16, device=DEV)
+    y4 = torch.empty((1, h), dtype=torch.bfloat16, device=DEV)
+    ws3 = torch.empty(ck.lib().ck_swiglu_mlp_workspace_size(2, h, i), dtype=torch.uint8, device=DEV)
+    ws4 = torch.empty(ck.lib().ck_swiglu_mlp_w8a16_workspace_size(1, h, i), dtype=torch.uint8, device=DEV)
 
     def calls():
         ck.ck_swiglu_mlp(x1, dgu, None, dd, None, g, out=y1, workspace=ws1, layout="decode")
         ck.ck_int8_linear(x2, wlb, sl, g, out=y2, workspace=ws2, layout="blocked")
+        ck.ck_swiglu_mlp(x3, bgu, gs, bd, ds, g, out=y3, workspace=ws3, layout="blocked")
+        ck.ck_swiglu_mlp_w8a16(x1, bgu, gs, bd, ds, g, out=y4, workspace=ws4)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -948,14 +957,15 @@ def test_calls_replay_bit_exact_from_a_hip_graph():
         a2 = rng.standard_normal((300, 768)).astype(np.float32)
         x1.copy_(torch.from_numpy(a1).to(DEV).to(torch.bfloat16))
         x2.copy_(torch.from_numpy(a2).to(DEV).to(torch.bfloat16))
+        x3.copy_(torch.from_numpy(rng.standard_normal((2, h)).astype(np.float32)).to(DEV).to(torch.bfloat16))
         graph.replay()
         torch.cuda.synchronize()
-        g1, g2 = y1.clone(), y2.clone()
+        got = [t.clone() for t in (y1, y2, y3, y4)]
         calls()                                   # eager reference on the same inputs
         torch.cuda.synchronize()
-        assert torch.equal(g1.view(torch.int16), y1.view(torch.int16)), f"replay {rep}: mlp differs"
-        assert torch.equal(g2.view(torch.int16), y2.view(torch.int16)), f"replay {rep}: linear differs"
-        assert g1.abs().sum() > 0 and g2.abs().sum() > 0
+        for what, gt, want in zip(("mlp decode", "linear", "mlp blocked", "mlp w8a16"), got, (y1, y2, y3, y4)):
+            assert torch.equal(gt.view(torch.int16), want.view(torch.int16)), f"replay {rep}: {what} differs"
+            assert gt.abs().sum() > 0, f"replay {rep}: {what} is all zeros"
 
 
 def test_concurrent_calls_on_separate_streams():

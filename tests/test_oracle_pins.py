@@ -358,6 +358,27 @@ def test_accuracy_class_tiny_workload(orc):
     assert 0.003 < e < 0.03, e
 
 
+def test_eager_swiglu_golden(orc):
+    """sglang PR #44196, "Motivation": the eager path rounds silu(gate) to BF16,
+    multiplies by up and rounds the product to BF16 (round-half-even).  The
+    golden's values are worked out by hand from the exact silu; cases 1-3 and
+    5-6 change if the silu rounding is dropped, case 2 and 5 if the final
+    rounding truncates, cases 4-6 if ties do not go to even."""
+    rows = read_golden("eager_swiglu_bf16.txt")
+    gate = np.array([int(r[0], 16) for r in rows], dtype=np.uint16)
+    up = np.array([int(r[1], 16) for r in rows], dtype=np.uint16)
+    eager = np.array([int(r[2], 16) for r in rows], dtype=np.uint16)
+    once = np.array([int(r[3], 16) for r in rows], dtype=np.uint16)
+    # one row [gate | up] per case, k = 1
+    x = np.stack([gate, up], axis=1)
+    got = orc.eager_swiglu_bf16(x)[:, 0]
+    np.testing.assert_array_equal(got, eager)
+    # the same cases with silu kept in FP32 (rounded once, after the product)
+    fused = orc.f32_to_bf16(orc.silu_bf16(gate) * orc.bf16_to_f32(up))
+    np.testing.assert_array_equal(fused, once)
+    assert np.count_nonzero(eager != once) == 5
+
+
 def test_fused_swiglu_not_worse_than_eager(orc):
     """sglang PR #44196, "Accuracy Tests": keeping silu(gate)*up in FP32 is no
     worse against the FP32 reference than rounding it to BF16 first."""

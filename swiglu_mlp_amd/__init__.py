@@ -8,25 +8,38 @@ missing, importing any entry point raises.
 
 Entry points keep the C names:
 
-* ``ck_weight_prep(w, group)``           -> (w_q int8 [n, k], w_scale f32 [n, 1])
-* ``ck_weight_pack(w_q)``                 -> w_q in the blocked layout [n_pad, k]
+* ``ck_weight_prep(w, group, layout="blocked")`` -> (w_q int8, w_scale f32 [n, 1])
+* ``ck_weight_pack(w_q)``                 -> w_q in the blocked layout
 * ``ck_weight_pack_decode(w_q, w_scale)`` -> codes and scales in the decode layout
-* ``ck_act_quant(x, act, group, k=None, layout=...)`` -> (x_q, x_scale f32 [m, 1])
-* ``ck_int8_linear(x, w_q, w_scale, group, input_act=None, layout=..., bias=None, residual=None)``
-* ``ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, layout=..., bias=None, residual=None)``
-* ``ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group, layout=...)`` -> y bf16
+* ``ck_act_quant(x, act, group, k=None, layout="blocked")`` -> (x_q, x_scale f32 [m, 1])
+* ``ck_int8_linear(x, w_q, w_scale, group, input_act=None, layout=None, bias=None, residual=None)``
+* ``ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, layout=None, bias=None, residual=None)``
+* ``ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group, layout=None)`` -> y bf16
 * W8A16 (BF16 activations, INT8 weights in the blocked layout):
   ``ck_act_rotate_bf16``, ``ck_w8a16_gemm_bf16``, ``ck_int8_linear_w8a16``,
   ``ck_swiglu_mlp_w8a16``
 * test hooks ``ck_int8_gemm_i32``, ``ck_w8a16_gemm_f32``, ``ck_silu_f32``, ``ck_act_rotate_f32``
 
-``layout`` is ``"rows"`` (row-major int8, the serialized checkpoint format),
-``"blocked"`` (the GEMM-native layout of include/ck.h, rows padded to 256) or
-``"decode"`` (weights only, at most 64 token rows: each 16-row group of the
-weight one linear stream with its row scales in front; activation codes are
-then blocked).  With blocked operands the logical row counts come from the
-scale vectors; a decode weight is a uint8 [n / 16, 64 + 16 k] tensor that
-carries its scales, and its ``w_scale`` argument may be None.
+INT8 operand layouts, each with its own tensor form so that a call can tell
+them apart:
+
+* blocked (the GEMMs' fast path, include/ck.h ``CK_LAYOUT_BLOCKED``): int8
+  ``[R / 32, k / 32, 1024]`` with R the row count padded to 256; entry (i, j)
+  is the 1 KB MFMA operand block of rows 32 i .. 32 i + 31 and columns
+  32 j .. 32 j + 31.  ``ck_weight_prep`` and ``ck_act_quant`` return it by
+  default, so ``ck_int8_linear(x, *ck_weight_prep(w))`` runs the blocked GEMM.
+* row-major (``layout="rows"``): int8 ``[rows, k]``, the serialized checkpoint
+  format.
+* decode (weights only, at most 64 token rows): uint8 ``[n / 16, 64 + 16 k]``,
+  each 16-row group of the weight one linear stream with its row scales in
+  front; its ``w_scale`` argument is None and the activation codes are blocked.
+
+With ``layout=None`` (the default of the linear, GEMM and MLP calls) the layout
+is read off the weight tensor; an explicit ``layout`` string also accepts a
+blocked operand as the same bytes viewed ``[R, k]``.  With blocked operands the
+logical row counts come from the scale vectors.  ``out`` must be a contiguous
+BF16 tensor of the output's shape on the input's device that shares no memory
+with the inputs (it may be the residual itself).
 
 Shapes and error behaviour follow sglang PR #35994 report, key source excerpts:
 an INT8 weight is 2-D ``[out_features, in_features]`` with an F32
@@ -170,6 +183,19 @@ def _layout_code(layout):
     raise ValueError(f"unknown layout {layout!r}")
 
 
+def _weight_layout(layout, w):
+    """The layout code of a weight operand: `layout` when given, else read off
+    the tensor (3-D int8: blocked; 2-D uint8: decode; 2-D int8: row-major)."""
+    import torch
+    if layout is not None:
+        return _layout_code(layout)
+    if not isinstance(w, torch.Tensor):
+        raise ValueError("weight must be a torch.Tensor")
+    if w.dtype == torch.uint8:
+        return CK_LAYOUT_DECODE
+    return CK_LAYOUT_BLOCKED if w.dim() == 3 else CK_LAYOUT_ROWS
+
+
 def blocked_rows(rows: int) -> int:
     return int(lib().ck_blocked_rows(rows))
 
@@ -184,21 +210,42 @@ def _decode_shape(w, what):
     return 16 * w.shape[0], (w.shape[1] - 64) // 16
 
 
+def _operand(t, rows, layout, what):
+    """Check an int8 operand holds `rows` logical rows in `layout`; returns k.
+    Row-major: [rows, k].  Blocked: [R / 32, k / 32, 1024] (one 1 KB block
+    per entry), or the same bytes as [R, k], with R = blocked_rows(rows)."""
+    import torch
+    if layout == CK_LAYOUT_ROWS:
+        _need(t, torch.int8, 2, what)
+        if t.shape[0] != rows:
+            raise ValueError(f"{what} needs {rows} rows in the row-major layout, got {t.shape[0]}")
+        return t.shape[1]
+    need = blocked_rows(rows)
+    if isinstance(t, torch.Tensor) and t.dim() == 3:
+        _need(t, torch.int8, 3, what)
+        if t.shape[0] * 32 != need or t.shape[2] != 1024:
+            raise ValueError(f"{what} needs shape ({need // 32}, k / 32, 1024) for {rows} logical rows "
+                             f"in the blocked layout, got {tuple(t.shape)}")
+        return t.shape[1] * 32
+    _need(t, torch.int8, 2, what)
+    if t.shape[0] != need:
+        raise ValueError(f"{what} needs {need} rows for {rows} logical rows in the blocked layout, "
+                         f"got {t.shape[0]}")
+    return t.shape[1]
+
+
 def _weight(w, w_scale, lay, what):
     """(n, k) of a weight operand in layout `lay`, with its scale checked."""
-    import torch
     if lay == CK_LAYOUT_DECODE:
         n, k = _decode_shape(w, what)
         if w_scale is not None:
             raise ValueError(f"{what}: the decode layout carries its scales; pass w_scale=None")
         return n, k
-    _need(w, torch.int8, 2, what)
     if w_scale is None:
         raise ValueError(f"{what}: weight scale missing")
     n = w_scale.shape[0]
-    _operand_rows(w, n, lay, what)
     _scale(w_scale, n, what + " scale")
-    return n, w.shape[1]
+    return n, _operand(w, n, lay, what)
 
 
 def _act_layout(lay):
@@ -210,13 +257,47 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _operand_rows(t, rows, layout, what):
-    """Check an int8 operand buffer holds `rows` logical rows in `layout`."""
-    need = rows if layout == CK_LAYOUT_ROWS else blocked_rows(rows)
-    if t.shape[0] != need:
-        raise ValueError(f"{what} needs {need} rows for {rows} logical rows in "
-                         f"{'row-major' if layout == CK_LAYOUT_ROWS else 'blocked'} layout, "
-                         f"got {t.shape[0]}")
+def _span(t):
+    a = t.data_ptr()
+    return a, a + t.numel() * t.element_size()
+
+
+def _overlaps(a, b):
+    (a0, a1), (b0, b1) = _span(a), _span(b)
+    return a0 < b1 and b0 < a1
+
+
+def _out(out, m, n, dev, inputs, residual=None):
+    """The BF16 [m, n] output: a new tensor, or `out` checked for dtype, shape,
+    device and contiguity.  It may not share memory with any of `inputs` (the
+    kernels read those while y is written); it may be the residual itself."""
+    import torch
+    if out is None:
+        return torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, 2, "out")
+    if tuple(out.shape) != (m, n) or out.device != dev:
+        raise ValueError(f"out needs a contiguous ({m}, {n}) bfloat16 tensor on {dev}, "
+                         f"got {tuple(out.shape)} on {out.device}")
+    for name, t in inputs:
+        if t is not None and out.numel() and t.numel() and _overlaps(out, t):
+            raise ValueError(f"out must not share memory with {name}")
+    if residual is not None and _overlaps(out, residual) and residual.data_ptr() != out.data_ptr():
+        raise ValueError("residual must be out itself or not overlap it")
+    return out
+
+
+def _workspace(ws, nbytes, dev):
+    """A caller's workspace: a contiguous uint8 tensor on `dev` of at least
+    `nbytes` bytes (a new one when None)."""
+    import torch
+    if ws is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _need(ws, torch.uint8, 1, "workspace")
+    if ws.device != dev:
+        raise ValueError(f"workspace must be on {dev}, got {ws.device}")
+    if ws.numel() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes, got {ws.numel()}")
+    return ws
 
 
 def _act_code(input_act):
@@ -230,24 +311,37 @@ def _act_code(input_act):
 # ---------------------------------------------------------------------------
 # Entry points (same names as the C ABI)
 # ---------------------------------------------------------------------------
-def ck_weight_prep(w, group: int = 128):
+def ck_weight_prep(w, group: int = 128, layout="blocked"):
+    """Rotate and quantize an FP32 weight [n, k] -> (w_q, w_scale [n, 1]).
+    layout "blocked" (default, the GEMMs' fast path): w_q [R / 32, k / 32, 1024];
+    "rows": row-major [n, k] (the serialized checkpoint format); "decode":
+    (uint8 [n / 16, 64 + 16 k] with the scales inside, None)."""
     import torch
     _need(w, torch.float32, 2, "weight")
+    lay = _layout_code(layout)
     n, k = w.shape
     _check_group(k, group)
     w_q = torch.empty((n, k), dtype=torch.int8, device=w.device)
     w_scale = torch.empty((n, 1), dtype=torch.float32, device=w.device)
     _call("ck_weight_prep", w.data_ptr(), n, k, group, w_q.data_ptr(), w_scale.data_ptr(),
           _stream(w))
+    if lay == CK_LAYOUT_BLOCKED:
+        return ck_weight_pack(w_q), w_scale
+    if lay == CK_LAYOUT_DECODE:
+        return ck_weight_pack_decode(w_q, w_scale), None
     return w_q, w_scale
 
 
 def ck_weight_pack(w_q):
-    """Relayout row-major int8 weight codes [n, k] into the blocked layout."""
+    """Relayout row-major int8 weight codes [n, k] into the blocked layout,
+    returned as [R / 32, k / 32, 1024] (R = blocked_rows(n)): entry (i, j) is
+    the 1 KB block of rows 32 i .. 32 i + 31 and columns 32 j .. 32 j + 31."""
     import torch
     _need(w_q, torch.int8, 2, "weight")
     n, k = w_q.shape
-    out = torch.empty((blocked_rows(n), k), dtype=torch.int8, device=w_q.device)
+    if k % 64:
+        raise ValueError(f"in_features must be a multiple of 64, got {k}")
+    out = torch.empty((blocked_rows(n) // 32, k // 32, 1024), dtype=torch.int8, device=w_q.device)
     _call("ck_weight_pack", w_q.data_ptr(), n, k, out.data_ptr(), _stream(w_q))
     return out
 
@@ -268,17 +362,26 @@ def ck_weight_pack_decode(w_q, w_scale):
     return out
 
 
-def ck_act_quant(x, input_act=None, group: int = 128, k: int | None = None, layout="rows"):
+def ck_act_quant(x, input_act=None, group: int = 128, k: int | None = None, layout="blocked"):
+    """Activation codes and per-row scales (x_q, x_scale [m, 1]).  layout
+    "blocked" (default): x_q [R / 32, k / 32, 1024], the operand form of the
+    blocked GEMMs; "rows": row-major [m, k]."""
     import torch
     _need(x, torch.bfloat16, 2, "activation")
     act = _act_code(input_act)
     lay = _layout_code(layout)
+    if lay == CK_LAYOUT_DECODE:
+        raise ValueError("activation codes use the rows or blocked layout")
     m, ldx = x.shape
     if k is None:
         k = ldx // 2 if act == CK_ACT_SWIGLU else ldx
     _check_group(k, group)
-    rows = m if lay == CK_LAYOUT_ROWS else blocked_rows(m)
-    x_q = torch.empty((rows, k), dtype=torch.int8, device=x.device)
+    if lay == CK_LAYOUT_ROWS:
+        x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    else:
+        if k % 64:
+            raise ValueError(f"in_features must be a multiple of 64, got {k}")
+        x_q = torch.empty((blocked_rows(m) // 32, k // 32, 1024), dtype=torch.int8, device=x.device)
     x_scale = torch.empty((m, 1), dtype=torch.float32, device=x.device)
     _call("ck_act_quant", x.data_ptr(), ldx, m, k, act, group, lay, x_q.data_ptr(),
           x_scale.data_ptr(), _stream(x))
@@ -303,10 +406,12 @@ def _extra(bias, residual, m, n, dev):
 
 
 def ck_int8_linear(x, w_q, w_scale, group: int = 128, input_act=None, out=None,
-                   workspace=None, layout="rows", bias=None, residual=None):
+                   workspace=None, layout=None, bias=None, residual=None):
+    """y = int8_linear(x) (+ bias + residual).  layout None: read off w_q (a
+    blocked weight from ck_weight_prep / ck_weight_pack is 3-D)."""
     import torch
     _need(x, torch.bfloat16, 2, "activation")
-    lay = _layout_code(layout)
+    lay = _weight_layout(layout, w_q)
     n, k = _weight(w_q, w_scale, lay, "weight")
     act = _act_code(input_act)
     m, ldx = x.shape
@@ -314,40 +419,43 @@ def ck_int8_linear(x, w_q, w_scale, group: int = 128, input_act=None, out=None,
     if ldx != need_ld:
         raise ValueError(f"activation needs {need_ld} columns for in_features {k}, got {ldx}")
     _check_group(k, group)
-    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
-    ws_bytes = lib().ck_int8_linear_workspace_size(m, k)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     bp, rp = _extra(bias, residual, m, n, x.device)
+    y = _out(out, m, n, x.device, [("the activation", x), ("the weight", w_q), ("the weight scale", w_scale),
+                                   ("the bias", bias)], residual)
+    ws = _workspace(workspace, lib().ck_int8_linear_workspace_size(m, k), x.device)
     _call("ck_int8_linear", x.data_ptr(), ldx, act, w_q.data_ptr(), _ptr(w_scale), bp, rp,
-          lay, m, n, k, group, y.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x))
+          lay, m, n, k, group, y.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x))
     return y
 
 
-def ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, out=None, layout="rows", bias=None,
+def ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, out=None, layout=None, bias=None,
                       residual=None):
     import torch
-    _need(x_q, torch.int8, 2, "activation codes")
-    lay = _layout_code(layout)
-    k = x_q.shape[1]
+    lay = _weight_layout(layout, w_q)
     m = x_scale.shape[0]
+    _scale(x_scale, m, "activation scale")
+    k = _operand(x_q, m, _act_layout(lay), "activation codes")
     n, kw = _weight(w_q, w_scale, lay, "weight")
     if kw != k:
         raise ValueError(f"in_features mismatch: activation {k}, weight {kw}")
-    _operand_rows(x_q, m, _act_layout(lay), "activation codes")
-    _scale(x_scale, m, "activation scale")
-    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x_q.device)
     bp, rp = _extra(bias, residual, m, n, x_q.device)
+    y = _out(out, m, n, x_q.device, [("the activation codes", x_q), ("the activation scale", x_scale),
+                                     ("the weight", w_q), ("the weight scale", w_scale), ("the bias", bias)],
+             residual)
     _call("ck_int8_gemm_bf16", x_q.data_ptr(), x_scale.data_ptr(), w_q.data_ptr(),
           _ptr(w_scale), bp, rp, lay, m, n, k, y.data_ptr(), _stream(x_q))
     return y
 
 
 def ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group: int = 128, out=None, workspace=None,
-                  layout="rows"):
+                  layout=None):
+    """The SwiGLU MLP block.  layout None: read off w_gu (both weights must
+    share it)."""
     import torch
     _need(x, torch.bfloat16, 2, "activation")
-    lay = _layout_code(layout)
+    lay = _weight_layout(layout, w_gu)
+    if layout is None and _weight_layout(None, w_down) != lay:
+        raise ValueError("gate_up and down weights must use the same layout")
     m, h = x.shape
     i2, kg = _weight(w_gu, s_gu, lay, "gate_up weight")
     if kg != h or i2 % 2:
@@ -358,33 +466,36 @@ def ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group: int = 128, out=None, wor
         raise ValueError(f"down weight needs ({h}, {i}), got ({hd}, {kd})")
     _check_group(h, group)
     _check_group(i, group)
-    y = out if out is not None else torch.empty((m, h), dtype=torch.bfloat16, device=x.device)
-    ws_bytes = lib().ck_swiglu_mlp_workspace_size(m, h, i)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    y = _out(out, m, h, x.device, [("the activation", x), ("the gate_up weight", w_gu), ("its scale", s_gu),
+                                   ("the down weight", w_down), ("its scale", s_down)])
+    ws = _workspace(workspace, lib().ck_swiglu_mlp_workspace_size(m, h, i), x.device)
+    if _overlaps(ws, y) or _overlaps(ws, x):
+        raise ValueError("the workspace must not share memory with the activation or out")
     _call("ck_swiglu_mlp", x.data_ptr(), w_gu.data_ptr(), _ptr(s_gu), w_down.data_ptr(),
-          _ptr(s_down), lay, m, h, i, group, y.data_ptr(), workspace.data_ptr(),
-          workspace.numel(), _stream(x))
+          _ptr(s_down), lay, m, h, i, group, y.data_ptr(), ws.data_ptr(),
+          ws.numel(), _stream(x))
     return y
 
 
-def ck_int8_gemm_i32(x_q, w_q, layout="rows", m: int | None = None, n: int | None = None):
+def ck_int8_gemm_i32(x_q, w_q, layout=None, m: int | None = None, n: int | None = None):
     """Raw int32 accumulators; with blocked operands pass the logical m and n."""
     import torch
-    _need(x_q, torch.int8, 2, "activation codes")
-    lay = _layout_code(layout)
-    k = x_q.shape[1]
-    m = x_q.shape[0] if m is None else m
+    lay = _weight_layout(layout, w_q)
+    if m is None:
+        if lay != CK_LAYOUT_ROWS:
+            raise ValueError("blocked activation codes need the logical row count m")
+        m = x_q.shape[0]
+    k = _operand(x_q, m, _act_layout(lay), "activation codes")
     if lay == CK_LAYOUT_DECODE:
         n, kw = _decode_shape(w_q, "weight")
     else:
-        _need(w_q, torch.int8, 2, "weight")
-        n = w_q.shape[0] if n is None else n
-        kw = w_q.shape[1]
-        _operand_rows(w_q, n, lay, "weight")
+        if n is None:
+            if lay != CK_LAYOUT_ROWS:
+                raise ValueError("a blocked weight needs the logical row count n")
+            n = w_q.shape[0]
+        kw = _operand(w_q, n, lay, "weight")
     if kw != k:
         raise ValueError(f"in_features mismatch: activation {k}, weight {kw}")
-    _operand_rows(x_q, m, _act_layout(lay), "activation codes")
     acc = torch.empty((m, n), dtype=torch.int32, device=x_q.device)
     _call("ck_int8_gemm_i32", x_q.data_ptr(), w_q.data_ptr(), lay, m, n, k, acc.data_ptr(),
           _stream(x_q))
@@ -411,24 +522,25 @@ def ck_act_rotate_bf16(x, input_act=None, group: int = 128, k: int | None = None
 def _w8a16_operands(x_rot, w_q, m, n):
     import torch
     _need(x_rot, torch.bfloat16, 2, "rotated activation")
-    _need(w_q, torch.int8, 2, "weight")
     k = x_rot.shape[1]
-    if w_q.shape[1] != k:
-        raise ValueError(f"in_features mismatch: activation {k}, weight {w_q.shape[1]}")
-    _operand_rows(x_rot, m, CK_LAYOUT_BLOCKED, "rotated activation")
-    _operand_rows(w_q, n, CK_LAYOUT_BLOCKED, "weight")
+    if x_rot.shape[0] != blocked_rows(m):
+        raise ValueError(f"rotated activation needs {blocked_rows(m)} rows for {m} logical rows in "
+                         f"the blocked layout, got {x_rot.shape[0]}")
+    kw = _operand(w_q, n, CK_LAYOUT_BLOCKED, "weight")
+    if kw != k:
+        raise ValueError(f"in_features mismatch: activation {k}, weight {kw}")
     return k
 
 
 def ck_w8a16_gemm_bf16(x_rot, w_q, w_scale, m: int, out=None, bias=None, residual=None):
     """y = bf16(acc * w_scale (+ bias) (+ residual)); x_rot in the BF16 blocked
     layout with m logical rows, w_q blocked."""
-    import torch
     n = w_scale.shape[0]
     _scale(w_scale, n, "weight_scale")
     k = _w8a16_operands(x_rot, w_q, m, n)
-    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x_rot.device)
     bp, rp = _extra(bias, residual, m, n, x_rot.device)
+    y = _out(out, m, n, x_rot.device, [("the rotated activation", x_rot), ("the weight", w_q),
+                                       ("the weight scale", w_scale), ("the bias", bias)], residual)
     _call("ck_w8a16_gemm_bf16", x_rot.data_ptr(), w_q.data_ptr(), w_scale.data_ptr(), bp, rp, m, n, k,
           y.data_ptr(), _stream(x_rot))
     return y
@@ -449,24 +561,21 @@ def ck_int8_linear_w8a16(x, w_q, w_scale, group: int = 128, input_act=None, out=
     """W8A16 linear: BF16 rotated activation times the blocked INT8 weight."""
     import torch
     _need(x, torch.bfloat16, 2, "activation")
-    _need(w_q, torch.int8, 2, "weight")
     n = w_scale.shape[0]
     _scale(w_scale, n, "weight_scale")
-    _operand_rows(w_q, n, CK_LAYOUT_BLOCKED, "weight")
-    k = w_q.shape[1]
+    k = _operand(w_q, n, CK_LAYOUT_BLOCKED, "weight")
     act = _act_code(input_act)
     m, ldx = x.shape
     need_ld = 2 * k if act == CK_ACT_SWIGLU else k
     if ldx != need_ld:
         raise ValueError(f"activation needs {need_ld} columns for in_features {k}, got {ldx}")
     _check_group(k, group)
-    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
-    ws_bytes = lib().ck_int8_linear_w8a16_workspace_size(m, k)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     bp, rp = _extra(bias, residual, m, n, x.device)
+    y = _out(out, m, n, x.device, [("the activation", x), ("the weight", w_q), ("the weight scale", w_scale),
+                                   ("the bias", bias)], residual)
+    ws = _workspace(workspace, lib().ck_int8_linear_w8a16_workspace_size(m, k), x.device)
     _call("ck_int8_linear_w8a16", x.data_ptr(), ldx, act, w_q.data_ptr(), w_scale.data_ptr(), bp, rp,
-          m, n, k, group, y.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x))
+          m, n, k, group, y.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x))
     return y
 
 
@@ -484,12 +593,13 @@ def ck_swiglu_mlp_w8a16(x, w_gu, s_gu, w_down, s_down, group: int = 128, out=Non
         raise ValueError(f"down weight needs ({h}, {i}), got ({hd}, {kd})")
     _check_group(h, group)
     _check_group(i, group)
-    y = out if out is not None else torch.empty((m, h), dtype=torch.bfloat16, device=x.device)
-    ws_bytes = lib().ck_swiglu_mlp_w8a16_workspace_size(m, h, i)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    y = _out(out, m, h, x.device, [("the activation", x), ("the gate_up weight", w_gu), ("its scale", s_gu),
+                                   ("the down weight", w_down), ("its scale", s_down)])
+    ws = _workspace(workspace, lib().ck_swiglu_mlp_w8a16_workspace_size(m, h, i), x.device)
+    if _overlaps(ws, y) or _overlaps(ws, x):
+        raise ValueError("the workspace must not share memory with the activation or out")
     _call("ck_swiglu_mlp_w8a16", x.data_ptr(), w_gu.data_ptr(), s_gu.data_ptr(), w_down.data_ptr(),
-          s_down.data_ptr(), m, h, i, group, y.data_ptr(), workspace.data_ptr(), workspace.numel(),
+          s_down.data_ptr(), m, h, i, group, y.data_ptr(), ws.data_ptr(), ws.numel(),
           _stream(x))
     return y
 

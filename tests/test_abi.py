@@ -235,3 +235,19 @@ def test_header_compiles_as_c_and_links(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "all checks passed" in r.stdout
+
+
+def test_binding_layout_inference_and_overlap_on_host_tensors():
+    """Host-side helpers of the binding (no GPU): the layout is read off the
+    weight tensor's form, and output/input overlap is detected by byte range."""
+    torch = pytest.importorskip("torch")
+    assert ck._weight_layout(None, torch.zeros((8, 2, 1024), dtype=torch.int8)) == ck.CK_LAYOUT_BLOCKED
+    assert ck._weight_layout(None, torch.zeros((256, 64), dtype=torch.int8)) == ck.CK_LAYOUT_ROWS
+    assert ck._weight_layout(None, torch.zeros((4, 1088), dtype=torch.uint8)) == ck.CK_LAYOUT_DECODE
+    assert ck._weight_layout("rows", torch.zeros((8, 2, 1024), dtype=torch.int8)) == ck.CK_LAYOUT_ROWS
+    with pytest.raises(ValueError):
+        ck._weight_layout("tiled", torch.zeros((8, 2), dtype=torch.int8))
+    buf = torch.zeros(64, dtype=torch.bfloat16)
+    assert ck._overlaps(buf[:32], buf[16:48])
+    assert not ck._overlaps(buf[:32], buf[32:])
+    assert ck._overlaps(buf, buf)

@@ -6,9 +6,10 @@ Bars (stated per check below):
   * BF16 outputs: within 1 BF16 ulp or 1e-2 relative per element; the pinned
     epilogue makes them bit-exact, which is asserted too.
   * relative L2 against the float64 reference: GPU <= oracle + 1e-4.
-Full-size workloads are compared on sampled rows (every step of the path is
-per row, so the oracle computes those rows end to end from the same inputs).
+Full-size workloads are compared on every element: the oracle runs each whole
+workload once (cached for the row-major and blocked tests alike).
 """
+import functools
 import sys
 
 import numpy as np
@@ -24,6 +25,11 @@ import swiglu_mlp_amd as ck  # noqa: E402
 from swiglu_mlp_amd import workloads as W  # noqa: E402
 
 DEV = "cuda:0"
+
+# row-major weight codes and activation codes (the bindings default to the
+# blocked layout; these tests also cover the row-major path)
+prep_rows = functools.partial(ck.ck_weight_prep, layout="rows")
+act_quant = functools.partial(ck.ck_act_quant, layout="rows")
 
 
 def say(msg):
@@ -71,16 +77,11 @@ def to_blocked(a):
 
 
 def from_blocked(b, rows):
+    if b.ndim == 3:                     # the binding's [R / 32, k / 32, 1024] form
+        b = b.reshape(b.shape[0] * 32, b.shape[1] * 32)
     rp, k = b.shape
     a = b.reshape(rp // 32, k // 32, 2, 32, 16).transpose(0, 3, 1, 2, 4).reshape(rp, k)
     return np.ascontiguousarray(a[:rows])
-
-
-def sample_rows(m, count=16, seed=0):
-    rng = np.random.default_rng(seed)
-    fixed = [0, 1, m // 3, m // 2, m - 2, m - 1]
-    rest = rng.choice(m, size=max(0, count - len(fixed)), replace=False)
-    return np.unique(np.clip(np.concatenate([fixed, rest]), 0, m - 1))
 
 
 _cache = {}
@@ -100,6 +101,40 @@ def prepped(orc, name, key="w"):
     return _cache[ck_key]
 
 
+def full_ref(orc, name):
+    """The oracle on the whole workload, with every intermediate (cached)."""
+    key = ("ref", name)
+    if key not in _cache:
+        wl = W.WORKLOADS[name]
+        d = inputs(name)
+        if wl.kind == "mlp":
+            (gq, gs), (dq, ds) = prepped(orc, name, "w_gu"), prepped(orc, name, "w_down")
+            _cache[key] = orc.swiglu_mlp(d["x"], gq, gs, dq, ds, wl.group, return_all=True)
+        else:
+            wq_o, sw_o = prepped(orc, name)
+            _cache[key] = orc.int8_linear(d["x"], wl.act, wq_o, sw_o, wl.group, return_all=True)
+    return _cache[key]
+
+
+def ref_f64(orc, name):
+    """The float64 reference (unrotated, unquantized weights) of the whole workload."""
+    key = ("f64", name)
+    if key not in _cache:
+        wl = W.WORKLOADS[name]
+        d = inputs(name)
+        _cache[key] = (orc.reference_mlp_f64(d["x"], d["w_gu"], d["w_down"]) if wl.kind == "mlp"
+                       else orc.reference_linear_f64(d["x"], wl.act, d["w"]))
+    return _cache[key]
+
+
+def check_codes(q_gpu, s_gpu, ref, m, what, blocked):
+    """Activation codes and scales of every row against the oracle's, bit for bit."""
+    q = from_blocked(host(q_gpu), m) if blocked else host(q_gpu)
+    np.testing.assert_array_equal(host(s_gpu).reshape(-1).view(np.uint32), ref["sx"].view(np.uint32),
+                                  err_msg=what + " scales")
+    np.testing.assert_array_equal(q, ref["xq"], err_msg=what + " codes")
+
+
 # ---------------------------------------------------------------------------
 def test_silu_exhaustive_bf16(orc):
     say("silu: all 65536 BF16 patterns")
@@ -116,7 +151,7 @@ def test_silu_exhaustive_bf16(orc):
 def test_weight_prep_bit_exact(orc, name, key):
     w = inputs(name)[key]
     say(f"weight_prep {name}.{key} {w.shape}")
-    q, s = ck.ck_weight_prep(dev(w), W.WORKLOADS[name].group)
+    q, s = prep_rows(dev(w), W.WORKLOADS[name].group)
     torch.cuda.synchronize()
     q_o, s_o = prepped(orc, name, key)
     np.testing.assert_array_equal(host(q), q_o)
@@ -129,7 +164,7 @@ def test_act_quant_bit_exact(orc, name):
     x = inputs(name)["x"]
     act = 0 if wl.kind == "mlp" else wl.act
     say(f"act_quant {name} act={act} x{x.shape}")
-    q, s = ck.ck_act_quant(bf16_dev(x), act, wl.group)
+    q, s = act_quant(bf16_dev(x), act, wl.group)
     torch.cuda.synchronize()
     q_o, s_o = orc.act_quant(x, act, wl.group)
     np.testing.assert_array_equal(host(s)[:, 0].view(np.uint32), s_o.view(np.uint32))
@@ -203,7 +238,7 @@ def test_int8_linear_bit_exact(orc, m, k, n, act, g):
     say(f"int8_linear m={m} k={k} n={n} act={act} g={g}")
     d = W.case(m, k, n, act, seed=1000 + m, zero_rows=(m // 2,) if m > 2 else ())
     wq_o, sw_o = orc.weight_prep(d["w"], g)
-    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    wq, sw = prep_rows(dev(d["w"]), g)
     y = bf16_host(ck.ck_int8_linear(bf16_dev(d["x"]), wq, sw, g, act))
     ref = orc.int8_linear(d["x"], act, wq_o, sw_o, g, return_all=True)
     np.testing.assert_array_equal(host(wq), wq_o)
@@ -213,43 +248,42 @@ def test_int8_linear_bit_exact(orc, m, k, n, act, g):
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
-def test_full_workload_sampled_rows(orc, name):
+def test_full_workload_all_elements(orc, name):
+    """Row-major path at full size: codes, scales, int32 accumulators and BF16
+    outputs of every row."""
     wl = W.WORKLOADS[name]
     d = inputs(name)
     say(f"int8_linear full {name}: {wl.desc}")
-    wq, sw = ck.ck_weight_prep(dev(d["w"]), wl.group)
+    wq, sw = prep_rows(dev(d["w"]), wl.group)
     x_dev = bf16_dev(d["x"])
     y = ck.ck_int8_linear(x_dev, wq, sw, wl.group, wl.act)
-    xq_dev, sx_dev = ck.ck_act_quant(x_dev, wl.act, wl.group)
+    xq_dev, sx_dev = act_quant(x_dev, wl.act, wl.group)
     acc = ck.ck_int8_gemm_i32(xq_dev, wq)
     torch.cuda.synchronize()
-    rows = sample_rows(wl.m)
-    y_rows = bf16_host(y)[rows]
-    wq_o, sw_o = prepped(orc, name)
-    ref = orc.int8_linear(d["x"][rows], wl.act, wq_o, sw_o, wl.group, return_all=True)
-    np.testing.assert_array_equal(host(acc)[rows], ref["acc"])
-    assert_bf16_close(y_rows, ref["y"], f"{name} sampled rows")
-    y64 = orc.reference_linear_f64(d["x"][rows], wl.act, d["w"])
-    e_gpu, e_orc = orc.rel_l2(y_rows, y64), orc.rel_l2(ref["y"], y64)
+    ref = full_ref(orc, name)
+    check_codes(xq_dev, sx_dev, ref, wl.m, name, False)
+    np.testing.assert_array_equal(host(acc), ref["acc"])
+    y_h = bf16_host(y)
+    assert_bf16_close(y_h, ref["y"], f"{name} all rows")
+    y64 = ref_f64(orc, name)
+    e_gpu, e_orc = orc.rel_l2(y_h, y64), orc.rel_l2(ref["y"], y64)
     say(f"{name}: relL2 gpu={e_gpu:.5f} oracle={e_orc:.5f}")
     assert e_gpu <= e_orc + 1e-4
 
 
-def test_swiglu_mlp_full_c5_sampled_rows(orc):
+def test_swiglu_mlp_full_c5_all_elements(orc):
     wl = W.WORKLOADS["c5"]
     d = inputs("c5")
     say(f"swiglu_mlp full c5: {wl.desc}")
-    wgu, sgu = ck.ck_weight_prep(dev(d["w_gu"]), wl.group)
-    wd, sd = ck.ck_weight_prep(dev(d["w_down"]), wl.group)
+    wgu, sgu = prep_rows(dev(d["w_gu"]), wl.group)
+    wd, sd = prep_rows(dev(d["w_down"]), wl.group)
     y = ck.ck_swiglu_mlp(bf16_dev(d["x"]), wgu, sgu, wd, sd, wl.group)
     torch.cuda.synchronize()
-    rows = sample_rows(wl.m)
-    y_rows = bf16_host(y)[rows]
-    (gq, gs), (dq, ds) = prepped(orc, "c5", "w_gu"), prepped(orc, "c5", "w_down")
-    ref = orc.swiglu_mlp(d["x"][rows], gq, gs, dq, ds, wl.group)
-    assert_bf16_close(y_rows, ref, "c5 sampled rows")
-    y64 = orc.reference_mlp_f64(d["x"][rows], d["w_gu"], d["w_down"])
-    e_gpu, e_orc = orc.rel_l2(y_rows, y64), orc.rel_l2(ref, y64)
+    ref = full_ref(orc, "c5")
+    y_h = bf16_host(y)
+    assert_bf16_close(y_h, ref["y"], "c5 all rows")
+    y64 = ref_f64(orc, "c5")
+    e_gpu, e_orc = orc.rel_l2(y_h, y64), orc.rel_l2(ref["y"], y64)
     say(f"c5: relL2 gpu={e_gpu:.5f} oracle={e_orc:.5f}")
     assert e_gpu <= e_orc + 1e-4
 
@@ -261,13 +295,13 @@ def test_swiglu_mlp_equals_its_stages():
     m, h, i, g = 512, 1024, 2048, 128
     rng = np.random.default_rng(21)
     x = bf16_dev(W.to_bf16_bits(rng.standard_normal((m, h)).astype(np.float32)))
-    wgu, sgu = ck.ck_weight_prep(dev((0.02 * rng.standard_normal((2 * i, h))).astype(np.float32)), g)
-    wd, sd = ck.ck_weight_prep(dev((0.01 * rng.standard_normal((h, i))).astype(np.float32)), g)
+    wgu, sgu = prep_rows(dev((0.02 * rng.standard_normal((2 * i, h))).astype(np.float32)), g)
+    wd, sd = prep_rows(dev((0.01 * rng.standard_normal((h, i))).astype(np.float32)), g)
     y1 = ck.ck_swiglu_mlp(x, wgu, sgu, wd, sd, g)
     y2 = ck.ck_swiglu_mlp(x, wgu, sgu, wd, sd, g)
-    xq, sx = ck.ck_act_quant(x, 0, g)
+    xq, sx = act_quant(x, 0, g)
     t = ck.ck_int8_gemm_bf16(xq, sx, wgu, sgu)
-    hq, sh = ck.ck_act_quant(t, 1, g)
+    hq, sh = act_quant(t, 1, g)
     y3 = ck.ck_int8_gemm_bf16(hq, sh, wd, sd)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
@@ -283,9 +317,9 @@ def test_packed_gate_up_equals_separate():
     x = bf16_dev(W.to_bf16_bits(rng.standard_normal((m, h)).astype(np.float32)))
     wg = (0.02 * rng.standard_normal((i, h))).astype(np.float32)
     wu = (0.02 * rng.standard_normal((i, h))).astype(np.float32)
-    q, s = ck.ck_weight_prep(dev(np.concatenate([wg, wu])), g)
-    qg, sg = ck.ck_weight_prep(dev(wg), g)
-    qu, su = ck.ck_weight_prep(dev(wu), g)
+    q, s = prep_rows(dev(np.concatenate([wg, wu])), g)
+    qg, sg = prep_rows(dev(wg), g)
+    qu, su = prep_rows(dev(wu), g)
     y = ck.ck_int8_linear(x, q, s, g)
     yg = ck.ck_int8_linear(x, qg, sg, g)
     yu = ck.ck_int8_linear(x, qu, su, g)
@@ -298,7 +332,7 @@ def test_empty_and_degenerate_calls(orc):
     say("empty and degenerate calls")
     g = 128
     x0 = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
-    wq, sw = ck.ck_weight_prep(torch.zeros((32, 256), dtype=torch.float32, device=DEV), g)
+    wq, sw = prep_rows(torch.zeros((32, 256), dtype=torch.float32, device=DEV), g)
     torch.cuda.synchronize()
     assert not wq.any() and not sw.any()                  # all-zero weight rows
     assert ck.ck_int8_linear(x0, wq, sw, g).shape == (0, 32)
@@ -330,7 +364,8 @@ def test_weight_pack_layout(orc, n, k):
     rng = np.random.default_rng(n + k)
     wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
     got = host(ck.ck_weight_pack(dev(wq)))
-    np.testing.assert_array_equal(got, to_blocked(wq))      # padding rows are zero too
+    assert got.shape == (-(-n // 256) * 8, k // 32, 1024)
+    np.testing.assert_array_equal(got.reshape(-1, k), to_blocked(wq))      # padding rows are zero too
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c4"])
@@ -338,7 +373,7 @@ def test_act_quant_blocked(orc, name):
     wl = W.WORKLOADS[name]
     x = inputs(name)["x"]
     say(f"act_quant blocked {name}")
-    q, s = ck.ck_act_quant(bf16_dev(x), wl.act, wl.group, layout="blocked")
+    q, s = act_quant(bf16_dev(x), wl.act, wl.group, layout="blocked")
     q_o, s_o = orc.act_quant(x, wl.act, wl.group)
     np.testing.assert_array_equal(from_blocked(host(q), wl.m), q_o)
     np.testing.assert_array_equal(host(s)[:, 0].view(np.uint32), s_o.view(np.uint32))
@@ -404,7 +439,7 @@ def test_int8_linear_bias_residual_bit_exact(orc, m, k, n, layout):
     bias = rng.standard_normal(n).astype(np.float32)
     res = orc.f32_to_bf16(rng.standard_normal((m, n)).astype(np.float32))
     wq_o, sw_o = orc.weight_prep(d["w"], g)
-    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    wq, sw = prep_rows(dev(d["w"]), g)
     if layout == "blocked":
         wq = ck.ck_weight_pack(wq)
     x = bf16_dev(d["x"])
@@ -426,43 +461,66 @@ def test_int8_linear_blocked_bit_exact(orc, m, k, n, act, g):
     say(f"int8_linear blocked m={m} k={k} n={n} act={act} g={g}")
     d = W.case(m, k, n, act, seed=1000 + m, zero_rows=(m // 2,) if m > 2 else ())
     wq_o, sw_o = orc.weight_prep(d["w"], g)
-    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    wq, sw = prep_rows(dev(d["w"]), g)
     y = bf16_host(ck.ck_int8_linear(bf16_dev(d["x"]), ck.ck_weight_pack(wq), sw, g, act,
                                     layout="blocked"))
     assert_bf16_close(y, orc.int8_linear(d["x"], act, wq_o, sw_o, g), "y")
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
-def test_full_workload_blocked_sampled_rows(orc, name):
+def test_full_workload_blocked_all_elements(orc, name):
+    """The blocked path at full size: blocked codes and scales, int32
+    accumulators and the linear's BF16 output, every element."""
     wl = W.WORKLOADS[name]
     d = inputs(name)
     say(f"int8_linear blocked full {name}: {wl.desc}")
-    wq, sw = ck.ck_weight_prep(dev(d["w"]), wl.group)
-    y = ck.ck_int8_linear(bf16_dev(d["x"]), ck.ck_weight_pack(wq), sw, wl.group, wl.act,
-                          layout="blocked")
+    wq, sw = ck.ck_weight_prep(dev(d["w"]), wl.group)          # blocked by default
+    x_dev = bf16_dev(d["x"])
+    y = ck.ck_int8_linear(x_dev, wq, sw, wl.group, wl.act)
+    xq, sx = ck.ck_act_quant(x_dev, wl.act, wl.group)          # blocked by default
+    acc = ck.ck_int8_gemm_i32(xq, wq, m=wl.m, n=wl.n)
     torch.cuda.synchronize()
-    rows = sample_rows(wl.m, seed=1)
-    wq_o, sw_o = prepped(orc, name)
-    ref = orc.int8_linear(d["x"][rows], wl.act, wq_o, sw_o, wl.group)
-    assert_bf16_close(bf16_host(y)[rows], ref, f"{name} blocked sampled rows")
+    ref = full_ref(orc, name)
+    check_codes(xq, sx, ref, wl.m, name + " blocked", True)
+    np.testing.assert_array_equal(host(acc), ref["acc"])
+    assert_bf16_close(bf16_host(y), ref["y"], f"{name} blocked all rows")
 
 
-def test_swiglu_mlp_blocked_full_c5_sampled_rows(orc):
-    """The benchmarked path: packed weights, blocked activation codes."""
+def test_swiglu_mlp_blocked_full_c5_all_elements(orc):
+    """The benchmarked path at full size: ck_swiglu_mlp's output and, through
+    the stage calls bench.py times, both stages' codes, scales, int32
+    accumulators and the stage-1 BF16 output, every element."""
     wl = W.WORKLOADS["c5"]
     d = inputs("c5")
+    g, m = wl.group, wl.m
     say(f"swiglu_mlp blocked full c5: {wl.desc}")
-    wgu, sgu = ck.ck_weight_prep(dev(d["w_gu"]), wl.group)
-    wd, sd = ck.ck_weight_prep(dev(d["w_down"]), wl.group)
-    y = ck.ck_swiglu_mlp(bf16_dev(d["x"]), ck.ck_weight_pack(wgu), sgu, ck.ck_weight_pack(wd), sd,
-                         wl.group, layout="blocked")
+    wgu, sgu = ck.ck_weight_prep(dev(d["w_gu"]), g)
+    wd, sd = ck.ck_weight_prep(dev(d["w_down"]), g)
+    x = bf16_dev(d["x"])
+    y = ck.ck_swiglu_mlp(x, wgu, sgu, wd, sd, g)
     torch.cuda.synchronize()
-    rows = sample_rows(wl.m, seed=2)
-    (gq, gs), (dq, ds) = prepped(orc, "c5", "w_gu"), prepped(orc, "c5", "w_down")
-    ref = orc.swiglu_mlp(d["x"][rows], gq, gs, dq, ds, wl.group)
-    assert_bf16_close(bf16_host(y)[rows], ref, "c5 blocked sampled rows")
-    y64 = orc.reference_mlp_f64(d["x"][rows], d["w_gu"], d["w_down"])
-    e_gpu, e_orc = orc.rel_l2(bf16_host(y)[rows], y64), orc.rel_l2(ref, y64)
+    ref = full_ref(orc, "c5")
+    s1, s2 = ref["stage1"], ref["stage2"]
+    y_h = bf16_host(y)
+    assert_bf16_close(y_h, ref["y"], "c5 blocked all rows")
+    # stage 1: x codes, scales, accumulators, the [m, 2i] BF16 output
+    xq, sx = ck.ck_act_quant(x, 0, g)
+    acc1 = ck.ck_int8_gemm_i32(xq, wgu, m=m, n=2 * wl.n)
+    torch.cuda.synchronize()
+    check_codes(xq, sx, s1, m, "c5 stage 1", True)
+    np.testing.assert_array_equal(host(acc1), s1["acc"])
+    del acc1
+    t1 = ck.ck_int8_gemm_bf16(xq, sx, wgu, sgu)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_host(t1), s1["y"])
+    # stage 2: the SwiGLU'd codes, scales and accumulators
+    hq, sh = ck.ck_act_quant(t1, 1, g)
+    acc2 = ck.ck_int8_gemm_i32(hq, wd, m=m, n=wl.k)
+    torch.cuda.synchronize()
+    check_codes(hq, sh, s2, m, "c5 stage 2", True)
+    np.testing.assert_array_equal(host(acc2), s2["acc"])
+    y64 = ref_f64(orc, "c5")
+    e_gpu, e_orc = orc.rel_l2(y_h, y64), orc.rel_l2(ref["y"], y64)
     say(f"c5 blocked: relL2 gpu={e_gpu:.5f} oracle={e_orc:.5f}")
     assert e_gpu <= e_orc + 1e-4
 
@@ -474,14 +532,14 @@ def test_blocked_stages_equal_swiglu_mlp():
     m, h, i, g = 1000, 1024, 2048, 128
     rng = np.random.default_rng(31)
     x = bf16_dev(W.to_bf16_bits(rng.standard_normal((m, h)).astype(np.float32)))
-    wgu, sgu = ck.ck_weight_prep(dev((0.02 * rng.standard_normal((2 * i, h))).astype(np.float32)), g)
-    wd, sd = ck.ck_weight_prep(dev((0.01 * rng.standard_normal((h, i))).astype(np.float32)), g)
+    wgu, sgu = prep_rows(dev((0.02 * rng.standard_normal((2 * i, h))).astype(np.float32)), g)
+    wd, sd = prep_rows(dev((0.01 * rng.standard_normal((h, i))).astype(np.float32)), g)
     pgu, pd = ck.ck_weight_pack(wgu), ck.ck_weight_pack(wd)
     y_rows = ck.ck_swiglu_mlp(x, wgu, sgu, wd, sd, g)
     y_blk = ck.ck_swiglu_mlp(x, pgu, sgu, pd, sd, g, layout="blocked")
-    xq, sx = ck.ck_act_quant(x, 0, g, layout="blocked")
+    xq, sx = act_quant(x, 0, g, layout="blocked")
     t1 = ck.ck_int8_gemm_bf16(xq, sx, pgu, sgu, layout="blocked")
-    hq, sh = ck.ck_act_quant(t1, 1, g, layout="blocked")
+    hq, sh = act_quant(t1, 1, g, layout="blocked")
     y_st = ck.ck_int8_gemm_bf16(hq, sh, pd, sd, layout="blocked")
     torch.cuda.synchronize()
     assert torch.equal(y_blk.view(torch.int16), y_rows.view(torch.int16))
@@ -574,7 +632,7 @@ def test_int8_linear_decode_bit_exact(orc, m, k, n, act, g, layout):
     say(f"int8_linear few rows m={m} k={k} n={n} act={act} g={g} layout={layout}")
     d = W.case(m, k, n, act, seed=3000 + m, zero_rows=(m // 2,) if m > 2 else ())
     wq_o, sw_o = orc.weight_prep(d["w"], g)
-    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    wq, sw = prep_rows(dev(d["w"]), g)
     if layout == "decode":
         wd, sl = ck.ck_weight_pack_decode(wq, sw), None
     else:
@@ -599,8 +657,8 @@ def test_swiglu_mlp_decode_bit_exact(orc, m):
     xb = W.to_bf16_bits(rng.standard_normal((m, h)).astype(np.float32))
     w_gu = (0.02 * rng.standard_normal((2 * i, h))).astype(np.float32)
     w_dn = (0.01 * rng.standard_normal((h, i))).astype(np.float32)
-    gq, gs = ck.ck_weight_prep(dev(w_gu), g)
-    dq, ds = ck.ck_weight_prep(dev(w_dn), g)
+    gq, gs = prep_rows(dev(w_gu), g)
+    dq, ds = prep_rows(dev(w_dn), g)
     y = ck.ck_swiglu_mlp(bf16_dev(xb), ck.ck_weight_pack_decode(gq, gs), None,
                          ck.ck_weight_pack_decode(dq, ds), None, g, layout="decode")
     y_blk = ck.ck_swiglu_mlp(bf16_dev(xb), ck.ck_weight_pack(gq), gs, ck.ck_weight_pack(dq), ds,
@@ -623,7 +681,7 @@ def test_fused_decode_equals_the_stages(m, k, act, g, layout):
     n = 1040
     rng = np.random.default_rng(77 + m + k)
     d = W.case(m, k, n, act, seed=4000 + m)
-    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    wq, sw = prep_rows(dev(d["w"]), g)
     if layout == "decode":
         wl, sl = ck.ck_weight_pack_decode(wq, sw), None
     else:
@@ -632,7 +690,7 @@ def test_fused_decode_equals_the_stages(m, k, act, g, layout):
     bias = dev(rng.standard_normal(n).astype(np.float32))
     res = bf16_dev(W.to_bf16_bits(rng.standard_normal((m, n)).astype(np.float32)))
     y = ck.ck_int8_linear(x, wl, sl, g, act, layout=layout, bias=bias, residual=res)
-    xq, sx = ck.ck_act_quant(x, act, g, k=k, layout="blocked")
+    xq, sx = act_quant(x, act, g, k=k, layout="blocked")
     y_st = ck.ck_int8_gemm_bf16(xq, sx, wl, sl, layout=layout, bias=bias, residual=res)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y_st.view(torch.int16))
@@ -649,7 +707,7 @@ def test_w8a16_fused_equals_the_stages(m, k, act, g):
     n = 1040
     rng = np.random.default_rng(79 + m + k)
     d = W.case(m, k, n, act, seed=4100 + m)
-    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    wq, sw = prep_rows(dev(d["w"]), g)
     wb = ck.ck_weight_pack(wq)
     x = bf16_dev(d["x"])
     bias = dev(rng.standard_normal(n).astype(np.float32))
@@ -663,7 +721,7 @@ def test_w8a16_fused_equals_the_stages(m, k, act, g):
 
 def test_decode_rejects_more_than_64_rows():
     say("decode layout with m=65 -> CK_EUNSUPPORTED")
-    wq, sw = ck.ck_weight_prep(torch.zeros((32, 256), dtype=torch.float32, device=DEV), 128)
+    wq, sw = prep_rows(torch.zeros((32, 256), dtype=torch.float32, device=DEV), 128)
     wd = ck.ck_weight_pack_decode(wq, sw)
     x = torch.zeros((65, 256), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(ck.CKError, match="CK_EUNSUPPORTED"):
@@ -790,7 +848,7 @@ def test_int8_linear_w8a16_within_bound(orc, m, k, n, act, g):
     say(f"int8_linear_w8a16 m={m} k={k} n={n} act={act} g={g}")
     d = W.case(m, k, n, act, seed=700 + m, zero_rows=(m // 2,) if m > 2 else ())
     wq_o, sw_o = orc.weight_prep(d["w"], g)
-    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    wq, sw = prep_rows(dev(d["w"]), g)
     x = bf16_dev(d["x"])
     y = bf16_host(ck.ck_int8_linear_w8a16(x, ck.ck_weight_pack(wq), sw, g, act))
     ref = orc.w8a16_linear(d["x"], act, wq_o, sw_o, g, return_all=True)
@@ -808,21 +866,20 @@ def test_int8_linear_w8a16_within_bound(orc, m, k, n, act, g):
 
 
 @pytest.mark.parametrize("name", ["c2", "c4"])
-def test_w8a16_full_workload_sampled_rows(orc, name):
+def test_w8a16_full_workload_all_elements(orc, name):
     wl = W.WORKLOADS[name]
     d = inputs(name)
     say(f"int8_linear_w8a16 full {name}: {wl.desc}")
     wq, sw = ck.ck_weight_prep(dev(d["w"]), wl.group)
-    y = ck.ck_int8_linear_w8a16(bf16_dev(d["x"]), ck.ck_weight_pack(wq), sw, wl.group, wl.act)
+    y = ck.ck_int8_linear_w8a16(bf16_dev(d["x"]), wq, sw, wl.group, wl.act)
     torch.cuda.synchronize()
-    rows = sample_rows(wl.m, seed=3)
     wq_o, sw_o = prepped(orc, name)
-    ref = orc.w8a16_linear(d["x"][rows], wl.act, wq_o, sw_o, wl.group, return_all=True)
-    assert_w8a16_close(orc, bf16_host(y)[rows], ref["y"], ref["x_rot"], wq_o, sw_o, wl.k,
-                       f"{name} w8a16 sampled rows")
-    y64 = orc.reference_linear_f64(d["x"][rows], wl.act, d["w"])
-    e16 = orc.rel_l2(bf16_host(y)[rows], y64)
-    e8 = orc.rel_l2(orc.int8_linear(d["x"][rows], wl.act, wq_o, sw_o, wl.group), y64)
+    ref = orc.w8a16_linear(d["x"], wl.act, wq_o, sw_o, wl.group, return_all=True)
+    y_h = bf16_host(y)
+    assert_w8a16_close(orc, y_h, ref["y"], ref["x_rot"], wq_o, sw_o, wl.k, f"{name} w8a16 all rows")
+    y64 = ref_f64(orc, name)
+    e16 = orc.rel_l2(y_h, y64)
+    e8 = orc.rel_l2(full_ref(orc, name)["y"], y64)
     say(f"{name}: relL2 vs float64  w8a16 gpu={e16:.5f}  int8 oracle={e8:.5f}")
     assert e16 < e8
 
@@ -849,8 +906,8 @@ def test_swiglu_mlp_w8a16(orc, m):
     xb = W.to_bf16_bits(rng.standard_normal((m, h)).astype(np.float32))
     w_gu = (0.02 * rng.standard_normal((2 * i, h))).astype(np.float32)
     w_dn = (0.01 * rng.standard_normal((h, i))).astype(np.float32)
-    gq, gs = ck.ck_weight_prep(dev(w_gu), g)
-    dq, ds = ck.ck_weight_prep(dev(w_dn), g)
+    gq, gs = prep_rows(dev(w_gu), g)
+    dq, ds = prep_rows(dev(w_dn), g)
     pgu, pd = ck.ck_weight_pack(gq), ck.ck_weight_pack(dq)
     x = bf16_dev(xb)
     y = ck.ck_swiglu_mlp_w8a16(x, pgu, gs, pd, ds, g)
@@ -869,24 +926,22 @@ def test_swiglu_mlp_w8a16(orc, m):
     assert e16 < e8
 
 
-def test_swiglu_mlp_w8a16_full_c5_sampled_rows(orc):
+def test_swiglu_mlp_w8a16_full_c5_all_elements(orc):
     wl = W.WORKLOADS["c5"]
     d = inputs("c5")
     say(f"swiglu_mlp_w8a16 full c5: {wl.desc}")
     g = wl.group
-    gq, gs = ck.ck_weight_prep(dev(d["w_gu"]), g)
-    dq, ds = ck.ck_weight_prep(dev(d["w_down"]), g)
-    pgu, pd = ck.ck_weight_pack(gq), ck.ck_weight_pack(dq)
+    pgu, gs = ck.ck_weight_prep(dev(d["w_gu"]), g)
+    pd, ds = ck.ck_weight_prep(dev(d["w_down"]), g)
     x = bf16_dev(d["x"])
     y = ck.ck_swiglu_mlp_w8a16(x, pgu, gs, pd, ds, g)
     y1 = ck.ck_w8a16_gemm_bf16(ck.ck_act_rotate_bf16(x, 0, g, layout="blocked"), pgu, gs, wl.m)
     torch.cuda.synchronize()
-    rows = sample_rows(wl.m, seed=4)
     (gq_o, gs_o), (dq_o, ds_o) = prepped(orc, "c5", "w_gu"), prepped(orc, "c5", "w_down")
-    _mlp_w8a16_check(orc, d["x"], rows, gq_o, gs_o, dq_o, ds_o, g, bf16_host(y), bf16_host(y1),
+    y_h = bf16_host(y)
+    _mlp_w8a16_check(orc, d["x"], np.arange(wl.m), gq_o, gs_o, dq_o, ds_o, g, y_h, bf16_host(y1),
                      "c5 w8a16")
-    y64 = orc.reference_mlp_f64(d["x"][rows], d["w_gu"], d["w_down"])
-    say(f"c5 w8a16: relL2 vs float64 {orc.rel_l2(bf16_host(y)[rows], y64):.5f}")
+    say(f"c5 w8a16: relL2 vs float64 {orc.rel_l2(y_h, ref_f64(orc, 'c5')):.5f}")
 
 
 @pytest.mark.parametrize("m", [1, 16, 64])
@@ -900,8 +955,8 @@ def test_swiglu_mlp_decode_c5_dims_bit_exact(orc, m):
     g = wl.group
     key = ("c5", "decode_weights")
     if key not in _cache:
-        gq, gs = ck.ck_weight_prep(dev(d["w_gu"]), g)
-        dq, ds = ck.ck_weight_prep(dev(d["w_down"]), g)
+        gq, gs = prep_rows(dev(d["w_gu"]), g)
+        dq, ds = prep_rows(dev(d["w_down"]), g)
         _cache[key] = (ck.ck_weight_pack_decode(gq, gs), ck.ck_weight_pack_decode(dq, ds))
     dgu, dd = _cache[key]
     xb = np.ascontiguousarray(d["x"][:m])
@@ -920,10 +975,10 @@ def test_calls_replay_bit_exact_from_a_hip_graph():
     g = 128
     rng = np.random.default_rng(17)
     h, i = 1024, 2816
-    gq, gs = ck.ck_weight_prep(dev((0.02 * rng.standard_normal((2 * i, h))).astype(np.float32)), g)
-    dq, ds = ck.ck_weight_prep(dev((0.01 * rng.standard_normal((h, i))).astype(np.float32)), g)
+    gq, gs = prep_rows(dev((0.02 * rng.standard_normal((2 * i, h))).astype(np.float32)), g)
+    dq, ds = prep_rows(dev((0.01 * rng.standard_normal((h, i))).astype(np.float32)), g)
     dgu, dd = ck.ck_weight_pack_decode(gq, gs), ck.ck_weight_pack_decode(dq, ds)
-    wl, sl = ck.ck_weight_prep(dev((0.02 * rng.standard_normal((528, 768))).astype(np.float32)), g)
+    wl, sl = prep_rows(dev((0.02 * rng.standard_normal((528, 768))).astype(np.float32)), g)
     wlb = ck.ck_weight_pack(wl)
     x1 = torch.zeros((1, h), dtype=torch.bfloat16, device=DEV)
     x2 = torch.zeros((300, 768), dtype=torch.bfloat16, device=DEV)
@@ -976,7 +1031,7 @@ def test_concurrent_calls_on_separate_streams():
     say("4 host threads x 5 ck_int8_linear calls on separate streams")
     g = 128
     rng = np.random.default_rng(23)
-    wq, sw = ck.ck_weight_prep(dev((0.02 * rng.standard_normal((1040, 1024))).astype(np.float32)), g)
+    wq, sw = prep_rows(dev((0.02 * rng.standard_normal((1040, 1024))).astype(np.float32)), g)
     wb = ck.ck_weight_pack(wq)
     xs = [bf16_dev(W.to_bf16_bits(rng.standard_normal((300 + 37 * t, 2048)).astype(np.float32)))
           for t in range(4)]
@@ -1033,7 +1088,7 @@ def test_random_shapes_bit_exact(orc, m, k, n, act, g, layout, extra):
     say(f"random m={m} k={k} n={n} act={act} g={g} layout={layout} extra={extra}")
     d = W.case(m, k, n, act, seed=m * 7 + n)
     wq_o, sw_o = orc.weight_prep(d["w"], g)
-    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    wq, sw = prep_rows(dev(d["w"]), g)
     if layout == "blocked":
         wq = ck.ck_weight_pack(wq)
     elif layout == "decode":

@@ -205,6 +205,29 @@ ck_status ck_int8_linear(const uint16_t *x, int64_t ldx, int32_t act,
                          void *stream);
 size_t ck_int8_linear_workspace_size(int64_t m, int64_t k);
 
+/* ck_int8_linear without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It allocates nothing; the activation
+ * codes and row scales go to a scratch buffer of CK_NOALLOC_SCRATCH_BYTES
+ * that the library holds in device memory, one per GPU, reserved when the
+ * library's code is loaded on that GPU and kept until the process ends.
+ *   Arguments, results and errors as ck_int8_linear, on the calling thread's
+ *   current device (`stream` must belong to it), with one more limit:
+ *   ck_int8_linear_workspace_size(m, k) > CK_NOALLOC_SCRATCH_BYTES returns
+ *   CK_EWORKSPACE and enqueues nothing (64 MiB holds m = 4096 rows at
+ *   k = 16384).  CK_EHIP if the scratch's device address cannot be queried.
+ *   Every call on one GPU uses that GPU's one buffer, and the buffer keeps
+ *   the last call's contents: calls that may overlap on one GPU (different
+ *   streams, or host threads without an order between them) race on it and
+ *   must not be issued.  Calls in one stream are ordered and safe. */
+#define CK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+size_t ck_noalloc_scratch_bytes(void);
+ck_status ck_int8_linear_noalloc(const uint16_t *x, int64_t ldx, int32_t act,
+                                 const int8_t *w_q, const float *w_scale, const float *bias,
+                                 const uint16_t *residual, int32_t layout,
+                                 int64_t m, int64_t n, int64_t k, int32_t group,
+                                 uint16_t *y, void *stream);
+
 /* The INT8 GEMM with its dequant epilogue alone (the second half of
  * ck_int8_linear), for callers that hold quantized activations.
  *   x_q, w_q int8 codes in `layout` (both), x_scale [m], w_scale [n] FP32,

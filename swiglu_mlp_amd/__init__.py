@@ -13,6 +13,9 @@ Entry points keep the C names:
 * ``ck_weight_pack_decode(w_q, w_scale)`` -> codes and scales in the decode layout
 * ``ck_act_quant(x, act, group, k=None, layout="blocked")`` -> (x_q, x_scale f32 [m, 1])
 * ``ck_int8_linear(x, w_q, w_scale, group, input_act=None, layout=None, bias=None, residual=None)``
+* ``ck_int8_linear_noalloc(x, w_q, w_scale, group, input_act=None, out=..., ...)``: the same
+  linear with no workspace (the library's own device scratch), for callers that
+  cannot allocate
 * ``ck_int8_gemm_bf16(x_q, x_scale, w_q, w_scale, layout=None, bias=None, residual=None)``
 * ``ck_swiglu_mlp(x, w_gu, s_gu, w_down, s_down, group, layout=None)`` -> y bf16
 * W8A16 (BF16 activations, INT8 weights in the blocked layout):
@@ -93,6 +96,7 @@ def bind(path: str) -> ctypes.CDLL:
         "ck_weight_pack_decode": [p, p, i64, i64, p, p],
         "ck_act_quant": [p, i64, i64, i64, i32, i32, i32, p, p, p],
         "ck_int8_linear": [p, i64, i32, p, p, p, p, i32, i64, i64, i64, i32, p, p, sz, p],
+        "ck_int8_linear_noalloc": [p, i64, i32, p, p, p, p, i32, i64, i64, i64, i32, p, p],
         "ck_int8_gemm_bf16": [p, p, p, p, p, p, i32, i64, i64, i64, p, p],
         "ck_swiglu_mlp": [p, p, p, p, p, i32, i64, i64, i64, i32, p, p, sz, p],
         "ck_int8_gemm_i32": [p, p, i32, i64, i64, i64, p, p],
@@ -116,6 +120,8 @@ def bind(path: str) -> ctypes.CDLL:
     L.ck_swiglu_mlp_w8a16_workspace_size.restype = sz
     L.ck_swiglu_mlp_workspace_size.argtypes = [i64, i64, i64]
     L.ck_swiglu_mlp_workspace_size.restype = sz
+    L.ck_noalloc_scratch_bytes.argtypes = []
+    L.ck_noalloc_scratch_bytes.restype = sz
     L.ck_blocked_rows.argtypes = [i64]
     L.ck_blocked_rows.restype = i64
     L.ck_blocked_size.argtypes = [i64, i64]
@@ -425,6 +431,34 @@ def ck_int8_linear(x, w_q, w_scale, group: int = 128, input_act=None, out=None,
     ws = _workspace(workspace, lib().ck_int8_linear_workspace_size(m, k), x.device)
     _call("ck_int8_linear", x.data_ptr(), ldx, act, w_q.data_ptr(), _ptr(w_scale), bp, rp,
           lay, m, n, k, group, y.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x))
+    return y
+
+
+def ck_int8_linear_noalloc(x, w_q, w_scale, group: int = 128, input_act=None, out=None,
+                           layout=None, bias=None, residual=None):
+    """ck_int8_linear with its codes and scales in the library's own device
+    scratch (no workspace; ck_noalloc_scratch_bytes() per GPU).  Calls that
+    overlap on one GPU race on that scratch; calls in one stream are ordered."""
+    import torch
+    _need(x, torch.bfloat16, 2, "activation")
+    lay = _weight_layout(layout, w_q)
+    n, k = _weight(w_q, w_scale, lay, "weight")
+    act = _act_code(input_act)
+    m, ldx = x.shape
+    need_ld = 2 * k if act == CK_ACT_SWIGLU else k
+    if ldx != need_ld:
+        raise ValueError(f"activation needs {need_ld} columns for in_features {k}, got {ldx}")
+    _check_group(k, group)
+    if lib().ck_int8_linear_workspace_size(m, k) > lib().ck_noalloc_scratch_bytes():
+        raise ValueError(f"m = {m}, k = {k} needs more than the {lib().ck_noalloc_scratch_bytes()} "
+                         "bytes of scratch; use ck_int8_linear with a workspace")
+    bp, rp = _extra(bias, residual, m, n, x.device)
+    if out is None:
+        raise ValueError("ck_int8_linear_noalloc allocates nothing: pass out")
+    y = _out(out, m, n, x.device, [("the activation", x), ("the weight", w_q), ("the weight scale", w_scale),
+                                   ("the bias", bias)], residual)
+    _call("ck_int8_linear_noalloc", x.data_ptr(), ldx, act, w_q.data_ptr(), _ptr(w_scale), bp, rp,
+          lay, m, n, k, group, y.data_ptr(), _stream(x))
     return y
 
 

@@ -4,6 +4,9 @@
 #include "ck.h"
 #include "ck_internal.hpp"
 
+#include <atomic>
+#include <mutex>
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -69,6 +72,38 @@ ck_status check_gemm_extent(int64_t m, int64_t n, int64_t k)
         const ck_status st_ = (expr);    \
         if (st_ != CK_OK) return st_;    \
     } while (0)
+
+// Scratch of ck_int8_linear_noalloc: the activation codes and row scales of
+// one call, in device memory the library holds itself (each GPU gets its own
+// copy when the library's code is loaded on it, kept until the process ends).
+// Host code never uses the array's name as an address: on the host it is only
+// a stand-in, and a kernel given it would fault.  The device address comes
+// from hipGetSymbolAddress, once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = CK_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoAllocScratchBytes % 256 == 0, "scratch size");
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+ck_status scratch_of_current_device(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return CK_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return CK_EUNSUPPORTED;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CK_EHIP;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return CK_OK;
+}
 
 }  // namespace
 
@@ -206,30 +241,42 @@ ck_status ck_int8_gemm_i32(const int8_t* x_q, const int8_t* w_q, int32_t layout,
     return from_hip(ck::launch_gemm_i32(x_q, w_q, m, n, k, acc, layout, (hipStream_t)stream));
 }
 
-ck_status ck_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, const int8_t* w_q,
-                         const float* w_scale, const float* bias, const uint16_t* residual,
-                         int32_t layout, int64_t m, int64_t n, int64_t k, int32_t group, uint16_t* y,
-                         void* workspace, size_t workspace_bytes, void* stream)
+// Argument checks of ck_int8_linear and its allocation-free variant (all but
+// the workspace).  CK_OK with *noop set for an empty call.
+static ck_status check_linear_args(const uint16_t* x, int64_t ldx, int32_t act, const int8_t* w_q,
+                                   const float* w_scale, const float* bias, const uint16_t* residual,
+                                   int32_t layout, int64_t m, int64_t n, int64_t k, int32_t group,
+                                   const uint16_t* y, bool* noop)
 {
+    *noop = false;
     CK_TRY(check_k(k, group));
     CK_TRY(check_act(act, ldx, k));
     CK_TRY(check_weight_layout(layout, m));
     if (m < 0 || n < 0 || n % 16 != 0) return CK_ESHAPE;
     CK_TRY(check_gemm_extent(m, n, k));
-    if (m == 0 || n == 0) return CK_OK;
+    if (m == 0 || n == 0) {
+        *noop = true;
+        return CK_OK;
+    }
     const bool dec = layout == CK_LAYOUT_DECODE;   // w_scale unused: the layout carries it
     if (!x || !w_q || (!w_scale && !dec) || !y) return CK_EINVAL;
     if (!aligned16(x) || !aligned16(w_q) || (!dec && !aligned16(w_scale)) || !aligned16(y))
         return CK_EINVAL;
-    CK_TRY(check_extra(bias, residual));
-    const size_t need = ck_int8_linear_workspace_size(m, k);
-    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
-        return CK_EWORKSPACE;
+    return check_extra(bias, residual);
+}
+
+// The linear after its checks: quantizer then GEMM, the codes and scales in
+// `workspace` (ck_int8_linear_workspace_size(m, k) bytes, 256-byte aligned).
+static ck_status run_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, const int8_t* w_q,
+                                 const float* w_scale, const float* bias, const uint16_t* residual,
+                                 int32_t layout, int64_t m, int64_t n, int64_t k, int32_t group,
+                                 uint16_t* y, void* workspace, hipStream_t st)
+{
+    const bool dec = layout == CK_LAYOUT_DECODE;
     const bool blocked = layout != CK_LAYOUT_ROWS;
     int8_t* xq = static_cast<int8_t*>(workspace);
     float* sx = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                          round_up((size_t)pad_rows(m) * (size_t)k));
-    hipStream_t st = (hipStream_t)stream;
     const int kind = act == CK_ACT_SWIGLU ? 1 : 0;
     if (blocked && ck::use_fused_decode(kind, m, k, group))   // quantizer inside the GEMM: one launch
         return from_hip(ck::launch_gemm_dec_fused(kind, x, ldx, m, k, group, w_q, w_scale, dec, n, y, st,
@@ -237,6 +284,38 @@ ck_status ck_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, const int8
     CK_TRY(from_hip(ck::launch_quant_rows(kind, x, ldx, m, k, group, xq, sx, nullptr, blocked, st)));
     return from_hip(ck::launch_gemm_bf16(xq, sx, w_q, w_scale, m, n, k, y, layout, st,
                                          ck::EpiExtra{bias, residual}));
+}
+
+ck_status ck_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, const int8_t* w_q,
+                         const float* w_scale, const float* bias, const uint16_t* residual,
+                         int32_t layout, int64_t m, int64_t n, int64_t k, int32_t group, uint16_t* y,
+                         void* workspace, size_t workspace_bytes, void* stream)
+{
+    bool noop;
+    CK_TRY(check_linear_args(x, ldx, act, w_q, w_scale, bias, residual, layout, m, n, k, group, y, &noop));
+    if (noop) return CK_OK;
+    const size_t need = ck_int8_linear_workspace_size(m, k);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
+        return CK_EWORKSPACE;
+    return run_int8_linear(x, ldx, act, w_q, w_scale, bias, residual, layout, m, n, k, group, y, workspace,
+                           (hipStream_t)stream);
+}
+
+size_t ck_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+ck_status ck_int8_linear_noalloc(const uint16_t* x, int64_t ldx, int32_t act, const int8_t* w_q,
+                                 const float* w_scale, const float* bias, const uint16_t* residual,
+                                 int32_t layout, int64_t m, int64_t n, int64_t k, int32_t group,
+                                 uint16_t* y, void* stream)
+{
+    bool noop;
+    CK_TRY(check_linear_args(x, ldx, act, w_q, w_scale, bias, residual, layout, m, n, k, group, y, &noop));
+    if (noop) return CK_OK;
+    if (ck_int8_linear_workspace_size(m, k) > kNoAllocScratchBytes) return CK_EWORKSPACE;
+    void* ws = nullptr;
+    CK_TRY(scratch_of_current_device(&ws));
+    return run_int8_linear(x, ldx, act, w_q, w_scale, bias, residual, layout, m, n, k, group, y, ws,
+                           (hipStream_t)stream);
 }
 
 // Sized for either layout: x codes, x scales, the [m, 2i] BF16 gate|up

@@ -251,3 +251,18 @@ def test_binding_layout_inference_and_overlap_on_host_tensors():
     assert ck._overlaps(buf[:32], buf[16:48])
     assert not ck._overlaps(buf[:32], buf[32:])
     assert ck._overlaps(buf, buf)
+
+
+def test_noalloc_linear_checks_before_the_gpu(L):
+    """The allocation-free linear checks its arguments, and its scratch limit,
+    before it touches the device (no GPU needed for these returns)."""
+    cap = L.ck_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    k = 16384
+    m = cap // k + 1
+    assert L.ck_int8_linear_workspace_size(m, k) > cap
+    args = (FAKE, k, 0, FAKE, FAKE, None, None, 0)
+    assert L.ck_int8_linear_noalloc(*args, m, 16, k, 128, FAKE, None) == EWS
+    assert L.ck_int8_linear_noalloc(*args, 4, 16, k, 100, FAKE, None) == EUNSUP
+    assert L.ck_int8_linear_noalloc(FAKE, k, 0, None, FAKE, None, None, 0, 4, 16, k, 128, FAKE, None) == EINVAL
+    assert L.ck_int8_linear_noalloc(*args, 0, 16, k, 128, FAKE, None) == OK

@@ -102,14 +102,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 // Taylor coefficients fl(1/n!); the seed constant minimises the seed's maximum
 // relative error (5.05%) over a binade.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float silu_f32(float gamma)
+// y = 1 / (1 + e^{-gc}) by the procedure above, for the clamped gate gc.
+__device__ __forceinline__ float silu_sigma(float gc)
 {
     constexpr float kNegLog2e = -0x1.715476p+0f;
     constexpr float kLn2Hi = 0x1.62e4p-1f;
     constexpr float kLn2Lo = 0x1.7f7d1cp-20f;
     constexpr uint32_t kRcpMagic = 0x7ef311c2u;
-    const float gl = fmaxf(gamma, -80.0f);
-    const float gc = fminf(gl, 80.0f);
     const float kf = __builtin_rintf(gc * kNegLog2e);
     float r = __builtin_fmaf(kf, -kLn2Hi, -gc);
     r = __builtin_fmaf(kf, -kLn2Lo, r);
@@ -129,7 +128,48 @@ __device__ __forceinline__ float silu_f32(float gamma)
         const float t = __builtin_fmaf(-d, y, 1.0f);
         y = __builtin_fmaf(y, t, y);
     }
-    return gl * y;
+    return y;
+}
+
+__device__ __forceinline__ float silu_f32(float gamma)
+{
+    const float gl = fmaxf(gamma, -80.0f);
+    const float gc = fminf(gl, 80.0f);
+    return gl * silu_sigma(gc);
+}
+
+// ---------------------------------------------------------------------------
+// silu of BF16 gates through a table of silu_sigma.  A gate is a BF16 value,
+// and silu_sigma depends only on gc = min(max(gamma, -80), 80): it is exactly 1
+// for every gamma >= 17 (1 + e^{-gamma} rounds to 1 and the reciprocal of 1 is
+// 1), and constant below -80.  So the BF16 patterns of magnitude up to that of
+// 80.0 (0x42A0), with either sign, cover every value, and
+//   silu(gamma) = fl(max(gamma, -80) * T[2 min(|bits|, 0x42A0) + sign])
+// is silu_f32(gamma) bit for bit (the same two clamps and the same product).
+// T has 2 * (0x42A0 + 1) FP32 entries (136,456 bytes): it fits the LDS of one
+// workgroup per CU, and a lookup costs a few integer ops instead of the ~20
+// FP32 ops of silu_sigma.
+// ---------------------------------------------------------------------------
+constexpr int kSiluTabMag = 0x42A0;                      // bits of 80.0f >> 16
+constexpr int kSiluTabEntries = 2 * (kSiluTabMag + 1);
+
+// Entry i of the table: silu_sigma of the BF16 gate with magnitude bits i / 2
+// and sign i % 2, clamped as silu_f32 clamps it.
+__device__ __forceinline__ float silu_tab_entry(int i)
+{
+    const uint32_t bits = ((uint32_t)(i & 1) << 31) | ((uint32_t)(i >> 1) << 16);
+    const float gamma = __uint_as_float(bits);
+    return silu_sigma(fminf(fmaxf(gamma, -80.0f), 80.0f));
+}
+
+// Byte offset in the table of the 16-bit gate pattern held in bits 0..15 (HI =
+// false) or 16..31 (HI = true) of w.
+template <bool HI>
+__device__ __forceinline__ uint32_t silu_tab_offset(uint32_t w)
+{
+    const uint32_t b = HI ? (w >> 16) : (w & 0xffffu);
+    const uint32_t mag = min(b & 0x7fffu, (uint32_t)kSiluTabMag);
+    return (mag << 3) | ((b >> 13) & 4u);
 }
 
 // ---------------------------------------------------------------------------
@@ -171,20 +211,38 @@ __device__ __forceinline__ float swizzle_xor(float v)
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (D << 10) | 0x1f));
 }
 
+// The same exchange for D = 1 or 2 through a DPP quad permutation (a VALU
+// move within each group of 4 lanes): no LDS traffic, one more VALU op.
+template <int D>
+__device__ __forceinline__ float dpp_xor(float v)
+{
+    static_assert(D == 1 || D == 2, "quad permutation distance");
+    constexpr int ctrl = D == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xf, 0xf, false));
+}
+
+template <int D, bool DPP>
+__device__ __forceinline__ float lane_xor(float v)
+{
+    if constexpr (DPP && D <= 2) return dpp_xor<D>(v);
+    else return swizzle_xor<D>(v);
+}
+
 // Cross-lane strides 8 .. G/2.  `lane` is the lane's position in its row team
-// (teams are aligned to the group size).
-template <int G>
+// (teams are aligned to the group size).  DPP: the two nearest exchanges
+// (strides 8 and 16) go through DPP moves instead of the LDS crossbar.
+template <int G, bool DPP = false>
 __device__ __forceinline__ void fwht_cross_lane(float (&v)[8], int lane)
 {
     if constexpr (G >= 16) {
         const float s = (lane & 1) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, swizzle_xor<1>(v[i]));
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, lane_xor<1, DPP>(v[i]));
     }
     if constexpr (G >= 32) {
         const float s = (lane & 2) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, swizzle_xor<2>(v[i]));
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, lane_xor<2, DPP>(v[i]));
     }
     if constexpr (G >= 64) {
         const float s = (lane & 4) ? -1.0f : 1.0f;

@@ -179,6 +179,17 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     static_assert((C::P - 1) * C::L + 1 + NST < 64, "vmcnt range");
     constexpr int STEPS1 = KSL * (NMF > NDS ? NMF : NDS);
     constexpr int STEPS0 = STEPS1 > AW + XW ? STEPS1 : AW + XW;
+    // The large INT8 tiles spread a stage's loads over both halves, one every
+    // few MFMAs: issued in a burst, the 32 loads of a stage fill the texture
+    // unit's command queue and stall the MFMA stream behind them.
+    constexpr bool SPREAD = !A16 && KSL == 1 && BM * BN >= 256 * 192;
+    constexpr int NL = AW + XW;                  // loads per wave per stage
+    constexpr int HL = SPREAD ? NL / 2 : NL;     // ... issued in the first half
+    // loads issued after a stage's last load and before the mid-stage wait two
+    // stages later: the next stage's (L) and the first-half loads of the stage
+    // after that, or (P - 1) L when every load goes out in the first half
+    constexpr int OUTS = SPREAD ? (C::P - 2) * C::L + HL : (C::P - 1) * C::L;
+    static_assert(OUTS + 1 + NST < 64, "vmcnt range");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -302,9 +313,10 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     //
     // vmcnt bookkeeping at the mid-stage wait of stage s: the loads of stage
     // s + 1 must have landed.  Issued after them are the loads of s + 2 ..
-    // s + P ((P - 1) L), plus, on a tile's stages kt <= P - 2, that tile's
-    // scale load (1) and, from the second tile on, the previous epilogue's NST
-    // stores.
+    // s + P ((P - 1) L; with SPREAD the loads of a stage go out over the two
+    // halves of the stage P earlier, so (P - 2) L + HL), plus, on a tile's
+    // stages kt <= P - 2, that tile's scale load (1) and, from the second tile
+    // on, the previous epilogue's NST stores.
     // A smaller wait count than the number issued after is always safe.
     // W8A16: the W fragments of a k-slice widened to BF16 (two MFMA operands
     // each); fragment i + 1 is widened in the shadow of fragment i's MFMAs.
@@ -369,29 +381,41 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
             }
         }
 #pragma unroll
-        for (int k = 0; k < STEPS0; ++k) {
+        for (int k = 0; k < (SPREAD ? STEPS1 : STEPS0); ++k) {
             if (k < KSL * NMF) mfma_step(k, fa, fb, decltype(first)::value);
             read_step(k, buf, KSL, ga, gb);
-            if (k < AW + XW) issue_one(k, lslot);
+            if constexpr (SPREAD) {
+                constexpr int SP = STEPS1 / HL;
+                if (k % SP == SP / 2 && k / SP < HL) issue_one(k / SP, lslot);
+            } else {
+                if (k < NL) issue_one(k, lslot);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
-        advance();
+        if constexpr (!SPREAD) advance();
 
         wait_lgkmcnt0();              // this wave's second-half fragments are in registers
         if (kt <= C::P - 2) {
-            if (after_epilogue) wait_vmcnt<(C::P - 1) * C::L + 1 + NST>();
-            else wait_vmcnt<(C::P - 1) * C::L + 1>();
+            if (after_epilogue) wait_vmcnt<OUTS + 1 + NST>();
+            else wait_vmcnt<OUTS + 1>();
         } else {
-            wait_vmcnt<(C::P - 1) * C::L>();
+            wait_vmcnt<OUTS>();
         }
         workgroup_barrier();          // ... for every wave; slot s % NBUF is no longer read
 
+        // slot (s + P) % NBUF was last read in stage s - 1, before that
+        // stage's barrier, so the second-half loads may go into it too
 #pragma unroll
         for (int k = 0; k < STEPS1; ++k) {
             if (k < KSL * NMF) mfma_step(k, ga, gb, false);
             read_step(k, nbuf, 0, fa, fb);
+            if constexpr (SPREAD) {
+                constexpr int SP = STEPS1 / (NL - HL);
+                if (k % SP == SP / 2 && k / SP < NL - HL) issue_one(HL + k / SP, lslot);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (SPREAD) advance();
     };
 
     auto epilogue = [&](int q, int tm, int tn) {

@@ -211,6 +211,145 @@ __global__ __launch_bounds__(BS) void quant_rows_kernel(
     if (row_ok && t == 0) s[row] = scale;
 }
 
+// The SwiGLU quantizer for large calls: persistent, one 1024-thread workgroup
+// per CU (16 waves).  silu here is a lookup in a table of silu_sigma (ck_device.hpp,
+// identical bits to silu_f32), which the workgroup builds in its LDS while the
+// loads of its first rows are in flight; it then walks its rows, a team of T
+// lanes per row as in quant_rows_kernel, with the next rows' loads issued
+// before the current rows are rotated and quantized (two register buffers).
+// The per-element work drops from ~43 to ~29 VALU instructions, which takes
+// the kernel from its VALU bound to the HBM stream.  Outputs are those of
+// quant_rows_kernel<IN_BF16_SWIGLU, ..., OUT_CODES> bit for bit.
+constexpr int kTabThreads = 1024;
+
+template <int LOG_G, int CH, bool BLOCKED>
+__global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
+    const uint16_t* __restrict__ src, int64_t ld, int m, int k, int log_t, float cg, int8_t* __restrict__ q,
+    float* __restrict__ s)
+{
+    constexpr int G = 1 << LOG_G;
+    __shared__ float tab[kSiluTabEntries];
+    __shared__ float red[2][kTabThreads / 64];
+    const int T = 1 << log_t;
+    const int t = threadIdx.x & (T - 1);
+    const int team = threadIdx.x >> log_t;
+    const int rpw = kTabThreads >> log_t;      // rows per workgroup pass
+    const int nwg = gridDim.x;
+    const int stride = nwg * rpw;
+    const int k8 = k >> 3;
+    const char* tb = reinterpret_cast<const char*>(tab);
+    // Row slots of rpw rows: in each pass the workgroups of one XCD (blockIdx
+    // % 8; the grid is a multiple of 8) take consecutive slots, so the 8 rows
+    // that share a 128-byte line of blocked codes are written from one L2
+    // (rpw divides 8 and the XCD's run of slots, nwg / 8 * rpw rows, is a
+    // multiple of 8).
+    int r0 = ((blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3)) * rpw;   // uniform in the workgroup
+    if (r0 >= m) return;                       // uniform exit (no barrier reached)
+
+    // Loads and stores go through buffer resources (the launcher keeps every
+    // extent below 2^31 bytes): a lane with nothing to load or store uses an
+    // offset past the end, which reads zeros or drops the store, so the code
+    // has no branches and the compiler can count the loads in flight exactly.
+    const __amdgpu_buffer_rsrc_t rs_x =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), (short)0, (int)((int64_t)m * ld * 2), 0x00020000);
+    const int64_t qbytes = BLOCKED ? (int64_t)((m + 255) / 256 * 256) * k : (int64_t)m * k;
+    const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(q, (short)0, (int)qbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(s, (short)0, m * 4, 0x00020000);
+    typedef int v4i_t __attribute__((ext_vector_type(4)));
+    typedef int v2i_t __attribute__((ext_vector_type(2)));
+
+    // Gate / up chunks in two register buffers: pass p reads buffer p % 2
+    // and, once its silu * up is formed, loads pass p + 2 into the same
+    // buffer, so two passes of loads are always in flight.  Chunks past k8
+    // read as zeros; rows past m read row m - 1 and store nothing.
+    v4i_t gb[2][CH], ub[2][CH];
+    auto load = [&](int h, int first) {
+        const uint32_t rb = (uint32_t)((int64_t)min(first + team, m - 1) * ld * 2);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = j * T + t;
+            const uint32_t og = c < k8 ? rb + (uint32_t)c * 16u : kBufferOutside;
+            const uint32_t ou = c < k8 ? og + (uint32_t)k * 2u : kBufferOutside;
+            gb[h][j] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, og, 0, 0);
+            ub[h][j] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, ou, 0, 0);
+        }
+    };
+    load(0, r0);
+    load(1, r0 + stride);
+    for (int i = threadIdx.x; i < kSiluTabEntries; i += kTabThreads) tab[i] = silu_tab_entry(i);
+    __syncthreads();
+
+    for (; r0 < m; r0 += 2 * stride) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int rp0 = r0 + h * stride;      // this pass's first row (uniform)
+            if (rp0 >= m) break;                  // uniform
+            float v[CH][8];
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const uint32_t wg[4] = {(uint32_t)gb[h][j][0], (uint32_t)gb[h][j][1], (uint32_t)gb[h][j][2],
+                                        (uint32_t)gb[h][j][3]};
+                const uint32_t wu[4] = {(uint32_t)ub[h][j][0], (uint32_t)ub[h][j][1], (uint32_t)ub[h][j][2],
+                                        (uint32_t)ub[h][j][3]};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float y0 = *reinterpret_cast<const float*>(tb + silu_tab_offset<false>(wg[e]));
+                    const float y1 = *reinterpret_cast<const float*>(tb + silu_tab_offset<true>(wg[e]));
+                    const float s0 = fmaxf(bf16_lo(wg[e]), -80.0f) * y0;    // silu_f32, bit for bit
+                    const float s1 = fmaxf(bf16_hi(wg[e]), -80.0f) * y1;
+                    v[j][2 * e] = s0 * bf16_lo(wu[e]);
+                    v[j][2 * e + 1] = s1 * bf16_hi(wu[e]);
+                }
+            }
+            if (rp0 + 2 * stride < m) load(h, rp0 + 2 * stride);   // uniform
+
+            float amax = 0.0f;
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                fwht_in_lane<G>(v[j]);
+                fwht_cross_lane<G, true>(v[j], t);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
+            }
+            // T >= 128 here (at most 8 rows per 1024-thread workgroup)
+            amax = fmaxf(amax, dpp_xor<1>(amax));
+            amax = fmaxf(amax, dpp_xor<2>(amax));
+            amax = fmaxf(amax, swizzle_xor<4>(amax));
+            amax = fmaxf(amax, swizzle_xor<8>(amax));
+            amax = fmaxf(amax, swizzle_xor<16>(amax));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            {
+                // the team spans T / 64 waves; red[h] alternates between passes,
+                // so a wave writing the next pass's entry never meets a wave
+                // still reading this one (every pass has this barrier)
+                const int wave = threadIdx.x >> 6;
+                if ((threadIdx.x & 63) == 0) red[h][wave] = amax;
+                __syncthreads();
+                const int w0 = (team * T) >> 6;
+                for (int w = 0; w < (T >> 6); ++w) amax = fmaxf(amax, red[h][w0 + w]);
+            }
+
+            const int row = rp0 + team;
+            const bool row_ok = row < m;
+            const float scale = (amax * cg) / 127.0f;
+            const float r = amax > 0.0f ? 127.0f / amax : 0.0f;
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const int c = j * T + t;
+                uint32_t bq[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) bq[i] = code_bits(v[j][i], r);
+                const v2i_t codes = {(int)pack4(bq[0], bq[1], bq[2], bq[3]), (int)pack4(bq[4], bq[5], bq[6], bq[7])};
+                const int64_t off = BLOCKED ? blocked_offset(row, c, k >> 5) : (int64_t)row * k + c * 8;
+                const uint32_t oq = (row_ok && c < k8) ? (uint32_t)off : kBufferOutside;
+                __builtin_amdgcn_raw_buffer_store_b64(codes, rs_q, oq, 0, 0);
+            }
+            const uint32_t os = (row_ok && t == 0) ? (uint32_t)row * 4u : kBufferOutside;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(scale), rs_s, os, 0, 0);
+        }
+    }
+}
+
 // Row-major [n, k] int8 -> blocked layout with rows padded to n_rows (zeros).
 // One thread per 16-byte unit of the output, written in order.
 __global__ __launch_bounds__(256) void pack_blocked_kernel(const int8_t* __restrict__ w, int n, int k,
@@ -374,6 +513,80 @@ bool plan(int64_t m, int64_t k, int g, bool blocked, Launch* p)
 
 }  // namespace
 
+namespace {
+
+// The table kernel pays for its table (~34K silu_sigma evaluations per CU)
+// once per launch, so it takes calls with enough elements per CU.
+// Team of the table kernel: T lanes (a power of two, 128..1024) times CH <= 3
+// chunks covering the row's k / 8 chunks with the fewest idle slots, then
+// the fewest chunks per lane (16 waves of at most 128 VGPRs each).
+bool tab_team(int64_t k, int* log_t, int* ch)
+{
+    const int64_t k8 = k / 8;
+    int64_t best = -1;
+    for (int lt = 7; lt <= 10; ++lt) {
+        for (int c = 1; c <= 3; ++c) {
+            const int64_t slots = ((int64_t)1 << lt) * c;
+            if (slots < k8) continue;
+            const int64_t score = (slots - k8) * 4 + c;
+            if (best < 0 || score < best) {
+                best = score;
+                *log_t = lt;
+                *ch = c;
+            }
+        }
+    }
+    return best >= 0;
+}
+
+bool use_swiglu_tab(int64_t m, int64_t k, int64_t ld, int g)
+{
+    const bool gs = g == 64 || g == 128 || g == 256;
+    const bool fits = m * ld * 2 < ((int64_t)1 << 31) && (m + 255) / 256 * 256 * k < ((int64_t)1 << 31);
+    return gs && fits && k >= 1024 && m >= 512 && m * k >= ((int64_t)1 << 24);
+}
+
+template <int LOG_G, bool BLOCKED>
+hipError_t launch_tab_ch(int ch, dim3 grid, hipStream_t st, const uint16_t* src, int64_t ld, int m, int k,
+                         int log_t, float cg, int8_t* q, float* s)
+{
+#define CK_TAB(C)                                                                                         \
+    case C:                                                                                               \
+        hipLaunchKernelGGL((quant_swiglu_tab_kernel<LOG_G, C, BLOCKED>), grid, dim3(kTabThreads), 0, st, src, \
+                           ld, m, k, log_t, cg, q, s);                                                    \
+        break;
+    switch (ch) {
+        CK_TAB(1) CK_TAB(2) CK_TAB(3)
+        default: return hipErrorInvalidValue;
+    }
+#undef CK_TAB
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_tab(const uint16_t* src, int64_t ld, int64_t m, int64_t k, int g, int8_t* q, float* s,
+                             bool blocked, hipStream_t st)
+{
+    int log_t = 0, ch = 0;
+    if (!tab_team(k, &log_t, &ch)) return hipErrorInvalidValue;
+    const int rpw = kTabThreads >> log_t;
+    const int64_t slots = (m + rpw - 1) / rpw;
+    int64_t wgs = num_cus();
+    if (slots < wgs) wgs = slots;
+    wgs = (wgs + 7) / 8 * 8;                   // the row-slot mapping needs a multiple of 8
+    const dim3 grid((unsigned)wgs);
+    const float cg = (float)(1.0 / sqrt((double)g));
+    const int lg = g == 64 ? 6 : g == 128 ? 7 : 8;
+#define CK_TAB_G(L)                                                                                     \
+    if (lg == L)                                                                                        \
+        return blocked ? launch_tab_ch<L, true>(ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s) \
+                       : launch_tab_ch<L, false>(ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s);
+    CK_TAB_G(6) CK_TAB_G(7) CK_TAB_G(8)
+#undef CK_TAB_G
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
 // kind: 0 = BF16, 1 = BF16 [gate | up] with SwiGLU, 2 = FP32 (weights).
 hipError_t launch_quant_rows(int kind, const void* src, int64_t ld, int64_t m, int64_t k, int g,
                              int8_t* q, float* s, float* u_out, bool blocked, hipStream_t st)
@@ -387,6 +600,8 @@ hipError_t launch_quant_rows(int kind, const void* src, int64_t ld, int64_t m, i
         if (kind == IN_BF16_SWIGLU) return launch_g<IN_BF16_SWIGLU, OUT_ROT_F32, false>(CK_ARGS, q, s, u_out);
         return hipErrorInvalidValue;
     }
+    if (kind == IN_BF16_SWIGLU && use_swiglu_tab(m, k, ld, g))
+        return launch_swiglu_tab(static_cast<const uint16_t*>(src), ld, m, k, g, q, s, blocked, st);
     switch (kind * 2 + (blocked ? 1 : 0)) {
         case 0: return launch_g<IN_BF16, OUT_CODES, false>(CK_ARGS, q, s, nullptr);
         case 1: return launch_g<IN_BF16, OUT_CODES, true>(CK_ARGS, q, s, nullptr);

@@ -379,6 +379,33 @@ def test_act_quant_blocked(orc, name):
     np.testing.assert_array_equal(host(s)[:, 0].view(np.uint32), s_o.view(np.uint32))
 
 
+@pytest.mark.parametrize("m,k,g,layout", [(2731, 6144, 64, "blocked"), (2049, 8192, 256, "rows"),
+                                        (1500, 12288, 128, "blocked"), (5600, 3072, 128, "rows"),
+                                        (4097, 4096, 128, "blocked")])
+def test_swiglu_quant_large_calls_bit_exact(orc, m, k, g, layout):
+    """Large SwiGLU quantizer calls take the persistent kernel whose silu is a
+    table lookup: codes and scales bit-exact against the oracle, ragged row
+    counts, teams of 128 and 256 lanes, 3, 4 and 6 chunks per lane."""
+    say(f"swiglu quant large m={m} k={k} g={g} {layout}")
+    rng = np.random.default_rng(m + k)
+    x = W.to_bf16_bits((rng.standard_normal((m, 2 * k)) * 2.0).astype(np.float32))
+    # every BF16 gate pattern of magnitude below 1000 appears in the first rows
+    # (the table's whole range, denormals, both clamps; larger gates would only
+    # overflow the products), and one all-zero row
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = (pats.astype(np.uint32) << 16).view(np.float32)
+    pats = pats[np.isfinite(f) & (np.abs(f) < 1000.0)]
+    flat = x[:, :k].reshape(-1)
+    flat[:pats.size] = pats
+    x[:, :k] = flat.reshape(m, k)
+    x[m // 2] = 0
+    q, sc = act_quant(bf16_dev(x), 1, g, layout=layout)
+    torch.cuda.synchronize()
+    q_o, s_o = orc.act_quant(x, 1, g)
+    np.testing.assert_array_equal(host(sc)[:, 0].view(np.uint32), s_o.view(np.uint32))
+    np.testing.assert_array_equal(from_blocked(host(q), m) if layout == "blocked" else host(q), q_o)
+
+
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
 def test_gemm_i32_blocked_bit_exact(orc, m, n, k):
     say(f"gemm_i32 blocked m={m} n={n} k={k}")

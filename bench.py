@@ -110,6 +110,10 @@ def parse():
     ap.add_argument("--decode-mlp", action="store_true",
                     help="time the c5 MLP block at M = 1..64 tokens with weights in the decode layout "
                          "(one line per M)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="measure what the chip delivers for this path's kernels: the INT8 MFMA loop on the "
+                         "workload's codes (with and without the GEMM's LDS reads) and row streams with the "
+                         "quantizers' HBM traffic, beside the quantizers themselves (one line per case)")
     ap.add_argument("--w8a16", action="store_true",
                     help="the W8A16 variant: BF16 rotated activations (no activation quantization) "
                          "times the INT8 weights on BF16 MFMA")
@@ -286,6 +290,107 @@ def decode_mlp(steps: int, warmup: int, w8a16: bool = False):
                                          "kernels": kernels}}), flush=True)
 
 
+def ceilings():
+    """What MI355X delivers for the path's kernels, measured on the c5 shapes.
+
+    The chip is power-limited: its INT8 MFMA rate depends on the operand bits,
+    so the MFMA loop (ck_probe_mfma_i8: one workgroup per CU, 16 independent
+    accumulators per wave) runs on 16 KB of the workload's own codes (weight
+    and activation, blocked), on uniform codes and on zeros, alone and with the
+    0.5 KB of LDS reads per MFMA that the 256 x 256 GEMM tile needs.  The HBM
+    side: ck_probe_stream_rows moves each quantizer's exact bytes (rows of BF16
+    in, one byte per element out) with trivial compute; it and the quantizer
+    itself are timed as single calls after a 512 MB read pass (median of 11)."""
+    import numpy as np
+    import torch
+    import swiglu_mlp_amd as ck
+    from swiglu_mlp_amd import workloads as W
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = ck.lib()
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    wl = W.WORKLOADS["c5"]
+    d = W.mlp_inputs(wl)
+    g, m, h, inter = wl.group, wl.m, wl.k, wl.n
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    x = to_dev(d["x"].view(np.int16)).view(torch.bfloat16)
+    wgu, sgu = ck.ck_weight_prep(to_dev(d["w_gu"]), g)
+    xq, sx = ck.ck_act_quant(x, None, g)
+    t1 = ck.ck_int8_gemm_bf16(xq, sx, wgu, sgu)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    codes = {"workload codes (W_gu and x, blocked)": torch.cat([wgu.reshape(-1)[:8192], xq.reshape(-1)[:8192]]),
+             "uniform codes in [-127, 127]": torch.randint(-127, 128, (16384,), dtype=torch.int8, device=dev,
+                                                           generator=gen),
+             "zero codes": torch.zeros(16384, dtype=torch.int8, device=dev)}
+    nwg = L.ck_probe_mfma_workgroups()
+    sink = torch.empty(nwg * 256, dtype=torch.int32, device=dev)
+    iters = 20000
+    ops = nwg * 4 * iters * 16 * 65536
+    for name, buf in codes.items():
+        buf = buf.contiguous()
+        for lds in (0, 1):
+            times = []
+            for rep in range(4):
+                e0, e1 = Event(), Event()
+                e0.record(stream)
+                rc = L.ck_probe_mfma_i8(buf.data_ptr(), iters, lds, sink.data_ptr(), sptr)
+                e1.record(stream)
+                if rc:
+                    raise RuntimeError(L.ck_status_str(rc).decode())
+                torch.cuda.synchronize()
+                if rep:
+                    times.append(e0.elapsed_time(e1) * 1000.0)
+            us = sorted(times)[len(times) // 2]
+            print(json.dumps({"ceiling": {"kind": "int8 MFMA loop", "operands": name,
+                                          "lds_reads": "0.5 KB per MFMA" if lds else "none",
+                                          "us": round(us, 1), "TOPS": round(ops / us / 1e6, 1),
+                                          "frac_int8_peak": round(ops / us / 1e6 / PEAK_INT8_TOPS, 4)}}),
+                  flush=True)
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def flushed(call, reps=11):
+        evs = [(Event(), Event()) for _ in range(reps)]
+        for a, b in evs:
+            flush.view(torch.int32).sum()
+            a.record(stream)
+            rc = call()
+            b.record(stream)
+            if rc:
+                raise RuntimeError(L.ck_status_str(rc).decode())
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs)[reps // 2] * 1000.0
+
+    hq = torch.empty((ck.blocked_rows(m), inter), dtype=torch.int8, device=dev)
+    sh = torch.empty((m,), dtype=torch.float32, device=dev)
+    cases = [
+        ("swiglu_quant", t1, 2 * inter * 2, inter,
+         lambda: L.ck_act_quant(t1.data_ptr(), 2 * inter, m, inter, 1, g, ck.CK_LAYOUT_BLOCKED, hq.data_ptr(),
+                                sh.data_ptr(), sptr)),
+        ("x_quant", x, h * 2, h,
+         lambda: L.ck_act_quant(x.data_ptr(), h, m, h, 0, g, ck.CK_LAYOUT_BLOCKED, xq.data_ptr(), sx.data_ptr(),
+                                sptr)),
+    ]
+    for name, src, rb, wb, quant in cases:
+        dst = torch.empty(m * wb, dtype=torch.uint8, device=dev)
+        stream_us = flushed(lambda: L.ck_probe_stream_rows(src.data_ptr(), rb, m, rb, wb, dst.data_ptr(), sptr))
+        quant_us = flushed(quant)
+        nbytes = m * rb + m * wb + 4 * m
+        print(json.dumps({"ceiling": {"kind": "HBM row stream", "traffic_of": f"c5 {name}",
+                                      "bytes": nbytes, "stream_us": round(stream_us, 2),
+                                      "stream_GBs": round(nbytes / stream_us / 1e3, 1),
+                                      "stream_frac_hbm_peak": round(nbytes / stream_us / 1e3 / PEAK_HBM_GBS, 4),
+                                      "quantizer_us": round(quant_us, 2),
+                                      "quantizer_GBs": round(nbytes / quant_us / 1e3, 1),
+                                      "quantizer_frac_of_stream": round(stream_us / quant_us, 4),
+                                      "timing": "median of single calls after a 512 MB read pass"}}), flush=True)
+
+
 def copy_calibration():
     """A plain elementwise copy of a known size: the reference that scales the
     FETCH_SIZE / WRITE_SIZE counters of the path's kernels to bytes."""
@@ -325,6 +430,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.ceilings:
+        ceilings()
         return
     if args.small_m_sweep:
         small_m_sweep(args.steps, args.warmup)

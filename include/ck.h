@@ -345,6 +345,33 @@ ck_status ck_act_rotate_f32(const uint16_t *x, int64_t ldx, int64_t m,
                             int64_t k, int32_t act, int32_t group, float *u,
                             void *stream);
 
+/* ---- measurement hooks: what the chip delivers, for the rooflines ----
+ * These compute nothing the path uses.  bench.py times them beside the path's
+ * kernels (MI355X is power-limited: its INT8 rate depends on the operand bits,
+ * and its HBM rate on the traffic pattern). */
+
+/* INT8 MFMA loop: one 256-thread workgroup per CU; each wave repeats `iters`
+ * times 16 independent v_mfma_i32_32x32x32_i8 (65,536 ops each) on operand
+ * fragments taken from `ops` (16 KB of INT8 codes, device, 16-byte aligned).
+ * lds != 0: each wave also reads 8 fragments (8 KB) from LDS per 16 MFMAs,
+ * the operand traffic of the 256 x 256 GEMM tile.  ops per call:
+ * ck_probe_mfma_workgroups() * 4 * iters * 16 * 65536.  sink: device int32
+ * [ck_probe_mfma_workgroups() * 256], never written for real operand data.
+ * Errors: CK_EINVAL on null or misaligned pointers, CK_ESHAPE on iters < 0. */
+int64_t ck_probe_mfma_workgroups(void);
+ck_status ck_probe_mfma_i8(const int8_t *ops, int64_t iters, int32_t lds, int32_t *sink,
+                           void *stream);
+
+/* Row stream with a quantizer's traffic and trivial compute: m rows; row r
+ * reads read_bytes at src + r * ld_bytes and writes write_bytes at
+ * dst + r * write_bytes.  read_bytes % 16 == 0, read_bytes <= 65536,
+ * write_bytes % 8 == 0, write_bytes / 8 <= read_bytes / 16,
+ * ld_bytes >= read_bytes, ld_bytes % 16 == 0; src 16-byte and dst 8-byte
+ * aligned.  Errors: CK_EINVAL (pointers), CK_ESHAPE (sizes),
+ * CK_EUNSUPPORTED (more than 2^31 rows). */
+ck_status ck_probe_stream_rows(const void *src, int64_t ld_bytes, int64_t m, int64_t read_bytes,
+                               int64_t write_bytes, void *dst, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -107,6 +107,8 @@ def bind(path: str) -> ctypes.CDLL:
         "ck_swiglu_mlp_w8a16": [p, p, p, p, p, i64, i64, i64, i32, p, p, sz, p],
         "ck_silu_f32": [p, i64, p, p],
         "ck_act_rotate_f32": [p, i64, i64, i64, i32, i32, p, p],
+        "ck_probe_mfma_i8": [p, i64, i32, p, p],
+        "ck_probe_stream_rows": [p, i64, i64, i64, i64, p, p],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -120,6 +122,8 @@ def bind(path: str) -> ctypes.CDLL:
     L.ck_swiglu_mlp_w8a16_workspace_size.restype = sz
     L.ck_swiglu_mlp_workspace_size.argtypes = [i64, i64, i64]
     L.ck_swiglu_mlp_workspace_size.restype = sz
+    L.ck_probe_mfma_workgroups.argtypes = []
+    L.ck_probe_mfma_workgroups.restype = i64
     L.ck_noalloc_scratch_bytes.argtypes = []
     L.ck_noalloc_scratch_bytes.restype = sz
     L.ck_blocked_rows.argtypes = [i64]

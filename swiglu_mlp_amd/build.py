@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libck_convrot.so")
 SOURCES = ["api.hip", "quant.hip", "gemm.hip", "gemm_big.hip", "gemm_blk.hip", "gemm_small.hip",
-           "gemm_fused.hip"]
+           "gemm_fused.hip", "probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

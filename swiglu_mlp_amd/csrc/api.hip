@@ -522,4 +522,28 @@ ck_status ck_act_rotate_f32(const uint16_t* x, int64_t ldx, int64_t m, int64_t k
                                           nullptr, nullptr, u, false, (hipStream_t)stream));
 }
 
+// ---- measurement hooks ----------------------------------------------------
+
+int64_t ck_probe_mfma_workgroups(void) { return ck::num_cus(); }
+
+ck_status ck_probe_mfma_i8(const int8_t* ops, int64_t iters, int32_t lds, int32_t* sink, void* stream)
+{
+    if (iters < 0 || iters > 0x7fffffff) return CK_ESHAPE;
+    if (!ops || !sink || !aligned16(ops) || ((uintptr_t)sink % 4) != 0) return CK_EINVAL;
+    if (iters == 0) return CK_OK;
+    return from_hip(ck::launch_probe_mfma(ops, iters, lds != 0, sink, (hipStream_t)stream));
+}
+
+ck_status ck_probe_stream_rows(const void* src, int64_t ld_bytes, int64_t m, int64_t read_bytes,
+                               int64_t write_bytes, void* dst, void* stream)
+{
+    if (m < 0 || read_bytes < 16 || read_bytes % 16 != 0 || read_bytes > 65536 || write_bytes < 0 ||
+        write_bytes % 8 != 0 || write_bytes / 8 > read_bytes / 16 || ld_bytes < read_bytes || ld_bytes % 16 != 0)
+        return CK_ESHAPE;
+    if (m > 0x7fffffff) return CK_EUNSUPPORTED;
+    if (m == 0) return CK_OK;
+    if (!src || !dst || !aligned16(src) || ((uintptr_t)dst % 8) != 0) return CK_EINVAL;
+    return from_hip(ck::launch_probe_stream(src, ld_bytes, m, read_bytes, write_bytes, dst, (hipStream_t)stream));
+}
+
 }  // extern "C"

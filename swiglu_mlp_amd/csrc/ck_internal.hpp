@@ -95,6 +95,13 @@ bool use_small_kernel(int64_t m, int64_t n);
 
 int num_cus();
 
+// Measurement kernels (probe.hip): the INT8 MFMA loop on one workgroup per CU
+// (optionally reading 0.5 KB of LDS per MFMA), and a row stream with a given
+// read / write byte count per row.
+hipError_t launch_probe_mfma(const void* ops, int64_t iters, bool lds, int32_t* sink, hipStream_t st);
+hipError_t launch_probe_stream(const void* src, int64_t ld_bytes, int64_t m, int64_t read_bytes, int64_t write_bytes,
+                               void* dst, hipStream_t st);
+
 // Persistent large-tile GEMM (256 x bn tiles, bn = 256 or 192), one workgroup
 // per CU; writes BF16 y (with scales) or int32 acc (out_i32).
 hipError_t launch_gemm_big(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,

@@ -1,0 +1,111 @@
+// probe.hip -- measurement kernels for the ceilings the path is measured
+// against on MI355X (gfx950): an INT8 MFMA loop and a row stream with a
+// quantizer's read/write bytes.  They compute nothing the path uses; bench.py
+// times them to state what the chip delivers under its power limit and for a
+// given traffic pattern.
+#include "ck_internal.hpp"
+
+namespace ck {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// One 256-thread workgroup per CU, 16 independent 32 x 32 x 32 INT8 MFMA
+// accumulators per wave with operands from `ops` (16 KB of codes staged in
+// LDS).  LDS: every 16 MFMAs each wave also reads 8 operand fragments (1 KB
+// each) from LDS for the next 16, the 0.5 KB per MFMA of the 256 x 256 GEMM
+// tile.  The sink store never happens for real data; it keeps the MFMAs.
+template <bool LDS>
+__global__ __launch_bounds__(256) void mfma_loop_kernel(const v4i* __restrict__ ops, int iters, int* __restrict__ sink)
+{
+    __shared__ v4i buf[1024];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    for (int i = t; i < 1024; i += 256) buf[i] = ops[i];
+    __syncthreads();
+    v4i a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = buf[i * 64 + lane];
+        b[i] = buf[(i + 4) * 64 + lane];
+    }
+    v16i acc[16];
+#pragma unroll
+    for (int f = 0; f < 16; ++f) acc[f] = v16i{};
+    for (int it = 0; it < iters; ++it) {
+        v4i na[4], nb[4];
+        if constexpr (LDS) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                na[i] = buf[(((it + wave) & 1) * 512 + i * 64 + lane) & 1023];
+                nb[i] = buf[(((it + wave) & 1) * 512 + (i + 4) * 64 + lane) & 1023];
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < 16; ++f) acc[f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[f & 3], b[f >> 2], acc[f], 0, 0, 0);
+        if constexpr (LDS) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[i] = na[i];
+                b[i] = nb[i];
+            }
+        }
+    }
+    int s = 0;
+#pragma unroll
+    for (int f = 0; f < 16; ++f)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s ^= acc[f][e];
+    if (s == 0x7fffffff) sink[blockIdx.x * 256 + t] = s;
+}
+
+// Rows of a quantizer's traffic: row r reads nr 16-byte chunks at
+// src + r * ld_bytes and writes nw 8-byte chunks at dst + r * nw * 8 (nw <=
+// nr); lane c of the row's team handles chunk c.  Persistent, one 1024-thread
+// workgroup per CU, teams of 512 lanes, the next rows' loads in flight while
+// the current ones are folded and written.
+__global__ __launch_bounds__(1024) void stream_rows_kernel(const char* __restrict__ src, int64_t ld_bytes, int m,
+                                                           int nr, int nw, uint2* __restrict__ dst)
+{
+    const int team = threadIdx.x >> 9, t = threadIdx.x & 511;
+    constexpr int MAXC = 8;                       // chunks per lane (nr <= 4096)
+    for (int row = blockIdx.x * 2 + team; row < m; row += gridDim.x * 2) {
+        const uint4* rp = reinterpret_cast<const uint4*>(src + (int64_t)row * ld_bytes);
+        uint4 v[MAXC];
+#pragma unroll
+        for (int j = 0; j < MAXC; ++j) {
+            const int c = j * 512 + t;
+            v[j] = c < nr ? rp[c] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int j = 0; j < MAXC; ++j) {
+            const int c = j * 512 + t;
+            if (c < nw) dst[(int64_t)row * nw + c] = make_uint2(v[j].x ^ v[j].z, v[j].y ^ v[j].w);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_probe_mfma(const void* ops, int64_t iters, bool lds, int32_t* sink, hipStream_t st)
+{
+    const int n = num_cus();
+    if (lds)
+        hipLaunchKernelGGL(mfma_loop_kernel<true>, dim3(n), dim3(256), 0, st, static_cast<const v4i*>(ops), (int)iters,
+                           sink);
+    else
+        hipLaunchKernelGGL(mfma_loop_kernel<false>, dim3(n), dim3(256), 0, st, static_cast<const v4i*>(ops), (int)iters,
+                           sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_stream(const void* src, int64_t ld_bytes, int64_t m, int64_t read_bytes, int64_t write_bytes,
+                               void* dst, hipStream_t st)
+{
+    const int64_t wgs = std::min<int64_t>((m + 1) / 2, num_cus());
+    hipLaunchKernelGGL(stream_rows_kernel, dim3((unsigned)wgs), dim3(1024), 0, st, static_cast<const char*>(src),
+                       ld_bytes, (int)m, (int)(read_bytes / 16), (int)(write_bytes / 8), static_cast<uint2*>(dst));
+    return hipGetLastError();
+}
+
+}  // namespace ck

@@ -266,3 +266,18 @@ def test_noalloc_linear_checks_before_the_gpu(L):
     assert L.ck_int8_linear_noalloc(*args, 4, 16, k, 100, FAKE, None) == EUNSUP
     assert L.ck_int8_linear_noalloc(FAKE, k, 0, None, FAKE, None, None, 0, 4, 16, k, 128, FAKE, None) == EINVAL
     assert L.ck_int8_linear_noalloc(*args, 0, 16, k, 128, FAKE, None) == OK
+
+
+def test_probe_hooks_check_arguments(L):
+    """The measurement hooks refuse bad sizes and pointers before launching."""
+    assert L.ck_probe_mfma_workgroups() >= 0
+    assert L.ck_probe_mfma_i8(FAKE, -1, 0, FAKE, None) == ESHAPE
+    assert L.ck_probe_mfma_i8(None, 10, 0, FAKE, None) == EINVAL
+    assert L.ck_probe_mfma_i8(FAKE + 4, 10, 0, FAKE, None) == EINVAL
+    assert L.ck_probe_mfma_i8(FAKE, 0, 1, FAKE, None) == OK
+    assert L.ck_probe_stream_rows(FAKE, 64, 4, 60, 16, FAKE, None) == ESHAPE      # read bytes % 16
+    assert L.ck_probe_stream_rows(FAKE, 64, 4, 64, 40, FAKE, None) == ESHAPE      # writes more chunks than it reads
+    assert L.ck_probe_stream_rows(FAKE, 32, 4, 64, 16, FAKE, None) == ESHAPE      # ld < read bytes
+    assert L.ck_probe_stream_rows(FAKE, 1 << 20, 4, 1 << 17, 16, FAKE, None) == ESHAPE
+    assert L.ck_probe_stream_rows(None, 64, 4, 64, 16, FAKE, None) == EINVAL
+    assert L.ck_probe_stream_rows(FAKE, 64, 0, 64, 16, FAKE, None) == OK

@@ -142,33 +142,43 @@ __device__ __forceinline__ float silu_f32(float gamma)
 // silu of BF16 gates through a table of silu_sigma.  A gate is a BF16 value,
 // and silu_sigma depends only on gc = min(max(gamma, -80), 80): it is exactly 1
 // for every gamma >= 17 (1 + e^{-gamma} rounds to 1 and the reciprocal of 1 is
-// 1), and constant below -80.  So the BF16 patterns of magnitude up to that of
-// 80.0 (0x42A0), with either sign, cover every value, and
-//   silu(gamma) = fl(max(gamma, -80) * T[2 min(|bits|, 0x42A0) + sign])
+// 1), and constant below -80.  It is also one constant for every |gamma| <=
+// 2^-25: there kf = 0 and r = -gc, the polynomial's last two steps round
+// 1 + r/2 and 1 + r to exactly 1 (|r| is at most half an ulp of 1), so e = 1,
+// d = 2, and the Newton steps see the same operands for every such gate.  So
+// the BF16 patterns of magnitude from that of 2^-30 (0x3080, well inside the
+// constant range) to that of 80.0 (0x42A0), with either sign, cover every
+// value, and
+//   silu(gamma) = fl(max(gamma, -80) * T[2 (med3(|bits|, 0x3080, 0x42A0) - 0x3080) + sign])
 // is silu_f32(gamma) bit for bit (the same two clamps and the same product).
-// T has 2 * (0x42A0 + 1) FP32 entries (136,456 bytes): it fits the LDS of one
-// workgroup per CU, and a lookup costs a few integer ops instead of the ~20
-// FP32 ops of silu_sigma.
+// T has 2 * (0x42A0 - 0x3080 + 1) FP32 entries (37,128 bytes), and a lookup
+// costs a few integer ops instead of the ~20 FP32 ops of silu_sigma.
 // ---------------------------------------------------------------------------
 constexpr int kSiluTabMag = 0x42A0;                      // bits of 80.0f >> 16
-constexpr int kSiluTabEntries = 2 * (kSiluTabMag + 1);
+constexpr int kSiluTabLow = 0x3080;                      // bits of 2^-30 >> 16
+constexpr int kSiluTabEntries = 2 * (kSiluTabMag - kSiluTabLow + 1);
 
-// Entry i of the table: silu_sigma of the BF16 gate with magnitude bits i / 2
-// and sign i % 2, clamped as silu_f32 clamps it.
+// Entry i of the table: silu_sigma of the BF16 gate with magnitude bits
+// kSiluTabLow + i / 2 and sign i % 2, clamped as silu_f32 clamps it.
 __device__ __forceinline__ float silu_tab_entry(int i)
 {
-    const uint32_t bits = ((uint32_t)(i & 1) << 31) | ((uint32_t)(i >> 1) << 16);
+    const uint32_t bits = ((uint32_t)(i & 1) << 31) | ((uint32_t)(kSiluTabLow + (i >> 1)) << 16);
     const float gamma = __uint_as_float(bits);
     return silu_sigma(fminf(fmaxf(gamma, -80.0f), 80.0f));
 }
 
-// Byte offset in the table of the 16-bit gate pattern held in bits 0..15 (HI =
-// false) or 16..31 (HI = true) of w.
+// Byte offset of the entry for the 16-bit gate pattern held in bits 0..15
+// (HI = false) or 16..31 (HI = true) of w, biased by kSiluTabBias: it is added
+// to the table's address minus kSiluTabBias, which keeps the lookup at one
+// med3 and one shift-or (the bias has zero low bits, so
+// ((mag - low) << 3) | sign = ((mag << 3) | sign) - bias).
+constexpr uint32_t kSiluTabBias = (uint32_t)kSiluTabLow << 3;
+
 template <bool HI>
 __device__ __forceinline__ uint32_t silu_tab_offset(uint32_t w)
 {
     const uint32_t b = HI ? (w >> 16) : (w & 0xffffu);
-    const uint32_t mag = min(b & 0x7fffu, (uint32_t)kSiluTabMag);
+    const uint32_t mag = min(max(b & 0x7fffu, (uint32_t)kSiluTabLow), (uint32_t)kSiluTabMag);
     return (mag << 3) | ((b >> 13) & 4u);
 }
 

@@ -17,6 +17,8 @@
 // absmax is known; codes are then written once.  A workgroup holds 256/T rows.
 // The kernel is bound by HBM and by VALU issue; every per-element step is a
 // single VALU op except the SwiGLU's exp/reciprocal.
+#include <algorithm>
+
 #include "ck_device.hpp"
 #include "ck_internal.hpp"
 
@@ -46,12 +48,34 @@ __device__ __forceinline__ int64_t blocked_bf16_offset(int row, int c, int kb)
 // row in FP32 (a diagnostic), or the normalised rotated row in BF16.
 enum OutKind { OUT_CODES = 0, OUT_ROT_F32 = 1, OUT_ROT_BF16 = 2 };
 
+// Staged blocked output: the LDS image of one 8-row group's codes.  In the
+// blocked layout the 8 rows' 16-byte pieces of one (k / 32 block, k half)
+// form one 128-byte line; the image keeps them in that order, 256 bytes per
+// k-block plus 16 bytes of padding (so the code writes of lanes 4 apart,
+// which are one k-block apart, fall in different banks).
+constexpr int kStageKbBytes = 272;
+// Largest k staged by quant_rows_kernel (its LDS image: 34,816 bytes) and by
+// the SwiGLU table kernel (121,856 bytes beside the 37,128-byte table).
+constexpr int kStageMaxK = 4096;
+constexpr int kTabStageMaxK = 14336;
+
+__device__ __forceinline__ int stage_offset(int r8, int c)
+{
+    return (c >> 2) * kStageKbBytes + ((c >> 1) & 1) * 128 + r8 * 16 + (c & 1) * 8;
+}
+
 // BS: threads per workgroup (256, or T for the wide teams of few-row calls).
-template <int KIND, int LOG_G, int CH, int OUT, bool BLOCKED, int BS>
+// STAGE (blocked codes, 8 rows per workgroup, i.e. BS = 8 T, k <= kStageMaxK):
+// the workgroup assembles its rows' codes in LDS and writes them as whole
+// 128-byte lines, 16 bytes per lane; without it each
+// lane writes 8 bytes into a line that seven other rows complete, and every
+// store instruction touches 32 lines.
+template <int KIND, int LOG_G, int CH, int OUT, bool BLOCKED, int BS, bool STAGE = false>
 __global__ __launch_bounds__(BS) void quant_rows_kernel(
     const void* __restrict__ src, int64_t ld, int m, int k, int log_t, float cg,
     int8_t* __restrict__ q, float* __restrict__ s, void* __restrict__ u_out)
 {
+    static_assert(!STAGE || (BLOCKED && OUT == OUT_CODES), "staging is for blocked codes");
     constexpr int G = 1 << LOG_G;
     const int T = 1 << log_t;
     const int t = threadIdx.x & (T - 1);
@@ -194,6 +218,7 @@ __global__ __launch_bounds__(BS) void quant_rows_kernel(
     const float scale = (amax * cg) / 127.0f;
     const float r = amax > 0.0f ? 127.0f / amax : 0.0f;
     int8_t* qp = q + (int64_t)row * k;
+    __shared__ __align__(16) char stage[STAGE ? kStageMaxK / 32 * kStageKbBytes : 16];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
         const int c = j * T + t;
@@ -201,7 +226,9 @@ __global__ __launch_bounds__(BS) void quant_rows_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) b[i] = code_bits(v[j][i], r);
         const uint2 codes = make_uint2(pack4(b[0], b[1], b[2], b[3]), pack4(b[4], b[5], b[6], b[7]));
-        if (row_ok && c < k8) {
+        if constexpr (STAGE) {
+            if (c < k8) *reinterpret_cast<uint2*>(stage + stage_offset(team, c)) = codes;
+        } else if (row_ok && c < k8) {
             if constexpr (BLOCKED)
                 *reinterpret_cast<uint2*>(q + blocked_offset(row, c, k >> 5)) = codes;
             else
@@ -209,6 +236,21 @@ __global__ __launch_bounds__(BS) void quant_rows_kernel(
         }
     }
     if (row_ok && t == 0) s[row] = scale;
+    if constexpr (STAGE) {
+        // 16-byte unit u of the group: k-block u / 16, half (u / 8) % 2, row
+        // u % 8; a wave writes 64 consecutive units, i.e. 8 whole lines
+        __syncthreads();
+        const int row0 = wg * 8;              // rows_per_wg == 8: one aligned 8-row group
+        const int kb = k >> 5;
+        int8_t* gq = q + ((int64_t)(row0 >> 5) * kb) * 1024 + ((row0 >> 3) & 3) * 128;
+        for (int u = threadIdx.x; u < kb * 16; u += BS) {
+            const int r8 = u & 7;
+            if (row0 + r8 < m) {
+                const uint4 w = *reinterpret_cast<const uint4*>(stage + (u >> 4) * kStageKbBytes + (u & 15) * 16);
+                *reinterpret_cast<uint4*>(gq + (int64_t)(u >> 4) * 1024 + ((u >> 3) & 1) * 512 + r8 * 16) = w;
+            }
+        }
+    }
 }
 
 // The SwiGLU quantizer for large calls: persistent, one 1024-thread workgroup
@@ -220,31 +262,51 @@ __global__ __launch_bounds__(BS) void quant_rows_kernel(
 // The per-element work drops from ~43 to ~29 VALU instructions, which takes
 // the kernel from its VALU bound to the HBM stream.  Outputs are those of
 // quant_rows_kernel<IN_BF16_SWIGLU, ..., OUT_CODES> bit for bit.
+//
+// STAGE (blocked codes, k <= kTabStageMaxK): rows are taken in aligned groups
+// of 8 (group i of the workgroup is blockIdx + i * gridDim), each in 8 / rpw
+// passes of rpw = 1024 / T rows; a group's codes are assembled in LDS (laid
+// out as in quant_rows_kernel) and written as whole 128-byte lines after its
+// last pass.  Otherwise pass p of the workgroup takes rpw rows of row slot
+// p * gridDim + (an XCD-grouped index of blockIdx): in each pass the
+// workgroups together read one contiguous band of rows, and the workgroups
+// of one XCD take consecutive slots, so the 8 rows that share a 128-byte line
+// of unstaged blocked codes are written from one L2 (the grid is a multiple
+// of 8, rpw divides 8, and an XCD's run of slots, gridDim / 8 * rpw rows, is
+// a multiple of 8).  Measured on c5's shape (4096 x 12288, after a MALL
+// flush): staged 56.4 us, the unstaged slot order 60.0 us, the group order
+// without staging 78.5 us; with row-major codes the slot order is 1.4 us
+// faster than the group order.
 constexpr int kTabThreads = 1024;
 
-template <int LOG_G, int CH, bool BLOCKED>
+template <int LOG_G, int CH, bool BLOCKED, bool STAGE>
 __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
     const uint16_t* __restrict__ src, int64_t ld, int m, int k, int log_t, float cg, int8_t* __restrict__ q,
     float* __restrict__ s)
 {
+    static_assert(!STAGE || BLOCKED, "staging is for blocked codes");
     constexpr int G = 1 << LOG_G;
     __shared__ float tab[kSiluTabEntries];
     __shared__ float red[2][kTabThreads / 64];
+    __shared__ __align__(16) char stage[STAGE ? kTabStageMaxK / 32 * kStageKbBytes : 16];
     const int T = 1 << log_t;
     const int t = threadIdx.x & (T - 1);
     const int team = threadIdx.x >> log_t;
-    const int rpw = kTabThreads >> log_t;      // rows per workgroup pass
+    const int rpw = kTabThreads >> log_t;      // rows per workgroup pass: 1, 2, 4 or 8
+    const int lppg = log_t - 7;                // log2 of the passes per 8-row group
     const int nwg = gridDim.x;
-    const int stride = nwg * rpw;
     const int k8 = k >> 3;
-    const char* tb = reinterpret_cast<const char*>(tab);
-    // Row slots of rpw rows: in each pass the workgroups of one XCD (blockIdx
-    // % 8; the grid is a multiple of 8) take consecutive slots, so the 8 rows
-    // that share a 128-byte line of blocked codes are written from one L2
-    // (rpw divides 8 and the XCD's run of slots, nwg / 8 * rpw rows, is a
-    // multiple of 8).
-    int r0 = ((blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3)) * rpw;   // uniform in the workgroup
-    if (r0 >= m) return;                       // uniform exit (no barrier reached)
+    const char* tb = reinterpret_cast<const char*>(tab) - kSiluTabBias;   // see silu_tab_offset
+    // STAGE: first row of the 8-row group of pass p (uniform); the pass ends
+    // the group when its index within the group is the last one
+    auto group_row = [&](int p) { return (blockIdx.x + (p >> lppg) * nwg) * 8; };
+    const int slot0 = ((blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3)) * rpw;
+    // first row of pass p (uniform), and whether pass p has rows to do
+    auto pass_row = [&](int p) {
+        return STAGE ? group_row(p) + (p & ((1 << lppg) - 1)) * rpw : slot0 + p * nwg * rpw;
+    };
+    auto pass_live = [&](int p) { return (STAGE ? group_row(p) : pass_row(p)) < m; };
+    if (!pass_live(0)) return;                 // uniform exit (no barrier reached)
 
     // Loads and stores go through buffer resources (the launcher keeps every
     // extent below 2^31 bytes): a lane with nothing to load or store uses an
@@ -274,16 +336,17 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
             ub[h][j] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, ou, 0, 0);
         }
     };
-    load(0, r0);
-    load(1, r0 + stride);
+    load(0, pass_row(0));
+    load(1, pass_row(1));
     for (int i = threadIdx.x; i < kSiluTabEntries; i += kTabThreads) tab[i] = silu_tab_entry(i);
     __syncthreads();
 
-    for (; r0 < m; r0 += 2 * stride) {
+    for (int p0 = 0;; p0 += 2) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int rp0 = r0 + h * stride;      // this pass's first row (uniform)
-            if (rp0 >= m) break;                  // uniform
+            const int pass = p0 + h;
+            if (!pass_live(pass)) return;         // uniform; every started group has been written
+            const int rp0 = pass_row(pass);       // this pass's first row (uniform)
             float v[CH][8];
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
@@ -301,7 +364,7 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
                     v[j][2 * e + 1] = s1 * bf16_hi(wu[e]);
                 }
             }
-            if (rp0 + 2 * stride < m) load(h, rp0 + 2 * stride);   // uniform
+            if (pass_live(pass + 2)) load(h, pass_row(pass + 2));   // uniform
 
             float amax = 0.0f;
 #pragma unroll
@@ -321,7 +384,9 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
             {
                 // the team spans T / 64 waves; red[h] alternates between passes,
                 // so a wave writing the next pass's entry never meets a wave
-                // still reading this one (every pass has this barrier)
+                // still reading this one (every pass has this barrier, which
+                // also orders the previous group's staged reads before this
+                // pass's staged writes)
                 const int wave = threadIdx.x >> 6;
                 if ((threadIdx.x & 63) == 0) red[h][wave] = amax;
                 __syncthreads();
@@ -340,12 +405,35 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
 #pragma unroll
                 for (int i = 0; i < 8; ++i) bq[i] = code_bits(v[j][i], r);
                 const v2i_t codes = {(int)pack4(bq[0], bq[1], bq[2], bq[3]), (int)pack4(bq[4], bq[5], bq[6], bq[7])};
-                const int64_t off = BLOCKED ? blocked_offset(row, c, k >> 5) : (int64_t)row * k + c * 8;
-                const uint32_t oq = (row_ok && c < k8) ? (uint32_t)off : kBufferOutside;
-                __builtin_amdgcn_raw_buffer_store_b64(codes, rs_q, oq, 0, 0);
+                if constexpr (STAGE) {
+                    if (c < k8) *reinterpret_cast<v2i_t*>(stage + stage_offset(row & 7, c)) = codes;
+                } else {
+                    const int64_t off = BLOCKED ? blocked_offset(row, c, k >> 5) : (int64_t)row * k + c * 8;
+                    const uint32_t oq = (row_ok && c < k8) ? (uint32_t)off : kBufferOutside;
+                    __builtin_amdgcn_raw_buffer_store_b64(codes, rs_q, oq, 0, 0);
+                }
             }
             const uint32_t os = (row_ok && t == 0) ? (uint32_t)row * 4u : kBufferOutside;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(scale), rs_s, os, 0, 0);
+
+            if constexpr (STAGE) {
+                if ((pass & ((1 << lppg) - 1)) == (1 << lppg) - 1) {   // the group's last pass (uniform)
+                    // 16-byte unit u of the group: k-block u / 16, half
+                    // (u / 8) % 2, row u % 8; a wave writes 8 whole lines
+                    __syncthreads();
+                    const int row0 = group_row(pass);
+                    const int kb = k >> 5;
+                    const uint32_t base = (uint32_t)((int64_t)(row0 >> 5) * kb * 1024) + ((row0 >> 3) & 3) * 128;
+                    for (int u = threadIdx.x; u < kb * 16; u += kTabThreads) {
+                        const int r8 = u & 7;
+                        const v4i_t w = *reinterpret_cast<const v4i_t*>(stage + (u >> 4) * kStageKbBytes + (u & 15) * 16);
+                        const uint32_t off = row0 + r8 < m
+                            ? base + (uint32_t)(u >> 4) * 1024u + (uint32_t)((u >> 3) & 1) * 512u + (uint32_t)r8 * 16u
+                            : kBufferOutside;
+                        __builtin_amdgcn_raw_buffer_store_b128(w, rs_q, off, 0, 0);
+                    }
+                }
+            }
         }
     }
 }
@@ -469,6 +557,53 @@ hipError_t launch_ch(int ch, dim3 grid, hipStream_t st, const void* src, int64_t
     return hipGetLastError();
 }
 
+// Staged blocked codes (see quant_rows_kernel): teams of 128 lanes with up to
+// 4 chunks each, 8 rows per 1024-thread workgroup, g in {64, 128, 256}.
+// Measured after a MALL flush against the unstaged kernel: faster from
+// m * k = 2^24 (4096 x 4096: 14.3 -> 11.7 us; 16384 x 3072: 36.5 -> 28.3 us),
+// slower below it (4096 x 3072: 9.3 -> 9.7 us), and slower with 8 chunks
+// per lane (4096 x 8192, whose registers allow 4 waves per SIMD).
+bool use_stage(int kind, int64_t m, int64_t k, int g)
+{
+    return (kind == IN_BF16 || kind == IN_BF16_SWIGLU) && k <= kStageMaxK && m * k >= ((int64_t)1 << 24) &&
+           (g == 64 || g == 128 || g == 256);
+}
+
+template <int KIND, int LOG_G>
+hipError_t launch_stage_ch(int ch, dim3 grid, hipStream_t st, const void* src, int64_t ld, int m, int k,
+                           float cg, int8_t* q, float* s)
+{
+#define CK_STAGE(C)                                                                                     \
+    case C:                                                                                             \
+        hipLaunchKernelGGL((quant_rows_kernel<KIND, LOG_G, C, OUT_CODES, true, 1024, true>), grid, dim3(1024), \
+                           0, st, src, ld, m, k, 7, cg, q, s, nullptr);                                 \
+        break;
+    switch (ch) {
+        CK_STAGE(1) CK_STAGE(2) CK_STAGE(3) CK_STAGE(4)
+        default: return hipErrorInvalidValue;
+    }
+#undef CK_STAGE
+    return hipGetLastError();
+}
+
+hipError_t launch_stage(int kind, const void* src, int64_t ld, int64_t m, int64_t k, int g, int8_t* q, float* s,
+                        hipStream_t st)
+{
+    const int64_t k8 = k / 8;
+    int ch = 0;
+    for (int c : {1, 2, 3, 4})
+        if (ch == 0 && 128 * c >= k8) ch = c;
+    if (ch == 0) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((m + 63) / 64 * 8));   // 8 rows per workgroup, a multiple of 8 workgroups
+    const float cg = (float)(1.0 / sqrt((double)g));
+#define CK_STAGE_G(KD, L, GV) \
+    if (kind == KD && g == GV) return launch_stage_ch<KD, L>(ch, grid, st, src, ld, (int)m, (int)k, cg, q, s);
+    CK_STAGE_G(IN_BF16, 6, 64) CK_STAGE_G(IN_BF16, 7, 128) CK_STAGE_G(IN_BF16, 8, 256)
+    CK_STAGE_G(IN_BF16_SWIGLU, 6, 64) CK_STAGE_G(IN_BF16_SWIGLU, 7, 128) CK_STAGE_G(IN_BF16_SWIGLU, 8, 256)
+#undef CK_STAGE_G
+    return hipErrorInvalidValue;
+}
+
 template <int KIND, int OUT, bool BLOCKED>
 hipError_t launch_g(int log_g, int ch, dim3 grid, hipStream_t st, const void* src, int64_t ld, int m,
                     int k, int log_t, float cg, int8_t* q, float* s, void* u)
@@ -515,7 +650,7 @@ bool plan(int64_t m, int64_t k, int g, bool blocked, Launch* p)
 
 namespace {
 
-// The table kernel pays for its table (~34K silu_sigma evaluations per CU)
+// The table kernel pays for its table (~9K silu_sigma evaluations per CU)
 // once per launch, so it takes calls with enough elements per CU.
 // Team of the table kernel: T lanes (a power of two, 128..1024) times CH <= 3
 // chunks covering the row's k / 8 chunks with the fewest idle slots, then
@@ -546,14 +681,14 @@ bool use_swiglu_tab(int64_t m, int64_t k, int64_t ld, int g)
     return gs && fits && k >= 1024 && m >= 512 && m * k >= ((int64_t)1 << 24);
 }
 
-template <int LOG_G, bool BLOCKED>
+template <int LOG_G, bool BLOCKED, bool STAGE>
 hipError_t launch_tab_ch(int ch, dim3 grid, hipStream_t st, const uint16_t* src, int64_t ld, int m, int k,
                          int log_t, float cg, int8_t* q, float* s)
 {
-#define CK_TAB(C)                                                                                         \
-    case C:                                                                                               \
-        hipLaunchKernelGGL((quant_swiglu_tab_kernel<LOG_G, C, BLOCKED>), grid, dim3(kTabThreads), 0, st, src, \
-                           ld, m, k, log_t, cg, q, s);                                                    \
+#define CK_TAB(C)                                                                                          \
+    case C:                                                                                                \
+        hipLaunchKernelGGL((quant_swiglu_tab_kernel<LOG_G, C, BLOCKED, STAGE>), grid, dim3(kTabThreads), 0, st, \
+                           src, ld, m, k, log_t, cg, q, s);                                                \
         break;
     switch (ch) {
         CK_TAB(1) CK_TAB(2) CK_TAB(3)
@@ -568,18 +703,20 @@ hipError_t launch_swiglu_tab(const uint16_t* src, int64_t ld, int64_t m, int64_t
 {
     int log_t = 0, ch = 0;
     if (!tab_team(k, &log_t, &ch)) return hipErrorInvalidValue;
+    const bool stage = blocked && k <= kTabStageMaxK;
     const int rpw = kTabThreads >> log_t;
-    const int64_t slots = (m + rpw - 1) / rpw;
-    int64_t wgs = num_cus();
-    if (slots < wgs) wgs = slots;
-    wgs = (wgs + 7) / 8 * 8;                   // the row-slot mapping needs a multiple of 8
+    // staged: aligned groups of 8 rows; otherwise row slots of rpw rows, and
+    // a multiple of 8 workgroups (see the slot order in the kernel)
+    int64_t wgs = std::min<int64_t>(stage ? (m + 7) / 8 : (m + rpw - 1) / rpw, num_cus());
+    if (!stage) wgs = (wgs + 7) / 8 * 8;
     const dim3 grid((unsigned)wgs);
     const float cg = (float)(1.0 / sqrt((double)g));
     const int lg = g == 64 ? 6 : g == 128 ? 7 : 8;
-#define CK_TAB_G(L)                                                                                     \
-    if (lg == L)                                                                                        \
-        return blocked ? launch_tab_ch<L, true>(ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s) \
-                       : launch_tab_ch<L, false>(ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s);
+#define CK_TAB_G(L)                                                                                            \
+    if (lg == L)                                                                                               \
+        return stage     ? launch_tab_ch<L, true, true>(ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s) \
+               : blocked ? launch_tab_ch<L, true, false>(ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s) \
+                         : launch_tab_ch<L, false, false>(ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s);
     CK_TAB_G(6) CK_TAB_G(7) CK_TAB_G(8)
 #undef CK_TAB_G
     return hipErrorInvalidValue;
@@ -602,6 +739,7 @@ hipError_t launch_quant_rows(int kind, const void* src, int64_t ld, int64_t m, i
     }
     if (kind == IN_BF16_SWIGLU && use_swiglu_tab(m, k, ld, g))
         return launch_swiglu_tab(static_cast<const uint16_t*>(src), ld, m, k, g, q, s, blocked, st);
+    if (blocked && use_stage(kind, m, k, g)) return launch_stage(kind, src, ld, m, k, g, q, s, st);
     switch (kind * 2 + (blocked ? 1 : 0)) {
         case 0: return launch_g<IN_BF16, OUT_CODES, false>(CK_ARGS, q, s, nullptr);
         case 1: return launch_g<IN_BF16, OUT_CODES, true>(CK_ARGS, q, s, nullptr);

@@ -379,13 +379,21 @@ def test_act_quant_blocked(orc, name):
     np.testing.assert_array_equal(host(s)[:, 0].view(np.uint32), s_o.view(np.uint32))
 
 
-@pytest.mark.parametrize("m,k,g,layout", [(2731, 6144, 64, "blocked"), (2049, 8192, 256, "rows"),
-                                        (1500, 12288, 128, "blocked"), (5600, 3072, 128, "rows"),
-                                        (4097, 4096, 128, "blocked")])
+@pytest.mark.parametrize("m,k,g,layout", [
+    (2731, 6144, 64, "blocked"), (2049, 8192, 256, "rows"), (1500, 12288, 128, "blocked"),
+    (5600, 3072, 128, "rows"), (4097, 4096, 128, "blocked"),
+    # staged blocked codes with 8, 4, 2 and 1 rows per pass (teams of 128 to
+    # 1024 lanes), the largest staged k, the unstaged blocked slot order past it
+    (5601, 3072, 64, "blocked"), (2051, 8192, 256, "blocked"), (1201, 14336, 128, "blocked"),
+    (1025, 16384, 64, "blocked"),
+    # k < 1024: the per-row kernel with staged blocked codes
+    (32769, 512, 64, "blocked")])
 def test_swiglu_quant_large_calls_bit_exact(orc, m, k, g, layout):
-    """Large SwiGLU quantizer calls take the persistent kernel whose silu is a
-    table lookup: codes and scales bit-exact against the oracle, ragged row
-    counts, teams of 128 and 256 lanes, 3, 4 and 6 chunks per lane."""
+    """Large SwiGLU quantizer calls: codes and scales bit-exact against the
+    oracle.  From k = 1024 the persistent kernel whose silu is a table lookup
+    takes them (teams of 128 to 1024 lanes, 1 to 3 chunks per lane); blocked
+    codes up to k = 14336 are staged in LDS per aligned 8-row group, ragged
+    row counts end in partial groups."""
     say(f"swiglu quant large m={m} k={k} g={g} {layout}")
     rng = np.random.default_rng(m + k)
     x = W.to_bf16_bits((rng.standard_normal((m, 2 * k)) * 2.0).astype(np.float32))
@@ -402,6 +410,34 @@ def test_swiglu_quant_large_calls_bit_exact(orc, m, k, g, layout):
     q, sc = act_quant(bf16_dev(x), 1, g, layout=layout)
     torch.cuda.synchronize()
     q_o, s_o = orc.act_quant(x, 1, g)
+    np.testing.assert_array_equal(host(sc)[:, 0].view(np.uint32), s_o.view(np.uint32))
+    np.testing.assert_array_equal(from_blocked(host(q), m) if layout == "blocked" else host(q), q_o)
+
+
+@pytest.mark.parametrize("m,k,g,layout", [
+    (2049, 1024, 64, "blocked"), (3001, 2048, 128, "rows"), (4096, 3072, 128, "blocked"),
+    (2050, 4096, 256, "rows"), (2560, 5120, 128, "blocked"), (2051, 12288, 64, "rows"),
+    (2304, 1536, 256, "blocked"),
+    # m * k >= 2^24, k <= 4096: blocked codes staged in LDS, 1 to 4 chunks per
+    # lane (k = 4032: idle chunk slots), ragged last 8-row group
+    (16385, 1024, 64, "blocked"), (8193, 2048, 128, "blocked"), (5462, 3072, 256, "blocked"),
+    (4097, 4096, 128, "blocked"), (4200, 4032, 64, "blocked")])
+def test_x_quant_large_calls_bit_exact(orc, m, k, g, layout):
+    """Large x quantizer calls: codes and scales bit-exact against the oracle,
+    ragged row counts, row-major and blocked codes (staged in LDS per 8-row
+    group from m * k = 2^24), outlier channels, an all-zero row and a row with
+    a single nonzero value."""
+    say(f"x quant large m={m} k={k} g={g} {layout}")
+    rng = np.random.default_rng(3 * m + k)
+    xf = rng.standard_normal((m, k)).astype(np.float32)
+    xf[:, rng.choice(k, size=max(1, k // 100), replace=False)] *= 20.0
+    x = W.to_bf16_bits(xf)
+    x[m // 3] = 0
+    x[m // 2] = 0
+    x[m // 2, k - 1] = W.to_bf16_bits(np.array([-3.0], dtype=np.float32))[0]
+    q, sc = act_quant(bf16_dev(x), 0, g, layout=layout)
+    torch.cuda.synchronize()
+    q_o, s_o = orc.act_quant(x, 0, g)
     np.testing.assert_array_equal(host(sc)[:, 0].view(np.uint32), s_o.view(np.uint32))
     np.testing.assert_array_equal(from_blocked(host(q), m) if layout == "blocked" else host(q), q_o)
 

@@ -357,7 +357,8 @@ ck_status ck_act_rotate_f32(const uint16_t *x, int64_t ldx, int64_t m,
  * the operand traffic of the 256 x 256 GEMM tile.  ops per call:
  * ck_probe_mfma_workgroups() * 4 * iters * 16 * 65536.  sink: device int32
  * [ck_probe_mfma_workgroups() * 256], never written for real operand data.
- * Errors: CK_EINVAL on null or misaligned pointers, CK_ESHAPE on iters < 0. */
+ * Errors: CK_EINVAL on null or misaligned pointers, CK_ESHAPE on iters < 0 or
+ * odd (the loop alternates two operand register sets). */
 int64_t ck_probe_mfma_workgroups(void);
 ck_status ck_probe_mfma_i8(const int8_t *ops, int64_t iters, int32_t lds, int32_t *sink,
                            void *stream);

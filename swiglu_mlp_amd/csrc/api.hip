@@ -528,7 +528,7 @@ int64_t ck_probe_mfma_workgroups(void) { return ck::num_cus(); }
 
 ck_status ck_probe_mfma_i8(const int8_t* ops, int64_t iters, int32_t lds, int32_t* sink, void* stream)
 {
-    if (iters < 0 || iters > 0x7fffffff) return CK_ESHAPE;
+    if (iters < 0 || iters > 0x7fffffff || (iters & 1)) return CK_ESHAPE;
     if (!ops || !sink || !aligned16(ops) || ((uintptr_t)sink % 4) != 0) return CK_EINVAL;
     if (iters == 0) return CK_OK;
     return from_hip(ck::launch_probe_mfma(ops, iters, lds != 0, sink, (hipStream_t)stream));

@@ -15,7 +15,9 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 // accumulators per wave with operands from `ops` (16 KB of codes staged in
 // LDS).  LDS: every 16 MFMAs each wave also reads 8 operand fragments (1 KB
 // each) from LDS for the next 16, the 0.5 KB per MFMA of the 256 x 256 GEMM
-// tile.  The sink store never happens for real data; it keeps the MFMAs.
+// tile, into the other of two register sets (no copies: a register an MFMA
+// still reads is never overwritten).  The sink store never happens for real
+// data; it keeps the MFMAs.
 template <bool LDS>
 __global__ __launch_bounds__(256) void mfma_loop_kernel(const v4i* __restrict__ ops, int iters, int* __restrict__ sink)
 {
@@ -23,32 +25,28 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(const v4i* __restrict__ 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     for (int i = t; i < 1024; i += 256) buf[i] = ops[i];
     __syncthreads();
-    v4i a[4], b[4];
+    v4i a[2][4], b[2][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        a[i] = buf[i * 64 + lane];
-        b[i] = buf[(i + 4) * 64 + lane];
+        a[0][i] = a[1][i] = buf[i * 64 + lane];
+        b[0][i] = b[1][i] = buf[(i + 4) * 64 + lane];
     }
     v16i acc[16];
 #pragma unroll
     for (int f = 0; f < 16; ++f) acc[f] = v16i{};
-    for (int it = 0; it < iters; ++it) {
-        v4i na[4], nb[4];
-        if constexpr (LDS) {
+    for (int it = 0; it < iters; it += 2) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                na[i] = buf[(((it + wave) & 1) * 512 + i * 64 + lane) & 1023];
-                nb[i] = buf[(((it + wave) & 1) * 512 + (i + 4) * 64 + lane) & 1023];
+        for (int h = 0; h < 2; ++h) {
+            if constexpr (LDS) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a[h ^ 1][i] = buf[(((it + h + wave) & 1) * 512 + i * 64 + lane) & 1023];
+                    b[h ^ 1][i] = buf[(((it + h + wave) & 1) * 512 + (i + 4) * 64 + lane) & 1023];
+                }
             }
-        }
 #pragma unroll
-        for (int f = 0; f < 16; ++f) acc[f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[f & 3], b[f >> 2], acc[f], 0, 0, 0);
-        if constexpr (LDS) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = na[i];
-                b[i] = nb[i];
-            }
+            for (int f = 0; f < 16; ++f)
+                acc[f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[h][f & 3], b[h][f >> 2], acc[f], 0, 0, 0);
         }
     }
     int s = 0;

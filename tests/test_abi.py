@@ -272,6 +272,7 @@ def test_probe_hooks_check_arguments(L):
     """The measurement hooks refuse bad sizes and pointers before launching."""
     assert L.ck_probe_mfma_workgroups() >= 0
     assert L.ck_probe_mfma_i8(FAKE, -1, 0, FAKE, None) == ESHAPE
+    assert L.ck_probe_mfma_i8(FAKE, 11, 0, FAKE, None) == ESHAPE
     assert L.ck_probe_mfma_i8(None, 10, 0, FAKE, None) == EINVAL
     assert L.ck_probe_mfma_i8(FAKE + 4, 10, 0, FAKE, None) == EINVAL
     assert L.ck_probe_mfma_i8(FAKE, 0, 1, FAKE, None) == OK

@@ -191,19 +191,25 @@ ck_status ck_act_quant(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,
  *   layout   layout of w_q; the activation codes use the same one (blocked
  *            for CK_LAYOUT_DECODE)
  *   y        [m, n] BF16, written (row stride n)
- *   workspace  device buffer of at least ck_int8_linear_workspace_size(m, k)
- *            bytes, 256-byte aligned; clobbered (holds x_q and x_scale).
+ *   workspace  device buffer, 256-byte aligned, clobbered, of
+ *            ck_int8_linear_workspace_size(m, k, n) bytes.  It holds x_q and
+ *            x_scale (the first R(ck_blocked_size(m, k)) + R(4 m) bytes, R:
+ *            rounded up to a multiple of 256; a smaller workspace is
+ *            CK_EWORKSPACE) and, past them, the int32 partial sums of the
+ *            split-K GEMM that CK_LAYOUT_BLOCKED uses for few output tiles
+ *            (m >= 48, k >= 8192, tiles for only part of the CUs); a
+ *            workspace without room for those runs the same shape unsplit.
  *            With CK_LAYOUT_BLOCKED or CK_LAYOUT_DECODE at m <= 2 (k <= 8192,
  *            or k <= 16384 with SwiGLU), group 64, 128 or 256, the quantizer runs
  *            inside the GEMM kernel and the workspace is left untouched (it is
- *            still required); the result is the same bit for bit. */
+ *            still required).  Every path gives the same result bit for bit. */
 ck_status ck_int8_linear(const uint16_t *x, int64_t ldx, int32_t act,
                          const int8_t *w_q, const float *w_scale, const float *bias,
                          const uint16_t *residual, int32_t layout,
                          int64_t m, int64_t n, int64_t k, int32_t group,
                          uint16_t *y, void *workspace, size_t workspace_bytes,
                          void *stream);
-size_t ck_int8_linear_workspace_size(int64_t m, int64_t k);
+size_t ck_int8_linear_workspace_size(int64_t m, int64_t k, int64_t n);
 
 /* ck_int8_linear without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
@@ -212,10 +218,12 @@ size_t ck_int8_linear_workspace_size(int64_t m, int64_t k);
  * that the library holds in device memory, one per GPU, reserved when the
  * library's code is loaded on that GPU and kept until the process ends.
  *   Arguments, results and errors as ck_int8_linear, on the calling thread's
- *   current device (`stream` must belong to it), with one more limit:
- *   ck_int8_linear_workspace_size(m, k) > CK_NOALLOC_SCRATCH_BYTES returns
- *   CK_EWORKSPACE and enqueues nothing (64 MiB holds m = 4096 rows at
- *   k = 16384).  CK_EHIP if the scratch's device address cannot be queried.
+ *   current device (`stream` must belong to it), with one more limit: when
+ *   x_q and x_scale (R(ck_blocked_size(m, k)) + R(4 m) bytes, R as there)
+ *   exceed CK_NOALLOC_SCRATCH_BYTES the call returns CK_EWORKSPACE and
+ *   enqueues nothing (64 MiB holds m = 4096 rows at k = 16384); the split-K
+ *   partials use the rest of the buffer when they fit.  CK_EHIP if the
+ *   scratch's device address cannot be queried.
  *   Every call on one GPU uses that GPU's one buffer, and the buffer keeps
  *   the last call's contents: calls that may overlap on one GPU (different
  *   streams, or host threads without an order between them) race on it and
@@ -250,11 +258,14 @@ ck_status ck_int8_gemm_bf16(const int8_t *x_q, const float *x_scale,
  *   layout layout of both weights (and of the internal activation codes;
  *          with CK_LAYOUT_DECODE, m <= 64, s_gu and s_down may be NULL)
  *   y      [m, h]  BF16, written
- *   workspace  at least ck_swiglu_mlp_workspace_size(m, h, i) bytes,
- *          256-byte aligned; clobbered (x codes/scales, the [m, 2i] BF16
- *          gate|up output, its codes/scales; with CK_LAYOUT_BLOCKED or
- *          CK_LAYOUT_DECODE at the fewest rows a stage's quantizer runs inside
- *          its GEMM, as in ck_int8_linear, and its codes are not written). */
+ *   workspace  ck_swiglu_mlp_workspace_size(m, h, i) bytes, 256-byte
+ *          aligned; clobbered (x codes/scales, the [m, 2i] BF16 gate|up
+ *          output, its codes/scales, then room for the split-K partials either
+ *          GEMM takes with CK_LAYOUT_BLOCKED as in ck_int8_linear; a workspace
+ *          short of that room, but holding the rest, runs both unsplit; with
+ *          CK_LAYOUT_BLOCKED or CK_LAYOUT_DECODE at the fewest rows a stage's
+ *          quantizer runs inside its GEMM, as in ck_int8_linear, and its codes
+ *          are not written). */
 ck_status ck_swiglu_mlp(const uint16_t *x, const int8_t *w_gu, const float *s_gu,
                         const int8_t *w_down, const float *s_down, int32_t layout,
                         int64_t m, int64_t h, int64_t i, int32_t group, uint16_t *y,

@@ -114,7 +114,7 @@ def bind(path: str) -> ctypes.CDLL:
         f = getattr(L, name)
         f.argtypes = args
         f.restype = ctypes.c_int
-    L.ck_int8_linear_workspace_size.argtypes = [i64, i64]
+    L.ck_int8_linear_workspace_size.argtypes = [i64, i64, i64]
     L.ck_int8_linear_workspace_size.restype = sz
     L.ck_int8_linear_w8a16_workspace_size.argtypes = [i64, i64]
     L.ck_int8_linear_w8a16_workspace_size.restype = sz
@@ -296,18 +296,30 @@ def _out(out, m, n, dev, inputs, residual=None):
     return out
 
 
-def _workspace(ws, nbytes, dev):
+def _workspace(ws, nbytes, dev, min_bytes=None):
     """A caller's workspace: a contiguous uint8 tensor on `dev` of at least
-    `nbytes` bytes (a new one when None)."""
+    `min_bytes` bytes (default `nbytes`; a new one of `nbytes` when None)."""
     import torch
     if ws is None:
         return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     _need(ws, torch.uint8, 1, "workspace")
     if ws.device != dev:
         raise ValueError(f"workspace must be on {dev}, got {ws.device}")
-    if ws.numel() < nbytes:
-        raise ValueError(f"workspace needs {nbytes} bytes, got {ws.numel()}")
+    need = nbytes if min_bytes is None else min_bytes
+    if ws.numel() < need:
+        raise ValueError(f"workspace needs {need} bytes, got {ws.numel()}")
     return ws
+
+
+def _round256(v: int) -> int:
+    return (v + 255) // 256 * 256
+
+
+def _linear_codes_bytes(m: int, k: int) -> int:
+    """The part of ck_int8_linear's workspace that holds the activation codes
+    and row scales (the least it accepts; the rest is room for split-K
+    partials)."""
+    return _round256(lib().ck_blocked_size(m, k)) + _round256(4 * m)
 
 
 def _act_code(input_act):
@@ -432,7 +444,7 @@ def ck_int8_linear(x, w_q, w_scale, group: int = 128, input_act=None, out=None,
     bp, rp = _extra(bias, residual, m, n, x.device)
     y = _out(out, m, n, x.device, [("the activation", x), ("the weight", w_q), ("the weight scale", w_scale),
                                    ("the bias", bias)], residual)
-    ws = _workspace(workspace, lib().ck_int8_linear_workspace_size(m, k), x.device)
+    ws = _workspace(workspace, lib().ck_int8_linear_workspace_size(m, k, n), x.device, _linear_codes_bytes(m, k))
     _call("ck_int8_linear", x.data_ptr(), ldx, act, w_q.data_ptr(), _ptr(w_scale), bp, rp,
           lay, m, n, k, group, y.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x))
     return y
@@ -453,7 +465,7 @@ def ck_int8_linear_noalloc(x, w_q, w_scale, group: int = 128, input_act=None, ou
     if ldx != need_ld:
         raise ValueError(f"activation needs {need_ld} columns for in_features {k}, got {ldx}")
     _check_group(k, group)
-    if lib().ck_int8_linear_workspace_size(m, k) > lib().ck_noalloc_scratch_bytes():
+    if _linear_codes_bytes(m, k) > lib().ck_noalloc_scratch_bytes():
         raise ValueError(f"m = {m}, k = {k} needs more than the {lib().ck_noalloc_scratch_bytes()} "
                          "bytes of scratch; use ck_int8_linear with a workspace")
     bp, rp = _extra(bias, residual, m, n, x.device)

@@ -4,6 +4,7 @@
 #include "ck.h"
 #include "ck_internal.hpp"
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -187,11 +188,19 @@ ck_status ck_act_quant(const uint16_t* x, int64_t ldx, int64_t m, int64_t k, int
                                           (hipStream_t)stream));
 }
 
-// Sized for either layout (the blocked codes are the larger).
-size_t ck_int8_linear_workspace_size(int64_t m, int64_t k)
+// The codes and scales, sized for either layout (the blocked codes are the
+// larger): what ck_int8_linear needs at least.
+static size_t linear_codes_bytes(int64_t m, int64_t k)
 {
-    if (m <= 0 || k <= 0) return 0;
     return round_up((size_t)pad_rows(m) * (size_t)k) + round_up((size_t)m * sizeof(float));
+}
+
+// The codes and scales, then room for the split-K partials of the GEMM when
+// its shape takes them on this device.
+size_t ck_int8_linear_workspace_size(int64_t m, int64_t k, int64_t n)
+{
+    if (m <= 0 || k <= 0 || n <= 0) return 0;
+    return linear_codes_bytes(m, k) + round_up(ck::gemm_splitk_bytes(m, n, k));
 }
 
 static ck_status check_gemm_args(const int8_t* x_q, const float* x_scale, const int8_t* w_q,
@@ -265,12 +274,13 @@ static ck_status check_linear_args(const uint16_t* x, int64_t ldx, int32_t act, 
     return check_extra(bias, residual);
 }
 
-// The linear after its checks: quantizer then GEMM, the codes and scales in
-// `workspace` (ck_int8_linear_workspace_size(m, k) bytes, 256-byte aligned).
+// The linear after its checks: quantizer then GEMM, the codes and scales at
+// the start of `workspace` (256-byte aligned, ws_bytes >=
+// linear_codes_bytes(m, k)); the GEMM may use the rest for split-K partials.
 static ck_status run_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, const int8_t* w_q,
                                  const float* w_scale, const float* bias, const uint16_t* residual,
                                  int32_t layout, int64_t m, int64_t n, int64_t k, int32_t group,
-                                 uint16_t* y, void* workspace, hipStream_t st)
+                                 uint16_t* y, void* workspace, size_t ws_bytes, hipStream_t st)
 {
     const bool dec = layout == CK_LAYOUT_DECODE;
     const bool blocked = layout != CK_LAYOUT_ROWS;
@@ -282,8 +292,10 @@ static ck_status run_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, co
         return from_hip(ck::launch_gemm_dec_fused(kind, x, ldx, m, k, group, w_q, w_scale, dec, n, y, st,
                                                   ck::EpiExtra{bias, residual}));
     CK_TRY(from_hip(ck::launch_quant_rows(kind, x, ldx, m, k, group, xq, sx, nullptr, blocked, st)));
+    const size_t used = linear_codes_bytes(m, k);
     return from_hip(ck::launch_gemm_bf16(xq, sx, w_q, w_scale, m, n, k, y, layout, st,
-                                         ck::EpiExtra{bias, residual}));
+                                         ck::EpiExtra{bias, residual}, static_cast<char*>(workspace) + used,
+                                         ws_bytes - used));
 }
 
 ck_status ck_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, const int8_t* w_q,
@@ -294,11 +306,10 @@ ck_status ck_int8_linear(const uint16_t* x, int64_t ldx, int32_t act, const int8
     bool noop;
     CK_TRY(check_linear_args(x, ldx, act, w_q, w_scale, bias, residual, layout, m, n, k, group, y, &noop));
     if (noop) return CK_OK;
-    const size_t need = ck_int8_linear_workspace_size(m, k);
-    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
+    if (!workspace || workspace_bytes < linear_codes_bytes(m, k) || ((uintptr_t)workspace % kAlign) != 0)
         return CK_EWORKSPACE;
     return run_int8_linear(x, ldx, act, w_q, w_scale, bias, residual, layout, m, n, k, group, y, workspace,
-                           (hipStream_t)stream);
+                           workspace_bytes, (hipStream_t)stream);
 }
 
 size_t ck_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
@@ -311,21 +322,28 @@ ck_status ck_int8_linear_noalloc(const uint16_t* x, int64_t ldx, int32_t act, co
     bool noop;
     CK_TRY(check_linear_args(x, ldx, act, w_q, w_scale, bias, residual, layout, m, n, k, group, y, &noop));
     if (noop) return CK_OK;
-    if (ck_int8_linear_workspace_size(m, k) > kNoAllocScratchBytes) return CK_EWORKSPACE;
+    if (linear_codes_bytes(m, k) > kNoAllocScratchBytes) return CK_EWORKSPACE;
     void* ws = nullptr;
     CK_TRY(scratch_of_current_device(&ws));
     return run_int8_linear(x, ldx, act, w_q, w_scale, bias, residual, layout, m, n, k, group, y, ws,
-                           (hipStream_t)stream);
+                           kNoAllocScratchBytes, (hipStream_t)stream);
 }
 
 // Sized for either layout: x codes, x scales, the [m, 2i] BF16 gate|up
-// output, its codes and scales.
+// output, its codes and scales (what ck_swiglu_mlp needs at least).
+static size_t mlp_base_bytes(int64_t m, int64_t h, int64_t i)
+{
+    const size_t M = (size_t)m, MP = (size_t)pad_rows(m), H = (size_t)h, I = (size_t)i;
+    return round_up(MP * H) + round_up(M * 4) + round_up(M * 2 * I * 2) + round_up(MP * I) + round_up(M * 4);
+}
+
+// The above, then room for the split-K partials of either GEMM (the two run
+// one after the other on the stream and share it).
 size_t ck_swiglu_mlp_workspace_size(int64_t m, int64_t h, int64_t i)
 {
     if (m <= 0 || h <= 0 || i <= 0) return 0;
-    const size_t M = (size_t)m, MP = (size_t)pad_rows(m), H = (size_t)h, I = (size_t)i;
-    return round_up(MP * H) + round_up(M * 4) + round_up(M * 2 * I * 2) + round_up(MP * I) +
-           round_up(M * 4);
+    const size_t part = std::max(ck::gemm_splitk_bytes(m, 2 * i, h), ck::gemm_splitk_bytes(m, h, i));
+    return mlp_base_bytes(m, h, i) + round_up(part);
 }
 
 ck_status ck_swiglu_mlp(const uint16_t* x, const int8_t* w_gu, const float* s_gu,
@@ -345,8 +363,8 @@ ck_status ck_swiglu_mlp(const uint16_t* x, const int8_t* w_gu, const float* s_gu
     if (!aligned16(x) || !aligned16(w_gu) || !aligned16(w_down) || !aligned16(y) ||
         (!dec && (!aligned16(s_gu) || !aligned16(s_down))))
         return CK_EINVAL;
-    const size_t need = ck_swiglu_mlp_workspace_size(m, h, i);
-    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
+    const size_t base = mlp_base_bytes(m, h, i);
+    if (!workspace || workspace_bytes < base || ((uintptr_t)workspace % kAlign) != 0)
         return CK_EWORKSPACE;
     const size_t M = (size_t)m, MP = (size_t)pad_rows(m), H = (size_t)h, I = (size_t)i;
     const bool blocked = layout != CK_LAYOUT_ROWS;
@@ -356,6 +374,8 @@ ck_status ck_swiglu_mlp(const uint16_t* x, const int8_t* w_gu, const float* s_gu
     uint16_t* y1 = reinterpret_cast<uint16_t*>(p);      p += round_up(M * 2 * I * 2);
     int8_t* hq = reinterpret_cast<int8_t*>(p);          p += round_up(MP * I);
     float* sh = reinterpret_cast<float*>(p);
+    char* part = static_cast<char*>(workspace) + base;   // split-K partials, if room
+    const size_t part_bytes = workspace_bytes - base;
     hipStream_t st = (hipStream_t)stream;
     // stage 1: packed [gate | up] projection, BF16 [m, 2i]; at the fewest rows
     // (blocked or decode weights) each stage's quantizer runs inside its GEMM
@@ -363,13 +383,15 @@ ck_status ck_swiglu_mlp(const uint16_t* x, const int8_t* w_gu, const float* s_gu
         CK_TRY(from_hip(ck::launch_gemm_dec_fused(0, x, h, m, h, group, w_gu, s_gu, dec, 2 * i, y1, st)));
     } else {
         CK_TRY(from_hip(ck::launch_quant_rows(0, x, h, m, h, group, xq, sx, nullptr, blocked, st)));
-        CK_TRY(from_hip(ck::launch_gemm_bf16(xq, sx, w_gu, s_gu, m, 2 * i, h, y1, layout, st)));
+        CK_TRY(from_hip(ck::launch_gemm_bf16(xq, sx, w_gu, s_gu, m, 2 * i, h, y1, layout, st, ck::EpiExtra{}, part,
+                                             part_bytes)));
     }
     // stage 2: silu(gate) * up inside the down projection's quantizer
     if (blocked && ck::use_fused_decode(1, m, i, group))
         return from_hip(ck::launch_gemm_dec_fused(1, y1, 2 * i, m, i, group, w_down, s_down, dec, h, y, st));
     CK_TRY(from_hip(ck::launch_quant_rows(1, y1, 2 * i, m, i, group, hq, sh, nullptr, blocked, st)));
-    return from_hip(ck::launch_gemm_bf16(hq, sh, w_down, s_down, m, h, i, y, layout, st));
+    return from_hip(ck::launch_gemm_bf16(hq, sh, w_down, s_down, m, h, i, y, layout, st, ck::EpiExtra{}, part,
+                                         part_bytes));
 }
 
 // ---- W8A16 ----------------------------------------------------------------

@@ -49,9 +49,11 @@ hipError_t launch_silu(const uint16_t* g, int64_t n, float* out, hipStream_t st)
 // the row-major or the blocked layout.
 // `ex` adds an optional bias and residual before the BF16 rounding.
 // layout: 0 rows, 1 blocked, 2 decode (W only; the activation codes are blocked).
+// ws / ws_bytes: optional room for split-K partials (blocked layout; see
+// gemm_splitk_bytes); without it every shape runs unsplit.
 hipError_t launch_gemm_bf16(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                             int64_t m, int64_t n, int64_t k, uint16_t* y, int layout, hipStream_t st,
-                            EpiExtra ex = EpiExtra{});
+                            EpiExtra ex = EpiExtra{}, void* ws = nullptr, size_t ws_bytes = 0);
 
 // acc[m, n] = x_q . w_q^T in int32.
 hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t m, int64_t n, int64_t k,
@@ -61,6 +63,17 @@ hipError_t launch_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t m, int64_
 hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                            int64_t m, int64_t n, int64_t k, void* out, bool out_i32, int num_cu,
                            hipStream_t st, EpiExtra ex = EpiExtra{});
+
+// Split-K form of the blocked BF16 GEMM for few-tile shapes (gemm_blk.hip):
+// gemm_splitk_bytes is the int32 partial buffer its plan needs on the current
+// device (0: no split for this shape).  launch_gemm_blk_splitk enqueues the
+// split GEMM and its reduction, with the partials in ws, and returns true, or
+// returns false without enqueuing anything when the shape takes no split or
+// ws is smaller than the plan needs (*err: the launch status).
+size_t gemm_splitk_bytes(int64_t m, int64_t n, int64_t k);
+bool launch_gemm_blk_splitk(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int64_t m,
+                            int64_t n, int64_t k, uint16_t* y, hipStream_t st, EpiExtra ex, void* ws,
+                            size_t ws_bytes, hipError_t* err);
 
 // W8A16 GEMM (gemm_blk.hip): x_rot BF16 in the BF16 blocked layout, W INT8
 // blocked; y = bf16(fl(acc * sw[n])) with FP32 accumulation, or (out_f32) the

@@ -301,11 +301,13 @@ hipError_t launch_gemm_t(const int8_t* xq, const float* sx, const int8_t* wq, co
 
 hipError_t launch_gemm_bf16(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                             int64_t m, int64_t n, int64_t k, uint16_t* y, int layout, hipStream_t st,
-                            EpiExtra ex)
+                            EpiExtra ex, void* ws, size_t ws_bytes)
 {
     if (m == 0 || n == 0) return hipSuccess;
     if (layout == 2) return launch_gemm_small(xq, sx, wq, sw, m, n, k, y, false, st, ex, true);
     const bool blocked = layout == 1;
+    hipError_t err = hipSuccess;
+    if (blocked && launch_gemm_blk_splitk(xq, sx, wq, sw, m, n, k, y, st, ex, ws, ws_bytes, &err)) return err;
     if (blocked && use_small_kernel(m, n)) return launch_gemm_small(xq, sx, wq, sw, m, n, k, y, false, st, ex);
     if (blocked) return launch_gemm_blk(xq, sx, wq, sw, m, n, k, y, false, num_cus(), st, ex);
     return launch_gemm_t<false>(xq, sx, wq, sw, m, n, k, y, st, ex);

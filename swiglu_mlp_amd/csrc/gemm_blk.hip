@@ -43,6 +43,10 @@
 //     tiles so the next tile's loads overlap the current tile's epilogue.  In
 //     each round the workgroups of one XCD take consecutive tiles of a grouped
 //     order, so they share operand panels in that XCD's L2.
+//   * Split K (few-tile GEMMs with a workspace): a work unit is a tile and one
+//     of ksplit equal k ranges; the int32 variant then writes unit (tile,
+//     split s) to partial s of [ksplit][M][N], and splitk_reduce_kernel adds
+//     the partials (exact in int32) and applies the same epilogue.
 #include "ck_device.hpp"
 #include "ck_internal.hpp"
 
@@ -153,7 +157,7 @@ template <int BM, int BN, bool OUT_I32, bool EXTRA, bool A16, int KSL>
 __global__ __launch_bounds__(256) void gemm_blk_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
     const float* __restrict__ sw, int M, int N, int K, int m_rows, int n_rows, void* __restrict__ out,
-    int tiles_m, int tiles_n, int group_m, EpiExtra ex)
+    int tiles_m, int tiles_n, int group_m, EpiExtra ex, int ksplit)
 {
     // The body uses AMDGPU-only types (buffer resources); the host pass only
     // needs this function's launch stub.
@@ -197,18 +201,20 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     const int G = gridDim.x;
     const int b = blockIdx.x;
     const int tiles = tiles_m * tiles_n;
-    const int KT = K / (64 * KSL);  // stages per tile
-    const int KB = K / 32;          // k-slices per 32-row block (W: 1 KB, X: XS KB each)
-    const int my_tiles = (tiles - b + G - 1) / G;
+    const int units = tiles * ksplit;   // work units: (split, tile), split-major
+    const int KU = K / ksplit;          // k of one unit
+    const int KT = KU / (64 * KSL);     // stages per unit
+    const int KB = K / 32;              // k-slices per 32-row block (W: 1 KB, X: XS KB each)
+    const int my_tiles = (units - b + G - 1) / G;
     const int total = my_tiles * KT;
     if (total == 0) return;
 
     // Within a full round the workgroups of one XCD (b % 8) take consecutive
-    // tiles; the last, partial round keeps the plain order.
+    // units; the last, partial round keeps the plain order.
     const bool xcd_order = (G & 7) == 0;
     const int b_xcd = (b & 7) * (G >> 3) + (b >> 3);
-    auto tile_of = [&](int q) {
-        const bool full = xcd_order & ((q + 1) * G <= tiles);
+    auto tile_of = [&](int q) {   // the unit index of this workgroup's q-th unit
+        const bool full = xcd_order & ((q + 1) * G <= units);
         return q * G + (full ? b_xcd : b);
     };
     // Operand buffers span the padded row counts m_rows, n_rows (multiples of
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     const v4i rs_sw = make_rsrc(sw, OUT_I32 ? 0u : (uint32_t)N * 4u);
     const v4i rs_b = make_rsrc(ex.bias, (EXTRA && ex.bias) ? (uint32_t)N * 4u : 0u);
     const __amdgpu_buffer_rsrc_t rs_o =
-        __builtin_amdgcn_make_buffer_rsrc(out, (short)0, M * N * (OUT_I32 ? 4 : 2), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(out, (short)0, M * N * (OUT_I32 ? 4 * ksplit : 2), 0x00020000);
     const uint32_t smem_addr = (uint32_t)(uintptr_t)(lds_void_t*)smem;
     const uint32_t lane16 = (uint32_t)lane * 16u;
 
@@ -229,14 +235,16 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     // stage, so the final P issues reload that stage into slots nobody reads
     // again; this keeps the number of loads per stage, and the wait counts,
     // constant).  la / lx: byte offset of the cursor tile's first W / X row
-    // block at k = 0.
+    // block at the unit's first k.
     int ls = 0, lq = 0, lkt = 0;
     uint32_t la = 0, lx = 0;
     auto set_tile = [&](int q) {
         int tm, tn;
-        tile_coords(tile_of(q), tiles_m, tiles_n, group_m, tm, tn);
-        la = (uint32_t)(tn * (BN / 32) * KB) * 1024u;
-        lx = (uint32_t)(tm * (BM / 32) * KB) * (1024u * C::XS);
+        const int u = tile_of(q);
+        const int k0 = (u / tiles) * (KU / 32);   // the unit's first k-slice
+        tile_coords(u % tiles, tiles_m, tiles_n, group_m, tm, tn);
+        la = (uint32_t)(tn * (BN / 32) * KB + k0) * 1024u;
+        lx = (uint32_t)(tm * (BM / 32) * KB + k0) * (1024u * C::XS);
     };
     auto advance = [&]() {
         if (ls + 1 < total) {
@@ -418,13 +426,15 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
         if constexpr (SPREAD) advance();
     };
 
-    auto epilogue = [&](int q, int tm, int tn) {
+    auto epilogue = [&](int q, int tm, int tn, int sp) {
         // D fragment (32 x 32): lane l holds column l % 32 (output row m)
         // and, in registers 4 qd .. 4 qd + 3, rows 8 qd + 4 (l / 32) + 0..3
         // (four consecutive output columns n).  Stores go through a buffer
         // resource: rows past M fall outside it, and masked columns are given
         // an offset past its end, so both are dropped while every lane still
-        // issues the same number of stores.
+        // issues the same number of stores.  The int32 variant writes split
+        // sp's partial (rows past M are given the past-the-end offset too: in
+        // a partial they would land in the next one).
         const int m_base = tm * BM + wm0 + lr;
         const int n_base = tn * BN + wn0 + 4 * lh;
         const char* sc = smem + C::NBUF * C::STAGE + (q & 1) * SCALES;
@@ -484,10 +494,12 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
                 asm volatile("" : "+v"(f));
                 const uint32_t row = (uint32_t)(m_base + 32 * j) * (uint32_t)N;
                 if constexpr (OUT_I32) {
+                    const uint32_t prow = row + (uint32_t)sp * (uint32_t)M * (uint32_t)N;
+                    const bool mok = m_base + 32 * j < M;
 #pragma unroll
                     for (int qd = 0; qd < 4; ++qd) {
                         const int n = n_base + 32 * i + 8 * qd;
-                        const uint32_t ob = n < N ? (row + (uint32_t)n) * 4u : kBufferOutside;
+                        const uint32_t ob = (mok && n < N) ? (prow + (uint32_t)n) * 4u : kBufferOutside;
                         const v4i d = __builtin_bit_cast(
                             v4i, (std::conditional_t<A16, float4, int4>){f[4 * qd], f[4 * qd + 1], f[4 * qd + 2],
                                                                          f[4 * qd + 3]});
@@ -549,7 +561,8 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
     int s = 0;
     for (int q = 0; q < my_tiles; ++q) {
         int tm, tn;
-        tile_coords(tile_of(q), tiles_m, tiles_n, group_m, tm, tn);
+        const int u = tile_of(q);
+        tile_coords(u % tiles, tiles_m, tiles_n, group_m, tm, tn);
         stage(s++, 0, std::true_type{}, q > 0, tm, tn, q);
         for (int kt = 1; kt < KT; ++kt) stage(s++, kt, std::false_type{}, q > 0, tm, tn, q);
         if (KT < C::P) {
@@ -557,19 +570,69 @@ __global__ __launch_bounds__(256) void gemm_blk_kernel(
             wait_vmcnt<0>();
             workgroup_barrier();
         }
-        epilogue(q, tm, tn);
+        epilogue(q, tm, tn, u / tiles);
     }
     wait_vmcnt<0>();   // no LDS load may land after the workgroup retires
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// Sum of the ksplit int32 partials [ksplit][M][N] and the dequant epilogue of
+// gemm_blk_kernel, bit for bit: y = bf16(fl(fl(f32(acc) * sx[m]) * sw[n])),
+// then + bias[n] and + residual[m, n] in that order when present.  One thread
+// per 8 consecutive outputs of a row (N % 16 == 0).
+template <bool EXTRA>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const int32_t* __restrict__ part, int ksplit, int M,
+                                                            int N, const float* __restrict__ sx,
+                                                            const float* __restrict__ sw, EpiExtra ex,
+                                                            uint16_t* __restrict__ y)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int n8 = N >> 3;
+    if (i >= (int64_t)M * n8) return;
+    const int m = (int)(i / n8), n0 = (int)(i % n8) * 8;
+    int a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int s = 0; s < ksplit; ++s) {
+        const int4* p = reinterpret_cast<const int4*>(part + ((int64_t)s * M + m) * N + n0);
+        const int4 u = p[0], v = p[1];
+        a[0] += u.x; a[1] += u.y; a[2] += u.z; a[3] += u.w;
+        a[4] += v.x; a[5] += v.y; a[6] += v.z; a[7] += v.w;
+    }
+    const float xs = sx[m];
+    const float4 w0 = *reinterpret_cast<const float4*>(sw + n0), w1 = *reinterpret_cast<const float4*>(sw + n0 + 4);
+    const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = ((float)a[e] * xs) * ws[e];
+    if constexpr (EXTRA) {
+        if (ex.bias != nullptr) {
+            const float4 b0 = *reinterpret_cast<const float4*>(ex.bias + n0);
+            const float4 b1 = *reinterpret_cast<const float4*>(ex.bias + n0 + 4);
+            const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = v[e] + bb[e];
+        }
+        if (ex.res != nullptr) {
+            const uint2* rp = reinterpret_cast<const uint2*>(ex.res + (int64_t)m * N + n0);
+            const uint2 r0 = rp[0], r1 = rp[1];
+            const uint32_t rw[4] = {r0.x, r0.y, r1.x, r1.y};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[2 * e] = v[2 * e] + bf16_lo(rw[e]);
+                v[2 * e + 1] = v[2 * e + 1] + bf16_hi(rw[e]);
+            }
+        }
+    }
+    *reinterpret_cast<uint4*>(y + (int64_t)m * N + n0) =
+        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
+
 template <int BM, int BN, bool I32, bool EXTRA, bool A16, int KSL = 1>
 hipError_t launch(const void* xq, const float* sx, const int8_t* wq, const float* sw, int M, int N,
-                  int K, void* out, int num_cu, hipStream_t st, EpiExtra ex)
+                  int K, void* out, int num_cu, hipStream_t st, EpiExtra ex, int ksplit = 1)
 {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
-    const int tiles = tiles_m * tiles_n;
+    const int tiles = tiles_m * tiles_n * ksplit;   // work units
     // LDS per workgroup: the stage ring and two scale buffers; 160 KB per CU.
     using C = Cfg<BM, BN, A16, KSL>;
     const int lds = C::NBUF * C::STAGE + (EXTRA ? 6144 : 4096);
@@ -581,7 +644,25 @@ hipError_t launch(const void* xq, const float* sx, const int8_t* wq, const float
     const int n_rows = (N + 255) / 256 * 256;
     hipLaunchKernelGGL((gemm_blk_kernel<BM, BN, I32, EXTRA, A16, KSL>), dim3(grid), dim3(256), 0, st,
                        static_cast<const int8_t*>(xq), sx, wq, sw, M, N, K, m_rows, n_rows, out, tiles_m,
-                       tiles_n, group_m, ex);
+                       tiles_n, group_m, ex, ksplit);
+    return hipGetLastError();
+}
+
+// Split-K GEMM: the int32 partials into `part` ([ksplit][M][N]), then the
+// reduction with the epilogue into y.
+template <int BM, int BN, int KSL>
+hipError_t launch_splitk(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int M, int N, int K,
+                         uint16_t* y, int num_cu, hipStream_t st, EpiExtra ex, int ksplit, int32_t* part)
+{
+    hipError_t e = launch<BM, BN, true, false, false, KSL>(xq, nullptr, wq, nullptr, M, N, K, part, num_cu, st,
+                                                           EpiExtra{}, ksplit);
+    if (e != hipSuccess) return e;
+    const int64_t threads = (int64_t)M * (N / 8);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (ex.bias || ex.res)
+        hipLaunchKernelGGL(splitk_reduce_kernel<true>, grid, dim3(256), 0, st, part, ksplit, M, N, sx, sw, ex, y);
+    else
+        hipLaunchKernelGGL(splitk_reduce_kernel<false>, grid, dim3(256), 0, st, part, ksplit, M, N, sx, sw, ex, y);
     return hipGetLastError();
 }
 
@@ -658,6 +739,58 @@ FewTiles few_tile_shape(int64_t m, int64_t n, int64_t k, int num_cu)
     return {-1, 1};
 }
 
+// Split K for few-tile GEMMs (INT8, with a workspace for the int32 partials).
+// Few tiles leave each CU streaming (BM + BN) K operand bytes for one tile; k
+// split s ways over s times the units cuts that to (BM + BN) K / s per CU at
+// the price of the partials (s M N int32, written and read once more).  The
+// estimate per plan: the unit's operand bytes at ~100 GB/s (one CU's L2 -> LDS
+// stream) plus 2 s M N 4 bytes at ~5 TB/s; a plan is taken when it beats the
+// unsplit tiles by 5%, or, for 48..128 rows at k >= 8192, instead of the
+// weight-streaming kernel.  Measured on whole ck_int8_linear calls (quantizer
+// included; single calls after a MALL flush, one box), unsplit -> split:
+// 64 x 12288 -> 4096 25.0 -> 21.5 us, 128 x 12288 -> 4096 33.2 -> 26.4 us,
+// 64 x 12288 -> 8192 38.7 -> 29.2 us, 48 x 12288 -> 3072 21.6 -> 20.2 us,
+// 256 x 12288 -> 3072 37.2 -> 32.5 us, 1024 x 12288 -> 1024 42.1 -> 38.8 us,
+// 128 x 8192 -> 4096 24.2 -> 21.4 us; at 33 rows even (21.4 / 21.6 us), and
+// at k = 4096 every split was slower.
+constexpr int64_t kSplitMinM = 48;
+constexpr int64_t kSplitMinK = 8192;
+constexpr int64_t kSplitMinKU = 1536;   // smallest k per unit
+
+struct SplitPlan {
+    int shape, ksl, s;   // shape as in choose_shape (4 = 64 x 64); s == 1: no split
+};
+
+SplitPlan splitk_plan(int64_t m, int64_t n, int64_t k, int num_cu)
+{
+    SplitPlan none{-1, 1, 1};
+    if (m < kSplitMinM || k < kSplitMinK || n % 16 != 0) return none;
+    struct Opt {
+        int shape, bm, bn, ksl;
+    };
+    static constexpr Opt opts[] = {{4, 64, 64, 4}, {1, 64, 128, 2}, {0, 128, 128, 2}};
+    auto tiles_of = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+    SplitPlan best = none;
+    double best_c = 0;
+    for (const Opt& o : opts) {
+        for (int sp = 2; sp <= 16; sp *= 2) {
+            const int64_t ku = k / sp;
+            if (k % sp || ku % (64 * o.ksl) || ku < kSplitMinKU || tiles_of(o.bm, o.bn) * sp > num_cu) continue;
+            const double c = (double)(o.bm + o.bn) * ku / 1e5 + 2.0 * sp * m * n * 4 / 5e6;
+            if (best.s == 1 || c < best_c) {
+                best = {o.shape, o.ksl, sp};
+                best_c = c;
+            }
+        }
+    }
+    if (best.s == 1) return none;
+    if (use_small_kernel(m, n)) return best;   // 33..128 rows: the split tiles beat the weight stream
+    const FewTiles few = few_tile_shape(m, n, k, num_cu);
+    if (few.shape < 0) return none;            // enough tiles for every CU
+    const int bm = few.shape == 0 ? 128 : 64, bn = few.shape == 4 ? 64 : 128;
+    return best_c < 0.95 * (double)(bm + bn) * k / 1e5 ? best : none;
+}
+
 template <bool A16>
 hipError_t launch_shape(const void* xq, const float* sx, const int8_t* wq, const float* sw, int64_t m,
                         int64_t n, int64_t k, void* out, bool out_raw, int num_cu, hipStream_t st,
@@ -696,6 +829,29 @@ hipError_t launch_gemm_blk(const int8_t* xq, const float* sx, const int8_t* wq, 
                            hipStream_t st, EpiExtra ex)
 {
     return launch_shape<false>(xq, sx, wq, sw, m, n, k, out, out_i32, num_cu, st, ex);
+}
+
+size_t gemm_splitk_bytes(int64_t m, int64_t n, int64_t k)
+{
+    const SplitPlan p = splitk_plan(m, n, k, num_cus());
+    return p.s > 1 ? (size_t)p.s * (size_t)m * (size_t)n * 4 : 0;
+}
+
+bool launch_gemm_blk_splitk(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int64_t m,
+                            int64_t n, int64_t k, uint16_t* y, hipStream_t st, EpiExtra ex, void* ws,
+                            size_t ws_bytes, hipError_t* err)
+{
+    const int num_cu = num_cus();
+    const SplitPlan p = splitk_plan(m, n, k, num_cu);
+    if (p.s == 1 || ws == nullptr || ws_bytes < (size_t)p.s * (size_t)m * (size_t)n * 4) return false;
+    int32_t* part = static_cast<int32_t*>(ws);
+    const int M = (int)m, N = (int)n, K = (int)k;
+    switch (p.shape) {
+        case 4: *err = blk::launch_splitk<64, 64, 4>(xq, sx, wq, sw, M, N, K, y, num_cu, st, ex, p.s, part); break;
+        case 1: *err = blk::launch_splitk<64, 128, 2>(xq, sx, wq, sw, M, N, K, y, num_cu, st, ex, p.s, part); break;
+        default: *err = blk::launch_splitk<128, 128, 2>(xq, sx, wq, sw, M, N, K, y, num_cu, st, ex, p.s, part); break;
+    }
+    return true;
 }
 
 hipError_t launch_gemm_w8a16(const uint16_t* x_rot, const int8_t* wq, const float* sw, int64_t m,

@@ -28,13 +28,13 @@ int main(void)
     expect("act_quant swiglu ld", ck_act_quant(FAKE, 256, 4, 256, CK_ACT_SWIGLU, 128, CK_LAYOUT_ROWS, FAKE, FAKE,
                                                NULL),
            CK_ESHAPE);
-    size_t ws = ck_int8_linear_workspace_size(4, 256);
+    size_t ws = ck_int8_linear_workspace_size(4, 256, 32);
     expect("int8_linear workspace", ck_int8_linear(FAKE, 256, CK_ACT_NONE, FAKE, FAKE, NULL, NULL,
                                                    CK_LAYOUT_BLOCKED, 4, 32, 256, 128, FAKE, FAKE, ws - 1, NULL),
            CK_EWORKSPACE);
     expect("int8_linear decode m>64", ck_int8_linear(FAKE, 256, CK_ACT_NONE, FAKE, NULL, NULL, NULL,
                                                      CK_LAYOUT_DECODE, 65, 32, 256, 128, FAKE, FAKE,
-                                                     ck_int8_linear_workspace_size(65, 256), NULL),
+                                                     ck_int8_linear_workspace_size(65, 256, 32), NULL),
            CK_EUNSUPPORTED);
     expect("swiglu_mlp shape", ck_swiglu_mlp(FAKE, FAKE, FAKE, FAKE, FAKE, CK_LAYOUT_BLOCKED, 8, 256, 500, 128,
                                              FAKE, FAKE, ck_swiglu_mlp_workspace_size(8, 256, 512), NULL),

@@ -53,8 +53,14 @@ def test_status_strings_and_version(L):
 
 
 def test_workspace_sizes(L):
-    assert L.ck_int8_linear_workspace_size(0, 256) == 0
-    assert L.ck_int8_linear_workspace_size(3, 256) == 256 * 256 + 256   # blocked codes: 256 rows
+    assert L.ck_int8_linear_workspace_size(0, 256, 32) == 0
+    assert L.ck_int8_linear_workspace_size(3, 256, 32) == 256 * 256 + 256   # blocked codes: 256 rows
+    # 64 x 4096 x 12288 takes split K on 256 CUs (four k ranges of 64 x 64 tiles): the int32 partials follow
+    # the codes and scales
+    assert L.ck_int8_linear_workspace_size(64, 12288, 4096) == 256 * 12288 + 256 + 4 * 64 * 4096 * 4
+    assert L.ck_int8_linear_workspace_size(64, 4096, 4096) == 256 * 4096 + 256            # k too small to split
+    assert L.ck_int8_linear_workspace_size(47, 12288, 4096) == 256 * 12288 + 256          # m too small
+    assert L.ck_swiglu_mlp_workspace_size(64, 3072, 12288) > L.ck_swiglu_mlp_workspace_size(64, 3072, 4096)
     assert L.ck_blocked_rows(1) == 256 and L.ck_blocked_rows(256) == 256 and L.ck_blocked_rows(257) == 512
     assert L.ck_blocked_size(300, 128) == 512 * 128 and L.ck_blocked_size(0, 128) == 0
     ws = L.ck_swiglu_mlp_workspace_size(4096, 3072, 12288)
@@ -92,7 +98,7 @@ def test_act_quant_checks(L):
 @pytest.mark.parametrize("layout", [0, 1])
 def test_int8_linear_checks(L, layout):
     f = L.ck_int8_linear
-    ws = L.ck_int8_linear_workspace_size(4, 256)
+    ws = L.ck_int8_linear_workspace_size(4, 256, 32)
     lay = layout
     assert f(FAKE, 256, 0, FAKE, FAKE, None, None, lay, 4, 40, 256, 128, FAKE, FAKE, ws, None) == ESHAPE  # n % 16
     assert f(FAKE, 256, 0, FAKE, FAKE, None, None, lay, 4, 32, 256, 128, FAKE, FAKE, ws - 1, None) == EWS
@@ -143,9 +149,9 @@ def test_decode_layout_checks(L):
     assert g(FAKE, FAKE, FAKE, None, None, None, 2, 65, 32, 256, FAKE, None) == EUNSUP
     assert g(FAKE, None, FAKE, None, None, None, 2, 4, 32, 256, FAKE, None) == EINVAL
     lin = L.ck_int8_linear
-    ws = L.ck_int8_linear_workspace_size(8, 256)
+    ws = L.ck_int8_linear_workspace_size(8, 256, 32)
     assert lin(FAKE, 256, 0, FAKE, None, None, None, 2, 65, 32, 256, 128, FAKE, FAKE,
-               L.ck_int8_linear_workspace_size(65, 256), None) == EUNSUP
+               L.ck_int8_linear_workspace_size(65, 256, 32), None) == EUNSUP
     assert lin(FAKE, 256, 0, FAKE, None, None, None, 2, 8, 32, 256, 128, FAKE, FAKE,
                ws - 1, None) == EWS
     assert lin(FAKE, 256, 0, FAKE, None, None, None, 1, 8, 32, 256, 128, FAKE, FAKE,
@@ -260,7 +266,7 @@ def test_noalloc_linear_checks_before_the_gpu(L):
     assert cap == 64 << 20
     k = 16384
     m = cap // k + 1
-    assert L.ck_int8_linear_workspace_size(m, k) > cap
+    assert L.ck_int8_linear_workspace_size(m, k, 16) > cap
     args = (FAKE, k, 0, FAKE, FAKE, None, None, 0)
     assert L.ck_int8_linear_noalloc(*args, m, 16, k, 128, FAKE, None) == EWS
     assert L.ck_int8_linear_noalloc(*args, 4, 16, k, 100, FAKE, None) == EUNSUP

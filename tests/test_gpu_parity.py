@@ -732,6 +732,61 @@ def test_swiglu_mlp_decode_bit_exact(orc, m):
     np.testing.assert_array_equal(bf16_host(y), orc.swiglu_mlp(xb, gq_o, gs_o, dq_o, ds_o, g))
 
 
+SPLITK_CASES = [  # (m, k, n, act, g, bias and residual): m >= 48, k >= 8192, few output tiles
+    (64, 12288, 4096, 0, 128, False),    # 64 x 64 tiles in four k ranges (the weight-stream regime)
+    (48, 12288, 3072, 1, 128, True),     # SwiGLU input, bias and residual
+    (128, 12288, 4096, 0, 256, False),
+    (100, 8192, 2048, 0, 64, True),      # ragged m
+    (53, 8192, 1056, 1, 128, False),     # ragged m and n (16.5 tiles of 64 columns)
+    (256, 12288, 3072, 0, 128, False),   # 128 x 128 tiles
+    (1024, 12288, 1024, 0, 128, True),
+]
+
+
+@pytest.mark.parametrize("m,k,n,act,g,extra", SPLITK_CASES)
+def test_int8_linear_splitk_bit_exact(orc, m, k, n, act, g, extra):
+    """Few-tile blocked linears split k over more CUs and add the int32 partial
+    sums in a second kernel that applies the epilogue: bit-exact against the
+    oracle, and equal to the same call with a workspace that only holds the
+    codes (which runs unsplit)."""
+    say(f"int8_linear split-k m={m} k={k} n={n} act={act} g={g} extra={extra}")
+    L = ck.lib()
+    codes = ck._linear_codes_bytes(m, k)
+    full = L.ck_int8_linear_workspace_size(m, k, n)
+    assert full > codes, "this shape is meant to take split K"
+    d = W.case(m, k, n, act, seed=3000 + m, zero_rows=(m // 2,))
+    rng = np.random.default_rng(m * 3 + n)
+    b = rng.standard_normal(n).astype(np.float32) if extra else None
+    r = orc.f32_to_bf16(rng.standard_normal((m, n)).astype(np.float32)) if extra else None
+    wq_o, sw_o = orc.weight_prep(d["w"], g)
+    wq, sw = ck.ck_weight_prep(dev(d["w"]), g)
+    x = bf16_dev(d["x"])
+    kw = dict(bias=None if b is None else dev(b), residual=None if r is None else bf16_dev(r))
+    y_split = ck.ck_int8_linear(x, wq, sw, g, act, workspace=torch.empty(full, dtype=torch.uint8, device=DEV), **kw)
+    y_plain = ck.ck_int8_linear(x, wq, sw, g, act, workspace=torch.empty(codes, dtype=torch.uint8, device=DEV), **kw)
+    want = orc.int8_linear(d["x"], act, wq_o, sw_o, g, bias=b, residual=r)
+    np.testing.assert_array_equal(bf16_host(y_split), want)
+    np.testing.assert_array_equal(bf16_host(y_plain), want)
+
+
+def test_swiglu_mlp_splitk_bit_exact(orc):
+    """The MLP block at 64 rows with c5's dimensions: the down projection (k =
+    12288, 3072 columns) takes split K; bit-exact against the oracle."""
+    m, h, i, g = 64, 3072, 12288, 128
+    say(f"swiglu_mlp split-k m={m} h={h} i={i}")
+    L = ck.lib()
+    assert L.ck_swiglu_mlp_workspace_size(m, h, i) > L.ck_swiglu_mlp_workspace_size(m, h, 4096)
+    rng = np.random.default_rng(4242)
+    xb = W.to_bf16_bits(rng.standard_normal((m, h)).astype(np.float32))
+    w_gu = (0.02 * rng.standard_normal((2 * i, h))).astype(np.float32)
+    w_dn = (0.01 * rng.standard_normal((h, i))).astype(np.float32)
+    gq, gs = ck.ck_weight_prep(dev(w_gu), g)
+    dq, ds = ck.ck_weight_prep(dev(w_dn), g)
+    y = ck.ck_swiglu_mlp(bf16_dev(xb), gq, gs, dq, ds, g)
+    (gq_o, gs_o), (dq_o, ds_o) = orc.weight_prep(w_gu, g), orc.weight_prep(w_dn, g)
+    np.testing.assert_array_equal(bf16_host(y), orc.swiglu_mlp(xb, gq_o, gs_o, dq_o, ds_o, g))
+
+
 @pytest.mark.parametrize("layout", ["decode", "blocked"])
 @pytest.mark.parametrize("m,k,act,g", [(1, 3072, 0, 128), (2, 3072, 0, 128), (2, 8192, 0, 64),
                                         (1, 12288, 1, 128), (1, 4096, 1, 256), (2, 12288, 1, 128)])
@@ -1048,7 +1103,7 @@ def test_calls_replay_bit_exact_from_a_hip_graph():
     y1 = torch.empty((1, h), dtype=torch.bfloat16, device=DEV)
     y2 = torch.empty((300, 528), dtype=torch.bfloat16, device=DEV)
     ws1 = torch.empty(ck.lib().ck_swiglu_mlp_workspace_size(1, h, i), dtype=torch.uint8, device=DEV)
-    ws2 = torch.empty(ck.lib().ck_int8_linear_workspace_size(300, 768), dtype=torch.uint8, device=DEV)
+    ws2 = torch.empty(ck.lib().ck_int8_linear_workspace_size(300, 768, 528), dtype=torch.uint8, device=DEV)
     bgu, bd = ck.ck_weight_pack(gq), ck.ck_weight_pack(dq)
     x3 = torch.zeros((2, h), dtype=torch.bfloat16, device=DEV)
     y3 = torch.empty((2, h), dtype=torch.bfloat16, device=DEV)

@@ -71,7 +71,7 @@ def test_noalloc_refuses_past_the_scratch():
     cap = L.ck_noalloc_scratch_bytes()
     k = 16384
     m = cap // k + 1                  # the codes alone exceed the scratch
-    assert L.ck_int8_linear_workspace_size(m, k) > cap
+    assert L.ck_int8_linear_workspace_size(m, k, 16) > cap
     y = torch.empty((m, 16), dtype=torch.bfloat16, device=DEV)
     x = torch.zeros((m, k), dtype=torch.bfloat16, device=DEV)
     wq = torch.zeros((16, k), dtype=torch.int8, device=DEV)

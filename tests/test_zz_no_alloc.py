@@ -66,6 +66,27 @@ def test_noalloc_equals_workspace_call_twice_then_smaller():
             assert torch.equal(y.view(torch.int16), want.view(torch.int16)), layout
 
 
+def test_noalloc_split_k_twice_then_smaller():
+    """Few-tile blocked shapes take split K, with the int32 partials in the
+    scratch past the codes: two calls in a row, the second smaller, each equal
+    to the workspace call (which splits the same way)."""
+    L = ck.lib()
+    stream = torch.cuda.current_stream(DEV).cuda_stream
+    outs = []
+    for (m, k, n, act, g), seed in (((256, 12288, 3072, 1, 128), 3), ((64, 8192, 2048, 0, 64), 4)):
+        assert L.ck_int8_linear_workspace_size(m, k, n) > ck._linear_codes_bytes(m, k), "meant to split"
+        say(f"split-k m={m} k={k} n={n} act={act} g={g}")
+        x, ldx, wq, sw = _case(m, k, n, act, g, "blocked", seed)
+        y = torch.full((m, n), -1.0, dtype=torch.bfloat16, device=DEV)
+        assert _noalloc(L, x, ldx, act, wq, sw, 1, m, n, k, g, y, stream) == 0
+        outs.append((y, x, wq, sw, act, g))
+    torch.cuda.synchronize()
+    for y, x, wq, sw, act, g in outs:
+        want = ck.ck_int8_linear(x, wq, sw, g, act, layout="blocked")
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), want.view(torch.int16))
+
+
 def test_noalloc_refuses_past_the_scratch():
     L = ck.lib()
     cap = L.ck_noalloc_scratch_bytes()

@@ -158,23 +158,30 @@ __global__ __launch_bounds__(BS) void quant_rows_kernel(
     }
 
     // ---- rotation (unnormalised blockwise FWHT) + absmax --------------------
-    float amax = 0.0f;
+    // From G = 32 the two nearest exchanges are fused into the butterfly and
+    // the values come out as sigma * u (fwht_cross_lane_signed; sigma = +-1,
+    // fixed per lane): |.| gives the absmax, and what the values are
+    // multiplied by below takes sigma.
+    float amax = 0.0f, sigma = 1.0f;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
         fwht_in_lane<G>(v[j]);
-        fwht_cross_lane<G>(v[j], t);
+        if constexpr (G >= 32) sigma = fwht_cross_lane_signed<G>(v[j], t);
+        else fwht_cross_lane<G>(v[j], t);
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
     }
 
     if constexpr (OUT == OUT_ROT_BF16) {
         // x_rot = bf16(fl(u * c_g)): the rotation with the orthonormal H
+        // (fl(sigma u * sigma c_g) = fl(u * c_g))
         char* ob = static_cast<char*>(u_out);
+        const float cs = cg * sigma;
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             const int c = j * T + t;
-            const uint4 w = make_uint4(pack_bf16x2(v[j][0] * cg, v[j][1] * cg), pack_bf16x2(v[j][2] * cg, v[j][3] * cg),
-                                       pack_bf16x2(v[j][4] * cg, v[j][5] * cg), pack_bf16x2(v[j][6] * cg, v[j][7] * cg));
+            const uint4 w = make_uint4(pack_bf16x2(v[j][0] * cs, v[j][1] * cs), pack_bf16x2(v[j][2] * cs, v[j][3] * cs),
+                                       pack_bf16x2(v[j][4] * cs, v[j][5] * cs), pack_bf16x2(v[j][6] * cs, v[j][7] * cs));
             if (row_ok && c < k8) {
                 const int64_t off = BLOCKED ? blocked_bf16_offset(row, c, k >> 5) : ((int64_t)row * k + c * 8) * 2;
                 *reinterpret_cast<uint4*>(ob + off) = w;
@@ -188,8 +195,10 @@ __global__ __launch_bounds__(BS) void quant_rows_kernel(
         for (int j = 0; j < CH; ++j) {
             const int c = j * T + t;
             if (row_ok && c < k8) {
-                *reinterpret_cast<float4*>(up + c * 8) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
-                *reinterpret_cast<float4*>(up + c * 8 + 4) = make_float4(v[j][4], v[j][5], v[j][6], v[j][7]);
+                *reinterpret_cast<float4*>(up + c * 8) =
+                    make_float4(v[j][0] * sigma, v[j][1] * sigma, v[j][2] * sigma, v[j][3] * sigma);
+                *reinterpret_cast<float4*>(up + c * 8 + 4) =
+                    make_float4(v[j][4] * sigma, v[j][5] * sigma, v[j][6] * sigma, v[j][7] * sigma);
             }
         }
         return;
@@ -216,7 +225,7 @@ __global__ __launch_bounds__(BS) void quant_rows_kernel(
     // s = fl(fl(A * c_g) / 127); r = fl(127 / A), or 0 for an all-zero row
     // (every code is then round(u * 0) = 0 and the scale is 0).
     const float scale = (amax * cg) / 127.0f;
-    const float r = amax > 0.0f ? 127.0f / amax : 0.0f;
+    const float r = (amax > 0.0f ? 127.0f / amax : 0.0f) * sigma;
     int8_t* qp = q + (int64_t)row * k;
     __shared__ __align__(16) char stage[STAGE ? kStageMaxK / 32 * kStageKbBytes : 16];
 #pragma unroll
@@ -366,11 +375,14 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
             }
             if (pass_live(pass + 2)) load(h, pass_row(pass + 2));   // uniform
 
-            float amax = 0.0f;
+            // the rotated values come out as sigma * u (fwht_cross_lane_signed),
+            // sigma = +-1 fixed per lane: |.| gives the absmax, and the code
+            // multiplier takes sigma
+            float amax = 0.0f, sigma = 1.0f;
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
                 fwht_in_lane<G>(v[j]);
-                fwht_cross_lane<G, true>(v[j], t);
+                sigma = fwht_cross_lane_signed<G>(v[j], t);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
             }
@@ -397,7 +409,7 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
             const int row = rp0 + team;
             const bool row_ok = row < m;
             const float scale = (amax * cg) / 127.0f;
-            const float r = amax > 0.0f ? 127.0f / amax : 0.0f;
+            const float r = (amax > 0.0f ? 127.0f / amax : 0.0f) * sigma;
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
                 const int c = j * T + t;

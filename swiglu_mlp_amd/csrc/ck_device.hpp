@@ -271,14 +271,16 @@ __device__ __forceinline__ void fwht_cross_lane(float (&v)[8], int lane)
     }
 }
 
-// Cross-lane strides 8 .. G/2 with the two nearest exchanges folded into the
-// butterfly: v_fmac_f32 with a DPP quad permutation on its first operand
+// Cross-lane strides 8 .. G/2 with the exchanges with lanes 1, 2 and 8 apart
+// folded into the butterfly: v_fmac_f32 with a DPP lane permutation (quad
+// permutations, a rotation by 8 within the 16-lane row) on its first operand
 // computes partner * t + own in one VALU op (the move-then-fma form above
 // takes two, and the compiler does not fold the move into an FMA).  With the
 // partner in the multiplied operand the upper lane gets q - p = -(p - q)
 // instead of p - q, so the lane's values come out as sigma * (the true value)
-// with sigma = t0 * t1 = (-1)^(bit 0 + bit 1 of the lane's position), which
-// the function returns: both are exact (t = +-1 makes the product exact, the
+// with sigma = the product of those stages' t = (-1)^(bits 0, 1 and 3 of the
+// lane's position), which the function returns: both are exact (t = +-1
+// makes the product exact, the
 // FMA rounds the sum once, and a negation is exact), and the later
 // exchanges pair lanes with equal sigma, where the usual form keeps it.  The
 // caller folds sigma into what it multiplies the values by (the code
@@ -290,7 +292,19 @@ __device__ __forceinline__ void fmac_dpp8(float (&v)[8], float t)
     // s_nop 1: two wait states between a VALU write of a register and a DPP
     // read of it; inside the block no op reads a register the op before it
     // wrote.
-    if constexpr (CTRL == 0xB1) {
+    if constexpr (CTRL == 0x128) {   // row_ror:8: lane l <- lane l ^ 8 within each row of 16
+        asm("s_nop 1\n\t"
+            "v_fmac_f32_dpp %0, %0, %8 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %1, %1, %8 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %2, %2, %8 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %3, %3, %8 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %4, %4, %8 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %5, %5, %8 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %6, %6, %8 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %7, %7, %8 row_ror:8 row_mask:0xf bank_mask:0xf"
+            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+            : "v"(t));
+    } else if constexpr (CTRL == 0xB1) {
         asm("s_nop 1\n\t"
             "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
             "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
@@ -303,7 +317,7 @@ __device__ __forceinline__ void fmac_dpp8(float (&v)[8], float t)
             : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
             : "v"(t));
     } else {
-        static_assert(CTRL == 0x4E, "quad permutation: xor 1 or xor 2");
+        static_assert(CTRL == 0x4E, "quad permutation xor 1 or xor 2, or row rotation xor 8");
         asm("s_nop 1\n\t"
             "v_fmac_f32_dpp %0, %0, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
             "v_fmac_f32_dpp %1, %1, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
@@ -331,17 +345,18 @@ __device__ __forceinline__ float fwht_cross_lane_signed(float (&v)[8], int lane)
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, swizzle_xor<4>(v[i]));
     }
-    if constexpr (G >= 128) {
-        const float s = (lane & 8) ? -1.0f : 1.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, swizzle_xor<8>(v[i]));
+    float sigma = t0 * t1;
+    if constexpr (G >= 128) {   // lane ^ 8 is a rotation by 8 within the 16-lane row: fused the same way
+        const float t3 = (lane & 8) ? -1.0f : 1.0f;
+        fmac_dpp8<0x128>(v, t3);
+        sigma *= t3;
     }
     if constexpr (G >= 256) {
         const float s = (lane & 16) ? -1.0f : 1.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, swizzle_xor<16>(v[i]));
     }
-    return t0 * t1;
+    return sigma;
 }
 
 // ---------------------------------------------------------------------------

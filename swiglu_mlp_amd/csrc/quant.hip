@@ -268,7 +268,7 @@ __global__ __launch_bounds__(BS) void quant_rows_kernel(
 // loads of its first rows are in flight; it then walks its rows, a team of T
 // lanes per row as in quant_rows_kernel, with the next rows' loads issued
 // before the current rows are rotated and quantized (two register buffers).
-// The per-element work drops from ~43 to ~29 VALU instructions, which takes
+// The per-element work drops from ~43 to ~28 VALU instructions, which takes
 // the kernel from its VALU bound to the HBM stream.  Outputs are those of
 // quant_rows_kernel<IN_BF16_SWIGLU, ..., OUT_CODES> bit for bit.
 //

@@ -222,7 +222,8 @@ __device__ __forceinline__ float swizzle_xor(float v)
 }
 
 // The same exchange for D = 1 or 2 through a DPP quad permutation (a VALU
-// move within each group of 4 lanes): no LDS traffic, one more VALU op.
+// move within each group of 4 lanes): no LDS traffic, one more VALU op.  Used
+// for reductions (the butterflies fuse the move, fwht_cross_lane_signed).
 template <int D>
 __device__ __forceinline__ float dpp_xor(float v)
 {
@@ -231,28 +232,20 @@ __device__ __forceinline__ float dpp_xor(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xf, 0xf, false));
 }
 
-template <int D, bool DPP>
-__device__ __forceinline__ float lane_xor(float v)
-{
-    if constexpr (DPP && D <= 2) return dpp_xor<D>(v);
-    else return swizzle_xor<D>(v);
-}
-
 // Cross-lane strides 8 .. G/2.  `lane` is the lane's position in its row team
-// (teams are aligned to the group size).  DPP: the two nearest exchanges
-// (strides 8 and 16) go through DPP moves instead of the LDS crossbar.
-template <int G, bool DPP = false>
+// (teams are aligned to the group size).
+template <int G>
 __device__ __forceinline__ void fwht_cross_lane(float (&v)[8], int lane)
 {
     if constexpr (G >= 16) {
         const float s = (lane & 1) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, lane_xor<1, DPP>(v[i]));
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, swizzle_xor<1>(v[i]));
     }
     if constexpr (G >= 32) {
         const float s = (lane & 2) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, lane_xor<2, DPP>(v[i]));
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(v[i], s, swizzle_xor<2>(v[i]));
     }
     if constexpr (G >= 64) {
         const float s = (lane & 4) ? -1.0f : 1.0f;

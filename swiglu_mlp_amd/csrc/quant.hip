@@ -158,10 +158,10 @@ __global__ __launch_bounds__(BS) void quant_rows_kernel(
     }
 
     // ---- rotation (unnormalised blockwise FWHT) + absmax --------------------
-    // From G = 32 the two nearest exchanges are fused into the butterfly and
-    // the values come out as sigma * u (fwht_cross_lane_signed; sigma = +-1,
-    // fixed per lane): |.| gives the absmax, and what the values are
-    // multiplied by below takes sigma.
+    // From G = 32 the exchanges with the lanes 1, 2 (and, from G = 128, 8)
+    // apart are fused into the butterfly and the values come out as sigma * u
+    // (fwht_cross_lane_signed; sigma = +-1, fixed per lane): |.| gives the
+    // absmax, and what the values are multiplied by below takes sigma.
     float amax = 0.0f, sigma = 1.0f;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {

@@ -374,9 +374,9 @@ int64_t ck_probe_mfma_workgroups(void);
 ck_status ck_probe_mfma_i8(const int8_t *ops, int64_t iters, int32_t lds, int32_t *sink,
                            void *stream);
 
-/* Row stream with a quantizer's traffic and trivial compute: m rows; row r
+/* Stream with a quantizer's traffic and trivial compute: m rows; row r
  * reads read_bytes at src + r * ld_bytes and writes write_bytes at
- * dst + r * write_bytes.  read_bytes % 16 == 0, read_bytes <= 65536,
+ * dst + r * write_bytes (a flat grid-stride loop over the 16-byte chunks).  read_bytes % 16 == 0, read_bytes <= 65536,
  * write_bytes % 8 == 0, write_bytes / 8 <= read_bytes / 16,
  * ld_bytes >= read_bytes, ld_bytes % 16 == 0; src 16-byte and dst 8-byte
  * aligned.  Errors: CK_EINVAL (pointers), CK_ESHAPE (sizes),

@@ -131,11 +131,26 @@ __device__ __forceinline__ float silu_sigma(float gc)
     return y;
 }
 
-__device__ __forceinline__ float silu_f32(float gamma)
+// max(gamma, -80) of a gate given as its FP32 bit pattern.  As unsigned
+// integers the patterns of all values at or above -80 (the non-negative ones,
+// sign bit clear, and the negatives down to -80 = 0xC2A00000) lie below those
+// of the values under -80, so an unsigned min with -80's pattern is the clamp,
+// bit for bit, for every gate that is not a NaN.  (fmaxf on a float that the
+// compiler got from a reinterpreted word is one canonicalizing max(x, x) more.)
+__device__ __forceinline__ float gate_clamp(uint32_t bits)
 {
-    const float gl = fmaxf(gamma, -80.0f);
-    const float gc = fminf(gl, 80.0f);
-    return gl * silu_sigma(gc);
+    return __uint_as_float(min(bits, 0xC2A00000u));
+}
+
+// silu_f32 of the gate with FP32 bit pattern `bits`: gl = max(gamma, -80) as
+// gate_clamp, gc = min(gl, 80) as a signed integer min (FP32 patterns of
+// non-negative values order as signed integers, and every negative pattern is
+// a negative integer, below 80's), then gl * silu_sigma(gc).
+__device__ __forceinline__ float silu_f32(uint32_t bits)
+{
+    const uint32_t gl = min(bits, 0xC2A00000u);
+    const int gc = min((int)gl, 0x42A00000);
+    return __uint_as_float(gl) * silu_sigma(__int_as_float(gc));
 }
 
 // ---------------------------------------------------------------------------
@@ -169,17 +184,20 @@ __device__ __forceinline__ float silu_tab_entry(int i)
 
 // Byte offset of the entry for the 16-bit gate pattern held in bits 0..15
 // (HI = false) or 16..31 (HI = true) of w, biased by kSiluTabBias: it is added
-// to the table's address minus kSiluTabBias, which keeps the lookup at one
-// med3 and one shift-or (the bias has zero low bits, so
-// ((mag - low) << 3) | sign = ((mag << 3) | sign) - bias).
+// to the table's address minus kSiluTabBias (the bias has zero low bits, so
+// ((mag - low) << 3) | sign = ((mag << 3) | sign) - bias).  (mag << 3) | (sign
+// << 2) is one alignbit of the clamped magnitude over the gate's FP32 pattern
+// (whose bit 31, the sign, lands on bit 2; the two bits below it are masked
+// off), the pattern the caller also clamps: four ops per gate with the med3.
 constexpr uint32_t kSiluTabBias = (uint32_t)kSiluTabLow << 3;
 
 template <bool HI>
 __device__ __forceinline__ uint32_t silu_tab_offset(uint32_t w)
 {
-    const uint32_t b = HI ? (w >> 16) : (w & 0xffffu);
-    const uint32_t mag = min(max(b & 0x7fffu, (uint32_t)kSiluTabLow), (uint32_t)kSiluTabMag);
-    return (mag << 3) | ((b >> 13) & 4u);
+    const uint32_t f = HI ? (w & 0xffff0000u) : (w << 16);          // the gate's FP32 pattern
+    const uint32_t b = HI ? (w >> 16) & 0x7fffu : w & 0x7fffu;      // its magnitude bits
+    const uint32_t mag = min(max(b, (uint32_t)kSiluTabLow), (uint32_t)kSiluTabMag);
+    return __builtin_amdgcn_alignbit(mag, f, 29) & 0x3fffcu;
 }
 
 // ---------------------------------------------------------------------------

@@ -91,8 +91,8 @@ __device__ __forceinline__ void row_values(int m, const uint4 (&rg)[MAXR][CH],
             const uint32_t wu[4] = {ru[m][j].x, ru[m][j].y, ru[m][j].z, ru[m][j].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                v[j][2 * e] = silu_f32(v[j][2 * e]) * bf16_lo(wu[e]);
-                v[j][2 * e + 1] = silu_f32(v[j][2 * e + 1]) * bf16_hi(wu[e]);
+                v[j][2 * e] = silu_f32(w[e] << 16) * bf16_lo(wu[e]);
+                v[j][2 * e + 1] = silu_f32(w[e] & 0xffff0000u) * bf16_hi(wu[e]);
             }
         }
     }

@@ -415,18 +415,27 @@ def test_swiglu_quant_large_calls_bit_exact(orc, m, k, g, layout):
 
 
 @pytest.mark.parametrize("m,k,g,layout", [
-    (2049, 1024, 64, "blocked"), (3001, 2048, 128, "rows"), (4096, 3072, 128, "blocked"),
-    (2050, 4096, 256, "rows"), (2560, 5120, 128, "blocked"), (2051, 12288, 64, "rows"),
-    (2304, 1536, 256, "blocked"),
+    (3001, 2048, 128, "rows"), (2050, 4096, 256, "rows"), (2051, 12288, 64, "rows"),
+    # blocked codes from the per-row kernel: shapes that would leave group
+    # slots of the line kernel idle (k = 5120 at g = 128, k = 1536 at g = 256),
+    # fewer than 8 rows per CU
+    (2560, 5120, 128, "blocked"), (2304, 1536, 256, "blocked"), (1500, 4096, 128, "blocked"),
+    # the line kernel (8 rows per workgroup, 4 to 16 waves, 1 to 8 loads per
+    # lane; ragged last 8-row group)
+    (2049, 1024, 64, "blocked"), (4096, 3072, 128, "blocked"), (2050, 8192, 128, "blocked"),
+    (3000, 6144, 256, "blocked"), (2500, 2048, 64, "blocked"), (4095, 2560, 64, "blocked"),
+    (2100, 1280, 64, "blocked"),
     # m * k >= 2^24, k <= 4096: blocked codes staged in LDS, 1 to 4 chunks per
-    # lane (k = 4032: idle chunk slots), ragged last 8-row group
+    # lane (k = 4032: idle chunk slots), ragged last 8-row group; at
+    # m * k = 2^24 the line writes are non-temporal
     (16385, 1024, 64, "blocked"), (8193, 2048, 128, "blocked"), (5462, 3072, 256, "blocked"),
-    (4097, 4096, 128, "blocked"), (4200, 4032, 64, "blocked")])
+    (4097, 4096, 128, "blocked"), (4200, 4032, 64, "blocked"), (8192, 2048, 64, "blocked"),
+    (16384, 1024, 256, "blocked")])
 def test_x_quant_large_calls_bit_exact(orc, m, k, g, layout):
     """Large x quantizer calls: codes and scales bit-exact against the oracle,
-    ragged row counts, row-major and blocked codes (staged in LDS per 8-row
-    group from m * k = 2^24), outlier channels, an all-zero row and a row with
-    a single nonzero value."""
+    ragged row counts, row-major and blocked codes (the line kernel, or staged
+    in LDS per 8-row group from m * k = 2^24), outlier channels, an all-zero
+    row and a row with a single nonzero value."""
     say(f"x quant large m={m} k={k} g={g} {layout}")
     rng = np.random.default_rng(3 * m + k)
     xf = rng.standard_normal((m, k)).astype(np.float32)

@@ -11,6 +11,14 @@ that each kernel can be bracketed by HIP events on the stream it runs on.
 Weight preparation and the one-time weight relayout happen before timing, as at
 model load.  Inputs are resident in HBM before the timed region.
 
+Settling: before the W warm-up steps the step runs untimed for --settle-ms of
+wall time (default 60 ms).  A GPU coming out of idle runs the first steps near
+its boost clock, then its power manager pulls the clock well below the level it
+sustains before settling there: c5's per-step time from a cold start was ~455 us,
+570-586 us at 3-6 ms and 453 us from ~40 ms on, so a 20-step timed region right
+after 5 warm-up steps fell into the dip (0.506 against 0.459 ms per step on the
+same box).  The JSON line reports settle_ms and the steps it took.
+
 Timing: after the warm-up, a short probe pass (HIP events between every stage)
 picks the kernel with the largest share of the step.  In the K timed steps only
 that kernel is bracketed by HIP events on its launch stream (events between
@@ -21,7 +29,7 @@ are then timed once more, each call alone after a 512 MB read pass that evicts
 the 256 MB MALL, and that flushed median is their headline figure.  The CPU
 baseline times the oracle stage by stage on the host cores.
 
-Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
+Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--settle-ms T]
 [--workload c1..c5] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -97,6 +105,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="untimed steps for this long before the warm-up (0: none)")
     ap.add_argument("--workload", default="c5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bias-residual", action="store_true",
@@ -576,8 +586,17 @@ def main():
         return {stages[j][0]: 1000.0 * sum(ev[i][j][0].elapsed_time(ev[i][j][1])
                                            for i in range(steps)) / steps for j in which}
 
-    # warm-up, then a short pass with every stage bracketed to find the kernel
-    # with the largest share of the step
+    # settle (see the module docstring), then the warm-up, then a short pass
+    # with every stage bracketed to find the kernel with the largest share of
+    # the step
+    settle_steps = 0
+    if args.settle_ms > 0:
+        t_end = time.perf_counter() + args.settle_ms / 1000.0
+        while time.perf_counter() < t_end or settle_steps < 8:
+            for _ in range(4):
+                run_step()
+            settle_steps += 4
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
@@ -678,7 +697,8 @@ def main():
         unit, dtype = "TFLOP/s", "bf16xint8"
     line = {
         "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "warmup": args.warmup, "settle_ms": args.settle_ms, "settle_steps": settle_steps,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.desc}", "m": wl.m, "k": wl.k, "n": wl.n,
                    "group": g, "int8_ops_per_step": wl.int8_ops, "parallelism": "single-gpu",

@@ -876,11 +876,21 @@ bool tab_team(int64_t k, int* log_t, int* ch)
     return best >= 0;
 }
 
+// The table kernel from m * k = 2^24 (m >= 512), and from 2^23 with at least 8
+// rows per CU: each workgroup builds the 37 KB table once, which its rows must
+// repay.  Measured after a MALL flush (events around single calls, one box)
+// against the per-row kernel: 4096 x 2048 13.7 -> 13.0 us, 2048 x 4096 13.1 ->
+// 12.8, 3072 x 4096 20.4 -> 18.9; at 2048 x 3072 the two are within the
+// box-to-box spread (11.0 against 11.3 us on one box, 12.0 against 11.4 on
+// another), and with fewer rows per CU the per-row kernel is ahead (1024 x 3072
+// 7.8 against 9.4, 512 x 12288 12.5 against 20.3 us).
 bool use_swiglu_tab(int64_t m, int64_t k, int64_t ld, int g)
 {
     const bool gs = g == 64 || g == 128 || g == 256;
     const bool fits = m * ld * 2 < ((int64_t)1 << 31) && (m + 255) / 256 * 256 * k < ((int64_t)1 << 31);
-    return gs && fits && k >= 1024 && m >= 512 && m * k >= ((int64_t)1 << 24);
+    const bool big = m >= 512 && m * k >= ((int64_t)1 << 24);
+    const bool many_rows = m >= 8 * (int64_t)num_cus() && m * k >= ((int64_t)1 << 23);
+    return gs && fits && k >= 1024 && (big || many_rows);
 }
 
 template <int LOG_G, bool BLOCKED, bool STAGE>

@@ -387,11 +387,14 @@ def test_act_quant_blocked(orc, name):
     (5601, 3072, 64, "blocked"), (2051, 8192, 256, "blocked"), (1201, 14336, 128, "blocked"),
     (1025, 16384, 64, "blocked"),
     # k < 1024: the per-row kernel with staged blocked codes
-    (32769, 512, 64, "blocked")])
+    (32769, 512, 64, "blocked"),
+    # m * k in [2^23, 2^24) with at least 8 rows per CU: the table kernel too
+    (4097, 2048, 64, "blocked"), (2048, 4096, 128, "rows"), (3001, 4096, 256, "blocked")])
 def test_swiglu_quant_large_calls_bit_exact(orc, m, k, g, layout):
     """Large SwiGLU quantizer calls: codes and scales bit-exact against the
     oracle.  From k = 1024 the persistent kernel whose silu is a table lookup
-    takes them (teams of 128 to 1024 lanes, 1 to 3 chunks per lane); blocked
+    takes them (m * k >= 2^24, or 2^23 with 8 rows per CU; teams of 128 to
+    1024 lanes, 1 to 3 chunks per lane); blocked
     codes up to k = 14336 are staged in LDS per aligned 8-row group, ragged
     row counts end in partial groups."""
     say(f"swiglu quant large m={m} k={k} g={g} {layout}")

@@ -392,8 +392,8 @@ __global__ __launch_bounds__(1024) void quant_lines_kernel(const uint16_t* __res
 // loads of its first rows are in flight; it then walks its rows, a team of T
 // lanes per row as in quant_rows_kernel, with the next rows' loads issued
 // before the current rows are rotated and quantized (two register buffers).
-// The per-element work drops from ~43 to ~28 VALU instructions, which takes
-// the kernel from its VALU bound to the HBM stream.  Outputs are those of
+// The per-element work drops from ~43 to ~24 VALU instructions (measured on
+// c5's shape, the table's construction included).  Outputs are those of
 // quant_rows_kernel<IN_BF16_SWIGLU, ..., OUT_CODES> bit for bit.
 //
 // STAGE (blocked codes, k <= kTabStageMaxK): rows are taken in aligned groups

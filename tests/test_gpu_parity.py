@@ -454,6 +454,45 @@ def test_x_quant_large_calls_bit_exact(orc, m, k, g, layout):
     np.testing.assert_array_equal(from_blocked(host(q), m) if layout == "blocked" else host(q), q_o)
 
 
+def _random_x_quant_shapes(count=48, seed=2026):
+    """Seeded random x-quantizer calls with blocked codes around the kernels'
+    domain borders: 1900..9000 rows (under and over 8 rows per CU, under and
+    over m * k = 2^24), k either a common model width or a random multiple of
+    the group in 768..8448 (both sides of the line kernel's 1024 and 8192 and
+    of the staged kernel's 4096; group counts that do and do not divide among
+    16, 12, 8 or 4 waves), g in {64, 128, 256}."""
+    rng = np.random.default_rng(seed)
+    widths = [1024, 1536, 2048, 2560, 3072, 4096, 5120, 6144, 7168, 8192]
+    shapes = []
+    for _ in range(count):
+        g = int(rng.choice([64, 128, 256]))
+        if rng.random() < 0.6:
+            k = int(rng.choice(widths))
+        else:
+            k = int(rng.integers(768 // g, 8448 // g + 1)) * g
+        m = int(rng.integers(1900, 9001))
+        shapes.append((m, k, g))
+    return shapes
+
+
+@pytest.mark.parametrize("m,k,g", _random_x_quant_shapes())
+def test_x_quant_random_blocked_bit_exact(orc, m, k, g):
+    """x quantizer, blocked codes, seeded random shapes (line kernel, staged
+    kernel with and without non-temporal line writes, per-row kernel): codes
+    and scales bit-exact against the oracle."""
+    say(f"x quant random m={m} k={k} g={g}")
+    rng = np.random.default_rng(m * 7 + k)
+    xf = rng.standard_normal((m, k)).astype(np.float32)
+    xf[:, rng.choice(k, size=max(1, k // 100), replace=False)] *= 20.0
+    x = W.to_bf16_bits(xf)
+    x[m // 5] = 0
+    q, sc = ck.ck_act_quant(bf16_dev(x), 0, g, layout="blocked")
+    torch.cuda.synchronize()
+    q_o, s_o = orc.act_quant(x, 0, g)
+    np.testing.assert_array_equal(host(sc)[:, 0].view(np.uint32), s_o.view(np.uint32))
+    np.testing.assert_array_equal(from_blocked(host(q), m), q_o)
+
+
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
 def test_gemm_i32_blocked_bit_exact(orc, m, n, k):
     say(f"gemm_i32 blocked m={m} n={n} k={k}")

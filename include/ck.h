@@ -289,7 +289,7 @@ size_t ck_swiglu_mlp_workspace_size(int64_t m, int64_t h, int64_t i);
 
 /* Rotated activation in BF16: a (= x, or silu(gate) * up for CK_ACT_SWIGLU,
  * in FP32), u = the unnormalised blockwise FWHT of a (as ck_act_quant),
- * x_rot = bf16(fl(u * fl(1 / sqrt(group)))).
+ * x_rot = bf16(fl(u * fl(1 / sqrt(group))) + 0): an exact zero is +0.
  *   layout  CK_LAYOUT_ROWS: x_rot [m, k] row-major; CK_LAYOUT_BLOCKED: the
  *           BF16 blocked layout, ck_blocked_size(m, k) * 2 bytes (the padding
  *           rows are not written)
@@ -351,7 +351,8 @@ ck_status ck_w8a16_gemm_f32(const uint16_t *x_rot, const int8_t *w_q, int64_t m,
 ck_status ck_silu_f32(const uint16_t *gate, int64_t n, float *out, void *stream);
 
 /* Unnormalised rotated activation u [m, k] FP32 (before quantization), by the
- * quantizer's own device code (comfy-kitchen PR #277, "The key observation"). */
+ * quantizer's own device code (comfy-kitchen PR #277, "The key observation");
+ * an exact zero is written as +0. */
 ck_status ck_act_rotate_f32(const uint16_t *x, int64_t ldx, int64_t m,
                             int64_t k, int32_t act, int32_t group, float *u,
                             void *stream);

@@ -283,9 +283,12 @@ def swiglu_mlp(x_bf16, wgu_q, sgu, wd_q, sd, g: int, return_all: bool = False):
 # --------------------------------------------------------------------------
 def act_rotate_bf16(x_bf16, act: int, g: int, k: int | None = None) -> np.ndarray:
     """x_rot = x H with the orthonormal H, rounded to BF16: the unnormalised
-    FWHT u of the (optionally SwiGLU'd) row, then bf16(fl(u * fl(1/sqrt(g))))."""
+    FWHT u of the (optionally SwiGLU'd) row, then bf16(fl(u * fl(1/sqrt(g))) + 0).
+    The + 0 writes an exact zero (also one the product underflows to) as +0:
+    x H is defined over the reals, where a zero has no sign."""
     u = act_rotate(x_bf16, act, g, k)
-    return f32_to_bf16(u * norm_const(g))      # float32 * float32: one FP32 rounding
+    # float32 * float32: one FP32 rounding; + 0 changes no nonzero value
+    return f32_to_bf16(u * norm_const(g) + np.float32(0.0))
 
 
 def w8a16_acc(x_rot_bf16, wq) -> np.ndarray:

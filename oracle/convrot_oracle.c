@@ -211,6 +211,9 @@ static int check_act_args(int64_t ldx, int64_t m, int64_t k, int act, int g)
     return 0;
 }
 
+/* The rotated row as values: the pages define x H over the reals, where a zero
+ * has no sign.  Reading: an exact zero of u is written as +0 (u + 0 changes no
+ * other value; the codes and scales never see the sign of a zero). */
 int orc_act_rotate(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, int act,
                    int g, float *u)
 {
@@ -220,6 +223,7 @@ int orc_act_rotate(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, int act
         float *ur = u + r * k;
         act_row(x + r * ldx, k, act, ur);
         orc_fwht_groups(ur, k, g);
+        for (int64_t j = 0; j < k; ++j) ur[j] = ur[j] + 0.0f;
     }
     return 0;
 }

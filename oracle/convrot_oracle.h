@@ -62,7 +62,8 @@ void orc_quant_row(const float *u, int64_t k, int g, int8_t *q, float *s);
 int orc_act_quant(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, int act,
                   int g, int8_t *q, float *s);
 
-/* Rotated-but-unquantized FP32 activation (unnormalised), for diagnostics. */
+/* Rotated-but-unquantized FP32 activation (unnormalised), for diagnostics;
+ * an exact zero is written as +0. */
 int orc_act_rotate(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, int act,
                    int g, float *u);
 

@@ -86,6 +86,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// A rotated pair as BF16: bf16(fl(a * c) + 0), bf16(fl(b * c) + 0).  Adding
+// +0 changes no value and writes an exact zero as +0, so the sign of a zero
+// does not depend on the butterfly form (the sign-folded butterflies hold a
+// cancelled value as +0 where the plain ones hold -0, and the reverse).
+__device__ __forceinline__ uint32_t rot_bf16x2(float a, float b, float c)
+{
+    return pack_bf16x2(a * c + 0.0f, b * c + 0.0f);
+}
+
 // ---------------------------------------------------------------------------
 // FP32 silu.  sglang PR #44196, "Accuracy Tests": the fused quantizer keeps
 // silu(gate) * up in FP32.  The evaluation procedure is fixed so the result is

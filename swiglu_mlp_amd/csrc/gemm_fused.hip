@@ -320,8 +320,8 @@ __global__ __launch_bounds__(NT) void gemm_w8a16_fused_kernel(
             fwht_in_lane<G>(v[j]);
             fwht_cross_lane<G>(v[j], tid);
             const int c = j * NT + tid;
-            const uint4 h = make_uint4(pack_bf16x2(v[j][0] * cg, v[j][1] * cg), pack_bf16x2(v[j][2] * cg, v[j][3] * cg),
-                                       pack_bf16x2(v[j][4] * cg, v[j][5] * cg), pack_bf16x2(v[j][6] * cg, v[j][7] * cg));
+            const uint4 h = make_uint4(rot_bf16x2(v[j][0], v[j][1], cg), rot_bf16x2(v[j][2], v[j][3], cg),
+                                       rot_bf16x2(v[j][4], v[j][5], cg), rot_bf16x2(v[j][6], v[j][7], cg));
             if (c < k8) *reinterpret_cast<uint4*>(xs + m * xs_stride + c * 8) = h;
         }
     }

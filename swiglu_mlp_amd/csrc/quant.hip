@@ -174,15 +174,15 @@ __global__ __launch_bounds__(BS) void quant_rows_kernel(
     }
 
     if constexpr (OUT == OUT_ROT_BF16) {
-        // x_rot = bf16(fl(u * c_g)): the rotation with the orthonormal H
-        // (fl(sigma u * sigma c_g) = fl(u * c_g))
+        // x_rot = bf16(fl(u * c_g) + 0): the rotation with the orthonormal H
+        // (fl(sigma u * sigma c_g) = fl(u * c_g) up to the sign of a zero)
         char* ob = static_cast<char*>(u_out);
         const float cs = cg * sigma;
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             const int c = j * T + t;
-            const uint4 w = make_uint4(pack_bf16x2(v[j][0] * cs, v[j][1] * cs), pack_bf16x2(v[j][2] * cs, v[j][3] * cs),
-                                       pack_bf16x2(v[j][4] * cs, v[j][5] * cs), pack_bf16x2(v[j][6] * cs, v[j][7] * cs));
+            const uint4 w = make_uint4(rot_bf16x2(v[j][0], v[j][1], cs), rot_bf16x2(v[j][2], v[j][3], cs),
+                                       rot_bf16x2(v[j][4], v[j][5], cs), rot_bf16x2(v[j][6], v[j][7], cs));
             if (row_ok && c < k8) {
                 const int64_t off = BLOCKED ? blocked_bf16_offset(row, c, k >> 5) : ((int64_t)row * k + c * 8) * 2;
                 *reinterpret_cast<uint4*>(ob + off) = w;
@@ -196,10 +196,11 @@ __global__ __launch_bounds__(BS) void quant_rows_kernel(
         for (int j = 0; j < CH; ++j) {
             const int c = j * T + t;
             if (row_ok && c < k8) {
-                *reinterpret_cast<float4*>(up + c * 8) =
-                    make_float4(v[j][0] * sigma, v[j][1] * sigma, v[j][2] * sigma, v[j][3] * sigma);
-                *reinterpret_cast<float4*>(up + c * 8 + 4) =
-                    make_float4(v[j][4] * sigma, v[j][5] * sigma, v[j][6] * sigma, v[j][7] * sigma);
+                // + 0: an exact zero as +0, whatever sign the butterflies left it
+                *reinterpret_cast<float4*>(up + c * 8) = make_float4(
+                    v[j][0] * sigma + 0.0f, v[j][1] * sigma + 0.0f, v[j][2] * sigma + 0.0f, v[j][3] * sigma + 0.0f);
+                *reinterpret_cast<float4*>(up + c * 8 + 4) = make_float4(
+                    v[j][4] * sigma + 0.0f, v[j][5] * sigma + 0.0f, v[j][6] * sigma + 0.0f, v[j][7] * sigma + 0.0f);
             }
         }
         return;
@@ -412,12 +413,18 @@ __global__ __launch_bounds__(1024) void quant_lines_kernel(const uint16_t* __res
 // faster than the group order.
 constexpr int kTabThreads = 1024;
 
-template <int LOG_G, int CH, bool BLOCKED, bool STAGE>
+// ROT: the W8A16 rotation instead of codes: q is the row-major BF16 output
+// (x_rot = bf16(fl(u * c_g) + 0), as quant_rows_kernel<IN_BF16_SWIGLU, ...,
+// OUT_ROT_BF16> writes it bit for bit), s is unused, and a pass has no absmax,
+// no barrier and no staging.  (The blocked BF16 layout is written by
+// rotate_lines_kernel.)
+template <int LOG_G, int CH, bool BLOCKED, bool STAGE, bool ROT = false>
 __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
     const uint16_t* __restrict__ src, int64_t ld, int m, int k, int log_t, float cg, int8_t* __restrict__ q,
     float* __restrict__ s)
 {
     static_assert(!STAGE || BLOCKED, "staging is for blocked codes");
+    static_assert(!(BLOCKED && ROT), "the rotation here is row-major");
     constexpr int G = 1 << LOG_G;
     __shared__ float tab[kSiluTabEntries];
     __shared__ float red[2][kTabThreads / 64];
@@ -447,7 +454,7 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
     // has no branches and the compiler can count the loads in flight exactly.
     const __amdgpu_buffer_rsrc_t rs_x =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), (short)0, (int)((int64_t)m * ld * 2), 0x00020000);
-    const int64_t qbytes = BLOCKED ? (int64_t)((m + 255) / 256 * 256) * k : (int64_t)m * k;
+    const int64_t qbytes = (BLOCKED ? (int64_t)((m + 255) / 256 * 256) * k : (int64_t)m * k) * (ROT ? 2 : 1);
     const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(q, (short)0, (int)qbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(s, (short)0, m * 4, 0x00020000);
     typedef int v4i_t __attribute__((ext_vector_type(4)));
@@ -514,6 +521,20 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
 #pragma unroll
                 for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
             }
+            if constexpr (ROT) {
+                // x_rot = bf16(fl(sigma u * sigma c_g) + 0) = bf16(fl(u * c_g) + 0)
+                const float cs = cg * sigma;
+                const int row = rp0 + team;
+#pragma unroll
+                for (int j = 0; j < CH; ++j) {
+                    const int c = j * T + t;
+                    const v4i_t w = {(int)rot_bf16x2(v[j][0], v[j][1], cs), (int)rot_bf16x2(v[j][2], v[j][3], cs),
+                                     (int)rot_bf16x2(v[j][4], v[j][5], cs), (int)rot_bf16x2(v[j][6], v[j][7], cs)};
+                    const uint32_t ou = (row < m && c < k8) ? (uint32_t)(((int64_t)row * k + c * 8) * 2) : kBufferOutside;
+                    __builtin_amdgcn_raw_buffer_store_b128(w, rs_q, ou, 0, 0);
+                }
+                continue;
+            }
             // T >= 128 here (at most 8 rows per 1024-thread workgroup)
             amax = fmaxf(amax, dpp_xor<1>(amax));
             amax = fmaxf(amax, dpp_xor<2>(amax));
@@ -573,6 +594,128 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
                         __builtin_amdgcn_raw_buffer_store_b128(w, rs_q, off, 0, 0);
                     }
                 }
+            }
+        }
+    }
+}
+
+// The rotation to BF16 in the blocked layout, written as whole lines (x
+// itself, or SWI: silu(gate) * up of [gate | up] rows, silu from the LDS
+// table as in quant_swiglu_tab_kernel).  In that layout a 128-byte line holds
+// the 16 bytes of one 8-column chunk of 8 consecutive rows.  The row-wise
+// kernels lay a row's chunks across a workgroup, so a line gathers its pieces
+// from several workgroups at different times, and those partial lines cost
+// more than the reads (the SwiGLU rotation of 4096 x 12288, after a MALL
+// flush: 117 us blocked against 53 us row-major).  Here a wave holds
+// RW = 64 / (g / 8) consecutive rows of one rotation group, one lane per
+// chunk, so a store writes RW * 16 contiguous bytes of each line it touches,
+// and the waves holding the other rows of the 8-row block write the rest of
+// those lines with the same instruction.  Unit of work: an aligned block of 8
+// rows times a slice of CH * SLOTS consecutive groups; workgroup b takes
+// units b + i * gridDim, with the loads of two units in flight.
+template <int LOG_G, int CH, bool SWI>
+__global__ __launch_bounds__(kTabThreads) void rotate_lines_kernel(const uint16_t* __restrict__ src, int64_t ld,
+                                                                   int m, int k, int nsl, float cg,
+                                                                   uint16_t* __restrict__ out)
+{
+    constexpr int G = 1 << LOG_G;
+    constexpr int LGL = LOG_G - 3;                    // log2 of a group's lanes
+    constexpr int RW = 64 >> LGL;                     // rows per wave
+    constexpr int WPB = 8 / RW;                       // waves per 8-row block and group slot
+    constexpr int SLOTS = kTabThreads / 64 / WPB;     // group slots of a workgroup
+    constexpr int NSG = CH * SLOTS;                   // groups per unit
+    __shared__ float tab[SWI ? kSiluTabEntries : 1];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int gpos = lane & ((1 << LGL) - 1);         // chunk within the group
+    const int r8 = (wave % WPB) * RW + (lane >> LGL); // row within the 8-row block
+    const int slot = wave / WPB;
+    const int ng = k >> LOG_G;
+    const int units = ((m + 7) >> 3) * nsl;
+    const int nwg = gridDim.x;
+    if ((int)blockIdx.x >= units) return;             // uniform exit (no barrier reached)
+    const char* tb = reinterpret_cast<const char*>(tab) - kSiluTabBias;   // see silu_tab_offset
+
+    // buffer resources as in quant_swiglu_tab_kernel: past-the-end offsets
+    // read zeros and drop stores (the launcher keeps both extents below 2^31)
+    const __amdgpu_buffer_rsrc_t rs_x =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), (short)0, (int)((int64_t)m * ld * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(
+        out, (short)0, (int)((int64_t)((m + 255) / 256 * 256) * k * 2), 0x00020000);
+    typedef int v4i_t __attribute__((ext_vector_type(4)));
+
+    v4i_t gb[2][CH], ub[2][SWI ? CH : 1];
+    auto load = [&](int h, int u) {   // u >= units: no memory access
+        const int row = u < units ? (u / nsl) * 8 + r8 : m;
+        const int g0 = (u % nsl) * NSG + slot;
+        const uint32_t rb = row < m ? (uint32_t)((int64_t)row * ld * 2) : kBufferOutside;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int gi = g0 + j * SLOTS;
+            const uint32_t og = gi < ng ? rb + (uint32_t)((gi << LGL) + gpos) * 16u : kBufferOutside;
+            gb[h][j] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, og, 0, 0);
+            if constexpr (SWI)
+                ub[h][j] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, gi < ng ? og + (uint32_t)k * 2u : kBufferOutside,
+                                                                 0, 0);
+        }
+    };
+    load(0, blockIdx.x);
+    load(1, blockIdx.x + nwg);
+    if constexpr (SWI) {
+        for (int i = threadIdx.x; i < kSiluTabEntries; i += kTabThreads) tab[i] = silu_tab_entry(i);
+        __syncthreads();
+    }
+
+    for (int i0 = 0;; i0 += 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int u = blockIdx.x + (i0 + h) * nwg;
+            if (u >= units) return;                   // uniform
+            const int row = (u / nsl) * 8 + r8;
+            const int g0 = (u % nsl) * NSG + slot;
+            float v[CH][8];
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const uint32_t wg[4] = {(uint32_t)gb[h][j][0], (uint32_t)gb[h][j][1], (uint32_t)gb[h][j][2],
+                                        (uint32_t)gb[h][j][3]};
+                if constexpr (SWI) {
+                    const uint32_t wu[4] = {(uint32_t)ub[h][j][0], (uint32_t)ub[h][j][1], (uint32_t)ub[h][j][2],
+                                            (uint32_t)ub[h][j][3]};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float y0 = *reinterpret_cast<const float*>(tb + silu_tab_offset<false>(wg[e]));
+                        const float y1 = *reinterpret_cast<const float*>(tb + silu_tab_offset<true>(wg[e]));
+                        const float s0 = gate_clamp(wg[e] << 16) * y0;    // silu_f32, bit for bit
+                        const float s1 = gate_clamp(wg[e] & 0xffff0000u) * y1;
+                        v[j][2 * e] = s0 * bf16_lo(wu[e]);
+                        v[j][2 * e + 1] = s1 * bf16_hi(wu[e]);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[j][2 * e] = bf16_lo(wg[e]);
+                        v[j][2 * e + 1] = bf16_hi(wg[e]);
+                    }
+                }
+            }
+            load(h, u + 2 * nwg);
+
+            // x_rot = bf16(fl(sigma u * sigma c_g) + 0) = bf16(fl(u * c_g) + 0)
+            float sigma = 1.0f;
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                fwht_in_lane<G>(v[j]);
+                sigma = fwht_cross_lane_signed<G>(v[j], gpos);
+            }
+            const float cs = cg * sigma;
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const int gi = g0 + j * SLOTS;
+                const int c = (gi << LGL) + gpos;
+                const v4i_t w = {(int)rot_bf16x2(v[j][0], v[j][1], cs), (int)rot_bf16x2(v[j][2], v[j][3], cs),
+                                 (int)rot_bf16x2(v[j][4], v[j][5], cs), (int)rot_bf16x2(v[j][6], v[j][7], cs)};
+                const uint32_t oo = (row < m && gi < ng) ? (uint32_t)blocked_bf16_offset(row, c, k >> 5) : kBufferOutside;
+                __builtin_amdgcn_raw_buffer_store_b128(w, rs_o, oo, 0, 0);
             }
         }
     }
@@ -893,14 +1036,14 @@ bool use_swiglu_tab(int64_t m, int64_t k, int64_t ld, int g)
     return gs && fits && k >= 1024 && (big || many_rows);
 }
 
-template <int LOG_G, bool BLOCKED, bool STAGE>
+template <int LOG_G, bool BLOCKED, bool STAGE, bool ROT = false>
 hipError_t launch_tab_ch(int ch, dim3 grid, hipStream_t st, const uint16_t* src, int64_t ld, int m, int k,
                          int log_t, float cg, int8_t* q, float* s)
 {
-#define CK_TAB(C)                                                                                          \
-    case C:                                                                                                \
-        hipLaunchKernelGGL((quant_swiglu_tab_kernel<LOG_G, C, BLOCKED, STAGE>), grid, dim3(kTabThreads), 0, st, \
-                           src, ld, m, k, log_t, cg, q, s);                                                \
+#define CK_TAB(C)                                                                                               \
+    case C:                                                                                                     \
+        hipLaunchKernelGGL((quant_swiglu_tab_kernel<LOG_G, C, BLOCKED, STAGE, ROT>), grid, dim3(kTabThreads), 0, \
+                           st, src, ld, m, k, log_t, cg, q, s);                                                 \
         break;
     switch (ch) {
         CK_TAB(1) CK_TAB(2) CK_TAB(3)
@@ -910,12 +1053,13 @@ hipError_t launch_tab_ch(int ch, dim3 grid, hipStream_t st, const uint16_t* src,
     return hipGetLastError();
 }
 
+// rot: the row-major BF16 rotation into q (s unused) instead of codes and scales
 hipError_t launch_swiglu_tab(const uint16_t* src, int64_t ld, int64_t m, int64_t k, int g, int8_t* q, float* s,
-                             bool blocked, hipStream_t st)
+                             bool blocked, bool rot, hipStream_t st)
 {
     int log_t = 0, ch = 0;
     if (!tab_team(k, &log_t, &ch)) return hipErrorInvalidValue;
-    const bool stage = blocked && k <= kTabStageMaxK;
+    const bool stage = !rot && blocked && k <= kTabStageMaxK;
     const int rpw = kTabThreads >> log_t;
     // staged: aligned groups of 8 rows; otherwise row slots of rpw rows, and
     // a multiple of 8 workgroups (see the slot order in the kernel)
@@ -924,13 +1068,70 @@ hipError_t launch_swiglu_tab(const uint16_t* src, int64_t ld, int64_t m, int64_t
     const dim3 grid((unsigned)wgs);
     const float cg = (float)(1.0 / sqrt((double)g));
     const int lg = g == 64 ? 6 : g == 128 ? 7 : 8;
-#define CK_TAB_G(L)                                                                                            \
-    if (lg == L)                                                                                               \
-        return stage     ? launch_tab_ch<L, true, true>(ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s) \
-               : blocked ? launch_tab_ch<L, true, false>(ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s) \
-                         : launch_tab_ch<L, false, false>(ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s);
+#define CK_TAB_ARGS ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s
+#define CK_TAB_G(L)                                                                            \
+    if (lg == L) {                                                                             \
+        if (rot) return launch_tab_ch<L, false, false, true>(CK_TAB_ARGS);                     \
+        return stage     ? launch_tab_ch<L, true, true>(CK_TAB_ARGS)                           \
+               : blocked ? launch_tab_ch<L, true, false>(CK_TAB_ARGS)                          \
+                         : launch_tab_ch<L, false, false>(CK_TAB_ARGS);                        \
+    }
     CK_TAB_G(6) CK_TAB_G(7) CK_TAB_G(8)
 #undef CK_TAB_G
+#undef CK_TAB_ARGS
+    return hipErrorInvalidValue;
+}
+
+// The line rotation (blocked BF16 output) for x from m * k = 2^20 with at
+// least 512 rows, and for SwiGLU where the table kernel takes the codes (the
+// table must be repaid as there).  Measured after a MALL flush against the
+// row-wise kernel: x 4096 x 3072 16.6 -> 12.7 us, 2048 x 4096 11.2 -> 8.3,
+// 1024 x 1024 4.8 -> 4.6; SwiGLU 4096 x 12288 94.0 -> 56.0, 2048 x 8192
+// 31.4 -> 21.6.  With fewer rows the units are too few for the CUs (256 x
+// 4096: 5.8 against 4.6 us).
+bool use_rotate_lines(int kind, int64_t m, int64_t k, int64_t ld, int g)
+{
+    const bool gs = g == 64 || g == 128 || g == 256;
+    const bool fits = m * ld * 2 < ((int64_t)1 << 31) && (m + 255) / 256 * 256 * k * 2 < ((int64_t)1 << 31);
+    if (!gs || !fits) return false;
+    if (kind == IN_BF16) return m >= 512 && m * k >= ((int64_t)1 << 20);
+    return kind == IN_BF16_SWIGLU && use_swiglu_tab(m, k, ld, g);
+}
+
+// Groups per lane and unit: the fewest idle group slots over a row's slices,
+// then the most groups per unit (at most 3 with SwiGLU, whose two inputs
+// double the registers in flight, else 4).
+hipError_t launch_rotate_lines(bool swi, const uint16_t* src, int64_t ld, int64_t m, int64_t k, int g,
+                               uint16_t* out, hipStream_t st)
+{
+    const int lg = g == 64 ? 6 : g == 128 ? 7 : 8;
+    const int slots = 16 / (8 / (64 >> (lg - 3)));
+    const int64_t ng = k / g;
+    int ch = 0;
+    int64_t nsl = 0, best = -1;
+    for (int c = swi ? 3 : 4; c >= 1; --c) {
+        const int64_t n = (ng + (int64_t)c * slots - 1) / ((int64_t)c * slots);
+        const int64_t idle = n * c * slots - ng;
+        if (best < 0 || idle < best) {
+            best = idle;
+            ch = c;
+            nsl = n;
+        }
+    }
+    const int64_t units = (m + 7) / 8 * nsl;
+    const dim3 grid((unsigned)std::min<int64_t>(units, num_cus()));
+    const float cg = (float)(1.0 / sqrt((double)g));
+#define CK_RL(L, C, S)                                                                                     \
+    if (lg == L && ch == C && swi == S) {                                                                  \
+        hipLaunchKernelGGL((rotate_lines_kernel<L, C, S>), grid, dim3(kTabThreads), 0, st, src, ld, (int)m, \
+                           (int)k, (int)nsl, cg, out);                                                     \
+        return hipGetLastError();                                                                          \
+    }
+#define CK_RL_G(L) CK_RL(L, 1, true) CK_RL(L, 2, true) CK_RL(L, 3, true) \
+    CK_RL(L, 1, false) CK_RL(L, 2, false) CK_RL(L, 3, false) CK_RL(L, 4, false)
+    CK_RL_G(6) CK_RL_G(7) CK_RL_G(8)
+#undef CK_RL_G
+#undef CK_RL
     return hipErrorInvalidValue;
 }
 
@@ -950,7 +1151,7 @@ hipError_t launch_quant_rows(int kind, const void* src, int64_t ld, int64_t m, i
         return hipErrorInvalidValue;
     }
     if (kind == IN_BF16_SWIGLU && use_swiglu_tab(m, k, ld, g))
-        return launch_swiglu_tab(static_cast<const uint16_t*>(src), ld, m, k, g, q, s, blocked, st);
+        return launch_swiglu_tab(static_cast<const uint16_t*>(src), ld, m, k, g, q, s, blocked, false, st);
     if (blocked && use_lines(kind, m, k, g)) return launch_lines(src, ld, m, k, g, q, s, st);
     if (blocked && use_stage(kind, m, k, g)) return launch_stage(kind, src, ld, m, k, g, q, s, st);
     switch (kind * 2 + (blocked ? 1 : 0)) {
@@ -969,6 +1170,14 @@ hipError_t launch_rotate_bf16(int kind, const void* src, int64_t ld, int64_t m, 
     if (m == 0) return hipSuccess;
     Launch p;
     if (!plan(m, k, g, blocked, &p)) return hipErrorInvalidValue;
+    const uint16_t* x = static_cast<const uint16_t*>(src);
+    if (blocked && use_rotate_lines(kind, m, k, ld, g))
+        return launch_rotate_lines(kind == IN_BF16_SWIGLU, x, ld, m, k, g, out, st);
+    // row-major SwiGLU: the table kernel where it takes the codes, its output
+    // (twice the bytes of codes) also below 2^31 bytes
+    if (!blocked && kind == IN_BF16_SWIGLU && use_swiglu_tab(m, k, ld, g) &&
+        (m + 255) / 256 * 256 * k * 2 < ((int64_t)1 << 31))
+        return launch_swiglu_tab(x, ld, m, k, g, reinterpret_cast<int8_t*>(out), nullptr, false, true, st);
     switch (kind * 2 + (blocked ? 1 : 0)) {
         case 0: return launch_g<IN_BF16, OUT_ROT_BF16, false>(CK_ARGS, nullptr, nullptr, out);
         case 1: return launch_g<IN_BF16, OUT_ROT_BF16, true>(CK_ARGS, nullptr, nullptr, out);

@@ -171,11 +171,25 @@ def test_act_quant_bit_exact(orc, name):
     np.testing.assert_array_equal(host(q), q_o)
 
 
+def plant_zero_rows(x, k, act):
+    """Rows whose rotation is all zeros, which IEEE sums would leave as -0 in
+    places (the rotation writes +0): row 0 all -0 (act 0) or up = +0 under
+    gates of both signs (act 1, silu(gate) * 0 = +-0), the last row all +0."""
+    x = x.copy()
+    if act == 1:
+        x[0, k:2 * k] = 0
+    else:
+        x[0, :k] = 0x8000
+    x[-1, :] = 0
+    return x
+
+
 @pytest.mark.parametrize("m,k,act,g", [(37, 384, 1, 128), (64, 1024, 0, 256), (9, 512, 1, 64),
                                        (5, 256, 0, 1), (3, 32768, 1, 128)])
 def test_act_rotate_bit_exact(orc, m, k, act, g):
     say(f"act_rotate m={m} k={k} act={act} g={g}")
     d = W.case(m, k, 16, act, seed=m + k)
+    d["x"] = plant_zero_rows(d["x"], k, act)
     u = host(ck.ck_act_rotate_f32(bf16_dev(d["x"]), act, g))
     np.testing.assert_array_equal(u.view(np.uint32), orc.act_rotate(d["x"], act, g).view(np.uint32))
 
@@ -949,6 +963,10 @@ def assert_w8a16_close(orc, got, want, x_rot, wq, sw, k, what, bias=None, residu
 
 ROTATE_CASES = [  # (m, k, act, g)
     (1, 256, 0, 128), (37, 384, 1, 128), (300, 1024, 0, 64), (257, 512, 1, 256), (64, 3072, 1, 128),
+    # from m * k = 2^20 and 512 rows the blocked layout of x comes from the line
+    # kernel: one group per lane with idle group slots (k = 640), two per lane
+    # (ragged m), four at g = 256, a row in five slices, a ragged last slice of two
+    (2049, 640, 0, 64), (1000, 1536, 0, 128), (520, 4096, 0, 256), (600, 5120, 0, 64), (521, 7424, 0, 256),
 ]
 
 
@@ -956,10 +974,38 @@ ROTATE_CASES = [  # (m, k, act, g)
 def test_act_rotate_bf16_bit_exact(orc, m, k, act, g):
     say(f"act_rotate_bf16 m={m} k={k} act={act} g={g}")
     d = W.case(m, k, 16, act, seed=500 + m)
+    if m > 1:
+        d["x"] = plant_zero_rows(d["x"], k, act)
     x = bf16_dev(d["x"])
     want = orc.act_rotate_bf16(d["x"], act, g, k=k)
     np.testing.assert_array_equal(bf16_host(ck.ck_act_rotate_bf16(x, act, g, k=k)), want)
     blk = bf16_host(ck.ck_act_rotate_bf16(x, act, g, k=k, layout="blocked"))
+    np.testing.assert_array_equal(from_blocked_bf16(blk, m), want)
+
+
+# The SwiGLU rotation at sizes where the silu table is built (from m * k =
+# 2^24 with m >= 512, or 2^23 with 8 rows per CU): row-major from the table
+# kernel with one row per workgroup pass (k = 8192), two (k = 4096, m ragged)
+# and four (k = 5120, a ragged last chunk column); blocked from the line kernel
+# with two groups per lane in four slices (k = 8192), one in five slices
+# (k = 5120), three (c5's width, ragged m), and a ragged last slice (k = 7424).  With random
+# inputs a few rotated values cancel to exactly zero at these sizes (the
+# sign-folded butterflies hold them as -0 in half the lanes): they and the
+# planted zero rows check that a zero is written as +0.
+ROTATE_TAB_CASES = [  # (m, k, g)
+    (2048, 8192, 128), (4097, 4096, 64), (2100, 5120, 64), (3001, 12288, 256), (2300, 7424, 256),
+]
+
+
+@pytest.mark.parametrize("m,k,g", ROTATE_TAB_CASES)
+def test_act_rotate_bf16_swiglu_tab_bit_exact(orc, m, k, g):
+    say(f"act_rotate_bf16 swiglu (table kernel) m={m} k={k} g={g}")
+    d = W.case(m, k, 16, 1, seed=510 + m)
+    d["x"] = plant_zero_rows(d["x"], k, 1)
+    x = bf16_dev(d["x"])
+    want = orc.act_rotate_bf16(d["x"], 1, g, k=k)
+    np.testing.assert_array_equal(bf16_host(ck.ck_act_rotate_bf16(x, 1, g, k=k)), want)
+    blk = bf16_host(ck.ck_act_rotate_bf16(x, 1, g, k=k, layout="blocked"))
     np.testing.assert_array_equal(from_blocked_bf16(blk, m), want)
 
 

@@ -488,6 +488,29 @@ def test_rotate_bf16_matches_float64_rotation(orc):
     assert np.all(np.abs(got - ref) <= bound)
 
 
+def test_rotated_zeros_are_positive(orc):
+    """Reading: x H is defined over the reals, so an exact zero of the rotated
+    row is written as +0.  Rows whose every input is -0 (x = -0; SwiGLU with a
+    negative gate and up = +0, silu(gate) * up = -0) sum to -0 in the first
+    output of each group under IEEE addition; the rotation writes +0 there,
+    and leaves a nonzero row's values as they are."""
+    g, k = 4, 8
+    neg0 = np.full((1, k), 0x8000, dtype=np.uint16)
+    gate = orc.f32_to_bf16(np.full((1, k), -1.0, dtype=np.float32))
+    up0 = np.zeros((1, k), dtype=np.uint16)
+    for xb, act in ((neg0, 0), (np.concatenate([gate, up0], axis=1), 1)):
+        u = orc.act_rotate(xb, act, g, k=k)
+        np.testing.assert_array_equal(u.view(np.uint32), np.zeros((1, k), np.uint32))
+        np.testing.assert_array_equal(orc.act_rotate_bf16(xb, act, g, k=k), np.zeros((1, k), np.uint16))
+    # a nonzero row: u = x (sqrt(g) H) exactly for small integers, with +0 where
+    # the sums cancel
+    x = np.array([[1, 1, 1, 1, 3, -1, 2, 0]], dtype=np.float32)
+    u = orc.act_rotate(orc.f32_to_bf16(x), 0, g, k=k)
+    want = (x.reshape(2, 4) @ sylvester_kron(4)).reshape(1, k).astype(np.float32)
+    np.testing.assert_array_equal(u, want)
+    assert not np.signbit(u[0, 1:4]).any() and u[0, 1] == 0
+
+
 def test_w8a16_acc_matches_int64_matmul(orc):
     """Small integer activations (exact in BF16): the accumulator is the
     integer product, computed by numpy int64 matmul."""

@@ -413,18 +413,12 @@ __global__ __launch_bounds__(1024) void quant_lines_kernel(const uint16_t* __res
 // faster than the group order.
 constexpr int kTabThreads = 1024;
 
-// ROT: the W8A16 rotation instead of codes: q is the row-major BF16 output
-// (x_rot = bf16(fl(u * c_g) + 0), as quant_rows_kernel<IN_BF16_SWIGLU, ...,
-// OUT_ROT_BF16> writes it bit for bit), s is unused, and a pass has no absmax,
-// no barrier and no staging.  (The blocked BF16 layout is written by
-// rotate_lines_kernel.)
-template <int LOG_G, int CH, bool BLOCKED, bool STAGE, bool ROT = false>
+template <int LOG_G, int CH, bool BLOCKED, bool STAGE>
 __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
     const uint16_t* __restrict__ src, int64_t ld, int m, int k, int log_t, float cg, int8_t* __restrict__ q,
     float* __restrict__ s)
 {
     static_assert(!STAGE || BLOCKED, "staging is for blocked codes");
-    static_assert(!(BLOCKED && ROT), "the rotation here is row-major");
     constexpr int G = 1 << LOG_G;
     __shared__ float tab[kSiluTabEntries];
     __shared__ float red[2][kTabThreads / 64];
@@ -454,7 +448,7 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
     // has no branches and the compiler can count the loads in flight exactly.
     const __amdgpu_buffer_rsrc_t rs_x =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), (short)0, (int)((int64_t)m * ld * 2), 0x00020000);
-    const int64_t qbytes = (BLOCKED ? (int64_t)((m + 255) / 256 * 256) * k : (int64_t)m * k) * (ROT ? 2 : 1);
+    const int64_t qbytes = BLOCKED ? (int64_t)((m + 255) / 256 * 256) * k : (int64_t)m * k;
     const __amdgpu_buffer_rsrc_t rs_q = __builtin_amdgcn_make_buffer_rsrc(q, (short)0, (int)qbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(s, (short)0, m * 4, 0x00020000);
     typedef int v4i_t __attribute__((ext_vector_type(4)));
@@ -520,20 +514,6 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
                 sigma = fwht_cross_lane_signed<G>(v[j], t);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
-            }
-            if constexpr (ROT) {
-                // x_rot = bf16(fl(sigma u * sigma c_g) + 0) = bf16(fl(u * c_g) + 0)
-                const float cs = cg * sigma;
-                const int row = rp0 + team;
-#pragma unroll
-                for (int j = 0; j < CH; ++j) {
-                    const int c = j * T + t;
-                    const v4i_t w = {(int)rot_bf16x2(v[j][0], v[j][1], cs), (int)rot_bf16x2(v[j][2], v[j][3], cs),
-                                     (int)rot_bf16x2(v[j][4], v[j][5], cs), (int)rot_bf16x2(v[j][6], v[j][7], cs)};
-                    const uint32_t ou = (row < m && c < k8) ? (uint32_t)(((int64_t)row * k + c * 8) * 2) : kBufferOutside;
-                    __builtin_amdgcn_raw_buffer_store_b128(w, rs_q, ou, 0, 0);
-                }
-                continue;
             }
             // T >= 128 here (at most 8 rows per 1024-thread workgroup)
             amax = fmaxf(amax, dpp_xor<1>(amax));
@@ -1036,13 +1016,13 @@ bool use_swiglu_tab(int64_t m, int64_t k, int64_t ld, int g)
     return gs && fits && k >= 1024 && (big || many_rows);
 }
 
-template <int LOG_G, bool BLOCKED, bool STAGE, bool ROT = false>
+template <int LOG_G, bool BLOCKED, bool STAGE>
 hipError_t launch_tab_ch(int ch, dim3 grid, hipStream_t st, const uint16_t* src, int64_t ld, int m, int k,
                          int log_t, float cg, int8_t* q, float* s)
 {
 #define CK_TAB(C)                                                                                               \
     case C:                                                                                                     \
-        hipLaunchKernelGGL((quant_swiglu_tab_kernel<LOG_G, C, BLOCKED, STAGE, ROT>), grid, dim3(kTabThreads), 0, \
+        hipLaunchKernelGGL((quant_swiglu_tab_kernel<LOG_G, C, BLOCKED, STAGE>), grid, dim3(kTabThreads), 0,      \
                            st, src, ld, m, k, log_t, cg, q, s);                                                 \
         break;
     switch (ch) {
@@ -1053,13 +1033,12 @@ hipError_t launch_tab_ch(int ch, dim3 grid, hipStream_t st, const uint16_t* src,
     return hipGetLastError();
 }
 
-// rot: the row-major BF16 rotation into q (s unused) instead of codes and scales
 hipError_t launch_swiglu_tab(const uint16_t* src, int64_t ld, int64_t m, int64_t k, int g, int8_t* q, float* s,
-                             bool blocked, bool rot, hipStream_t st)
+                             bool blocked, hipStream_t st)
 {
     int log_t = 0, ch = 0;
     if (!tab_team(k, &log_t, &ch)) return hipErrorInvalidValue;
-    const bool stage = !rot && blocked && k <= kTabStageMaxK;
+    const bool stage = blocked && k <= kTabStageMaxK;
     const int rpw = kTabThreads >> log_t;
     // staged: aligned groups of 8 rows; otherwise row slots of rpw rows, and
     // a multiple of 8 workgroups (see the slot order in the kernel)
@@ -1071,7 +1050,6 @@ hipError_t launch_swiglu_tab(const uint16_t* src, int64_t ld, int64_t m, int64_t
 #define CK_TAB_ARGS ch, grid, st, src, ld, (int)m, (int)k, log_t, cg, q, s
 #define CK_TAB_G(L)                                                                            \
     if (lg == L) {                                                                             \
-        if (rot) return launch_tab_ch<L, false, false, true>(CK_TAB_ARGS);                     \
         return stage     ? launch_tab_ch<L, true, true>(CK_TAB_ARGS)                           \
                : blocked ? launch_tab_ch<L, true, false>(CK_TAB_ARGS)                          \
                          : launch_tab_ch<L, false, false>(CK_TAB_ARGS);                        \
@@ -1151,7 +1129,7 @@ hipError_t launch_quant_rows(int kind, const void* src, int64_t ld, int64_t m, i
         return hipErrorInvalidValue;
     }
     if (kind == IN_BF16_SWIGLU && use_swiglu_tab(m, k, ld, g))
-        return launch_swiglu_tab(static_cast<const uint16_t*>(src), ld, m, k, g, q, s, blocked, false, st);
+        return launch_swiglu_tab(static_cast<const uint16_t*>(src), ld, m, k, g, q, s, blocked, st);
     if (blocked && use_lines(kind, m, k, g)) return launch_lines(src, ld, m, k, g, q, s, st);
     if (blocked && use_stage(kind, m, k, g)) return launch_stage(kind, src, ld, m, k, g, q, s, st);
     switch (kind * 2 + (blocked ? 1 : 0)) {
@@ -1170,14 +1148,10 @@ hipError_t launch_rotate_bf16(int kind, const void* src, int64_t ld, int64_t m, 
     if (m == 0) return hipSuccess;
     Launch p;
     if (!plan(m, k, g, blocked, &p)) return hipErrorInvalidValue;
-    const uint16_t* x = static_cast<const uint16_t*>(src);
+    // row-major output: the row-wise kernel writes whole rows (the table
+    // kernel's rows took as long: 4096 x 12288 SwiGLU 51.9 against 49.8 us)
     if (blocked && use_rotate_lines(kind, m, k, ld, g))
-        return launch_rotate_lines(kind == IN_BF16_SWIGLU, x, ld, m, k, g, out, st);
-    // row-major SwiGLU: the table kernel where it takes the codes, its output
-    // (twice the bytes of codes) also below 2^31 bytes
-    if (!blocked && kind == IN_BF16_SWIGLU && use_swiglu_tab(m, k, ld, g) &&
-        (m + 255) / 256 * 256 * k * 2 < ((int64_t)1 << 31))
-        return launch_swiglu_tab(x, ld, m, k, g, reinterpret_cast<int8_t*>(out), nullptr, false, true, st);
+        return launch_rotate_lines(kind == IN_BF16_SWIGLU, static_cast<const uint16_t*>(src), ld, m, k, g, out, st);
     switch (kind * 2 + (blocked ? 1 : 0)) {
         case 0: return launch_g<IN_BF16, OUT_ROT_BF16, false>(CK_ARGS, nullptr, nullptr, out);
         case 1: return launch_g<IN_BF16, OUT_ROT_BF16, true>(CK_ARGS, nullptr, nullptr, out);

@@ -983,12 +983,12 @@ def test_act_rotate_bf16_bit_exact(orc, m, k, act, g):
     np.testing.assert_array_equal(from_blocked_bf16(blk, m), want)
 
 
-# The SwiGLU rotation at sizes where the silu table is built (from m * k =
-# 2^24 with m >= 512, or 2^23 with 8 rows per CU): row-major from the table
-# kernel with one row per workgroup pass (k = 8192), two (k = 4096, m ragged)
-# and four (k = 5120, a ragged last chunk column); blocked from the line kernel
-# with two groups per lane in four slices (k = 8192), one in five slices
-# (k = 5120), three (c5's width, ragged m), and a ragged last slice (k = 7424).  With random
+# The SwiGLU rotation at sizes where the blocked layout comes from the line
+# kernel with its silu table (from m * k = 2^24 with m >= 512, or 2^23 with 8
+# rows per CU): two groups per lane in four slices (k = 8192), two in two
+# slices (k = 4096, ragged m), one in five slices (k = 5120), three (c5's
+# width, ragged m), and a ragged last slice (k = 7424); row-major from the
+# row-wise kernel at the same sizes.  With random
 # inputs a few rotated values cancel to exactly zero at these sizes (the
 # sign-folded butterflies hold them as -0 in half the lanes): they and the
 # planted zero rows check that a zero is written as +0.
@@ -1006,6 +1006,33 @@ def test_act_rotate_bf16_swiglu_tab_bit_exact(orc, m, k, g):
     want = orc.act_rotate_bf16(d["x"], 1, g, k=k)
     np.testing.assert_array_equal(bf16_host(ck.ck_act_rotate_bf16(x, 1, g, k=k)), want)
     blk = bf16_host(ck.ck_act_rotate_bf16(x, 1, g, k=k, layout="blocked"))
+    np.testing.assert_array_equal(from_blocked_bf16(blk, m), want)
+
+
+def _random_rotate_shapes(count=32, seed=2027):
+    """Seeded random shapes of the line rotation: x from 512 rows and m * k >=
+    2^20, SwiGLU from 2048 rows (8 per CU) and m * k >= 2^23; k a multiple of
+    the group, up to 8192 (x) or 6144 (SwiGLU)."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < count:
+        act = int(rng.integers(0, 2))
+        g = int(rng.choice([64, 128, 256]))
+        k = g * int(rng.integers(max(1, 1024 // g), (8192 if act == 0 else 6144) // g + 1))
+        lo = 2048 if act else 512
+        m = int(rng.integers(lo, lo + 2200))
+        if m * k >= (1 << 23 if act else 1 << 20):
+            shapes.append((m, k, act, g))
+    return shapes
+
+
+@pytest.mark.parametrize("m,k,act,g", _random_rotate_shapes())
+def test_act_rotate_bf16_random_blocked_bit_exact(orc, m, k, act, g):
+    say(f"act_rotate_bf16 random blocked m={m} k={k} act={act} g={g}")
+    d = W.case(m, k, 16, act, seed=m * 7 + k)
+    x = bf16_dev(d["x"])
+    want = orc.act_rotate_bf16(d["x"], act, g, k=k)
+    blk = bf16_host(ck.ck_act_rotate_bf16(x, act, g, k=k, layout="blocked"))
     np.testing.assert_array_equal(from_blocked_bf16(blk, m), want)
 
 

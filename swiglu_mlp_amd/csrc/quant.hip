@@ -979,7 +979,12 @@ namespace {
 // once per launch, so it takes calls with enough elements per CU.
 // Team of the table kernel: T lanes (a power of two, 128..1024) times CH <= 3
 // chunks covering the row's k / 8 chunks with the fewest idle slots, then
-// the fewest chunks per lane (16 waves of at most 128 VGPRs each).
+// the fewest chunks per lane (16 waves of at most 128 VGPRs each), except
+// that a one-row pass (T = 1024, CH = 1) gives way to two rows of two chunks
+// per lane: 8 values per lane and pass leave the pass's barrier and absmax
+// reduction too little to hide behind (after a MALL flush: 3072 x 8192
+// 34.6 -> 30.7 us, 4096 x 8192 38.3 -> 35.7; at k = 4096, T = 512 with one
+// chunk stays ahead of T = 256 with two, 19.9 against 20.6 us).
 bool tab_team(int64_t k, int* log_t, int* ch)
 {
     const int64_t k8 = k / 8;
@@ -988,7 +993,7 @@ bool tab_team(int64_t k, int* log_t, int* ch)
         for (int c = 1; c <= 3; ++c) {
             const int64_t slots = ((int64_t)1 << lt) * c;
             if (slots < k8) continue;
-            const int64_t score = (slots - k8) * 4 + c;
+            const int64_t score = (slots - k8) * 4 + c + (lt == 10 && c == 1 ? 2 : 0);
             if (best < 0 || score < best) {
                 best = score;
                 *log_t = lt;

@@ -403,7 +403,10 @@ def test_act_quant_blocked(orc, name):
     # k < 1024: the per-row kernel with staged blocked codes
     (32769, 512, 64, "blocked"),
     # m * k in [2^23, 2^24) with at least 8 rows per CU: the table kernel too
-    (4097, 2048, 64, "blocked"), (2048, 4096, 128, "rows"), (3001, 4096, 256, "blocked")])
+    (4097, 2048, 64, "blocked"), (2048, 4096, 128, "rows"), (3001, 4096, 256, "blocked"),
+    # k in (6144, 8192]: two rows of two chunks per lane instead of one-row
+    # passes, with idle chunk slots (k = 7168)
+    (2048, 7168, 64, "rows"), (2313, 7168, 128, "blocked")])
 def test_swiglu_quant_large_calls_bit_exact(orc, m, k, g, layout):
     """Large SwiGLU quantizer calls: codes and scales bit-exact against the
     oracle.  From k = 1024 the persistent kernel whose silu is a table lookup

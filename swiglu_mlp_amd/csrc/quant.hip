@@ -581,7 +581,7 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
 
 // The rotation to BF16 in the blocked layout, written as whole lines (x
 // itself, or SWI: silu(gate) * up of [gate | up] rows, silu from the LDS
-// table as in quant_swiglu_tab_kernel).  In that layout a 128-byte line holds
+// table as in quant_swiglu_tab_kernel when TAB, else silu_f32 itself).  In that layout a 128-byte line holds
 // the 16 bytes of one 8-column chunk of 8 consecutive rows.  The row-wise
 // kernels lay a row's chunks across a workgroup, so a line gathers its pieces
 // from several workgroups at different times, and those partial lines cost
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
 // those lines with the same instruction.  Unit of work: an aligned block of 8
 // rows times a slice of CH * SLOTS consecutive groups; workgroup b takes
 // units b + i * gridDim, with the loads of two units in flight.
-template <int LOG_G, int CH, bool SWI>
+template <int LOG_G, int CH, bool SWI, bool TAB>
 __global__ __launch_bounds__(kTabThreads) void rotate_lines_kernel(const uint16_t* __restrict__ src, int64_t ld,
                                                                    int m, int k, int nsl, float cg,
                                                                    uint16_t* __restrict__ out)
@@ -604,7 +604,8 @@ __global__ __launch_bounds__(kTabThreads) void rotate_lines_kernel(const uint16_
     constexpr int WPB = 8 / RW;                       // waves per 8-row block and group slot
     constexpr int SLOTS = kTabThreads / 64 / WPB;     // group slots of a workgroup
     constexpr int NSG = CH * SLOTS;                   // groups per unit
-    __shared__ float tab[SWI ? kSiluTabEntries : 1];
+    static_assert(SWI || !TAB, "the table is silu's");
+    __shared__ float tab[TAB ? kSiluTabEntries : 1];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int gpos = lane & ((1 << LGL) - 1);         // chunk within the group
@@ -641,7 +642,7 @@ __global__ __launch_bounds__(kTabThreads) void rotate_lines_kernel(const uint16_
     };
     load(0, blockIdx.x);
     load(1, blockIdx.x + nwg);
-    if constexpr (SWI) {
+    if constexpr (TAB) {
         for (int i = threadIdx.x; i < kSiluTabEntries; i += kTabThreads) tab[i] = silu_tab_entry(i);
         __syncthreads();
     }
@@ -663,10 +664,16 @@ __global__ __launch_bounds__(kTabThreads) void rotate_lines_kernel(const uint16_
                                             (uint32_t)ub[h][j][3]};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float y0 = *reinterpret_cast<const float*>(tb + silu_tab_offset<false>(wg[e]));
-                        const float y1 = *reinterpret_cast<const float*>(tb + silu_tab_offset<true>(wg[e]));
-                        const float s0 = gate_clamp(wg[e] << 16) * y0;    // silu_f32, bit for bit
-                        const float s1 = gate_clamp(wg[e] & 0xffff0000u) * y1;
+                        float s0, s1;
+                        if constexpr (TAB) {
+                            const float y0 = *reinterpret_cast<const float*>(tb + silu_tab_offset<false>(wg[e]));
+                            const float y1 = *reinterpret_cast<const float*>(tb + silu_tab_offset<true>(wg[e]));
+                            s0 = gate_clamp(wg[e] << 16) * y0;    // silu_f32, bit for bit
+                            s1 = gate_clamp(wg[e] & 0xffff0000u) * y1;
+                        } else {
+                            s0 = silu_f32(wg[e] << 16);
+                            s1 = silu_f32(wg[e] & 0xffff0000u);
+                        }
                         v[j][2 * e] = s0 * bf16_lo(wu[e]);
                         v[j][2 * e + 1] = s1 * bf16_hi(wu[e]);
                     }
@@ -1065,28 +1072,36 @@ hipError_t launch_swiglu_tab(const uint16_t* src, int64_t ld, int64_t m, int64_t
     return hipErrorInvalidValue;
 }
 
-// The line rotation (blocked BF16 output) for x from m * k = 2^20 with at
-// least 512 rows, and for SwiGLU where the table kernel takes the codes (the
-// table must be repaid as there).  Measured after a MALL flush against the
-// row-wise kernel: x 4096 x 3072 16.6 -> 12.7 us, 2048 x 4096 11.2 -> 8.3,
-// 1024 x 1024 4.8 -> 4.6; SwiGLU 4096 x 12288 94.0 -> 56.0, 2048 x 8192
-// 31.4 -> 21.6.  With fewer rows the units are too few for the CUs (256 x
-// 4096: 5.8 against 4.6 us).
-bool use_rotate_lines(int kind, int64_t m, int64_t k, int64_t ld, int g)
+// Which line rotation (blocked BF16 output) a call takes: 0 none, 1 x, 2
+// SwiGLU with the silu table, 3 SwiGLU with silu_f32 itself.  x from m * k =
+// 2^20 with at least 512 rows; SwiGLU with the table where the table kernel
+// takes the codes (the table must be repaid as there), else from m * k = 2^22
+// with at least 1024 rows.  Measured after a MALL flush against the row-wise
+// kernel: x 4096 x 3072 16.6 -> 12.7 us, 2048 x 4096 11.2 -> 8.3, 1024 x 1024
+// 4.8 -> 4.6; SwiGLU 4096 x 12288 94.0 -> 56.0 (the table's 56.2 against 59.3
+// without it), 2048 x 8192 31.4 -> 21.6; without the table 2048 x 3072
+// 11.4 -> 10.8, 1024 x 12288 21.2 -> 18.9.  With fewer rows the units are too
+// few for the CUs (x 256 x 4096: 5.8 against 4.6 us; SwiGLU 1024 x 3072: 8.4
+// against 8.0).
+int rotate_lines_mode(int kind, int64_t m, int64_t k, int64_t ld, int g)
 {
     const bool gs = g == 64 || g == 128 || g == 256;
     const bool fits = m * ld * 2 < ((int64_t)1 << 31) && (m + 255) / 256 * 256 * k * 2 < ((int64_t)1 << 31);
-    if (!gs || !fits) return false;
-    if (kind == IN_BF16) return m >= 512 && m * k >= ((int64_t)1 << 20);
-    return kind == IN_BF16_SWIGLU && use_swiglu_tab(m, k, ld, g);
+    if (!gs || !fits) return 0;
+    if (kind == IN_BF16) return m >= 512 && m * k >= ((int64_t)1 << 20) ? 1 : 0;
+    if (kind != IN_BF16_SWIGLU) return 0;
+    if (use_swiglu_tab(m, k, ld, g)) return 2;
+    return m >= 1024 && m * k >= ((int64_t)1 << 22) ? 3 : 0;
 }
 
 // Groups per lane and unit: the fewest idle group slots over a row's slices,
 // then the most groups per unit (at most 3 with SwiGLU, whose two inputs
 // double the registers in flight, else 4).
-hipError_t launch_rotate_lines(bool swi, const uint16_t* src, int64_t ld, int64_t m, int64_t k, int g,
+// mode as rotate_lines_mode (1, 2 or 3)
+hipError_t launch_rotate_lines(int mode, const uint16_t* src, int64_t ld, int64_t m, int64_t k, int g,
                                uint16_t* out, hipStream_t st)
 {
+    const bool swi = mode >= 2;
     const int lg = g == 64 ? 6 : g == 128 ? 7 : 8;
     const int slots = 16 / (8 / (64 >> (lg - 3)));
     const int64_t ng = k / g;
@@ -1104,14 +1119,14 @@ hipError_t launch_rotate_lines(bool swi, const uint16_t* src, int64_t ld, int64_
     const int64_t units = (m + 7) / 8 * nsl;
     const dim3 grid((unsigned)std::min<int64_t>(units, num_cus()));
     const float cg = (float)(1.0 / sqrt((double)g));
-#define CK_RL(L, C, S)                                                                                     \
-    if (lg == L && ch == C && swi == S) {                                                                  \
-        hipLaunchKernelGGL((rotate_lines_kernel<L, C, S>), grid, dim3(kTabThreads), 0, st, src, ld, (int)m, \
-                           (int)k, (int)nsl, cg, out);                                                     \
-        return hipGetLastError();                                                                          \
+#define CK_RL(L, C, MODE)                                                                                \
+    if (lg == L && ch == C && mode == MODE) {                                                            \
+        hipLaunchKernelGGL((rotate_lines_kernel<L, C, (MODE >= 2), (MODE == 2)>), grid, dim3(kTabThreads), 0, st, \
+                           src, ld, (int)m, (int)k, (int)nsl, cg, out);                                  \
+        return hipGetLastError();                                                                        \
     }
-#define CK_RL_G(L) CK_RL(L, 1, true) CK_RL(L, 2, true) CK_RL(L, 3, true) \
-    CK_RL(L, 1, false) CK_RL(L, 2, false) CK_RL(L, 3, false) CK_RL(L, 4, false)
+#define CK_RL_G(L) CK_RL(L, 1, 1) CK_RL(L, 2, 1) CK_RL(L, 3, 1) CK_RL(L, 4, 1) \
+    CK_RL(L, 1, 2) CK_RL(L, 2, 2) CK_RL(L, 3, 2) CK_RL(L, 1, 3) CK_RL(L, 2, 3) CK_RL(L, 3, 3)
     CK_RL_G(6) CK_RL_G(7) CK_RL_G(8)
 #undef CK_RL_G
 #undef CK_RL
@@ -1155,8 +1170,8 @@ hipError_t launch_rotate_bf16(int kind, const void* src, int64_t ld, int64_t m, 
     if (!plan(m, k, g, blocked, &p)) return hipErrorInvalidValue;
     // row-major output: the row-wise kernel writes whole rows (the table
     // kernel's rows took as long: 4096 x 12288 SwiGLU 51.9 against 49.8 us)
-    if (blocked && use_rotate_lines(kind, m, k, ld, g))
-        return launch_rotate_lines(kind == IN_BF16_SWIGLU, static_cast<const uint16_t*>(src), ld, m, k, g, out, st);
+    const int lines = blocked ? rotate_lines_mode(kind, m, k, ld, g) : 0;
+    if (lines) return launch_rotate_lines(lines, static_cast<const uint16_t*>(src), ld, m, k, g, out, st);
     switch (kind * 2 + (blocked ? 1 : 0)) {
         case 0: return launch_g<IN_BF16, OUT_ROT_BF16, false>(CK_ARGS, nullptr, nullptr, out);
         case 1: return launch_g<IN_BF16, OUT_ROT_BF16, true>(CK_ARGS, nullptr, nullptr, out);

@@ -970,6 +970,9 @@ ROTATE_CASES = [  # (m, k, act, g)
     # kernel: one group per lane with idle group slots (k = 640), two per lane
     # (ragged m), four at g = 256, a row in five slices, a ragged last slice of two
     (2049, 640, 0, 64), (1000, 1536, 0, 128), (520, 4096, 0, 256), (600, 5120, 0, 64), (521, 7424, 0, 256),
+    # SwiGLU from m * k = 2^22 and 1024 rows, below the silu table's sizes: the
+    # line kernel with silu_f32 itself (c2's shape; g = 64 and 256, ragged m)
+    (2048, 3072, 1, 128), (1100, 4096, 1, 64), (1501, 5120, 1, 256),
 ]
 
 
@@ -1014,17 +1017,17 @@ def test_act_rotate_bf16_swiglu_tab_bit_exact(orc, m, k, g):
 
 def _random_rotate_shapes(count=32, seed=2027):
     """Seeded random shapes of the line rotation: x from 512 rows and m * k >=
-    2^20, SwiGLU from 2048 rows (8 per CU) and m * k >= 2^23; k a multiple of
-    the group, up to 8192 (x) or 6144 (SwiGLU)."""
+    2^20; SwiGLU from 1024 rows and m * k >= 2^22 (with and without the silu
+    table); k a multiple of the group, up to 8192 (x) or 6144 (SwiGLU)."""
     rng = np.random.default_rng(seed)
     shapes = []
     while len(shapes) < count:
         act = int(rng.integers(0, 2))
         g = int(rng.choice([64, 128, 256]))
         k = g * int(rng.integers(max(1, 1024 // g), (8192 if act == 0 else 6144) // g + 1))
-        lo = 2048 if act else 512
-        m = int(rng.integers(lo, lo + 2200))
-        if m * k >= (1 << 23 if act else 1 << 20):
+        lo = 1024 if act else 512
+        m = int(rng.integers(lo, lo + 3000))
+        if m * k >= (1 << 22 if act else 1 << 20):
             shapes.append((m, k, act, g))
     return shapes
 

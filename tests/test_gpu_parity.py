@@ -1015,6 +1015,44 @@ def test_act_rotate_bf16_swiglu_tab_bit_exact(orc, m, k, g):
     np.testing.assert_array_equal(from_blocked_bf16(blk, m), want)
 
 
+@pytest.mark.parametrize("m,k,act,g,pad,layout", [
+    (300, 1024, 0, 128, 32, "rows"),          # the per-row kernel
+    (2048, 3072, 0, 128, 64, "blocked"),      # the line quantizer
+    (4096, 4096, 0, 64, 16, "blocked"),       # staged per-row codes
+    (2100, 8192, 1, 128, 128, "blocked"),     # the table kernel, staged
+    (2048, 4096, 1, 64, 8, "rows"),           # the table kernel, row-major codes
+])
+def test_act_quant_padded_rows_bit_exact(orc, m, k, act, g, pad, layout):
+    """Rows with a leading dimension past their values (ldx = k or 2k, plus
+    pad, NaN in the padding) through each quantizer kernel."""
+    say(f"act_quant padded rows m={m} k={k} act={act} g={g} pad={pad} {layout}")
+    d = W.case(m, k, 16, act, seed=540 + m)
+    width = d["x"].shape[1]
+    xp = np.full((m, width + pad), 0x7FC0, dtype=np.uint16)
+    xp[:, :width] = d["x"]
+    q_o, s_o = orc.act_quant(d["x"], act, g, k=k)
+    q, sc = ck.ck_act_quant(bf16_dev(xp), act, g, k=k, layout=layout)
+    q = host(q)
+    np.testing.assert_array_equal(host(sc).reshape(-1).view(np.uint32), s_o.view(np.uint32))
+    np.testing.assert_array_equal(q if layout == "rows" else from_blocked(q, m), q_o)
+
+
+@pytest.mark.parametrize("m,k,act,g,pad", [(600, 2048, 0, 128, 64), (1100, 4096, 1, 64, 128),
+                                           (2100, 4096, 1, 256, 8)])
+def test_act_rotate_bf16_padded_rows_bit_exact(orc, m, k, act, g, pad):
+    """Rows with a leading dimension past their values (ldx = k or 2k, plus
+    pad) on the line kernel: x, and SwiGLU without and with the silu table."""
+    say(f"act_rotate_bf16 padded rows m={m} k={k} act={act} g={g} pad={pad}")
+    d = W.case(m, k, 16, act, seed=530 + m)
+    width = d["x"].shape[1]
+    xp = np.full((m, width + pad), 0x7FC0, dtype=np.uint16)     # NaN in the padding
+    xp[:, :width] = d["x"]
+    want = orc.act_rotate_bf16(xp, act, g, k=k)
+    np.testing.assert_array_equal(want, orc.act_rotate_bf16(d["x"], act, g, k=k))
+    blk = bf16_host(ck.ck_act_rotate_bf16(bf16_dev(xp), act, g, k=k, layout="blocked"))
+    np.testing.assert_array_equal(from_blocked_bf16(blk, m), want)
+
+
 def _random_rotate_shapes(count=32, seed=2027):
     """Seeded random shapes of the line rotation: x from 512 rows and m * k >=
     2^20; SwiGLU from 1024 rows and m * k >= 2^22 (with and without the silu

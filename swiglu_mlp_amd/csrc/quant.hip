@@ -398,10 +398,14 @@ __global__ __launch_bounds__(1024) void quant_lines_kernel(const uint16_t* __res
 // quant_rows_kernel<IN_BF16_SWIGLU, ..., OUT_CODES> bit for bit.
 //
 // STAGE (blocked codes, k <= kTabStageMaxK): rows are taken in aligned groups
-// of 8 (group i of the workgroup is blockIdx + i * gridDim), each in 8 / rpw
-// passes of rpw = 1024 / T rows; a group's codes are assembled in LDS (laid
-// out as in quant_rows_kernel) and written as whole 128-byte lines after its
-// last pass.  Otherwise pass p of the workgroup takes rpw rows of row slot
+// of 8, last group first (group i of the workgroup is the (blockIdx + i *
+// gridDim)-th from the end), each in 8 / rpw passes of rpw = 1024 / T rows; a
+// group's codes are assembled in LDS (laid out as in quant_rows_kernel) and
+// written as whole 128-byte lines after its last pass.  Last rows first: in
+// the MLP the gate_up GEMM writes its rows in ascending bands just before, so
+// the rows it wrote last are the likeliest still to sit in the MALL (c5's
+// block, back to back: 432.9 -> 431.0 us per step, lower in 9 of 10 paired
+// rounds).  Otherwise pass p of the workgroup takes rpw rows of row slot
 // p * gridDim + (an XCD-grouped index of blockIdx): in each pass the
 // workgroups together read one contiguous band of rows, and the workgroups
 // of one XCD take consecutive slots, so the 8 rows that share a 128-byte line
@@ -431,9 +435,14 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
     const int nwg = gridDim.x;
     const int k8 = k >> 3;
     const char* tb = reinterpret_cast<const char*>(tab) - kSiluTabBias;   // see silu_tab_offset
-    // STAGE: first row of the 8-row group of pass p (uniform); the pass ends
-    // the group when its index within the group is the last one
-    auto group_row = [&](int p) { return (blockIdx.x + (p >> lppg) * nwg) * 8; };
+    // STAGE: first row of the 8-row group of pass p (uniform; past m when the
+    // workgroup has no group left); the pass ends the group when its index
+    // within the group is the last one
+    const int ng8 = (m + 7) >> 3;
+    auto group_row = [&](int p) {
+        const int gi = blockIdx.x + (p >> lppg) * nwg;
+        return gi < ng8 ? (ng8 - 1 - gi) * 8 : m + 8;
+    };
     const int slot0 = ((blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3)) * rpw;
     // first row of pass p (uniform), and whether pass p has rows to do
     auto pass_row = [&](int p) {

@@ -404,8 +404,8 @@ __global__ __launch_bounds__(1024) void quant_lines_kernel(const uint16_t* __res
 // written as whole 128-byte lines after its last pass.  Last rows first: in
 // the MLP the gate_up GEMM writes its rows in ascending bands just before, so
 // the rows it wrote last are the likeliest still to sit in the MALL (c5's
-// block, back to back: 432.9 -> 431.0 us per step, lower in 9 of 10 paired
-// rounds).  Otherwise pass p of the workgroup takes rpw rows of row slot
+// block, back to back, paired rounds on two boxes: 1.9 us per step faster in
+// 9 of 10 on one, 0.4 us in 11 of 22 (one tie) on the other).  Otherwise pass p of the workgroup takes rpw rows of row slot
 // p * gridDim + (an XCD-grouped index of blockIdx): in each pass the
 // workgroups together read one contiguous band of rows, and the workgroups
 // of one XCD take consecutive slots, so the 8 rows that share a 128-byte line

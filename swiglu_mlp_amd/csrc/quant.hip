@@ -1028,13 +1028,21 @@ bool tab_team(int64_t k, int* log_t, int* ch)
 // box-to-box spread (11.0 against 11.3 us on one box, 12.0 against 11.4 on
 // another), and with fewer rows per CU the per-row kernel is ahead (1024 x 3072
 // 7.8 against 9.4, 512 x 12288 12.5 against 20.3 us).
+bool swiglu_tab_pays(int64_t m, int64_t k)
+{
+    const bool big = m >= 512 && m * k >= ((int64_t)1 << 24);
+    const bool many_rows = m >= 8 * (int64_t)num_cus() && m * k >= ((int64_t)1 << 23);
+    return k >= 1024 && (big || many_rows);
+}
+
+// The table quantizer also needs a team for the row: k <= 24576 (at most
+// 1024 lanes of 3 chunks); longer rows take the per-row kernel.
 bool use_swiglu_tab(int64_t m, int64_t k, int64_t ld, int g)
 {
     const bool gs = g == 64 || g == 128 || g == 256;
     const bool fits = m * ld * 2 < ((int64_t)1 << 31) && (m + 255) / 256 * 256 * k < ((int64_t)1 << 31);
-    const bool big = m >= 512 && m * k >= ((int64_t)1 << 24);
-    const bool many_rows = m >= 8 * (int64_t)num_cus() && m * k >= ((int64_t)1 << 23);
-    return gs && fits && k >= 1024 && (big || many_rows);
+    int log_t = 0, ch = 0;
+    return gs && fits && swiglu_tab_pays(m, k) && tab_team(k, &log_t, &ch);
 }
 
 template <int LOG_G, bool BLOCKED, bool STAGE>
@@ -1083,9 +1091,9 @@ hipError_t launch_swiglu_tab(const uint16_t* src, int64_t ld, int64_t m, int64_t
 
 // Which line rotation (blocked BF16 output) a call takes: 0 none, 1 x, 2
 // SwiGLU with the silu table, 3 SwiGLU with silu_f32 itself.  x from m * k =
-// 2^20 with at least 512 rows; SwiGLU with the table where the table kernel
-// takes the codes (the table must be repaid as there), else from m * k = 2^22
-// with at least 1024 rows.  Measured after a MALL flush against the row-wise
+// 2^20 with at least 512 rows; SwiGLU with the table at the sizes where the
+// table kernel takes the codes (the table must be repaid as there), else from
+// m * k = 2^22 with at least 1024 rows.  Measured after a MALL flush against the row-wise
 // kernel: x 4096 x 3072 16.6 -> 12.7 us, 2048 x 4096 11.2 -> 8.3, 1024 x 1024
 // 4.8 -> 4.6; SwiGLU 4096 x 12288 94.0 -> 56.0 (the table's 56.2 against 59.3
 // without it), 2048 x 8192 31.4 -> 21.6; without the table 2048 x 3072
@@ -1099,7 +1107,7 @@ int rotate_lines_mode(int kind, int64_t m, int64_t k, int64_t ld, int g)
     if (!gs || !fits) return 0;
     if (kind == IN_BF16) return m >= 512 && m * k >= ((int64_t)1 << 20) ? 1 : 0;
     if (kind != IN_BF16_SWIGLU) return 0;
-    if (use_swiglu_tab(m, k, ld, g)) return 2;
+    if (swiglu_tab_pays(m, k)) return 2;
     return m >= 1024 && m * k >= ((int64_t)1 << 22) ? 3 : 0;
 }
 

@@ -406,7 +406,10 @@ def test_act_quant_blocked(orc, name):
     (4097, 2048, 64, "blocked"), (2048, 4096, 128, "rows"), (3001, 4096, 256, "blocked"),
     # k in (6144, 8192]: two rows of two chunks per lane instead of one-row
     # passes, with idle chunk slots (k = 7168)
-    (2048, 7168, 64, "rows"), (2313, 7168, 128, "blocked")])
+    (2048, 7168, 64, "rows"), (2313, 7168, 128, "blocked"),
+    # table sizes with rows past the table kernel's team (k > 24576, up to
+    # CK_MAX_K): the per-row kernel
+    (512, 32768, 128, "blocked"), (700, 26624, 256, "rows")])
 def test_swiglu_quant_large_calls_bit_exact(orc, m, k, g, layout):
     """Large SwiGLU quantizer calls: codes and scales bit-exact against the
     oracle.  From k = 1024 the persistent kernel whose silu is a table lookup
@@ -1000,6 +1003,7 @@ def test_act_rotate_bf16_bit_exact(orc, m, k, act, g):
 # planted zero rows check that a zero is written as +0.
 ROTATE_TAB_CASES = [  # (m, k, g)
     (2048, 8192, 128), (4097, 4096, 64), (2100, 5120, 64), (3001, 12288, 256), (2300, 7424, 256),
+    (512, 32768, 128),   # CK_MAX_K
 ]
 
 

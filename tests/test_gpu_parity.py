@@ -976,6 +976,8 @@ ROTATE_CASES = [  # (m, k, act, g)
     # SwiGLU from m * k = 2^22 and 1024 rows, below the silu table's sizes: the
     # line kernel with silu_f32 itself (c2's shape; g = 64 and 256, ragged m)
     (2048, 3072, 1, 128), (1100, 4096, 1, 64), (1501, 5120, 1, 256),
+    # short rows on the line kernel: fewer groups than a workgroup has slots
+    (2048, 512, 0, 64), (4096, 256, 0, 256), (8192, 512, 1, 128),
 ]
 
 

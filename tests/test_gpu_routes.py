@@ -165,3 +165,31 @@ def test_mlp_routes(orc, h):
                     np.testing.assert_array_equal(got, want, err_msg=what)
                     checked += 1
     say(f"h={h}: {calls} calls, {checked} compared with the oracle")
+
+
+@pytest.mark.parametrize("k", [128, 1024, 3072, 12288, 32768])
+def test_w8a16_linear_routes(orc, k):
+    """The W8A16 linear's routes (the rotation inside the few-row GEMM, the
+    weight-streaming and the tiled GEMMs, both rotation kernels): every call
+    succeeds and gives finite outputs (its parity against the derived bound
+    is in test_gpu_parity.py)."""
+    g = 128
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(17 + k)
+    calls = 0
+    for n in (16, 128, 1024, 4112, 24576):
+        if n * k > (1 << 28):
+            continue
+        wq = torch.randint(-127, 128, (n, k), device=DEV, generator=gen, dtype=torch.int32).to(torch.int8)
+        sw = (torch.rand(n, device=DEV, generator=gen) * 1e-3 + 1e-4).float()
+        wb = ck.ck_weight_pack(wq)
+        for m, act in itertools.product((1, 2, 3, 16, 64, 65, 512, 2048, 4096), (0, 1)):
+            ld = 2 * k if act else k
+            if m * ld * 2 >= (1 << 30) or m * n * 2 >= (1 << 30):
+                continue
+            x = (torch.randn(m, ld, device=DEV, generator=gen) * 2).to(torch.bfloat16)
+            y = ck.ck_int8_linear_w8a16(x, wb, sw, g, act)
+            torch.cuda.synchronize()
+            calls += 1
+            assert np.isfinite(orc.bf16_to_f32(u16(y))).all(), f"m={m} k={k} n={n} act={act}"
+    say(f"w8a16 k={k}: {calls} calls")

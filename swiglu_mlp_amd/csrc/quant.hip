@@ -405,8 +405,10 @@ __global__ __launch_bounds__(1024) void quant_lines_kernel(const uint16_t* __res
 // the MLP the gate_up GEMM writes its rows in ascending bands just before, so
 // the rows it wrote last are the likeliest still to sit in the MALL (c5's
 // block, back to back, paired rounds on two boxes: 1.9 us per step faster in
-// 9 of 10 on one, 0.4 us in 11 of 22 (one tie) on the other).  Otherwise pass p of the workgroup takes rpw rows of row slot
-// p * gridDim + (an XCD-grouped index of blockIdx): in each pass the
+// 9 of 10 on one, 0.4 us in 11 of 22 (one tie) on the other).
+//
+// Otherwise pass p of the workgroup takes rpw rows of row slot p * gridDim +
+// (an XCD-grouped index of blockIdx): in each pass the
 // workgroups together read one contiguous band of rows, and the workgroups
 // of one XCD take consecutive slots, so the 8 rows that share a 128-byte line
 // of unstaged blocked codes are written from one L2 (the grid is a multiple
@@ -576,7 +578,8 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
                     const uint32_t base = (uint32_t)((int64_t)(row0 >> 5) * kb * 1024) + ((row0 >> 3) & 3) * 128;
                     for (int u = threadIdx.x; u < kb * 16; u += kTabThreads) {
                         const int r8 = u & 7;
-                        const v4i_t w = *reinterpret_cast<const v4i_t*>(stage + (u >> 4) * kStageKbBytes + (u & 15) * 16);
+                        const v4i_t w =
+                            *reinterpret_cast<const v4i_t*>(stage + (u >> 4) * kStageKbBytes + (u & 15) * 16);
                         const uint32_t off = row0 + r8 < m
                             ? base + (uint32_t)(u >> 4) * 1024u + (uint32_t)((u >> 3) & 1) * 512u + (uint32_t)r8 * 16u
                             : kBufferOutside;
@@ -590,8 +593,9 @@ __global__ __launch_bounds__(kTabThreads) void quant_swiglu_tab_kernel(
 
 // The rotation to BF16 in the blocked layout, written as whole lines (x
 // itself, or SWI: silu(gate) * up of [gate | up] rows, silu from the LDS
-// table as in quant_swiglu_tab_kernel when TAB, else silu_f32 itself).  In that layout a 128-byte line holds
-// the 16 bytes of one 8-column chunk of 8 consecutive rows.  The row-wise
+// table as in quant_swiglu_tab_kernel when TAB, else silu_f32 itself).  In
+// that layout a 128-byte line holds the 16 bytes of one 8-column chunk of 8
+// consecutive rows.  The row-wise
 // kernels lay a row's chunks across a workgroup, so a line gathers its pieces
 // from several workgroups at different times, and those partial lines cost
 // more than the reads (the SwiGLU rotation of 4096 x 12288, after a MALL
@@ -710,7 +714,8 @@ __global__ __launch_bounds__(kTabThreads) void rotate_lines_kernel(const uint16_
                 const int c = (gi << LGL) + gpos;
                 const v4i_t w = {(int)rot_bf16x2(v[j][0], v[j][1], cs), (int)rot_bf16x2(v[j][2], v[j][3], cs),
                                  (int)rot_bf16x2(v[j][4], v[j][5], cs), (int)rot_bf16x2(v[j][6], v[j][7], cs)};
-                const uint32_t oo = (row < m && gi < ng) ? (uint32_t)blocked_bf16_offset(row, c, k >> 5) : kBufferOutside;
+                const uint32_t oo =
+                    (row < m && gi < ng) ? (uint32_t)blocked_bf16_offset(row, c, k >> 5) : kBufferOutside;
                 __builtin_amdgcn_raw_buffer_store_b128(w, rs_o, oo, 0, 0);
             }
         }

@@ -193,3 +193,38 @@ def test_w8a16_linear_routes(orc, k):
             calls += 1
             assert np.isfinite(orc.bf16_to_f32(u16(y))).all(), f"m={m} k={k} n={n} act={act}"
     say(f"w8a16 k={k}: {calls} calls")
+
+
+@pytest.mark.parametrize("g", [64, 128, 256])
+def test_weight_prep_and_rotate_f32_routes(orc, g):
+    """Weight preparation (rows and blocked codes) and the FP32 rotation
+    diagnostic over n, k grids: every call succeeds, the small ones bit-exact."""
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(19 + g)
+    calls = checked = 0
+    for k in sorted({g, 1024, 3072, 12288, 32768}):
+        for n in (16, 48, 300, 4112, 24576):
+            if n * k > (1 << 28):
+                continue
+            w = (torch.randn(n, k, device=DEV, generator=gen) * 0.02).float()
+            small = n * k <= (1 << 22)
+            for lay in ("rows", "blocked"):
+                wq, sw = ck.ck_weight_prep(w, g, layout=lay)
+                torch.cuda.synchronize()
+                calls += 1
+                if small:
+                    q_o, s_o = orc.weight_prep(w.cpu().numpy(), g)
+                    qh = wq.cpu().numpy()
+                    qh = qh if lay == "rows" else from_blocked(qh, n)
+                    np.testing.assert_array_equal(qh, q_o, err_msg=f"n={n} k={k} g={g} {lay}")
+                    np.testing.assert_array_equal(sw.cpu().numpy().reshape(-1).view(np.uint32), s_o.view(np.uint32))
+                    checked += 1
+            x = (torch.randn(min(n, 2048), k, device=DEV, generator=gen) * 2).to(torch.bfloat16)
+            u = ck.ck_act_rotate_f32(x, 0, g)
+            torch.cuda.synchronize()
+            calls += 1
+            if x.shape[0] * k <= (1 << 22):
+                np.testing.assert_array_equal(u.cpu().numpy().view(np.uint32),
+                                              orc.act_rotate(u16(x), 0, g).view(np.uint32))
+                checked += 1
+    say(f"g={g}: {calls} calls, {checked} compared with the oracle")

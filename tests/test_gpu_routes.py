@@ -111,20 +111,27 @@ def test_linear_routes(orc, k):
             if m * ld * 2 >= (1 << 30) or m * n * 2 >= (1 << 30):
                 continue
             x = (torch.randn(m, ld, device=DEV, generator=gen) * 2).to(torch.bfloat16)
+            bias = torch.randn(n, device=DEV, generator=gen).float()
+            res = torch.randn(m, n, device=DEV, generator=gen).to(torch.bfloat16)
             small = m * n * k <= (1 << 27) and m * k <= (1 << 22)
-            want = None
+            want = want_br = None
             if small:
                 q_o, s_o = orc.act_quant(u16(x), act, g, k=k)
-                want = orc.epilogue(orc.gemm_i32(q_o, wq_h), s_o, sw_h)
+                acc = orc.gemm_i32(q_o, wq_h)
+                want = orc.epilogue(acc, s_o, sw_h)
+                want_br = orc.epilogue(acc, s_o, sw_h, bias.cpu().numpy(), u16(res))
             for lay, (w, s) in weights.items():
                 if lay == "decode" and (m > 64 or w is None):
                     continue
                 y = ck.ck_int8_linear(x, w, s, g, act, layout=lay)
+                y_br = ck.ck_int8_linear(x, w, s, g, act, layout=lay, bias=bias, residual=res)
                 torch.cuda.synchronize()
-                calls += 1
+                calls += 2
                 if small:
-                    np.testing.assert_array_equal(u16(y), want, err_msg=f"m={m} k={k} n={n} act={act} {lay}")
-                    checked += 1
+                    what = f"m={m} k={k} n={n} act={act} {lay}"
+                    np.testing.assert_array_equal(u16(y), want, err_msg=what)
+                    np.testing.assert_array_equal(u16(y_br), want_br, err_msg=what + " + bias + residual")
+                    checked += 2
     say(f"k={k}: {calls} calls, {checked} compared with the oracle")
 
 

@@ -1262,8 +1262,8 @@ def test_calls_replay_bit_exact_from_a_hip_graph():
     synchronisation), so a call sequence can be captured into a HIP graph.
     Each replay, with new inputs copied in eagerly between replays, must match
     the eager calls bit for bit."""
-    say("graph capture: ck_swiglu_mlp (decode, m=1; blocked, m=2) + ck_swiglu_mlp_w8a16 (m=1) + "
-        "ck_int8_linear (blocked, m=300)")
+    say("graph capture: ck_swiglu_mlp (decode, m=1; blocked, m=2 and 2048) + ck_swiglu_mlp_w8a16 (m=1 and "
+        "2048) + ck_int8_linear (blocked, m=300)")
     g = 128
     rng = np.random.default_rng(17)
     h, i = 1024, 2816
@@ -1284,12 +1284,26 @@ def test_calls_replay_bit_exact_from_a_hip_graph():
     y4 = torch.empty((1, h), dtype=torch.bfloat16, device=DEV)
     ws3 = torch.empty(ck.lib().ck_swiglu_mlp_workspace_size(2, h, i), dtype=torch.uint8, device=DEV)
     ws4 = torch.empty(ck.lib().ck_swiglu_mlp_w8a16_workspace_size(1, h, i), dtype=torch.uint8, device=DEV)
+    # m = 2048 with i = 8192: the line x quantizer, the staged table quantizer
+    # and the large-tile GEMMs; in W8A16 both line rotations (x, SwiGLU with
+    # the silu table)
+    i5 = 8192
+    gq5, gs5 = prep_rows(dev((0.02 * rng.standard_normal((2 * i5, h))).astype(np.float32)), g)
+    dq5, ds5 = prep_rows(dev((0.01 * rng.standard_normal((h, i5))).astype(np.float32)), g)
+    bgu5, bd5 = ck.ck_weight_pack(gq5), ck.ck_weight_pack(dq5)
+    x5 = torch.zeros((2048, h), dtype=torch.bfloat16, device=DEV)
+    y5 = torch.empty((2048, h), dtype=torch.bfloat16, device=DEV)
+    y6 = torch.empty((2048, h), dtype=torch.bfloat16, device=DEV)
+    ws5 = torch.empty(ck.lib().ck_swiglu_mlp_workspace_size(2048, h, i5), dtype=torch.uint8, device=DEV)
+    ws6 = torch.empty(ck.lib().ck_swiglu_mlp_w8a16_workspace_size(2048, h, i5), dtype=torch.uint8, device=DEV)
 
     def calls():
         ck.ck_swiglu_mlp(x1, dgu, None, dd, None, g, out=y1, workspace=ws1, layout="decode")
         ck.ck_int8_linear(x2, wlb, sl, g, out=y2, workspace=ws2, layout="blocked")
         ck.ck_swiglu_mlp(x3, bgu, gs, bd, ds, g, out=y3, workspace=ws3, layout="blocked")
         ck.ck_swiglu_mlp_w8a16(x1, bgu, gs, bd, ds, g, out=y4, workspace=ws4)
+        ck.ck_swiglu_mlp(x5, bgu5, gs5, bd5, ds5, g, out=y5, workspace=ws5, layout="blocked")
+        ck.ck_swiglu_mlp_w8a16(x5, bgu5, gs5, bd5, ds5, g, out=y6, workspace=ws6)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -1305,12 +1319,14 @@ def test_calls_replay_bit_exact_from_a_hip_graph():
         x1.copy_(torch.from_numpy(a1).to(DEV).to(torch.bfloat16))
         x2.copy_(torch.from_numpy(a2).to(DEV).to(torch.bfloat16))
         x3.copy_(torch.from_numpy(rng.standard_normal((2, h)).astype(np.float32)).to(DEV).to(torch.bfloat16))
+        x5.copy_(torch.from_numpy(rng.standard_normal((2048, h)).astype(np.float32)).to(DEV).to(torch.bfloat16))
         graph.replay()
         torch.cuda.synchronize()
-        got = [t.clone() for t in (y1, y2, y3, y4)]
+        got = [t.clone() for t in (y1, y2, y3, y4, y5, y6)]
         calls()                                   # eager reference on the same inputs
         torch.cuda.synchronize()
-        for what, gt, want in zip(("mlp decode", "linear", "mlp blocked", "mlp w8a16"), got, (y1, y2, y3, y4)):
+        for what, gt, want in zip(("mlp decode", "linear", "mlp blocked", "mlp w8a16", "mlp blocked m=2048",
+                                   "mlp w8a16 m=2048"), got, (y1, y2, y3, y4, y5, y6)):
             assert torch.equal(gt.view(torch.int16), want.view(torch.int16)), f"replay {rep}: {what} differs"
             assert gt.abs().sum() > 0, f"replay {rep}: {what} is all zeros"
 

@@ -174,22 +174,37 @@ def test_mlp_routes(orc, h):
     say(f"h={h}: {calls} calls, {checked} compared with the oracle")
 
 
+def w8a16_within_bound(orc, got, ref, wq, sw, k):
+    """|got - oracle| within the derived bound of FP32 accumulation in any
+    order (gamma_k * sum |x q| * s_w), the epilogue's FP32 rounding and one
+    BF16 ulp, element by element."""
+    u = 2.0 ** -24
+    gamma = k * u / (1 - k * u)
+    s_abs = orc.w8a16_abs_acc(ref["x_rot"], wq) * sw.astype(np.float64)[None, :]
+    t = np.abs(orc.w8a16_acc(ref["x_rot"], wq) * sw.astype(np.float64)[None, :])
+    want = orc.bf16_to_f32(ref["y"]).astype(np.float64)
+    ulp = np.spacing(np.maximum(np.abs(want), 1e-38).astype(np.float32)).astype(np.float64) * 65536.0
+    bound = ulp + gamma * s_abs + 2 * 2.0 ** -23 * t
+    return bool((np.abs(orc.bf16_to_f32(got).astype(np.float64) - want) <= bound).all())
+
+
 @pytest.mark.parametrize("k", [128, 1024, 3072, 12288, 32768])
 def test_w8a16_linear_routes(orc, k):
     """The W8A16 linear's routes (the rotation inside the few-row GEMM, the
     weight-streaming and the tiled GEMMs, both rotation kernels): every call
-    succeeds and gives finite outputs (its parity against the derived bound
-    is in test_gpu_parity.py)."""
+    succeeds with finite outputs, and the small ones are within the derived
+    FP32-summation bound of the oracle."""
     g = 128
     gen = torch.Generator(device=DEV)
     gen.manual_seed(17 + k)
-    calls = 0
+    calls = checked = 0
     for n in (16, 128, 1024, 4112, 24576):
         if n * k > (1 << 28):
             continue
         wq = torch.randint(-127, 128, (n, k), device=DEV, generator=gen, dtype=torch.int32).to(torch.int8)
         sw = (torch.rand(n, device=DEV, generator=gen) * 1e-3 + 1e-4).float()
         wb = ck.ck_weight_pack(wq)
+        wq_h, sw_h = wq.cpu().numpy(), sw.cpu().numpy()
         for m, act in itertools.product((1, 2, 3, 16, 64, 65, 512, 2048, 4096), (0, 1)):
             ld = 2 * k if act else k
             if m * ld * 2 >= (1 << 30) or m * n * 2 >= (1 << 30):
@@ -198,8 +213,14 @@ def test_w8a16_linear_routes(orc, k):
             y = ck.ck_int8_linear_w8a16(x, wb, sw, g, act)
             torch.cuda.synchronize()
             calls += 1
-            assert np.isfinite(orc.bf16_to_f32(u16(y))).all(), f"m={m} k={k} n={n} act={act}"
-    say(f"w8a16 k={k}: {calls} calls")
+            got = u16(y)
+            what = f"m={m} k={k} n={n} act={act}"
+            assert np.isfinite(orc.bf16_to_f32(got)).all(), what
+            if m * n * k <= (1 << 26):
+                ref = orc.w8a16_linear(u16(x), act, wq_h, sw_h, g, return_all=True)
+                assert w8a16_within_bound(orc, got, ref, wq_h, sw_h, k), what
+                checked += 1
+    say(f"w8a16 k={k}: {calls} calls, {checked} within the bound of the oracle")
 
 
 @pytest.mark.parametrize("g", [64, 128, 256])
